@@ -1,0 +1,457 @@
+/*
+ * oracle.c -- plain, slow, serial CPU oracle for the exact drafted-decoding
+ * verify pass.  TEST INFRASTRUCTURE ONLY: nothing in the product path may
+ * include, link or call this file.  It shares no code, header, table or
+ * constant generator with the HIP library; it decodes every number format
+ * itself and implements the keyed hash itself.
+ *
+ * Sources (the pages this follows):
+ *   [README]  TensorFold project README (mirror at git.imzlh.top/EugeneClaw/
+ *             TensorFold), the paragraph that states the two exactness
+ *             guarantees (keyed Gumbel-max token, row-exact verify rows) and the
+ *             options table (temperature 0 is greedy, --no-drafts is the serial
+ *             reference).
+ *   [BLOG]    "TensorFold: The engine that makes local LLMs 2-3x faster -- without
+ *             a single token changing" (contextstudios.ai), sections "The
+ *             differentiator: byte-exact drafted decoding" and "FAQ".
+ *   [650G]    650 Group, "Faster, provably the same model" (marketintelligence
+ *             research.com), section "TensorFold: the contract is what it does
+ *             not change".
+ *   [NEVIZ]   "TensorFold v0.6 ..." (nevizhai.com), section "How exact
+ *             speculative decoding works".
+ *
+ * Arithmetic: every value is computed in IEEE double.  The only roundings are
+ * the data-type boundaries the method fixes for its tensors: linear inputs are
+ * bf16, linear outputs / logits / the residual stream are fp32, the KV cache is
+ * fp16.  Each such rounding is round-to-nearest-even, written out below.
+ * Compile with -O2 -fno-fast-math -ffp-contract=off.  OpenMP is used only over
+ * independent output columns, which cannot change any value.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ------------------------------------------------------------------------- */
+/* Number formats.                                                           */
+/* ------------------------------------------------------------------------- */
+
+/* bf16 is the top half of an IEEE binary32: value = the float whose bits are
+ * (b << 16).  Exact. */
+double ov_bf16_to_f64(uint16_t b)
+{
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return (double)f;
+}
+
+/* IEEE binary16: 1 sign, 5 exponent (bias 15), 10 fraction bits.  Exact. */
+double ov_f16_to_f64(uint16_t h)
+{
+    int sign = (h >> 15) & 1;
+    int e = (h >> 10) & 31;
+    int m = h & 1023;
+    double v;
+    if (e == 0)
+        v = ldexp((double)m, -24); /* subnormal: m * 2^-24 */
+    else if (e == 31)
+        v = m ? NAN : INFINITY;
+    else
+        v = ldexp((double)(1024 + m), e - 25); /* (1 + m/1024) * 2^(e-15) */
+    return sign ? -v : v;
+}
+
+/* Round a double to the nearest value of a binary format with p significand
+ * bits, minimum normal exponent emin and largest finite value maxfin; ties go
+ * to the even significand.  Overflow gives +-inf. */
+static double round_to_format(double v, int p, int emin, double maxfin)
+{
+    if (v == 0.0 || !isfinite(v))
+        return v;
+    int e;
+    frexp(v, &e);        /* |v| = f * 2^e, 0.5 <= f < 1 */
+    int lead = e - 1;    /* exponent of the leading bit */
+    if (lead < emin)
+        lead = emin;     /* subnormal range: fixed quantum */
+    double quantum = ldexp(1.0, lead - (p - 1));
+    double r = nearbyint(v / quantum) * quantum; /* default mode: nearest-even */
+    if (fabs(r) > maxfin)
+        return v > 0 ? INFINITY : -INFINITY;
+    return r;
+}
+
+uint16_t ov_f64_to_bf16(double v)
+{
+    if (isnan(v))
+        return 0x7FC0;
+    double r = round_to_format(v, 8, -126, ldexp(255.0, 120)); /* (2-2^-7)*2^127 */
+    float f = (float)r; /* exact: r is a bf16 value, hence a binary32 value */
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    return (uint16_t)(u >> 16);
+}
+
+uint16_t ov_f64_to_f16(double v)
+{
+    if (isnan(v))
+        return 0x7E00;
+    double r = round_to_format(v, 11, -14, 65504.0);
+    uint16_t sign = signbit(r) ? 0x8000 : 0;
+    double a = fabs(r);
+    if (isinf(a))
+        return sign | 0x7C00;
+    if (a == 0.0)
+        return sign;
+    int e;
+    frexp(a, &e);
+    int lead = e - 1;
+    if (lead < -14) /* subnormal: a = m * 2^-24 */
+        return sign | (uint16_t)ldexp(a, 24);
+    uint16_t m = (uint16_t)(ldexp(a, 10 - lead) - 1024.0);
+    return sign | (uint16_t)((lead + 15) << 10) | m;
+}
+
+float ov_f64_to_f32(double v) { return (float)v; } /* C conversion: nearest-even */
+
+/* ------------------------------------------------------------------------- */
+/* Keyed noise: a hash of (seed, position, token id) [README exactness        */
+/* paragraph; 650G].  The hash is SplitMix64 (Steele, Lea & Flood, OOPSLA     */
+/* 2014): its output function mix64 and its increment gamma.                  */
+/* ------------------------------------------------------------------------- */
+
+#define OV_GAMMA 0x9E3779B97F4A7C15ULL
+
+uint64_t ov_mix64(uint64_t z)
+{
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ULL;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBULL;
+    return z ^ (z >> 31);
+}
+
+/* Row key: the (pos+1)-th output of a SplitMix64 stream whose state starts at
+ * mix64(seed).  Token hash: the (tok+1)-th output of the stream that starts at
+ * the row key. */
+uint64_t ov_noise_hash(uint64_t seed, int64_t pos, int32_t tok)
+{
+    uint64_t row = ov_mix64(ov_mix64(seed) + (uint64_t)(pos + 1) * OV_GAMMA);
+    return ov_mix64(row + (uint64_t)((int64_t)tok + 1) * OV_GAMMA);
+}
+
+/* Uniform in (0,1): the top 52 bits plus one half, over 2^52, so u is never 0
+ * or 1.  Gumbel(0,1) by inversion: g = -log(-log(u)). */
+double ov_uniform(uint64_t h) { return ((double)(h >> 12) + 0.5) * 0x1p-52; }
+double ov_gumbel(uint64_t h) { return -log(-log(ov_uniform(h))); }
+
+/* ------------------------------------------------------------------------- */
+/* W4 linear: y[r][n] = sum_k x[r][k] * w[n][k], with the affine group        */
+/* dequantisation w[n][k] = s[n][k/G] * q[n][k] + b[n][k/G].  4-bit weights in */
+/* groups of 32 or 64 ([BLOG] "The numbers": same 4-bit checkpoints; [README] */
+/* checkpoint list: groups of 64 / of 32).  q is packed two per byte, the low */
+/* nibble holding the even k:  q[n][k] = (byte[n][k/2] >> (4*(k%2))) & 15.    */
+/* Each row r is computed alone, in order.                                   */
+/* ------------------------------------------------------------------------- */
+
+static int q_at(const uint8_t* q, int K, int n, int k)
+{
+    uint8_t byte = q[(size_t)n * (size_t)(K / 2) + (size_t)(k / 2)];
+    return (k % 2 == 0) ? (byte & 15) : (byte >> 4);
+}
+
+void ov_w4_linear(const uint16_t* x, int R, int K, const uint8_t* q,
+                  const uint16_t* s, const uint16_t* b, int N, int G, double* y)
+{
+    int ng = K / G;
+    for (int r = 0; r < R; r++) {
+        const uint16_t* xr = x + (size_t)r * K;
+#pragma omp parallel for schedule(static)
+        for (int n = 0; n < N; n++) {
+            double acc = 0.0;
+            for (int k = 0; k < K; k++) {
+                double sc = ov_f16_to_f64(s[(size_t)n * ng + k / G]);
+                double bi = ov_f16_to_f64(b[(size_t)n * ng + k / G]);
+                double w = sc * (double)q_at(q, K, n, k) + bi;
+                acc += w * ov_bf16_to_f64(xr[k]);
+            }
+            y[(size_t)r * N + n] = acc;
+        }
+    }
+}
+
+/* The same linear with its output rounded to the method's output type, fp32. */
+void ov_w4_linear_f32(const uint16_t* x, int R, int K, const uint8_t* q,
+                      const uint16_t* s, const uint16_t* b, int N, int G, float* y)
+{
+    double* t = (double*)malloc(sizeof(double) * (size_t)R * N);
+    ov_w4_linear(x, R, K, q, s, b, N, G, t);
+    for (size_t i = 0; i < (size_t)R * N; i++)
+        y[i] = (float)t[i];
+    free(t);
+}
+
+/* ------------------------------------------------------------------------- */
+/* SiLU-gated MLP glue: h = bf16(silu(g) * u), silu(v) = v / (1 + e^-v).      */
+/* ------------------------------------------------------------------------- */
+
+double ov_silu(double v) { return v / (1.0 + exp(-v)); }
+
+void ov_silu_mul_bf16(const float* g, const float* u, size_t n, uint16_t* h)
+{
+    for (size_t i = 0; i < n; i++)
+        h[i] = ov_f64_to_bf16(ov_silu((double)g[i]) * (double)u[i]);
+}
+
+/* Dense MLP slice: gate and up W4 linears H->I, the glue, down W4 linear I->H.
+ * Optional intermediates (g, u as fp32, h as bf16) are returned when non-NULL. */
+void ov_mlp(const uint16_t* x, int R, int H, int I, int G,
+            const uint8_t* gq, const uint16_t* gs, const uint16_t* gb,
+            const uint8_t* uq, const uint16_t* us, const uint16_t* ub,
+            const uint8_t* dq, const uint16_t* ds, const uint16_t* db,
+            float* y, float* g_out, float* u_out, uint16_t* h_out)
+{
+    size_t ri = (size_t)R * I;
+    float* g = (float*)malloc(sizeof(float) * ri);
+    float* u = (float*)malloc(sizeof(float) * ri);
+    uint16_t* h = (uint16_t*)malloc(sizeof(uint16_t) * ri);
+    ov_w4_linear_f32(x, R, H, gq, gs, gb, I, G, g);
+    ov_w4_linear_f32(x, R, H, uq, us, ub, I, G, u);
+    ov_silu_mul_bf16(g, u, ri, h);
+    ov_w4_linear_f32(h, R, I, dq, ds, db, H, G, y);
+    if (g_out) memcpy(g_out, g, sizeof(float) * ri);
+    if (u_out) memcpy(u_out, u, sizeof(float) * ri);
+    if (h_out) memcpy(h_out, h, sizeof(uint16_t) * ri);
+    free(g);
+    free(u);
+    free(h);
+}
+
+/* ------------------------------------------------------------------------- */
+/* Keyed sampler [README exactness paragraph; 650G]: the token at position p  */
+/* is the argmax, over the top-k / top-p candidates, of l/T + g(seed, p, id). */
+/* Temperature 0 is greedy [README options table].                            */
+/* Order used for every selection and tie: larger logit first, then the lower */
+/* token id.                                                                  */
+/* ------------------------------------------------------------------------- */
+
+static int ranks_before(const float* l, int a, int b) /* a before b? */
+{
+    return l[a] > l[b] || (l[a] == l[b] && a < b);
+}
+
+/* The k first token ids under (logit desc, id asc), by k scans of the row. */
+int ov_topk(const float* l, int V, int k, int32_t* ids)
+{
+    if (k > V) k = V;
+    char* taken = (char*)calloc((size_t)V, 1);
+    for (int j = 0; j < k; j++) {
+        int best = -1;
+        for (int i = 0; i < V; i++)
+            if (!taken[i] && (best < 0 || ranks_before(l, i, best)))
+                best = i;
+        taken[best] = 1;
+        ids[j] = best;
+    }
+    free(taken);
+    return k;
+}
+
+typedef struct {
+    int32_t token;    /* sampled token id */
+    double gap;       /* best minus second-best perturbed score (+inf if one) */
+    int32_t n_cand;   /* candidates after top-k */
+    int32_t n_kept;   /* candidates after top-p */
+    int32_t topp_edge;/* 1 if the nucleus cut lies within 1e-9*Z of top_p*Z */
+} ov_sample_out;
+
+/* Second stage: top-p over the n ordered candidates, then the keyed argmax.
+ * cand[] must be ordered (logit desc, id asc). */
+void ov_sample_from_candidates(const float* l, const int32_t* cand, int n,
+                               int64_t pos, double T, double top_p,
+                               uint64_t seed, ov_sample_out* out)
+{
+    double* e = (double*)malloc(sizeof(double) * (size_t)n);
+    double m = (double)l[cand[0]];
+    double Z = 0.0;
+    for (int j = 0; j < n; j++) {
+        e[j] = exp(((double)l[cand[j]] - m) / T);
+        Z += e[j];
+    }
+    /* nucleus: candidate j stays while the mass strictly before it is below
+     * top_p * Z; candidate 0 always stays. */
+    int kept = 0;
+    double before = 0.0;
+    int edge = 0;
+    for (int j = 0; j < n; j++) {
+        if (j > 0 && !(before < top_p * Z))
+            break;
+        kept = j + 1;
+        before += e[j];
+    }
+    /* flag a cut whose decision lies within 1e-9 Z of the threshold */
+    {
+        double acc = 0.0;
+        for (int j = 0; j < n; j++) {
+            if (j > 0 && fabs(acc - top_p * Z) < 1e-9 * Z)
+                edge = 1;
+            acc += e[j];
+        }
+    }
+    int best = -1;
+    double zb = -INFINITY, z2 = -INFINITY;
+    for (int j = 0; j < kept; j++) {
+        int t = cand[j];
+        double z = (double)l[t] / T + ov_gumbel(ov_noise_hash(seed, pos, t));
+        if (best < 0 || z > zb || (z == zb && t < best)) {
+            z2 = zb;
+            zb = z;
+            best = t;
+        } else if (z > z2) {
+            z2 = z;
+        }
+    }
+    out->token = best;
+    out->gap = (kept > 1) ? zb - z2 : INFINITY;
+    out->n_cand = n;
+    out->n_kept = kept;
+    out->topp_edge = edge;
+    free(e);
+}
+
+/* One row: greedy when T == 0, else top-k, top-p and the keyed argmax. */
+void ov_sample_row(const float* l, int V, int64_t pos, double T, int top_k,
+                   double top_p, uint64_t seed, ov_sample_out* out)
+{
+    if (T == 0.0) {
+        int best = 0;
+        for (int i = 1; i < V; i++)
+            if (ranks_before(l, i, best))
+                best = i;
+        int second = -1;
+        for (int i = 0; i < V; i++)
+            if (i != best && (second < 0 || ranks_before(l, i, second)))
+                second = i;
+        out->token = best;
+        out->gap = (second < 0) ? INFINITY : (double)l[best] - (double)l[second];
+        out->n_cand = V;
+        out->n_kept = 1;
+        out->topp_edge = 0;
+        return;
+    }
+    int k = top_k < V ? top_k : V;
+    int32_t* cand = (int32_t*)malloc(sizeof(int32_t) * (size_t)k);
+    ov_topk(l, V, k, cand);
+    ov_sample_from_candidates(l, cand, k, pos, T, top_p, seed, out);
+    free(cand);
+}
+
+/* Serial sampling of R rows, one at a time. */
+void ov_sample_rows(const float* logits, int R, int V, const int64_t* pos,
+                    double T, int top_k, double top_p, uint64_t seed,
+                    int32_t* tokens, double* gaps, int32_t* n_kept, int32_t* edge)
+{
+    for (int r = 0; r < R; r++) {
+        ov_sample_out o;
+        ov_sample_row(logits + (size_t)r * V, V, pos[r], T, top_k, top_p, seed, &o);
+        tokens[r] = o.token;
+        if (gaps) gaps[r] = o.gap;
+        if (n_kept) n_kept[r] = o.n_kept;
+        if (edge) edge[r] = o.topp_edge;
+    }
+}
+
+/* ------------------------------------------------------------------------- */
+/* Accept rule [README; BLOG FAQ; 650G]: a draft is accepted exactly when it  */
+/* equals the token serial decoding samples there.  Row i's sample is         */
+/* compared with draft i; the leading run of equal pairs is accepted, and the */
+/* next row's sample is committed with it (capped at the R rows sampled).     */
+/* ------------------------------------------------------------------------- */
+
+void ov_accept(const int32_t* sampled, int R, const int32_t* draft, int D,
+               int32_t* n_accept, int32_t* n_commit)
+{
+    int a = 0;
+    while (a < D && draft[a] == sampled[a])
+        a++;
+    *n_accept = a;
+    *n_commit = (a + 1 < R) ? a + 1 : R;
+}
+
+/* ------------------------------------------------------------------------- */
+/* MoE verify layer (30B-A3B-like): router softmax, top-E_k experts, weights  */
+/* renormalised over the chosen experts, each expert a SwiGLU MLP of W4        */
+/* linears, outputs summed in rank order.  Every lane is routed on its own.   */
+/* Expert e's matrices sit at offset e in each stacked array.                 */
+/* ------------------------------------------------------------------------- */
+
+void ov_moe_route(const float* rho, int E, int top, int32_t* ids, double* w)
+{
+    /* softmax over all experts */
+    double m = -INFINITY;
+    for (int e = 0; e < E; e++)
+        if ((double)rho[e] > m) m = (double)rho[e];
+    double* p = (double*)malloc(sizeof(double) * (size_t)E);
+    double S = 0.0;
+    for (int e = 0; e < E; e++) {
+        p[e] = exp((double)rho[e] - m);
+        S += p[e];
+    }
+    for (int e = 0; e < E; e++)
+        p[e] /= S;
+    /* top experts by router logit (the softmax is increasing), lower id on ties */
+    ov_topk(rho, E, top, ids);
+    double sel = 0.0;
+    for (int j = 0; j < top; j++)
+        sel += p[ids[j]];
+    for (int j = 0; j < top; j++)
+        w[j] = p[ids[j]] / sel;
+    free(p);
+}
+
+void ov_moe(const uint16_t* x, const float* rho, int R, int H, int I, int E,
+            int top, int G,
+            const uint8_t* gq, const uint16_t* gs, const uint16_t* gb,
+            const uint8_t* uq, const uint16_t* us, const uint16_t* ub,
+            const uint8_t* dq, const uint16_t* ds, const uint16_t* db,
+            float* y, int32_t* ids_out, double* w_out)
+{
+    size_t qi = (size_t)I * H / 2, si = (size_t)I * H / G; /* gate/up per expert */
+    size_t qd = (size_t)H * I / 2, sd = (size_t)H * I / G; /* down per expert */
+    int32_t* ids = (int32_t*)malloc(sizeof(int32_t) * (size_t)top);
+    double* w = (double*)malloc(sizeof(double) * (size_t)top);
+    float* ye = (float*)malloc(sizeof(float) * (size_t)H);
+    double* acc = (double*)malloc(sizeof(double) * (size_t)H);
+    for (int r = 0; r < R; r++) {
+        ov_moe_route(rho + (size_t)r * E, E, top, ids, w);
+        for (int i = 0; i < H; i++) acc[i] = 0.0;
+        for (int j = 0; j < top; j++) {
+            int e = ids[j];
+            ov_mlp(x + (size_t)r * H, 1, H, I, G,
+                   gq + e * qi, gs + e * si, gb + e * si,
+                   uq + e * qi, us + e * si, ub + e * si,
+                   dq + e * qd, ds + e * sd, db + e * sd, ye, NULL, NULL, NULL);
+            for (int i = 0; i < H; i++)
+                acc[i] += w[j] * (double)ye[i];
+        }
+        for (int i = 0; i < H; i++)
+            y[(size_t)r * H + i] = (float)acc[i];
+        if (ids_out) memcpy(ids_out + (size_t)r * top, ids, sizeof(int32_t) * top);
+        if (w_out) memcpy(w_out + (size_t)r * top, w, sizeof(double) * top);
+    }
+    free(ids);
+    free(w);
+    free(ye);
+    free(acc);
+}
+
+/* Harness loop for statistical tests: n independent calls of ov_sample_row on
+ * one logit row, call i with position pos[i] and seed seeds[i]. */
+void ov_sample_many(const float* l, int V, int n, const int64_t* pos,
+                    const uint64_t* seeds, double T, int top_k, double top_p,
+                    int32_t* tokens)
+{
+    for (int i = 0; i < n; i++) {
+        ov_sample_out o;
+        ov_sample_row(l, V, pos[i], T, top_k, top_p, seeds[i], &o);
+        tokens[i] = o.token;
+    }
+}

@@ -1,0 +1,115 @@
+"""Seeded synthetic inputs for the verify-pass workloads.
+
+This module only draws random numbers and encodes them into the storage
+formats the library takes (bf16 / fp16 bit patterns, packed 4-bit weights).  It
+holds none of the method's arithmetic, and it is the only code that both the
+CPU oracle's tests and the GPU path consume.
+
+Workloads (all draws from numpy's PCG64 `default_rng(seed)`):
+  tiny      one W4 linear K=256 -> N=512, G=64, 4 lanes, sampler over V=512
+  mlp       dense 27B-class MLP slice: gate/up 5120 -> 17408, down 17408 -> 5120, G=64
+  lm_head   W4 5120 -> 151936, G=64, 64 hidden rows
+  moe       hidden 2048, 128 experts, top-8, expert intermediate 768, G=32
+  decoder   8-layer toy decoder (hidden 2048, 16 q / 4 kv heads, head dim 128,
+            MLP 6144, vocab 32768, G=64)
+
+Weight recipe: every 4-bit code is uniform on 0..15 (a uniform random byte is
+two independent uniform nibbles), scale ~ U(0.01, 0.05) and bias ~ N(0, 0.1)
+per group, both rounded to fp16; activations ~ N(0, 1) rounded to bf16.
+"""
+import numpy as np
+
+
+def rng(seed):
+    return np.random.default_rng(seed)
+
+
+def bf16_bits(a):
+    """Round float values to bf16 (nearest-even) and return the uint16 bits."""
+    f = np.ascontiguousarray(a, dtype=np.float32)
+    u = f.view(np.uint32).astype(np.uint64)
+    lsb = (u >> 16) & 1
+    r = ((u + 0x7FFF + lsb) >> 16).astype(np.uint16)
+    nan = np.isnan(f)
+    if nan.any():
+        r[nan] = 0x7FC0
+    return r.reshape(np.shape(a))
+
+
+def fp16_bits(a):
+    """Round to IEEE binary16 (nearest-even, numpy) and return the uint16 bits."""
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float64).astype(np.float16)).view(np.uint16)
+
+
+def bf16_values(bits):
+    """bf16 bits -> float32 values (for building test inputs only)."""
+    b = np.ascontiguousarray(bits, dtype=np.uint16)
+    return (b.astype(np.uint32) << 16).view(np.float32)
+
+
+def w4_matrix(g, N, K, G):
+    """Random packed 4-bit weights q [N][K/2] u8, scale/bias [N][K/G] fp16 bits."""
+    assert K % G == 0 and K % 2 == 0
+    q = g.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+    s = fp16_bits(g.uniform(0.01, 0.05, size=(N, K // G)))
+    b = fp16_bits(g.normal(0.0, 0.1, size=(N, K // G)))
+    return q, s, b
+
+
+def activations(g, R, K):
+    return bf16_bits(g.standard_normal((R, K), dtype=np.float32))
+
+
+# ---------------------------------------------------------------------------
+# Workloads.
+# ---------------------------------------------------------------------------
+
+def tiny(seed=1001):
+    """One W4 linear K=256 -> N=512 (G=64) on 4 lanes, and the sampler setting
+    T=0.8, top-k 20, top-p 0.95, seed 42 over V=512."""
+    g = rng(seed)
+    q, s, b = w4_matrix(g, 512, 256, 64)
+    x = activations(g, 4, 256)
+    return dict(K=256, N=512, G=64, q=q, s=s, b=b, x=x,
+                T=0.8, top_k=20, top_p=0.95, seed=42)
+
+
+def mlp(seed=1002, H=5120, I=17408, G=64, R=16):
+    g = rng(seed)
+    gate = w4_matrix(g, I, H, G)
+    up = w4_matrix(g, I, H, G)
+    down = w4_matrix(g, H, I, G)
+    x = activations(g, R, H)
+    return dict(H=H, I=I, G=G, gate=gate, up=up, down=down, x=x)
+
+
+def lm_head(seed=1003, K=5120, V=151936, G=64, rows=64):
+    g = rng(seed)
+    w = w4_matrix(g, V, K, G)
+    h = activations(g, rows, K)
+    return dict(K=K, V=V, G=G, w=w, h=h)
+
+
+def moe(seed=1004, H=2048, I=768, E=128, top=8, G=32, R=16):
+    g = rng(seed)
+    gate = w4_matrix(g, E * I, H, G)
+    up = w4_matrix(g, E * I, H, G)
+    down = w4_matrix(g, E * H, I, G)
+    stack = lambda w, rows: (w[0].reshape(E, rows, -1), w[1].reshape(E, rows, -1),
+                             w[2].reshape(E, rows, -1))
+    x = activations(g, R, H)
+    rho = g.standard_normal((R, E), dtype=np.float32)
+    return dict(H=H, I=I, E=E, top=top, G=G, gate=stack(gate, I), up=stack(up, I),
+                down=stack(down, H), x=x, rho=rho)
+
+
+def logits(g, R, V, scale=4.0):
+    """Synthetic fp32 logit rows for sampler tests: N(0, scale^2)."""
+    return (g.standard_normal((R, V)) * scale).astype(np.float32)
+
+
+def draft_coins(seed, n, p):
+    """Pre-drawn drafter decisions: accept-coin per slot with probability p, and a
+    random offset 1..V-1 used to make a guaranteed-wrong guess."""
+    g = rng(seed)
+    return g.random(n) < p, g.integers(1, 1 << 30, size=n)

@@ -1,0 +1,65 @@
+"""Pins for the keyed noise: SplitMix64's published stream, the uniform map's
+range, the Gumbel bounds, and the distribution of the noise."""
+import math
+import os
+
+import numpy as np
+import pytest
+from scipy import stats
+
+import oracle
+
+GAMMA = 0x9E3779B97F4A7C15
+M64 = (1 << 64) - 1
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def _golden_stream():
+    out = []
+    with open(os.path.join(HERE, "golden", "splitmix64_seed0.txt")) as f:
+        for line in f:
+            if line.strip() and not line.startswith("#"):
+                i, h = line.split()
+                out.append((int(i), int(h, 16)))
+    return out
+
+
+def test_mix64_and_gamma_reproduce_published_splitmix64_stream():
+    for i, h in _golden_stream():
+        assert oracle.mix64((i * GAMMA) & M64) == h
+
+
+def test_row_key_for_seed0_pos0_is_first_stream_output():
+    # mix64(0) == 0, so the row key of (seed 0, position 0) is mix64(gamma), the
+    # stream's first output; the token hash for token t is then that key's own
+    # stream at index t+1.
+    first = _golden_stream()[0][1]
+    assert oracle.mix64(0) == 0
+    for t in (0, 1, 7, 151935):
+        assert oracle.noise_hash(0, 0, t) == oracle.mix64((first + (t + 1) * GAMMA) & M64)
+
+
+def test_uniform_range_and_endpoints():
+    assert oracle.uniform(0) == 2.0 ** -53
+    assert oracle.uniform(M64) == 1.0 - 2.0 ** -53
+    g_lo = oracle.gumbel(0)
+    g_hi = oracle.gumbel(M64)
+    assert g_lo == pytest.approx(-math.log(53 * math.log(2.0)), rel=1e-15)
+    assert g_hi == pytest.approx(53 * math.log(2.0), rel=1e-12)
+    assert -3.6037789929704576 == pytest.approx(g_lo, rel=1e-15)
+
+
+def test_noise_is_uniform_and_gumbel_distributed():
+    # over tokens at a fixed (seed, position), and over positions at a fixed token
+    u_tok = np.array([oracle.uniform(oracle.noise_hash(42, 5, t)) for t in range(20000)])
+    u_pos = np.array([oracle.uniform(oracle.noise_hash(42, p, 3)) for p in range(20000)])
+    u_seed = np.array([oracle.uniform(oracle.noise_hash(s, 5, 3)) for s in range(20000)])
+    for u in (u_tok, u_pos, u_seed):
+        assert stats.kstest(u, "uniform").pvalue > 1e-3
+    g = -np.log(-np.log(u_tok))
+    assert stats.kstest(g, stats.gumbel_r.cdf).pvalue > 1e-3
+    gg = np.array([oracle.gumbel(oracle.noise_hash(42, 5, t)) for t in range(2000)])
+    assert np.allclose(gg, g[:2000], rtol=1e-14, atol=1e-14)
+    # neighbouring positions and tokens are uncorrelated
+    assert abs(np.corrcoef(u_pos[:-1], u_pos[1:])[0, 1]) < 0.03
+    assert abs(np.corrcoef(u_tok[:-1], u_tok[1:])[0, 1]) < 0.03
