@@ -56,6 +56,7 @@ def _declare(L):
     L.ov_uniform.restype = f64
     L.ov_gumbel.argtypes = [C.c_uint64]
     L.ov_gumbel.restype = f64
+    L.ov_num_threads.restype = C.c_int
     L.ov_silu.argtypes = [f64]
     L.ov_silu.restype = f64
     L.ov_w4_linear.argtypes = [_p(u16), i32, i32, _p(u8), _p(u16), _p(u16), i32, i32, _p(f64)]
@@ -144,6 +145,10 @@ def uniform(h):
 
 def gumbel(h):
     return float(lib().ov_gumbel(h))
+
+
+def num_threads():
+    return int(lib().ov_num_threads())
 
 
 def silu(v):

@@ -162,20 +162,26 @@ void ov_w4_linear(const uint16_t* x, int R, int K, const uint8_t* q,
                   const uint16_t* s, const uint16_t* b, int N, int G, double* y)
 {
     int ng = K / G;
+    double* xd = (double*)malloc(sizeof(double) * (size_t)K);
     for (int r = 0; r < R; r++) {
-        const uint16_t* xr = x + (size_t)r * K;
+        for (int k = 0; k < K; k++)
+            xd[k] = ov_bf16_to_f64(x[(size_t)r * K + k]);
 #pragma omp parallel for schedule(static)
         for (int n = 0; n < N; n++) {
             double acc = 0.0;
+            double sc = 0.0, bi = 0.0; /* the current group's scale and bias */
             for (int k = 0; k < K; k++) {
-                double sc = ov_f16_to_f64(s[(size_t)n * ng + k / G]);
-                double bi = ov_f16_to_f64(b[(size_t)n * ng + k / G]);
+                if (k % G == 0) {
+                    sc = ov_f16_to_f64(s[(size_t)n * ng + k / G]);
+                    bi = ov_f16_to_f64(b[(size_t)n * ng + k / G]);
+                }
                 double w = sc * (double)q_at(q, K, n, k) + bi;
-                acc += w * ov_bf16_to_f64(xr[k]);
+                acc += w * xd[k];
             }
             y[(size_t)r * N + n] = acc;
         }
     }
+    free(xd);
 }
 
 /* The same linear with its output rounded to the method's output type, fp32. */
@@ -455,3 +461,11 @@ void ov_sample_many(const float* l, int V, int n, const int64_t* pos,
         tokens[i] = o.token;
     }
 }
+
+/* Threads OpenMP would use for the column loops (reported with timings). */
+#ifdef _OPENMP
+#include <omp.h>
+int ov_num_threads(void) { return omp_get_max_threads(); }
+#else
+int ov_num_threads(void) { return 1; }
+#endif
