@@ -1,0 +1,200 @@
+"""Python binding of libexactverify.so, the MI355X verify pass of exact drafted
+decoding.  Argument marshalling only: every step runs in the HIP kernels of
+the library; PyTorch supplies device memory and the current stream.
+
+The functions mirror the C ABI in include/exactverify.h and take torch tensors
+on the current HIP device.  bf16 / fp16 data may be passed as torch.bfloat16 /
+torch.float16 tensors or as int16/uint16 bit patterns.
+
+There is no fallback: if the library is not built, or no GPU is visible,
+calls raise.
+"""
+import ctypes as C
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libexactverify.so")
+
+EV_OK, EV_EINVAL, EV_EUNSUPPORTED, EV_EHIP, EV_EWORKSPACE = 0, -1, -2, -3, -4
+MAX_LANES = 16
+MAX_TOPK = 64
+
+_lib = None
+
+
+class EvError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__(f"[{code}] {msg}")
+        self.code = code
+
+
+class Sampling(C.Structure):
+    _fields_ = [("temperature", C.c_double), ("top_k", C.c_int32), ("top_p", C.c_double),
+                ("seed", C.c_uint64)]
+
+
+_vp, _sz, _i32, _i64 = C.c_void_p, C.c_size_t, C.c_int32, C.c_int64
+
+# name -> (restype, argtypes)
+_SIGS = {
+    "ev_last_error": (C.c_char_p, []),
+    "ev_version": (_i32, []),
+    "verify_linear_w4_workspace": (_sz, [_i32, _i32, _i32]),
+    "verify_linear_w4": (_i32, [_vp, _i32, _i32, _vp, _vp, _vp, _i32, _i32, _vp, _vp, _sz, _vp]),
+    "verify_mlp_w4_workspace": (_sz, [_i32, _i32, _i32]),
+    "verify_mlp_w4": (_i32, [_vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp,
+                             _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "keyed_sample_workspace": (_sz, [_i32]),
+    "keyed_sample": (_i32, [_vp, _i32, _i32, _vp, Sampling, _vp, _vp, _vp, _sz, _vp]),
+    "accept_prefix": (_i32, [_vp, _i32, _vp, _i32, _vp, _vp, _vp]),
+    "ev_w4_timing": (_i32, [_i32]),
+    "ev_w4_timing_read": (_i32, [C.POINTER(_i64), C.POINTER(C.c_double), C.POINTER(C.c_double)]),
+}
+
+
+def lib():
+    """Load the library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built: run `python __graft_entry__.py` "
+                               "(build()) or `python exact_speculative_decoding_amd/build.py`")
+        L = C.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def exported_symbols():
+    return list(_SIGS)
+
+
+def _check(rc):
+    if rc != EV_OK:
+        raise EvError(rc, lib().ev_last_error().decode(errors="replace"))
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return C.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _dev(t, name, dtypes):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name}: must be a device tensor")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name}: dtype {t.dtype} not in {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    return C.c_void_p(t.data_ptr())
+
+
+_B16 = (torch.bfloat16, torch.int16, torch.uint16)
+_F16 = (torch.float16, torch.int16, torch.uint16)
+_U8 = (torch.uint8,)
+
+
+def _workspace(nbytes, device, ws):
+    if nbytes == 0:
+        return None, 0
+    if ws is None:
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    if ws.numel() * ws.element_size() < nbytes:
+        raise ValueError(f"workspace too small: {ws.numel()} < {nbytes}")
+    return ws, ws.numel() * ws.element_size()
+
+
+def verify_linear_w4_workspace(K, N, G):
+    return int(lib().verify_linear_w4_workspace(K, N, G))
+
+
+def verify_linear_w4(x, q, s, b, G, y=None, ws=None, stream=None):
+    """y[R][N] fp32 = W4 linear of x[R][K] (bf16) with q[N][K/2], s/b[N][K/G]."""
+    R, K = x.shape
+    N = q.shape[0]
+    if y is None:
+        y = torch.empty((R, N), dtype=torch.float32, device=x.device)
+    ws, nb = _workspace(verify_linear_w4_workspace(K, N, G), x.device, ws)
+    _check(lib().verify_linear_w4(
+        _dev(x, "x", _B16), R, K, _dev(q, "q", _U8), _dev(s, "s", _F16), _dev(b, "b", _F16),
+        N, G, _dev(y, "y", (torch.float32,)),
+        None if ws is None else C.c_void_p(ws.data_ptr()), nb, _stream(stream)))
+    return y
+
+
+def verify_mlp_w4_workspace(H, I, G):
+    return int(lib().verify_mlp_w4_workspace(H, I, G))
+
+
+def verify_mlp_w4(x, gate, up, down, G, y=None, h=None, ws=None, stream=None):
+    """Dense SiLU-gated MLP slice; gate/up/down are (q, s, b) tensors."""
+    R, H = x.shape
+    I = gate[0].shape[0]
+    if y is None:
+        y = torch.empty((R, H), dtype=torch.float32, device=x.device)
+    ws, nb = _workspace(verify_mlp_w4_workspace(H, I, G), x.device, ws)
+    w = []
+    for name, (q, s, b) in (("gate", gate), ("up", up), ("down", down)):
+        w += [_dev(q, name + ".q", _U8), _dev(s, name + ".s", _F16), _dev(b, name + ".b", _F16)]
+    _check(lib().verify_mlp_w4(
+        _dev(x, "x", _B16), R, H, I, G, *w, _dev(y, "y", (torch.float32,)),
+        None if h is None else _dev(h, "h", _B16),
+        C.c_void_p(ws.data_ptr()), nb, _stream(stream)))
+    return y
+
+
+def keyed_sample_workspace(V):
+    return int(lib().keyed_sample_workspace(V))
+
+
+def keyed_sample(logits, positions, temperature, top_k, top_p, seed, tokens=None, gap=None,
+                 ws=None, stream=None):
+    """tokens [R] int32 (and gap [R] fp64 if given) for logits [R][V] fp32."""
+    R, V = logits.shape
+    if tokens is None:
+        tokens = torch.empty(R, dtype=torch.int32, device=logits.device)
+    ws, nb = _workspace(keyed_sample_workspace(V), logits.device, ws)
+    sp = Sampling(float(temperature), int(top_k), float(top_p), int(seed) & ((1 << 64) - 1))
+    _check(lib().keyed_sample(
+        _dev(logits, "logits", (torch.float32,)), R, V, _dev(positions, "positions", (torch.int64,)),
+        sp, _dev(tokens, "tokens", (torch.int32,)),
+        None if gap is None else _dev(gap, "gap", (torch.float64,)),
+        C.c_void_p(ws.data_ptr()), nb, _stream(stream)))
+    return tokens
+
+
+def accept_prefix(sampled, draft, n_accept=None, n_commit=None, stream=None):
+    """(n_accept, n_commit) as one-element int32 device tensors."""
+    R = sampled.shape[0]
+    D = 0 if draft is None else draft.shape[0]
+    dev = sampled.device
+    if n_accept is None:
+        n_accept = torch.empty(1, dtype=torch.int32, device=dev)
+    if n_commit is None:
+        n_commit = torch.empty(1, dtype=torch.int32, device=dev)
+    _check(lib().accept_prefix(
+        _dev(sampled, "sampled", (torch.int32,)), R,
+        None if D == 0 else _dev(draft, "draft", (torch.int32,)), D,
+        _dev(n_accept, "n_accept", (torch.int32,)), _dev(n_commit, "n_commit", (torch.int32,)),
+        _stream(stream)))
+    return n_accept, n_commit
+
+
+def w4_timing(enable):
+    """Turn the per-launch event timing of the W4 kernel on or off."""
+    _check(lib().ev_w4_timing(1 if enable else 0))
+
+
+def w4_timing_read():
+    """(launches, total_ms, total_algorithmic_bytes) since the last read."""
+    n, ms, by = C.c_int64(), C.c_double(), C.c_double()
+    _check(lib().ev_w4_timing_read(C.byref(n), C.byref(ms), C.byref(by)))
+    return n.value, ms.value, by.value

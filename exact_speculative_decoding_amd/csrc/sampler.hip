@@ -1,0 +1,280 @@
+// Keyed Gumbel-max sampler and the accept rule on gfx950.
+//
+// TensorFold README, exactness paragraph (restated by 650 Group, "TensorFold:
+// the contract is what it does not change"): the token at position p is the
+// argmax over the top-k/top-p candidates of logit/T + g(seed, p, token), with g
+// Gumbel noise from a hash of seed, position and token id -- an exact draw that
+// depends only on that row's logits and its position.  Temperature 0 is greedy
+// (README options table).
+//
+// Two launches per call, neither depending on R except through the grid's row
+// dimension (each row is processed by its own workgroups, identically):
+//   topk_chunk_kernel   grid (ceil(V/8192), R) x 256: each workgroup selects
+//                       the top-kk of its 8192 logits under (logit desc, id asc)
+//                       by kk rounds of a block-wide max of 64-bit order keys
+//                       (DPP/swizzle wave max + a 4-way LDS merge);
+//   merge_sample_kernel grid R x 64: one wave merges the chunk lists into the
+//                       row's top-kk, then top-p and the keyed argmax in fp64.
+// The selection involves no arithmetic, so it is exact; the fp64 stage follows
+// the same fixed order for every row.
+#include "ev_internal.h"
+
+namespace ev {
+
+constexpr int kChunk = 8192;         // logits per top-k workgroup
+constexpr int kSThreads = 256;
+constexpr int kPer = kChunk / kSThreads;
+constexpr int kMaxChunks = 32;       // V <= 32 * 8192 = 262144
+constexpr unsigned long long kGamma = 0x9E3779B97F4A7C15ull;
+
+// Order key: larger key = earlier in (logit desc, id asc).  -0 and +0 compare
+// equal as logits, so -0 is folded onto +0.  Key 0 is below every real key.
+__device__ __forceinline__ unsigned long long order_key(float l, int id) {
+    uint32_t u = __float_as_uint(l);
+    if ((u & 0x7fffffffu) == 0u) u = 0u;
+    const uint32_t ok = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return ((unsigned long long)ok << 32) | (unsigned long long)(~(uint32_t)id);
+}
+__device__ __forceinline__ float key_logit(unsigned long long k) {
+    const uint32_t ok = (uint32_t)(k >> 32);
+    const uint32_t u = (ok & 0x80000000u) ? (ok & 0x7fffffffu) : ~ok;
+    return __uint_as_float(u);
+}
+__device__ __forceinline__ int key_id(unsigned long long k) { return (int)(~(uint32_t)k); }
+
+__device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        const unsigned long long o = __shfl_xor(v, off, 64);
+        v = o > v ? o : v;
+    }
+    return v;
+}
+
+// SplitMix64 output function (Steele, Lea & Flood, OOPSLA 2014).
+__device__ __forceinline__ unsigned long long mix64(unsigned long long z) {
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    return z ^ (z >> 31);
+}
+
+// g(seed, p, id): row key = output p+1 of the stream started at mix64(seed);
+// token hash = output id+1 of the stream started at the row key; uniform from
+// the top 52 bits plus a half; Gumbel by inversion, all in fp64.
+__device__ __forceinline__ double keyed_gumbel(unsigned long long seed, long long pos, int id) {
+    const unsigned long long row = mix64(mix64(seed) + (unsigned long long)(pos + 1) * kGamma);
+    const unsigned long long h = mix64(row + (unsigned long long)((long long)id + 1) * kGamma);
+    const double u = ((double)(h >> 12) + 0.5) * 0x1p-52;
+    return -log(-log(u));
+}
+
+__global__ __launch_bounds__(kSThreads) void topk_chunk_kernel(const float* __restrict__ logits,
+                                                               int V, int kk, int nchunk,
+                                                               unsigned long long* __restrict__ out) {
+    __shared__ unsigned long long wbest[kSThreads / 64];
+    const int r = blockIdx.y, chunk = blockIdx.x;
+    const int base = chunk * kChunk;
+    const float* row = logits + (size_t)r * V;
+    unsigned long long keys[kPer];
+    unsigned long long best = 0ull;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        const int idx = base + i * kSThreads + threadIdx.x;
+        keys[i] = idx < V ? order_key(row[idx], idx) : 0ull;
+        best = keys[i] > best ? keys[i] : best;
+    }
+    unsigned long long* dst = out + ((size_t)r * nchunk + chunk) * kk;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    for (int round = 0; round < kk; ++round) {
+        const unsigned long long w = wave_max_u64(best);
+        if (lane == 0) wbest[wave] = w;
+        __syncthreads();
+        unsigned long long win = wbest[0];
+#pragma unroll
+        for (int i = 1; i < kSThreads / 64; ++i) win = wbest[i] > win ? wbest[i] : win;
+        __syncthreads();
+        if (threadIdx.x == 0) dst[round] = win;
+        if (win != 0ull && best == win) {
+            best = 0ull;
+#pragma unroll
+            for (int i = 0; i < kPer; ++i) {
+                if (keys[i] == win) keys[i] = 0ull;
+                best = keys[i] > best ? keys[i] : best;
+            }
+        }
+    }
+}
+
+struct SampleArgs {
+    const unsigned long long* cand;  // [R][nchunk][kk]
+    const long long* positions;
+    int nchunk, kk, V;
+    double T, top_p;
+    unsigned long long seed;
+    int* tokens;
+    double* gap;
+};
+
+__global__ __launch_bounds__(64) void merge_sample_kernel(SampleArgs a) {
+    const int r = blockIdx.x, lane = threadIdx.x;
+    const int n = a.nchunk * a.kk;  // <= 32 * 64
+    const unsigned long long* src = a.cand + (size_t)r * n;
+    unsigned long long keys[kMaxChunks];
+    unsigned long long best = 0ull;
+#pragma unroll
+    for (int i = 0; i < kMaxChunks; ++i) {
+        const int idx = lane + 64 * i;
+        keys[i] = idx < n ? src[idx] : 0ull;
+        best = keys[i] > best ? keys[i] : best;
+    }
+    // the row's top-kk, candidate j ends up in lane j
+    unsigned long long mine = 0ull;
+    for (int round = 0; round < a.kk; ++round) {
+        const unsigned long long win = wave_max_u64(best);
+        if (lane == round) mine = win;
+        if (win != 0ull && best == win) {
+            best = 0ull;
+#pragma unroll
+            for (int i = 0; i < kMaxChunks; ++i) {
+                if (keys[i] == win) keys[i] = 0ull;
+                best = keys[i] > best ? keys[i] : best;
+            }
+        }
+    }
+    const int ncand = a.kk < a.V ? a.kk : a.V;
+    const float l = key_logit(mine);
+    const int id = key_id(mine);
+
+    if (a.T == 0.0) {  // greedy: candidates 0 and 1 of the exact order
+        const double l0 = (double)__shfl(l, 0, 64), l1 = (double)__shfl(l, 1, 64);
+        const int id0 = __shfl(id, 0, 64);
+        if (lane == 0) {
+            a.tokens[r] = id0;
+            if (a.gap) a.gap[r] = ncand > 1 ? l0 - l1 : __builtin_huge_val();
+        }
+        return;
+    }
+
+    // top-p: e_j = exp((l_j - l_0) / T), Z summed in candidate order; keep j
+    // while the mass before it is below top_p * Z.  Every lane runs the same
+    // sequential loop on the shuffled values, so all lanes agree.
+    const double m = (double)__shfl(l, 0, 64);
+    const double e = lane < ncand ? exp(((double)l - m) / a.T) : 0.0;
+    double Z = 0.0;
+    for (int jj = 0; jj < ncand; ++jj) Z += __shfl(e, jj, 64);
+    const double thr = a.top_p * Z;
+    int kept = 0;
+    double before = 0.0;
+    for (int jj = 0; jj < ncand; ++jj) {
+        if (jj > 0 && !(before < thr)) break;
+        kept = jj + 1;
+        before += __shfl(e, jj, 64);
+    }
+
+    // perturbed scores and the argmax (lower id on equal scores)
+    const long long pos = a.positions[r];
+    double z = -__builtin_huge_val();
+    if (lane < kept) z = (double)l / a.T + keyed_gumbel(a.seed, pos, id);
+    double bz = z;
+    int bid = lane < kept ? id : 0x7fffffff;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        const double oz = __shfl_xor(bz, off, 64);
+        const int oid = __shfl_xor(bid, off, 64);
+        if (oz > bz || (oz == bz && oid < bid)) {
+            bz = oz;
+            bid = oid;
+        }
+    }
+    // second best: the best score among the other kept candidates
+    double sz = (lane < kept && id != bid) ? z : -__builtin_huge_val();
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        const double oz = __shfl_xor(sz, off, 64);
+        sz = oz > sz ? oz : sz;
+    }
+    if (lane == 0) {
+        a.tokens[r] = bid;
+        if (a.gap) a.gap[r] = kept > 1 ? bz - sz : __builtin_huge_val();
+    }
+}
+
+// n_accept = leading i < D with draft[i] == sampled[i]; n_commit = min(a+1, R).
+__global__ __launch_bounds__(64) void accept_kernel(const int* __restrict__ sampled, int R,
+                                                    const int* __restrict__ draft, int D,
+                                                    int* __restrict__ n_accept,
+                                                    int* __restrict__ n_commit) {
+    const int i = threadIdx.x;
+    const bool mism = i < D && draft[i] != sampled[i];
+    const unsigned long long mask = __ballot(mism);
+    const int acc = mask ? (__ffsll((long long)mask) - 1) : D;
+    if (i == 0) {
+        *n_accept = acc;
+        *n_commit = acc + 1 < R ? acc + 1 : R;
+    }
+}
+
+static int sample_nchunk(int V) { return (V + kChunk - 1) / kChunk; }
+static int sample_kk(const ev_sampling& s, int V) {
+    const int k = s.temperature == 0.0 ? 2 : s.top_k;
+    return k < V ? k : V;
+}
+
+}  // namespace ev
+
+using namespace ev;
+
+extern "C" size_t keyed_sample_workspace(int32_t V) {
+    if (V <= 0) return 0;
+    return (size_t)EV_MAX_LANES * sample_nchunk(V) * EV_MAX_TOPK * sizeof(unsigned long long);
+}
+
+extern "C" int32_t keyed_sample(const float* logits, int32_t R, int32_t V, const int64_t* positions,
+                                ev_sampling s, int32_t* tokens, double* gap, void* ws,
+                                size_t ws_bytes, void* stream) {
+    clear_error();
+    const char* who = "keyed_sample";
+    if (R < 1 || R > EV_MAX_LANES) return fail(EV_EINVAL, "%s: R=%d outside 1..16", who, R);
+    if (V < 1) return fail(EV_EINVAL, "%s: V=%d", who, V);
+    if (V > kMaxChunks * kChunk) return fail(EV_EUNSUPPORTED, "%s: V=%d above %d", who, V, kMaxChunks * kChunk);
+    if (!logits || !positions || !tokens) return fail(EV_EINVAL, "%s: NULL pointer", who);
+    if (!aligned(logits, 4) || !aligned(positions, 8) || !aligned(tokens, 4) || (gap && !aligned(gap, 8)))
+        return fail(EV_EINVAL, "%s: misaligned pointer", who);
+    if (!(s.temperature >= 0.0) || !(s.temperature < __builtin_huge_val()))
+        return fail(EV_EINVAL, "%s: temperature must be finite and >= 0", who);
+    if (s.temperature > 0.0) {
+        if (s.top_k < 1) return fail(EV_EINVAL, "%s: top_k=%d", who, s.top_k);
+        if (s.top_k > EV_MAX_TOPK) return fail(EV_EUNSUPPORTED, "%s: top_k=%d above 64", who, s.top_k);
+        if (!(s.top_p > 0.0 && s.top_p <= 1.0)) return fail(EV_EINVAL, "%s: top_p outside (0,1]", who);
+    }
+    const size_t need = keyed_sample_workspace(V);
+    if (!ws || ws_bytes < need)
+        return fail(EV_EWORKSPACE, "%s: workspace needs %zu bytes, got %zu", who, need, ws ? ws_bytes : (size_t)0);
+    if (!aligned(ws, 8)) return fail(EV_EINVAL, "%s: workspace must be 8-byte aligned", who);
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    const int nchunk = sample_nchunk(V);
+    const int kk = sample_kk(s, V);
+    unsigned long long* cand = reinterpret_cast<unsigned long long*>(ws);
+    hipLaunchKernelGGL(topk_chunk_kernel, dim3(nchunk, R), dim3(kSThreads), 0, st, logits, V, kk,
+                       nchunk, cand);
+    int32_t rc = check_hip(hipGetLastError(), "topk_chunk launch");
+    if (rc) return rc;
+    SampleArgs a{cand, reinterpret_cast<const long long*>(positions), nchunk, kk, V,
+                 s.temperature, s.top_p, (unsigned long long)s.seed, tokens, gap};
+    hipLaunchKernelGGL(merge_sample_kernel, dim3(R), dim3(64), 0, st, a);
+    return check_hip(hipGetLastError(), "merge_sample launch");
+}
+
+extern "C" int32_t accept_prefix(const int32_t* sampled, int32_t R, const int32_t* draft, int32_t D,
+                                 int32_t* n_accept, int32_t* n_commit, void* stream) {
+    clear_error();
+    const char* who = "accept_prefix";
+    if (R < 1 || R > EV_MAX_LANES) return fail(EV_EINVAL, "%s: R=%d outside 1..16", who, R);
+    if (D < 0 || D > R) return fail(EV_EINVAL, "%s: D=%d outside 0..R", who, D);
+    if (!sampled || !n_accept || !n_commit || (D > 0 && !draft))
+        return fail(EV_EINVAL, "%s: NULL pointer", who);
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    hipLaunchKernelGGL(accept_kernel, dim3(1), dim3(64), 0, st, sampled, R, draft, D, n_accept,
+                       n_commit);
+    return check_hip(hipGetLastError(), "accept launch");
+}

@@ -1,0 +1,176 @@
+/*
+ * exactverify.h -- C ABI of libexactverify.so, the multi-row verify pass of
+ * exact ("byte-identical") drafted decoding on AMD Instinct MI355X (gfx950).
+ *
+ * What the method computes (sources, by page and part):
+ *   - TensorFold README (project page mirror), the exactness paragraph: the
+ *     token at position p is the argmax over the top-k/top-p candidates of
+ *     logit/T + g(seed, p, token), g Gumbel noise from a hash of seed, position
+ *     and token id; and a row of a multi-row verify pass gets the same bits as a
+ *     one-row step.  Options table: temperature 0 is greedy; --no-drafts (one
+ *     token a round) is the serial reference.
+ *   - "TensorFold: The engine that makes local LLMs 2-3x faster ...", section
+ *     "The differentiator: byte-exact drafted decoding": drafts are verified as
+ *     several rows ("lanes") of one forward pass; sampling is keyed.  FAQ: the
+ *     target keeps exactly the guessed tokens it would have chosen itself.
+ *   - 650 Group, "TensorFold: the contract is what it does not change": the same
+ *     two rules, restated.
+ *
+ * Conventions for every entry point
+ *   - Pointers marked (device) are device memory on the current HIP device;
+ *     (host) pointers are read before the call returns.  The caller allocates and
+ *     owns every buffer; the library never allocates in these calls.
+ *   - bf16 and fp16 values travel as their raw uint16_t bit patterns.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Calls enqueue work
+ *     and return without synchronising; outputs are valid once the stream has
+ *     reached that point.
+ *   - Return value: EV_OK, or a negative EV_E* code.  Arguments are validated
+ *     before anything is enqueued, so on error no output is written.
+ *     ev_last_error() then returns a message (thread-local).
+ *   - Row exactness: for any R, row r's outputs are bit-identical to those of a
+ *     call with R = 1 on row r alone.  Internal tiling, split counts and
+ *     workspace sizes are functions of (N, K, G) or V, never of R.
+ */
+#ifndef EXACTVERIFY_H
+#define EXACTVERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define EV_OK 0
+#define EV_EINVAL (-1)      /* bad pointer, size, alignment or parameter value */
+#define EV_EUNSUPPORTED (-2)/* a valid value this build does not handle     */
+#define EV_EHIP (-3)        /* the HIP runtime reported an error             */
+#define EV_EWORKSPACE (-4)  /* workspace pointer NULL or smaller than needed */
+
+#define EV_MAX_LANES 16     /* R, the rows of one verify pass, is 1..16     */
+#define EV_MAX_TOPK 64      /* top_k limit when sampling (T > 0)             */
+
+/* Message for the last error on this thread ("" if none). */
+const char* ev_last_error(void);
+
+/* Library version, major*10000 + minor*100 + patch. */
+int32_t ev_version(void);
+
+/* ------------------------------------------------------------------------- */
+/* W4 verify linear.                                                          */
+/*                                                                            */
+/* y[r][n] = sum_k x[r][k] * (s[n][k/G] * q[n][k] + b[n][k/G]),  r < R, n < N. */
+/* Four-bit weights in groups of 32 or 64 with an affine dequantisation (the  */
+/* "4-bit checkpoints" the blog's "The numbers" section and the README's      */
+/* checkpoint list name; the README gives groups of 64 and of 32).            */
+/*                                                                            */
+/*   x_bf16   (device) [R][K] bf16, 16-byte aligned.                          */
+/*   q        (device) [N][K/2] bytes; byte k/2 of row n holds q[n][k] in its */
+/*            low nibble when k is even, its high nibble when k is odd.       */
+/*            16-byte aligned.                                                */
+/*   scale_f16, bias_f16 (device) [N][K/G] fp16.                              */
+/*   y        (device) [R][N] fp32, written.                                  */
+/*   ws       (device) workspace of at least verify_linear_w4_workspace(K,N,G) */
+/*            bytes (may be NULL when that is 0); contents are scratch.        */
+/* Limits: 1 <= R <= 16; K > 0, K % G == 0, K % 32 == 0; N > 0; G in {32, 64}. */
+/* Errors: EV_EINVAL (NULL/misaligned pointer, R or K or N out of range),      */
+/* EV_EUNSUPPORTED (G not 32 or 64), EV_EWORKSPACE, EV_EHIP.                   */
+/* Reduction order: fixed per (n) by (N, K, G) -- never by R.                 */
+/* ------------------------------------------------------------------------- */
+size_t verify_linear_w4_workspace(int32_t K, int32_t N, int32_t G);
+int32_t verify_linear_w4(const uint16_t* x_bf16, int32_t R, int32_t K,
+                         const uint8_t* q, const uint16_t* scale_f16,
+                         const uint16_t* bias_f16, int32_t N, int32_t G, float* y,
+                         void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------- */
+/* SiLU-gated MLP verify slice (dense).                                       */
+/*                                                                            */
+/*   g = W_gate x, u = W_up x          (W4 linears H -> I, fp32 out)          */
+/*   h = bf16_rne(silu(g) * u),  silu(v) = v / (1 + e^-v)  (fp32)             */
+/*   y = W_down h                      (W4 linear I -> H, fp32 out)           */
+/* Each W4 linear is the one defined above.  Matrices use the layouts above:  */
+/* gate/up q [I][H/2], s/b [I][H/G]; down q [H][I/2], s/b [H][I/G].           */
+/*   h_bf16  (device, optional) [R][I] bf16: if non-NULL, h is also written.  */
+/* Limits as verify_linear_w4 for both shapes.                                */
+/* ------------------------------------------------------------------------- */
+size_t verify_mlp_w4_workspace(int32_t H, int32_t I, int32_t G);
+int32_t verify_mlp_w4(const uint16_t* x_bf16, int32_t R, int32_t H, int32_t I, int32_t G,
+                      const uint8_t* gate_q, const uint16_t* gate_s, const uint16_t* gate_b,
+                      const uint8_t* up_q, const uint16_t* up_s, const uint16_t* up_b,
+                      const uint8_t* down_q, const uint16_t* down_s, const uint16_t* down_b,
+                      float* y, uint16_t* h_bf16, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------- */
+/* Keyed sampler.                                                             */
+/*                                                                            */
+/* README exactness paragraph / 650 Group: token at position p = argmax over  */
+/* the top-k / top-p candidates of l/T + g(seed, p, id).  Readings used here: */
+/*   1. candidates: the top_k largest logits under (logit desc, id asc);      */
+/*   2. in fp64, e_j = exp((l_j - l_0)/T), Z = sum of e_j in candidate order; */
+/*      candidate j is kept while the mass of the candidates before it is     */
+/*      < top_p * Z (candidate 0 always kept);                                */
+/*   3. noise key: row = mix64(mix64(seed) + (p+1)*gamma),                    */
+/*      h = mix64(row + (id+1)*gamma)  (SplitMix64: gamma 0x9E3779B97F4A7C15, */
+/*      mix64 its output function); u = ((h >> 12) + 0.5) * 2^-52;           */
+/*      g = -log(-log(u)), all fp64;                                          */
+/*   4. z = (double)l / (double)T + g; token = argmax z, lower id on ties;    */
+/*      gap = best z - second z (+inf with one kept candidate).               */
+/* temperature == 0: greedy, token = argmax l (lower id on ties), gap = l(1) - */
+/* l(2) on the raw logits (+inf if V == 1); top_k / top_p are ignored.        */
+/*                                                                            */
+/*   logits     (device) [R][V] fp32, finite (non-finite values: undefined).  */
+/*   positions  (device) [R] int64, the absolute position p each row samples. */
+/*   tokens     (device) [R] int32, written.                                  */
+/*   gap        (device, optional) [R] fp64, written when non-NULL.           */
+/*   ws         (device) at least keyed_sample_workspace(V) bytes.            */
+/* Limits: 1 <= R <= 16; V >= 1; temperature >= 0 and finite; when            */
+/* temperature > 0: 1 <= top_k <= 64 and 0 < top_p <= 1.                      */
+/* Errors: EV_EINVAL, EV_EUNSUPPORTED (top_k > 64), EV_EWORKSPACE, EV_EHIP.   */
+/* ------------------------------------------------------------------------- */
+typedef struct {
+    double temperature; /* T; 0 selects greedy */
+    int32_t top_k;      /* 1..64 when T > 0   */
+    double top_p;       /* (0, 1] when T > 0  */
+    uint64_t seed;      /* key of the noise    */
+} ev_sampling;
+
+size_t keyed_sample_workspace(int32_t V);
+int32_t keyed_sample(const float* logits, int32_t R, int32_t V, const int64_t* positions,
+                     ev_sampling sampling, int32_t* tokens, double* gap,
+                     void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------- */
+/* Accept prefix.                                                             */
+/*                                                                            */
+/* A draft is accepted exactly when it equals the token serial decoding       */
+/* samples at its position (README exactness paragraph; blog FAQ).  Row i's   */
+/* sample is compared with draft i:                                           */
+/*   n_accept = number of leading i < D with draft[i] == sampled[i];          */
+/*   n_commit = min(n_accept + 1, R)   (the accepted drafts' samples plus the */
+/*              sample of the first row whose draft differs).                 */
+/*   sampled (device) [R] int32; draft (device) [D] int32 (may be NULL if     */
+/*   D == 0); n_accept, n_commit (device) [1] int32, written.                 */
+/* Limits: 1 <= R <= 16, 0 <= D <= R.  Errors: EV_EINVAL, EV_EHIP.            */
+/* ------------------------------------------------------------------------- */
+int32_t accept_prefix(const int32_t* sampled, int32_t R, const int32_t* draft, int32_t D,
+                      int32_t* n_accept, int32_t* n_commit, void* stream);
+
+/* ------------------------------------------------------------------------- */
+/* Measurement hook for the W4 verify kernel (every entry point that streams  */
+/* W4 weights launches it).  ev_w4_timing(1) makes each later launch record a */
+/* HIP event before and after it on its own stream, together with the        */
+/* launch's algorithmic bytes: nmat * (N*K/2 + 4*N*K/G + 2*R*K + 4*R*N).      */
+/* ev_w4_timing_read waits for the recorded events, returns the number of     */
+/* launches, their summed durations (ms) and summed algorithmic bytes, and    */
+/* forgets them.  Off by default; the events themselves are created here.    */
+/* Errors: EV_EHIP.                                                           */
+/* ------------------------------------------------------------------------- */
+int32_t ev_w4_timing(int32_t enable);
+int32_t ev_w4_timing_read(int64_t* launches, double* total_ms, double* total_bytes);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EXACTVERIFY_H */

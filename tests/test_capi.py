@@ -1,0 +1,100 @@
+"""C-ABI contract checks that need no GPU: the library loads, exports every
+function include/exactverify.h declares, and rejects bad arguments with the
+documented codes before anything is launched (so these run anywhere)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+import exact_speculative_decoding_amd as ev
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+P = C.c_void_p(0x10000)  # never dereferenced: every call below fails validation
+
+
+def _declared():
+    names = set()
+    for h in os.listdir(os.path.join(ROOT, "include")):
+        if not h.endswith(".h"):
+            continue
+        src = open(os.path.join(ROOT, "include", h)).read()
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        for m in re.finditer(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([a-z_][a-z0-9_]*)\s*\(",
+                             src, flags=re.M):
+            names.add(m.group(1))
+    return names
+
+
+def test_every_declared_function_is_exported():
+    L = ev.lib()
+    declared = _declared()
+    assert {"verify_linear_w4", "keyed_sample", "accept_prefix"} <= declared
+    for name in declared:
+        assert hasattr(L, name), name
+    assert set(ev.exported_symbols()) >= declared
+
+
+def test_workspace_sizes_do_not_depend_on_rows():
+    # the workspace functions take no R at all; check they are stable and sane
+    assert ev.verify_linear_w4_workspace(256, 512, 64) >= 0
+    w = ev.verify_linear_w4_workspace(17408, 5120, 64)
+    assert w % (16 * 5120 * 4) == 0
+    assert ev.keyed_sample_workspace(151936) == 16 * 19 * 64 * 8
+    assert ev.verify_mlp_w4_workspace(5120, 17408, 64) > 0
+
+
+def _lin(**kw):
+    a = dict(x=P, R=4, K=256, q=P, s=P, b=P, N=512, G=64, y=P, ws=None, nb=0)
+    a.update(kw)
+    L = ev.lib()
+    return L.verify_linear_w4(a["x"], a["R"], a["K"], a["q"], a["s"], a["b"], a["N"], a["G"],
+                              a["y"], a["ws"], a["nb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(R=0), ev.EV_EINVAL), (dict(R=17), ev.EV_EINVAL), (dict(K=0), ev.EV_EINVAL),
+    (dict(N=0), ev.EV_EINVAL), (dict(K=100), ev.EV_EINVAL), (dict(K=96, G=64), ev.EV_EINVAL),
+    (dict(G=128), ev.EV_EUNSUPPORTED), (dict(G=16), ev.EV_EUNSUPPORTED),
+    (dict(x=None), ev.EV_EINVAL), (dict(q=None), ev.EV_EINVAL), (dict(y=None), ev.EV_EINVAL),
+    (dict(x=C.c_void_p(0x10002)), ev.EV_EINVAL), (dict(q=C.c_void_p(0x10008)), ev.EV_EINVAL),
+    (dict(K=17408, N=5120), ev.EV_EWORKSPACE),
+])
+def test_linear_rejects_bad_arguments(kw, code):
+    if kw.get("K") == 17408:
+        assert ev.verify_linear_w4_workspace(17408, 5120, 64) > 0
+    assert _lin(**kw) == code
+    assert ev.lib().ev_last_error()
+
+
+def _samp(R=2, V=512, T=0.7, k=20, p=0.95, ws=P, nb=1 << 20, logits=P, pos=P, tok=P):
+    sp = ev.Sampling(T, k, p, 42)
+    return ev.lib().keyed_sample(logits, R, V, pos, sp, tok, None, ws, nb, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(R=0), ev.EV_EINVAL), (dict(R=17), ev.EV_EINVAL), (dict(V=0), ev.EV_EINVAL),
+    (dict(V=262145), ev.EV_EUNSUPPORTED), (dict(T=-1.0), ev.EV_EINVAL),
+    (dict(T=float("inf")), ev.EV_EINVAL), (dict(T=float("nan")), ev.EV_EINVAL),
+    (dict(k=0), ev.EV_EINVAL), (dict(k=65), ev.EV_EUNSUPPORTED), (dict(p=0.0), ev.EV_EINVAL),
+    (dict(p=1.5), ev.EV_EINVAL), (dict(ws=None), ev.EV_EWORKSPACE), (dict(nb=8), ev.EV_EWORKSPACE),
+    (dict(logits=None), ev.EV_EINVAL), (dict(tok=None), ev.EV_EINVAL),
+])
+def test_sampler_rejects_bad_arguments(kw, code):
+    assert _samp(**kw) == code
+
+
+@pytest.mark.parametrize("R,D,draft,code", [(0, 0, P, ev.EV_EINVAL), (17, 0, P, ev.EV_EINVAL),
+                                            (4, 5, P, ev.EV_EINVAL), (4, -1, P, ev.EV_EINVAL),
+                                            (4, 2, None, ev.EV_EINVAL)])
+def test_accept_rejects_bad_arguments(R, D, draft, code):
+    assert ev.lib().accept_prefix(P, R, draft, D, P, P, None) == code
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    x = torch.zeros(2, 256, dtype=torch.bfloat16)
+    q = torch.zeros(512, 128, dtype=torch.uint8)
+    s = torch.zeros(512, 4, dtype=torch.float16)
+    with pytest.raises((ValueError, RuntimeError)):
+        ev.verify_linear_w4(x, q, s, s, 64, y=torch.zeros(2, 512))

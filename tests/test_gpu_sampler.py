@@ -1,0 +1,88 @@
+"""GPU parity of keyed_sample and accept_prefix against the oracle.
+
+The same seeded fp32 logits go to both sides, so the sampled tokens must be
+identical; the only allowed differences are rows whose decision sits at the
+last bits of fp64 (a top-two gap below 1e-12, or a top-p cut within 1e-9 Z of
+the threshold), which are counted.  Gaps must agree to fp64 rounding.
+Rows of an R-row call are bit-identical to single-row calls.
+"""
+import numpy as np
+import pytest
+import torch
+
+import exact_speculative_decoding_amd as ev
+import oracle
+import synthetic as syn
+from helpers import dev, host
+
+pytestmark = pytest.mark.gpu
+
+CASES = [  # V, T, top_k, top_p
+    (1, 0.7, 20, 0.95), (2, 0.7, 20, 0.95), (7, 1.0, 5, 0.9), (512, 0.8, 20, 0.95),
+    (512, 0.0, 20, 0.95), (8192, 0.7, 64, 1.0), (8193, 1.0, 1, 0.5), (32768, 0.7, 20, 0.95),
+    (32768, 0.0, 1, 1.0), (151936, 0.7, 20, 0.95), (151936, 1.0, 20, 0.95),
+    (151936, 0.0, 20, 0.95), (262144, 2.0, 64, 0.3), (1000, 0.05, 10, 0.99),
+]
+
+
+def _compare(logits, pos, T, k, p, seed):
+    R = logits.shape[0]
+    ld, pd = dev(logits), dev(pos)
+    gap = torch.empty(R, dtype=torch.float64, device="cuda")
+    tok = host(ev.keyed_sample(ld, pd, T, k, p, seed, gap=gap))
+    gap = host(gap)
+    rt, rg, rk, re = oracle.sample_rows(logits, pos, T, k, p, seed)
+    edge = (re != 0) | (rg < 1e-12)
+    assert np.all((tok == rt) | edge), (tok, rt)
+    both_inf = np.isinf(gap) & np.isinf(rg)
+    fin = ~both_inf & ~edge
+    assert np.all(np.abs(gap[fin] - rg[fin]) <= 1e-12 * np.maximum(1.0, np.abs(rg[fin])))
+    return tok, gap, int(edge.sum())
+
+
+@pytest.mark.parametrize("V,T,k,p", CASES)
+def test_sampler_matches_oracle_and_rows_are_exact(V, T, k, p):
+    g = np.random.default_rng(V + int(T * 100) + k)
+    R = 16
+    logits = syn.logits(g, R, V, scale=3.0)
+    pos = g.integers(0, 1 << 40, R).astype(np.int64)
+    seed = int(g.integers(0, 1 << 63))
+    tok, gap, _ = _compare(logits, pos, T, k, p, seed)
+    # row exactness: each row alone gives the same token and gap bits
+    for r in (0, 5, 15):
+        t1 = torch.empty(1, dtype=torch.float64, device="cuda")
+        o = host(ev.keyed_sample(dev(logits[r:r + 1]), dev(pos[r:r + 1]), T, k, p, seed, gap=t1))
+        assert o[0] == tok[r] and host(t1)[0].tobytes() == gap[r].tobytes()
+
+
+def test_sampler_ties_and_many_seeds():
+    g = np.random.default_rng(77)
+    V = 700
+    # integer logits: many exact ties, so the (logit desc, id asc) order decides
+    logits = g.integers(-3, 4, (16, V)).astype(np.float32)
+    pos = np.arange(16, dtype=np.int64)
+    for seed in range(40):
+        for T, k, p in ((0.0, 20, 1.0), (1.0, 20, 0.95), (0.5, 64, 0.7)):
+            _compare(logits, pos, T, k, p, seed)
+
+
+def test_sampler_positions_and_seeds_sweep():
+    g = np.random.default_rng(78)
+    V = 4096
+    logits = syn.logits(g, 16, V, scale=2.0)
+    for trial in range(30):
+        pos = g.integers(0, 1 << 20, 16).astype(np.int64)
+        seed = int(g.integers(0, 1 << 63))
+        _compare(logits, pos, 0.7, 20, 0.95, seed)
+
+
+def test_accept_matches_oracle():
+    g = np.random.default_rng(9)
+    for trial in range(200):
+        R = int(g.integers(1, 17))
+        D = int(g.integers(0, R + 1))
+        sampled = g.integers(0, 4, R).astype(np.int32)
+        draft = np.where(g.random(D) < 0.8, sampled[:D], g.integers(0, 4, D)).astype(np.int32)
+        a, n = ev.accept_prefix(dev(sampled), dev(draft) if D else None)
+        ra, rn = oracle.accept(sampled, draft)
+        assert (int(host(a)[0]), int(host(n)[0])) == (ra, rn)
