@@ -25,6 +25,7 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
     flags = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
              "-I", os.path.join(ROOT, "include"), "-I", os.path.join(HERE, "csrc"),
+             "-mllvm", "-amdgpu-mfma-vgpr-form",
              "-Wall", "-Wno-unused-function"]
     procs, objs = [], []
     for src in sources():

@@ -9,22 +9,25 @@
 // Row exactness by construction: the R rows are always padded to the 16 rows
 // of one bf16 MFMA tile, so R = 1 and R = 16 execute the same instruction
 // stream; an MFMA output element depends only on its own A row and B column;
-// the split of K over workgroups, and therefore every reduction order, is a
+// the split of K over waves, and therefore every reduction order, is a
 // function of (N, K, G) only.
 //
-// Kernel shape (per workgroup of 4 waves):
-//   * 128 output columns (each wave: two 16-column MFMA tiles) over one K-split
-//     of up to 14 chunks of 128;
-//   * the split's activations for all 16 rows sit in LDS, each 8-element group
-//     reordered [0,4,1,5,2,6,3,7] to match the nibble decode below;
-//   * each lane streams 16 B of packed nibbles per tile per chunk (one 64 B run
-//     per row per wave load), a 4x4 dword transpose across the four 16-lane
-//     rows (v_permlane32_swap / v_permlane16_swap) turns them into MFMA B
-//     fragments;
-//   * nibbles decode exactly into bf16 as 16 + q (bits 0x4180 | q << 3: a shift
-//     and an and-or per pair); the offset is removed per group with the group
-//     sum of x, so y = sum_g s_g * (acc_g - 16 * xs_g) + b_g * xs_g;
-//   * partial sums of K-splits go to a workspace [S][16][N] and are added in
+// Kernel shape: every wave is an independent work item (no LDS, no barriers):
+// kNT 16-column MFMA tiles over one K-split of `cps` chunks of 128.
+//   * A operand = the 16 activation rows (rows >= R read as zero through the
+//     buffer range check), loaded per 32-k step straight from L2, each 8-element
+//     group reordered [0,4,1,5,2,6,3,7] to match the nibble decode;
+//   * B operand = 16 columns of packed nibbles: each lane streams 16 B of one
+//     row per tile per chunk (a wave load covers 16 rows x 64 B), and a 4x4
+//     dword transpose across the four 16-lane rows (v_permlane32_swap /
+//     v_permlane16_swap) turns them into per-step fragments;
+//   * nibbles decode exactly into bf16 as 16 + q (0x4180 | q << 3: a shift and
+//     an and-or per pair); one more MFMA against an all-ones B gives the group
+//     sum xs of every row, and the fold is p += s * acc + (b - 16 s) * xs into
+//     a per-chunk partial p that is added to y once per chunk;
+//   * a ring of kPD chunks of loads is kept in flight per wave; all loads are
+//     buffer loads, so out-of-range rows/columns read zero without branches;
+//   * K-split partial sums go to a workspace [S][16][N] and are added in
 //     ascending split order by a second kernel (fused with SiLU * up for the
 //     MLP gate/up pair).
 #include <mutex>
@@ -32,41 +35,51 @@
 
 #include "ev_internal.h"
 
+#ifndef EV_W4_NT
+#define EV_W4_NT 4  // 16-column tiles per wave
+#endif
+#ifndef EV_W4_PD
+#define EV_W4_PD 2  // chunks of loads in flight per wave
+#endif
+#ifndef EV_W4_TARGET_WAVES
+#define EV_W4_TARGET_WAVES 2048
+#endif
+#ifndef EV_W4_MIN_CPS
+#define EV_W4_MIN_CPS 8  // at least this many chunks per K-split when K allows
+#endif
+
 namespace ev {
 
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
-constexpr int kNT = 2;                  // 16-column tiles per wave
-constexpr int kBN = kWaves * kNT * 16;  // 128 columns per workgroup
-constexpr int kKC = 128;                // k per chunk (4 MFMA steps of 32)
-constexpr int kMaxCps = 14;             // chunks per split: LDS slab <= 1792 k
-constexpr int kXPad = 8;                // bf16 pad per LDS row (bank skew)
-constexpr int kTargetBlocks = 512;      // aim: >= 2 workgroups per CU
+constexpr int kThreads = 256;  // 4 independent waves per workgroup
+constexpr int kNT = EV_W4_NT;
+constexpr int kPD = EV_W4_PD;
+constexpr int kWaveCols = 16 * kNT;
+constexpr int kKC = 128;  // k per chunk (4 MFMA steps of 32)
+constexpr uint32_t kOOB = 0x80000000u;  // offset beyond every buffer: reads 0
 
 struct W4Plan {
     int S;        // K-splits
     int cps;      // chunks per split
     int nchunks;  // ceil(K / 128)
+    int ncg;      // column groups of kWaveCols
+    long items;   // waves = nmat * S * ncg
 };
 
-// Split plan from the column count of the launch and K only (never R).
-static W4Plan plan_w4(long ncols, int K) {
+// Split plan from (N, K) and the number of matrices of the launch, never R.
+static W4Plan plan_w4(int N, int K, int nmat) {
     W4Plan p;
     p.nchunks = (K + kKC - 1) / kKC;
-    long ncb = (ncols + kBN - 1) / kBN;
-    long S = (kTargetBlocks + ncb - 1) / ncb;
+    p.ncg = (N + kWaveCols - 1) / kWaveCols;
+    const long base = (long)p.ncg * nmat;
+    long S = (EV_W4_TARGET_WAVES + base - 1) / base;
+    long smax = p.nchunks / EV_W4_MIN_CPS;
+    if (smax < 1) smax = 1;
+    if (S > smax) S = smax;
     if (S < 1) S = 1;
-    long smin = (p.nchunks + kMaxCps - 1) / kMaxCps;
-    if (S < smin) S = smin;
-    if (S > p.nchunks) S = p.nchunks;
     p.cps = (int)((p.nchunks + S - 1) / S);
     p.S = (p.nchunks + p.cps - 1) / p.cps;
+    p.items = base * p.S;
     return p;
-}
-
-static size_t w4_lds_bytes(const W4Plan& p, int G) {
-    size_t kb = (size_t)p.cps * kKC;
-    return 16 * (kb + kXPad) * sizeof(uint16_t) + (kb / G) * 16 * sizeof(float);
 }
 
 struct W4Mat {
@@ -77,25 +90,53 @@ struct W4Mat {
 };
 
 struct W4Args {
-    W4Mat m[2];  // blockIdx.z selects the matrix (gate/up share one launch)
+    W4Mat m[2];  // the item's matrix index picks one (gate/up share one launch)
     const uint16_t* x;
     int R, K, N;
-    int nchunks, cps;
+    int nchunks, cps, S, ncg;
+    long items;
     long split_stride;  // floats between consecutive splits' outputs
+    // nibble-decode constants, passed as arguments so that they sit in
+    // registers (gfx9 VOP3 encodings cannot carry 32-bit literals)
+    uint32_t dmask, doff;
 };
 
-__device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+// voff: per-lane byte offset; soff: wave-uniform byte offset (scalar register)
+__device__ __forceinline__ u32x4 bload128(rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+__device__ __forceinline__ uint32_t bload32(rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+}
+__device__ __forceinline__ uint16_t bload16(rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
+}
 
 // Eight nibbles q0..q7 (q_i in bits 4i..4i+3) -> four bf16 pairs holding
 // 16 + q in the order (q0,q4) (q1,q5) (q2,q6) (q3,q7).  Exact.
-__device__ __forceinline__ u32x4 decode_nibbles(uint32_t d) {
-    const uint32_t m = 0x00780078u, off = 0x41804180u;
+__device__ __forceinline__ u32x4 decode_nibbles(uint32_t d, uint32_t m, uint32_t off) {
     u32x4 r;
     r[0] = ((d << 3) & m) | off;
     r[1] = ((d >> 1) & m) | off;
     r[2] = ((d >> 5) & m) | off;
     r[3] = ((d >> 9) & m) | off;
     return r;
+}
+
+// Eight bf16 x0..x7 (natural order) -> (x0,x4) (x1,x5) (x2,x6) (x3,x7), one
+// byte permute per output dword.
+__device__ __forceinline__ u32x4 reorder_x(u32x4 v) {
+    u32x4 o;
+    o[0] = __builtin_amdgcn_perm(v[2], v[0], 0x05040100u);
+    o[1] = __builtin_amdgcn_perm(v[2], v[0], 0x07060302u);
+    o[2] = __builtin_amdgcn_perm(v[3], v[1], 0x05040100u);
+    o[3] = __builtin_amdgcn_perm(v[3], v[1], 0x07060302u);
+    return o;
 }
 
 // 4x4 transpose of dwords across the four 16-lane rows of a wave: afterwards
@@ -120,150 +161,176 @@ __device__ __forceinline__ void transpose_rows(u32x4& v) {
     v[3] = d3;
 }
 
-template <int G>
+__device__ __forceinline__ float half_lo(uint32_t w) { return f16_to_f32((uint16_t)(w & 0xffffu)); }
+__device__ __forceinline__ float half_hi(uint32_t w) { return f16_to_f32((uint16_t)(w >> 16)); }
+
+// ALIGNED: K % 128 == 0 -- every chunk is whole, and a chunk's GPC scales (or
+// biases) of one row are one aligned 4 B (G = 64) or 8 B (G = 32) word.
+template <int G, bool ALIGNED>
 __global__ __launch_bounds__(kThreads) void w4_verify_kernel(W4Args a) {
-    extern __shared__ __align__(16) unsigned char smem[];
-    constexpr int GPC = kKC / G;  // groups per chunk
-    const W4Mat mat = a.m[blockIdx.z];
-    const int split = blockIdx.y;
+    constexpr int GPC = kKC / G;        // groups per chunk
+    constexpr int SBW = ALIGNED ? GPC / 2 : GPC;  // s/b words per chunk (b32 or b16)
+    const int lane = threadIdx.x & 63;
+    // wave-uniform work item (readfirstlane keeps it, the matrix and the buffer
+    // descriptors in scalar registers)
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const long item = (long)blockIdx.x * (kThreads / 64) + wave;
+    if (item >= a.items) return;  // whole wave
+    const int ln = lane & 15, j = lane >> 4;
+    const int cg = (int)(item % a.ncg);
+    const long rest = item / a.ncg;
+    const int split = (int)(rest % a.S);
+    const int mi = (int)(rest / a.S);
+    const W4Mat mat = a.m[mi];
     const int c0 = split * a.cps;
     const int c1 = min(a.nchunks, c0 + a.cps);
-    const int k0 = c0 * kKC;
-    const int k1 = min(a.K, c1 * kKC);
-    const int kb = k1 - k0;
-    const int xstride = a.cps * kKC + kXPad;  // LDS row stride (bf16 elements)
-    uint16_t* xl = reinterpret_cast<uint16_t*>(smem);
-    float* xsl = reinterpret_cast<float*>(smem + (size_t)16 * xstride * sizeof(uint16_t));
+    const int K = a.K, N = a.N;
+    const uint32_t Kh = (uint32_t)K >> 1;
+    const uint32_t KG = (uint32_t)(K / G);
 
-    // 1. activations of this split -> LDS (rows >= R are zero)
-    const int n8 = kb >> 3;
-    for (int idx = threadIdx.x; idx < 16 * n8; idx += kThreads) {
-        const int r = idx / n8, c = idx - r * n8;
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (r < a.R) v = ld16(a.x + (size_t)r * a.K + k0 + c * 8);
-        u32x4 o;
-        o[0] = (v[0] & 0xffffu) | (v[2] << 16);
-        o[1] = (v[0] >> 16) | (v[2] & 0xffff0000u);
-        o[2] = (v[1] & 0xffffu) | (v[3] << 16);
-        o[3] = (v[1] >> 16) | (v[3] & 0xffff0000u);
-        *reinterpret_cast<u32x4*>(xl + r * xstride + c * 8) = o;
-    }
-    __syncthreads();
+    const rsrc_t rq = make_rsrc(mat.q, (uint32_t)((size_t)N * Kh));
+    const rsrc_t rs = make_rsrc(mat.s, (uint32_t)((size_t)N * KG * 2));
+    const rsrc_t rb = make_rsrc(mat.b, (uint32_t)((size_t)N * KG * 2));
+    const rsrc_t rx = make_rsrc(a.x, (uint32_t)((size_t)a.R * K * 2));
 
-    // 2. group sums of x, one (row, group) per thread, fixed sequential order
-    const int ngl = kb / G;
-    for (int idx = threadIdx.x; idx < 16 * ngl; idx += kThreads) {
-        const int r = idx & 15, g = idx >> 4;
-        const uint16_t* p = xl + r * xstride + g * G;
-        float sum = 0.f;
-#pragma unroll 8
-        for (int i = 0; i < G; ++i) sum += bf16_to_f32(p[i]);
-        xsl[g * 16 + r] = sum;
-    }
-    __syncthreads();
-
-    // 3. stream the weights
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int ln = lane & 15, j = lane >> 4;
-    const size_t Kh = (size_t)(a.K >> 1);
-    const size_t KG = (size_t)(a.K / G);
-    const uint8_t* qrow[kNT];
-    const uint16_t* srow[kNT];
-    const uint16_t* brow[kNT];
     int ncol[kNT];
+    uint32_t qoff[kNT], soff[kNT];
 #pragma unroll
     for (int t = 0; t < kNT; ++t) {
-        ncol[t] = blockIdx.x * kBN + wave * (kNT * 16) + t * 16 + ln;
-        const size_t nr = (size_t)min(ncol[t], a.N - 1);
-        qrow[t] = mat.q + nr * Kh;
-        srow[t] = mat.s + nr * KG;
-        brow[t] = mat.b + nr * KG;
+        ncol[t] = cg * kWaveCols + t * 16 + ln;
+        const bool ok = ncol[t] < N;
+        qoff[t] = ok ? (uint32_t)ncol[t] * Kh + 16u * j : kOOB;
+        soff[t] = ok ? (uint32_t)ncol[t] * KG * 2u : kOOB;
     }
+    const uint32_t xoff = ln < a.R ? ((uint32_t)ln * K + 8u * j) * 2u : kOOB;
+    // the mask stays scalar, the or-constant goes to a vector register: gfx9
+    // VALU ops read at most one scalar operand, and this lets each decoded pair
+    // be one v_and_or_b32
+    const uint32_t dm = a.dmask;
+    uint32_t doff;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(doff) : "s"(a.doff));
 
+    // register ring of kPD chunks
+    u32x4 qr[kPD][kNT];
+    uint32_t sr[kPD][kNT][SBW], br[kPD][kNT][SBW];
+    u32x4 xr[kPD][4];
+
+    // Loads of chunk c into ring slot `slot`.  The chunk's offset is a scalar
+    // (soffset); chunks at or past c1 use an out-of-range scalar offset
+    // (zeros, no memory traffic), so every slot is written on every path and
+    // the ring never has to be copied.
+    auto fetch = [&](int c, int slot) {
+        const bool live = c < c1;
+        const uint32_t kc = (uint32_t)c * kKC;
+        const uint32_t sq = live ? (kc >> 1) : kOOB;
+        const uint32_t ss = live ? (kc / G) * 2u : kOOB;
+        const uint32_t sx = live ? kc * 2u : kOOB;
+#pragma unroll
+        for (int t = 0; t < kNT; ++t) {
+            uint32_t vq = qoff[t];
+            if (!ALIGNED && kc + 32u * j >= (uint32_t)K) vq = kOOB;
+            qr[slot][t] = bload128(rq, vq, sq);
+#pragma unroll
+            for (int w = 0; w < SBW; ++w) {
+                if (ALIGNED) {
+                    sr[slot][t][w] = bload32(rs, soff[t] + 4u * w, ss);
+                    br[slot][t][w] = bload32(rb, soff[t] + 4u * w, ss);
+                } else {
+                    uint32_t so = soff[t] + 2u * w;
+                    if (kc + (uint32_t)(w * G) >= (uint32_t)K) so = kOOB;
+                    sr[slot][t][w] = bload16(rs, so, ss);
+                    br[slot][t][w] = bload16(rb, so, ss);
+                }
+            }
+        }
+#pragma unroll
+        for (int st = 0; st < 4; ++st) xr[slot][st] = bload128(rx, xoff + 64u * st, sx);
+    };
+
+    const u32x4 ones = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
     f32x4 y[kNT];
 #pragma unroll
     for (int t = 0; t < kNT; ++t) y[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // prefetch registers for the next chunk
-    u32x4 qn[kNT];
-    uint16_t sn[kNT][GPC], bn[kNT][GPC];
-    auto fetch = [&](int c) {
-        const int kc = c * kKC;
-        const int nst = min(4, (a.K - kc) >> 5);
-        const int g0 = kc / G;
+    // One chunk: per 32-k step, one MFMA for the group sums of x and one per
+    // tile; per group, p += s * acc + (b - 16 s) * xs into a chunk partial p,
+    // which is added to y once per chunk.
+    auto compute = [&](int c, int slot) {
+        const int nst = ALIGNED ? 4 : min(4, (K - c * kKC) >> 5);
 #pragma unroll
-        for (int t = 0; t < kNT; ++t) {
-            qn[t] = (j < nst) ? ld16(qrow[t] + (kc >> 1) + 16 * j) : u32x4{0u, 0u, 0u, 0u};
+        for (int t = 0; t < kNT; ++t) transpose_rows(qr[slot][t]);
+        f32x4 acc[kNT], part[kNT], xs = {0.f, 0.f, 0.f, 0.f};
+        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int g = 0; g < GPC; ++g) {
-                const bool ok = g * G < (a.K - kc);
-                sn[t][g] = ok ? srow[t][g0 + g] : (uint16_t)0;
-                bn[t][g] = ok ? brow[t][g0 + g] : (uint16_t)0;
-            }
-        }
-    };
-
-    fetch(c0);
-    for (int c = c0; c < c1; ++c) {
-        u32x4 qv[kNT];
-        float sv[kNT][GPC], bv[kNT][GPC];
-#pragma unroll
-        for (int t = 0; t < kNT; ++t) {
-            qv[t] = qn[t];
-#pragma unroll
-            for (int g = 0; g < GPC; ++g) {
-                sv[t][g] = f16_to_f32(sn[t][g]);
-                bv[t][g] = f16_to_f32(bn[t][g]);
-            }
-        }
-        if (c + 1 < c1) fetch(c + 1);
-
-        const int kc = c * kKC;
-        const int nst = min(4, (a.K - kc) >> 5);
-#pragma unroll
-        for (int t = 0; t < kNT; ++t) transpose_rows(qv[t]);
-
-        f32x4 acc[kNT];
+        for (int t = 0; t < kNT; ++t) part[t] = zero;
 #pragma unroll
         for (int st = 0; st < 4; ++st) {
-            if (st < nst) {
-                const u32x4 xa = ld16(xl + ln * xstride + (kc - k0) + 32 * st + 8 * j);
-                const bf16x8 A = __builtin_bit_cast(bf16x8, xa);
+            if (ALIGNED || st < nst) {
+                const bf16x8 A = __builtin_bit_cast(bf16x8, reorder_x(xr[slot][st]));
                 const bool first = (G == 32) || ((st & 1) == 0);
+                xs = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, __builtin_bit_cast(bf16x8, ones),
+                                                            first ? zero : xs, 0, 0, 0);
 #pragma unroll
                 for (int t = 0; t < kNT; ++t) {
-                    const bf16x8 B = __builtin_bit_cast(bf16x8, decode_nibbles(qv[t][st]));
-                    const f32x4 cin = first ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[t];
-                    acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, cin, 0, 0, 0);
+                    const bf16x8 B =
+                        __builtin_bit_cast(bf16x8, decode_nibbles(qr[slot][t][st], dm, doff));
+                    acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, first ? zero : acc[t], 0, 0, 0);
                 }
                 const bool last = (G == 32) || ((st & 1) == 1);
                 if (last) {
                     const int gc = (32 * st) / G;  // group within the chunk
-                    const int gl = (kc - k0) / G + gc;
-                    const f32x4 xs4 = *reinterpret_cast<const f32x4*>(xsl + gl * 16 + 4 * j);
 #pragma unroll
                     for (int t = 0; t < kNT; ++t) {
+                        float sv, bv;
+                        if (ALIGNED) {
+                            const uint32_t sw = sr[slot][t][gc >> 1], bw = br[slot][t][gc >> 1];
+                            sv = (gc & 1) ? half_hi(sw) : half_lo(sw);
+                            bv = (gc & 1) ? half_hi(bw) : half_lo(bw);
+                        } else {
+                            sv = f16_to_f32((uint16_t)sr[slot][t][gc]);
+                            bv = f16_to_f32((uint16_t)br[slot][t][gc]);
+                        }
+                        const float bp = fmaf(-16.f, sv, bv);  // removes the decode offset
 #pragma unroll
                         for (int i = 0; i < 4; ++i) {
-                            const float d = fmaf(-16.f, xs4[i], acc[t][i]);
-                            y[t][i] = fmaf(sv[t][gc], d, y[t][i]);
-                            y[t][i] = fmaf(bv[t][gc], xs4[i], y[t][i]);
+                            part[t][i] = fmaf(sv, acc[t][i], part[t][i]);
+                            part[t][i] = fmaf(bp, xs[i], part[t][i]);
                         }
                     }
                 }
             }
         }
-    }
+#pragma unroll
+        for (int t = 0; t < kNT; ++t) y[t] += part[t];
+    };
 
-    // 4. rows r = 4j + i of columns ncol[t]
+    // sched_barrier keeps each refill where it is written, so the loads of the
+    // other ring slots stay in flight across the compute of this one.
+#pragma unroll
+    for (int p = 0; p < kPD; ++p) {
+        __builtin_amdgcn_sched_barrier(0);
+        fetch(c0 + p, p);
+    }
+    for (int cb = c0; cb < c1; cb += kPD) {
+#pragma unroll
+        for (int p = 0; p < kPD; ++p) {
+            __builtin_amdgcn_sched_barrier(0);
+            compute(cb + p, p);
+            __builtin_amdgcn_sched_barrier(0);
+            fetch(cb + p + kPD, p);
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // rows r = 4j + i of columns ncol[t]
     float* out = mat.out + (size_t)split * a.split_stride;
 #pragma unroll
     for (int t = 0; t < kNT; ++t) {
-        if (ncol[t] < a.N) {
+        if (ncol[t] < N) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = 4 * j + i;
-                if (r < a.R) out[(size_t)r * a.N + ncol[t]] = y[t][i];
+                if (r < a.R) out[(size_t)r * N + ncol[t]] = y[t][i];
             }
         }
     }
@@ -316,10 +383,16 @@ static double w4_algo_bytes(int nmat, int R, int K, int N, int G) {
     return nmat * (w + 2.0 * R * K + 4.0 * R * N);
 }
 
-static int32_t launch_w4(const W4Args& args, int nmat, const W4Plan& p, int G, long ncols,
-                         hipStream_t st) {
-    dim3 grid((unsigned)((ncols + kBN - 1) / kBN), (unsigned)p.S, (unsigned)nmat);
-    const size_t lds = w4_lds_bytes(p, G);
+static int32_t launch_w4(W4Args args, int nmat, const W4Plan& p, int G, hipStream_t st) {
+    args.nchunks = p.nchunks;
+    args.cps = p.cps;
+    args.S = p.S;
+    args.ncg = p.ncg;
+    args.items = p.items;
+    args.dmask = 0x00780078u;
+    args.doff = 0x41804180u;
+    const unsigned blocks = (unsigned)((p.items + 3) / 4);
+    const bool aligned_k = args.K % kKC == 0;
     hipEvent_t ea = nullptr, eb = nullptr;
     bool timed;
     {
@@ -329,15 +402,22 @@ static int32_t launch_w4(const W4Args& args, int nmat, const W4Plan& p, int G, l
     if (timed) {
         if (hipEventCreate(&ea) != hipSuccess || hipEventCreate(&eb) != hipSuccess)
             return fail(EV_EHIP, "w4 timing: hipEventCreate failed");
-        hipEventRecord(ea, st);
+        if (hipEventRecord(ea, st) != hipSuccess) return fail(EV_EHIP, "w4 timing: record failed");
     }
-    if (G == 64)
-        hipLaunchKernelGGL(w4_verify_kernel<64>, grid, dim3(kThreads), lds, st, args);
-    else
-        hipLaunchKernelGGL(w4_verify_kernel<32>, grid, dim3(kThreads), lds, st, args);
+    if (G == 64) {
+        if (aligned_k)
+            hipLaunchKernelGGL((w4_verify_kernel<64, true>), dim3(blocks), dim3(kThreads), 0, st, args);
+        else
+            hipLaunchKernelGGL((w4_verify_kernel<64, false>), dim3(blocks), dim3(kThreads), 0, st, args);
+    } else {
+        if (aligned_k)
+            hipLaunchKernelGGL((w4_verify_kernel<32, true>), dim3(blocks), dim3(kThreads), 0, st, args);
+        else
+            hipLaunchKernelGGL((w4_verify_kernel<32, false>), dim3(blocks), dim3(kThreads), 0, st, args);
+    }
     int32_t rc = check_hip(hipGetLastError(), "w4_verify_kernel launch");
     if (timed) {
-        hipEventRecord(eb, st);
+        if (hipEventRecord(eb, st) != hipSuccess) return fail(EV_EHIP, "w4 timing: record failed");
         std::lock_guard<std::mutex> lk(g_timing.mu);
         g_timing.recs.push_back({ea, eb, w4_algo_bytes(nmat, args.R, args.K, args.N, G)});
     }
@@ -346,6 +426,8 @@ static int32_t launch_w4(const W4Args& args, int nmat, const W4Plan& p, int G, l
 
 static int32_t check_w4_shape(const char* who, int R, int K, int N, int G) {
     if (R < 1 || R > EV_MAX_LANES) return fail(EV_EINVAL, "%s: R=%d outside 1..16", who, R);
+    if ((long long)N * (K / 2) >= (1LL << 31) || (long long)EV_MAX_LANES * K * 2 >= (1LL << 31))
+        return fail(EV_EUNSUPPORTED, "%s: N*K/2 must stay below 2^31 bytes", who);
     if (G != 32 && G != 64) return fail(EV_EUNSUPPORTED, "%s: group size %d (32 or 64)", who, G);
     if (K <= 0 || N <= 0) return fail(EV_EINVAL, "%s: K=%d N=%d must be positive", who, K, N);
     if (K % G != 0 || K % 32 != 0)
@@ -387,8 +469,8 @@ extern "C" int32_t ev_w4_timing_read(int64_t* launches, double* total_ms, double
             rc = fail(EV_EHIP, "ev_w4_timing_read: event query failed");
         ms += t;
         bytes += r.bytes;
-        hipEventDestroy(r.a);
-        hipEventDestroy(r.b);
+        (void)hipEventDestroy(r.a);
+        (void)hipEventDestroy(r.b);
     }
     if (launches) *launches = (int64_t)recs.size();
     if (total_ms) *total_ms = ms;
@@ -398,7 +480,7 @@ extern "C" int32_t ev_w4_timing_read(int64_t* launches, double* total_ms, double
 
 extern "C" size_t verify_linear_w4_workspace(int32_t K, int32_t N, int32_t G) {
     if (K <= 0 || N <= 0 || (G != 32 && G != 64)) return 0;
-    const W4Plan p = plan_w4(N, K);
+    const W4Plan p = plan_w4(N, K, 1);
     return p.S > 1 ? (size_t)p.S * 16 * (size_t)N * sizeof(float) : 0;
 }
 
@@ -413,7 +495,7 @@ extern "C" int32_t verify_linear_w4(const uint16_t* x, int32_t R, int32_t K, con
     if (!x || !y) return fail(EV_EINVAL, "%s: NULL x or y", who);
     if (!aligned(x, 16)) return fail(EV_EINVAL, "%s: x must be 16-byte aligned", who);
     if (!aligned(y, 4)) return fail(EV_EINVAL, "%s: y must be 4-byte aligned", who);
-    const W4Plan p = plan_w4(N, K);
+    const W4Plan p = plan_w4(N, K, 1);
     const size_t need = verify_linear_w4_workspace(K, N, G);
     if (need > 0) {
         if (!ws || ws_bytes < need)
@@ -429,10 +511,8 @@ extern "C" int32_t verify_linear_w4(const uint16_t* x, int32_t R, int32_t K, con
     a.R = R;
     a.K = K;
     a.N = N;
-    a.nchunks = p.nchunks;
-    a.cps = p.cps;
     a.split_stride = p.S > 1 ? (long)16 * N : 0;
-    if ((rc = launch_w4(a, 1, p, G, N, st))) return rc;
+    if ((rc = launch_w4(a, 1, p, G, st))) return rc;
     if (p.S > 1) {
         dim3 grid((unsigned)((N + 255) / 256), (unsigned)R);
         hipLaunchKernelGGL(splitk_reduce_kernel, grid, dim3(256), 0, st,
@@ -451,8 +531,8 @@ struct MlpLayout {
 
 static MlpLayout mlp_layout(int H, int I) {
     MlpLayout L;
-    L.p1 = plan_w4(2L * I, H);
-    L.p2 = plan_w4(H, I);
+    L.p1 = plan_w4(I, H, 2);
+    L.p2 = plan_w4(H, I, 1);
     const size_t part1 = align256((size_t)L.p1.S * 16 * I * sizeof(float));
     L.off_pu = part1;
     L.off_h = 2 * part1;
@@ -504,10 +584,8 @@ extern "C" int32_t verify_mlp_w4(const uint16_t* x, int32_t R, int32_t H, int32_
     a.R = R;
     a.K = H;
     a.N = I;
-    a.nchunks = L.p1.nchunks;
-    a.cps = L.p1.cps;
     a.split_stride = (long)16 * I;
-    if ((rc = launch_w4(a, 2, L.p1, G, I, st))) return rc;
+    if ((rc = launch_w4(a, 2, L.p1, G, st))) return rc;
     {
         dim3 grid((unsigned)((I + 255) / 256), (unsigned)R);
         hipLaunchKernelGGL(silu_reduce_kernel, grid, dim3(256), 0, st, pg, pu, L.p1.S, I, h, h_out);
@@ -521,10 +599,8 @@ extern "C" int32_t verify_mlp_w4(const uint16_t* x, int32_t R, int32_t H, int32_
     d.R = R;
     d.K = I;
     d.N = H;
-    d.nchunks = L.p2.nchunks;
-    d.cps = L.p2.cps;
     d.split_stride = L.p2.S > 1 ? (long)16 * H : 0;
-    if ((rc = launch_w4(d, 1, L.p2, G, H, st))) return rc;
+    if ((rc = launch_w4(d, 1, L.p2, G, st))) return rc;
     if (L.p2.S > 1) {
         dim3 grid((unsigned)((H + 255) / 256), (unsigned)R);
         hipLaunchKernelGGL(splitk_reduce_kernel, grid, dim3(256), 0, st, pd, L.p2.S, H, y);
