@@ -3,10 +3,13 @@
 
 Workload (one "step"): the dense 27B-class MLP verify slice -- gate/up W4
 5120 -> 17408, SiLU * up, down W4 17408 -> 5120, group 64 -- over R = 16 draft
-lanes, through the library's verify_mlp_w4 entry point (W4 kernel for gate+up,
-split reduce fused with SiLU * up, W4 kernel for down, split reduce).  Inputs
-are resident in HBM before timing; the weights rotate over several copies
-(> 2 x 256 MB in total) so the 256 MB Infinity Cache cannot serve them.
+lanes, through the library's verify_mlp_w4 entry point (activation pack, W4
+kernel for gate+up, split reduce fused with SiLU * up, W4 kernel for down,
+split reduce).  The weights are packed once at load (w4_pack, an exact byte
+reordering with the same byte count), outside the timed region, like any
+model load; inputs are resident in HBM before timing; the weights rotate over
+several copies (> 2 x 256 MB in total) so the 256 MB Infinity Cache cannot
+serve them.
 
 Printed: one JSON line with the metric (algorithmic HBM GB/s of the verify
 pass), the per-R sweep (R = 1, 2, 4, 8, 16), the dominant kernel's roofline
@@ -111,7 +114,13 @@ def main():
 
     copies = []
     for c in range(args.copies):
-        copies.append(tuple(tuple(to_dev(a) for a in d[m]) for m in ("gate", "up", "down")))
+        mats = []
+        for m in ("gate", "up", "down"):
+            q, s, b = (to_dev(a) for a in d[m])
+            mats.append(ev.w4_pack(q, s, b, G))
+            del q, s, b
+        copies.append(tuple(mats))
+    torch.cuda.synchronize()
     x_all = to_dev(d["x"])
     ws = torch.empty(ev.verify_mlp_w4_workspace(H, I, G), dtype=torch.uint8, device=dev)
     y = torch.empty((16, H), dtype=torch.float32, device=dev)
@@ -119,7 +128,7 @@ def main():
 
     def step(i, R):
         gate, up, down = copies[i % len(copies)]
-        ev.verify_mlp_w4(x_all[:R], gate, up, down, G, y=y[:R], ws=ws, stream=stream)
+        ev.verify_mlp_w4(x_all[:R], gate, up, down, y=y[:R], ws=ws, stream=stream)
 
     def timed(R, steps, warmup):
         for i in range(warmup):

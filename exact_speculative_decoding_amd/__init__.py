@@ -41,11 +41,13 @@ _vp, _sz, _i32, _i64 = C.c_void_p, C.c_size_t, C.c_int32, C.c_int64
 _SIGS = {
     "ev_last_error": (C.c_char_p, []),
     "ev_version": (_i32, []),
+    "w4_packed_bytes": (_sz, [_i32, _i32, _i32]),
+    "w4_pack": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _vp, _sz, _vp]),
     "verify_linear_w4_workspace": (_sz, [_i32, _i32, _i32]),
-    "verify_linear_w4": (_i32, [_vp, _i32, _i32, _vp, _vp, _vp, _i32, _i32, _vp, _vp, _sz, _vp]),
+    "verify_linear_w4": (_i32, [_vp, _i32, _i32, _vp, _i32, _i32, _vp, _vp, _sz, _vp]),
     "verify_mlp_w4_workspace": (_sz, [_i32, _i32, _i32]),
-    "verify_mlp_w4": (_i32, [_vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp,
-                             _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "verify_mlp_w4": (_i32, [_vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _sz,
+                             _vp]),
     "keyed_sample_workspace": (_sz, [_i32]),
     "keyed_sample": (_i32, [_vp, _i32, _i32, _vp, Sampling, _vp, _vp, _vp, _sz, _vp]),
     "accept_prefix": (_i32, [_vp, _i32, _vp, _i32, _vp, _vp, _vp]),
@@ -112,20 +114,44 @@ def _workspace(nbytes, device, ws):
     return ws, ws.numel() * ws.element_size()
 
 
+class PackedW4:
+    """A W4 matrix in the packed layout (device bytes) with its shape."""
+
+    def __init__(self, blob, N, K, G):
+        self.blob, self.N, self.K, self.G = blob, N, K, G
+
+
+def w4_packed_bytes(N, K, G):
+    return int(lib().w4_packed_bytes(N, K, G))
+
+
+def w4_pack(q, s, b, G, out=None, stream=None):
+    """Pack a standard-layout matrix q [N][K/2] u8, s/b [N][K/G] fp16 (device)."""
+    N, Kh = q.shape
+    K = 2 * Kh
+    nb = w4_packed_bytes(N, K, G)
+    if out is None:
+        out = torch.empty(nb, dtype=torch.uint8, device=q.device)
+    _check(lib().w4_pack(_dev(q, "q", _U8), _dev(s, "s", _F16), _dev(b, "b", _F16), N, K, G,
+                         _dev(out, "packed", _U8), out.numel(), _stream(stream)))
+    return PackedW4(out, N, K, G)
+
+
 def verify_linear_w4_workspace(K, N, G):
     return int(lib().verify_linear_w4_workspace(K, N, G))
 
 
-def verify_linear_w4(x, q, s, b, G, y=None, ws=None, stream=None):
-    """y[R][N] fp32 = W4 linear of x[R][K] (bf16) with q[N][K/2], s/b[N][K/G]."""
+def verify_linear_w4(x, w, y=None, ws=None, stream=None):
+    """y[R][N] fp32 = W4 linear of x[R][K] (bf16) with the packed matrix w."""
     R, K = x.shape
-    N = q.shape[0]
+    if K != w.K:
+        raise ValueError(f"x has K={K}, the matrix K={w.K}")
     if y is None:
-        y = torch.empty((R, N), dtype=torch.float32, device=x.device)
-    ws, nb = _workspace(verify_linear_w4_workspace(K, N, G), x.device, ws)
+        y = torch.empty((R, w.N), dtype=torch.float32, device=x.device)
+    ws, nb = _workspace(verify_linear_w4_workspace(K, w.N, w.G), x.device, ws)
     _check(lib().verify_linear_w4(
-        _dev(x, "x", _B16), R, K, _dev(q, "q", _U8), _dev(s, "s", _F16), _dev(b, "b", _F16),
-        N, G, _dev(y, "y", (torch.float32,)),
+        _dev(x, "x", _B16), R, K, _dev(w.blob, "w", _U8), w.N, w.G,
+        _dev(y, "y", (torch.float32,)),
         None if ws is None else C.c_void_p(ws.data_ptr()), nb, _stream(stream)))
     return y
 
@@ -134,18 +160,18 @@ def verify_mlp_w4_workspace(H, I, G):
     return int(lib().verify_mlp_w4_workspace(H, I, G))
 
 
-def verify_mlp_w4(x, gate, up, down, G, y=None, h=None, ws=None, stream=None):
-    """Dense SiLU-gated MLP slice; gate/up/down are (q, s, b) tensors."""
+def verify_mlp_w4(x, gate, up, down, y=None, h=None, ws=None, stream=None):
+    """Dense SiLU-gated MLP slice on packed gate/up (I x H) and down (H x I)."""
     R, H = x.shape
-    I = gate[0].shape[0]
+    I, G = gate.N, gate.G
+    if not (gate.K == up.K == down.N == H and up.N == down.K == I and up.G == down.G == G):
+        raise ValueError("inconsistent MLP matrix shapes")
     if y is None:
         y = torch.empty((R, H), dtype=torch.float32, device=x.device)
     ws, nb = _workspace(verify_mlp_w4_workspace(H, I, G), x.device, ws)
-    w = []
-    for name, (q, s, b) in (("gate", gate), ("up", up), ("down", down)):
-        w += [_dev(q, name + ".q", _U8), _dev(s, name + ".s", _F16), _dev(b, name + ".b", _F16)]
     _check(lib().verify_mlp_w4(
-        _dev(x, "x", _B16), R, H, I, G, *w, _dev(y, "y", (torch.float32,)),
+        _dev(x, "x", _B16), R, H, I, G, _dev(gate.blob, "gate", _U8), _dev(up.blob, "up", _U8),
+        _dev(down.blob, "down", _U8), _dev(y, "y", (torch.float32,)),
         None if h is None else _dev(h, "h", _B16),
         C.c_void_p(ws.data_ptr()), nb, _stream(stream)))
     return y

@@ -1,0 +1,48 @@
+// Packed W4 weight and activation layouts (internal to libexactverify).
+//
+// Weights of an N x K W4 linear (group size G) are repacked once, exactly, into
+// tiles of 16 output rows and chunks of 128 k:
+//   blob[tile][chunk] = 1024 B of nibbles + 64*(128/G) B of (scale, bias)
+//   * nibbles: lane L = ln + 16 j of a wave reads 16 B at 16 L; dword t holds
+//     the 8 codes of row 16*tile + ln for k = 128 c + 32 t + 8 j .. +7, in k
+//     order, low nibble first (the standard byte order of those 8 codes);
+//   * (scale, bias): for row ln and group g of the chunk, the fp16 pair
+//     (scale | bias << 16) at 1024 + 4 (ln * GPC + g).
+// Rows >= N and k >= K are padding: codes, scales and biases 0, which adds
+// exactly 0 to every output.  Without padding the blob has exactly the bytes
+// of the standard layout: N*K/2 + 4*N*K/G.
+//
+// Activations of a call are repacked per chunk and 32-k step into the MFMA A
+// fragments: xp[chunk][step][lane L][16 B] = the 8 bf16 x[ln][128 c + 32 st +
+// 8 j + i] in the order i = 0,4,1,5,2,6,3,7 (matching the nibble decode);
+// rows >= R and k >= K are 0.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ev {
+
+constexpr int kKC = 128;         // k per chunk
+constexpr int kXChunkBytes = 4096;  // packed activations per chunk
+
+__host__ __device__ inline int w4_tiles(int N) { return (N + 15) / 16; }
+__host__ __device__ inline int w4_chunks(int K) { return (K + kKC - 1) / kKC; }
+__host__ __device__ inline int w4_chunk_bytes(int G) { return 1024 + 64 * (kKC / G); }
+__host__ __device__ inline size_t w4_blob_bytes(int N, int K, int G) {
+    return (size_t)w4_tiles(N) * (size_t)w4_chunks(K) * (size_t)w4_chunk_bytes(G);
+}
+__host__ __device__ inline size_t w4_xpack_bytes(int K) { return (size_t)w4_chunks(K) * kXChunkBytes; }
+
+#ifndef EV_W4_CHUNK_MAJOR
+#define EV_W4_CHUNK_MAJOR 0
+#endif
+// Byte offset of tile-chunk (tile, c) in the blob: tile-major (a tile's chunks
+// are adjacent) or chunk-major (a chunk's tiles are adjacent).
+__host__ __device__ inline size_t w4_tc_offset(long tile, int c, int tiles, int nchunks, int G) {
+    return (EV_W4_CHUNK_MAJOR ? ((size_t)c * tiles + tile) : ((size_t)tile * nchunks + c)) *
+           (size_t)w4_chunk_bytes(G);
+}
+
+}  // namespace ev

@@ -1,0 +1,112 @@
+// Exact repacking of W4 weights (once, at load) and of activations (per call)
+// into the layouts of w4_layout.h.  Pure data movement: every output value is
+// a copy of an input value or a padding zero.
+#include "ev_internal.h"
+#include "w4_layout.h"
+
+namespace ev {
+
+// One thread per (tile, chunk, lane): 16 B of codes, plus (for the lanes of
+// row group j == 0) the row's (scale, bias) pairs of the chunk.
+__global__ void w4_pack_kernel(const uint8_t* __restrict__ q, const uint16_t* __restrict__ s,
+                               const uint16_t* __restrict__ b, int N, int K, int G,
+                               uint8_t* __restrict__ out) {
+    const int NC = w4_chunks(K);
+    const long total = (long)w4_tiles(N) * NC * 64;
+    const long gid = (long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (gid >= total) return;
+    const int L = (int)(gid & 63);
+    const long tc = gid >> 6;
+    const int c = (int)(tc % NC);
+    const long tile = tc / NC;
+    const int ln = L & 15, j = L >> 4;
+    const long n = tile * 16 + ln;
+    const int GPC = kKC / G;
+    uint8_t* dst = out + w4_tc_offset(tile, c, w4_tiles(N), NC, G);
+    const size_t Kh = (size_t)K / 2;
+    u32x4 w = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const int k = kKC * c + 32 * t + 8 * j;
+        if (n < N && k < K) w[t] = *reinterpret_cast<const uint32_t*>(q + (size_t)n * Kh + k / 2);
+    }
+    *reinterpret_cast<u32x4*>(dst + 16 * L) = w;
+    if (j == 0) {
+        const int KG = K / G;
+        for (int g = 0; g < GPC; ++g) {
+            const int kg = kKC * c + g * G;
+            uint32_t v = 0u;
+            if (n < N && kg < K) {
+                const size_t o = (size_t)n * KG + kg / G;
+                v = (uint32_t)s[o] | ((uint32_t)b[o] << 16);
+            }
+            *reinterpret_cast<uint32_t*>(dst + 1024 + 4 * (ln * GPC + g)) = v;
+        }
+    }
+}
+
+// One thread per (chunk, step, lane): 8 bf16 of row ln, reordered.
+__global__ void x_pack_kernel(const uint16_t* __restrict__ x, int R, int K, uint8_t* __restrict__ out) {
+    const long total = (long)w4_chunks(K) * 256;
+    const long gid = (long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (gid >= total) return;
+    const int L = (int)(gid & 63);
+    const int st = (int)((gid >> 6) & 3);
+    const int c = (int)(gid >> 8);
+    const int ln = L & 15, j = L >> 4;
+    const int k = kKC * c + 32 * st + 8 * j;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (ln < R && k < K) v = *reinterpret_cast<const u32x4*>(x + (size_t)ln * K + k);
+    u32x4 o;
+    o[0] = __builtin_amdgcn_perm(v[2], v[0], 0x05040100u);
+    o[1] = __builtin_amdgcn_perm(v[2], v[0], 0x07060302u);
+    o[2] = __builtin_amdgcn_perm(v[3], v[1], 0x05040100u);
+    o[3] = __builtin_amdgcn_perm(v[3], v[1], 0x07060302u);
+    *reinterpret_cast<u32x4*>(out + 16 * gid) = o;
+}
+
+int32_t launch_x_pack(const uint16_t* x, int R, int K, void* out, hipStream_t st) {
+    const long total = (long)w4_chunks(K) * 256;
+    hipLaunchKernelGGL(x_pack_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, x, R, K,
+                       reinterpret_cast<uint8_t*>(out));
+    return check_hip(hipGetLastError(), "x_pack launch");
+}
+
+int32_t check_w4_dims(const char* who, int K, int N, int G) {
+    if (G != 32 && G != 64) return fail(EV_EUNSUPPORTED, "%s: group size %d (32 or 64)", who, G);
+    if (K <= 0 || N <= 0) return fail(EV_EINVAL, "%s: K=%d N=%d must be positive", who, K, N);
+    if (K % G != 0 || K % 32 != 0)
+        return fail(EV_EINVAL, "%s: K=%d must be a multiple of 32 and of G=%d", who, K, G);
+    if (w4_blob_bytes(N, K, G) >= (1ull << 31))
+        return fail(EV_EUNSUPPORTED, "%s: packed weights of %zu bytes exceed 2^31", who,
+                    w4_blob_bytes(N, K, G));
+    return EV_OK;
+}
+
+}  // namespace ev
+
+using namespace ev;
+
+extern "C" size_t w4_packed_bytes(int32_t N, int32_t K, int32_t G) {
+    if (N <= 0 || K <= 0 || (G != 32 && G != 64)) return 0;
+    return w4_blob_bytes(N, K, G);
+}
+
+extern "C" int32_t w4_pack(const uint8_t* q, const uint16_t* s, const uint16_t* b, int32_t N, int32_t K,
+                           int32_t G, void* packed, size_t packed_bytes, void* stream) {
+    clear_error();
+    const char* who = "w4_pack";
+    int32_t rc = check_w4_dims(who, K, N, G);
+    if (rc) return rc;
+    if (!q || !s || !b || !packed) return fail(EV_EINVAL, "%s: NULL pointer", who);
+    if (!aligned(q, 4) || !aligned(s, 2) || !aligned(b, 2) || !aligned(packed, 16))
+        return fail(EV_EINVAL, "%s: misaligned pointer (q 4 B, s/b 2 B, packed 16 B)", who);
+    if (packed_bytes < w4_blob_bytes(N, K, G))
+        return fail(EV_EINVAL, "%s: packed buffer needs %zu bytes, got %zu", who, w4_blob_bytes(N, K, G),
+                    packed_bytes);
+    const long total = (long)w4_tiles(N) * w4_chunks(K) * 64;
+    hipLaunchKernelGGL(w4_pack_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
+                       reinterpret_cast<hipStream_t>(stream), q, s, b, N, K, G,
+                       reinterpret_cast<uint8_t*>(packed));
+    return check_hip(hipGetLastError(), "w4_pack launch");
+}

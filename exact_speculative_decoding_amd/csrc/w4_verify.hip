@@ -13,20 +13,18 @@
 // function of (N, K, G) only.
 //
 // Kernel shape: every wave is an independent work item (no LDS, no barriers):
-// kNT 16-column MFMA tiles over one K-split of `cps` chunks of 128.
-//   * A operand = the 16 activation rows (rows >= R read as zero through the
-//     buffer range check), loaded per 32-k step straight from L2, each 8-element
-//     group reordered [0,4,1,5,2,6,3,7] to match the nibble decode;
-//   * B operand = 16 columns of packed nibbles: each lane streams 16 B of one
-//     row per tile per chunk (a wave load covers 16 rows x 64 B), and a 4x4
-//     dword transpose across the four 16-lane rows (v_permlane32_swap /
-//     v_permlane16_swap) turns them into per-step fragments;
+// kNT tiles of 16 output rows over one K-split of `cps` chunks of 128 k, on the
+// packed layouts of w4_layout.h.
+//   * per chunk and tile one contiguous 1 KB load gives the B fragments of the
+//     four 32-k MFMA steps, and one 8/16 B load the (scale, bias) pairs; per
+//     step one contiguous 1 KB load gives the A fragment (16 activation rows);
 //   * nibbles decode exactly into bf16 as 16 + q (0x4180 | q << 3: a shift and
 //     an and-or per pair); one more MFMA against an all-ones B gives the group
 //     sum xs of every row, and the fold is p += s * acc + (b - 16 s) * xs into
 //     a per-chunk partial p that is added to y once per chunk;
-//   * a ring of kPD chunks of loads is kept in flight per wave; all loads are
-//     buffer loads, so out-of-range rows/columns read zero without branches;
+//   * a ring of kPD chunks of loads is kept in flight per wave; loads past the
+//     split's last chunk use an out-of-range per-lane offset, which the buffer
+//     range check turns into zeros without touching memory;
 //   * K-split partial sums go to a workspace [S][16][N] and are added in
 //     ascending split order by a second kernel (fused with SiLU * up for the
 //     MLP gate/up pair).
@@ -34,9 +32,10 @@
 #include <vector>
 
 #include "ev_internal.h"
+#include "w4_layout.h"
 
 #ifndef EV_W4_NT
-#define EV_W4_NT 4  // 16-column tiles per wave
+#define EV_W4_NT 4  // 16-row tiles per wave
 #endif
 #ifndef EV_W4_PD
 #define EV_W4_PD 2  // chunks of loads in flight per wave
@@ -50,26 +49,27 @@
 
 namespace ev {
 
+int32_t launch_x_pack(const uint16_t* x, int R, int K, void* out, hipStream_t st);
+int32_t check_w4_dims(const char* who, int K, int N, int G);
+
 constexpr int kThreads = 256;  // 4 independent waves per workgroup
 constexpr int kNT = EV_W4_NT;
 constexpr int kPD = EV_W4_PD;
-constexpr int kWaveCols = 16 * kNT;
-constexpr int kKC = 128;  // k per chunk (4 MFMA steps of 32)
-constexpr uint32_t kOOB = 0x80000000u;  // offset beyond every buffer: reads 0
+constexpr uint32_t kOOB = 0x80000000u;  // per-lane offset beyond every buffer: reads 0
 
 struct W4Plan {
     int S;        // K-splits
     int cps;      // chunks per split
-    int nchunks;  // ceil(K / 128)
-    int ncg;      // column groups of kWaveCols
+    int nchunks;  // chunks of 128 k
+    int ncg;      // tile groups of kNT tiles
     long items;   // waves = nmat * S * ncg
 };
 
 // Split plan from (N, K) and the number of matrices of the launch, never R.
 static W4Plan plan_w4(int N, int K, int nmat) {
     W4Plan p;
-    p.nchunks = (K + kKC - 1) / kKC;
-    p.ncg = (N + kWaveCols - 1) / kWaveCols;
+    p.nchunks = w4_chunks(K);
+    p.ncg = (w4_tiles(N) + kNT - 1) / kNT;
     const long base = (long)p.ncg * nmat;
     long S = (EV_W4_TARGET_WAVES + base - 1) / base;
     long smax = p.nchunks / EV_W4_MIN_CPS;
@@ -82,20 +82,15 @@ static W4Plan plan_w4(int N, int K, int nmat) {
     return p;
 }
 
-struct W4Mat {
-    const uint8_t* q;
-    const uint16_t* s;
-    const uint16_t* b;
-    float* out;  // split s writes rows at out + s * split_stride
-};
-
 struct W4Args {
-    W4Mat m[2];  // the item's matrix index picks one (gate/up share one launch)
-    const uint16_t* x;
-    int R, K, N;
-    int nchunks, cps, S, ncg;
+    const uint8_t* w[2];  // packed weights; the item's matrix index picks one
+    float* out[2];        // split s writes rows at out + s * split_stride
+    const uint8_t* xp;    // packed activations
+    int R, N, nchunks, tiles;
+    int cps, S, ncg;
     long items;
-    long split_stride;  // floats between consecutive splits' outputs
+    long split_stride;
+    uint32_t wbytes, xbytes;
     // nibble-decode constants, passed as arguments so that they sit in
     // registers (gfx9 VOP3 encodings cannot carry 32-bit literals)
     uint32_t dmask, doff;
@@ -106,15 +101,13 @@ typedef __amdgpu_buffer_rsrc_t rsrc_t;
 __device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
 }
-// voff: per-lane byte offset; soff: wave-uniform byte offset (scalar register)
+// voff: per-lane byte offset (range-checked); soff: wave-uniform byte offset
 __device__ __forceinline__ u32x4 bload128(rsrc_t r, uint32_t voff, uint32_t soff) {
     return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
 }
-__device__ __forceinline__ uint32_t bload32(rsrc_t r, uint32_t voff, uint32_t soff) {
-    return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
-}
-__device__ __forceinline__ uint16_t bload16(rsrc_t r, uint32_t voff, uint32_t soff) {
-    return __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ u32x2 bload64(rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
 }
 
 // Eight nibbles q0..q7 (q_i in bits 4i..4i+3) -> four bf16 pairs holding
@@ -128,48 +121,14 @@ __device__ __forceinline__ u32x4 decode_nibbles(uint32_t d, uint32_t m, uint32_t
     return r;
 }
 
-// Eight bf16 x0..x7 (natural order) -> (x0,x4) (x1,x5) (x2,x6) (x3,x7), one
-// byte permute per output dword.
-__device__ __forceinline__ u32x4 reorder_x(u32x4 v) {
-    u32x4 o;
-    o[0] = __builtin_amdgcn_perm(v[2], v[0], 0x05040100u);
-    o[1] = __builtin_amdgcn_perm(v[2], v[0], 0x07060302u);
-    o[2] = __builtin_amdgcn_perm(v[3], v[1], 0x05040100u);
-    o[3] = __builtin_amdgcn_perm(v[3], v[1], 0x07060302u);
-    return o;
-}
-
-// 4x4 transpose of dwords across the four 16-lane rows of a wave: afterwards
-// register t of row j holds what register j of row t held.
-__device__ __forceinline__ void transpose_rows(u32x4& v) {
-    uint32_t d0 = v[0], d1 = v[1], d2 = v[2], d3 = v[3];
-    auto a = __builtin_amdgcn_permlane32_swap(d0, d2, false, false);
-    d0 = a[0];
-    d2 = a[1];
-    auto b = __builtin_amdgcn_permlane32_swap(d1, d3, false, false);
-    d1 = b[0];
-    d3 = b[1];
-    auto c = __builtin_amdgcn_permlane16_swap(d0, d1, false, false);
-    d0 = c[0];
-    d1 = c[1];
-    auto e = __builtin_amdgcn_permlane16_swap(d2, d3, false, false);
-    d2 = e[0];
-    d3 = e[1];
-    v[0] = d0;
-    v[1] = d1;
-    v[2] = d2;
-    v[3] = d3;
-}
-
 __device__ __forceinline__ float half_lo(uint32_t w) { return f16_to_f32((uint16_t)(w & 0xffffu)); }
 __device__ __forceinline__ float half_hi(uint32_t w) { return f16_to_f32((uint16_t)(w >> 16)); }
 
-// ALIGNED: K % 128 == 0 -- every chunk is whole, and a chunk's GPC scales (or
-// biases) of one row are one aligned 4 B (G = 64) or 8 B (G = 32) word.
-template <int G, bool ALIGNED>
+template <int G>
 __global__ __launch_bounds__(kThreads) void w4_verify_kernel(W4Args a) {
-    constexpr int GPC = kKC / G;        // groups per chunk
-    constexpr int SBW = ALIGNED ? GPC / 2 : GPC;  // s/b words per chunk (b32 or b16)
+    constexpr int GPC = kKC / G;                // groups per chunk
+    constexpr int SBW = GPC;                    // (scale, bias) dwords per lane per chunk
+    constexpr uint32_t CB = 1024 + 64 * GPC;    // packed bytes per tile-chunk
     const int lane = threadIdx.x & 63;
     // wave-uniform work item (readfirstlane keeps it, the matrix and the buffer
     // descriptors in scalar registers)
@@ -181,28 +140,25 @@ __global__ __launch_bounds__(kThreads) void w4_verify_kernel(W4Args a) {
     const long rest = item / a.ncg;
     const int split = (int)(rest % a.S);
     const int mi = (int)(rest / a.S);
-    const W4Mat mat = a.m[mi];
     const int c0 = split * a.cps;
     const int c1 = min(a.nchunks, c0 + a.cps);
-    const int K = a.K, N = a.N;
-    const uint32_t Kh = (uint32_t)K >> 1;
-    const uint32_t KG = (uint32_t)(K / G);
 
-    const rsrc_t rq = make_rsrc(mat.q, (uint32_t)((size_t)N * Kh));
-    const rsrc_t rs = make_rsrc(mat.s, (uint32_t)((size_t)N * KG * 2));
-    const rsrc_t rb = make_rsrc(mat.b, (uint32_t)((size_t)N * KG * 2));
-    const rsrc_t rx = make_rsrc(a.x, (uint32_t)((size_t)a.R * K * 2));
-
-    int ncol[kNT];
-    uint32_t qoff[kNT], soff[kNT];
+    const rsrc_t rw = make_rsrc(a.w[mi], a.wbytes);
+    const rsrc_t rx = make_rsrc(a.xp, a.xbytes);
+    // tile bases are wave-uniform; a tile past the last one reads zeros
+    uint32_t tbase[kNT];
+    bool tok[kNT];
 #pragma unroll
     for (int t = 0; t < kNT; ++t) {
-        ncol[t] = cg * kWaveCols + t * 16 + ln;
-        const bool ok = ncol[t] < N;
-        qoff[t] = ok ? (uint32_t)ncol[t] * Kh + 16u * j : kOOB;
-        soff[t] = ok ? (uint32_t)ncol[t] * KG * 2u : kOOB;
+        const int tile = cg * kNT + t;
+        tok[t] = tile < a.tiles;
+        tbase[t] = tok[t] ? (EV_W4_CHUNK_MAJOR ? (uint32_t)tile * CB : (uint32_t)tile * (uint32_t)a.nchunks * CB)
+                          : 0u;
     }
-    const uint32_t xoff = ln < a.R ? ((uint32_t)ln * K + 8u * j) * 2u : kOOB;
+    const uint32_t cstride = EV_W4_CHUNK_MAJOR ? (uint32_t)a.tiles * CB : CB;  // bytes per chunk step
+    const uint32_t vq = 16u * lane;
+    const uint32_t vsb = 1024u + 4u * GPC * ln;
+    const uint32_t vx = 16u * lane;
     // the mask stays scalar, the or-constant goes to a vector register: gfx9
     // VALU ops read at most one scalar operand, and this lets each decoded pair
     // be one v_and_or_b32
@@ -212,39 +168,33 @@ __global__ __launch_bounds__(kThreads) void w4_verify_kernel(W4Args a) {
 
     // register ring of kPD chunks
     u32x4 qr[kPD][kNT];
-    uint32_t sr[kPD][kNT][SBW], br[kPD][kNT][SBW];
+    uint32_t sbr[kPD][kNT][SBW];
     u32x4 xr[kPD][4];
 
-    // Loads of chunk c into ring slot `slot`.  The chunk's offset is a scalar
-    // (soffset); chunks at or past c1 use an out-of-range scalar offset
-    // (zeros, no memory traffic), so every slot is written on every path and
-    // the ring never has to be copied.
+    // Loads of chunk c into ring slot `slot`.  Offsets within the chunk are
+    // per-lane constants, the chunk and tile offsets a scalar; chunks at or past
+    // c1 (and tiles past the last) get an out-of-range per-lane offset, so
+    // every slot is written on every path and the ring never has to be copied.
     auto fetch = [&](int c, int slot) {
         const bool live = c < c1;
-        const uint32_t kc = (uint32_t)c * kKC;
-        const uint32_t sq = live ? (kc >> 1) : kOOB;
-        const uint32_t ss = live ? (kc / G) * 2u : kOOB;
-        const uint32_t sx = live ? kc * 2u : kOOB;
 #pragma unroll
         for (int t = 0; t < kNT; ++t) {
-            uint32_t vq = qoff[t];
-            if (!ALIGNED && kc + 32u * j >= (uint32_t)K) vq = kOOB;
-            qr[slot][t] = bload128(rq, vq, sq);
+            const bool ok = live && tok[t];
+            const uint32_t so = tbase[t] + (uint32_t)c * cstride;
+            qr[slot][t] = bload128(rw, ok ? vq : kOOB, so);
+            if (GPC == 2) {
+                const u32x2 v = bload64(rw, ok ? vsb : kOOB, so);
+                sbr[slot][t][0] = v[0];
+                sbr[slot][t][GPC - 1] = v[1];
+            } else {
+                const u32x4 v = bload128(rw, ok ? vsb : kOOB, so);
 #pragma unroll
-            for (int w = 0; w < SBW; ++w) {
-                if (ALIGNED) {
-                    sr[slot][t][w] = bload32(rs, soff[t] + 4u * w, ss);
-                    br[slot][t][w] = bload32(rb, soff[t] + 4u * w, ss);
-                } else {
-                    uint32_t so = soff[t] + 2u * w;
-                    if (kc + (uint32_t)(w * G) >= (uint32_t)K) so = kOOB;
-                    sr[slot][t][w] = bload16(rs, so, ss);
-                    br[slot][t][w] = bload16(rb, so, ss);
-                }
+                for (int g = 0; g < SBW; ++g) sbr[slot][t][g] = v[g & 3];
             }
         }
+        const uint32_t sx = (uint32_t)c * kXChunkBytes;
 #pragma unroll
-        for (int st = 0; st < 4; ++st) xr[slot][st] = bload128(rx, xoff + 64u * st, sx);
+        for (int st = 0; st < 4; ++st) xr[slot][st] = bload128(rx, live ? vx + 1024u * st : kOOB, sx);
     };
 
     const u32x4 ones = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
@@ -254,48 +204,36 @@ __global__ __launch_bounds__(kThreads) void w4_verify_kernel(W4Args a) {
 
     // One chunk: per 32-k step, one MFMA for the group sums of x and one per
     // tile; per group, p += s * acc + (b - 16 s) * xs into a chunk partial p,
-    // which is added to y once per chunk.
-    auto compute = [&](int c, int slot) {
-        const int nst = ALIGNED ? 4 : min(4, (K - c * kKC) >> 5);
-#pragma unroll
-        for (int t = 0; t < kNT; ++t) transpose_rows(qr[slot][t]);
+    // which is added to y once per chunk.  A chunk that was loaded as zeros
+    // (past c1) adds exactly zero.
+    auto compute = [&](int slot) {
         f32x4 acc[kNT], part[kNT], xs = {0.f, 0.f, 0.f, 0.f};
         const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int t = 0; t < kNT; ++t) part[t] = zero;
 #pragma unroll
         for (int st = 0; st < 4; ++st) {
-            if (ALIGNED || st < nst) {
-                const bf16x8 A = __builtin_bit_cast(bf16x8, reorder_x(xr[slot][st]));
-                const bool first = (G == 32) || ((st & 1) == 0);
-                xs = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, __builtin_bit_cast(bf16x8, ones),
-                                                            first ? zero : xs, 0, 0, 0);
+            const bf16x8 A = __builtin_bit_cast(bf16x8, xr[slot][st]);
+            const bool first = (G == 32) || ((st & 1) == 0);
+            xs = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, __builtin_bit_cast(bf16x8, ones),
+                                                        first ? zero : xs, 0, 0, 0);
+#pragma unroll
+            for (int t = 0; t < kNT; ++t) {
+                const bf16x8 B = __builtin_bit_cast(bf16x8, decode_nibbles(qr[slot][t][st], dm, doff));
+                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, first ? zero : acc[t], 0, 0, 0);
+            }
+            const bool last = (G == 32) || ((st & 1) == 1);
+            if (last) {
+                const int gc = (32 * st) / G;  // group within the chunk
 #pragma unroll
                 for (int t = 0; t < kNT; ++t) {
-                    const bf16x8 B =
-                        __builtin_bit_cast(bf16x8, decode_nibbles(qr[slot][t][st], dm, doff));
-                    acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, first ? zero : acc[t], 0, 0, 0);
-                }
-                const bool last = (G == 32) || ((st & 1) == 1);
-                if (last) {
-                    const int gc = (32 * st) / G;  // group within the chunk
+                    const uint32_t sb = sbr[slot][t][gc];
+                    const float sv = half_lo(sb), bv = half_hi(sb);
+                    const float bp = fmaf(-16.f, sv, bv);  // removes the decode offset
 #pragma unroll
-                    for (int t = 0; t < kNT; ++t) {
-                        float sv, bv;
-                        if (ALIGNED) {
-                            const uint32_t sw = sr[slot][t][gc >> 1], bw = br[slot][t][gc >> 1];
-                            sv = (gc & 1) ? half_hi(sw) : half_lo(sw);
-                            bv = (gc & 1) ? half_hi(bw) : half_lo(bw);
-                        } else {
-                            sv = f16_to_f32((uint16_t)sr[slot][t][gc]);
-                            bv = f16_to_f32((uint16_t)br[slot][t][gc]);
-                        }
-                        const float bp = fmaf(-16.f, sv, bv);  // removes the decode offset
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            part[t][i] = fmaf(sv, acc[t][i], part[t][i]);
-                            part[t][i] = fmaf(bp, xs[i], part[t][i]);
-                        }
+                    for (int i = 0; i < 4; ++i) {
+                        part[t][i] = fmaf(sv, acc[t][i], part[t][i]);
+                        part[t][i] = fmaf(bp, xs[i], part[t][i]);
                     }
                 }
             }
@@ -304,8 +242,10 @@ __global__ __launch_bounds__(kThreads) void w4_verify_kernel(W4Args a) {
         for (int t = 0; t < kNT; ++t) y[t] += part[t];
     };
 
-    // sched_barrier keeps each refill where it is written, so the loads of the
-    // other ring slots stay in flight across the compute of this one.
+    // Straight-line ring: every slot is computed and refilled on every trip
+    // (the trip count is cps rounded up to kPD).  sched_barrier keeps each
+    // refill where it is written, so the loads of the other ring slots stay in
+    // flight across the compute of this one.
 #pragma unroll
     for (int p = 0; p < kPD; ++p) {
         __builtin_amdgcn_sched_barrier(0);
@@ -315,57 +255,105 @@ __global__ __launch_bounds__(kThreads) void w4_verify_kernel(W4Args a) {
 #pragma unroll
         for (int p = 0; p < kPD; ++p) {
             __builtin_amdgcn_sched_barrier(0);
-            compute(cb + p, p);
+            compute(p);
             __builtin_amdgcn_sched_barrier(0);
             fetch(cb + p + kPD, p);
         }
     }
     __builtin_amdgcn_sched_barrier(0);
 
-    // rows r = 4j + i of columns ncol[t]
-    float* out = mat.out + (size_t)split * a.split_stride;
+    // rows r = 4j + i of columns 16 * tile + ln
+    float* out = a.out[mi] + (size_t)split * a.split_stride;
 #pragma unroll
     for (int t = 0; t < kNT; ++t) {
-        if (ncol[t] < N) {
+        const int n = (cg * kNT + t) * 16 + ln;
+        if (n < a.N) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = 4 * j + i;
-                if (r < a.R) out[(size_t)r * N + ncol[t]] = y[t][i];
+                if (r < a.R) out[(size_t)r * a.N + n] = y[t][i];
             }
         }
     }
 }
 
-// y[r][n] = sum over s = 0..S-1, ascending, of part[s][r][n].
-__global__ void splitk_reduce_kernel(const float* __restrict__ part, int S, int N,
-                                     float* __restrict__ y) {
-    const int n = blockIdx.x * 256 + threadIdx.x;
+// y[r][n] = sum over s = 0..S-1, ascending, of part[s][r][n].  One thread per
+// 4 consecutive n of one row; the loads of all splits are issued ahead of the
+// additions, which run in ascending s.
+__global__ __launch_bounds__(64) void splitk_reduce_kernel(const float* __restrict__ part, int S, int N,
+                                                           float* __restrict__ y) {
+    const int n4 = (blockIdx.x * 64 + threadIdx.x) * 4;
     const int r = blockIdx.y;
-    if (n >= N) return;
+    if (n4 >= N) return;
     const size_t stride = (size_t)16 * N;
-    float acc = part[(size_t)r * N + n];
-    for (int s = 1; s < S; ++s) acc += part[s * stride + (size_t)r * N + n];
-    y[(size_t)r * N + n] = acc;
+    const size_t o = (size_t)r * N + n4;
+    const bool vec = (N & 3) == 0 && (reinterpret_cast<uintptr_t>(y) & 15) == 0 &&
+                     (reinterpret_cast<uintptr_t>(part) & 15) == 0;
+    if (vec) {
+        f32x4 acc = *reinterpret_cast<const f32x4*>(part + o);
+#pragma unroll 8
+        for (int s = 1; s < S; ++s) acc += *reinterpret_cast<const f32x4*>(part + s * stride + o);
+        *reinterpret_cast<f32x4*>(y + o) = acc;
+    } else {
+        for (int i = 0; i < 4 && n4 + i < N; ++i) {
+            float acc = part[o + i];
+            for (int s = 1; s < S; ++s) acc += part[s * stride + o + i];
+            y[o + i] = acc;
+        }
+    }
 }
 
-// g, u = split sums (ascending s); h = bf16_rne(silu(g) * u).
-__global__ void silu_reduce_kernel(const float* __restrict__ pg, const float* __restrict__ pu,
-                                   int S, int I, uint16_t* __restrict__ h,
-                                   uint16_t* __restrict__ h_copy) {
-    const int n = blockIdx.x * 256 + threadIdx.x;
+// g, u = split sums (ascending s); h = bf16_rne(silu(g) * u).  One thread per
+// 8 consecutive k of one of the 16 rows: writes the 16 B of the down
+// projection's packed activations (rows >= R and k >= I as zeros) and, when
+// asked, h in the standard [R][I] layout.
+__global__ __launch_bounds__(64) void silu_reduce_kernel(const float* __restrict__ pg,
+                                                         const float* __restrict__ pu, int S, int R,
+                                                         int I, uint8_t* __restrict__ hp,
+                                                         uint16_t* __restrict__ h_out) {
+    const int NC = w4_chunks(I);
+    const int m = blockIdx.x * 64 + threadIdx.x;  // 8-element group of the padded row
     const int r = blockIdx.y;
-    if (n >= I) return;
-    const size_t stride = (size_t)16 * I;
-    const size_t o = (size_t)r * I + n;
-    float g = pg[o], u = pu[o];
-    for (int s = 1; s < S; ++s) {
-        g += pg[s * stride + o];
-        u += pu[s * stride + o];
+    if (m >= NC * 16) return;
+    const int k0 = 8 * m;
+    uint16_t hv[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) hv[i] = 0;
+    if (r < R && k0 < I) {  // I % 32 == 0, so all 8 are inside the row
+        const size_t stride = (size_t)16 * I;
+        const size_t o = (size_t)r * I + k0;
+        f32x4 g0 = *reinterpret_cast<const f32x4*>(pg + o), g1 = *reinterpret_cast<const f32x4*>(pg + o + 4);
+        f32x4 u0 = *reinterpret_cast<const f32x4*>(pu + o), u1 = *reinterpret_cast<const f32x4*>(pu + o + 4);
+#pragma unroll 4
+        for (int sp = 1; sp < S; ++sp) {
+            const size_t so = sp * stride + o;
+            g0 += *reinterpret_cast<const f32x4*>(pg + so);
+            g1 += *reinterpret_cast<const f32x4*>(pg + so + 4);
+            u0 += *reinterpret_cast<const f32x4*>(pu + so);
+            u1 += *reinterpret_cast<const f32x4*>(pu + so + 4);
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float g = i < 4 ? g0[i] : g1[i - 4];
+            const float u = i < 4 ? u0[i] : u1[i - 4];
+            const float sg = g / (1.0f + expf(-g));
+            hv[i] = f32_to_bf16_rne(sg * u);
+        }
+        if (h_out) {
+            u32x4 w;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) w[i] = (uint32_t)hv[2 * i] | ((uint32_t)hv[2 * i + 1] << 16);
+            *reinterpret_cast<u32x4*>(h_out + o) = w;
+        }
     }
-    const float sg = g / (1.0f + expf(-g));
-    const uint16_t hb = f32_to_bf16_rne(sg * u);
-    h[o] = hb;
-    if (h_copy) h_copy[o] = hb;
+    // packed position: chunk c, step st, lane r + 16 j; order 0,4,1,5,2,6,3,7
+    const int c = k0 / kKC, st = (k0 % kKC) / 32, j = (k0 % 32) / 8;
+    u32x4 pw;
+    pw[0] = (uint32_t)hv[0] | ((uint32_t)hv[4] << 16);
+    pw[1] = (uint32_t)hv[1] | ((uint32_t)hv[5] << 16);
+    pw[2] = (uint32_t)hv[2] | ((uint32_t)hv[6] << 16);
+    pw[3] = (uint32_t)hv[3] | ((uint32_t)hv[7] << 16);
+    *reinterpret_cast<u32x4*>(hp + (size_t)c * kXChunkBytes + 1024 * st + 16 * (r + 16 * j)) = pw;
 }
 
 // Measurement hook: when on, each W4 kernel launch is bracketed by HIP events
@@ -383,16 +371,18 @@ static double w4_algo_bytes(int nmat, int R, int K, int N, int G) {
     return nmat * (w + 2.0 * R * K + 4.0 * R * N);
 }
 
-static int32_t launch_w4(W4Args args, int nmat, const W4Plan& p, int G, hipStream_t st) {
+static int32_t launch_w4(W4Args args, int nmat, const W4Plan& p, int K, int G, hipStream_t st) {
     args.nchunks = p.nchunks;
+    args.tiles = w4_tiles(args.N);
     args.cps = p.cps;
     args.S = p.S;
     args.ncg = p.ncg;
     args.items = p.items;
+    args.wbytes = (uint32_t)w4_blob_bytes(args.N, K, G);
+    args.xbytes = (uint32_t)w4_xpack_bytes(K);
     args.dmask = 0x00780078u;
     args.doff = 0x41804180u;
     const unsigned blocks = (unsigned)((p.items + 3) / 4);
-    const bool aligned_k = args.K % kKC == 0;
     hipEvent_t ea = nullptr, eb = nullptr;
     bool timed;
     {
@@ -404,45 +394,66 @@ static int32_t launch_w4(W4Args args, int nmat, const W4Plan& p, int G, hipStrea
             return fail(EV_EHIP, "w4 timing: hipEventCreate failed");
         if (hipEventRecord(ea, st) != hipSuccess) return fail(EV_EHIP, "w4 timing: record failed");
     }
-    if (G == 64) {
-        if (aligned_k)
-            hipLaunchKernelGGL((w4_verify_kernel<64, true>), dim3(blocks), dim3(kThreads), 0, st, args);
-        else
-            hipLaunchKernelGGL((w4_verify_kernel<64, false>), dim3(blocks), dim3(kThreads), 0, st, args);
-    } else {
-        if (aligned_k)
-            hipLaunchKernelGGL((w4_verify_kernel<32, true>), dim3(blocks), dim3(kThreads), 0, st, args);
-        else
-            hipLaunchKernelGGL((w4_verify_kernel<32, false>), dim3(blocks), dim3(kThreads), 0, st, args);
-    }
+    if (G == 64)
+        hipLaunchKernelGGL(w4_verify_kernel<64>, dim3(blocks), dim3(kThreads), 0, st, args);
+    else
+        hipLaunchKernelGGL(w4_verify_kernel<32>, dim3(blocks), dim3(kThreads), 0, st, args);
     int32_t rc = check_hip(hipGetLastError(), "w4_verify_kernel launch");
     if (timed) {
         if (hipEventRecord(eb, st) != hipSuccess) return fail(EV_EHIP, "w4 timing: record failed");
         std::lock_guard<std::mutex> lk(g_timing.mu);
-        g_timing.recs.push_back({ea, eb, w4_algo_bytes(nmat, args.R, args.K, args.N, G)});
+        g_timing.recs.push_back({ea, eb, w4_algo_bytes(nmat, args.R, K, args.N, G)});
     }
     return rc;
 }
 
-static int32_t check_w4_shape(const char* who, int R, int K, int N, int G) {
-    if (R < 1 || R > EV_MAX_LANES) return fail(EV_EINVAL, "%s: R=%d outside 1..16", who, R);
-    if ((long long)N * (K / 2) >= (1LL << 31) || (long long)EV_MAX_LANES * K * 2 >= (1LL << 31))
-        return fail(EV_EUNSUPPORTED, "%s: N*K/2 must stay below 2^31 bytes", who);
-    if (G != 32 && G != 64) return fail(EV_EUNSUPPORTED, "%s: group size %d (32 or 64)", who, G);
-    if (K <= 0 || N <= 0) return fail(EV_EINVAL, "%s: K=%d N=%d must be positive", who, K, N);
-    if (K % G != 0 || K % 32 != 0)
-        return fail(EV_EINVAL, "%s: K=%d must be a multiple of 32 and of G=%d", who, K, G);
-    return EV_OK;
-}
-
-static int32_t check_w4_ptrs(const char* who, const void* q, const void* s, const void* b) {
-    if (!q || !s || !b) return fail(EV_EINVAL, "%s: NULL weight pointer", who);
-    if (!aligned(q, 16)) return fail(EV_EINVAL, "%s: q must be 16-byte aligned", who);
-    if (!aligned(s, 2) || !aligned(b, 2)) return fail(EV_EINVAL, "%s: scale/bias must be 2-byte aligned", who);
-    return EV_OK;
-}
-
 static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+// Workspace of verify_linear_w4: packed x, then split partials [S][16][N].
+struct LinLayout {
+    W4Plan p;
+    size_t off_part, total;
+};
+static LinLayout lin_layout(int K, int N) {
+    LinLayout L;
+    L.p = plan_w4(N, K, 1);
+    L.off_part = align256(w4_xpack_bytes(K));
+    L.total = L.off_part + (L.p.S > 1 ? (size_t)L.p.S * 16 * N * sizeof(float) : 0);
+    return L;
+}
+
+// Workspace of the MLP slice: packed x, gate and up partials [S1][16][I],
+// packed h, down partials [S2][16][H] (if S2 > 1).
+struct MlpLayout {
+    W4Plan p1, p2;
+    size_t off_pg, off_pu, off_hp, off_pd, total;
+};
+static MlpLayout mlp_layout(int H, int I) {
+    MlpLayout L;
+    L.p1 = plan_w4(I, H, 2);
+    L.p2 = plan_w4(H, I, 1);
+    L.off_pg = align256(w4_xpack_bytes(H));
+    const size_t part1 = align256((size_t)L.p1.S * 16 * I * sizeof(float));
+    L.off_pu = L.off_pg + part1;
+    L.off_hp = L.off_pu + part1;
+    L.off_pd = L.off_hp + align256(w4_xpack_bytes(I));
+    L.total = L.off_pd + (L.p2.S > 1 ? (size_t)L.p2.S * 16 * H * sizeof(float) : 0);
+    return L;
+}
+
+static int32_t check_lanes(const char* who, int R) {
+    if (R < 1 || R > EV_MAX_LANES) return fail(EV_EINVAL, "%s: R=%d outside 1..16", who, R);
+    return EV_OK;
+}
+
+static int32_t check_ws(const char* who, void* ws, size_t ws_bytes, size_t need) {
+    if (need == 0) return EV_OK;
+    if (!ws || ws_bytes < need)
+        return fail(EV_EWORKSPACE, "%s: workspace needs %zu bytes, got %zu", who, need,
+                    ws ? ws_bytes : (size_t)0);
+    if (!aligned(ws, 256)) return fail(EV_EINVAL, "%s: workspace must be 256-byte aligned", who);
+    return EV_OK;
+}
 
 }  // namespace ev
 
@@ -480,65 +491,38 @@ extern "C" int32_t ev_w4_timing_read(int64_t* launches, double* total_ms, double
 
 extern "C" size_t verify_linear_w4_workspace(int32_t K, int32_t N, int32_t G) {
     if (K <= 0 || N <= 0 || (G != 32 && G != 64)) return 0;
-    const W4Plan p = plan_w4(N, K, 1);
-    return p.S > 1 ? (size_t)p.S * 16 * (size_t)N * sizeof(float) : 0;
+    return lin_layout(K, N).total;
 }
 
-extern "C" int32_t verify_linear_w4(const uint16_t* x, int32_t R, int32_t K, const uint8_t* q,
-                                    const uint16_t* s, const uint16_t* b, int32_t N, int32_t G,
-                                    float* y, void* ws, size_t ws_bytes, void* stream) {
+extern "C" int32_t verify_linear_w4(const uint16_t* x, int32_t R, int32_t K, const void* w, int32_t N,
+                                    int32_t G, float* y, void* ws, size_t ws_bytes, void* stream) {
     clear_error();
     const char* who = "verify_linear_w4";
-    int32_t rc = check_w4_shape(who, R, K, N, G);
-    if (rc) return rc;
-    if ((rc = check_w4_ptrs(who, q, s, b))) return rc;
-    if (!x || !y) return fail(EV_EINVAL, "%s: NULL x or y", who);
-    if (!aligned(x, 16)) return fail(EV_EINVAL, "%s: x must be 16-byte aligned", who);
-    if (!aligned(y, 4)) return fail(EV_EINVAL, "%s: y must be 4-byte aligned", who);
-    const W4Plan p = plan_w4(N, K, 1);
-    const size_t need = verify_linear_w4_workspace(K, N, G);
-    if (need > 0) {
-        if (!ws || ws_bytes < need)
-            return fail(EV_EWORKSPACE, "%s: workspace needs %zu bytes, got %zu", who, need,
-                        ws ? ws_bytes : (size_t)0);
-        if (!aligned(ws, 16)) return fail(EV_EINVAL, "%s: workspace must be 16-byte aligned", who);
-    }
+    int32_t rc;
+    if ((rc = check_lanes(who, R)) || (rc = check_w4_dims(who, K, N, G))) return rc;
+    if (!x || !w || !y) return fail(EV_EINVAL, "%s: NULL pointer", who);
+    if (!aligned(x, 16) || !aligned(w, 16) || !aligned(y, 4))
+        return fail(EV_EINVAL, "%s: misaligned pointer (x, w 16 B; y 4 B)", who);
+    const LinLayout L = lin_layout(K, N);
+    if ((rc = check_ws(who, ws, ws_bytes, L.total))) return rc;
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    unsigned char* wsb = reinterpret_cast<unsigned char*>(ws);
+    if ((rc = launch_x_pack(x, R, K, wsb, st))) return rc;
+    float* part = reinterpret_cast<float*>(wsb + L.off_part);
     W4Args a{};
-    a.m[0] = W4Mat{q, s, b, p.S > 1 ? reinterpret_cast<float*>(ws) : y};
-    a.m[1] = a.m[0];
-    a.x = x;
+    a.w[0] = a.w[1] = reinterpret_cast<const uint8_t*>(w);
+    a.out[0] = a.out[1] = L.p.S > 1 ? part : y;
+    a.xp = wsb;
     a.R = R;
-    a.K = K;
     a.N = N;
-    a.split_stride = p.S > 1 ? (long)16 * N : 0;
-    if ((rc = launch_w4(a, 1, p, G, st))) return rc;
-    if (p.S > 1) {
+    a.split_stride = L.p.S > 1 ? (long)16 * N : 0;
+    if ((rc = launch_w4(a, 1, L.p, K, G, st))) return rc;
+    if (L.p.S > 1) {
         dim3 grid((unsigned)((N + 255) / 256), (unsigned)R);
-        hipLaunchKernelGGL(splitk_reduce_kernel, grid, dim3(256), 0, st,
-                           reinterpret_cast<const float*>(ws), p.S, N, y);
+        hipLaunchKernelGGL(splitk_reduce_kernel, grid, dim3(64), 0, st, part, L.p.S, N, y);
         if ((rc = check_hip(hipGetLastError(), "splitk_reduce launch"))) return rc;
     }
     return EV_OK;
-}
-
-// Workspace layout of the MLP slice: gate partials [S1][16][I] f32, up partials
-// [S1][16][I] f32, h [16][I] bf16, down partials [S2][16][H] f32 (if S2 > 1).
-struct MlpLayout {
-    W4Plan p1, p2;
-    size_t off_pu, off_h, off_pd, total;
-};
-
-static MlpLayout mlp_layout(int H, int I) {
-    MlpLayout L;
-    L.p1 = plan_w4(I, H, 2);
-    L.p2 = plan_w4(H, I, 1);
-    const size_t part1 = align256((size_t)L.p1.S * 16 * I * sizeof(float));
-    L.off_pu = part1;
-    L.off_h = 2 * part1;
-    L.off_pd = L.off_h + align256((size_t)16 * I * sizeof(uint16_t));
-    L.total = L.off_pd + (L.p2.S > 1 ? (size_t)L.p2.S * 16 * H * sizeof(float) : 0);
-    return L;
 }
 
 extern "C" size_t verify_mlp_w4_workspace(int32_t H, int32_t I, int32_t G) {
@@ -547,63 +531,56 @@ extern "C" size_t verify_mlp_w4_workspace(int32_t H, int32_t I, int32_t G) {
 }
 
 extern "C" int32_t verify_mlp_w4(const uint16_t* x, int32_t R, int32_t H, int32_t I, int32_t G,
-                                 const uint8_t* gq, const uint16_t* gs, const uint16_t* gb,
-                                 const uint8_t* uq, const uint16_t* us, const uint16_t* ub,
-                                 const uint8_t* dq, const uint16_t* ds, const uint16_t* db,
-                                 float* y, uint16_t* h_out, void* ws, size_t ws_bytes,
-                                 void* stream) {
+                                 const void* w_gate, const void* w_up, const void* w_down, float* y,
+                                 uint16_t* h_out, void* ws, size_t ws_bytes, void* stream) {
     clear_error();
     const char* who = "verify_mlp_w4";
-    int32_t rc = check_w4_shape(who, R, H, I, G);
-    if (rc) return rc;
-    if ((rc = check_w4_shape(who, R, I, H, G))) return rc;
-    if ((rc = check_w4_ptrs(who, gq, gs, gb)) || (rc = check_w4_ptrs(who, uq, us, ub)) ||
-        (rc = check_w4_ptrs(who, dq, ds, db)))
+    int32_t rc;
+    if ((rc = check_lanes(who, R)) || (rc = check_w4_dims(who, H, I, G)) ||
+        (rc = check_w4_dims(who, I, H, G)))
         return rc;
-    if (!x || !y) return fail(EV_EINVAL, "%s: NULL x or y", who);
-    if (!aligned(x, 16)) return fail(EV_EINVAL, "%s: x must be 16-byte aligned", who);
-    if (!aligned(y, 4) || (h_out && !aligned(h_out, 2)))
-        return fail(EV_EINVAL, "%s: misaligned y or h", who);
+    if (!x || !w_gate || !w_up || !w_down || !y) return fail(EV_EINVAL, "%s: NULL pointer", who);
+    if (!aligned(x, 16) || !aligned(w_gate, 16) || !aligned(w_up, 16) || !aligned(w_down, 16) ||
+        !aligned(y, 4) || (h_out && !aligned(h_out, 16)))
+        return fail(EV_EINVAL, "%s: misaligned pointer (x, weights, h 16 B; y 4 B)", who);
     const MlpLayout L = mlp_layout(H, I);
-    if (!ws || ws_bytes < L.total)
-        return fail(EV_EWORKSPACE, "%s: workspace needs %zu bytes, got %zu", who, L.total,
-                    ws ? ws_bytes : (size_t)0);
-    if (!aligned(ws, 256)) return fail(EV_EINVAL, "%s: workspace must be 256-byte aligned", who);
+    if ((rc = check_ws(who, ws, ws_bytes, L.total))) return rc;
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-    unsigned char* w = reinterpret_cast<unsigned char*>(ws);
-    float* pg = reinterpret_cast<float*>(w);
-    float* pu = reinterpret_cast<float*>(w + L.off_pu);
-    uint16_t* h = reinterpret_cast<uint16_t*>(w + L.off_h);
-    float* pd = reinterpret_cast<float*>(w + L.off_pd);
-
-    // gate and up: one launch, blockIdx.z picks the matrix; always via partials
+    unsigned char* wsb = reinterpret_cast<unsigned char*>(ws);
+    float* pg = reinterpret_cast<float*>(wsb + L.off_pg);
+    float* pu = reinterpret_cast<float*>(wsb + L.off_pu);
+    uint8_t* hp = wsb + L.off_hp;
+    float* pd = reinterpret_cast<float*>(wsb + L.off_pd);
+    if ((rc = launch_x_pack(x, R, H, wsb, st))) return rc;
+    // gate and up: one launch (the item's matrix index picks one), via partials
     W4Args a{};
-    a.m[0] = W4Mat{gq, gs, gb, pg};
-    a.m[1] = W4Mat{uq, us, ub, pu};
-    a.x = x;
+    a.w[0] = reinterpret_cast<const uint8_t*>(w_gate);
+    a.w[1] = reinterpret_cast<const uint8_t*>(w_up);
+    a.out[0] = pg;
+    a.out[1] = pu;
+    a.xp = wsb;
     a.R = R;
-    a.K = H;
     a.N = I;
     a.split_stride = (long)16 * I;
-    if ((rc = launch_w4(a, 2, L.p1, G, st))) return rc;
+    if ((rc = launch_w4(a, 2, L.p1, H, G, st))) return rc;
     {
-        dim3 grid((unsigned)((I + 255) / 256), (unsigned)R);
-        hipLaunchKernelGGL(silu_reduce_kernel, grid, dim3(256), 0, st, pg, pu, L.p1.S, I, h, h_out);
+        const int groups = w4_chunks(I) * 16;
+        dim3 grid((unsigned)((groups + 63) / 64), 16);
+        hipLaunchKernelGGL(silu_reduce_kernel, grid, dim3(64), 0, st, pg, pu, L.p1.S, R, I, hp, h_out);
         if ((rc = check_hip(hipGetLastError(), "silu_reduce launch"))) return rc;
     }
-    // down
+    // down, reading the packed h
     W4Args d{};
-    d.m[0] = W4Mat{dq, ds, db, L.p2.S > 1 ? pd : y};
-    d.m[1] = d.m[0];
-    d.x = h;
+    d.w[0] = d.w[1] = reinterpret_cast<const uint8_t*>(w_down);
+    d.out[0] = d.out[1] = L.p2.S > 1 ? pd : y;
+    d.xp = hp;
     d.R = R;
-    d.K = I;
     d.N = H;
     d.split_stride = L.p2.S > 1 ? (long)16 * H : 0;
-    if ((rc = launch_w4(d, 1, L.p2, G, st))) return rc;
+    if ((rc = launch_w4(d, 1, L.p2, I, G, st))) return rc;
     if (L.p2.S > 1) {
         dim3 grid((unsigned)((H + 255) / 256), (unsigned)R);
-        hipLaunchKernelGGL(splitk_reduce_kernel, grid, dim3(256), 0, st, pd, L.p2.S, H, y);
+        hipLaunchKernelGGL(splitk_reduce_kernel, grid, dim3(64), 0, st, pd, L.p2.S, H, y);
         if ((rc = check_hip(hipGetLastError(), "splitk_reduce launch"))) return rc;
     }
     return EV_OK;

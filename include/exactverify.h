@@ -57,31 +57,49 @@ const char* ev_last_error(void);
 int32_t ev_version(void);
 
 /* ------------------------------------------------------------------------- */
+/* W4 weights: standard layout and the packed layout the kernels stream.     */
+/*                                                                            */
+/* Four-bit weights in groups of 32 or 64 with an affine dequantisation      */
+/* w[n][k] = s[n][k/G] * q[n][k] + b[n][k/G] (the "4-bit checkpoints" of the  */
+/* blog's "The numbers" section; the README's checkpoint list gives groups of */
+/* 64 and of 32).  Standard layout of an N x K matrix:                        */
+/*   q  [N][K/2] bytes: byte k/2 of row n holds q[n][k] in its low nibble     */
+/*      when k is even, its high nibble when k is odd;                        */
+/*   s, b [N][K/G] fp16.                                                      */
+/* w4_pack copies a matrix, once (at load), into the packed layout: tiles of  */
+/* 16 rows by chunks of 128 k, each tile-chunk holding its 1 KB of codes in   */
+/* the order the kernels' lanes read them, followed by its (scale, bias)      */
+/* pairs.  The copy is exact; rows and k beyond N and K are zero padding, so  */
+/* for N % 16 == 0 and K % 128 == 0 the packed bytes equal the standard ones. */
+/*   q (device, 4-byte aligned), s, b (device, 2-byte aligned): inputs.       */
+/*   packed (device, 16-byte aligned) of at least w4_packed_bytes(N, K, G).   */
+/* Limits: K > 0, K % G == 0, K % 32 == 0; N > 0; G in {32, 64}; packed size  */
+/* below 2^31 bytes.  Errors: EV_EINVAL, EV_EUNSUPPORTED, EV_EHIP.            */
+/* ------------------------------------------------------------------------- */
+size_t w4_packed_bytes(int32_t N, int32_t K, int32_t G);
+int32_t w4_pack(const uint8_t* q, const uint16_t* scale_f16, const uint16_t* bias_f16,
+                int32_t N, int32_t K, int32_t G, void* packed, size_t packed_bytes,
+                void* stream);
+
+/* ------------------------------------------------------------------------- */
 /* W4 verify linear.                                                          */
 /*                                                                            */
-/* y[r][n] = sum_k x[r][k] * (s[n][k/G] * q[n][k] + b[n][k/G]),  r < R, n < N. */
-/* Four-bit weights in groups of 32 or 64 with an affine dequantisation (the  */
-/* "4-bit checkpoints" the blog's "The numbers" section and the README's      */
-/* checkpoint list name; the README gives groups of 64 and of 32).            */
-/*                                                                            */
+/* y[r][n] = sum_k x[r][k] * (s[n][k/G] * q[n][k] + b[n][k/G]),  r < R, n < N, */
+/* for the R draft rows ("lanes") of one verify pass, which share one read of */
+/* the weights (blog, "The differentiator: byte-exact drafted decoding").    */
 /*   x_bf16   (device) [R][K] bf16, 16-byte aligned.                          */
-/*   q        (device) [N][K/2] bytes; byte k/2 of row n holds q[n][k] in its */
-/*            low nibble when k is even, its high nibble when k is odd.       */
-/*            16-byte aligned.                                                */
-/*   scale_f16, bias_f16 (device) [N][K/G] fp16.                              */
+/*   w_packed (device) the matrix as written by w4_pack, 16-byte aligned.     */
 /*   y        (device) [R][N] fp32, written.                                  */
 /*   ws       (device) workspace of at least verify_linear_w4_workspace(K,N,G) */
-/*            bytes (may be NULL when that is 0); contents are scratch.        */
-/* Limits: 1 <= R <= 16; K > 0, K % G == 0, K % 32 == 0; N > 0; G in {32, 64}. */
-/* Errors: EV_EINVAL (NULL/misaligned pointer, R or K or N out of range),      */
-/* EV_EUNSUPPORTED (G not 32 or 64), EV_EWORKSPACE, EV_EHIP.                   */
-/* Reduction order: fixed per (n) by (N, K, G) -- never by R.                 */
+/*            bytes, 256-byte aligned; contents are scratch.                  */
+/* Limits: 1 <= R <= 16 and those of w4_pack.  Errors: EV_EINVAL,             */
+/* EV_EUNSUPPORTED, EV_EWORKSPACE, EV_EHIP.                                   */
+/* Reduction order: fixed per n by (N, K, G) -- never by R.                   */
 /* ------------------------------------------------------------------------- */
 size_t verify_linear_w4_workspace(int32_t K, int32_t N, int32_t G);
-int32_t verify_linear_w4(const uint16_t* x_bf16, int32_t R, int32_t K,
-                         const uint8_t* q, const uint16_t* scale_f16,
-                         const uint16_t* bias_f16, int32_t N, int32_t G, float* y,
-                         void* ws, size_t ws_bytes, void* stream);
+int32_t verify_linear_w4(const uint16_t* x_bf16, int32_t R, int32_t K, const void* w_packed,
+                         int32_t N, int32_t G, float* y, void* ws, size_t ws_bytes,
+                         void* stream);
 
 /* ------------------------------------------------------------------------- */
 /* SiLU-gated MLP verify slice (dense).                                       */
@@ -89,16 +107,15 @@ int32_t verify_linear_w4(const uint16_t* x_bf16, int32_t R, int32_t K,
 /*   g = W_gate x, u = W_up x          (W4 linears H -> I, fp32 out)          */
 /*   h = bf16_rne(silu(g) * u),  silu(v) = v / (1 + e^-v)  (fp32)             */
 /*   y = W_down h                      (W4 linear I -> H, fp32 out)           */
-/* Each W4 linear is the one defined above.  Matrices use the layouts above:  */
-/* gate/up q [I][H/2], s/b [I][H/G]; down q [H][I/2], s/b [H][I/G].           */
-/*   h_bf16  (device, optional) [R][I] bf16: if non-NULL, h is also written.  */
+/* Each W4 linear is the one defined above; the three matrices are passed     */
+/* packed (gate and up I x H, down H x I).                                    */
+/*   h_bf16  (device, optional, 16-byte aligned) [R][I] bf16: if non-NULL, h  */
+/*           is also written there.                                           */
 /* Limits as verify_linear_w4 for both shapes.                                */
 /* ------------------------------------------------------------------------- */
 size_t verify_mlp_w4_workspace(int32_t H, int32_t I, int32_t G);
 int32_t verify_mlp_w4(const uint16_t* x_bf16, int32_t R, int32_t H, int32_t I, int32_t G,
-                      const uint8_t* gate_q, const uint16_t* gate_s, const uint16_t* gate_b,
-                      const uint8_t* up_q, const uint16_t* up_s, const uint16_t* up_b,
-                      const uint8_t* down_q, const uint16_t* down_s, const uint16_t* down_b,
+                      const void* gate_packed, const void* up_packed, const void* down_packed,
                       float* y, uint16_t* h_bf16, void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------- */

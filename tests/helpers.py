@@ -38,3 +38,10 @@ def row_rel_err(y, ref):
 def weights_dev(w):
     q, s, b = w
     return dev(q), dev(s), dev(b)
+
+
+def packed(w, G):
+    """Standard-layout numpy (q, s, b) -> PackedW4 on the device via w4_pack."""
+    import exact_speculative_decoding_amd as ev
+    q, s, b = weights_dev(w)
+    return ev.w4_pack(q, s, b, G)

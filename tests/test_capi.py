@@ -38,33 +38,48 @@ def test_every_declared_function_is_exported():
 def test_workspace_sizes_do_not_depend_on_rows():
     # the workspace functions take no R at all; check they are stable and sane
     assert ev.verify_linear_w4_workspace(256, 512, 64) >= 0
-    w = ev.verify_linear_w4_workspace(17408, 5120, 64)
-    assert w % (16 * 5120 * 4) == 0
+    assert ev.verify_linear_w4_workspace(17408, 5120, 64) > 16 * 5120 * 4
     assert ev.keyed_sample_workspace(151936) == 16 * 19 * 64 * 8
     assert ev.verify_mlp_w4_workspace(5120, 17408, 64) > 0
 
 
 def _lin(**kw):
-    a = dict(x=P, R=4, K=256, q=P, s=P, b=P, N=512, G=64, y=P, ws=None, nb=0)
+    a = dict(x=P, R=4, K=256, w=P, N=512, G=64, y=P, ws=P, nb=1 << 30)
     a.update(kw)
     L = ev.lib()
-    return L.verify_linear_w4(a["x"], a["R"], a["K"], a["q"], a["s"], a["b"], a["N"], a["G"],
-                              a["y"], a["ws"], a["nb"], None)
+    return L.verify_linear_w4(a["x"], a["R"], a["K"], a["w"], a["N"], a["G"], a["y"], a["ws"],
+                              a["nb"], None)
 
 
 @pytest.mark.parametrize("kw,code", [
     (dict(R=0), ev.EV_EINVAL), (dict(R=17), ev.EV_EINVAL), (dict(K=0), ev.EV_EINVAL),
     (dict(N=0), ev.EV_EINVAL), (dict(K=100), ev.EV_EINVAL), (dict(K=96, G=64), ev.EV_EINVAL),
     (dict(G=128), ev.EV_EUNSUPPORTED), (dict(G=16), ev.EV_EUNSUPPORTED),
-    (dict(x=None), ev.EV_EINVAL), (dict(q=None), ev.EV_EINVAL), (dict(y=None), ev.EV_EINVAL),
-    (dict(x=C.c_void_p(0x10002)), ev.EV_EINVAL), (dict(q=C.c_void_p(0x10008)), ev.EV_EINVAL),
-    (dict(K=17408, N=5120), ev.EV_EWORKSPACE),
+    (dict(x=None), ev.EV_EINVAL), (dict(w=None), ev.EV_EINVAL), (dict(y=None), ev.EV_EINVAL),
+    (dict(x=C.c_void_p(0x10002)), ev.EV_EINVAL), (dict(w=C.c_void_p(0x10008)), ev.EV_EINVAL),
+    (dict(ws=None), ev.EV_EWORKSPACE), (dict(nb=64), ev.EV_EWORKSPACE),
+    (dict(ws=C.c_void_p(0x10010)), ev.EV_EINVAL), (dict(K=1 << 20, N=1 << 14), ev.EV_EUNSUPPORTED),
 ])
 def test_linear_rejects_bad_arguments(kw, code):
-    if kw.get("K") == 17408:
-        assert ev.verify_linear_w4_workspace(17408, 5120, 64) > 0
     assert _lin(**kw) == code
     assert ev.lib().ev_last_error()
+
+
+@pytest.mark.parametrize("args,code", [
+    ((P, P, P, 0, 256, 64), ev.EV_EINVAL), ((P, P, P, 512, 100, 64), ev.EV_EINVAL),
+    ((P, P, P, 512, 256, 48), ev.EV_EUNSUPPORTED), ((None, P, P, 512, 256, 64), ev.EV_EINVAL),
+    ((C.c_void_p(0x10001), P, P, 512, 256, 64), ev.EV_EINVAL),
+])
+def test_pack_rejects_bad_arguments(args, code):
+    q, s, b, N, K, G = args
+    assert ev.lib().w4_pack(q, s, b, N, K, G, P, 1 << 30, None) == code
+    assert ev.lib().w4_pack(P, P, P, 512, 256, 64, P, 16, None) == ev.EV_EINVAL
+
+
+def test_packed_size_is_the_standard_size_when_aligned():
+    for N, K, G in ((17408, 5120, 64), (5120, 17408, 64), (768, 2048, 32), (151936, 5120, 64)):
+        assert ev.w4_packed_bytes(N, K, G) == N * K // 2 + 4 * N * (K // G)
+    assert ev.w4_packed_bytes(17, 96, 32) == 2 * 1 * (1024 + 256)
 
 
 def _samp(R=2, V=512, T=0.7, k=20, p=0.95, ws=P, nb=1 << 20, logits=P, pos=P, tok=P):
@@ -94,7 +109,6 @@ def test_accept_rejects_bad_arguments(R, D, draft, code):
 def test_binding_refuses_host_tensors():
     import torch
     x = torch.zeros(2, 256, dtype=torch.bfloat16)
-    q = torch.zeros(512, 128, dtype=torch.uint8)
-    s = torch.zeros(512, 4, dtype=torch.float16)
+    w = ev.PackedW4(torch.zeros(ev.w4_packed_bytes(512, 256, 64), dtype=torch.uint8), 512, 256, 64)
     with pytest.raises((ValueError, RuntimeError)):
-        ev.verify_linear_w4(x, q, s, s, 64, y=torch.zeros(2, 512))
+        ev.verify_linear_w4(x, w, y=torch.zeros(2, 512))

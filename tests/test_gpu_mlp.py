@@ -15,7 +15,7 @@ import torch
 import exact_speculative_decoding_amd as ev
 import oracle
 import synthetic as syn
-from helpers import ROW_REL_TOL, dev, host, row_rel_err, weights_dev
+from helpers import ROW_REL_TOL, dev, host, packed, row_rel_err
 
 pytestmark = pytest.mark.gpu
 
@@ -24,7 +24,7 @@ def _mlp(x, gate, up, down, G):
     R = x.shape[0]
     I = gate[0].shape[0]
     h = torch.empty((R, I), dtype=torch.int16, device="cuda")
-    y = ev.verify_mlp_w4(dev(x), weights_dev(gate), weights_dev(up), weights_dev(down), G, h=h)
+    y = ev.verify_mlp_w4(dev(x), packed(gate, G), packed(up, G), packed(down, G), h=h)
     return host(y), host(h).view(np.uint16)
 
 

@@ -9,7 +9,7 @@ import pytest
 import exact_speculative_decoding_amd as ev
 import oracle
 import synthetic as syn
-from helpers import NEAR_TIE, ROW_REL_TOL, dev, host, row_rel_err
+from helpers import NEAR_TIE, ROW_REL_TOL, dev, host, packed, row_rel_err
 
 pytestmark = pytest.mark.gpu
 
@@ -30,7 +30,7 @@ def test_tiny_round(R):
     ra, rn = oracle.accept(rt, draft)
     assert ra == min(2, R)
     # GPU
-    y = ev.verify_linear_w4(dev(x), dev(t["q"]), dev(t["s"]), dev(t["b"]), G)
+    y = ev.verify_linear_w4(dev(x), packed(w, G))
     assert np.all(row_rel_err(host(y), rl) <= ROW_REL_TOL)
     tok = ev.keyed_sample(y, dev(pos), t["T"], t["top_k"], t["top_p"], t["seed"])
     ht = host(tok)

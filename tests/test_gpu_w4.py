@@ -16,7 +16,7 @@ import torch
 import exact_speculative_decoding_amd as ev
 import oracle
 import synthetic as syn
-from helpers import ROW_REL_TOL, dev, host, row_rel_err
+from helpers import ROW_REL_TOL, dev, host, packed, row_rel_err
 
 pytestmark = pytest.mark.gpu
 
@@ -27,8 +27,7 @@ def _pack(qv):
 
 
 def _run(x, w, G):
-    q, s, b = w
-    return host(ev.verify_linear_w4(dev(x), dev(q), dev(s), dev(b), G))
+    return host(ev.verify_linear_w4(dev(x), packed(w, G)))
 
 
 @pytest.mark.parametrize("G", [32, 64])
@@ -87,14 +86,14 @@ def test_rows_bit_identical_to_single_row_calls(K, N, G):
     g = np.random.default_rng(5 + K + N)
     w = syn.w4_matrix(g, N, K, G)
     x = syn.activations(g, 16, K)
-    qd, sd, bd = dev(w[0]), dev(w[1]), dev(w[2])
+    wp = packed(w, G)
     xd = dev(x)
-    alone = np.stack([host(ev.verify_linear_w4(xd[r:r + 1].contiguous(), qd, sd, bd, G))[0]
+    alone = np.stack([host(ev.verify_linear_w4(xd[r:r + 1].contiguous(), wp))[0]
                       for r in range(16)])
     for R in range(1, 17):
-        y = host(ev.verify_linear_w4(xd[:R].contiguous(), qd, sd, bd, G))
+        y = host(ev.verify_linear_w4(xd[:R].contiguous(), wp))
         assert np.array_equal(y.view(np.uint32), alone[:R].view(np.uint32)), R
-    again = host(ev.verify_linear_w4(xd, qd, sd, bd, G))
+    again = host(ev.verify_linear_w4(xd, wp))
     assert np.array_equal(again.view(np.uint32), alone.view(np.uint32))
 
 
@@ -105,9 +104,9 @@ def test_full_size_sampled_columns(name, K, N):
     g = np.random.default_rng(1002 if name != "lm_head" else 1003)
     q, s, b = syn.w4_matrix(g, N, K, G)
     x = syn.activations(g, 16, K)
-    qd, sd, bd = dev(q), dev(s), dev(b)
+    wp = packed((q, s, b), G)
     xd = dev(x)
-    y16 = host(ev.verify_linear_w4(xd, qd, sd, bd, G))
+    y16 = host(ev.verify_linear_w4(xd, wp))
     cols = np.unique(np.concatenate([np.arange(0, N, N // 97), [N - 1, N - 2, 127, 128]]))
     ref = oracle.w4_linear(x, q[cols], s[cols], b[cols], G)
     err = row_rel_err(y16[:, cols], ref)
@@ -115,7 +114,7 @@ def test_full_size_sampled_columns(name, K, N):
     assert np.all(err <= 1e-5), err
     # rows of the R = 16 pass equal the rows of R = 1 passes, bitwise
     for r in (0, 7, 15):
-        y1 = host(ev.verify_linear_w4(xd[r:r + 1].contiguous(), qd, sd, bd, G))
+        y1 = host(ev.verify_linear_w4(xd[r:r + 1].contiguous(), wp))
         assert np.array_equal(y1[0].view(np.uint32), y16[r].view(np.uint32))
-    del qd, sd, bd
+    del wp
     torch.cuda.empty_cache()
