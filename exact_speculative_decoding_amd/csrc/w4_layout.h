@@ -12,10 +12,10 @@
 // exactly 0 to every output.  Without padding the blob has exactly the bytes
 // of the standard layout: N*K/2 + 4*N*K/G.
 //
-// Activations of a call are repacked per chunk and 32-k step into the MFMA A
-// fragments: xp[chunk][step][lane L][16 B] = the 8 bf16 x[ln][128 c + 32 st +
-// 8 j + i] in the order i = 0,4,1,5,2,6,3,7 (matching the nibble decode);
-// rows >= R and k >= K are 0.
+// Inside the kernel, the activations of a chunk are staged in LDS as MFMA A
+// fragments: [step][lane L][16 B] = the 8 bf16 x[ln][128 c + 32 st + 8 j + i]
+// in the order i = 0,4,1,5,2,6,3,7 (matching the nibble decode); rows >= R
+// and k >= K are 0.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -25,7 +25,7 @@
 namespace ev {
 
 constexpr int kKC = 128;         // k per chunk
-constexpr int kXChunkBytes = 4096;  // packed activations per chunk
+constexpr int kXChunkBytes = 4096;  // staged activations (A fragments) per chunk
 
 __host__ __device__ inline int w4_tiles(int N) { return (N + 15) / 16; }
 __host__ __device__ inline int w4_chunks(int K) { return (K + kKC - 1) / kKC; }
@@ -33,10 +33,9 @@ __host__ __device__ inline int w4_chunk_bytes(int G) { return 1024 + 64 * (kKC /
 __host__ __device__ inline size_t w4_blob_bytes(int N, int K, int G) {
     return (size_t)w4_tiles(N) * (size_t)w4_chunks(K) * (size_t)w4_chunk_bytes(G);
 }
-__host__ __device__ inline size_t w4_xpack_bytes(int K) { return (size_t)w4_chunks(K) * kXChunkBytes; }
 
 #ifndef EV_W4_CHUNK_MAJOR
-#define EV_W4_CHUNK_MAJOR 0
+#define EV_W4_CHUNK_MAJOR 1
 #endif
 // Byte offset of tile-chunk (tile, c) in the blob: tile-major (a tile's chunks
 // are adjacent) or chunk-major (a chunk's tiles are adjacent).

@@ -1,6 +1,6 @@
-// Exact repacking of W4 weights (once, at load) and of activations (per call)
-// into the layouts of w4_layout.h.  Pure data movement: every output value is
-// a copy of an input value or a padding zero.
+// Exact repacking of W4 weights (once, at load) into the layout of
+// w4_layout.h.  Pure data movement: every output value is a copy of an input
+// value or a padding zero.
 #include "ev_internal.h"
 #include "w4_layout.h"
 
@@ -43,33 +43,6 @@ __global__ void w4_pack_kernel(const uint8_t* __restrict__ q, const uint16_t* __
             *reinterpret_cast<uint32_t*>(dst + 1024 + 4 * (ln * GPC + g)) = v;
         }
     }
-}
-
-// One thread per (chunk, step, lane): 8 bf16 of row ln, reordered.
-__global__ void x_pack_kernel(const uint16_t* __restrict__ x, int R, int K, uint8_t* __restrict__ out) {
-    const long total = (long)w4_chunks(K) * 256;
-    const long gid = (long)blockIdx.x * blockDim.x + threadIdx.x;
-    if (gid >= total) return;
-    const int L = (int)(gid & 63);
-    const int st = (int)((gid >> 6) & 3);
-    const int c = (int)(gid >> 8);
-    const int ln = L & 15, j = L >> 4;
-    const int k = kKC * c + 32 * st + 8 * j;
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (ln < R && k < K) v = *reinterpret_cast<const u32x4*>(x + (size_t)ln * K + k);
-    u32x4 o;
-    o[0] = __builtin_amdgcn_perm(v[2], v[0], 0x05040100u);
-    o[1] = __builtin_amdgcn_perm(v[2], v[0], 0x07060302u);
-    o[2] = __builtin_amdgcn_perm(v[3], v[1], 0x05040100u);
-    o[3] = __builtin_amdgcn_perm(v[3], v[1], 0x07060302u);
-    *reinterpret_cast<u32x4*>(out + 16 * gid) = o;
-}
-
-int32_t launch_x_pack(const uint16_t* x, int R, int K, void* out, hipStream_t st) {
-    const long total = (long)w4_chunks(K) * 256;
-    hipLaunchKernelGGL(x_pack_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, x, R, K,
-                       reinterpret_cast<uint8_t*>(out));
-    return check_hip(hipGetLastError(), "x_pack launch");
 }
 
 int32_t check_w4_dims(const char* who, int K, int N, int G) {

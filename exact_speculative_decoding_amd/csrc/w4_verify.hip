@@ -12,12 +12,15 @@
 // the split of K over waves, and therefore every reduction order, is a
 // function of (N, K, G) only.
 //
-// Kernel shape: every wave is an independent work item (no LDS, no barriers):
-// kNT tiles of 16 output rows over one K-split of `cps` chunks of 128 k, on the
-// packed layouts of w4_layout.h.
+// Kernel shape: a workgroup of 4 waves shares one K-split of `cps` chunks of
+// 128 k; each wave owns kNT tiles of 16 output rows, on the packed weight
+// layout of w4_layout.h.
 //   * per chunk and tile one contiguous 1 KB load gives the B fragments of the
-//     four 32-k MFMA steps, and one 8/16 B load the (scale, bias) pairs; per
-//     step one contiguous 1 KB load gives the A fragment (16 activation rows);
+//     four 32-k MFMA steps, and one 8/16 B load the (scale, bias) pairs;
+//   * the activations of 4 chunks (a 512-k superchunk) are loaded once per
+//     workgroup, 1 KB of one row per wave load, reordered into MFMA A fragments
+//     on the way into a double-buffered LDS slab, and read back with
+//     conflict-free ds_read_b128 (one barrier per superchunk);
 //   * nibbles decode exactly into bf16 as 16 + q (0x4180 | q << 3: a shift and
 //     an and-or per pair); one more MFMA against an all-ones B gives the group
 //     sum xs of every row, and the fold is p += s * acc + (b - 16 s) * xs into
@@ -35,7 +38,7 @@
 #include "w4_layout.h"
 
 #ifndef EV_W4_NT
-#define EV_W4_NT 4  // 16-row tiles per wave
+#define EV_W4_NT 2  // 16-row tiles per wave
 #endif
 #ifndef EV_W4_PD
 #define EV_W4_PD 2  // chunks of loads in flight per wave
@@ -49,13 +52,14 @@
 
 namespace ev {
 
-int32_t launch_x_pack(const uint16_t* x, int R, int K, void* out, hipStream_t st);
 int32_t check_w4_dims(const char* who, int K, int N, int G);
 
 constexpr int kThreads = 256;  // 4 independent waves per workgroup
 constexpr int kNT = EV_W4_NT;
 constexpr int kPD = EV_W4_PD;
 constexpr uint32_t kOOB = 0x80000000u;  // per-lane offset beyond every buffer: reads 0
+constexpr int kSC = 4;                   // chunks per activation superchunk (512 k)
+constexpr int kSlab = kSC * kXChunkBytes;  // LDS bytes of one superchunk of activations
 
 struct W4Plan {
     int S;        // K-splits
@@ -77,18 +81,19 @@ static W4Plan plan_w4(int N, int K, int nmat) {
     if (S > smax) S = smax;
     if (S < 1) S = 1;
     p.cps = (int)((p.nchunks + S - 1) / S);
+    p.cps = (p.cps + kSC - 1) / kSC * kSC;  // splits start on superchunk boundaries
     p.S = (p.nchunks + p.cps - 1) / p.cps;
     p.items = base * p.S;
     return p;
 }
 
 struct W4Args {
-    const uint8_t* w[2];  // packed weights; the item's matrix index picks one
+    const uint8_t* w[2];  // packed weights; the workgroup's matrix index picks one
     float* out[2];        // split s writes rows at out + s * split_stride
-    const uint8_t* xp;    // packed activations
-    int R, N, nchunks, tiles;
-    int cps, S, ncg;
-    long items;
+    const uint16_t* x;    // activations [R][K] bf16
+    int R, K, N, nchunks, tiles;
+    int cps, S, ncg, ncgb;  // ncgb: workgroups per (matrix, split)
+    long blocks;
     long split_stride;
     uint32_t wbytes, xbytes;
     // nibble-decode constants, passed as arguments so that they sit in
@@ -129,23 +134,26 @@ __global__ __launch_bounds__(kThreads) void w4_verify_kernel(W4Args a) {
     constexpr int GPC = kKC / G;                // groups per chunk
     constexpr int SBW = GPC;                    // (scale, bias) dwords per lane per chunk
     constexpr uint32_t CB = 1024 + 64 * GPC;    // packed bytes per tile-chunk
-    const int lane = threadIdx.x & 63;
-    // wave-uniform work item (readfirstlane keeps it, the matrix and the buffer
+    static_assert(kSC % kPD == 0, "ring depth must divide the superchunk");
+    __shared__ __align__(16) uint8_t xlds[2][kSlab];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    // wave-uniform indices (readfirstlane keeps them, the matrix and the buffer
     // descriptors in scalar registers)
-    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-    const long item = (long)blockIdx.x * (kThreads / 64) + wave;
-    if (item >= a.items) return;  // whole wave
-    const int ln = lane & 15, j = lane >> 4;
-    const int cg = (int)(item % a.ncg);
-    const long rest = item / a.ncg;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const long blk = blockIdx.x;
+    const int cgb = (int)(blk % a.ncgb);
+    const long rest = blk / a.ncgb;
     const int split = (int)(rest % a.S);
     const int mi = (int)(rest / a.S);
-    const int c0 = split * a.cps;
+    const int cg = cgb * 4 + wave;  // a wave past the last tile group computes zeros
+    const int c0 = split * a.cps;   // a multiple of kSC
     const int c1 = min(a.nchunks, c0 + a.cps);
+    const int ln = lane & 15, j = lane >> 4;
 
     const rsrc_t rw = make_rsrc(a.w[mi], a.wbytes);
-    const rsrc_t rx = make_rsrc(a.xp, a.xbytes);
-    // tile bases are wave-uniform; a tile past the last one reads zeros
+    const rsrc_t rx = make_rsrc(a.x, a.xbytes);
     uint32_t tbase[kNT];
     bool tok[kNT];
 #pragma unroll
@@ -158,7 +166,6 @@ __global__ __launch_bounds__(kThreads) void w4_verify_kernel(W4Args a) {
     const uint32_t cstride = EV_W4_CHUNK_MAJOR ? (uint32_t)a.tiles * CB : CB;  // bytes per chunk step
     const uint32_t vq = 16u * lane;
     const uint32_t vsb = 1024u + 4u * GPC * ln;
-    const uint32_t vx = 16u * lane;
     // the mask stays scalar, the or-constant goes to a vector register: gfx9
     // VALU ops read at most one scalar operand, and this lets each decoded pair
     // be one v_and_or_b32
@@ -166,15 +173,43 @@ __global__ __launch_bounds__(kThreads) void w4_verify_kernel(W4Args a) {
     uint32_t doff;
     asm volatile("v_mov_b32 %0, %1" : "=v"(doff) : "s"(a.doff));
 
-    // register ring of kPD chunks
-    u32x4 qr[kPD][kNT];
-    uint32_t sbr[kPD][kNT][SBW];
-    u32x4 xr[kPD][4];
+    // ---- activations: one superchunk = 4 chunks = 512 k of the 16 rows.
+    // Thread tid loads 16 B of row wave + 4 m (m = 0..3) at k = 512 sc + 8 (tid % 64):
+    // one wave load is 1 KB of one row.  Rows >= R and k >= K read zeros.
+    const int col = tid & 63;
+    const int xc = col >> 4, xst = (col >> 2) & 3, xj = col & 3;
+    u32x4 xin[4];
+    auto xload = [&](int sc) {
+        const int k = sc * (kSC * kKC) + 8 * col;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const int r = wave + 4 * m;
+            const bool ok = r < a.R && k < a.K;
+            xin[m] = bload128(rx, ok ? (uint32_t)(r * a.K + k) * 2u : kOOB, 0u);
+        }
+    };
+    // reorder (x0,x4) (x1,x5) (x2,x6) (x3,x7) and store as the A fragment of
+    // lane r + 16 xj of step xst of chunk xc
+    auto xstore = [&](int buf) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const int r = wave + 4 * m;
+            const u32x4 v = xin[m];
+            u32x4 o;
+            o[0] = __builtin_amdgcn_perm(v[2], v[0], 0x05040100u);
+            o[1] = __builtin_amdgcn_perm(v[2], v[0], 0x07060302u);
+            o[2] = __builtin_amdgcn_perm(v[3], v[1], 0x05040100u);
+            o[3] = __builtin_amdgcn_perm(v[3], v[1], 0x07060302u);
+            *reinterpret_cast<u32x4*>(&xlds[buf][(size_t)((xc * 4 + xst) * 64 + r + 16 * xj) * 16]) = o;
+        }
+    };
 
-    // Loads of chunk c into ring slot `slot`.  Offsets within the chunk are
+    // ---- weights: register ring of kPD chunks.  Offsets within the chunk are
     // per-lane constants, the chunk and tile offsets a scalar; chunks at or past
     // c1 (and tiles past the last) get an out-of-range per-lane offset, so
     // every slot is written on every path and the ring never has to be copied.
+    u32x4 qr[kPD][kNT];
+    uint32_t sbr[kPD][kNT][SBW];
     auto fetch = [&](int c, int slot) {
         const bool live = c < c1;
 #pragma unroll
@@ -192,9 +227,6 @@ __global__ __launch_bounds__(kThreads) void w4_verify_kernel(W4Args a) {
                 for (int g = 0; g < SBW; ++g) sbr[slot][t][g] = v[g & 3];
             }
         }
-        const uint32_t sx = (uint32_t)c * kXChunkBytes;
-#pragma unroll
-        for (int st = 0; st < 4; ++st) xr[slot][st] = bload128(rx, live ? vx + 1024u * st : kOOB, sx);
     };
 
     const u32x4 ones = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
@@ -206,14 +238,15 @@ __global__ __launch_bounds__(kThreads) void w4_verify_kernel(W4Args a) {
     // tile; per group, p += s * acc + (b - 16 s) * xs into a chunk partial p,
     // which is added to y once per chunk.  A chunk that was loaded as zeros
     // (past c1) adds exactly zero.
-    auto compute = [&](int slot) {
+    auto compute = [&](int slot, const uint8_t* xchunk) {
         f32x4 acc[kNT], part[kNT], xs = {0.f, 0.f, 0.f, 0.f};
         const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int t = 0; t < kNT; ++t) part[t] = zero;
 #pragma unroll
         for (int st = 0; st < 4; ++st) {
-            const bf16x8 A = __builtin_bit_cast(bf16x8, xr[slot][st]);
+            const u32x4 xa = *reinterpret_cast<const u32x4*>(xchunk + (size_t)(st * 64 + lane) * 16);
+            const bf16x8 A = __builtin_bit_cast(bf16x8, xa);
             const bool first = (G == 32) || ((st & 1) == 0);
             xs = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, __builtin_bit_cast(bf16x8, ones),
                                                         first ? zero : xs, 0, 0, 0);
@@ -242,23 +275,39 @@ __global__ __launch_bounds__(kThreads) void w4_verify_kernel(W4Args a) {
         for (int t = 0; t < kNT; ++t) y[t] += part[t];
     };
 
-    // Straight-line ring: every slot is computed and refilled on every trip
-    // (the trip count is cps rounded up to kPD).  sched_barrier keeps each
-    // refill where it is written, so the loads of the other ring slots stay in
-    // flight across the compute of this one.
+    // Prologue: superchunk 0 of the split into LDS slab 0, the first kPD
+    // chunks of weights in flight, superchunk 1 in registers.
+    const int sc0 = c0 / kSC;
+    xload(sc0);
+    xstore(0);
 #pragma unroll
     for (int p = 0; p < kPD; ++p) {
         __builtin_amdgcn_sched_barrier(0);
         fetch(c0 + p, p);
     }
-    for (int cb = c0; cb < c1; cb += kPD) {
+    __builtin_amdgcn_sched_barrier(0);
+    xload(sc0 + 1);
+    __syncthreads();
+
+    // Main loop over superchunks: 4 chunks of compute on slab `buf`, each
+    // refilling its ring slot; then the next superchunk's activations go to
+    // the other slab, the one after is loaded, and the workgroup syncs.
+    // sched_barrier keeps each refill where it is written, so the loads of the
+    // other ring slots stay in flight across the compute of this one.
+    int buf = 0;
+    for (int cb = c0; cb < c1; cb += kSC) {
 #pragma unroll
-        for (int p = 0; p < kPD; ++p) {
+        for (int p = 0; p < kSC; ++p) {
             __builtin_amdgcn_sched_barrier(0);
-            compute(p);
+            compute(p % kPD, &xlds[buf][(size_t)p * kXChunkBytes]);
             __builtin_amdgcn_sched_barrier(0);
-            fetch(cb + p + kPD, p);
+            fetch(cb + p + kPD, p % kPD);
         }
+        __builtin_amdgcn_sched_barrier(0);
+        xstore(buf ^ 1);
+        xload(cb / kSC + 2);
+        __syncthreads();
+        buf ^= 1;
     }
     __builtin_amdgcn_sched_barrier(0);
 
@@ -267,7 +316,7 @@ __global__ __launch_bounds__(kThreads) void w4_verify_kernel(W4Args a) {
 #pragma unroll
     for (int t = 0; t < kNT; ++t) {
         const int n = (cg * kNT + t) * 16 + ln;
-        if (n < a.N) {
+        if (tok[t] && n < a.N) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = 4 * j + i;
@@ -303,57 +352,41 @@ __global__ __launch_bounds__(64) void splitk_reduce_kernel(const float* __restri
     }
 }
 
-// g, u = split sums (ascending s); h = bf16_rne(silu(g) * u).  One thread per
-// 8 consecutive k of one of the 16 rows: writes the 16 B of the down
-// projection's packed activations (rows >= R and k >= I as zeros) and, when
-// asked, h in the standard [R][I] layout.
+// g, u = split sums (ascending s); h = bf16_rne(silu(g) * u) for rows < R.
+// One thread per 8 consecutive k of one row; h is written to `h` (the down
+// projection's input) and, when asked, to `h_copy`.
 __global__ __launch_bounds__(64) void silu_reduce_kernel(const float* __restrict__ pg,
-                                                         const float* __restrict__ pu, int S, int R,
-                                                         int I, uint8_t* __restrict__ hp,
-                                                         uint16_t* __restrict__ h_out) {
-    const int NC = w4_chunks(I);
-    const int m = blockIdx.x * 64 + threadIdx.x;  // 8-element group of the padded row
+                                                         const float* __restrict__ pu, int S, int I,
+                                                         uint16_t* __restrict__ h,
+                                                         uint16_t* __restrict__ h_copy) {
+    const int m = blockIdx.x * 64 + threadIdx.x;  // I % 32 == 0: groups of 8 never straddle rows
     const int r = blockIdx.y;
-    if (m >= NC * 16) return;
-    const int k0 = 8 * m;
+    if (8 * m >= I) return;
+    const size_t stride = (size_t)16 * I;
+    const size_t o = (size_t)r * I + 8 * m;
+    f32x4 g0 = *reinterpret_cast<const f32x4*>(pg + o), g1 = *reinterpret_cast<const f32x4*>(pg + o + 4);
+    f32x4 u0 = *reinterpret_cast<const f32x4*>(pu + o), u1 = *reinterpret_cast<const f32x4*>(pu + o + 4);
+#pragma unroll 4
+    for (int sp = 1; sp < S; ++sp) {
+        const size_t so = sp * stride + o;
+        g0 += *reinterpret_cast<const f32x4*>(pg + so);
+        g1 += *reinterpret_cast<const f32x4*>(pg + so + 4);
+        u0 += *reinterpret_cast<const f32x4*>(pu + so);
+        u1 += *reinterpret_cast<const f32x4*>(pu + so + 4);
+    }
     uint16_t hv[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) hv[i] = 0;
-    if (r < R && k0 < I) {  // I % 32 == 0, so all 8 are inside the row
-        const size_t stride = (size_t)16 * I;
-        const size_t o = (size_t)r * I + k0;
-        f32x4 g0 = *reinterpret_cast<const f32x4*>(pg + o), g1 = *reinterpret_cast<const f32x4*>(pg + o + 4);
-        f32x4 u0 = *reinterpret_cast<const f32x4*>(pu + o), u1 = *reinterpret_cast<const f32x4*>(pu + o + 4);
-#pragma unroll 4
-        for (int sp = 1; sp < S; ++sp) {
-            const size_t so = sp * stride + o;
-            g0 += *reinterpret_cast<const f32x4*>(pg + so);
-            g1 += *reinterpret_cast<const f32x4*>(pg + so + 4);
-            u0 += *reinterpret_cast<const f32x4*>(pu + so);
-            u1 += *reinterpret_cast<const f32x4*>(pu + so + 4);
-        }
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const float g = i < 4 ? g0[i] : g1[i - 4];
-            const float u = i < 4 ? u0[i] : u1[i - 4];
-            const float sg = g / (1.0f + expf(-g));
-            hv[i] = f32_to_bf16_rne(sg * u);
-        }
-        if (h_out) {
-            u32x4 w;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) w[i] = (uint32_t)hv[2 * i] | ((uint32_t)hv[2 * i + 1] << 16);
-            *reinterpret_cast<u32x4*>(h_out + o) = w;
-        }
+    for (int i = 0; i < 8; ++i) {
+        const float g = i < 4 ? g0[i] : g1[i - 4];
+        const float u = i < 4 ? u0[i] : u1[i - 4];
+        const float sg = g / (1.0f + expf(-g));
+        hv[i] = f32_to_bf16_rne(sg * u);
     }
-    // packed position: chunk c, step st, lane r + 16 j; order 0,4,1,5,2,6,3,7
-    const int c = k0 / kKC, st = (k0 % kKC) / 32, j = (k0 % 32) / 8;
-    u32x4 pw;
-    pw[0] = (uint32_t)hv[0] | ((uint32_t)hv[4] << 16);
-    pw[1] = (uint32_t)hv[1] | ((uint32_t)hv[5] << 16);
-    pw[2] = (uint32_t)hv[2] | ((uint32_t)hv[6] << 16);
-    pw[3] = (uint32_t)hv[3] | ((uint32_t)hv[7] << 16);
-    *reinterpret_cast<u32x4*>(hp + (size_t)c * kXChunkBytes + 1024 * st + 16 * (r + 16 * j)) = pw;
+    u32x4 w;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = (uint32_t)hv[2 * i] | ((uint32_t)hv[2 * i + 1] << 16);
+    *reinterpret_cast<u32x4*>(h + o) = w;
+    if (h_copy) *reinterpret_cast<u32x4*>(h_copy + o) = w;
 }
 
 // Measurement hook: when on, each W4 kernel launch is bracketed by HIP events
@@ -372,17 +405,19 @@ static double w4_algo_bytes(int nmat, int R, int K, int N, int G) {
 }
 
 static int32_t launch_w4(W4Args args, int nmat, const W4Plan& p, int K, int G, hipStream_t st) {
+    args.K = K;
     args.nchunks = p.nchunks;
     args.tiles = w4_tiles(args.N);
     args.cps = p.cps;
     args.S = p.S;
     args.ncg = p.ncg;
-    args.items = p.items;
+    args.ncgb = (p.ncg + 3) / 4;
+    args.blocks = (long)nmat * p.S * args.ncgb;
     args.wbytes = (uint32_t)w4_blob_bytes(args.N, K, G);
-    args.xbytes = (uint32_t)w4_xpack_bytes(K);
+    args.xbytes = (uint32_t)((size_t)args.R * K * 2);
     args.dmask = 0x00780078u;
     args.doff = 0x41804180u;
-    const unsigned blocks = (unsigned)((p.items + 3) / 4);
+    const unsigned blocks = (unsigned)args.blocks;
     hipEvent_t ea = nullptr, eb = nullptr;
     bool timed;
     {
@@ -409,34 +444,32 @@ static int32_t launch_w4(W4Args args, int nmat, const W4Plan& p, int K, int G, h
 
 static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
-// Workspace of verify_linear_w4: packed x, then split partials [S][16][N].
+// Workspace of verify_linear_w4: split partials [S][16][N] (none if S == 1).
 struct LinLayout {
     W4Plan p;
-    size_t off_part, total;
+    size_t total;
 };
 static LinLayout lin_layout(int K, int N) {
     LinLayout L;
     L.p = plan_w4(N, K, 1);
-    L.off_part = align256(w4_xpack_bytes(K));
-    L.total = L.off_part + (L.p.S > 1 ? (size_t)L.p.S * 16 * N * sizeof(float) : 0);
+    L.total = L.p.S > 1 ? (size_t)L.p.S * 16 * N * sizeof(float) : 0;
     return L;
 }
 
-// Workspace of the MLP slice: packed x, gate and up partials [S1][16][I],
-// packed h, down partials [S2][16][H] (if S2 > 1).
+// Workspace of the MLP slice: gate and up partials [S1][16][I], h [16][I]
+// bf16, down partials [S2][16][H] (if S2 > 1).
 struct MlpLayout {
     W4Plan p1, p2;
-    size_t off_pg, off_pu, off_hp, off_pd, total;
+    size_t off_pu, off_h, off_pd, total;
 };
 static MlpLayout mlp_layout(int H, int I) {
     MlpLayout L;
     L.p1 = plan_w4(I, H, 2);
     L.p2 = plan_w4(H, I, 1);
-    L.off_pg = align256(w4_xpack_bytes(H));
     const size_t part1 = align256((size_t)L.p1.S * 16 * I * sizeof(float));
-    L.off_pu = L.off_pg + part1;
-    L.off_hp = L.off_pu + part1;
-    L.off_pd = L.off_hp + align256(w4_xpack_bytes(I));
+    L.off_pu = part1;
+    L.off_h = 2 * part1;
+    L.off_pd = L.off_h + align256((size_t)16 * I * sizeof(uint16_t));
     L.total = L.off_pd + (L.p2.S > 1 ? (size_t)L.p2.S * 16 * H * sizeof(float) : 0);
     return L;
 }
@@ -506,13 +539,11 @@ extern "C" int32_t verify_linear_w4(const uint16_t* x, int32_t R, int32_t K, con
     const LinLayout L = lin_layout(K, N);
     if ((rc = check_ws(who, ws, ws_bytes, L.total))) return rc;
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-    unsigned char* wsb = reinterpret_cast<unsigned char*>(ws);
-    if ((rc = launch_x_pack(x, R, K, wsb, st))) return rc;
-    float* part = reinterpret_cast<float*>(wsb + L.off_part);
+    float* part = reinterpret_cast<float*>(ws);
     W4Args a{};
     a.w[0] = a.w[1] = reinterpret_cast<const uint8_t*>(w);
     a.out[0] = a.out[1] = L.p.S > 1 ? part : y;
-    a.xp = wsb;
+    a.x = x;
     a.R = R;
     a.N = N;
     a.split_stride = L.p.S > 1 ? (long)16 * N : 0;
@@ -547,33 +578,31 @@ extern "C" int32_t verify_mlp_w4(const uint16_t* x, int32_t R, int32_t H, int32_
     if ((rc = check_ws(who, ws, ws_bytes, L.total))) return rc;
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     unsigned char* wsb = reinterpret_cast<unsigned char*>(ws);
-    float* pg = reinterpret_cast<float*>(wsb + L.off_pg);
+    float* pg = reinterpret_cast<float*>(wsb);
     float* pu = reinterpret_cast<float*>(wsb + L.off_pu);
-    uint8_t* hp = wsb + L.off_hp;
+    uint16_t* h = reinterpret_cast<uint16_t*>(wsb + L.off_h);
     float* pd = reinterpret_cast<float*>(wsb + L.off_pd);
-    if ((rc = launch_x_pack(x, R, H, wsb, st))) return rc;
     // gate and up: one launch (the item's matrix index picks one), via partials
     W4Args a{};
     a.w[0] = reinterpret_cast<const uint8_t*>(w_gate);
     a.w[1] = reinterpret_cast<const uint8_t*>(w_up);
     a.out[0] = pg;
     a.out[1] = pu;
-    a.xp = wsb;
+    a.x = x;
     a.R = R;
     a.N = I;
     a.split_stride = (long)16 * I;
     if ((rc = launch_w4(a, 2, L.p1, H, G, st))) return rc;
     {
-        const int groups = w4_chunks(I) * 16;
-        dim3 grid((unsigned)((groups + 63) / 64), 16);
-        hipLaunchKernelGGL(silu_reduce_kernel, grid, dim3(64), 0, st, pg, pu, L.p1.S, R, I, hp, h_out);
+        dim3 grid((unsigned)((I / 8 + 63) / 64), (unsigned)R);
+        hipLaunchKernelGGL(silu_reduce_kernel, grid, dim3(64), 0, st, pg, pu, L.p1.S, I, h, h_out);
         if ((rc = check_hip(hipGetLastError(), "silu_reduce launch"))) return rc;
     }
     // down, reading the packed h
     W4Args d{};
     d.w[0] = d.w[1] = reinterpret_cast<const uint8_t*>(w_down);
     d.out[0] = d.out[1] = L.p2.S > 1 ? pd : y;
-    d.xp = hp;
+    d.x = h;
     d.R = R;
     d.N = H;
     d.split_stride = L.p2.S > 1 ? (long)16 * H : 0;

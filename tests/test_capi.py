@@ -57,10 +57,13 @@ def _lin(**kw):
     (dict(G=128), ev.EV_EUNSUPPORTED), (dict(G=16), ev.EV_EUNSUPPORTED),
     (dict(x=None), ev.EV_EINVAL), (dict(w=None), ev.EV_EINVAL), (dict(y=None), ev.EV_EINVAL),
     (dict(x=C.c_void_p(0x10002)), ev.EV_EINVAL), (dict(w=C.c_void_p(0x10008)), ev.EV_EINVAL),
-    (dict(ws=None), ev.EV_EWORKSPACE), (dict(nb=64), ev.EV_EWORKSPACE),
-    (dict(ws=C.c_void_p(0x10010)), ev.EV_EINVAL), (dict(K=1 << 20, N=1 << 14), ev.EV_EUNSUPPORTED),
+    (dict(K=17408, N=5120, ws=None), ev.EV_EWORKSPACE), (dict(K=17408, N=5120, nb=64), ev.EV_EWORKSPACE),
+    (dict(K=17408, N=5120, ws=C.c_void_p(0x10010)), ev.EV_EINVAL),
+    (dict(K=1 << 20, N=1 << 14), ev.EV_EUNSUPPORTED),
 ])
 def test_linear_rejects_bad_arguments(kw, code):
+    if "ws" in kw or "nb" in kw:  # these cases must need a workspace, or the call would launch
+        assert ev.verify_linear_w4_workspace(kw["K"], kw["N"], 64) > 64
     assert _lin(**kw) == code
     assert ev.lib().ev_last_error()
 
