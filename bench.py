@@ -39,6 +39,11 @@ def parse():
     ap.add_argument("--copies", type=int, default=4, help="weight copies rotated per step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay each step from a captured HIP graph (checked against eager)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain device copy of 512 MiB five times (the known-size "
+                         "reference for scaling the FETCH_SIZE / WRITE_SIZE counters)")
     return ap.parse_args()
 
 
@@ -103,6 +108,17 @@ def main():
     torch.cuda.set_device(0)
     dev = torch.device("cuda:0")
 
+    if args.calibrate_copy:
+        n = 512 << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration": "device copy", "bytes_read": n, "bytes_written": n,
+                          "launches": 5}), flush=True)
+        return
+
     d = syn.mlp()
     H, I, G = d["H"], d["I"], d["G"]
 
@@ -124,11 +140,34 @@ def main():
     x_all = to_dev(d["x"])
     ws = torch.empty(ev.verify_mlp_w4_workspace(H, I, G), dtype=torch.uint8, device=dev)
     y = torch.empty((16, H), dtype=torch.float32, device=dev)
-    stream = torch.cuda.current_stream()
+    stream = torch.cuda.Stream() if args.graph else torch.cuda.current_stream()
 
-    def step(i, R):
+    def eager(i, R):
         gate, up, down = copies[i % len(copies)]
         ev.verify_mlp_w4(x_all[:R], gate, up, down, y=y[:R], ws=ws, stream=stream)
+
+    graphs = {}
+
+    def step(i, R):
+        if not args.graph:
+            return eager(i, R)
+        key = (i % len(copies), R)
+        if key not in graphs:
+            # capture on a side stream, then check that replays reproduce eager bits
+            eager(i, R)
+            torch.cuda.synchronize()
+            ref = y[:R].clone()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                eager(i, R)
+            for _ in range(3):
+                y.zero_()
+                g.replay()
+                torch.cuda.synchronize()
+                if not torch.equal(y[:R].view(torch.int32), ref.view(torch.int32)):
+                    raise RuntimeError("graph replay differs from eager")
+            graphs[key] = g
+        graphs[key].replay()
 
     def timed(R, steps, warmup):
         for i in range(warmup):
@@ -143,6 +182,7 @@ def main():
         return e0.elapsed_time(e1) / steps
 
     R = args.R
+    torch.cuda.set_stream(stream)
     ms = timed(R, args.steps, args.warmup)
     gbs = mlp_bytes(R, H, I, G) / (ms * 1e-3) / 1e9
     print(f"# R={R}: {ms * 1e3:.1f} us/step, {gbs:.0f} GB/s", file=sys.stderr, flush=True)
@@ -163,7 +203,7 @@ def main():
     ev.w4_timing_read()
     ev.w4_timing(True)
     for i in range(args.steps):
-        step(i, R)
+        eager(i, R)
     torch.cuda.synchronize()
     ev.w4_timing(False)
     n_launch, k_ms, k_bytes = ev.w4_timing_read()
@@ -182,7 +222,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": "dense 27B-class MLP verify slice: gate/up W4 5120->17408, "
                                "SiLU*up, down W4 17408->5120, group 64",
-                   "R": R, "H": H, "I": I, "G": G, "weight_copies": args.copies,
+                   "R": R, "launch": "hip graph replay" if args.graph else "eager", "H": H, "I": I, "G": G, "weight_copies": args.copies,
                    "weight_bytes_per_copy": int(mlp_bytes(0, H, I, G))},
         "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "lanes_per_s": round(R / (ms * 1e-3), 1),
