@@ -3,9 +3,9 @@
 
 Workload (one "step"): the dense 27B-class MLP verify slice -- gate/up W4
 5120 -> 17408, SiLU * up, down W4 17408 -> 5120, group 64 -- over R = 16 draft
-lanes, through the library's verify_mlp_w4 entry point (activation pack, W4
-kernel for gate+up, split reduce fused with SiLU * up, W4 kernel for down,
-split reduce).  The weights are packed once at load (w4_pack, an exact byte
+lanes, through the library's verify_mlp_w4 entry point (W4 kernel for gate and
+up in one launch, split reduce fused with SiLU * up, W4 kernel for down, split
+reduce).  The weights are packed once at load (w4_pack, an exact byte
 reordering with the same byte count), outside the timed region, like any
 model load; inputs are resident in HBM before timing; the weights rotate over
 several copies (> 2 x 256 MB in total) so the 256 MB Infinity Cache cannot
@@ -13,8 +13,13 @@ serve them.
 
 Printed: one JSON line with the metric (algorithmic HBM GB/s of the verify
 pass), the per-R sweep (R = 1, 2, 4, 8, 16), the dominant kernel's roofline
-(W4 kernel, measured with HIP events on its own stream) and the CPU oracle's
-time on a bounded sample of the same workload.
+and the CPU oracle's time on a bounded sample of the same workload.  The step
+time comes from HIP events recorded on the stream the path runs on, around
+the whole timed region.  The W4 kernel's launch duration comes from the
+library's timing hook: each workgroup stamps the device wall clock at its
+start and at its end, and a launch lasts from its first start to its last end
+(HIP events around single launches add the event packets' own overhead, about
+a quarter of a 20 us launch).
 """
 import argparse
 import hashlib
@@ -197,8 +202,8 @@ def main():
                              "lanes_per_s": round(r / (m * 1e-3), 1)}
             print(f"# R={r}: {m * 1e3:.1f} us/pass, {g:.0f} GB/s", file=sys.stderr, flush=True)
 
-    # dominant kernel: the W4 verify kernel, timed per launch with HIP events
-    # on the stream it runs on, over the same steps
+    # dominant kernel: the W4 verify kernel, each launch timed by the device
+    # wall-clock stamps of its workgroups, over as many steps again
     torch.cuda.synchronize()
     ev.w4_timing_read()
     ev.w4_timing(True)

@@ -1,8 +1,9 @@
 // Packed W4 weight and activation layouts (internal to libexactverify).
 //
 // Weights of an N x K W4 linear (group size G) are repacked once, exactly, into
-// tiles of 16 output rows and chunks of 128 k:
-//   blob[tile][chunk] = 1024 B of nibbles + 64*(128/G) B of (scale, bias)
+// tiles of 16 output rows and chunks of 128 k, chunk-major (the tiles of
+// chunk 0, then those of chunk 1, ...; see w4_tc_offset):
+//   blob[chunk][tile] = 1024 B of nibbles + 64*(128/G) B of (scale, bias)
 //   * nibbles: lane L = ln + 16 j of a wave reads 16 B at 16 L; dword t holds
 //     the 8 codes of row 16*tile + ln for k = 128 c + 32 t + 8 j .. +7, in k
 //     order, low nibble first (the standard byte order of those 8 codes);

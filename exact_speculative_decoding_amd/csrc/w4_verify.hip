@@ -31,6 +31,7 @@
 //   * K-split partial sums go to a workspace [S][16][N] and are added in
 //     ascending split order by a second kernel (fused with SiLU * up for the
 //     MLP gate/up pair).
+#include <algorithm>
 #include <mutex>
 #include <vector>
 
@@ -99,6 +100,9 @@ struct W4Args {
     // nibble-decode constants, passed as arguments so that they sit in
     // registers (gfx9 VOP3 encodings cannot carry 32-bit literals)
     uint32_t dmask, doff;
+    // measurement: when non-NULL, workgroup b stores the device wall clock at
+    // its start in tstamp[2b] and at its end in tstamp[2b + 1]
+    unsigned long long* tstamp;
 };
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
@@ -139,6 +143,7 @@ __global__ __launch_bounds__(kThreads) void w4_verify_kernel(W4Args a) {
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
+    if (a.tstamp && tid == 0) a.tstamp[2 * blockIdx.x] = wall_clock64();
     // wave-uniform indices (readfirstlane keeps them, the matrix and the buffer
     // descriptors in scalar registers)
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -324,6 +329,10 @@ __global__ __launch_bounds__(kThreads) void w4_verify_kernel(W4Args a) {
             }
         }
     }
+    if (a.tstamp) {  // uniform
+        __syncthreads();
+        if (tid == 0) a.tstamp[2 * blockIdx.x + 1] = wall_clock64();
+    }
 }
 
 // y[r][n] = sum over s = 0..S-1, ascending, of part[s][r][n].  One thread per
@@ -389,13 +398,20 @@ __global__ __launch_bounds__(64) void silu_reduce_kernel(const float* __restrict
     if (h_copy) *reinterpret_cast<u32x4*>(h_copy + o) = w;
 }
 
-// Measurement hook: when on, each W4 kernel launch is bracketed by HIP events
-// on its own stream, with the launch's algorithmic bytes (weights, x, y).
+// Measurement hook: when on, each W4 kernel launch gets a run of slots in a
+// device buffer, one (start, end) pair of device wall-clock stamps per
+// workgroup; a launch's execution interval runs from its earliest start to its
+// latest end.  Plain stores to distinct slots, so timing adds no contention.
+// The buffer is allocated when the hook is first switched on, never in a
+// verify call.
+constexpr long kTimingSlots = 1l << 20;  // workgroups recorded between reads
 struct W4Timing {
     std::mutex mu;
     bool on = false;
-    struct Rec { hipEvent_t a, b; double bytes; };
-    std::vector<Rec> recs;
+    unsigned long long* slots = nullptr;  // [kTimingSlots][2]
+    long used = 0;
+    std::vector<long> first, count;  // per launch: first slot, workgroups
+    std::vector<double> bytes;       // per launch: algorithmic bytes
 };
 static W4Timing g_timing;
 
@@ -418,27 +434,24 @@ static int32_t launch_w4(W4Args args, int nmat, const W4Plan& p, int K, int G, h
     args.dmask = 0x00780078u;
     args.doff = 0x41804180u;
     const unsigned blocks = (unsigned)args.blocks;
-    hipEvent_t ea = nullptr, eb = nullptr;
-    bool timed;
     {
         std::lock_guard<std::mutex> lk(g_timing.mu);
-        timed = g_timing.on;
-    }
-    if (timed) {
-        if (hipEventCreate(&ea) != hipSuccess || hipEventCreate(&eb) != hipSuccess)
-            return fail(EV_EHIP, "w4 timing: hipEventCreate failed");
-        if (hipEventRecord(ea, st) != hipSuccess) return fail(EV_EHIP, "w4 timing: record failed");
+        args.tstamp = nullptr;
+        if (g_timing.on) {
+            if (g_timing.used + args.blocks > kTimingSlots)
+                return fail(EV_EINVAL, "w4 timing: more than %ld workgroups recorded without a read", kTimingSlots);
+            args.tstamp = g_timing.slots + 2 * g_timing.used;
+            g_timing.first.push_back(g_timing.used);
+            g_timing.count.push_back(args.blocks);
+            g_timing.used += args.blocks;
+            g_timing.bytes.push_back(w4_algo_bytes(nmat, args.R, K, args.N, G));
+        }
     }
     if (G == 64)
         hipLaunchKernelGGL(w4_verify_kernel<64>, dim3(blocks), dim3(kThreads), 0, st, args);
     else
         hipLaunchKernelGGL(w4_verify_kernel<32>, dim3(blocks), dim3(kThreads), 0, st, args);
     int32_t rc = check_hip(hipGetLastError(), "w4_verify_kernel launch");
-    if (timed) {
-        if (hipEventRecord(eb, st) != hipSuccess) return fail(EV_EHIP, "w4 timing: record failed");
-        std::lock_guard<std::mutex> lk(g_timing.mu);
-        g_timing.recs.push_back({ea, eb, w4_algo_bytes(nmat, args.R, K, args.N, G)});
-    }
     return rc;
 }
 
@@ -492,34 +505,55 @@ static int32_t check_ws(const char* who, void* ws, size_t ws_bytes, size_t need)
 
 using namespace ev;
 
+static void timing_reset() {
+    g_timing.used = 0;
+    g_timing.first.clear();
+    g_timing.count.clear();
+    g_timing.bytes.clear();
+}
+
 extern "C" int32_t ev_w4_timing(int32_t enable) {
+    clear_error();
     std::lock_guard<std::mutex> lk(g_timing.mu);
+    if (enable && !g_timing.slots) {
+        if (hipMalloc(&g_timing.slots, sizeof(unsigned long long) * 2 * kTimingSlots) != hipSuccess)
+            return fail(EV_EHIP, "w4 timing: hipMalloc failed");
+        timing_reset();
+    }
     g_timing.on = enable != 0;
     return EV_OK;
 }
 
 extern "C" int32_t ev_w4_timing_read(int64_t* launches, double* total_ms, double* total_bytes) {
     clear_error();
-    std::vector<W4Timing::Rec> recs;
-    {
-        std::lock_guard<std::mutex> lk(g_timing.mu);
-        recs.swap(g_timing.recs);
-    }
+    std::lock_guard<std::mutex> lk(g_timing.mu);
     double ms = 0.0, bytes = 0.0;
-    int32_t rc = EV_OK;
-    for (auto& r : recs) {
-        float t = 0.f;
-        if (hipEventSynchronize(r.b) != hipSuccess || hipEventElapsedTime(&t, r.a, r.b) != hipSuccess)
-            rc = fail(EV_EHIP, "ev_w4_timing_read: event query failed");
-        ms += t;
-        bytes += r.bytes;
-        (void)hipEventDestroy(r.a);
-        (void)hipEventDestroy(r.b);
+    const long n = (long)g_timing.first.size();
+    if (n > 0) {
+        std::vector<unsigned long long> h(2 * (size_t)g_timing.used);
+        int rate_khz = 0, dev = 0;
+        if (hipDeviceSynchronize() != hipSuccess ||
+            hipMemcpy(h.data(), g_timing.slots, sizeof(unsigned long long) * h.size(), hipMemcpyDeviceToHost) !=
+                hipSuccess)
+            return fail(EV_EHIP, "ev_w4_timing_read: copy failed");
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&rate_khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess || rate_khz <= 0)
+            return fail(EV_EHIP, "ev_w4_timing_read: wall clock rate unavailable");
+        for (long i = 0; i < n; ++i) {
+            unsigned long long t0 = ~0ull, t1 = 0ull;
+            for (long w = g_timing.first[i]; w < g_timing.first[i] + g_timing.count[i]; ++w) {
+                t0 = std::min(t0, h[2 * w]);
+                t1 = std::max(t1, h[2 * w + 1]);
+            }
+            if (t1 > t0) ms += (double)(t1 - t0) / (double)rate_khz;
+            bytes += g_timing.bytes[i];
+        }
+        timing_reset();
     }
-    if (launches) *launches = (int64_t)recs.size();
+    if (launches) *launches = n;
     if (total_ms) *total_ms = ms;
     if (total_bytes) *total_bytes = bytes;
-    return rc;
+    return EV_OK;
 }
 
 extern "C" size_t verify_linear_w4_workspace(int32_t K, int32_t N, int32_t G) {

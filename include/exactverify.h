@@ -175,13 +175,16 @@ int32_t accept_prefix(const int32_t* sampled, int32_t R, const int32_t* draft, i
 
 /* ------------------------------------------------------------------------- */
 /* Measurement hook for the W4 verify kernel (every entry point that streams  */
-/* W4 weights launches it).  ev_w4_timing(1) makes each later launch record a */
-/* HIP event before and after it on its own stream, together with the        */
-/* launch's algorithmic bytes: nmat * (N*K/2 + 4*N*K/G + 2*R*K + 4*R*N).      */
-/* ev_w4_timing_read waits for the recorded events, returns the number of     */
-/* launches, their summed durations (ms) and summed algorithmic bytes, and    */
-/* forgets them.  Off by default; the events themselves are created here.    */
-/* Errors: EV_EHIP.                                                           */
+/* W4 weights launches it).  ev_w4_timing(1) allocates (once) a 16 MiB device */
+/* buffer of timing slots; while on, each workgroup of each W4 launch stores  */
+/* the device wall clock at its start and at its end in slots of its own, and */
+/* the launch's execution interval is its earliest start to its latest end.   */
+/* Each launch also adds its algorithmic bytes                                */
+/* nmat * (N*K/2 + 4*N*K/G + 2*R*K + 4*R*N).  ev_w4_timing_read synchronises  */
+/* the device, returns the number of launches since the last read, their      */
+/* summed intervals (ms) and summed algorithmic bytes, and starts afresh.     */
+/* Off by default.  Errors: EV_EHIP; EV_EINVAL past 2^20 recorded workgroups  */
+/* without a read (that launch is refused).                                   */
 /* ------------------------------------------------------------------------- */
 int32_t ev_w4_timing(int32_t enable);
 int32_t ev_w4_timing_read(int64_t* launches, double* total_ms, double* total_bytes);

@@ -1,6 +1,7 @@
 """The packed W4 layout is an exact copy: w4_pack's bytes equal an independent
-numpy construction of the layout (16-row tiles by 128-k chunks, codes in lane
-order, then the chunk's (scale, bias) pairs; zero padding past N and K)."""
+numpy construction of the layout (16-row tiles by 128-k chunks, chunk-major:
+all tiles of chunk 0, then of chunk 1, ...; each tile-chunk holds its codes in
+lane order, then its (scale, bias) pairs; zero padding past N and K)."""
 import numpy as np
 import pytest
 
@@ -19,7 +20,7 @@ def _layout(q, s, b, N, K, G):
     qv[:N, 1:K:2] = q >> 4
     sp = np.zeros((Np, Kp // G), np.uint32)
     sp[:N, :K // G] = s.astype(np.uint32) | (b.astype(np.uint32) << 16)
-    out = np.zeros((T, NC, 1024 + 64 * GPC), np.uint8)
+    out = np.zeros((NC, T, 1024 + 64 * GPC), np.uint8)
     for tile in range(T):
         for c in range(NC):
             blk = np.zeros((64, 4, 8), np.uint8)  # lane, dword t, nibble i
@@ -29,9 +30,9 @@ def _layout(q, s, b, N, K, G):
                     k = 128 * c + 32 * t + 8 * j
                     blk[L, t] = qv[16 * tile + ln, k:k + 8]
             codes = (blk[..., 0::2] | (blk[..., 1::2] << 4)).reshape(-1)
-            out[tile, c, :1024] = codes
+            out[c, tile, :1024] = codes
             pairs = sp[16 * tile:16 * tile + 16, c * GPC:(c + 1) * GPC]  # [ln][g]
-            out[tile, c, 1024:] = pairs.astype('<u4').view(np.uint8).reshape(-1)
+            out[c, tile, 1024:] = pairs.astype('<u4').view(np.uint8).reshape(-1)
     return out.reshape(-1)
 
 
