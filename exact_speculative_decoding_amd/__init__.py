@@ -48,6 +48,9 @@ _SIGS = {
     "verify_mlp_w4_workspace": (_sz, [_i32, _i32, _i32]),
     "verify_mlp_w4": (_i32, [_vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _sz,
                              _vp]),
+    "verify_moe_w4_workspace": (_sz, [_i32, _i32, _i32, _i32, _i32]),
+    "verify_moe_w4": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp,
+                             _vp, _vp, _sz, _vp]),
     "keyed_sample_workspace": (_sz, [_i32]),
     "keyed_sample": (_i32, [_vp, _i32, _i32, _vp, Sampling, _vp, _vp, _vp, _sz, _vp]),
     "accept_prefix": (_i32, [_vp, _i32, _vp, _i32, _vp, _vp, _vp]),
@@ -174,6 +177,51 @@ def verify_mlp_w4(x, gate, up, down, y=None, h=None, ws=None, stream=None):
         _dev(down.blob, "down", _U8), _dev(y, "y", (torch.float32,)),
         None if h is None else _dev(h, "h", _B16),
         C.c_void_p(ws.data_ptr()), nb, _stream(stream)))
+    return y
+
+
+class PackedW4Stack:
+    """E W4 matrices of one shape, packed back to back (expert e at e * nbytes)."""
+
+    def __init__(self, blob, E, N, K, G):
+        self.blob, self.E, self.N, self.K, self.G = blob, E, N, K, G
+        self.nbytes = w4_packed_bytes(N, K, G)
+
+
+def w4_pack_stack(q, s, b, G, stream=None):
+    """Pack E standard-layout matrices q [E][N][K/2] u8, s/b [E][N][K/G] fp16."""
+    E, N, Kh = q.shape
+    K = 2 * Kh
+    nb = w4_packed_bytes(N, K, G)
+    out = torch.empty(E * nb, dtype=torch.uint8, device=q.device)
+    for e in range(E):
+        w4_pack(q[e], s[e], b[e], G, out=out[e * nb:(e + 1) * nb], stream=stream)
+    return PackedW4Stack(out, E, N, K, G)
+
+
+def verify_moe_w4_workspace(H, I, E, top, G):
+    return int(lib().verify_moe_w4_workspace(H, I, E, top, G))
+
+
+def verify_moe_w4(x, router, gate, up, down, top, y=None, expert_ids=None, expert_w=None, ws=None,
+                  stream=None):
+    """MoE verify layer: x [R][H] bf16, router [R][E] fp32, stacks of packed
+    experts (gate/up I x H, down H x I).  Returns y [R][H] fp32."""
+    R, H = x.shape
+    E, I, G = gate.E, gate.N, gate.G
+    if not (gate.K == up.K == down.N == H and up.N == down.K == I and up.E == down.E == E
+            and up.G == down.G == G and router.shape == (R, E)):
+        raise ValueError("inconsistent MoE shapes")
+    if y is None:
+        y = torch.empty((R, H), dtype=torch.float32, device=x.device)
+    ws, nb = _workspace(verify_moe_w4_workspace(H, I, E, top, G), x.device, ws)
+    _check(lib().verify_moe_w4(
+        _dev(x, "x", _B16), _dev(router, "router", (torch.float32,)), R, H, I, E, top, G,
+        _dev(gate.blob, "gate", _U8), _dev(up.blob, "up", _U8), _dev(down.blob, "down", _U8),
+        _dev(y, "y", (torch.float32,)),
+        None if expert_ids is None else _dev(expert_ids, "expert_ids", (torch.int32,)),
+        None if expert_w is None else _dev(expert_w, "expert_w", (torch.float32,)),
+        None if ws is None else C.c_void_p(ws.data_ptr()), nb, _stream(stream)))
     return y
 
 

@@ -40,4 +40,29 @@ __device__ __forceinline__ float f16_to_f32(uint16_t h) {
     return (float)v;
 }
 
+// Order key of (value l, index id): a larger key comes earlier in the order
+// (l desc, id asc).  -0 and +0 compare equal as values, so -0 is folded onto
+// +0.  Key 0 is below every real key.
+__device__ __forceinline__ unsigned long long order_key(float l, int id) {
+    uint32_t u = __float_as_uint(l);
+    if ((u & 0x7fffffffu) == 0u) u = 0u;
+    const uint32_t ok = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return ((unsigned long long)ok << 32) | (unsigned long long)(~(uint32_t)id);
+}
+__device__ __forceinline__ float key_logit(unsigned long long k) {
+    const uint32_t ok = (uint32_t)(k >> 32);
+    const uint32_t u = (ok & 0x80000000u) ? (ok & 0x7fffffffu) : ~ok;
+    return __uint_as_float(u);
+}
+__device__ __forceinline__ int key_id(unsigned long long k) { return (int)(~(uint32_t)k); }
+
+__device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        const unsigned long long o = __shfl_xor(v, off, 64);
+        v = o > v ? o : v;
+    }
+    return v;
+}
+
 }  // namespace ev

@@ -1,0 +1,104 @@
+// The W4 verify kernel's launch interface, shared by the dense entry points
+// (w4_verify.hip) and the grouped MoE layer (moe.hip).  Internal to
+// libexactverify.
+#pragma once
+
+#include "ev_internal.h"
+#include "w4_layout.h"
+
+#ifndef EV_W4_NT
+#define EV_W4_NT 2  // 16-row tiles per wave
+#endif
+#ifndef EV_W4_PD
+#define EV_W4_PD 2  // chunks of loads in flight per wave
+#endif
+#ifndef EV_W4_TARGET_WAVES
+#define EV_W4_TARGET_WAVES 2048
+#endif
+#ifndef EV_W4_MIN_CPS
+#define EV_W4_MIN_CPS 8  // at least this many chunks per K-split when K allows
+#endif
+
+namespace ev {
+
+int32_t check_w4_dims(const char* who, int K, int N, int G);
+
+constexpr int kThreads = 256;  // 4 independent waves per workgroup
+constexpr int kNT = EV_W4_NT;
+constexpr int kPD = EV_W4_PD;
+constexpr int kSC = 4;  // chunks per activation superchunk (512 k)
+
+struct W4Plan {
+    int S;        // K-splits
+    int cps;      // chunks per split
+    int nchunks;  // chunks of 128 k
+    int ncg;      // tile groups of kNT tiles
+    long items;   // waves = nmat * S * ncg
+};
+
+// Split plan from (N, K) and the number of matrices of the launch, never R:
+// every reduction order of an output element follows from the plan.
+inline W4Plan plan_w4(int N, int K, int nmat) {
+    W4Plan p;
+    p.nchunks = w4_chunks(K);
+    p.ncg = (w4_tiles(N) + kNT - 1) / kNT;
+    const long base = (long)p.ncg * nmat;
+    long S = (EV_W4_TARGET_WAVES + base - 1) / base;
+    long smax = p.nchunks / EV_W4_MIN_CPS;
+    if (smax < 1) smax = 1;
+    if (S > smax) S = smax;
+    if (S < 1) S = 1;
+    p.cps = (int)((p.nchunks + S - 1) / S);
+    p.cps = (p.cps + kSC - 1) / kSC * kSC;  // splits start on superchunk boundaries
+    p.S = (p.nchunks + p.cps - 1) / p.cps;
+    p.items = base * p.S;
+    return p;
+}
+
+struct W4Args {
+    const uint8_t* w[2];  // packed weights; the workgroup's matrix index picks one
+    float* out[2];        // split s writes rows at out + s * split_stride
+    const uint16_t* x;    // activations [rows][K] bf16
+    int R, K, N, nchunks, tiles;
+    int cps, S, ncg, ncgb;  // ncgb: workgroups per (matrix, split)
+    int nmat;               // matrices per group (1 or 2)
+    long blocks;
+    long split_stride;
+    uint32_t wbytes, xbytes;
+    // nibble-decode constants, passed as arguments so that they sit in
+    // registers (gfx9 VOP3 encodings cannot carry 32-bit literals)
+    uint32_t dmask, doff;
+    // measurement: when non-NULL, workgroup b stores the device wall clock at
+    // its start in tstamp[2b] and at its end in tstamp[2b + 1]
+    unsigned long long* tstamp;
+    // Grouped launch (one group per touched MoE expert); gexp == NULL for a
+    // plain launch.  Group g (< *gcount, else its workgroups exit at once)
+    // streams matrix w[m] + gexp[g] * wstride over rows 0..gcnt[g]-1, whose
+    // activations are x rows grows[16 g + r] (grows == NULL: rows 16 g + r),
+    // and writes its outputs at out[m] + g * ogstride + split * split_stride.
+    const int* gcount;
+    const int* gexp;
+    const int* gcnt;
+    const int* grows;
+    long wstride, ogstride;
+};
+
+// Launch the W4 kernel over `ngroups` groups (1 for a plain launch) of
+// `nmat` matrices each.  Fills the plan-derived fields of `args`.
+int32_t launch_w4(W4Args args, int nmat, const W4Plan& p, int K, int G, hipStream_t st,
+                  int ngroups = 1);
+
+// h[r][k] = bf16_rne(silu(sum_s pg[s][r][k]) * sum_s pu[s][r][k]) for rows
+// r < R, splits added in ascending s (split stride 16 * I).  Grouped when gcnt
+// != NULL: group g < *gcount (grid z) covers rows < gcnt[g] at offsets
+// g * gstride_p (partials) and g * gstride_h (h).
+int32_t launch_silu_reduce(const float* pg, const float* pu, int S, int I, int R, uint16_t* h,
+                           uint16_t* h_copy, int ngroups, const int* gcount, const int* gcnt,
+                           long gstride_p, long gstride_h, hipStream_t st);
+
+inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+int32_t check_lanes(const char* who, int R);
+int32_t check_ws(const char* who, void* ws, size_t ws_bytes, size_t need);
+
+}  // namespace ev

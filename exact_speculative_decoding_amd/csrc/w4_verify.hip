@@ -35,75 +35,12 @@
 #include <mutex>
 #include <vector>
 
-#include "ev_internal.h"
-#include "w4_layout.h"
-
-#ifndef EV_W4_NT
-#define EV_W4_NT 2  // 16-row tiles per wave
-#endif
-#ifndef EV_W4_PD
-#define EV_W4_PD 2  // chunks of loads in flight per wave
-#endif
-#ifndef EV_W4_TARGET_WAVES
-#define EV_W4_TARGET_WAVES 2048
-#endif
-#ifndef EV_W4_MIN_CPS
-#define EV_W4_MIN_CPS 8  // at least this many chunks per K-split when K allows
-#endif
+#include "w4_kernel.h"
 
 namespace ev {
 
-int32_t check_w4_dims(const char* who, int K, int N, int G);
-
-constexpr int kThreads = 256;  // 4 independent waves per workgroup
-constexpr int kNT = EV_W4_NT;
-constexpr int kPD = EV_W4_PD;
 constexpr uint32_t kOOB = 0x80000000u;  // per-lane offset beyond every buffer: reads 0
-constexpr int kSC = 4;                   // chunks per activation superchunk (512 k)
 constexpr int kSlab = kSC * kXChunkBytes;  // LDS bytes of one superchunk of activations
-
-struct W4Plan {
-    int S;        // K-splits
-    int cps;      // chunks per split
-    int nchunks;  // chunks of 128 k
-    int ncg;      // tile groups of kNT tiles
-    long items;   // waves = nmat * S * ncg
-};
-
-// Split plan from (N, K) and the number of matrices of the launch, never R.
-static W4Plan plan_w4(int N, int K, int nmat) {
-    W4Plan p;
-    p.nchunks = w4_chunks(K);
-    p.ncg = (w4_tiles(N) + kNT - 1) / kNT;
-    const long base = (long)p.ncg * nmat;
-    long S = (EV_W4_TARGET_WAVES + base - 1) / base;
-    long smax = p.nchunks / EV_W4_MIN_CPS;
-    if (smax < 1) smax = 1;
-    if (S > smax) S = smax;
-    if (S < 1) S = 1;
-    p.cps = (int)((p.nchunks + S - 1) / S);
-    p.cps = (p.cps + kSC - 1) / kSC * kSC;  // splits start on superchunk boundaries
-    p.S = (p.nchunks + p.cps - 1) / p.cps;
-    p.items = base * p.S;
-    return p;
-}
-
-struct W4Args {
-    const uint8_t* w[2];  // packed weights; the workgroup's matrix index picks one
-    float* out[2];        // split s writes rows at out + s * split_stride
-    const uint16_t* x;    // activations [R][K] bf16
-    int R, K, N, nchunks, tiles;
-    int cps, S, ncg, ncgb;  // ncgb: workgroups per (matrix, split)
-    long blocks;
-    long split_stride;
-    uint32_t wbytes, xbytes;
-    // nibble-decode constants, passed as arguments so that they sit in
-    // registers (gfx9 VOP3 encodings cannot carry 32-bit literals)
-    uint32_t dmask, doff;
-    // measurement: when non-NULL, workgroup b stores the device wall clock at
-    // its start in tstamp[2b] and at its end in tstamp[2b + 1]
-    unsigned long long* tstamp;
-};
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
@@ -149,15 +86,34 @@ __global__ __launch_bounds__(kThreads) void w4_verify_kernel(W4Args a) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const long blk = blockIdx.x;
     const int cgb = (int)(blk % a.ncgb);
-    const long rest = blk / a.ncgb;
+    long rest = blk / a.ncgb;
     const int split = (int)(rest % a.S);
-    const int mi = (int)(rest / a.S);
+    rest /= a.S;
+    const int mi = (int)(rest % a.nmat);
+    const int grp = (int)(rest / a.nmat);
     const int cg = cgb * 4 + wave;  // a wave past the last tile group computes zeros
     const int c0 = split * a.cps;   // a multiple of kSC
     const int c1 = min(a.nchunks, c0 + a.cps);
     const int ln = lane & 15, j = lane >> 4;
 
-    const rsrc_t rw = make_rsrc(a.w[mi], a.wbytes);
+    // rows of this workgroup's pass, their activation rows, weights and outputs
+    int rows = a.R;
+    const uint8_t* wmat = a.w[mi];
+    float* out = a.out[mi] + (size_t)split * a.split_stride;
+    if (a.gexp) {
+        if (grp >= a.gcount[0]) return;  // whole workgroup: no barrier reached
+        rows = a.gcnt[grp];
+        wmat += (size_t)a.gexp[grp] * a.wstride;
+        out += (size_t)grp * a.ogstride;
+    }
+    int xrow[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        const int r = wave + 4 * m;
+        xrow[m] = a.grows ? a.grows[16 * grp + r] : (a.gexp ? 16 * grp + r : r);
+    }
+
+    const rsrc_t rw = make_rsrc(wmat, a.wbytes);
     const rsrc_t rx = make_rsrc(a.x, a.xbytes);
     uint32_t tbase[kNT];
     bool tok[kNT];
@@ -188,9 +144,8 @@ __global__ __launch_bounds__(kThreads) void w4_verify_kernel(W4Args a) {
         const int k = sc * (kSC * kKC) + 8 * col;
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-            const int r = wave + 4 * m;
-            const bool ok = r < a.R && k < a.K;
-            xin[m] = bload128(rx, ok ? (uint32_t)(r * a.K + k) * 2u : kOOB, 0u);
+            const bool ok = wave + 4 * m < rows && k < a.K;
+            xin[m] = bload128(rx, ok ? (uint32_t)(xrow[m] * a.K + k) * 2u : kOOB, 0u);
         }
     };
     // reorder (x0,x4) (x1,x5) (x2,x6) (x3,x7) and store as the A fragment of
@@ -317,7 +272,6 @@ __global__ __launch_bounds__(kThreads) void w4_verify_kernel(W4Args a) {
     __builtin_amdgcn_sched_barrier(0);
 
     // rows r = 4j + i of columns 16 * tile + ln
-    float* out = a.out[mi] + (size_t)split * a.split_stride;
 #pragma unroll
     for (int t = 0; t < kNT; ++t) {
         const int n = (cg * kNT + t) * 16 + ln;
@@ -325,7 +279,7 @@ __global__ __launch_bounds__(kThreads) void w4_verify_kernel(W4Args a) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = 4 * j + i;
-                if (r < a.R) out[(size_t)r * a.N + n] = y[t][i];
+                if (r < rows) out[(size_t)r * a.N + n] = y[t][i];
             }
         }
     }
@@ -363,14 +317,25 @@ __global__ __launch_bounds__(64) void splitk_reduce_kernel(const float* __restri
 
 // g, u = split sums (ascending s); h = bf16_rne(silu(g) * u) for rows < R.
 // One thread per 8 consecutive k of one row; h is written to `h` (the down
-// projection's input) and, when asked, to `h_copy`.
+// projection's input) and, when asked, to `h_copy`.  Grouped (gcnt != NULL):
+// grid z is the group, rows < gcnt[z] of groups < *gcount.
 __global__ __launch_bounds__(64) void silu_reduce_kernel(const float* __restrict__ pg,
                                                          const float* __restrict__ pu, int S, int I,
                                                          uint16_t* __restrict__ h,
-                                                         uint16_t* __restrict__ h_copy) {
+                                                         uint16_t* __restrict__ h_copy,
+                                                         const int* __restrict__ gcount,
+                                                         const int* __restrict__ gcnt, long gstride_p,
+                                                         long gstride_h) {
     const int m = blockIdx.x * 64 + threadIdx.x;  // I % 32 == 0: groups of 8 never straddle rows
     const int r = blockIdx.y;
     if (8 * m >= I) return;
+    if (gcnt) {
+        const int g = blockIdx.z;
+        if (g >= gcount[0] || r >= gcnt[g]) return;
+        pg += g * gstride_p;
+        pu += g * gstride_p;
+        h += g * gstride_h;
+    }
     const size_t stride = (size_t)16 * I;
     const size_t o = (size_t)r * I + 8 * m;
     f32x4 g0 = *reinterpret_cast<const f32x4*>(pg + o), g1 = *reinterpret_cast<const f32x4*>(pg + o + 4);
@@ -398,6 +363,15 @@ __global__ __launch_bounds__(64) void silu_reduce_kernel(const float* __restrict
     if (h_copy) *reinterpret_cast<u32x4*>(h_copy + o) = w;
 }
 
+int32_t launch_silu_reduce(const float* pg, const float* pu, int S, int I, int R, uint16_t* h,
+                           uint16_t* h_copy, int ngroups, const int* gcount, const int* gcnt,
+                           long gstride_p, long gstride_h, hipStream_t st) {
+    dim3 grid((unsigned)((I / 8 + 63) / 64), (unsigned)R, (unsigned)ngroups);
+    hipLaunchKernelGGL(silu_reduce_kernel, grid, dim3(64), 0, st, pg, pu, S, I, h, h_copy, gcount, gcnt,
+                       gstride_p, gstride_h);
+    return check_hip(hipGetLastError(), "silu_reduce launch");
+}
+
 // Measurement hook: when on, each W4 kernel launch gets a run of slots in a
 // device buffer, one (start, end) pair of device wall-clock stamps per
 // workgroup; a launch's execution interval runs from its earliest start to its
@@ -420,24 +394,25 @@ static double w4_algo_bytes(int nmat, int R, int K, int N, int G) {
     return nmat * (w + 2.0 * R * K + 4.0 * R * N);
 }
 
-static int32_t launch_w4(W4Args args, int nmat, const W4Plan& p, int K, int G, hipStream_t st) {
+int32_t launch_w4(W4Args args, int nmat, const W4Plan& p, int K, int G, hipStream_t st, int ngroups) {
     args.K = K;
+    args.nmat = nmat;
     args.nchunks = p.nchunks;
     args.tiles = w4_tiles(args.N);
     args.cps = p.cps;
     args.S = p.S;
     args.ncg = p.ncg;
     args.ncgb = (p.ncg + 3) / 4;
-    args.blocks = (long)nmat * p.S * args.ncgb;
+    args.blocks = (long)ngroups * nmat * p.S * args.ncgb;
     args.wbytes = (uint32_t)w4_blob_bytes(args.N, K, G);
-    args.xbytes = (uint32_t)((size_t)args.R * K * 2);
+    if (!args.gexp) args.xbytes = (uint32_t)((size_t)args.R * K * 2);  // grouped: set by the caller
     args.dmask = 0x00780078u;
     args.doff = 0x41804180u;
     const unsigned blocks = (unsigned)args.blocks;
     {
         std::lock_guard<std::mutex> lk(g_timing.mu);
         args.tstamp = nullptr;
-        if (g_timing.on) {
+        if (g_timing.on && !args.gexp) {  // grouped launches' bytes depend on the routing
             if (g_timing.used + args.blocks > kTimingSlots)
                 return fail(EV_EINVAL, "w4 timing: more than %ld workgroups recorded without a read", kTimingSlots);
             args.tstamp = g_timing.slots + 2 * g_timing.used;
@@ -454,8 +429,6 @@ static int32_t launch_w4(W4Args args, int nmat, const W4Plan& p, int K, int G, h
     int32_t rc = check_hip(hipGetLastError(), "w4_verify_kernel launch");
     return rc;
 }
-
-static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 // Workspace of verify_linear_w4: split partials [S][16][N] (none if S == 1).
 struct LinLayout {
@@ -487,12 +460,12 @@ static MlpLayout mlp_layout(int H, int I) {
     return L;
 }
 
-static int32_t check_lanes(const char* who, int R) {
+int32_t check_lanes(const char* who, int R) {
     if (R < 1 || R > EV_MAX_LANES) return fail(EV_EINVAL, "%s: R=%d outside 1..16", who, R);
     return EV_OK;
 }
 
-static int32_t check_ws(const char* who, void* ws, size_t ws_bytes, size_t need) {
+int32_t check_ws(const char* who, void* ws, size_t ws_bytes, size_t need) {
     if (need == 0) return EV_OK;
     if (!ws || ws_bytes < need)
         return fail(EV_EWORKSPACE, "%s: workspace needs %zu bytes, got %zu", who, need,
@@ -627,11 +600,7 @@ extern "C" int32_t verify_mlp_w4(const uint16_t* x, int32_t R, int32_t H, int32_
     a.N = I;
     a.split_stride = (long)16 * I;
     if ((rc = launch_w4(a, 2, L.p1, H, G, st))) return rc;
-    {
-        dim3 grid((unsigned)((I / 8 + 63) / 64), (unsigned)R);
-        hipLaunchKernelGGL(silu_reduce_kernel, grid, dim3(64), 0, st, pg, pu, L.p1.S, I, h, h_out);
-        if ((rc = check_hip(hipGetLastError(), "silu_reduce launch"))) return rc;
-    }
+    if ((rc = launch_silu_reduce(pg, pu, L.p1.S, I, R, h, h_out, 1, nullptr, nullptr, 0, 0, st))) return rc;
     // down, reading the packed h
     W4Args d{};
     d.w[0] = d.w[1] = reinterpret_cast<const uint8_t*>(w_down);

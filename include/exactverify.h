@@ -119,6 +119,38 @@ int32_t verify_mlp_w4(const uint16_t* x_bf16, int32_t R, int32_t H, int32_t I, i
                       float* y, uint16_t* h_bf16, void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------- */
+/* MoE verify layer (top-`top` routing over E experts, SiLU-gated experts).   */
+/*                                                                            */
+/* The pages' MoE models (TensorFold README model notes; blog "The numbers":  */
+/* Nemotron 30B-A3B) verify their drafted rows through this layer; each lane  */
+/* (row) is routed on its own and, by the README's exactness paragraph, its   */
+/* output must not depend on the other lanes.  Per lane r:                    */
+/*   pi = softmax(router[r]);  ids = the `top` experts by pi (lower id on     */
+/*   ties);  w_j = pi[ids_j] / sum_j' pi[ids_j'];                             */
+/*   y[r] = sum over j = 0..top-1, in that order, of w_j * MLP_{ids_j}(x[r])  */
+/* with MLP_e the SiLU-gated MLP of verify_mlp_w4 on expert e's matrices.     */
+/*   x_bf16   (device) [R][H] bf16, 16-byte aligned.                          */
+/*   router   (device) [R][E] fp32 router logits (finite), 4-byte aligned.    */
+/*   w_gate, w_up (device) E packed I x H matrices, expert e at byte offset   */
+/*            e * w4_packed_bytes(I, H, G); w_down: E packed H x I matrices,  */
+/*            expert e at e * w4_packed_bytes(H, I, G).  16-byte aligned.     */
+/*   y        (device) [R][H] fp32, 16-byte aligned, written.                 */
+/*   expert_ids, expert_w (device, optional) [R][top] int32 / fp32: if        */
+/*            non-NULL, the routing (ids in rank order, renormalised weights).*/
+/*   ws       (device) verify_moe_w4_workspace(H, I, E, top, G) bytes,        */
+/*            256-byte aligned (a function of the shapes only, never of R).   */
+/* Only the experts some lane selects are read (one grouped pass; each        */
+/* expert's weights once for all its lanes).  Limits: 1 <= R <= 16;           */
+/* 1 <= E <= 256; 1 <= top <= min(8, E); H and I as for verify_linear_w4.     */
+/* Errors: EV_EINVAL, EV_EUNSUPPORTED, EV_EWORKSPACE, EV_EHIP.                */
+/* ------------------------------------------------------------------------- */
+size_t verify_moe_w4_workspace(int32_t H, int32_t I, int32_t E, int32_t top, int32_t G);
+int32_t verify_moe_w4(const uint16_t* x_bf16, const float* router, int32_t R, int32_t H,
+                      int32_t I, int32_t E, int32_t top, int32_t G, const void* w_gate,
+                      const void* w_up, const void* w_down, float* y, int32_t* expert_ids,
+                      float* expert_w, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------- */
 /* Keyed sampler.                                                             */
 /*                                                                            */
 /* README exactness paragraph / 650 Group: token at position p = argmax over  */

@@ -115,3 +115,33 @@ def test_binding_refuses_host_tensors():
     w = ev.PackedW4(torch.zeros(ev.w4_packed_bytes(512, 256, 64), dtype=torch.uint8), 512, 256, 64)
     with pytest.raises((ValueError, RuntimeError)):
         ev.verify_linear_w4(x, w, y=torch.zeros(2, 512))
+
+
+def _moe(**kw):
+    a = dict(x=P, rho=P, R=4, H=256, I=128, E=16, top=4, G=32, wg=P, wu=P, wd=P, y=P, ids=None,
+             w=None, ws=None, nb=0)
+    a.update(kw)
+    return ev.lib().verify_moe_w4(a["x"], a["rho"], a["R"], a["H"], a["I"], a["E"], a["top"], a["G"],
+                                  a["wg"], a["wu"], a["wd"], a["y"], a["ids"], a["w"], a["ws"], a["nb"],
+                                  None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(R=0), ev.EV_EINVAL), (dict(R=17), ev.EV_EINVAL), (dict(E=0), ev.EV_EUNSUPPORTED),
+    (dict(E=257), ev.EV_EUNSUPPORTED), (dict(top=0), ev.EV_EUNSUPPORTED), (dict(top=9), ev.EV_EUNSUPPORTED),
+    (dict(E=3, top=4), ev.EV_EUNSUPPORTED), (dict(G=16), ev.EV_EUNSUPPORTED), (dict(H=100), ev.EV_EINVAL),
+    (dict(I=48, G=32), ev.EV_EINVAL), (dict(x=None), ev.EV_EINVAL), (dict(rho=None), ev.EV_EINVAL),
+    (dict(wd=None), ev.EV_EINVAL), (dict(y=None), ev.EV_EINVAL), (dict(y=C.c_void_p(0x10004)), ev.EV_EINVAL),
+    (dict(ids=C.c_void_p(0x10002)), ev.EV_EINVAL), (dict(), ev.EV_EWORKSPACE),
+    (dict(nb=64, ws=P), ev.EV_EWORKSPACE),
+])
+def test_moe_rejects_bad_arguments(kw, code):
+    assert _moe(**kw) == code
+    assert ev.lib().ev_last_error()
+
+
+def test_moe_workspace_depends_on_shapes_only():
+    a = ev.verify_moe_w4_workspace(2048, 768, 128, 8, 32)
+    assert a > 0 and a == ev.verify_moe_w4_workspace(2048, 768, 128, 8, 32)
+    assert ev.verify_moe_w4_workspace(2048, 768, 128, 9, 32) == 0
+    assert ev.verify_moe_w4_workspace(256, 128, 16, 4, 32) < a
