@@ -290,3 +290,8 @@ def moe(x, rho, top, G, gate, up, down):
                  *[ptr(a, a.dtype) for a in t], ptr(y, np.float32), ptr(ids, np.int32),
                  ptr(w, np.float64))
     return y, ids, w
+
+
+# --- decoder (oracle/decoder.c) ---------------------------------------------
+
+from .decoder import Decoder, attend, rmsnorm_bf16, rope  # noqa: E402,F401

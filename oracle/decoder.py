@@ -1,0 +1,92 @@
+"""numpy wrappers of oracle/decoder.c (TEST INFRASTRUCTURE): RMSNorm, rotary
+positions, single-query attention, and the serial decoding step of the small
+decoder.  Imported only through the `oracle` package."""
+import ctypes as C
+
+import numpy as np
+
+
+def declare(L):
+    u16, i32, i64, f32, f64 = C.c_uint16, C.c_int32, C.c_int64, C.c_float, C.c_double
+    P = C.POINTER
+    L.ov_rmsnorm_bf16.argtypes = [P(f32), i32, P(f32), f64, P(u16)]
+    L.ov_rope.argtypes = [P(f32), i32, i64, f64]
+    L.ov_attend.argtypes = [P(f32), P(u16), P(u16), i32, i32, P(f64)]
+    L.ov_decoder_step.argtypes = [P(i32), P(f64), P(C.c_void_p), P(u16), P(u16), i32, i32, i64,
+                                  f64, i32, f64, C.c_uint64, P(f32), P(i32), P(f64)]
+
+
+def _lib():
+    from . import lib
+    return lib()
+
+
+def _ptr(a, dt):
+    from . import ptr
+    return ptr(a, dt)
+
+
+def rmsnorm_bf16(x, gain, eps):
+    x = np.ascontiguousarray(x, np.float32)
+    gain = np.ascontiguousarray(gain, np.float32)
+    out = np.empty(x.shape, np.uint16)
+    _lib().ov_rmsnorm_bf16(_ptr(x, np.float32), x.size, _ptr(gain, np.float32), float(eps),
+                           _ptr(out, np.uint16))
+    return out
+
+
+def rope(v, pos, base):
+    v = np.array(v, np.float32)
+    _lib().ov_rope(_ptr(v, np.float32), v.size, int(pos), float(base))
+    return v
+
+
+def attend(q, K, V):
+    q = np.ascontiguousarray(q, np.float32)
+    K = np.ascontiguousarray(K, np.uint16)
+    V = np.ascontiguousarray(V, np.uint16)
+    n, d = K.shape
+    o = np.empty(d, np.float64)
+    _lib().ov_attend(_ptr(q, np.float32), _ptr(K, np.uint16), _ptr(V, np.uint16), n, d,
+                     _ptr(o, np.float64))
+    return o
+
+
+# weight order of ov_decoder_step's pointer table
+WEIGHT_KEYS = ["embed", "attn_norm", "mlp_norm", "final_norm",
+               "qkv_q", "qkv_s", "qkv_b", "o_q", "o_s", "o_b",
+               "gate_q", "gate_s", "gate_b", "up_q", "up_s", "up_b",
+               "down_q", "down_s", "down_b", "lm_q", "lm_s", "lm_b"]
+_DT = {"embed": np.uint16, "attn_norm": np.float32, "mlp_norm": np.float32,
+       "final_norm": np.float32}
+
+
+class Decoder:
+    """The oracle decoder on a weight dict (standard layouts, see decoder.c)
+    with its own copies of the K/V caches [L][kv_heads][C][d] fp16."""
+
+    def __init__(self, cfg, weights, kc, vc):
+        self.cfg = cfg
+        self.ci = np.array([cfg["layers"], cfg["hidden"], cfg["heads"], cfg["kv_heads"],
+                            cfg["head_dim"], cfg["inter"], cfg["vocab"], cfg["G"]], np.int32)
+        self.cd = np.array([cfg["rope_base"], cfg["eps"]], np.float64)
+        self.w = [np.ascontiguousarray(weights[k], _DT.get(k, np.uint8 if k.endswith("_q")
+                                                           else np.uint16)) for k in WEIGHT_KEYS]
+        self.tab = (C.c_void_p * len(self.w))(*[a.ctypes.data for a in self.w])
+        self.kc = np.array(kc, np.uint16, copy=True)
+        self.vc = np.array(vc, np.uint16, copy=True)
+        self.C = self.kc.shape[2]
+
+    def step(self, token, pos, T, top_k, top_p, seed):
+        """Token at slot `pos` -> (logits of position pos + 1 [V] fp32, the token
+        sampled there, its gap).  Writes slot `pos` of the caches."""
+        V = self.cfg["vocab"]
+        logits = np.empty(V, np.float32)
+        tok = np.zeros(1, np.int32)
+        gap = np.zeros(1, np.float64)
+        _lib().ov_decoder_step(_ptr(self.ci, np.int32), _ptr(self.cd, np.float64), self.tab,
+                               _ptr(self.kc, np.uint16), _ptr(self.vc, np.uint16), self.C,
+                               int(token), int(pos), float(T), int(top_k), float(top_p),
+                               int(seed) & ((1 << 64) - 1), _ptr(logits, np.float32),
+                               _ptr(tok, np.int32), _ptr(gap, np.float64))
+        return logits, int(tok[0]), float(gap[0])

@@ -113,3 +113,69 @@ def draft_coins(seed, n, p):
     random offset 1..V-1 used to make a guaranteed-wrong guess."""
     g = rng(seed)
     return g.random(n) < p, g.integers(1, 1 << 30, size=n)
+
+
+def decoder(seed=1005, layers=8, hidden=2048, heads=16, kv_heads=4, head_dim=128, inter=6144,
+            vocab=32768, G=64, C=4096, prefill=None, rope_base=1e6, eps=1e-6):
+    """Random-init decoder in standard layouts (the weight keys of the oracle's
+    decoder), plus K/V caches [layers][kv_heads][C][head_dim] fp16 whose first
+    `prefill` slots (default C - 512) hold N(0, 1) entries, the same bytes on
+    every run.  RMSNorm gains are drawn from U(0.8, 1.2) rather than set to 1,
+    so that a gain applied to the wrong element is visible."""
+    g = rng(seed)
+    nqkv, dq = (heads + 2 * kv_heads) * head_dim, heads * head_dim
+
+    def stack(N, K):
+        parts = [w4_matrix(g, N, K, G) for _ in range(layers)]
+        return tuple(np.stack([p[i] for p in parts]) for i in range(3))
+
+    w = {"embed": bf16_bits(g.standard_normal((vocab, hidden), dtype=np.float32)),
+         "attn_norm": g.uniform(0.8, 1.2, (layers, hidden)).astype(np.float32),
+         "mlp_norm": g.uniform(0.8, 1.2, (layers, hidden)).astype(np.float32),
+         "final_norm": g.uniform(0.8, 1.2, hidden).astype(np.float32)}
+    for name, (N, K) in (("qkv", (nqkv, hidden)), ("o", (hidden, dq)), ("gate", (inter, hidden)),
+                         ("up", (inter, hidden)), ("down", (hidden, inter))):
+        w[name + "_q"], w[name + "_s"], w[name + "_b"] = stack(N, K)
+    w["lm_q"], w["lm_s"], w["lm_b"] = w4_matrix(g, vocab, hidden, G)
+    prefill = C - 512 if prefill is None else prefill
+    kc = np.zeros((layers, kv_heads, C, head_dim), np.uint16)
+    vc = np.zeros((layers, kv_heads, C, head_dim), np.uint16)
+    for l in range(layers):
+        kc[l, :, :prefill] = fp16_bits(g.standard_normal((kv_heads, prefill, head_dim), dtype=np.float32))
+        vc[l, :, :prefill] = fp16_bits(g.standard_normal((kv_heads, prefill, head_dim), dtype=np.float32))
+    cfg = dict(layers=layers, hidden=hidden, heads=heads, kv_heads=kv_heads, head_dim=head_dim,
+               inter=inter, vocab=vocab, G=G, rope_base=rope_base, eps=eps, C=C, prefill=prefill)
+    first = int(g.integers(0, vocab))
+    return dict(cfg=cfg, w=w, kc=kc, vc=vc, first_token=first)
+
+
+def tiny_decoder(seed=1006, **kw):
+    """A 2-layer decoder small enough for the oracle's exhaustive checks."""
+    a = dict(layers=2, hidden=256, heads=2, kv_heads=1, head_dim=128, inter=384, vocab=512, G=64,
+             C=64, prefill=8)
+    a.update(kw)
+    return decoder(seed, **a)
+
+
+def transcript_drafter(transcript, pos_first, p, seed, V):
+    """Drafts that equal a known serial transcript with probability p per
+    position (pre-drawn coins keyed by position), else a token that is
+    certainly wrong.  transcript[i] is the token at position pos_first + i."""
+    n = len(transcript)
+    coin, off = draft_coins(seed, n + 1, p)
+
+    def draft(position, count):
+        out = []
+        for q in range(position, position + count):
+            i = q - pos_first
+            t = int(transcript[i]) if 0 <= i < n else 0
+            out.append(t if (0 <= i < n and coin[i]) else (t + 1 + int(off[max(i, 0) % (n + 1)]) % (V - 1)) % V)
+        return out
+    return draft
+
+
+def random_drafter(seed, V):
+    """Drafts drawn uniformly over the vocabulary, keyed by position."""
+    def draft(position, count):
+        return [int(rng((seed, q)).integers(0, V)) for q in range(position, position + count)]
+    return draft
