@@ -35,6 +35,24 @@ class Sampling(C.Structure):
                 ("seed", C.c_uint64)]
 
 
+class DecoderConfig(C.Structure):
+    _fields_ = [("layers", C.c_int32), ("hidden", C.c_int32), ("heads", C.c_int32),
+                ("kv_heads", C.c_int32), ("head_dim", C.c_int32), ("intermediate", C.c_int32),
+                ("vocab", C.c_int32), ("group", C.c_int32), ("rope_base", C.c_double),
+                ("rms_eps", C.c_double)]
+
+
+class DecoderLayer(C.Structure):
+    _fields_ = [("attn_norm", C.c_void_p), ("w_qkv", C.c_void_p), ("w_o", C.c_void_p),
+                ("mlp_norm", C.c_void_p), ("w_gate", C.c_void_p), ("w_up", C.c_void_p),
+                ("w_down", C.c_void_p)]
+
+
+class DecoderWeights(C.Structure):
+    _fields_ = [("embed", C.c_void_p), ("layers", C.POINTER(DecoderLayer)),
+                ("final_norm", C.c_void_p), ("w_lm", C.c_void_p)]
+
+
 _vp, _sz, _i32, _i64 = C.c_void_p, C.c_size_t, C.c_int32, C.c_int64
 
 # name -> (restype, argtypes)
@@ -54,6 +72,11 @@ _SIGS = {
     "keyed_sample_workspace": (_sz, [_i32]),
     "keyed_sample": (_i32, [_vp, _i32, _i32, _vp, Sampling, _vp, _vp, _vp, _sz, _vp]),
     "accept_prefix": (_i32, [_vp, _i32, _vp, _i32, _vp, _vp, _vp]),
+    "toy_decoder_create": (_i32, [C.POINTER(DecoderConfig), C.POINTER(DecoderWeights), _vp, _vp, _i32,
+                                  C.POINTER(_vp)]),
+    "toy_decoder_destroy": (None, [_vp]),
+    "verify_step_workspace": (_sz, [_vp]),
+    "verify_step": (_i32, [_vp, _vp, _i32, _i64, Sampling, _vp, _vp, _vp, _vp, _sz, _vp]),
     "ev_w4_timing": (_i32, [_i32]),
     "ev_w4_timing_read": (_i32, [C.POINTER(_i64), C.POINTER(C.c_double), C.POINTER(C.c_double)]),
 }
@@ -260,6 +283,85 @@ def accept_prefix(sampled, draft, n_accept=None, n_commit=None, stream=None):
         _dev(n_accept, "n_accept", (torch.int32,)), _dev(n_commit, "n_commit", (torch.int32,)),
         _stream(stream)))
     return n_accept, n_commit
+
+
+class ToyDecoder:
+    """A decoder whose weights and K/V caches live on the device, driven by
+    verify_step.  `weights` holds device tensors: embed [V][H] bf16,
+    final_norm [H] fp32, lm (PackedW4), and per layer (list `layers` of dicts)
+    attn_norm, mlp_norm [H] fp32 and packed qkv, o, gate, up, down.  The caches
+    are [layers][kv_heads][max_ctx][128] fp16 device tensors."""
+
+    def __init__(self, cfg, weights, k_cache, v_cache):
+        self.cfg = cfg
+        self.weights, self.k_cache, self.v_cache = weights, k_cache, v_cache
+        self.max_ctx = int(k_cache.shape[2])
+        c = DecoderConfig(cfg["layers"], cfg["hidden"], cfg["heads"], cfg["kv_heads"],
+                          cfg["head_dim"], cfg["inter"], cfg["vocab"], cfg["G"],
+                          float(cfg["rope_base"]), float(cfg["eps"]))
+        L = weights["layers"]
+        self._layers = (DecoderLayer * len(L))(*[
+            DecoderLayer(_dev(y["attn_norm"], "attn_norm", (torch.float32,)).value,
+                         _dev(y["qkv"].blob, "qkv", _U8).value, _dev(y["o"].blob, "o", _U8).value,
+                         _dev(y["mlp_norm"], "mlp_norm", (torch.float32,)).value,
+                         _dev(y["gate"].blob, "gate", _U8).value, _dev(y["up"].blob, "up", _U8).value,
+                         _dev(y["down"].blob, "down", _U8).value) for y in L])
+        w = DecoderWeights(_dev(weights["embed"], "embed", _B16).value, self._layers,
+                           _dev(weights["final_norm"], "final_norm", (torch.float32,)).value,
+                           _dev(weights["lm"].blob, "lm", _U8).value)
+        h = C.c_void_p()
+        _check(lib().toy_decoder_create(C.byref(c), C.byref(w), _dev(k_cache, "k_cache", _F16),
+                                        _dev(v_cache, "v_cache", _F16), self.max_ctx, C.byref(h)))
+        self._h = h
+        self.ws = torch.empty(int(lib().verify_step_workspace(h)), dtype=torch.uint8,
+                              device=k_cache.device)
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value and _lib is not None:
+            _lib.toy_decoder_destroy(h)
+            self._h = None
+
+    def verify_step(self, tokens, pos0, temperature, top_k, top_p, seed, sampled=None,
+                    n_commit=None, logits=None, stream=None):
+        """One verify pass over tokens [R] int32 (device) at slots pos0..; returns
+        (sampled [R] int32, n_commit [1] int32), device tensors."""
+        R = tokens.shape[0]
+        dev = tokens.device
+        if sampled is None:
+            sampled = torch.empty(R, dtype=torch.int32, device=dev)
+        if n_commit is None:
+            n_commit = torch.empty(1, dtype=torch.int32, device=dev)
+        sp = Sampling(float(temperature), int(top_k), float(top_p), int(seed) & ((1 << 64) - 1))
+        _check(lib().verify_step(
+            self._h, _dev(tokens, "tokens", (torch.int32,)), R, int(pos0), sp,
+            _dev(sampled, "sampled", (torch.int32,)), _dev(n_commit, "n_commit", (torch.int32,)),
+            None if logits is None else _dev(logits, "logits", (torch.float32,)),
+            C.c_void_p(self.ws.data_ptr()), self.ws.numel(), _stream(stream)))
+        return sampled, n_commit
+
+
+def load_decoder(cfg, w, kc, vc, device="cuda"):
+    """Upload a decoder given in standard layouts (numpy: embed [V][H] bf16 bits,
+    norms fp32, W4 q/s/b per matrix stacked over layers, caches fp16 bits) and
+    pack its matrices; returns a ToyDecoder."""
+    import numpy as np
+
+    def t(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            a = a.view(np.int16)
+        return torch.from_numpy(a).to(device)
+
+    def pack(name, l=None):
+        q, s_, b = (w[name + p] if l is None else w[name + p][l] for p in ("_q", "_s", "_b"))
+        return w4_pack(t(q), t(s_), t(b), cfg["G"])
+
+    layers = [dict(attn_norm=t(w["attn_norm"][l]), mlp_norm=t(w["mlp_norm"][l]),
+                   qkv=pack("qkv", l), o=pack("o", l), gate=pack("gate", l), up=pack("up", l),
+                   down=pack("down", l)) for l in range(cfg["layers"])]
+    weights = dict(embed=t(w["embed"]), final_norm=t(w["final_norm"]), lm=pack("lm"), layers=layers)
+    return ToyDecoder(cfg, weights, t(kc), t(vc))
 
 
 def w4_timing(enable):

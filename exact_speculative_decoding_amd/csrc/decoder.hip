@@ -1,0 +1,527 @@
+// Verify step of a small decoder on gfx950: the whole model over the R rows of
+// one drafted-decoding round, row-exact end to end.
+//
+// TensorFold README, exactness paragraph: a row of a multi-row verify pass gets
+// the same bits as a one-row step, so drafted decoding commits the bytes serial
+// decoding would.  Every kernel below keeps that property by construction:
+//   * the W4 linears are the row-exact verify kernel (w4_verify.hip);
+//   * norms, RoPE, cache writes and the residual stream are per row, with
+//     reductions in a fixed tree that does not depend on R;
+//   * attention splits the key slots at absolute boundaries (chunks of
+//     kAttnChunk, sub-blocks of kAttnSub), so row r at position p sees the same
+//     chunks, sub-blocks and online-softmax updates whatever other rows share
+//     the pass; slots past p are skipped, never added as zeros; the chunks are
+//     merged in ascending order;
+//   * row r writes cache slot p and reads slots <= p only, all of which hold the
+//     bytes serial decoding wrote (slot p in this pass, from the same input).
+//
+// Launches per layer: W4 q|k|v, split sum + RoPE + fp16 cache write, attention
+// partials, chunk merge, W4 o, split sum + residual + RMSNorm, W4 gate|up,
+// split sum + SiLU * up, W4 down, split sum + residual + RMSNorm (with the next
+// layer's gains or the final ones).  Then W4 LM head, split sum, keyed sample,
+// accept prefix.
+#include <math.h>
+
+#include <algorithm>
+#include <vector>
+
+#include "w4_kernel.h"
+
+namespace ev {
+
+constexpr int kHD = 128;          // head dimension
+constexpr int kHalf = kHD / 2;
+constexpr int kAttnChunk = 256;   // key slots per attention partial (absolute boundaries)
+constexpr int kAttnSub = 64;      // key slots per LDS sub-block
+constexpr int kMaxQ = 64;         // queries per attention workgroup: R * heads / kv_heads
+constexpr int kPartStride = kHD + 2;  // one attention partial: m, l, acc[128]
+
+struct RopeTab {
+    double invf[kHalf];  // rope_base^(-2i/128), computed once on the host
+};
+
+// Sum of one value per thread over a 256-thread block, in a fixed tree.
+__device__ __forceinline__ float block_sum256(float v, float* red) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+    const int tid = threadIdx.x;
+    if ((tid & 63) == 0) red[tid >> 6] = v;
+    __syncthreads();
+    const float t = ((red[0] + red[1]) + red[2]) + red[3];
+    __syncthreads();
+    return t;
+}
+
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float v) {
+    return __builtin_bit_cast(uint16_t, (_Float16)v);
+}
+
+// x[r] = embedding row of tokens[r] (bf16 -> fp32); n[r] = bf16(RMSNorm(x) *
+// gain); positions[r] = pos0 + 1 + r (the positions the rows sample).
+__global__ __launch_bounds__(256) void embed_norm_kernel(const int* __restrict__ tokens,
+                                                         const uint16_t* __restrict__ embed, int H, int V,
+                                                         const float* __restrict__ gain, float eps,
+                                                         float* __restrict__ x, uint16_t* __restrict__ n,
+                                                         long long* __restrict__ positions, long long pos0) {
+    __shared__ float red[4];
+    const int r = blockIdx.x, tid = threadIdx.x;
+    int tok = tokens[r];
+    tok = tok < 0 ? 0 : (tok >= V ? V - 1 : tok);  // keeps the read inside the table
+    const uint16_t* e = embed + (size_t)tok * H;
+    float ss = 0.f;
+    for (int c = tid; c < H; c += 256) {
+        const float v = bf16_to_f32(e[c]);
+        x[(size_t)r * H + c] = v;
+        ss += v * v;
+    }
+    const float rs = 1.0f / sqrtf(block_sum256(ss, red) / (float)H + eps);
+    for (int c = tid; c < H; c += 256)
+        n[(size_t)r * H + c] = f32_to_bf16_rne(bf16_to_f32(e[c]) * rs * gain[c]);
+    if (tid == 0) positions[r] = pos0 + 1 + r;
+}
+
+// x[r] += sum over s ascending of part[s][r] (a linear's split partials);
+// n[r] = bf16(RMSNorm(x[r]) * gain).
+__global__ __launch_bounds__(256) void res_norm_kernel(const float* __restrict__ part, int S, int H,
+                                                       float* __restrict__ x, const float* __restrict__ gain,
+                                                       float eps, uint16_t* __restrict__ n) {
+    __shared__ float red[4];
+    const int r = blockIdx.x, tid = threadIdx.x;
+    const size_t stride = (size_t)16 * H;
+    float ss = 0.f;
+    for (int c = tid; c < H; c += 256) {
+        const size_t o = (size_t)r * H + c;
+        float lin = part[o];
+        for (int s = 1; s < S; ++s) lin += part[s * stride + o];
+        const float v = x[o] + lin;
+        x[o] = v;
+        ss += v * v;
+    }
+    const float rs = 1.0f / sqrtf(block_sum256(ss, red) / (float)H + eps);
+    for (int c = tid; c < H; c += 256) {
+        const size_t o = (size_t)r * H + c;
+        n[o] = f32_to_bf16_rne(x[o] * rs * gain[c]);
+    }
+}
+
+// q|k|v of row r = split sums; rotate q and k by position pos0 + r; q to
+// qout [R][NH][128] fp32, k and v to cache slot pos0 + r in fp16.
+__global__ __launch_bounds__(256) void qkv_rope_kernel(const float* __restrict__ part, int S, int NH, int NKV,
+                                                       long long pos0, RopeTab rt, float* __restrict__ qout,
+                                                       uint16_t* __restrict__ kc, uint16_t* __restrict__ vc,
+                                                       int C) {
+    const int r = blockIdx.x, tid = threadIdx.x;
+    const long long P = pos0 + r;
+    const int NQKV = (NH + 2 * NKV) * kHD;
+    const size_t stride = (size_t)16 * NQKV;
+    const float* row = part + (size_t)r * NQKV;
+    auto colsum = [&](int c) {
+        float a = row[c];
+        for (int s = 1; s < S; ++s) a += row[s * stride + c];
+        return a;
+    };
+    for (int p = tid; p < (NH + NKV) * kHalf; p += 256) {
+        const int hd = p / kHalf, i = p % kHalf;
+        const float a = colsum(hd * kHD + i), b = colsum(hd * kHD + i + kHalf);
+        const double ang = (double)P * rt.invf[i];
+        const float c = (float)cos(ang), s = (float)sin(ang);
+        const float a2 = a * c - b * s;
+        const float b2 = b * c + a * s;
+        if (hd < NH) {
+            float* q = qout + ((size_t)r * NH + hd) * kHD;
+            q[i] = a2;
+            q[i + kHalf] = b2;
+        } else {
+            uint16_t* k = kc + ((size_t)(hd - NH) * C + P) * kHD;
+            k[i] = f32_to_f16_bits(a2);
+            k[i + kHalf] = f32_to_f16_bits(b2);
+        }
+    }
+    for (int p = tid; p < NKV * kHD; p += 256) {
+        const int g = p / kHD, d = p % kHD;
+        vc[((size_t)g * C + P) * kHD + d] = f32_to_f16_bits(colsum((NH + NKV) * kHD + p));
+    }
+}
+
+struct AttnArgs {
+    const float* q;      // [R][NH][128]
+    const uint16_t* kc;  // this layer's keys [NKV][C][128] fp16
+    const uint16_t* vc;
+    float* part;         // [16][NH][nchunk_max][130]
+    int R, NH, NKV, C, nchunk_max;
+    long long pos0;
+    float scale;         // 1/sqrt(128)
+};
+
+// Attention partials of chunk blockIdx.x (slots [256 c, 256 c + 256)) for kv
+// head blockIdx.y and all queries that read it (R rows x heads/kv_heads).  Per
+// query: running max m, sum l and acc[128] over its valid slots, sub-block by
+// sub-block in ascending order.
+__global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
+    __shared__ float Qs[kMaxQ][kHD];
+    __shared__ uint16_t Kt[kHD][kAttnSub + 2];
+    __shared__ __align__(16) uint16_t Vs[kAttnSub][kHD];
+    __shared__ float Ps[kMaxQ][kAttnSub];
+    __shared__ float sm[kMaxQ], sl[kMaxQ], ssc[kMaxQ];
+    __shared__ int snv[kMaxQ];
+
+    const int tid = threadIdx.x;
+    const int chunk = blockIdx.x, g = blockIdx.y;
+    const int gq = a.NH / a.NKV, nq = a.R * gq;
+    const long long cstart = (long long)chunk * kAttnChunk;
+    const long long pmax = a.pos0 + a.R - 1;
+    const uint16_t* kb = a.kc + (size_t)g * a.C * kHD;
+    const uint16_t* vb = a.vc + (size_t)g * a.C * kHD;
+
+    for (int e = tid; e < nq * kHD; e += 256) {
+        const int qi = e / kHD, d = e % kHD;
+        const int r = qi / gq, hh = qi % gq;
+        Qs[qi][d] = a.q[((size_t)r * a.NH + g * gq + hh) * kHD + d];
+    }
+    if (tid < kMaxQ) {
+        sm[tid] = -INFINITY;
+        sl[tid] = 0.f;
+    }
+    float acc[kMaxQ / 2];
+#pragma unroll
+    for (int i = 0; i < kMaxQ / 2; ++i) acc[i] = 0.f;
+    __syncthreads();
+
+    for (int sb = 0; sb < kAttnChunk / kAttnSub; ++sb) {
+        const long long base = cstart + (long long)sb * kAttnSub;
+        if (base > pmax) break;  // uniform
+        {   // stage keys (transposed) and values of slots base .. base + 63
+            const int j = tid >> 2, dp = (tid & 3) * 32;
+            const long long slot = base + j;
+            u32x4 kv[4], vv[4];
+            if (slot <= pmax) {
+                const u32x4* ks = reinterpret_cast<const u32x4*>(kb + (size_t)slot * kHD + dp);
+                const u32x4* vs = reinterpret_cast<const u32x4*>(vb + (size_t)slot * kHD + dp);
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    kv[u] = ks[u];
+                    vv[u] = vs[u];
+                }
+            } else {
+#pragma unroll
+                for (int u = 0; u < 4; ++u) kv[u] = vv[u] = u32x4{0u, 0u, 0u, 0u};
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                *reinterpret_cast<u32x4*>(&Vs[j][dp + 8 * u]) = vv[u];
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    Kt[dp + 8 * u + 2 * w][j] = (uint16_t)(kv[u][w] & 0xffffu);
+                    Kt[dp + 8 * u + 2 * w + 1][j] = (uint16_t)(kv[u][w] >> 16);
+                }
+            }
+        }
+        __syncthreads();
+        {   // scores: lane = slot, wave w = queries w, w + 4, ...
+            const int jj = tid & 63, wq = tid >> 6;
+#pragma unroll
+            for (int i = 0; i < kMaxQ / 4; ++i) {
+                const int qi = wq + 4 * i;
+                if (qi < nq) {
+                    float s = 0.f;
+                    for (int d = 0; d < kHD; ++d)
+                        s = fmaf(Qs[qi][d], (float)__builtin_bit_cast(_Float16, Kt[d][jj]), s);
+                    Ps[qi][jj] = s * a.scale;
+                }
+            }
+        }
+        __syncthreads();
+        if (tid < nq) {  // online softmax update of query tid over its valid slots
+            const int qi = tid;
+            const long long P = a.pos0 + qi / gq;
+            long long nvl = P - base + 1;
+            const int nv = nvl < 0 ? 0 : (nvl > kAttnSub ? kAttnSub : (int)nvl);
+            snv[qi] = nv;
+            if (nv > 0) {
+                float mx = Ps[qi][0];
+                for (int j = 1; j < nv; ++j) mx = fmaxf(mx, Ps[qi][j]);
+                const float mold = sm[qi], mnew = fmaxf(mold, mx);
+                const float sc = expf(mold - mnew);
+                float lsum = 0.f;
+                for (int j = 0; j < nv; ++j) {
+                    const float p = expf(Ps[qi][j] - mnew);
+                    Ps[qi][j] = p;
+                    lsum += p;
+                }
+                sl[qi] = sl[qi] * sc + lsum;
+                sm[qi] = mnew;
+                ssc[qi] = sc;
+            }
+        }
+        __syncthreads();
+        {   // acc[q][d] = acc * scale + sum_j p_j v_j[d]; thread = d, queries qh, qh + 2, ...
+            const int d = tid & (kHD - 1), qh = tid >> 7;
+#pragma unroll
+            for (int i = 0; i < kMaxQ / 2; ++i) {
+                const int qi = qh + 2 * i;
+                if (qi < nq) {
+                    const int nv = snv[qi];
+                    if (nv > 0) {
+                        float t = 0.f;
+                        for (int j = 0; j < nv; ++j)
+                            t = fmaf(Ps[qi][j], (float)__builtin_bit_cast(_Float16, Vs[j][d]), t);
+                        acc[i] = fmaf(acc[i], ssc[qi], t);
+                    }
+                }
+            }
+        }
+        __syncthreads();
+    }
+
+    const int d = tid & (kHD - 1), qh = tid >> 7;
+#pragma unroll
+    for (int i = 0; i < kMaxQ / 2; ++i) {
+        const int qi = qh + 2 * i;
+        if (qi < nq) {
+            const int r = qi / gq;
+            if (a.pos0 + r >= cstart) {
+                const int h = g * gq + qi % gq;
+                float* o = a.part + (((size_t)r * a.NH + h) * a.nchunk_max + chunk) * kPartStride;
+                o[2 + d] = acc[i];
+                if (d == 0) {
+                    o[0] = sm[qi];
+                    o[1] = sl[qi];
+                }
+            }
+        }
+    }
+}
+
+// o[r][h][d] = bf16(sum_c acc_c[d] e^(m_c - M) / sum_c l_c e^(m_c - M)) over
+// the chunks c = 0 .. (pos0 + r) / 256, ascending.
+__global__ __launch_bounds__(kHD) void attn_merge_kernel(const float* __restrict__ part, int NH, int nchunk_max,
+                                                         long long pos0, uint16_t* __restrict__ o) {
+    const int r = blockIdx.x, h = blockIdx.y, d = threadIdx.x;
+    const int nch = (int)((pos0 + r) / kAttnChunk) + 1;
+    const float* b = part + ((size_t)r * NH + h) * nchunk_max * kPartStride;
+    float M = -INFINITY;
+    for (int c = 0; c < nch; ++c) M = fmaxf(M, b[(size_t)c * kPartStride]);
+    float L = 0.f, acc = 0.f;
+    for (int c = 0; c < nch; ++c) {
+        const float* pc = b + (size_t)c * kPartStride;
+        const float e = expf(pc[0] - M);
+        L = fmaf(pc[1], e, L);
+        acc = fmaf(pc[2 + d], e, acc);
+    }
+    o[((size_t)r * NH + h) * kHD + d] = f32_to_bf16_rne(acc / L);
+}
+
+// Workspace of a verify step, from the configuration and max_ctx only.
+struct StepLayout {
+    W4Plan p_qkv, p_o, p_gu, p_down, p_lm;
+    int nchunk_max;
+    size_t off_x, off_n, off_o, off_q, off_part, off_pg, off_pu, off_h, off_att, off_logits, off_pos, off_acc,
+        off_sws, total;
+};
+
+}  // namespace ev
+
+using namespace ev;
+
+struct ev_decoder {
+    ev_decoder_config cfg;
+    std::vector<ev_decoder_layer> layers;
+    const uint16_t* embed;
+    const float* final_norm;
+    const void* w_lm;
+    uint16_t* kc;
+    uint16_t* vc;
+    int C;
+    RopeTab rope;
+    int NQKV, DQ;
+    StepLayout L;
+};
+
+static StepLayout step_layout(const ev_decoder_config& c, int NQKV, int DQ, int C) {
+    StepLayout L;
+    const int H = c.hidden, I = c.intermediate, V = c.vocab;
+    L.p_qkv = plan_w4(NQKV, H, 1);
+    L.p_o = plan_w4(H, DQ, 1);
+    L.p_gu = plan_w4(I, H, 2);
+    L.p_down = plan_w4(H, I, 1);
+    L.p_lm = plan_w4(V, H, 1);
+    L.nchunk_max = (C + kAttnChunk - 1) / kAttnChunk;
+    size_t part = (size_t)L.p_qkv.S * NQKV;
+    part = std::max(part, (size_t)L.p_o.S * H);
+    part = std::max(part, (size_t)L.p_down.S * H);
+    part = std::max(part, (size_t)L.p_lm.S * V);
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t o = off;
+        off += align256(bytes);
+        return o;
+    };
+    L.off_x = take(sizeof(float) * 16 * H);
+    L.off_n = take(sizeof(uint16_t) * 16 * H);
+    L.off_o = take(sizeof(uint16_t) * 16 * DQ);
+    L.off_q = take(sizeof(float) * 16 * DQ);
+    L.off_part = take(sizeof(float) * 16 * part);
+    L.off_pg = take(sizeof(float) * 16 * (size_t)L.p_gu.S * I);
+    L.off_pu = take(sizeof(float) * 16 * (size_t)L.p_gu.S * I);
+    L.off_h = take(sizeof(uint16_t) * 16 * I);
+    L.off_att = take(sizeof(float) * 16 * (size_t)c.heads * L.nchunk_max * kPartStride);
+    L.off_logits = take(sizeof(float) * 16 * (size_t)V);
+    L.off_pos = take(sizeof(long long) * 16);
+    L.off_acc = take(sizeof(int32_t) * 4);
+    L.off_sws = take(keyed_sample_workspace(V));
+    L.total = off;
+    return L;
+}
+
+extern "C" int32_t toy_decoder_create(const ev_decoder_config* cfg, const ev_decoder_weights* w, uint16_t* k_cache,
+                                      uint16_t* v_cache, int32_t max_ctx, ev_decoder** out) {
+    clear_error();
+    const char* who = "toy_decoder_create";
+    if (!cfg || !w || !out || !w->layers) return fail(EV_EINVAL, "%s: NULL pointer", who);
+    *out = nullptr;
+    const ev_decoder_config c = *cfg;
+    if (c.layers < 1 || c.layers > 1024) return fail(EV_EINVAL, "%s: layers=%d", who, c.layers);
+    if (c.head_dim != kHD) return fail(EV_EUNSUPPORTED, "%s: head_dim=%d (128 only)", who, c.head_dim);
+    if (c.heads < 1 || c.kv_heads < 1 || c.heads % c.kv_heads != 0)
+        return fail(EV_EINVAL, "%s: heads=%d kv_heads=%d", who, c.heads, c.kv_heads);
+    if ((c.heads / c.kv_heads) * EV_MAX_LANES > kMaxQ)
+        return fail(EV_EUNSUPPORTED, "%s: heads / kv_heads = %d above 4", who, c.heads / c.kv_heads);
+    if (c.vocab < 2 || c.vocab > 262144) return fail(EV_EUNSUPPORTED, "%s: vocab=%d (2..262144)", who, c.vocab);
+    if (!(c.rope_base > 0.0) || !(c.rope_base < __builtin_huge_val()) || !(c.rms_eps >= 0.0) ||
+        !(c.rms_eps < __builtin_huge_val()))
+        return fail(EV_EINVAL, "%s: rope_base must be finite > 0 and rms_eps finite >= 0", who);
+    if (max_ctx < 1 || max_ctx > (1 << 22)) return fail(EV_EINVAL, "%s: max_ctx=%d", who, max_ctx);
+    const int NQKV = (c.heads + 2 * c.kv_heads) * kHD, DQ = c.heads * kHD;
+    int32_t rc;
+    if ((rc = check_w4_dims(who, c.hidden, NQKV, c.group)) || (rc = check_w4_dims(who, DQ, c.hidden, c.group)) ||
+        (rc = check_w4_dims(who, c.hidden, c.intermediate, c.group)) ||
+        (rc = check_w4_dims(who, c.intermediate, c.hidden, c.group)) ||
+        (rc = check_w4_dims(who, c.hidden, c.vocab, c.group)))
+        return rc;
+    if (!w->embed || !w->final_norm || !w->w_lm || !k_cache || !v_cache)
+        return fail(EV_EINVAL, "%s: NULL pointer", who);
+    if (!aligned(w->embed, 2) || !aligned(w->final_norm, 4) || !aligned(w->w_lm, 16) || !aligned(k_cache, 16) ||
+        !aligned(v_cache, 16))
+        return fail(EV_EINVAL, "%s: misaligned pointer", who);
+    for (int l = 0; l < c.layers; ++l) {
+        const ev_decoder_layer& y = w->layers[l];
+        if (!y.attn_norm || !y.w_qkv || !y.w_o || !y.mlp_norm || !y.w_gate || !y.w_up || !y.w_down)
+            return fail(EV_EINVAL, "%s: layer %d: NULL pointer", who, l);
+        if (!aligned(y.attn_norm, 4) || !aligned(y.mlp_norm, 4) || !aligned(y.w_qkv, 16) || !aligned(y.w_o, 16) ||
+            !aligned(y.w_gate, 16) || !aligned(y.w_up, 16) || !aligned(y.w_down, 16))
+            return fail(EV_EINVAL, "%s: layer %d: misaligned pointer", who, l);
+    }
+    ev_decoder* m = new ev_decoder;
+    m->cfg = c;
+    m->layers.assign(w->layers, w->layers + c.layers);
+    m->embed = w->embed;
+    m->final_norm = w->final_norm;
+    m->w_lm = w->w_lm;
+    m->kc = k_cache;
+    m->vc = v_cache;
+    m->C = max_ctx;
+    for (int i = 0; i < kHalf; ++i) m->rope.invf[i] = pow(c.rope_base, -2.0 * i / kHD);
+    m->NQKV = NQKV;
+    m->DQ = DQ;
+    m->L = step_layout(c, NQKV, DQ, max_ctx);
+    *out = m;
+    return EV_OK;
+}
+
+extern "C" void toy_decoder_destroy(ev_decoder* m) { delete m; }
+
+extern "C" size_t verify_step_workspace(const ev_decoder* m) { return m ? m->L.total : 0; }
+
+extern "C" int32_t verify_step(ev_decoder* m, const int32_t* tokens, int32_t R, int64_t pos0, ev_sampling sampling,
+                               int32_t* sampled, int32_t* n_commit, float* logits, void* ws, size_t ws_bytes,
+                               void* stream) {
+    clear_error();
+    const char* who = "verify_step";
+    int32_t rc;
+    if (!m) return fail(EV_EINVAL, "%s: NULL decoder", who);
+    if ((rc = check_lanes(who, R))) return rc;
+    if (!tokens || !sampled || !n_commit) return fail(EV_EINVAL, "%s: NULL pointer", who);
+    if (!aligned(tokens, 4) || !aligned(sampled, 4) || !aligned(n_commit, 4) || (logits && !aligned(logits, 16)))
+        return fail(EV_EINVAL, "%s: misaligned pointer", who);
+    if (pos0 < 0 || pos0 + R > m->C)
+        return fail(EV_EINVAL, "%s: slots %lld..%lld outside the cache of %d", who, (long long)pos0,
+                    (long long)pos0 + R - 1, m->C);
+    if ((rc = check_sampling(who, sampling))) return rc;
+    const StepLayout& L = m->L;
+    if ((rc = check_ws(who, ws, ws_bytes, L.total))) return rc;
+
+    const ev_decoder_config& c = m->cfg;
+    const int H = c.hidden, I = c.intermediate, V = c.vocab, G = c.group, NH = c.heads, NKV = c.kv_heads;
+    const float eps = (float)c.rms_eps;
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    unsigned char* b = reinterpret_cast<unsigned char*>(ws);
+    float* x = reinterpret_cast<float*>(b + L.off_x);
+    uint16_t* n = reinterpret_cast<uint16_t*>(b + L.off_n);
+    uint16_t* o = reinterpret_cast<uint16_t*>(b + L.off_o);
+    float* q = reinterpret_cast<float*>(b + L.off_q);
+    float* part = reinterpret_cast<float*>(b + L.off_part);
+    float* pg = reinterpret_cast<float*>(b + L.off_pg);
+    float* pu = reinterpret_cast<float*>(b + L.off_pu);
+    uint16_t* h = reinterpret_cast<uint16_t*>(b + L.off_h);
+    float* att = reinterpret_cast<float*>(b + L.off_att);
+    float* lg = logits ? logits : reinterpret_cast<float*>(b + L.off_logits);
+    int64_t* pos = reinterpret_cast<int64_t*>(b + L.off_pos);
+    int32_t* n_accept = reinterpret_cast<int32_t*>(b + L.off_acc);
+    void* sws = b + L.off_sws;
+
+    auto linear = [&](const void* wmat, const uint16_t* xin, int K, int N, const W4Plan& p) {
+        W4Args a{};
+        a.w[0] = a.w[1] = reinterpret_cast<const uint8_t*>(wmat);
+        a.out[0] = a.out[1] = part;
+        a.x = xin;
+        a.R = R;
+        a.N = N;
+        a.split_stride = (long)16 * N;
+        return launch_w4(a, 1, p, K, G, st);
+    };
+
+    hipLaunchKernelGGL(embed_norm_kernel, dim3(R), dim3(256), 0, st, tokens, m->embed, H, V, m->layers[0].attn_norm,
+                       eps, x, n, reinterpret_cast<long long*>(pos), (long long)pos0);
+    if ((rc = check_hip(hipGetLastError(), "embed_norm launch"))) return rc;
+
+    const int nchunks = (int)((pos0 + R - 1) / kAttnChunk) + 1;
+    for (int l = 0; l < c.layers; ++l) {
+        const ev_decoder_layer& y = m->layers[l];
+        uint16_t* kcl = m->kc + (size_t)l * NKV * m->C * kHD;
+        uint16_t* vcl = m->vc + (size_t)l * NKV * m->C * kHD;
+        if ((rc = linear(y.w_qkv, n, H, m->NQKV, L.p_qkv))) return rc;
+        hipLaunchKernelGGL(qkv_rope_kernel, dim3(R), dim3(256), 0, st, part, L.p_qkv.S, NH, NKV, (long long)pos0,
+                           m->rope, q, kcl, vcl, m->C);
+        if ((rc = check_hip(hipGetLastError(), "qkv_rope launch"))) return rc;
+        AttnArgs aa{q, kcl, vcl, att, R, NH, NKV, m->C, L.nchunk_max, (long long)pos0, 0.08838834764831845f};
+        hipLaunchKernelGGL(attn_partial_kernel, dim3(nchunks, NKV), dim3(256), 0, st, aa);
+        if ((rc = check_hip(hipGetLastError(), "attn_partial launch"))) return rc;
+        hipLaunchKernelGGL(attn_merge_kernel, dim3(R, NH), dim3(kHD), 0, st, att, NH, L.nchunk_max, (long long)pos0, o);
+        if ((rc = check_hip(hipGetLastError(), "attn_merge launch"))) return rc;
+        if ((rc = linear(y.w_o, o, m->DQ, H, L.p_o))) return rc;
+        hipLaunchKernelGGL(res_norm_kernel, dim3(R), dim3(256), 0, st, part, L.p_o.S, H, x, y.mlp_norm, eps, n);
+        if ((rc = check_hip(hipGetLastError(), "res_norm launch"))) return rc;
+        {
+            W4Args a{};
+            a.w[0] = reinterpret_cast<const uint8_t*>(y.w_gate);
+            a.w[1] = reinterpret_cast<const uint8_t*>(y.w_up);
+            a.out[0] = pg;
+            a.out[1] = pu;
+            a.x = n;
+            a.R = R;
+            a.N = I;
+            a.split_stride = (long)16 * I;
+            if ((rc = launch_w4(a, 2, L.p_gu, H, G, st))) return rc;
+        }
+        if ((rc = launch_silu_reduce(pg, pu, L.p_gu.S, I, R, h, nullptr, 1, nullptr, nullptr, 0, 0, st))) return rc;
+        if ((rc = linear(y.w_down, h, I, H, L.p_down))) return rc;
+        const float* next = l + 1 < c.layers ? m->layers[l + 1].attn_norm : m->final_norm;
+        hipLaunchKernelGGL(res_norm_kernel, dim3(R), dim3(256), 0, st, part, L.p_down.S, H, x, next, eps, n);
+        if ((rc = check_hip(hipGetLastError(), "res_norm launch"))) return rc;
+    }
+    if ((rc = linear(m->w_lm, n, H, V, L.p_lm))) return rc;
+    if ((rc = launch_splitk_reduce(part, L.p_lm.S, V, R, lg, st))) return rc;
+    if ((rc = keyed_sample(lg, R, V, pos, sampling, sampled, nullptr, sws, keyed_sample_workspace(V), stream)))
+        return rc;
+    return accept_prefix(sampled, R, R > 1 ? tokens + 1 : nullptr, R - 1, n_accept, n_commit, stream);
+}

@@ -16,6 +16,9 @@ void clear_error();
 // Check the result of a launch / runtime call.
 int32_t check_hip(hipError_t e, const char* what);
 
+// Sampling parameters as keyed_sample accepts them (EV_OK or the error code).
+int32_t check_sampling(const char* who, const ev_sampling& s);
+
 inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 // ---- device helpers -------------------------------------------------------

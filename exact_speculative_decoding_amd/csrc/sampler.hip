@@ -200,6 +200,19 @@ static int sample_kk(const ev_sampling& s, int V) {
 
 using namespace ev;
 
+namespace ev {
+int32_t check_sampling(const char* who, const ev_sampling& s) {
+    if (!(s.temperature >= 0.0) || !(s.temperature < __builtin_huge_val()))
+        return fail(EV_EINVAL, "%s: temperature must be finite and >= 0", who);
+    if (s.temperature > 0.0) {
+        if (s.top_k < 1) return fail(EV_EINVAL, "%s: top_k=%d", who, s.top_k);
+        if (s.top_k > EV_MAX_TOPK) return fail(EV_EUNSUPPORTED, "%s: top_k=%d above 64", who, s.top_k);
+        if (!(s.top_p > 0.0 && s.top_p <= 1.0)) return fail(EV_EINVAL, "%s: top_p outside (0,1]", who);
+    }
+    return EV_OK;
+}
+}  // namespace ev
+
 extern "C" size_t keyed_sample_workspace(int32_t V) {
     if (V <= 0) return 0;
     return (size_t)EV_MAX_LANES * sample_nchunk(V) * EV_MAX_TOPK * sizeof(unsigned long long);
@@ -216,13 +229,8 @@ extern "C" int32_t keyed_sample(const float* logits, int32_t R, int32_t V, const
     if (!logits || !positions || !tokens) return fail(EV_EINVAL, "%s: NULL pointer", who);
     if (!aligned(logits, 4) || !aligned(positions, 8) || !aligned(tokens, 4) || (gap && !aligned(gap, 8)))
         return fail(EV_EINVAL, "%s: misaligned pointer", who);
-    if (!(s.temperature >= 0.0) || !(s.temperature < __builtin_huge_val()))
-        return fail(EV_EINVAL, "%s: temperature must be finite and >= 0", who);
-    if (s.temperature > 0.0) {
-        if (s.top_k < 1) return fail(EV_EINVAL, "%s: top_k=%d", who, s.top_k);
-        if (s.top_k > EV_MAX_TOPK) return fail(EV_EUNSUPPORTED, "%s: top_k=%d above 64", who, s.top_k);
-        if (!(s.top_p > 0.0 && s.top_p <= 1.0)) return fail(EV_EINVAL, "%s: top_p outside (0,1]", who);
-    }
+    int32_t rc0 = check_sampling(who, s);
+    if (rc0) return rc0;
     const size_t need = keyed_sample_workspace(V);
     if (!ws || ws_bytes < need)
         return fail(EV_EWORKSPACE, "%s: workspace needs %zu bytes, got %zu", who, need, ws ? ws_bytes : (size_t)0);

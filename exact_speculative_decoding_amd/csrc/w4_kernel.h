@@ -88,6 +88,9 @@ struct W4Args {
 int32_t launch_w4(W4Args args, int nmat, const W4Plan& p, int K, int G, hipStream_t st,
                   int ngroups = 1);
 
+// y[r][n] = sum over s ascending of part[s][r][n] (split stride 16 * N), r < R.
+int32_t launch_splitk_reduce(const float* part, int S, int N, int R, float* y, hipStream_t st);
+
 // h[r][k] = bf16_rne(silu(sum_s pg[s][r][k]) * sum_s pu[s][r][k]) for rows
 // r < R, splits added in ascending s (split stride 16 * I).  Grouped when gcnt
 // != NULL: group g < *gcount (grid z) covers rows < gcnt[g] at offsets

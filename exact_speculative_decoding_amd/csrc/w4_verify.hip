@@ -363,6 +363,12 @@ __global__ __launch_bounds__(64) void silu_reduce_kernel(const float* __restrict
     if (h_copy) *reinterpret_cast<u32x4*>(h_copy + o) = w;
 }
 
+int32_t launch_splitk_reduce(const float* part, int S, int N, int R, float* y, hipStream_t st) {
+    dim3 grid((unsigned)((N + 255) / 256), (unsigned)R);
+    hipLaunchKernelGGL(splitk_reduce_kernel, grid, dim3(64), 0, st, part, S, N, y);
+    return check_hip(hipGetLastError(), "splitk_reduce launch");
+}
+
 int32_t launch_silu_reduce(const float* pg, const float* pu, int S, int I, int R, uint16_t* h,
                            uint16_t* h_copy, int ngroups, const int* gcount, const int* gcnt,
                            long gstride_p, long gstride_h, hipStream_t st) {
@@ -555,11 +561,7 @@ extern "C" int32_t verify_linear_w4(const uint16_t* x, int32_t R, int32_t K, con
     a.N = N;
     a.split_stride = L.p.S > 1 ? (long)16 * N : 0;
     if ((rc = launch_w4(a, 1, L.p, K, G, st))) return rc;
-    if (L.p.S > 1) {
-        dim3 grid((unsigned)((N + 255) / 256), (unsigned)R);
-        hipLaunchKernelGGL(splitk_reduce_kernel, grid, dim3(64), 0, st, part, L.p.S, N, y);
-        if ((rc = check_hip(hipGetLastError(), "splitk_reduce launch"))) return rc;
-    }
+    if (L.p.S > 1 && (rc = launch_splitk_reduce(part, L.p.S, N, R, y, st))) return rc;
     return EV_OK;
 }
 
@@ -610,10 +612,6 @@ extern "C" int32_t verify_mlp_w4(const uint16_t* x, int32_t R, int32_t H, int32_
     d.N = H;
     d.split_stride = L.p2.S > 1 ? (long)16 * H : 0;
     if ((rc = launch_w4(d, 1, L.p2, I, G, st))) return rc;
-    if (L.p2.S > 1) {
-        dim3 grid((unsigned)((H + 255) / 256), (unsigned)R);
-        hipLaunchKernelGGL(splitk_reduce_kernel, grid, dim3(64), 0, st, pd, L.p2.S, H, y);
-        if ((rc = check_hip(hipGetLastError(), "splitk_reduce launch"))) return rc;
-    }
+    if (L.p2.S > 1 && (rc = launch_splitk_reduce(pd, L.p2.S, H, R, y, st))) return rc;
     return EV_OK;
 }

@@ -206,6 +206,94 @@ int32_t accept_prefix(const int32_t* sampled, int32_t R, const int32_t* draft, i
                       int32_t* n_accept, int32_t* n_commit, void* stream);
 
 /* ------------------------------------------------------------------------- */
+/* Verify step of a small decoder (end to end).                               */
+/*                                                                            */
+/* One verify pass of drafted decoding (TensorFold README, exactness          */
+/* paragraph; 650 Group, "TensorFold: the contract is what it does not        */
+/* change"): R rows whose inputs are the last committed token and R-1 drafts  */
+/* go through the whole model at once; row r's logits, sample and cache entry */
+/* are bit-identical to a one-row (serial) step at its position, so a draft   */
+/* is accepted exactly when it equals the serial sample.                      */
+/*                                                                            */
+/* The model: pre-norm decoder layers, each                                   */
+/*   n = bf16(RMSNorm(x) * attn_norm);  q|k|v = W_qkv n  (W4, fp32 out);      */
+/*   rotate-half RoPE on q and k at the row's position p, angle               */
+/*   p * rope_base^(-2i/head_dim) for pair (i, i + head_dim/2);               */
+/*   k, v -> fp16 into cache slot p;  query head h reads kv head              */
+/*   h / (heads / kv_heads) over slots 0..p: softmax(q.k / sqrt(head_dim)) v; */
+/*   x += W_o bf16(attention);  x += MLP(bf16(RMSNorm(x) * mlp_norm)) with    */
+/*   the SiLU-gated MLP of verify_mlp_w4;                                     */
+/* then logits = W_lm bf16(RMSNorm(x) * final_norm), x = the fp32 residual    */
+/* stream starting from the bf16 embedding row of the input token.            */
+/* RMSNorm(x) = x / sqrt(mean(x^2) + rms_eps).                                */
+/* ------------------------------------------------------------------------- */
+typedef struct {
+    int32_t layers;        /* >= 1                                           */
+    int32_t hidden;        /* H                                              */
+    int32_t heads;         /* query heads                                    */
+    int32_t kv_heads;      /* key/value heads; heads / kv_heads in {1,2,4}   */
+    int32_t head_dim;      /* must be 128                                    */
+    int32_t intermediate;  /* MLP width I                                    */
+    int32_t vocab;         /* V <= 262144                                    */
+    int32_t group;         /* W4 group size, 32 or 64                        */
+    double rope_base;      /* > 0                                            */
+    double rms_eps;        /* >= 0                                           */
+} ev_decoder_config;
+
+/* Device pointers of one layer (packed W4 matrices as written by w4_pack).   */
+typedef struct {
+    const float* attn_norm; /* [H] fp32 gains                                */
+    const void* w_qkv;      /* [(heads + 2 kv_heads) * 128][H]: q, k, v rows  */
+    const void* w_o;        /* [H][heads * 128]                              */
+    const float* mlp_norm;  /* [H] fp32 gains                                */
+    const void* w_gate;     /* [I][H]                                        */
+    const void* w_up;       /* [I][H]                                        */
+    const void* w_down;     /* [H][I]                                        */
+} ev_decoder_layer;
+
+typedef struct {
+    const uint16_t* embed;          /* (device) [V][H] bf16                   */
+    const ev_decoder_layer* layers; /* (host) array of `layers` entries,      */
+                                    /* copied by toy_decoder_create           */
+    const float* final_norm;        /* (device) [H] fp32 gains                */
+    const void* w_lm;               /* (device) packed [V][H]                 */
+} ev_decoder_weights;
+
+typedef struct ev_decoder ev_decoder;
+
+/* Creates a host-side handle (no device memory) over the caller's weights    */
+/* and K/V caches k_cache, v_cache: (device) [layers][kv_heads][max_ctx][128] */
+/* fp16 each, 16-byte aligned.  The handle keeps non-owning pointers: the     */
+/* weights and caches must outlive it.  Errors: EV_EINVAL, EV_EUNSUPPORTED.   */
+int32_t toy_decoder_create(const ev_decoder_config* cfg, const ev_decoder_weights* w,
+                           uint16_t* k_cache, uint16_t* v_cache, int32_t max_ctx,
+                           ev_decoder** out);
+void toy_decoder_destroy(ev_decoder* m);
+
+/* Workspace of verify_step: a function of the configuration and max_ctx.     */
+size_t verify_step_workspace(const ev_decoder* m);
+
+/* One verify pass.                                                           */
+/*   tokens   (device) [R] int32: row r's input token, at cache slot pos0 + r */
+/*            (tokens[0] = the last committed token, tokens[1..] the drafts); */
+/*            values outside [0, V) are undefined.                            */
+/*   pos0     slot of tokens[0]; 0 <= pos0 and pos0 + R <= max_ctx.           */
+/*   sampling as keyed_sample; row r samples position pos0 + 1 + r.           */
+/*   sampled  (device) [R] int32, written: the token sampled after each row.  */
+/*   n_commit (device) [1] int32, written: accept_prefix of sampled against   */
+/*            the drafts tokens[1..R-1]; commit sampled[0 .. n_commit-1].     */
+/*   logits   (device, optional, 16-byte aligned) [R][V] fp32: if non-NULL,   */
+/*            the rows' logits are written there.                             */
+/* Writes cache slots pos0 .. pos0+R-1 of every layer; slots at and after     */
+/* pos0 + n_commit are stale and are rewritten by the next round, which       */
+/* starts at pos0 + n_commit with sampled[n_commit-1].  R = 1 is serial       */
+/* decoding.  Limits: 1 <= R <= 16.  Errors: EV_EINVAL, EV_EUNSUPPORTED,      */
+/* EV_EWORKSPACE, EV_EHIP; nothing is launched on a validation error.         */
+int32_t verify_step(ev_decoder* m, const int32_t* tokens, int32_t R, int64_t pos0,
+                    ev_sampling sampling, int32_t* sampled, int32_t* n_commit, float* logits,
+                    void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------- */
 /* Measurement hook for the W4 verify kernel (every entry point that streams  */
 /* W4 weights launches it).  ev_w4_timing(1) allocates (once) a 16 MiB device */
 /* buffer of timing slots; while on, each workgroup of each W4 launch stores  */
