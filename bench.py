@@ -44,6 +44,8 @@ def parse():
     ap.add_argument("--copies", type=int, default=4, help="weight copies rotated per step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--no-legs", action="store_true",
+                    help="skip the LM-head, MoE and decoder legs")
     ap.add_argument("--graph", action="store_true",
                     help="replay each step from a captured HIP graph (checked against eager)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -91,6 +93,124 @@ def cpu_baseline(d, R):
     return {"value": round(gbs, 4), "unit": "GB/s", "cores": int(oracle.num_threads()),
             "kind": "oracle", "seconds": round(dt, 2),
             "sample": f"one {R}-row pass of the MLP slice (all three W4 linears and the glue)"}
+
+
+def _event_time(stream, fn, steps, warmup):
+    import torch
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(steps):
+        fn(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def leg_lm_head(ev, syn, to_dev, stream, steps):
+    """LM head + sampler (5120 -> 151936, G 64): W4 logits of R hidden rows, then
+    the keyed sample (T 0.7, top-k 20, top-p 0.95), per R."""
+    import torch
+    d = syn.lm_head()
+    K, V, G = d["K"], d["V"], d["G"]
+    copies = [ev.w4_pack(*(to_dev(a) for a in d["w"]), G) for _ in range(2)]  # 2 x 437.6 MB
+    h = to_dev(d["h"])
+    y = torch.empty((16, V), dtype=torch.float32, device="cuda")
+    ws = torch.empty(ev.verify_linear_w4_workspace(K, V, G), dtype=torch.uint8, device="cuda")
+    sws = torch.empty(ev.keyed_sample_workspace(V), dtype=torch.uint8, device="cuda")
+    tok = torch.empty(16, dtype=torch.int32, device="cuda")
+    out = {}
+    for R in (1, 2, 4, 8, 16):
+        pos = torch.arange(R, dtype=torch.int64, device="cuda")
+
+        def step(i):
+            ev.verify_linear_w4(h[:R], copies[i % 2], y=y[:R], ws=ws, stream=stream)
+            ev.keyed_sample(y[:R], pos, 0.7, 20, 0.95, 42, tokens=tok[:R], ws=sws, stream=stream)
+        ms = _event_time(stream, step, steps, 3)
+        by = V * K * 0.5 + 4.0 * V * (K // G) + 2.0 * R * K + 4.0 * R * V * 2  # logits written + read
+        out[str(R)] = {"us_per_pass": round(ms * 1e3, 2), "GB_s": round(by / (ms * 1e-3) / 1e9, 1),
+                       "pct_hbm_peak": round(100 * by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 1),
+                       "lanes_per_s": round(R / (ms * 1e-3), 1)}
+    del copies
+    return {"workload": "LM head 5120 -> 151936 W4 G64 + keyed sample", "per_R": out}
+
+
+def leg_moe(ev, syn, to_dev, stream, steps):
+    """MoE verify layer (hidden 2048, 128 experts, top 8, I 768, G 32), per R;
+    bytes = the touched experts' weights (read once) + x + y."""
+    import numpy as np
+    import torch
+    d = syn.moe()
+    H, I, E, top, G = d["H"], d["I"], d["E"], d["top"], d["G"]
+    stacks = [tuple(ev.w4_pack_stack(*(to_dev(a) for a in d[m]), G) for m in ("gate", "up", "down"))
+              for _ in range(2)]  # 2 x 378 MB
+    x = to_dev(d["x"])
+    rho = torch.from_numpy(np.ascontiguousarray(d["rho"])).cuda()
+    ws = torch.empty(ev.verify_moe_w4_workspace(H, I, E, top, G), dtype=torch.uint8, device="cuda")
+    y = torch.empty((16, H), dtype=torch.float32, device="cuda")
+    ids = torch.empty((16, top), dtype=torch.int32, device="cuda")
+    per_expert = 3 * (I * H * 0.5 + 4.0 * I * (H // G))
+    out = {}
+    for R in (1, 2, 4, 8, 16):
+        def step(i):
+            g, u, dn = stacks[i % 2]
+            ev.verify_moe_w4(x[:R], rho[:R], g, u, dn, top, y=y[:R], expert_ids=ids[:R], ws=ws, stream=stream)
+        ms = _event_time(stream, step, steps, 3)
+        touched = len(np.unique(ids[:R].cpu().numpy()))
+        by = touched * per_expert + 2.0 * R * H + 4.0 * R * H
+        out[str(R)] = {"us_per_pass": round(ms * 1e3, 2), "experts": touched,
+                       "GB_s": round(by / (ms * 1e-3) / 1e9, 1),
+                       "pct_hbm_peak": round(100 * by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 1)}
+    del stacks
+    return {"workload": "MoE layer H2048 E128 top8 I768 W4 G32", "per_R": out}
+
+
+def leg_decoder(ev, syn, C, n_tokens=512, R=8, p_draft=0.65):
+    """The 8-layer decoder: serial decoding (R = 1) of n_tokens, then drafted
+    decoding with R - 1 drafts a round that match the serial transcript with
+    probability p_draft; exact accepted tok/s = committed tokens / wall time
+    (host drafter and the one read-back per round included)."""
+    import numpy as np
+    import torch
+    from exact_speculative_decoding_amd.loop import decode
+    d = syn.decoder(C=C)
+    cfg = d["cfg"]
+    pos0, V = cfg["prefill"], cfg["vocab"]
+    samp = (0.7, 20, 0.95, 42)
+
+    def run(m, Rr, drafter):
+        def fn(tokens, pos):
+            s, nc = m.verify_step(torch.tensor(tokens, dtype=torch.int32, device="cuda"), pos, *samp)
+            return s.cpu().tolist(), int(nc.cpu()[0])
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        toks, rounds = decode(fn, d["first_token"], pos0, n_tokens, Rr, drafter)
+        torch.cuda.synchronize()
+        return toks, rounds, time.perf_counter() - t0
+
+    m = ev.load_decoder(cfg, d["w"], d["kc"], d["vc"])
+    kc0, vc0 = m.k_cache.clone(), m.v_cache.clone()
+    run(m, 1, lambda p, c: [])  # warm-up
+    m.k_cache.copy_(kc0)
+    m.v_cache.copy_(vc0)
+    serial, _, t_serial = run(m, 1, lambda p, c: [])
+    m.k_cache.copy_(kc0)
+    m.v_cache.copy_(vc0)
+    drafted, rounds, t_drafted = run(m, R, syn.transcript_drafter(serial, pos0 + 1, p_draft, 21, V))
+    w_bytes = sum(np.asarray(d["w"][k]).nbytes for k in d["w"] if k.endswith(("_q", "_s", "_b")))
+    kv_round = 2 * cfg["layers"] * cfg["kv_heads"] * (pos0 + n_tokens // 2) * cfg["head_dim"] * 2
+    per_round = n_tokens / rounds
+    roof = per_round * HBM_PEAK_GBS * 1e9 / (w_bytes + kv_round)
+    tps = n_tokens / t_drafted
+    return {"workload": f"8-layer decoder H2048 16/4 heads MLP6144 V32768 W4 G64, cache {C}",
+            "tokens": n_tokens, "R": R, "draft_match": p_draft, "rounds": rounds,
+            "tokens_per_round": round(per_round, 3), "identical_to_serial": drafted == serial,
+            "accepted_tok_s": round(tps, 1), "serial_tok_s": round(n_tokens / t_serial, 1),
+            "ms_per_round": round(1e3 * t_drafted / rounds, 3),
+            "bytes_per_round": int(w_bytes + kv_round),
+            "roofline_tok_s": round(roof, 1), "pct_roofline": round(100 * tps / roof, 2)}
 
 
 def main():
@@ -234,6 +354,18 @@ def main():
         "per_R": per_r,
         "roofline": roofline,
     }
+    if not args.no_legs:
+        legs = {}
+        legs["lm_head_sampler"] = leg_lm_head(ev, syn, to_dev, stream, args.steps)
+        print("# lm head leg done", file=sys.stderr, flush=True)
+        legs["moe_layer"] = leg_moe(ev, syn, to_dev, stream, args.steps)
+        print("# moe leg done", file=sys.stderr, flush=True)
+        legs["decoder_4096"] = leg_decoder(ev, syn, 4096)
+        print("# decoder leg (cache 4096) done", file=sys.stderr, flush=True)
+        legs["decoder_32768"] = leg_decoder(ev, syn, 32768)
+        print("# decoder leg (cache 32768) done", file=sys.stderr, flush=True)
+        out["legs"] = legs
+        out["exact_accepted_tok_s"] = legs["decoder_4096"]["accepted_tok_s"]
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(d, R)
     print(json.dumps(out), flush=True)

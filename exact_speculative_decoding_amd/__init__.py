@@ -290,7 +290,8 @@ class ToyDecoder:
     verify_step.  `weights` holds device tensors: embed [V][H] bf16,
     final_norm [H] fp32, lm (PackedW4), and per layer (list `layers` of dicts)
     attn_norm, mlp_norm [H] fp32 and packed qkv, o, gate, up, down.  The caches
-    are [layers][kv_heads][max_ctx][128] fp16 device tensors."""
+    are [layers][kv_heads][max_ctx][128] fp16 device tensors, the value cache
+    in the blocked slot order (v_cache_blocked)."""
 
     def __init__(self, cfg, weights, k_cache, v_cache):
         self.cfg = cfg
@@ -315,6 +316,10 @@ class ToyDecoder:
         self._h = h
         self.ws = torch.empty(int(lib().verify_step_workspace(h)), dtype=torch.uint8,
                               device=k_cache.device)
+
+    def v_cache_standard(self):
+        """The value cache in the plain [layers][kv_heads][C][128] order."""
+        return v_cache_standard(self.v_cache)
 
     def __del__(self):
         h = getattr(self, "_h", None)
@@ -341,6 +346,27 @@ class ToyDecoder:
         return sampled, n_commit
 
 
+# Value-cache slot order inside a block of 32 slots (see verify_step in
+# include/exactverify.h): slot s sits at position VSLOT_POS[s].
+VSLOT_POS = [8 * (s // 4) + s % 4 if s < 16 else 8 * ((s - 16) // 4) + 4 + s % 4 for s in range(32)]
+_VSLOT_AT = [VSLOT_POS.index(k) for k in range(32)]
+
+
+def v_cache_blocked(v):
+    """[layers][kv_heads][C][128] -> the blocked layout [layers][kv_heads][C/32][128][32]
+    (numpy array or torch tensor)."""
+    L, KV, C, D = v.shape
+    x = v.reshape(L, KV, C // 32, 32, D)[:, :, :, _VSLOT_AT, :]
+    return x.swapaxes(-1, -2).reshape(L, KV, C, D)
+
+
+def v_cache_standard(vb):
+    """Inverse of v_cache_blocked."""
+    L, KV, C, D = vb.shape
+    x = vb.reshape(L, KV, C // 32, D, 32).swapaxes(-1, -2)
+    return x[:, :, :, VSLOT_POS, :].reshape(L, KV, C, D)
+
+
 def load_decoder(cfg, w, kc, vc, device="cuda"):
     """Upload a decoder given in standard layouts (numpy: embed [V][H] bf16 bits,
     norms fp32, W4 q/s/b per matrix stacked over layers, caches fp16 bits) and
@@ -361,7 +387,7 @@ def load_decoder(cfg, w, kc, vc, device="cuda"):
                    qkv=pack("qkv", l), o=pack("o", l), gate=pack("gate", l), up=pack("up", l),
                    down=pack("down", l)) for l in range(cfg["layers"])]
     weights = dict(embed=t(w["embed"]), final_norm=t(w["final_norm"]), lm=pack("lm"), layers=layers)
-    return ToyDecoder(cfg, weights, t(kc), t(vc))
+    return ToyDecoder(cfg, weights, t(kc), t(np.ascontiguousarray(v_cache_blocked(vc))))
 
 
 def w4_timing(enable):

@@ -7,11 +7,11 @@
 //   * the W4 linears are the row-exact verify kernel (w4_verify.hip);
 //   * norms, RoPE, cache writes and the residual stream are per row, with
 //     reductions in a fixed tree that does not depend on R;
-//   * attention splits the key slots at absolute boundaries (chunks of
-//     kAttnChunk, sub-blocks of kAttnSub), so row r at position p sees the same
-//     chunks, sub-blocks and online-softmax updates whatever other rows share
-//     the pass; slots past p are skipped, never added as zeros; the chunks are
-//     merged in ascending order;
+//   * attention splits the key slots at absolute boundaries (chunks whose size
+//     follows from the cache size, online-softmax steps of 32 slots), so row r
+//     at position p sees the same chunks, steps and updates whatever other rows
+//     share the pass; a step with no slot <= p leaves the row's state untouched;
+//     the chunks are merged in ascending order;
 //   * row r writes cache slot p and reads slots <= p only, all of which hold the
 //     bytes serial decoding wrote (slot p in this pass, from the same input).
 //
@@ -31,9 +31,9 @@ namespace ev {
 
 constexpr int kHD = 128;          // head dimension
 constexpr int kHalf = kHD / 2;
-constexpr int kAttnChunk = 256;   // key slots per attention partial (absolute boundaries)
-constexpr int kAttnSub = 64;      // key slots per LDS sub-block
-constexpr int kMaxQ = 64;         // queries per attention workgroup: R * heads / kv_heads
+constexpr int kKStep = 32;        // key slots per online-softmax step (absolute boundaries)
+constexpr int kMaxChunks = 128;   // attention partials per (row, head) at most
+constexpr int kMaxQ = 64;         // queries per kv head: R * heads / kv_heads
 constexpr int kPartStride = kHD + 2;  // one attention partial: m, l, acc[128]
 
 struct RopeTab {
@@ -104,6 +104,16 @@ __global__ __launch_bounds__(256) void res_norm_kernel(const float* __restrict__
     }
 }
 
+// Value cache layout: blocks of 32 slots, d-major inside a block
+// ([kv_heads][C/32][128][32]), and within a block slot s at position
+// vslot_pos(s): positions 8j..8j+7 hold slots 4j..4j+3 and 16+4j..16+4j+3.
+// That is the order in which one lane of the PV product's B operand (the
+// probabilities, straight out of the score MFMA's accumulator layout) holds
+// its 8 slots, so the values' A operand is one 16-byte load.
+__host__ __device__ inline int vslot_pos(int s) {
+    return s < 16 ? 8 * (s >> 2) + (s & 3) : 8 * ((s - 16) >> 2) + 4 + (s & 3);
+}
+
 // q|k|v of row r = split sums; rotate q and k by position pos0 + r; q to
 // qout [R][NH][128] fp32, k and v to cache slot pos0 + r in fp16.
 __global__ __launch_bounds__(256) void qkv_rope_kernel(const float* __restrict__ part, int S, int NH, int NKV,
@@ -137,176 +147,228 @@ __global__ __launch_bounds__(256) void qkv_rope_kernel(const float* __restrict__
             k[i + kHalf] = f32_to_f16_bits(b2);
         }
     }
+    const size_t vblk = ((size_t)(P / kKStep)) * kHD * kKStep;
+    const int vpos = vslot_pos((int)(P % kKStep));
     for (int p = tid; p < NKV * kHD; p += 256) {
         const int g = p / kHD, d = p % kHD;
-        vc[((size_t)g * C + P) * kHD + d] = f32_to_f16_bits(colsum((NH + NKV) * kHD + p));
+        vc[(size_t)g * C * kHD + vblk + (size_t)d * kKStep + vpos] = f32_to_f16_bits(colsum((NH + NKV) * kHD + p));
     }
 }
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 struct AttnArgs {
     const float* q;      // [R][NH][128]
     const uint16_t* kc;  // this layer's keys [NKV][C][128] fp16
-    const uint16_t* vc;
+    const uint16_t* vc;  // this layer's values, blocked (vslot_pos)
     float* part;         // [16][NH][nchunk_max][130]
-    int R, NH, NKV, C, nchunk_max;
+    int R, NH, NKV, C, chunk, nchunk_max;
     long long pos0;
     float scale;         // 1/sqrt(128)
 };
 
-// Attention partials of chunk blockIdx.x (slots [256 c, 256 c + 256)) for kv
-// head blockIdx.y and all queries that read it (R rows x heads/kv_heads).  Per
-// query: running max m, sum l and acc[128] over its valid slots, sub-block by
-// sub-block in ascending order.
-__global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
-    __shared__ float Qs[kMaxQ][kHD];
-    __shared__ uint16_t Kt[kHD][kAttnSub + 2];
-    __shared__ __align__(16) uint16_t Vs[kAttnSub][kHD];
-    __shared__ float Ps[kMaxQ][kAttnSub];
-    __shared__ float sm[kMaxQ], sl[kMaxQ], ssc[kMaxQ];
-    __shared__ int snv[kMaxQ];
+__device__ __forceinline__ f16x8 load_f16x8(const uint16_t* p) {
+    return __builtin_bit_cast(f16x8, *reinterpret_cast<const u32x4*>(p));
+}
 
-    const int tid = threadIdx.x;
-    const int chunk = blockIdx.x, g = blockIdx.y;
+// Attention partial of one chunk of slots (blockIdx.x), one kv head
+// (blockIdx.y) and one tile of 16 queries (blockIdx.z; query qi = row qi/gq,
+// head g*gq + qi%gq), one wave:
+//   S^T = K Q^T and O^T += V^T P^T on v_mfma_f32_16x16x32_f16.  Q and P are
+//   split into fp16 hi + lo (products exact, fp32 accumulation), Q after a
+//   per-query power-of-two scale that keeps it inside the fp16 range; K and V
+//   are fp16 already.  The score tile's accumulator layout (slot rows, query
+//   columns) is exactly the B operand of the PV product (with the value
+//   cache's slot order), so no data moves between the two.
+//   Online softmax over steps of 32 slots; lane (grp, ln) keeps the state of
+//   query ln (replicated over grp) and O^T rows d = 16 dt + 4 grp + v.
+__global__ __launch_bounds__(64) void attn_partial_kernel(AttnArgs a) {
+    const int lane = threadIdx.x, ln = lane & 15, grp = lane >> 4;
+    const int chunk = blockIdx.x, g = blockIdx.y, qt = blockIdx.z;
     const int gq = a.NH / a.NKV, nq = a.R * gq;
-    const long long cstart = (long long)chunk * kAttnChunk;
+    const int qi = qt * 16 + ln;
+    const bool qok = qi < nq;
+    const int r = qok ? qi / gq : 0;
+    const int h = g * gq + (qok ? qi % gq : 0);
+    const long long P = a.pos0 + r;
     const long long pmax = a.pos0 + a.R - 1;
+    const long long cstart = (long long)chunk * a.chunk;
+    const long long cend = min(cstart + a.chunk - 1, pmax);
+
+    // Q^T fragments: query ln, d = 32 ds + 8 grp + i
+    float qv[4][8];
+    const float* qp = a.q + ((size_t)r * a.NH + h) * kHD + 8 * grp;
+#pragma unroll
+    for (int ds = 0; ds < 4; ++ds) {
+        f32x4 v0 = {0.f, 0.f, 0.f, 0.f}, v1 = v0;
+        if (qok) {
+            v0 = *reinterpret_cast<const f32x4*>(qp + 32 * ds);
+            v1 = *reinterpret_cast<const f32x4*>(qp + 32 * ds + 4);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            qv[ds][i] = v0[i];
+            qv[ds][4 + i] = v1[i];
+        }
+    }
+    float amax = 0.f;
+#pragma unroll
+    for (int ds = 0; ds < 4; ++ds)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(qv[ds][i]));
+    amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
+    amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+    int ex = 0;
+    frexpf(amax, &ex);  // amax in [2^(ex-1), 2^ex)
+    const int e = amax > 0.f ? max(-100, min(100, 15 - ex)) : 0;
+    const float up = ldexpf(1.0f, e);
+    const float sback = ldexpf(1.0f, -e) * a.scale;  // exact: a power of two times the scale
+    f16x8 qh[4], ql[4];
+#pragma unroll
+    for (int ds = 0; ds < 4; ++ds)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float v = qv[ds][i] * up;
+            const _Float16 hv = (_Float16)v;
+            qh[ds][i] = hv;
+            ql[ds][i] = (_Float16)(v - (float)hv);
+        }
+
+    float m = -INFINITY, l = 0.f;
+    f32x4 acc[8];
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     const uint16_t* kb = a.kc + (size_t)g * a.C * kHD;
     const uint16_t* vb = a.vc + (size_t)g * a.C * kHD;
+    const f16x8 z8 = {};
 
-    for (int e = tid; e < nq * kHD; e += 256) {
-        const int qi = e / kHD, d = e % kHD;
-        const int r = qi / gq, hh = qi % gq;
-        Qs[qi][d] = a.q[((size_t)r * a.NH + g * gq + hh) * kHD + d];
-    }
-    if (tid < kMaxQ) {
-        sm[tid] = -INFINITY;
-        sl[tid] = 0.f;
-    }
-    float acc[kMaxQ / 2];
+    for (long long s0 = cstart; s0 <= cend; s0 += kKStep) {
+        // keys: rows slot = s0 + 16 t + ln, d = 32 ds + 8 grp .. + 7
+        f16x8 kf[2][4];
 #pragma unroll
-    for (int i = 0; i < kMaxQ / 2; ++i) acc[i] = 0.f;
-    __syncthreads();
-
-    for (int sb = 0; sb < kAttnChunk / kAttnSub; ++sb) {
-        const long long base = cstart + (long long)sb * kAttnSub;
-        if (base > pmax) break;  // uniform
-        {   // stage keys (transposed) and values of slots base .. base + 63
-            const int j = tid >> 2, dp = (tid & 3) * 32;
-            const long long slot = base + j;
-            u32x4 kv[4], vv[4];
-            if (slot <= pmax) {
-                const u32x4* ks = reinterpret_cast<const u32x4*>(kb + (size_t)slot * kHD + dp);
-                const u32x4* vs = reinterpret_cast<const u32x4*>(vb + (size_t)slot * kHD + dp);
+        for (int t = 0; t < 2; ++t) {
+            const long long slot = s0 + 16 * t + ln;
+            const uint16_t* kp = kb + (size_t)slot * kHD + 8 * grp;
 #pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    kv[u] = ks[u];
-                    vv[u] = vs[u];
-                }
-            } else {
+            for (int ds = 0; ds < 4; ++ds) kf[t][ds] = slot <= pmax ? load_f16x8(kp + 32 * ds) : z8;
+        }
+        // values: V^T rows d = 16 dt + ln, positions 8 grp .. + 7 of block s0 / 32
+        f16x8 vf[8];
+        const uint16_t* vp = vb + (size_t)(s0 / kKStep) * kHD * kKStep + (size_t)ln * kKStep + 8 * grp;
 #pragma unroll
-                for (int u = 0; u < 4; ++u) kv[u] = vv[u] = u32x4{0u, 0u, 0u, 0u};
-            }
+        for (int dt = 0; dt < 8; ++dt) vf[dt] = load_f16x8(vp + (size_t)16 * dt * kKStep);
+        if (s0 + kKStep - 1 > pmax) {  // zero the slots past the pass (stale or never written)
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                *reinterpret_cast<u32x4*>(&Vs[j][dp + 8 * u]) = vv[u];
+            for (int kk = 0; kk < 8; ++kk) {
+                const long long slot = s0 + (kk < 4 ? 4 * grp + kk : 16 + 4 * grp + kk - 4);
+                if (slot > pmax)
 #pragma unroll
-                for (int w = 0; w < 4; ++w) {
-                    Kt[dp + 8 * u + 2 * w][j] = (uint16_t)(kv[u][w] & 0xffffu);
-                    Kt[dp + 8 * u + 2 * w + 1][j] = (uint16_t)(kv[u][w] >> 16);
-                }
+                    for (int dt = 0; dt < 8; ++dt) vf[dt][kk] = (_Float16)0.f;
             }
         }
-        __syncthreads();
-        {   // scores: lane = slot, wave w = queries w, w + 4, ...
-            const int jj = tid & 63, wq = tid >> 6;
+        // scores S^T: lane holds slots s0 + 16 t + 4 grp + v for query ln
+        f32x4 sc4[2];
 #pragma unroll
-            for (int i = 0; i < kMaxQ / 4; ++i) {
-                const int qi = wq + 4 * i;
-                if (qi < nq) {
-                    float s = 0.f;
-                    for (int d = 0; d < kHD; ++d)
-                        s = fmaf(Qs[qi][d], (float)__builtin_bit_cast(_Float16, Kt[d][jj]), s);
-                    Ps[qi][jj] = s * a.scale;
-                }
-            }
-        }
-        __syncthreads();
-        if (tid < nq) {  // online softmax update of query tid over its valid slots
-            const int qi = tid;
-            const long long P = a.pos0 + qi / gq;
-            long long nvl = P - base + 1;
-            const int nv = nvl < 0 ? 0 : (nvl > kAttnSub ? kAttnSub : (int)nvl);
-            snv[qi] = nv;
-            if (nv > 0) {
-                float mx = Ps[qi][0];
-                for (int j = 1; j < nv; ++j) mx = fmaxf(mx, Ps[qi][j]);
-                const float mold = sm[qi], mnew = fmaxf(mold, mx);
-                const float sc = expf(mold - mnew);
-                float lsum = 0.f;
-                for (int j = 0; j < nv; ++j) {
-                    const float p = expf(Ps[qi][j] - mnew);
-                    Ps[qi][j] = p;
-                    lsum += p;
-                }
-                sl[qi] = sl[qi] * sc + lsum;
-                sm[qi] = mnew;
-                ssc[qi] = sc;
-            }
-        }
-        __syncthreads();
-        {   // acc[q][d] = acc * scale + sum_j p_j v_j[d]; thread = d, queries qh, qh + 2, ...
-            const int d = tid & (kHD - 1), qh = tid >> 7;
+        for (int t = 0; t < 2; ++t) {
+            f32x4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int i = 0; i < kMaxQ / 2; ++i) {
-                const int qi = qh + 2 * i;
-                if (qi < nq) {
-                    const int nv = snv[qi];
-                    if (nv > 0) {
-                        float t = 0.f;
-                        for (int j = 0; j < nv; ++j)
-                            t = fmaf(Ps[qi][j], (float)__builtin_bit_cast(_Float16, Vs[j][d]), t);
-                        acc[i] = fmaf(acc[i], ssc[qi], t);
-                    }
-                }
+            for (int ds = 0; ds < 4; ++ds) {
+                c = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[t][ds], qh[ds], c, 0, 0, 0);
+                c = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[t][ds], ql[ds], c, 0, 0, 0);
             }
+            sc4[t] = c;
         }
-        __syncthreads();
+        const bool live = qok && s0 <= P;  // the query has a slot in this step
+        float sv[8], mx = -INFINITY;
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const long long slot = s0 + 16 * t + 4 * grp + v;
+                const float x = sc4[t][v] * sback;
+                sv[4 * t + v] = slot <= P ? x : -INFINITY;
+                mx = fmaxf(mx, sv[4 * t + v]);
+            }
+        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        const float mnew = live ? fmaxf(m, mx) : m;
+        const float scl = live ? expf(m - mnew) : 1.f;
+        float p[8], ps = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            p[i] = live ? expf(sv[i] - mnew) : 0.f;
+            ps += p[i];
+        }
+        ps += __shfl_xor(ps, 16, 64);  // a butterfly: every lane gets the same sum
+        ps += __shfl_xor(ps, 32, 64);
+        if (live) {
+            l = l * scl + ps;
+            m = mnew;
+        }
+        f16x8 ph, pl;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const _Float16 hv = (_Float16)p[i];
+            ph[i] = hv;
+            pl[i] = (_Float16)(p[i] - (float)hv);
+        }
+        // O^T = O^T * scale + V^T P^T; a query without a slot here keeps its state bit for bit
+        const bool keep_any = __any(qok && !live);
+        f32x4 keep[8];
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+            keep[dt] = acc[dt];
+            acc[dt] *= scl;
+            acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf[dt], ph, acc[dt], 0, 0, 0);
+            acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf[dt], pl, acc[dt], 0, 0, 0);
+        }
+        if (keep_any && !live) {
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt) acc[dt] = keep[dt];
+        }
     }
 
-    const int d = tid & (kHD - 1), qh = tid >> 7;
-#pragma unroll
-    for (int i = 0; i < kMaxQ / 2; ++i) {
-        const int qi = qh + 2 * i;
-        if (qi < nq) {
-            const int r = qi / gq;
-            if (a.pos0 + r >= cstart) {
-                const int h = g * gq + qi % gq;
-                float* o = a.part + (((size_t)r * a.NH + h) * a.nchunk_max + chunk) * kPartStride;
-                o[2 + d] = acc[i];
-                if (d == 0) {
-                    o[0] = sm[qi];
-                    o[1] = sl[qi];
-                }
-            }
+    if (qok && P >= cstart) {
+        float* o = a.part + (((size_t)r * a.NH + h) * a.nchunk_max + chunk) * kPartStride;
+        if (grp == 0) {
+            o[0] = m;
+            o[1] = l;
         }
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) o[2 + 16 * dt + 4 * grp + v] = acc[dt][v];
     }
 }
 
 // o[r][h][d] = bf16(sum_c acc_c[d] e^(m_c - M) / sum_c l_c e^(m_c - M)) over
-// the chunks c = 0 .. (pos0 + r) / 256, ascending.
-__global__ __launch_bounds__(kHD) void attn_merge_kernel(const float* __restrict__ part, int NH, int nchunk_max,
-                                                         long long pos0, uint16_t* __restrict__ o) {
+// the chunks c = 0 .. (pos0 + r) / chunk, ascending; M = max_c m_c.
+__global__ __launch_bounds__(kHD) void attn_merge_kernel(const float* __restrict__ part, int NH, int chunk,
+                                                         int nchunk_max, long long pos0, uint16_t* __restrict__ o) {
+    __shared__ float sm[kMaxChunks], se[kMaxChunks], sl[kMaxChunks];
+    __shared__ float red[2];
     const int r = blockIdx.x, h = blockIdx.y, d = threadIdx.x;
-    const int nch = (int)((pos0 + r) / kAttnChunk) + 1;
+    const int nch = (int)((pos0 + r) / chunk) + 1;
     const float* b = part + ((size_t)r * NH + h) * nchunk_max * kPartStride;
-    float M = -INFINITY;
-    for (int c = 0; c < nch; ++c) M = fmaxf(M, b[(size_t)c * kPartStride]);
+    float mv = -INFINITY;
+    if (d < nch) {
+        mv = b[(size_t)d * kPartStride];
+        sm[d] = mv;
+        sl[d] = b[(size_t)d * kPartStride + 1];
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) mv = fmaxf(mv, __shfl_xor(mv, off, 64));
+    if ((d & 63) == 0) red[d >> 6] = mv;
+    __syncthreads();
+    const float M = fmaxf(red[0], red[1]);
+    if (d < nch) se[d] = expf(sm[d] - M);
+    __syncthreads();
     float L = 0.f, acc = 0.f;
+#pragma unroll 8
     for (int c = 0; c < nch; ++c) {
-        const float* pc = b + (size_t)c * kPartStride;
-        const float e = expf(pc[0] - M);
-        L = fmaf(pc[1], e, L);
-        acc = fmaf(pc[2 + d], e, acc);
+        const float e = se[c];
+        L = fmaf(sl[c], e, L);
+        acc = fmaf(b[(size_t)c * kPartStride + 2 + d], e, acc);
     }
     o[((size_t)r * NH + h) * kHD + d] = f32_to_bf16_rne(acc / L);
 }
@@ -314,7 +376,7 @@ __global__ __launch_bounds__(kHD) void attn_merge_kernel(const float* __restrict
 // Workspace of a verify step, from the configuration and max_ctx only.
 struct StepLayout {
     W4Plan p_qkv, p_o, p_gu, p_down, p_lm;
-    int nchunk_max;
+    int chunk, nchunk_max;
     size_t off_x, off_n, off_o, off_q, off_part, off_pg, off_pu, off_h, off_att, off_logits, off_pos, off_acc,
         off_sws, total;
 };
@@ -345,7 +407,9 @@ static StepLayout step_layout(const ev_decoder_config& c, int NQKV, int DQ, int 
     L.p_gu = plan_w4(I, H, 2);
     L.p_down = plan_w4(H, I, 1);
     L.p_lm = plan_w4(V, H, 1);
-    L.nchunk_max = (C + kAttnChunk - 1) / kAttnChunk;
+    // chunk: a multiple of 64 slots with at most kMaxChunks chunks in the cache
+    L.chunk = 64 * ((C + 64 * kMaxChunks - 1) / (64 * kMaxChunks));
+    L.nchunk_max = (C + L.chunk - 1) / L.chunk;
     size_t part = (size_t)L.p_qkv.S * NQKV;
     part = std::max(part, (size_t)L.p_o.S * H);
     part = std::max(part, (size_t)L.p_down.S * H);
@@ -390,7 +454,8 @@ extern "C" int32_t toy_decoder_create(const ev_decoder_config* cfg, const ev_dec
     if (!(c.rope_base > 0.0) || !(c.rope_base < __builtin_huge_val()) || !(c.rms_eps >= 0.0) ||
         !(c.rms_eps < __builtin_huge_val()))
         return fail(EV_EINVAL, "%s: rope_base must be finite > 0 and rms_eps finite >= 0", who);
-    if (max_ctx < 1 || max_ctx > (1 << 22)) return fail(EV_EINVAL, "%s: max_ctx=%d", who, max_ctx);
+    if (max_ctx < 32 || max_ctx > (1 << 22) || max_ctx % 32 != 0)
+        return fail(EV_EINVAL, "%s: max_ctx=%d (a multiple of 32, at most 2^22)", who, max_ctx);
     const int NQKV = (c.heads + 2 * c.kv_heads) * kHD, DQ = c.heads * kHD;
     int32_t rc;
     if ((rc = check_w4_dims(who, c.hidden, NQKV, c.group)) || (rc = check_w4_dims(who, DQ, c.hidden, c.group)) ||
@@ -484,7 +549,8 @@ extern "C" int32_t verify_step(ev_decoder* m, const int32_t* tokens, int32_t R, 
                        eps, x, n, reinterpret_cast<long long*>(pos), (long long)pos0);
     if ((rc = check_hip(hipGetLastError(), "embed_norm launch"))) return rc;
 
-    const int nchunks = (int)((pos0 + R - 1) / kAttnChunk) + 1;
+    const int nchunks = (int)((pos0 + R - 1) / L.chunk) + 1;
+    const int nqt = (R * (NH / NKV) + 15) / 16;
     for (int l = 0; l < c.layers; ++l) {
         const ev_decoder_layer& y = m->layers[l];
         uint16_t* kcl = m->kc + (size_t)l * NKV * m->C * kHD;
@@ -493,10 +559,11 @@ extern "C" int32_t verify_step(ev_decoder* m, const int32_t* tokens, int32_t R, 
         hipLaunchKernelGGL(qkv_rope_kernel, dim3(R), dim3(256), 0, st, part, L.p_qkv.S, NH, NKV, (long long)pos0,
                            m->rope, q, kcl, vcl, m->C);
         if ((rc = check_hip(hipGetLastError(), "qkv_rope launch"))) return rc;
-        AttnArgs aa{q, kcl, vcl, att, R, NH, NKV, m->C, L.nchunk_max, (long long)pos0, 0.08838834764831845f};
-        hipLaunchKernelGGL(attn_partial_kernel, dim3(nchunks, NKV), dim3(256), 0, st, aa);
+        AttnArgs aa{q, kcl, vcl, att, R, NH, NKV, m->C, L.chunk, L.nchunk_max, (long long)pos0, 0.08838834764831845f};
+        hipLaunchKernelGGL(attn_partial_kernel, dim3(nchunks, NKV, nqt), dim3(64), 0, st, aa);
         if ((rc = check_hip(hipGetLastError(), "attn_partial launch"))) return rc;
-        hipLaunchKernelGGL(attn_merge_kernel, dim3(R, NH), dim3(kHD), 0, st, att, NH, L.nchunk_max, (long long)pos0, o);
+        hipLaunchKernelGGL(attn_merge_kernel, dim3(R, NH), dim3(kHD), 0, st, att, NH, L.chunk, L.nchunk_max,
+                           (long long)pos0, o);
         if ((rc = check_hip(hipGetLastError(), "attn_merge launch"))) return rc;
         if ((rc = linear(y.w_o, o, m->DQ, H, L.p_o))) return rc;
         hipLaunchKernelGGL(res_norm_kernel, dim3(R), dim3(256), 0, st, part, L.p_o.S, H, x, y.mlp_norm, eps, n);

@@ -262,9 +262,13 @@ typedef struct {
 typedef struct ev_decoder ev_decoder;
 
 /* Creates a host-side handle (no device memory) over the caller's weights    */
-/* and K/V caches k_cache, v_cache: (device) [layers][kv_heads][max_ctx][128] */
-/* fp16 each, 16-byte aligned.  The handle keeps non-owning pointers: the     */
-/* weights and caches must outlive it.  Errors: EV_EINVAL, EV_EUNSUPPORTED.   */
+/* and caches, 16-byte aligned, max_ctx a multiple of 32:                     */
+/*   k_cache (device) [layers][kv_heads][max_ctx][128] fp16;                  */
+/*   v_cache (device) [layers][kv_heads][max_ctx/32][128][32] fp16: blocks of */
+/*           32 slots, d-major, slot s of a block at position                 */
+/*           8*floor((s%16)/4) + 4*floor(s/16) + s%4.                         */
+/* The handle keeps non-owning pointers: the weights and caches must outlive  */
+/* it.  Errors: EV_EINVAL, EV_EUNSUPPORTED.                                   */
 int32_t toy_decoder_create(const ev_decoder_config* cfg, const ev_decoder_weights* w,
                            uint16_t* k_cache, uint16_t* v_cache, int32_t max_ctx,
                            ev_decoder** out);

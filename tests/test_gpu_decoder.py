@@ -97,7 +97,7 @@ def test_tiny_rows_bit_identical_to_single_row_steps(tiny):
         lg = torch.empty((R, V), dtype=torch.float32, device="cuda")
         s, _ = m.verify_step(torch.tensor(tokens, dtype=torch.int32, device="cuda"), base, *SAMPLED, logits=lg)
         many_l, many_s = host(lg), host(s)
-        kcR = m.k_cache.clone()
+        kcR, vcR = m.k_cache.clone(), m.v_cache.clone()
         m.k_cache.copy_(kc0)
         m.v_cache.copy_(vc0)
         for r, t in enumerate(tokens):
@@ -106,7 +106,7 @@ def test_tiny_rows_bit_identical_to_single_row_steps(tiny):
                                    logits=l1)
             assert np.array_equal(host(l1)[0].view(np.uint32), many_l[r].view(np.uint32)), (R, r)
             assert int(host(s1)[0]) == int(many_s[r]) and int(host(n1)[0]) == 1
-        assert torch.equal(m.k_cache, kcR)
+        assert torch.equal(m.k_cache, kcR) and torch.equal(m.v_cache, vcR)
 
 
 @pytest.mark.parametrize("sampling", [SAMPLED, GREEDY])
@@ -117,7 +117,7 @@ def test_tiny_drafted_equals_serial_and_matches_oracle(tiny, sampling):
     log = []
     serial, rounds = decode(_gpu_round(m, sampling, log), d["first_token"], pos0, n, 1, lambda p, c: [])
     assert rounds == n
-    kc_s, vc_s = host(m.k_cache), host(m.v_cache)
+    kc_s, vc_s = host(m.k_cache), host(m.v_cache_standard())
     gpu_logits = [x[2][0] for x in log]
     res = _teacher_forced(d, serial, pos0, sampling, set(range(n)), gpu_logits)
     near = _check_stream(res)
@@ -129,7 +129,7 @@ def test_tiny_drafted_equals_serial_and_matches_oracle(tiny, sampling):
         assert got == serial, R
         L = pos0 + n
         assert np.array_equal(host(m2.k_cache)[:, :, :L], kc_s[:, :, :L])
-        assert np.array_equal(host(m2.v_cache)[:, :, :L], vc_s[:, :, :L])
+        assert np.array_equal(host(m2.v_cache_standard())[:, :, :L], vc_s[:, :, :L])
 
 
 def test_tiny_decodes_to_the_last_slot(tiny):
@@ -160,7 +160,7 @@ def test_full_decoder_drafted_equals_serial_and_oracle(C, n, positions):
     m = _fresh(d)
     log = []
     serial, _ = decode(_gpu_round(m, SAMPLED, log), d["first_token"], pos0, n, 1, lambda p, c: [])
-    kc_s, vc_s = m.k_cache.clone(), m.v_cache.clone()
+    kc_s, vc_s = m.k_cache.clone(), m.v_cache_standard()
     del m
     m2 = _fresh(d)
     rounds_log = []
@@ -169,7 +169,8 @@ def test_full_decoder_drafted_equals_serial_and_oracle(C, n, positions):
                          on_round=lambda t, s, c: rounds_log.append(c))
     assert got == serial
     L = pos0 + n
-    assert torch.equal(m2.k_cache[:, :, :L], kc_s[:, :, :L]) and torch.equal(m2.v_cache[:, :, :L], vc_s[:, :, :L])
+    assert torch.equal(m2.k_cache[:, :, :L], kc_s[:, :, :L])
+    assert torch.equal(m2.v_cache_standard()[:, :, :L], vc_s[:, :, :L])
     sha = hashlib.sha256(np.array(serial, np.int32).tobytes()).hexdigest()[:16]
     print(f"C={C}: {n} tokens in {rounds} rounds of 8 rows ({n / rounds:.2f} per round), sha256 {sha}")
     del m2
