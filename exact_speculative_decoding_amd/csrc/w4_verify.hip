@@ -44,6 +44,15 @@ constexpr int kSlab = kSC * kXChunkBytes;  // LDS bytes of one superchunk of act
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
+// A pointer every lane holds the same value of, moved to scalar registers.
+template <class T>
+__device__ __forceinline__ T* uniform_ptr(T* p) {
+    const uint64_t v = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return reinterpret_cast<T*>(((uint64_t)hi << 32) | lo);
+}
+
 __device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
 }
@@ -70,21 +79,21 @@ __device__ __forceinline__ u32x4 decode_nibbles(uint32_t d, uint32_t m, uint32_t
 __device__ __forceinline__ float half_lo(uint32_t w) { return f16_to_f32((uint16_t)(w & 0xffffu)); }
 __device__ __forceinline__ float half_hi(uint32_t w) { return f16_to_f32((uint16_t)(w >> 16)); }
 
+// One workgroup of a W4 pass: workgroup index blk of the launch described by
+// `a` computes its 4 waves' tiles over its K-split and writes them to the
+// split's partial (or output) rows.
 template <int G>
-__global__ __launch_bounds__(kThreads) void w4_verify_kernel(W4Args a) {
+__device__ __forceinline__ void w4_block(const W4Args& a, long blk, uint8_t (*xlds)[kSlab]) {
     constexpr int GPC = kKC / G;                // groups per chunk
     constexpr int SBW = GPC;                    // (scale, bias) dwords per lane per chunk
     constexpr uint32_t CB = 1024 + 64 * GPC;    // packed bytes per tile-chunk
     static_assert(kSC % kPD == 0, "ring depth must divide the superchunk");
-    __shared__ __align__(16) uint8_t xlds[2][kSlab];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    if (a.tstamp && tid == 0) a.tstamp[2 * blockIdx.x] = wall_clock64();
     // wave-uniform indices (readfirstlane keeps them, the matrix and the buffer
     // descriptors in scalar registers)
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const long blk = blockIdx.x;
     const int cgb = (int)(blk % a.ncgb);
     long rest = blk / a.ncgb;
     const int split = (int)(rest % a.S);
@@ -113,8 +122,10 @@ __global__ __launch_bounds__(kThreads) void w4_verify_kernel(W4Args a) {
         xrow[m] = a.grows ? a.grows[16 * grp + r] : (a.gexp ? 16 * grp + r : r);
     }
 
-    const rsrc_t rw = make_rsrc(wmat, a.wbytes);
-    const rsrc_t rx = make_rsrc(a.x, a.xbytes);
+    // the buffer descriptors in scalar registers whatever the compiler proved
+    wmat = uniform_ptr(wmat);
+    const rsrc_t rw = make_rsrc(wmat, __builtin_amdgcn_readfirstlane(a.wbytes));
+    const rsrc_t rx = make_rsrc(uniform_ptr(a.x), __builtin_amdgcn_readfirstlane(a.xbytes));
     uint32_t tbase[kNT];
     bool tok[kNT];
 #pragma unroll
@@ -283,9 +294,16 @@ __global__ __launch_bounds__(kThreads) void w4_verify_kernel(W4Args a) {
             }
         }
     }
-    if (a.tstamp) {  // uniform
+}
+
+template <int G>
+__global__ __launch_bounds__(kThreads) void w4_verify_kernel(W4Args a) {
+    __shared__ __align__(16) uint8_t xlds[2][kSlab];
+    if (a.tstamp && threadIdx.x == 0) a.tstamp[2 * blockIdx.x] = wall_clock64();
+    w4_block<G>(a, blockIdx.x, xlds);
+    if (a.tstamp) {  // uniform; grouped launches (which may return early) are never timed
         __syncthreads();
-        if (tid == 0) a.tstamp[2 * blockIdx.x + 1] = wall_clock64();
+        if (threadIdx.x == 0) a.tstamp[2 * blockIdx.x + 1] = wall_clock64();
     }
 }
 
@@ -400,7 +418,8 @@ static double w4_algo_bytes(int nmat, int R, int K, int N, int G) {
     return nmat * (w + 2.0 * R * K + 4.0 * R * N);
 }
 
-int32_t launch_w4(W4Args args, int nmat, const W4Plan& p, int K, int G, hipStream_t st, int ngroups) {
+// Fills the plan-derived fields of a W4 launch.
+static void prep_w4(W4Args& args, int nmat, const W4Plan& p, int K, int G, int ngroups) {
     args.K = K;
     args.nmat = nmat;
     args.nchunks = p.nchunks;
@@ -414,26 +433,37 @@ int32_t launch_w4(W4Args args, int nmat, const W4Plan& p, int K, int G, hipStrea
     if (!args.gexp) args.xbytes = (uint32_t)((size_t)args.R * K * 2);  // grouped: set by the caller
     args.dmask = 0x00780078u;
     args.doff = 0x41804180u;
-    const unsigned blocks = (unsigned)args.blocks;
-    {
-        std::lock_guard<std::mutex> lk(g_timing.mu);
-        args.tstamp = nullptr;
-        if (g_timing.on && !args.gexp) {  // grouped launches' bytes depend on the routing
-            if (g_timing.used + args.blocks > kTimingSlots)
-                return fail(EV_EINVAL, "w4 timing: more than %ld workgroups recorded without a read", kTimingSlots);
-            args.tstamp = g_timing.slots + 2 * g_timing.used;
-            g_timing.first.push_back(g_timing.used);
-            g_timing.count.push_back(args.blocks);
-            g_timing.used += args.blocks;
-            g_timing.bytes.push_back(w4_algo_bytes(nmat, args.R, K, args.N, G));
-        }
+    args.tstamp = nullptr;
+}
+
+// Timing slots for a launch of `blocks` workgroups moving `bytes` algorithmic
+// bytes, or NULL when the hook is off.
+static int32_t timing_slots(long blocks, double bytes, unsigned long long** out) {
+    std::lock_guard<std::mutex> lk(g_timing.mu);
+    *out = nullptr;
+    if (!g_timing.on) return EV_OK;
+    if (g_timing.used + blocks > kTimingSlots)
+        return fail(EV_EINVAL, "w4 timing: more than %ld workgroups recorded without a read", kTimingSlots);
+    *out = g_timing.slots + 2 * g_timing.used;
+    g_timing.first.push_back(g_timing.used);
+    g_timing.count.push_back(blocks);
+    g_timing.used += blocks;
+    g_timing.bytes.push_back(bytes);
+    return EV_OK;
+}
+
+int32_t launch_w4(W4Args args, int nmat, const W4Plan& p, int K, int G, hipStream_t st, int ngroups) {
+    prep_w4(args, nmat, p, K, G, ngroups);
+    if (!args.gexp) {  // grouped launches' bytes depend on the routing: not timed
+        int32_t rc = timing_slots(args.blocks, w4_algo_bytes(nmat, args.R, K, args.N, G), &args.tstamp);
+        if (rc) return rc;
     }
+    const unsigned blocks = (unsigned)args.blocks;
     if (G == 64)
         hipLaunchKernelGGL(w4_verify_kernel<64>, dim3(blocks), dim3(kThreads), 0, st, args);
     else
         hipLaunchKernelGGL(w4_verify_kernel<32>, dim3(blocks), dim3(kThreads), 0, st, args);
-    int32_t rc = check_hip(hipGetLastError(), "w4_verify_kernel launch");
-    return rc;
+    return check_hip(hipGetLastError(), "w4_verify_kernel launch");
 }
 
 // Workspace of verify_linear_w4: split partials [S][16][N] (none if S == 1).
@@ -591,7 +621,7 @@ extern "C" int32_t verify_mlp_w4(const uint16_t* x, int32_t R, int32_t H, int32_
     float* pu = reinterpret_cast<float*>(wsb + L.off_pu);
     uint16_t* h = reinterpret_cast<uint16_t*>(wsb + L.off_h);
     float* pd = reinterpret_cast<float*>(wsb + L.off_pd);
-    // gate and up: one launch (the item's matrix index picks one), via partials
+    // gate|up, split sum + SiLU * up, down, split sum
     W4Args a{};
     a.w[0] = reinterpret_cast<const uint8_t*>(w_gate);
     a.w[1] = reinterpret_cast<const uint8_t*>(w_up);
@@ -603,7 +633,6 @@ extern "C" int32_t verify_mlp_w4(const uint16_t* x, int32_t R, int32_t H, int32_
     a.split_stride = (long)16 * I;
     if ((rc = launch_w4(a, 2, L.p1, H, G, st))) return rc;
     if ((rc = launch_silu_reduce(pg, pu, L.p1.S, I, R, h, h_out, 1, nullptr, nullptr, 0, 0, st))) return rc;
-    // down, reading the packed h
     W4Args d{};
     d.w[0] = d.w[1] = reinterpret_cast<const uint8_t*>(w_down);
     d.out[0] = d.out[1] = L.p2.S > 1 ? pd : y;
