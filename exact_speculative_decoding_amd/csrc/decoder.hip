@@ -40,14 +40,18 @@ struct RopeTab {
     double invf[kHalf];  // rope_base^(-2i/128), computed once on the host
 };
 
-// Sum of one value per thread over a 256-thread block, in a fixed tree.
-__device__ __forceinline__ float block_sum256(float v, float* red) {
+constexpr int kRowThreads = 512;  // threads per row in the row kernels (4 columns each per pass)
+
+// Sum of one value per thread over a kRowThreads block, in a fixed tree.
+__device__ __forceinline__ float row_sum(float v, float* red) {
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
     const int tid = threadIdx.x;
     if ((tid & 63) == 0) red[tid >> 6] = v;
     __syncthreads();
-    const float t = ((red[0] + red[1]) + red[2]) + red[3];
+    float t = red[0];
+#pragma unroll
+    for (int w = 1; w < kRowThreads / 64; ++w) t += red[w];
     __syncthreads();
     return t;
 }
@@ -56,52 +60,87 @@ __device__ __forceinline__ uint16_t f32_to_f16_bits(float v) {
     return __builtin_bit_cast(uint16_t, (_Float16)v);
 }
 
+// n = bf16(RMSNorm(x) * gain) of one row held as float4s by the block
+// (thread tid owns columns 4 (tid + kRowThreads j)); ss = its sum of squares.
+template <int NV>
+__device__ __forceinline__ void norm_store(const f32x4 (&xv)[NV], float ss, const float* __restrict__ gain,
+                                           float eps, int H, uint16_t* __restrict__ nrow, float* red) {
+    const float rs = 1.0f / sqrtf(row_sum(ss, red) / (float)H + eps);
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+        const int c = 4 * (threadIdx.x + kRowThreads * j);
+        if (c >= H) continue;
+        const f32x4 g = *reinterpret_cast<const f32x4*>(gain + c);
+        uint32_t w0 = (uint32_t)f32_to_bf16_rne(xv[j][0] * rs * g[0]) | ((uint32_t)f32_to_bf16_rne(xv[j][1] * rs * g[1]) << 16);
+        uint32_t w1 = (uint32_t)f32_to_bf16_rne(xv[j][2] * rs * g[2]) | ((uint32_t)f32_to_bf16_rne(xv[j][3] * rs * g[3]) << 16);
+        *reinterpret_cast<uint2*>(nrow + c) = make_uint2(w0, w1);
+    }
+}
+
+constexpr int kMaxRowVec = 4;  // H <= 4 * 4 * kRowThreads = 8192
+
 // x[r] = embedding row of tokens[r] (bf16 -> fp32); n[r] = bf16(RMSNorm(x) *
 // gain); positions[r] = pos0 + 1 + r (the positions the rows sample).
-__global__ __launch_bounds__(256) void embed_norm_kernel(const int* __restrict__ tokens,
-                                                         const uint16_t* __restrict__ embed, int H, int V,
-                                                         const float* __restrict__ gain, float eps,
-                                                         float* __restrict__ x, uint16_t* __restrict__ n,
-                                                         long long* __restrict__ positions, long long pos0) {
-    __shared__ float red[4];
+__global__ __launch_bounds__(kRowThreads) void embed_norm_kernel(const int* __restrict__ tokens,
+                                                                 const uint16_t* __restrict__ embed, int H, int V,
+                                                                 const float* __restrict__ gain, float eps,
+                                                                 float* __restrict__ x, uint16_t* __restrict__ n,
+                                                                 long long* __restrict__ positions, long long pos0) {
+    __shared__ float red[kRowThreads / 64];
     const int r = blockIdx.x, tid = threadIdx.x;
     int tok = tokens[r];
     tok = tok < 0 ? 0 : (tok >= V ? V - 1 : tok);  // keeps the read inside the table
     const uint16_t* e = embed + (size_t)tok * H;
+    f32x4 xv[kMaxRowVec];
     float ss = 0.f;
-    for (int c = tid; c < H; c += 256) {
-        const float v = bf16_to_f32(e[c]);
-        x[(size_t)r * H + c] = v;
-        ss += v * v;
+#pragma unroll
+    for (int j = 0; j < kMaxRowVec; ++j) {
+        const int c = 4 * (tid + kRowThreads * j);
+        xv[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (c >= H) continue;
+        const uint2 b = *reinterpret_cast<const uint2*>(e + c);
+        const f32x4 v = {bf16_to_f32((uint16_t)(b.x & 0xffffu)), bf16_to_f32((uint16_t)(b.x >> 16)),
+                         bf16_to_f32((uint16_t)(b.y & 0xffffu)), bf16_to_f32((uint16_t)(b.y >> 16))};
+        xv[j] = v;
+        *reinterpret_cast<f32x4*>(x + (size_t)r * H + c) = v;
+        ss += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
     }
-    const float rs = 1.0f / sqrtf(block_sum256(ss, red) / (float)H + eps);
-    for (int c = tid; c < H; c += 256)
-        n[(size_t)r * H + c] = f32_to_bf16_rne(bf16_to_f32(e[c]) * rs * gain[c]);
+    norm_store(xv, ss, gain, eps, H, n + (size_t)r * H, red);
     if (tid == 0) positions[r] = pos0 + 1 + r;
 }
 
 // x[r] += sum over s ascending of part[s][r] (a linear's split partials);
 // n[r] = bf16(RMSNorm(x[r]) * gain).
-__global__ __launch_bounds__(256) void res_norm_kernel(const float* __restrict__ part, int S, int H,
-                                                       float* __restrict__ x, const float* __restrict__ gain,
-                                                       float eps, uint16_t* __restrict__ n) {
-    __shared__ float red[4];
+__global__ __launch_bounds__(kRowThreads) void res_norm_kernel(const float* __restrict__ part, int S, int H,
+                                                               float* __restrict__ x, const float* __restrict__ gain,
+                                                               float eps, uint16_t* __restrict__ n) {
+    __shared__ float red[kRowThreads / 64];
     const int r = blockIdx.x, tid = threadIdx.x;
     const size_t stride = (size_t)16 * H;
+    f32x4 xv[kMaxRowVec];
     float ss = 0.f;
-    for (int c = tid; c < H; c += 256) {
+#pragma unroll
+    for (int j = 0; j < kMaxRowVec; ++j) {
+        const int c = 4 * (tid + kRowThreads * j);
+        xv[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (c >= H) continue;
         const size_t o = (size_t)r * H + c;
-        float lin = part[o];
-        for (int s = 1; s < S; ++s) lin += part[s * stride + o];
-        const float v = x[o] + lin;
-        x[o] = v;
-        ss += v * v;
+        f32x4 lin = *reinterpret_cast<const f32x4*>(part + o);
+        for (int s0 = 1; s0 < S; s0 += 8) {  // 8 splits' loads in flight at a time, added in order
+            f32x4 p[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                if (s0 + u < S) p[u] = *reinterpret_cast<const f32x4*>(part + (s0 + u) * stride + o);
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                if (s0 + u < S) lin += p[u];
+        }
+        const f32x4 v = *reinterpret_cast<const f32x4*>(x + o) + lin;
+        *reinterpret_cast<f32x4*>(x + o) = v;
+        xv[j] = v;
+        ss += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
     }
-    const float rs = 1.0f / sqrtf(block_sum256(ss, red) / (float)H + eps);
-    for (int c = tid; c < H; c += 256) {
-        const size_t o = (size_t)r * H + c;
-        n[o] = f32_to_bf16_rne(x[o] * rs * gain[c]);
-    }
+    norm_store(xv, ss, gain, eps, H, n + (size_t)r * H, red);
 }
 
 // Value cache layout: blocks of 32 slots, d-major inside a block
@@ -130,11 +169,17 @@ __global__ __launch_bounds__(256) void qkv_rope_kernel(const float* __restrict__
         for (int s = 1; s < S; ++s) a += row[s * stride + c];
         return a;
     };
+    __shared__ float cs[kHalf], sn[kHalf];
+    if (tid < kHalf) {  // the row's rotation, once per frequency
+        const double ang = (double)P * rt.invf[tid];
+        cs[tid] = (float)cos(ang);
+        sn[tid] = (float)sin(ang);
+    }
+    __syncthreads();
     for (int p = tid; p < (NH + NKV) * kHalf; p += 256) {
         const int hd = p / kHalf, i = p % kHalf;
         const float a = colsum(hd * kHD + i), b = colsum(hd * kHD + i + kHalf);
-        const double ang = (double)P * rt.invf[i];
-        const float c = (float)cos(ang), s = (float)sin(ang);
+        const float c = cs[i], s = sn[i];
         const float a2 = a * c - b * s;
         const float b2 = b * c + a * s;
         if (hd < NH) {
@@ -454,6 +499,8 @@ extern "C" int32_t toy_decoder_create(const ev_decoder_config* cfg, const ev_dec
     if (!(c.rope_base > 0.0) || !(c.rope_base < __builtin_huge_val()) || !(c.rms_eps >= 0.0) ||
         !(c.rms_eps < __builtin_huge_val()))
         return fail(EV_EINVAL, "%s: rope_base must be finite > 0 and rms_eps finite >= 0", who);
+    if (c.hidden > 4 * kMaxRowVec * kRowThreads)
+        return fail(EV_EUNSUPPORTED, "%s: hidden=%d above %d", who, c.hidden, 4 * kMaxRowVec * kRowThreads);
     if (max_ctx < 32 || max_ctx > (1 << 22) || max_ctx % 32 != 0)
         return fail(EV_EINVAL, "%s: max_ctx=%d (a multiple of 32, at most 2^22)", who, max_ctx);
     const int NQKV = (c.heads + 2 * c.kv_heads) * kHD, DQ = c.heads * kHD;
@@ -465,14 +512,14 @@ extern "C" int32_t toy_decoder_create(const ev_decoder_config* cfg, const ev_dec
         return rc;
     if (!w->embed || !w->final_norm || !w->w_lm || !k_cache || !v_cache)
         return fail(EV_EINVAL, "%s: NULL pointer", who);
-    if (!aligned(w->embed, 2) || !aligned(w->final_norm, 4) || !aligned(w->w_lm, 16) || !aligned(k_cache, 16) ||
+    if (!aligned(w->embed, 16) || !aligned(w->final_norm, 16) || !aligned(w->w_lm, 16) || !aligned(k_cache, 16) ||
         !aligned(v_cache, 16))
         return fail(EV_EINVAL, "%s: misaligned pointer", who);
     for (int l = 0; l < c.layers; ++l) {
         const ev_decoder_layer& y = w->layers[l];
         if (!y.attn_norm || !y.w_qkv || !y.w_o || !y.mlp_norm || !y.w_gate || !y.w_up || !y.w_down)
             return fail(EV_EINVAL, "%s: layer %d: NULL pointer", who, l);
-        if (!aligned(y.attn_norm, 4) || !aligned(y.mlp_norm, 4) || !aligned(y.w_qkv, 16) || !aligned(y.w_o, 16) ||
+        if (!aligned(y.attn_norm, 16) || !aligned(y.mlp_norm, 16) || !aligned(y.w_qkv, 16) || !aligned(y.w_o, 16) ||
             !aligned(y.w_gate, 16) || !aligned(y.w_up, 16) || !aligned(y.w_down, 16))
             return fail(EV_EINVAL, "%s: layer %d: misaligned pointer", who, l);
     }
@@ -545,7 +592,7 @@ extern "C" int32_t verify_step(ev_decoder* m, const int32_t* tokens, int32_t R, 
         return launch_w4(a, 1, p, K, G, st);
     };
 
-    hipLaunchKernelGGL(embed_norm_kernel, dim3(R), dim3(256), 0, st, tokens, m->embed, H, V, m->layers[0].attn_norm,
+    hipLaunchKernelGGL(embed_norm_kernel, dim3(R), dim3(kRowThreads), 0, st, tokens, m->embed, H, V, m->layers[0].attn_norm,
                        eps, x, n, reinterpret_cast<long long*>(pos), (long long)pos0);
     if ((rc = check_hip(hipGetLastError(), "embed_norm launch"))) return rc;
 
@@ -566,7 +613,7 @@ extern "C" int32_t verify_step(ev_decoder* m, const int32_t* tokens, int32_t R, 
                            (long long)pos0, o);
         if ((rc = check_hip(hipGetLastError(), "attn_merge launch"))) return rc;
         if ((rc = linear(y.w_o, o, m->DQ, H, L.p_o))) return rc;
-        hipLaunchKernelGGL(res_norm_kernel, dim3(R), dim3(256), 0, st, part, L.p_o.S, H, x, y.mlp_norm, eps, n);
+        hipLaunchKernelGGL(res_norm_kernel, dim3(R), dim3(kRowThreads), 0, st, part, L.p_o.S, H, x, y.mlp_norm, eps, n);
         if ((rc = check_hip(hipGetLastError(), "res_norm launch"))) return rc;
         {
             W4Args a{};
@@ -583,7 +630,7 @@ extern "C" int32_t verify_step(ev_decoder* m, const int32_t* tokens, int32_t R, 
         if ((rc = launch_silu_reduce(pg, pu, L.p_gu.S, I, R, h, nullptr, 1, nullptr, nullptr, 0, 0, st))) return rc;
         if ((rc = linear(y.w_down, h, I, H, L.p_down))) return rc;
         const float* next = l + 1 < c.layers ? m->layers[l + 1].attn_norm : m->final_norm;
-        hipLaunchKernelGGL(res_norm_kernel, dim3(R), dim3(256), 0, st, part, L.p_down.S, H, x, next, eps, n);
+        hipLaunchKernelGGL(res_norm_kernel, dim3(R), dim3(kRowThreads), 0, st, part, L.p_down.S, H, x, next, eps, n);
         if ((rc = check_hip(hipGetLastError(), "res_norm launch"))) return rc;
     }
     if ((rc = linear(m->w_lm, n, H, V, L.p_lm))) return rc;

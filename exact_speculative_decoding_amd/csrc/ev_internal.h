@@ -59,13 +59,37 @@ __device__ __forceinline__ float key_logit(unsigned long long k) {
 }
 __device__ __forceinline__ int key_id(unsigned long long k) { return (int)(~(uint32_t)k); }
 
+// Maximum of v over the 64 lanes of the wave, returned to every lane.  DPP
+// moves (VALU, no LDS round trip): prefix maxima within each row of 16 lanes
+// (row_shr 1, 2, 4, 8), then rows 0..1 and 2..3 via row_bcast15, then all via
+// row_bcast31, so lane 63 holds the maximum; max is exact in any order.
+__device__ __forceinline__ unsigned long long dpp_max_step(unsigned long long v, int ctrl_sel) {
+    const uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+    uint32_t olo, ohi;
+    // lanes without a source keep their own value (bound_ctrl off)
+    switch (ctrl_sel) {
+        case 0: olo = __builtin_amdgcn_update_dpp(lo, lo, 0x111, 0xf, 0xf, false);
+                ohi = __builtin_amdgcn_update_dpp(hi, hi, 0x111, 0xf, 0xf, false); break;  // row_shr:1
+        case 1: olo = __builtin_amdgcn_update_dpp(lo, lo, 0x112, 0xf, 0xf, false);
+                ohi = __builtin_amdgcn_update_dpp(hi, hi, 0x112, 0xf, 0xf, false); break;  // row_shr:2
+        case 2: olo = __builtin_amdgcn_update_dpp(lo, lo, 0x114, 0xf, 0xf, false);
+                ohi = __builtin_amdgcn_update_dpp(hi, hi, 0x114, 0xf, 0xf, false); break;  // row_shr:4
+        case 3: olo = __builtin_amdgcn_update_dpp(lo, lo, 0x118, 0xf, 0xf, false);
+                ohi = __builtin_amdgcn_update_dpp(hi, hi, 0x118, 0xf, 0xf, false); break;  // row_shr:8
+        case 4: olo = __builtin_amdgcn_update_dpp(lo, lo, 0x142, 0xa, 0xf, false);
+                ohi = __builtin_amdgcn_update_dpp(hi, hi, 0x142, 0xa, 0xf, false); break;  // row_bcast:15
+        default: olo = __builtin_amdgcn_update_dpp(lo, lo, 0x143, 0xc, 0xf, false);
+                 ohi = __builtin_amdgcn_update_dpp(hi, hi, 0x143, 0xc, 0xf, false); break;  // row_bcast:31
+    }
+    const unsigned long long o = ((unsigned long long)ohi << 32) | olo;
+    return o > v ? o : v;
+}
 __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        const unsigned long long o = __shfl_xor(v, off, 64);
-        v = o > v ? o : v;
-    }
-    return v;
+    for (int k = 0; k < 6; ++k) v = dpp_max_step(v, k);
+    const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)v, 63);
+    const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(v >> 32), 63);
+    return ((unsigned long long)hi << 32) | lo;
 }
 
 }  // namespace ev

@@ -21,10 +21,10 @@
 
 namespace ev {
 
-constexpr int kChunk = 8192;         // logits per top-k workgroup
+constexpr int kChunk = 4096;         // logits per top-k workgroup
 constexpr int kSThreads = 256;
 constexpr int kPer = kChunk / kSThreads;
-constexpr int kMaxChunks = 32;       // V <= 32 * 8192 = 262144
+constexpr int kMaxChunks = 64;       // V <= 64 * 4096 = 262144 (one merge lane per chunk)
 constexpr unsigned long long kGamma = 0x9E3779B97F4A7C15ull;
 
 // SplitMix64 output function (Steele, Lea & Flood, OOPSLA 2014).
@@ -44,41 +44,62 @@ __device__ __forceinline__ double keyed_gumbel(unsigned long long seed, long lon
     return -log(-log(u));
 }
 
+// Sorts 16 keys descending in registers (a fixed bitonic network).
+__device__ __forceinline__ void sort16_desc(unsigned long long (&k)[kPer]) {
+    static_assert(kPer == 16, "network for 16 keys");
+#pragma unroll
+    for (int size = 2; size <= 16; size <<= 1)
+#pragma unroll
+        for (int stride = size >> 1; stride > 0; stride >>= 1)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int j = i ^ stride;
+                if (j > i) {
+                    const bool desc = (i & size) == 0;  // direction of this bitonic block
+                    const unsigned long long a = k[i], b = k[j];
+                    const bool sw = desc ? (a < b) : (a > b);
+                    k[i] = sw ? b : a;
+                    k[j] = sw ? a : b;
+                }
+            }
+}
+
+// The chunk's top-kk keys in order (kk rounds): every thread sorts its 16
+// keys once; a round takes the block maximum of the threads' heads, and the
+// thread that held it shifts its list (no scan in a round).
 __global__ __launch_bounds__(kSThreads) void topk_chunk_kernel(const float* __restrict__ logits,
                                                                int V, int kk, int nchunk,
                                                                unsigned long long* __restrict__ out) {
     __shared__ unsigned long long wbest[kSThreads / 64];
+    __shared__ unsigned long long sel[EV_MAX_TOPK];  // the chunk's winners, in order
     const int r = blockIdx.y, chunk = blockIdx.x;
     const int base = chunk * kChunk;
     const float* row = logits + (size_t)r * V;
     unsigned long long keys[kPer];
-    unsigned long long best = 0ull;
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
         const int idx = base + i * kSThreads + threadIdx.x;
         keys[i] = idx < V ? order_key(row[idx], idx) : 0ull;
-        best = keys[i] > best ? keys[i] : best;
     }
-    unsigned long long* dst = out + ((size_t)r * nchunk + chunk) * kk;
+    sort16_desc(keys);
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     for (int round = 0; round < kk; ++round) {
-        const unsigned long long w = wave_max_u64(best);
+        const unsigned long long w = wave_max_u64(keys[0]);
         if (lane == 0) wbest[wave] = w;
         __syncthreads();
         unsigned long long win = wbest[0];
 #pragma unroll
         for (int i = 1; i < kSThreads / 64; ++i) win = wbest[i] > win ? wbest[i] : win;
         __syncthreads();
-        if (threadIdx.x == 0) dst[round] = win;
-        if (win != 0ull && best == win) {
-            best = 0ull;
+        if (threadIdx.x == 0) sel[round] = win;
+        const bool pop = win != 0ull && keys[0] == win;  // keys are unique: one thread
 #pragma unroll
-            for (int i = 0; i < kPer; ++i) {
-                if (keys[i] == win) keys[i] = 0ull;
-                best = keys[i] > best ? keys[i] : best;
-            }
-        }
+        for (int i = 0; i < kPer - 1; ++i) keys[i] = pop ? keys[i + 1] : keys[i];
+        keys[kPer - 1] = pop ? 0ull : keys[kPer - 1];
     }
+    __syncthreads();
+    unsigned long long* dst = out + ((size_t)r * nchunk + chunk) * kk;
+    if (threadIdx.x < kk) dst[threadIdx.x] = sel[threadIdx.x];
 }
 
 struct SampleArgs {
@@ -92,29 +113,23 @@ struct SampleArgs {
 };
 
 __global__ __launch_bounds__(64) void merge_sample_kernel(SampleArgs a) {
+    __shared__ unsigned long long lists[kMaxChunks * EV_MAX_TOPK];  // [chunk][kk], each in order
     const int r = blockIdx.x, lane = threadIdx.x;
-    const int n = a.nchunk * a.kk;  // <= 32 * 64
+    const int n = a.nchunk * a.kk;  // <= 64 * 64
     const unsigned long long* src = a.cand + (size_t)r * n;
-    unsigned long long keys[kMaxChunks];
-    unsigned long long best = 0ull;
-#pragma unroll
-    for (int i = 0; i < kMaxChunks; ++i) {
-        const int idx = lane + 64 * i;
-        keys[i] = idx < n ? src[idx] : 0ull;
-        best = keys[i] > best ? keys[i] : best;
-    }
-    // the row's top-kk, candidate j ends up in lane j
-    unsigned long long mine = 0ull;
+    for (int i = lane; i < n; i += 64) lists[i] = src[i];
+    __syncthreads();
+    // k-way merge: lane c follows list c; a round takes the maximum of the
+    // heads, and the lane that held it advances (keys are unique)
+    int at = 0;
+    unsigned long long head = lane < a.nchunk ? lists[lane * a.kk] : 0ull;
+    unsigned long long mine = 0ull;  // candidate j ends up in lane j
     for (int round = 0; round < a.kk; ++round) {
-        const unsigned long long win = wave_max_u64(best);
+        const unsigned long long win = wave_max_u64(head);
         if (lane == round) mine = win;
-        if (win != 0ull && best == win) {
-            best = 0ull;
-#pragma unroll
-            for (int i = 0; i < kMaxChunks; ++i) {
-                if (keys[i] == win) keys[i] = 0ull;
-                best = keys[i] > best ? keys[i] : best;
-            }
+        if (win != 0ull && head == win) {
+            ++at;
+            head = at < a.kk ? lists[lane * a.kk + at] : 0ull;
         }
     }
     const int ncand = a.kk < a.V ? a.kk : a.V;

@@ -229,7 +229,7 @@ int32_t accept_prefix(const int32_t* sampled, int32_t R, const int32_t* draft, i
 /* ------------------------------------------------------------------------- */
 typedef struct {
     int32_t layers;        /* >= 1                                           */
-    int32_t hidden;        /* H                                              */
+    int32_t hidden;        /* H <= 8192                                      */
     int32_t heads;         /* query heads                                    */
     int32_t kv_heads;      /* key/value heads; heads / kv_heads in {1,2,4}   */
     int32_t head_dim;      /* must be 128                                    */
@@ -240,7 +240,8 @@ typedef struct {
     double rms_eps;        /* >= 0                                           */
 } ev_decoder_config;
 
-/* Device pointers of one layer (packed W4 matrices as written by w4_pack).   */
+/* Device pointers of one layer (packed W4 matrices as written by w4_pack),   */
+/* all 16-byte aligned.                                                       */
 typedef struct {
     const float* attn_norm; /* [H] fp32 gains                                */
     const void* w_qkv;      /* [(heads + 2 kv_heads) * 128][H]: q, k, v rows  */
@@ -252,10 +253,10 @@ typedef struct {
 } ev_decoder_layer;
 
 typedef struct {
-    const uint16_t* embed;          /* (device) [V][H] bf16                   */
+    const uint16_t* embed;          /* (device) [V][H] bf16, 16-byte aligned  */
     const ev_decoder_layer* layers; /* (host) array of `layers` entries,      */
                                     /* copied by toy_decoder_create           */
-    const float* final_norm;        /* (device) [H] fp32 gains                */
+    const float* final_norm;        /* (device) [H] fp32 gains, 16-B aligned  */
     const void* w_lm;               /* (device) packed [V][H]                 */
 } ev_decoder_weights;
 

@@ -39,7 +39,7 @@ def test_workspace_sizes_do_not_depend_on_rows():
     # the workspace functions take no R at all; check they are stable and sane
     assert ev.verify_linear_w4_workspace(256, 512, 64) >= 0
     assert ev.verify_linear_w4_workspace(17408, 5120, 64) > 16 * 5120 * 4
-    assert ev.keyed_sample_workspace(151936) == 16 * 19 * 64 * 8
+    assert ev.keyed_sample_workspace(151936) == 16 * 38 * 64 * 8
     assert ev.verify_mlp_w4_workspace(5120, 17408, 64) > 0
 
 
