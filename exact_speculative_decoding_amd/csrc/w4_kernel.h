@@ -16,7 +16,7 @@
 #define EV_W4_TARGET_WAVES 2048
 #endif
 #ifndef EV_W4_MIN_CPS
-#define EV_W4_MIN_CPS 8  // at least this many chunks per K-split when K allows
+#define EV_W4_MIN_CPS 4  // at least this many chunks (one superchunk) per K-split when K allows
 #endif
 
 namespace ev {
