@@ -13,7 +13,7 @@
 #define EV_W4_PD 2  // chunks of loads in flight per wave
 #endif
 #ifndef EV_W4_TARGET_WAVES
-#define EV_W4_TARGET_WAVES 2048
+#define EV_W4_TARGET_WAVES 4096
 #endif
 #ifndef EV_W4_MIN_CPS
 #define EV_W4_MIN_CPS 4  // at least this many chunks (one superchunk) per K-split when K allows
@@ -23,10 +23,17 @@ namespace ev {
 
 int32_t check_w4_dims(const char* who, int K, int N, int G);
 
-constexpr int kThreads = 256;  // 4 independent waves per workgroup
+#ifndef EV_W4_WAVES
+#define EV_W4_WAVES 4
+#endif
+constexpr int kWaves = EV_W4_WAVES;  // waves per workgroup, sharing one activation slab
+constexpr int kThreads = 64 * kWaves;
 constexpr int kNT = EV_W4_NT;
 constexpr int kPD = EV_W4_PD;
-constexpr int kSC = 4;  // chunks per activation superchunk (512 k)
+#ifndef EV_W4_SC
+#define EV_W4_SC 2
+#endif
+constexpr int kSC = EV_W4_SC;  // chunks per activation superchunk (staged in LDS together)
 
 struct W4Plan {
     int S;        // K-splits
@@ -60,7 +67,7 @@ struct W4Args {
     float* out[2];        // split s writes rows at out + s * split_stride
     const uint16_t* x;    // activations [rows][K] bf16
     int R, K, N, nchunks, tiles;
-    int cps, S, ncg, ncgb;  // ncgb: workgroups per (matrix, split)
+    int cps, S, ncg, ncgb;  // ncgb: workgroups per (matrix, split), of kWaves tile groups
     int nmat;               // matrices per group (1 or 2)
     long blocks;
     long split_stride;

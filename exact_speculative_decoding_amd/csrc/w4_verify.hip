@@ -23,8 +23,7 @@
 //     conflict-free ds_read_b128 (one barrier per superchunk);
 //   * nibbles decode exactly into bf16 as 16 + q (0x4180 | q << 3: a shift and
 //     an and-or per pair); one more MFMA against an all-ones B gives the group
-//     sum xs of every row, and the fold is p += s * acc + (b - 16 s) * xs into
-//     a per-chunk partial p that is added to y once per chunk;
+//     sum xs of every row, and the fold is y += s * acc + (b - 16 s) * xs;
 //   * a ring of kPD chunks of loads is kept in flight per wave; loads past the
 //     split's last chunk use an out-of-range per-lane offset, which the buffer
 //     range check turns into zeros without touching memory;
@@ -66,7 +65,13 @@ __device__ __forceinline__ u32x2 bload64(rsrc_t r, uint32_t voff, uint32_t soff)
 }
 
 // Eight nibbles q0..q7 (q_i in bits 4i..4i+3) -> four bf16 pairs holding
-// 16 + q in the order (q0,q4) (q1,q5) (q2,q6) (q3,q7).  Exact.
+// 16 + q in the order (q0,q4) (q1,q5) (q2,q6) (q3,q7): bf16 0x4180 is 16, and
+// q goes to mantissa bits 3..6.  Exact.  The offset 16 (rather than 128 with q
+// in the low mantissa bits, which would save one shift in four) keeps
+// b - 16 s exact in fp32 for every fp16 pair (s, b), so a one-hot row reads
+// back s * q + b with a single rounding.
+constexpr float kDecodeOffset = 16.f;
+constexpr uint32_t kDecodeMask = 0x00780078u, kDecodeOr = 0x41804180u;
 __device__ __forceinline__ u32x4 decode_nibbles(uint32_t d, uint32_t m, uint32_t off) {
     u32x4 r;
     r[0] = ((d << 3) & m) | off;
@@ -100,7 +105,7 @@ __device__ __forceinline__ void w4_block(const W4Args& a, long blk, uint8_t (*xl
     rest /= a.S;
     const int mi = (int)(rest % a.nmat);
     const int grp = (int)(rest / a.nmat);
-    const int cg = cgb * 4 + wave;  // a wave past the last tile group computes zeros
+    const int cg = cgb * kWaves + wave;  // a wave past the last tile group computes zeros
     const int c0 = split * a.cps;   // a multiple of kSC
     const int c1 = min(a.nchunks, c0 + a.cps);
     const int ln = lane & 15, j = lane >> 4;
@@ -115,10 +120,17 @@ __device__ __forceinline__ void w4_block(const W4Args& a, long blk, uint8_t (*xl
         wmat += (size_t)a.gexp[grp] * a.wstride;
         out += (size_t)grp * a.ogstride;
     }
-    int xrow[4];
+    // activation staging: a superchunk is 16 rows of kSC * 128 k; thread tid
+    // loads 16 B (8 k) of row tid / kXL + kXR * m at k = 8 (tid % kXL), m < kXP
+    constexpr int kXL = 16 * kSC;          // lanes per row
+    constexpr int kXR = kThreads / kXL;    // rows per pass of the workgroup
+    constexpr int kXP = 16 / kXR;          // passes
+    static_assert(kXR * kXP == 16, "the workgroup's passes must cover the 16 rows");
+    const int xr0 = tid / kXL, col = tid % kXL;
+    int xrow[kXP];
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-        const int r = wave + 4 * m;
+    for (int m = 0; m < kXP; ++m) {
+        const int r = xr0 + kXR * m;
         xrow[m] = a.grows ? a.grows[16 * grp + r] : (a.gexp ? 16 * grp + r : r);
     }
 
@@ -145,17 +157,15 @@ __device__ __forceinline__ void w4_block(const W4Args& a, long blk, uint8_t (*xl
     uint32_t doff;
     asm volatile("v_mov_b32 %0, %1" : "=v"(doff) : "s"(a.doff));
 
-    // ---- activations: one superchunk = 4 chunks = 512 k of the 16 rows.
-    // Thread tid loads 16 B of row wave + 4 m (m = 0..3) at k = 512 sc + 8 (tid % 64):
-    // one wave load is 1 KB of one row.  Rows >= R and k >= K read zeros.
-    const int col = tid & 63;
+    // ---- activations: one superchunk = kSC chunks of the 16 rows.  Rows >= R
+    // and k >= K read zeros.
     const int xc = col >> 4, xst = (col >> 2) & 3, xj = col & 3;
-    u32x4 xin[4];
+    u32x4 xin[kXP];
     auto xload = [&](int sc) {
         const int k = sc * (kSC * kKC) + 8 * col;
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            const bool ok = wave + 4 * m < rows && k < a.K;
+        for (int m = 0; m < kXP; ++m) {
+            const bool ok = xr0 + kXR * m < rows && k < a.K;
             xin[m] = bload128(rx, ok ? (uint32_t)(xrow[m] * a.K + k) * 2u : kOOB, 0u);
         }
     };
@@ -163,8 +173,8 @@ __device__ __forceinline__ void w4_block(const W4Args& a, long blk, uint8_t (*xl
     // lane r + 16 xj of step xst of chunk xc
     auto xstore = [&](int buf) {
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            const int r = wave + 4 * m;
+        for (int m = 0; m < kXP; ++m) {
+            const int r = xr0 + kXR * m;
             const u32x4 v = xin[m];
             u32x4 o;
             o[0] = __builtin_amdgcn_perm(v[2], v[0], 0x05040100u);
@@ -206,14 +216,11 @@ __device__ __forceinline__ void w4_block(const W4Args& a, long blk, uint8_t (*xl
     for (int t = 0; t < kNT; ++t) y[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     // One chunk: per 32-k step, one MFMA for the group sums of x and one per
-    // tile; per group, p += s * acc + (b - 16 s) * xs into a chunk partial p,
-    // which is added to y once per chunk.  A chunk that was loaded as zeros
-    // (past c1) adds exactly zero.
+    // tile; per group, y += s * acc + (b - 16 s) * xs.  A chunk that was
+    // loaded as zeros (past c1) adds exactly zero.
     auto compute = [&](int slot, const uint8_t* xchunk) {
-        f32x4 acc[kNT], part[kNT], xs = {0.f, 0.f, 0.f, 0.f};
+        f32x4 acc[kNT], xs = {0.f, 0.f, 0.f, 0.f};
         const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int t = 0; t < kNT; ++t) part[t] = zero;
 #pragma unroll
         for (int st = 0; st < 4; ++st) {
             const u32x4 xa = *reinterpret_cast<const u32x4*>(xchunk + (size_t)(st * 64 + lane) * 16);
@@ -233,17 +240,15 @@ __device__ __forceinline__ void w4_block(const W4Args& a, long blk, uint8_t (*xl
                 for (int t = 0; t < kNT; ++t) {
                     const uint32_t sb = sbr[slot][t][gc];
                     const float sv = half_lo(sb), bv = half_hi(sb);
-                    const float bp = fmaf(-16.f, sv, bv);  // removes the decode offset
+                    const float bp = fmaf(-kDecodeOffset, sv, bv);  // removes the decode offset
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        part[t][i] = fmaf(sv, acc[t][i], part[t][i]);
-                        part[t][i] = fmaf(bp, xs[i], part[t][i]);
+                        y[t][i] = fmaf(sv, acc[t][i], y[t][i]);
+                        y[t][i] = fmaf(bp, xs[i], y[t][i]);
                     }
                 }
             }
         }
-#pragma unroll
-        for (int t = 0; t < kNT; ++t) y[t] += part[t];
     };
 
     // Prologue: superchunk 0 of the split into LDS slab 0, the first kPD
@@ -427,12 +432,12 @@ static void prep_w4(W4Args& args, int nmat, const W4Plan& p, int K, int G, int n
     args.cps = p.cps;
     args.S = p.S;
     args.ncg = p.ncg;
-    args.ncgb = (p.ncg + 3) / 4;
+    args.ncgb = (p.ncg + kWaves - 1) / kWaves;
     args.blocks = (long)ngroups * nmat * p.S * args.ncgb;
     args.wbytes = (uint32_t)w4_blob_bytes(args.N, K, G);
     if (!args.gexp) args.xbytes = (uint32_t)((size_t)args.R * K * 2);  // grouped: set by the caller
-    args.dmask = 0x00780078u;
-    args.doff = 0x41804180u;
+    args.dmask = kDecodeMask;
+    args.doff = kDecodeOr;
     args.tstamp = nullptr;
 }
 
