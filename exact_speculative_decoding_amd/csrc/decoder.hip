@@ -422,6 +422,7 @@ __global__ __launch_bounds__(kHD) void attn_merge_kernel(const float* __restrict
 struct StepLayout {
     W4Plan p_qkv, p_o, p_gu, p_down, p_lm;
     int chunk, nchunk_max;
+    bool gu_pair;
     size_t off_x, off_n, off_o, off_q, off_part, off_pg, off_pu, off_h, off_att, off_logits, off_pos, off_acc,
         off_sws, total;
 };
@@ -449,7 +450,8 @@ static StepLayout step_layout(const ev_decoder_config& c, int NQKV, int DQ, int 
     const int H = c.hidden, I = c.intermediate, V = c.vocab;
     L.p_qkv = plan_w4(NQKV, H, 1);
     L.p_o = plan_w4(H, DQ, 1);
-    L.p_gu = plan_w4(I, H, 2);
+    L.gu_pair = use_pair(I);
+    L.p_gu = L.gu_pair ? plan_w4_pair(I, H) : plan_w4(I, H, 2);
     L.p_down = plan_w4(H, I, 1);
     L.p_lm = plan_w4(V, H, 1);
     // chunk: a multiple of 64 slots with at most kMaxChunks chunks in the cache
@@ -470,8 +472,8 @@ static StepLayout step_layout(const ev_decoder_config& c, int NQKV, int DQ, int 
     L.off_o = take(sizeof(uint16_t) * 16 * DQ);
     L.off_q = take(sizeof(float) * 16 * DQ);
     L.off_part = take(sizeof(float) * 16 * part);
-    L.off_pg = take(sizeof(float) * 16 * (size_t)L.p_gu.S * I);
-    L.off_pu = take(sizeof(float) * 16 * (size_t)L.p_gu.S * I);
+    L.off_pg = take(L.gu_pair ? 0 : sizeof(float) * 16 * (size_t)L.p_gu.S * I);
+    L.off_pu = take(L.gu_pair ? 0 : sizeof(float) * 16 * (size_t)L.p_gu.S * I);
     L.off_h = take(sizeof(uint16_t) * 16 * I);
     L.off_att = take(sizeof(float) * 16 * (size_t)c.heads * L.nchunk_max * kPartStride);
     L.off_logits = take(sizeof(float) * 16 * (size_t)V);
@@ -615,19 +617,25 @@ extern "C" int32_t verify_step(ev_decoder* m, const int32_t* tokens, int32_t R, 
         if ((rc = linear(y.w_o, o, m->DQ, H, L.p_o))) return rc;
         hipLaunchKernelGGL(res_norm_kernel, dim3(R), dim3(kRowThreads), 0, st, part, L.p_o.S, H, x, y.mlp_norm, eps, n);
         if ((rc = check_hip(hipGetLastError(), "res_norm launch"))) return rc;
-        {
+        {  // h = SiLU(gate) * up: one paired launch, or gate|up + split sum with SiLU * up
             W4Args a{};
             a.w[0] = reinterpret_cast<const uint8_t*>(y.w_gate);
             a.w[1] = reinterpret_cast<const uint8_t*>(y.w_up);
-            a.out[0] = pg;
-            a.out[1] = pu;
             a.x = n;
             a.R = R;
             a.N = I;
-            a.split_stride = (long)16 * I;
-            if ((rc = launch_w4(a, 2, L.p_gu, H, G, st))) return rc;
+            if (L.gu_pair) {
+                a.h = h;
+                if ((rc = launch_w4_pair(a, L.p_gu, H, G, st))) return rc;
+            } else {
+                a.out[0] = pg;
+                a.out[1] = pu;
+                a.split_stride = (long)16 * I;
+                if ((rc = launch_w4(a, 2, L.p_gu, H, G, st))) return rc;
+                if ((rc = launch_silu_reduce(pg, pu, L.p_gu.S, I, R, h, nullptr, 1, nullptr, nullptr, 0, 0, st)))
+                    return rc;
+            }
         }
-        if ((rc = launch_silu_reduce(pg, pu, L.p_gu.S, I, R, h, nullptr, 1, nullptr, nullptr, 0, 0, st))) return rc;
         if ((rc = linear(y.w_down, h, I, H, L.p_down))) return rc;
         const float* next = l + 1 < c.layers ? m->layers[l + 1].attn_norm : m->final_norm;
         hipLaunchKernelGGL(res_norm_kernel, dim3(R), dim3(kRowThreads), 0, st, part, L.p_down.S, H, x, next, eps, n);

@@ -19,8 +19,8 @@
 //   moe_route_kernel    1 x 256: routing of all lanes, then per expert its
 //                       lanes in ascending order, the list of touched experts
 //                       in ascending id, and each (lane, rank)'s place;
-//   w4_verify_kernel    grouped: gate and up of every touched expert;
-//   silu_reduce_kernel  grouped: h = bf16(silu(gate) * up) per expert row;
+//   w4_pair_kernel      grouped: h = bf16(silu(gate) * up) per expert row, gate
+//                       and up of every touched expert in one paired pass;
 //   w4_verify_kernel    grouped: down of every touched expert;
 //   moe_combine_kernel  per lane: split sums, then the weighted sum in rank order.
 #include "w4_kernel.h"
@@ -151,17 +151,17 @@ __global__ __launch_bounds__(64) void moe_combine_kernel(const float* __restrict
     *reinterpret_cast<f32x4*>(y + (size_t)r * H + n4) = acc;
 }
 
-// Workspace: routing tables, then gate/up partials [gmax][S1][16][I], h
-// [gmax][16][I] bf16 and down partials [gmax][S2][16][H]; gmax = min(E, 16 top)
-// groups at most.  A function of (H, I, E, top) only.
+// Workspace: routing tables, then h [gmax][16][I] bf16 and down partials
+// [gmax][S2][16][H]; gmax = min(E, 16 top) groups at most.  A function of
+// (H, I, E, top) only.
 struct MoeLayout {
     W4Plan p1, p2;
     int gmax;
-    size_t off_w, off_pos, off_gcount, off_gexp, off_gcnt, off_grows, off_pg, off_pu, off_h, off_pd, total;
+    size_t off_w, off_pos, off_gcount, off_gexp, off_gcnt, off_grows, off_h, off_pd, total;
 };
 static MoeLayout moe_layout(int H, int I, int E, int top) {
     MoeLayout L;
-    L.p1 = plan_w4(I, H, 2);
+    L.p1 = plan_w4_pair(I, H);
     L.p2 = plan_w4(H, I, 1);
     L.gmax = E < 16 * top ? E : 16 * top;
     const size_t tab = align256(sizeof(int) * 16 * kMoeMaxTop);
@@ -171,10 +171,7 @@ static MoeLayout moe_layout(int H, int I, int E, int top) {
     L.off_gexp = L.off_gcount + 256;
     L.off_gcnt = L.off_gexp + align256(sizeof(int) * L.gmax);
     L.off_grows = L.off_gcnt + align256(sizeof(int) * L.gmax);
-    L.off_pg = L.off_grows + align256(sizeof(int) * 16 * L.gmax);
-    const size_t part1 = align256((size_t)L.gmax * L.p1.S * 16 * I * sizeof(float));
-    L.off_pu = L.off_pg + part1;
-    L.off_h = L.off_pu + part1;
+    L.off_h = L.off_grows + align256(sizeof(int) * 16 * L.gmax);
     L.off_pd = L.off_h + align256((size_t)L.gmax * 16 * I * sizeof(uint16_t));
     L.total = L.off_pd + align256((size_t)L.gmax * L.p2.S * 16 * H * sizeof(float));
     return L;
@@ -229,8 +226,6 @@ extern "C" int32_t verify_moe_w4(const uint16_t* x, const float* router, int32_t
     t.grows = reinterpret_cast<int*>(b + L.off_grows);
     t.ids_out = expert_ids;
     t.w_out = expert_w;
-    float* pg = reinterpret_cast<float*>(b + L.off_pg);
-    float* pu = reinterpret_cast<float*>(b + L.off_pu);
     uint16_t* h = reinterpret_cast<uint16_t*>(b + L.off_h);
     float* pd = reinterpret_cast<float*>(b + L.off_pd);
     // groups launched: at most the distinct experts R lanes can touch
@@ -242,24 +237,18 @@ extern "C" int32_t verify_moe_w4(const uint16_t* x, const float* router, int32_t
     W4Args a{};
     a.w[0] = reinterpret_cast<const uint8_t*>(w_gate);
     a.w[1] = reinterpret_cast<const uint8_t*>(w_up);
-    a.out[0] = pg;
-    a.out[1] = pu;
     a.x = x;
     a.R = R;
     a.N = I;
-    a.split_stride = (long)16 * I;
+    a.h = h;
+    a.hgstride = (long)16 * I;
     a.gcount = t.gcount;
     a.gexp = t.gexp;
     a.gcnt = t.gcnt;
     a.grows = t.grows;
     a.wstride = (long)w4_blob_bytes(I, H, G);
-    a.ogstride = (long)L.p1.S * 16 * I;
     a.xbytes = (uint32_t)((size_t)R * H * sizeof(uint16_t));
-    if ((rc = launch_w4(a, 2, L.p1, H, G, st, ng))) return rc;
-
-    if ((rc = launch_silu_reduce(pg, pu, L.p1.S, I, 16, h, nullptr, ng, t.gcount, t.gcnt, (long)L.p1.S * 16 * I,
-                                 (long)16 * I, st)))
-        return rc;
+    if ((rc = launch_w4_pair(a, L.p1, H, G, st, ng))) return rc;
 
     W4Args d{};
     d.w[0] = d.w[1] = reinterpret_cast<const uint8_t*>(w_down);

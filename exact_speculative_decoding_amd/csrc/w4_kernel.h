@@ -88,12 +88,39 @@ struct W4Args {
     const int* gcnt;
     const int* grows;
     long wstride, ogstride;
+    // Paired gate/up launch only: h = bf16(silu(gate) * up) rows [R][N] (group
+    // g at h + g * hgstride), and a second copy at h_copy when non-NULL.
+    uint16_t* h;
+    uint16_t* h_copy;
+    long hgstride;
 };
 
 // Launch the W4 kernel over `ngroups` groups (1 for a plain launch) of
 // `nmat` matrices each.  Fills the plan-derived fields of `args`.
 int32_t launch_w4(W4Args args, int nmat, const W4Plan& p, int K, int G, hipStream_t st,
                   int ngroups = 1);
+
+// Plan of the paired gate/up launch: K in two halves of cps chunks (a
+// multiple of kSC), one workgroup of 2 kWaves waves per kWaves tiles.
+inline W4Plan plan_w4_pair(int N, int K) {
+    W4Plan p;
+    p.nchunks = w4_chunks(K);
+    p.ncg = w4_tiles(N);
+    const int half = (p.nchunks + 1) / 2;
+    p.cps = (half + kSC - 1) / kSC * kSC;
+    p.S = 2;
+    p.items = 2l * p.ncg;
+    return p;
+}
+
+// Paired gate/up launch (args.w = {gate, up}, args.h / h_copy / hgstride set):
+// h = bf16(silu(x W_gate^T) * (x W_up^T)) for the launch's rows, per group.
+int32_t launch_w4_pair(W4Args args, const W4Plan& p, int K, int G, hipStream_t st, int ngroups = 1);
+
+// A dense gate/up pair (I x H each) runs paired when its tiles alone give the
+// target wave count; otherwise as a split launch of both matrices followed by
+// silu_reduce, whose extra split waves outweigh the partial rows.
+inline bool use_pair(int I) { return 2l * w4_tiles(I) >= EV_W4_TARGET_WAVES; }
 
 // y[r][n] = sum over s ascending of part[s][r][n] (split stride 16 * N), r < R.
 int32_t launch_splitk_reduce(const float* part, int S, int N, int R, float* y, hipStream_t st);

@@ -29,7 +29,10 @@
 //     range check turns into zeros without touching memory;
 //   * K-split partial sums go to a workspace [S][16][N] and are added in
 //     ascending split order by a second kernel (fused with SiLU * up for the
-//     MLP gate/up pair).
+//     MLP gate/up pair); a gate/up pair with enough tiles to fill the chip on
+//     its own, and every grouped MoE pass, runs instead as one paired launch
+//     that splits K in two halves inside the workgroup and writes
+//     h = bf16(silu(g) * u) itself, with no partial rows.
 #include <algorithm>
 #include <mutex>
 #include <vector>
@@ -84,41 +87,72 @@ __device__ __forceinline__ u32x4 decode_nibbles(uint32_t d, uint32_t m, uint32_t
 __device__ __forceinline__ float half_lo(uint32_t w) { return f16_to_f32((uint16_t)(w & 0xffffu)); }
 __device__ __forceinline__ float half_hi(uint32_t w) { return f16_to_f32((uint16_t)(w >> 16)); }
 
-// One workgroup of a W4 pass: workgroup index blk of the launch described by
-// `a` computes its 4 waves' tiles over its K-split and writes them to the
-// split's partial (or output) rows.
-template <int G>
+// bf16_rne(silu(g) * u), silu(g) = g / (1 + e^-g): the one formula of the
+// MLP glue, shared by the paired gate/up epilogue and silu_reduce_kernel.
+__device__ __forceinline__ uint16_t silu_mul_bf16(float g, float u) {
+    const float sg = g / (1.0f + expf(-g));
+    return f32_to_bf16_rne(sg * u);
+}
+
+// One workgroup of a W4 pass.
+//  * Plain (PAIR false, kWaves waves): workgroup blk computes its waves' kNT
+//    tiles of one matrix over one K-split and writes them to the split's
+//    partial (or output) rows.
+//  * Paired gate/up (PAIR true, 2 kWaves waves): wave w's two tiles are the
+//    gate and the up tile of the same 16 columns; the first kWaves waves take
+//    the first half of K (a.cps chunks), the others the rest, each half with
+//    its own activation slabs.  The halves meet in LDS, g = first + second
+//    half (that order), likewise u, and the workgroup writes
+//    h = bf16(silu(g) * u): no partial rows and no second kernel.
+template <int G, bool PAIR>
 __device__ __forceinline__ void w4_block(const W4Args& a, long blk, uint8_t (*xlds)[kSlab]) {
     constexpr int GPC = kKC / G;                // groups per chunk
     constexpr int SBW = GPC;                    // (scale, bias) dwords per lane per chunk
     constexpr uint32_t CB = 1024 + 64 * GPC;    // packed bytes per tile-chunk
     static_assert(kSC % kPD == 0, "ring depth must divide the superchunk");
+    static_assert(!PAIR || kNT == 2, "a paired wave holds one gate and one up tile");
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     // wave-uniform indices (readfirstlane keeps them, the matrix and the buffer
     // descriptors in scalar registers)
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int cgb = (int)(blk % a.ncgb);
-    long rest = blk / a.ncgb;
-    const int split = (int)(rest % a.S);
-    rest /= a.S;
-    const int mi = (int)(rest % a.nmat);
-    const int grp = (int)(rest / a.nmat);
-    const int cg = cgb * kWaves + wave;  // a wave past the last tile group computes zeros
-    const int c0 = split * a.cps;   // a multiple of kSC
+    const int half = PAIR ? wave / kWaves : 0;
+    const int wv = wave - half * kWaves;    // wave within its half
+    const int xt = tid - half * kThreads;   // thread within its half (activation staging)
+    int cgb, split, mi, grp;
+    if (PAIR) {
+        cgb = (int)(blk % a.ncgb);
+        grp = (int)(blk / a.ncgb);
+        split = half;
+        mi = 0;
+    } else {
+        cgb = (int)(blk % a.ncgb);
+        long rest = blk / a.ncgb;
+        split = (int)(rest % a.S);
+        rest /= a.S;
+        mi = (int)(rest % a.nmat);
+        grp = (int)(rest / a.nmat);
+    }
+    const int cg = cgb * kWaves + wv;  // a wave past the last tile group computes zeros
+    const int c0 = split * a.cps;      // a multiple of kSC
     const int c1 = min(a.nchunks, c0 + a.cps);
     const int ln = lane & 15, j = lane >> 4;
 
     // rows of this workgroup's pass, their activation rows, weights and outputs
     int rows = a.R;
     const uint8_t* wmat = a.w[mi];
+    const uint8_t* wmat1 = a.w[1];  // the up matrix of a paired launch
     float* out = a.out[mi] + (size_t)split * a.split_stride;
+    uint16_t* hout = a.h;
+    uint16_t* hcopy = a.h_copy;
     if (a.gexp) {
         if (grp >= a.gcount[0]) return;  // whole workgroup: no barrier reached
         rows = a.gcnt[grp];
         wmat += (size_t)a.gexp[grp] * a.wstride;
+        wmat1 += (size_t)a.gexp[grp] * a.wstride;
         out += (size_t)grp * a.ogstride;
+        hout += (size_t)grp * a.hgstride;
     }
     // activation staging: a superchunk is 16 rows of kSC * 128 k; thread tid
     // loads 16 B (8 k) of row tid / kXL + kXR * m at k = 8 (tid % kXL), m < kXP
@@ -126,7 +160,7 @@ __device__ __forceinline__ void w4_block(const W4Args& a, long blk, uint8_t (*xl
     constexpr int kXR = kThreads / kXL;    // rows per pass of the workgroup
     constexpr int kXP = 16 / kXR;          // passes
     static_assert(kXR * kXP == 16, "the workgroup's passes must cover the 16 rows");
-    const int xr0 = tid / kXL, col = tid % kXL;
+    const int xr0 = xt / kXL, col = xt % kXL;
     int xrow[kXP];
 #pragma unroll
     for (int m = 0; m < kXP; ++m) {
@@ -135,14 +169,15 @@ __device__ __forceinline__ void w4_block(const W4Args& a, long blk, uint8_t (*xl
     }
 
     // the buffer descriptors in scalar registers whatever the compiler proved
-    wmat = uniform_ptr(wmat);
-    const rsrc_t rw = make_rsrc(wmat, __builtin_amdgcn_readfirstlane(a.wbytes));
+    const uint32_t wbytes = __builtin_amdgcn_readfirstlane(a.wbytes);
+    const rsrc_t rw = make_rsrc(uniform_ptr(wmat), wbytes);
+    const rsrc_t rw1 = PAIR ? make_rsrc(uniform_ptr(wmat1), wbytes) : rw;
     const rsrc_t rx = make_rsrc(uniform_ptr(a.x), __builtin_amdgcn_readfirstlane(a.xbytes));
     uint32_t tbase[kNT];
     bool tok[kNT];
 #pragma unroll
     for (int t = 0; t < kNT; ++t) {
-        const int tile = cg * kNT + t;
+        const int tile = PAIR ? cg : cg * kNT + t;
         tok[t] = tile < a.tiles;
         tbase[t] = tok[t] ? (EV_W4_CHUNK_MAJOR ? (uint32_t)tile * CB : (uint32_t)tile * (uint32_t)a.nchunks * CB)
                           : 0u;
@@ -181,7 +216,7 @@ __device__ __forceinline__ void w4_block(const W4Args& a, long blk, uint8_t (*xl
             o[1] = __builtin_amdgcn_perm(v[2], v[0], 0x07060302u);
             o[2] = __builtin_amdgcn_perm(v[3], v[1], 0x05040100u);
             o[3] = __builtin_amdgcn_perm(v[3], v[1], 0x07060302u);
-            *reinterpret_cast<u32x4*>(&xlds[buf][(size_t)((xc * 4 + xst) * 64 + r + 16 * xj) * 16]) = o;
+            *reinterpret_cast<u32x4*>(&xlds[2 * half + buf][(size_t)((xc * 4 + xst) * 64 + r + 16 * xj) * 16]) = o;
         }
     };
 
@@ -197,13 +232,14 @@ __device__ __forceinline__ void w4_block(const W4Args& a, long blk, uint8_t (*xl
         for (int t = 0; t < kNT; ++t) {
             const bool ok = live && tok[t];
             const uint32_t so = tbase[t] + (uint32_t)c * cstride;
-            qr[slot][t] = bload128(rw, ok ? vq : kOOB, so);
+            const rsrc_t r = (PAIR && t == 1) ? rw1 : rw;
+            qr[slot][t] = bload128(r, ok ? vq : kOOB, so);
             if (GPC == 2) {
-                const u32x2 v = bload64(rw, ok ? vsb : kOOB, so);
+                const u32x2 v = bload64(r, ok ? vsb : kOOB, so);
                 sbr[slot][t][0] = v[0];
                 sbr[slot][t][GPC - 1] = v[1];
             } else {
-                const u32x4 v = bload128(rw, ok ? vsb : kOOB, so);
+                const u32x4 v = bload128(r, ok ? vsb : kOOB, so);
 #pragma unroll
                 for (int g = 0; g < SBW; ++g) sbr[slot][t][g] = v[g & 3];
             }
@@ -265,17 +301,20 @@ __device__ __forceinline__ void w4_block(const W4Args& a, long blk, uint8_t (*xl
     xload(sc0 + 1);
     __syncthreads();
 
-    // Main loop over superchunks: 4 chunks of compute on slab `buf`, each
+    // Main loop over superchunks: kSC chunks of compute on slab `buf`, each
     // refilling its ring slot; then the next superchunk's activations go to
     // the other slab, the one after is loaded, and the workgroup syncs.
     // sched_barrier keeps each refill where it is written, so the loads of the
-    // other ring slots stay in flight across the compute of this one.
+    // other ring slots stay in flight across the compute of this one.  Both
+    // halves of a paired workgroup run a.cps / kSC superchunks (chunks past
+    // the end of K read zeros), so every wave reaches the same barriers.
+    const int ntrip = PAIR ? a.cps / kSC : (c1 - c0 + kSC - 1) / kSC;
     int buf = 0;
-    for (int cb = c0; cb < c1; cb += kSC) {
+    for (int it = 0, cb = c0; it < ntrip; ++it, cb += kSC) {
 #pragma unroll
         for (int p = 0; p < kSC; ++p) {
             __builtin_amdgcn_sched_barrier(0);
-            compute(p % kPD, &xlds[buf][(size_t)p * kXChunkBytes]);
+            compute(p % kPD, &xlds[2 * half + buf][(size_t)p * kXChunkBytes]);
             __builtin_amdgcn_sched_barrier(0);
             fetch(cb + p + kPD, p % kPD);
         }
@@ -286,6 +325,35 @@ __device__ __forceinline__ void w4_block(const W4Args& a, long blk, uint8_t (*xl
         buf ^= 1;
     }
     __builtin_amdgcn_sched_barrier(0);
+
+    if (PAIR) {
+        // the second half's accumulators through LDS (the slabs are no longer
+        // read), then h for rows r = 4j + i of columns 16 cg + ln
+        f32x4* ex = reinterpret_cast<f32x4*>(&xlds[0][0]);
+        static_assert(kWaves * kNT * 64 * 16 <= 2 * kSlab, "exchange fits the first half's slabs");
+        if (half == 1) {
+#pragma unroll
+            for (int t = 0; t < kNT; ++t) ex[(wv * kNT + t) * 64 + lane] = y[t];
+        }
+        __syncthreads();
+        if (half == 0) {
+#pragma unroll
+            for (int t = 0; t < kNT; ++t) y[t] += ex[(wv * kNT + t) * 64 + lane];
+            const int n = cg * 16 + ln;
+            if (tok[0] && n < a.N) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int r = 4 * j + i;
+                    if (r < rows) {
+                        const uint16_t hv = silu_mul_bf16(y[0][i], y[1][i]);
+                        hout[(size_t)r * a.N + n] = hv;
+                        if (hcopy) hcopy[(size_t)r * a.N + n] = hv;
+                    }
+                }
+            }
+        }
+        return;
+    }
 
     // rows r = 4j + i of columns 16 * tile + ln
 #pragma unroll
@@ -305,8 +373,20 @@ template <int G>
 __global__ __launch_bounds__(kThreads) void w4_verify_kernel(W4Args a) {
     __shared__ __align__(16) uint8_t xlds[2][kSlab];
     if (a.tstamp && threadIdx.x == 0) a.tstamp[2 * blockIdx.x] = wall_clock64();
-    w4_block<G>(a, blockIdx.x, xlds);
+    w4_block<G, false>(a, blockIdx.x, xlds);
     if (a.tstamp) {  // uniform; grouped launches (which may return early) are never timed
+        __syncthreads();
+        if (threadIdx.x == 0) a.tstamp[2 * blockIdx.x + 1] = wall_clock64();
+    }
+}
+
+// Paired gate/up launch: workgroups of two halves (see w4_block).
+template <int G>
+__global__ __launch_bounds__(2 * kThreads) void w4_pair_kernel(W4Args a) {
+    __shared__ __align__(16) uint8_t xlds[4][kSlab];
+    if (a.tstamp && threadIdx.x == 0) a.tstamp[2 * blockIdx.x] = wall_clock64();
+    w4_block<G, true>(a, blockIdx.x, xlds);
+    if (a.tstamp) {
         __syncthreads();
         if (threadIdx.x == 0) a.tstamp[2 * blockIdx.x + 1] = wall_clock64();
     }
@@ -376,8 +456,7 @@ __global__ __launch_bounds__(64) void silu_reduce_kernel(const float* __restrict
     for (int i = 0; i < 8; ++i) {
         const float g = i < 4 ? g0[i] : g1[i - 4];
         const float u = i < 4 ? u0[i] : u1[i - 4];
-        const float sg = g / (1.0f + expf(-g));
-        hv[i] = f32_to_bf16_rne(sg * u);
+        hv[i] = silu_mul_bf16(g, u);
     }
     u32x4 w;
 #pragma unroll
@@ -471,6 +550,33 @@ int32_t launch_w4(W4Args args, int nmat, const W4Plan& p, int K, int G, hipStrea
     return check_hip(hipGetLastError(), "w4_verify_kernel launch");
 }
 
+int32_t launch_w4_pair(W4Args args, const W4Plan& p, int K, int G, hipStream_t st, int ngroups) {
+    args.K = K;
+    args.nmat = 2;
+    args.nchunks = p.nchunks;
+    args.tiles = w4_tiles(args.N);
+    args.cps = p.cps;
+    args.S = 2;
+    args.ncg = p.ncg;
+    args.ncgb = (p.ncg + kWaves - 1) / kWaves;
+    args.blocks = (long)ngroups * args.ncgb;
+    args.wbytes = (uint32_t)w4_blob_bytes(args.N, K, G);
+    if (!args.gexp) args.xbytes = (uint32_t)((size_t)args.R * K * 2);  // grouped: set by the caller
+    args.dmask = kDecodeMask;
+    args.doff = kDecodeOr;
+    args.tstamp = nullptr;
+    if (!args.gexp) {
+        int32_t rc = timing_slots(args.blocks, w4_algo_bytes(2, args.R, K, args.N, G), &args.tstamp);
+        if (rc) return rc;
+    }
+    const unsigned blocks = (unsigned)args.blocks;
+    if (G == 64)
+        hipLaunchKernelGGL(w4_pair_kernel<64>, dim3(blocks), dim3(2 * kThreads), 0, st, args);
+    else
+        hipLaunchKernelGGL(w4_pair_kernel<32>, dim3(blocks), dim3(2 * kThreads), 0, st, args);
+    return check_hip(hipGetLastError(), "w4_pair_kernel launch");
+}
+
 // Workspace of verify_linear_w4: split partials [S][16][N] (none if S == 1).
 struct LinLayout {
     W4Plan p;
@@ -483,20 +589,22 @@ static LinLayout lin_layout(int K, int N) {
     return L;
 }
 
-// Workspace of the MLP slice: gate and up partials [S1][16][I], h [16][I]
-// bf16, down partials [S2][16][H] (if S2 > 1).
+// Workspace of the MLP slice: h [16][I] bf16, gate and up partials
+// [S1][16][I] (split launch only), down partials [S2][16][H] (if S2 > 1).
 struct MlpLayout {
+    bool pair;
     W4Plan p1, p2;
-    size_t off_pu, off_h, off_pd, total;
+    size_t off_pg, off_pu, off_pd, total;
 };
 static MlpLayout mlp_layout(int H, int I) {
     MlpLayout L;
-    L.p1 = plan_w4(I, H, 2);
+    L.pair = use_pair(I);
+    L.p1 = L.pair ? plan_w4_pair(I, H) : plan_w4(I, H, 2);
     L.p2 = plan_w4(H, I, 1);
-    const size_t part1 = align256((size_t)L.p1.S * 16 * I * sizeof(float));
-    L.off_pu = part1;
-    L.off_h = 2 * part1;
-    L.off_pd = L.off_h + align256((size_t)16 * I * sizeof(uint16_t));
+    const size_t part1 = L.pair ? 0 : align256((size_t)L.p1.S * 16 * I * sizeof(float));
+    L.off_pg = align256((size_t)16 * I * sizeof(uint16_t));
+    L.off_pu = L.off_pg + part1;
+    L.off_pd = L.off_pu + part1;
     L.total = L.off_pd + (L.p2.S > 1 ? (size_t)L.p2.S * 16 * H * sizeof(float) : 0);
     return L;
 }
@@ -622,22 +730,29 @@ extern "C" int32_t verify_mlp_w4(const uint16_t* x, int32_t R, int32_t H, int32_
     if ((rc = check_ws(who, ws, ws_bytes, L.total))) return rc;
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     unsigned char* wsb = reinterpret_cast<unsigned char*>(ws);
-    float* pg = reinterpret_cast<float*>(wsb);
+    uint16_t* h = reinterpret_cast<uint16_t*>(wsb);
+    float* pg = reinterpret_cast<float*>(wsb + L.off_pg);
     float* pu = reinterpret_cast<float*>(wsb + L.off_pu);
-    uint16_t* h = reinterpret_cast<uint16_t*>(wsb + L.off_h);
     float* pd = reinterpret_cast<float*>(wsb + L.off_pd);
-    // gate|up, split sum + SiLU * up, down, split sum
+    // h = SiLU(gate) * up (one paired launch, or gate|up + split sum with
+    // SiLU * up), then down and its split sum
     W4Args a{};
     a.w[0] = reinterpret_cast<const uint8_t*>(w_gate);
     a.w[1] = reinterpret_cast<const uint8_t*>(w_up);
-    a.out[0] = pg;
-    a.out[1] = pu;
     a.x = x;
     a.R = R;
     a.N = I;
-    a.split_stride = (long)16 * I;
-    if ((rc = launch_w4(a, 2, L.p1, H, G, st))) return rc;
-    if ((rc = launch_silu_reduce(pg, pu, L.p1.S, I, R, h, h_out, 1, nullptr, nullptr, 0, 0, st))) return rc;
+    if (L.pair) {
+        a.h = h;
+        a.h_copy = h_out;
+        if ((rc = launch_w4_pair(a, L.p1, H, G, st))) return rc;
+    } else {
+        a.out[0] = pg;
+        a.out[1] = pu;
+        a.split_stride = (long)16 * I;
+        if ((rc = launch_w4(a, 2, L.p1, H, G, st))) return rc;
+        if ((rc = launch_silu_reduce(pg, pu, L.p1.S, I, R, h, h_out, 1, nullptr, nullptr, 0, 0, st))) return rc;
+    }
     W4Args d{};
     d.w[0] = d.w[1] = reinterpret_cast<const uint8_t*>(w_down);
     d.out[0] = d.out[1] = L.p2.S > 1 ? pd : y;

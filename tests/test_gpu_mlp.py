@@ -1,6 +1,7 @@
 """GPU parity of the dense SiLU-gated MLP verify slice.
 
-Small shapes: per-row relative error of y <= 2e-3, and h (bf16) within one bf16
+Small shapes (the split gate/up launch with its SiLU kernel, and one shape wide
+enough for the paired launch): per-row relative error of y <= 2e-3, and h (bf16) within one bf16
 ulp of the oracle's h plus the first-order effect of the linears' absolute
 error (eps = 1e-5 of each row's max |g|, |u|) on silu(g) * u -- near g = 0 or
 u = 0 a tiny absolute error in g or u is a large relative error in h.
@@ -49,7 +50,10 @@ def _check_h(h, rh, x, gate, up, G, eps=1e-5):
     assert np.mean(h != rh) < 2e-3
 
 
-@pytest.mark.parametrize("H,I,G", [(256, 384, 64), (256, 96, 32), (512, 1024, 32), (2048, 768, 32)])
+# (384, 32800, 32): enough gate/up tiles (2050) for the paired launch, with a
+# ragged last workgroup and K (3 chunks) ending inside the second half
+@pytest.mark.parametrize("H,I,G", [(256, 384, 64), (256, 96, 32), (512, 1024, 32), (2048, 768, 32),
+                                   (384, 32800, 32)])
 def test_small_mlp_parity_and_row_exactness(H, I, G):
     g = np.random.default_rng(H + I + G)
     gate = syn.w4_matrix(g, I, H, G)
