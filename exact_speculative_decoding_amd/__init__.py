@@ -77,6 +77,7 @@ _SIGS = {
     "toy_decoder_destroy": (None, [_vp]),
     "verify_step_workspace": (_sz, [_vp]),
     "verify_step": (_i32, [_vp, _vp, _i32, _i64, Sampling, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "toy_decoder_set_graphs": (_i32, [_vp, _i32]),
     "ev_w4_timing": (_i32, [_i32]),
     "ev_w4_timing_read": (_i32, [C.POINTER(_i64), C.POINTER(C.c_double), C.POINTER(C.c_double)]),
 }
@@ -314,6 +315,7 @@ class ToyDecoder:
         _check(lib().toy_decoder_create(C.byref(c), C.byref(w), _dev(k_cache, "k_cache", _F16),
                                         _dev(v_cache, "v_cache", _F16), self.max_ctx, C.byref(h)))
         self._h = h
+        self._outs = {}  # R -> (sampled, n_commit) kept for graph replay
         self.ws = torch.empty(int(lib().verify_step_workspace(h)), dtype=torch.uint8,
                               device=k_cache.device)
 
@@ -327,16 +329,26 @@ class ToyDecoder:
             _lib.toy_decoder_destroy(h)
             self._h = None
 
+    def set_graphs(self, enable):
+        """Graph replay of verify_step on or off (on by default)."""
+        _check(lib().toy_decoder_set_graphs(self._h, 1 if enable else 0))
+
     def verify_step(self, tokens, pos0, temperature, top_k, top_p, seed, sampled=None,
                     n_commit=None, logits=None, stream=None):
         """One verify pass over tokens [R] int32 (device) at slots pos0..; returns
-        (sampled [R] int32, n_commit [1] int32), device tensors."""
+        (sampled [R] int32, n_commit [1] int32), device tensors.  Without
+        caller buffers the results land in buffers this handle keeps per R, so
+        that the captured step is replayed; the next call with the same R
+        overwrites them."""
         R = tokens.shape[0]
         dev = tokens.device
-        if sampled is None:
-            sampled = torch.empty(R, dtype=torch.int32, device=dev)
-        if n_commit is None:
-            n_commit = torch.empty(1, dtype=torch.int32, device=dev)
+        if sampled is None or n_commit is None:
+            outs = self._outs.get(R)
+            if outs is None:
+                outs = (torch.empty(R, dtype=torch.int32, device=dev), torch.empty(1, dtype=torch.int32, device=dev))
+                self._outs[R] = outs
+            sampled = outs[0] if sampled is None else sampled
+            n_commit = outs[1] if n_commit is None else n_commit
         sp = Sampling(float(temperature), int(top_k), float(top_p), int(seed) & ((1 << 64) - 1))
         _check(lib().verify_step(
             self._h, _dev(tokens, "tokens", (torch.int32,)), R, int(pos0), sp,

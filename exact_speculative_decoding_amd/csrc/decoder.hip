@@ -15,14 +15,19 @@
 //   * row r writes cache slot p and reads slots <= p only, all of which hold the
 //     bytes serial decoding wrote (slot p in this pass, from the same input).
 //
-// Launches per layer: W4 q|k|v, split sum + RoPE + fp16 cache write, attention
-// partials, chunk merge, W4 o, split sum + residual + RMSNorm, W4 gate|up,
-// split sum + SiLU * up, W4 down, split sum + residual + RMSNorm (with the next
-// layer's gains or the final ones).  Then W4 LM head, split sum, keyed sample,
-// accept prefix.
+// Launches per layer (a kernel boundary costs a few microseconds on this
+// chip, more than most of these kernels' work, so the count is kept low):
+// W4 q|k|v with RoPE and the fp16 cache write in its epilogue, attention
+// partials, chunk merge, W4 o, split sum + residual + RMSNorm, W4 gate|up with
+// SiLU * up in its epilogue, W4 down, split sum + residual + RMSNorm (with the
+// next layer's gains or the final ones).  Then W4 LM head, split sum, keyed
+// sample, accept prefix.  After the first kernel (embedding and norm, which
+// takes the call's tokens and position) the step is captured once and
+// replayed as a HIP graph.
 #include <math.h>
 
 #include <algorithm>
+#include <mutex>
 #include <vector>
 
 #include "w4_kernel.h"
@@ -36,9 +41,9 @@ constexpr int kMaxChunks = 128;   // attention partials per (row, head) at most
 constexpr int kMaxQ = 64;         // queries per kv head: R * heads / kv_heads
 constexpr int kPartStride = kHD + 2;  // one attention partial: m, l, acc[128]
 
-struct RopeTab {
-    double invf[kHalf];  // rope_base^(-2i/128), computed once on the host
-};
+// The step's first position sits in the positions array at kPos0Slot (after
+// the 16 rows' sampling positions); every kernel after embed_norm reads it
+// there, so a captured step can be replayed at any position.
 
 constexpr int kRowThreads = 512;  // threads per row in the row kernels (4 columns each per pass)
 
@@ -54,10 +59,6 @@ __device__ __forceinline__ float row_sum(float v, float* red) {
     for (int w = 1; w < kRowThreads / 64; ++w) t += red[w];
     __syncthreads();
     return t;
-}
-
-__device__ __forceinline__ uint16_t f32_to_f16_bits(float v) {
-    return __builtin_bit_cast(uint16_t, (_Float16)v);
 }
 
 // n = bf16(RMSNorm(x) * gain) of one row held as float4s by the block
@@ -85,10 +86,12 @@ __global__ __launch_bounds__(kRowThreads) void embed_norm_kernel(const int* __re
                                                                  const uint16_t* __restrict__ embed, int H, int V,
                                                                  const float* __restrict__ gain, float eps,
                                                                  float* __restrict__ x, uint16_t* __restrict__ n,
-                                                                 long long* __restrict__ positions, long long pos0) {
+                                                                 long long* __restrict__ positions, long long pos0,
+                                                                 int* __restrict__ tok_copy) {
     __shared__ float red[kRowThreads / 64];
     const int r = blockIdx.x, tid = threadIdx.x;
     int tok = tokens[r];
+    if (tid == 0) tok_copy[r] = tok;  // the drafts, where the rest of the step reads them
     tok = tok < 0 ? 0 : (tok >= V ? V - 1 : tok);  // keeps the read inside the table
     const uint16_t* e = embed + (size_t)tok * H;
     f32x4 xv[kMaxRowVec];
@@ -107,6 +110,7 @@ __global__ __launch_bounds__(kRowThreads) void embed_norm_kernel(const int* __re
     }
     norm_store(xv, ss, gain, eps, H, n + (size_t)r * H, red);
     if (tid == 0) positions[r] = pos0 + 1 + r;
+    if (tid == 0 && r == 0) positions[kPos0Slot] = pos0;
 }
 
 // x[r] += sum over s ascending of part[s][r] (a linear's split partials);
@@ -145,71 +149,22 @@ __global__ __launch_bounds__(kRowThreads) void res_norm_kernel(const float* __re
 
 // Value cache layout: blocks of 32 slots, d-major inside a block
 // ([kv_heads][C/32][128][32]), and within a block slot s at position
-// vslot_pos(s): positions 8j..8j+7 hold slots 4j..4j+3 and 16+4j..16+4j+3.
+// vslot_pos32(s): positions 8j..8j+7 hold slots 4j..4j+3 and 16+4j..16+4j+3.
 // That is the order in which one lane of the PV product's B operand (the
 // probabilities, straight out of the score MFMA's accumulator layout) holds
-// its 8 slots, so the values' A operand is one 16-byte load.
-__host__ __device__ inline int vslot_pos(int s) {
-    return s < 16 ? 8 * (s >> 2) + (s & 3) : 8 * ((s - 16) >> 2) + 4 + (s & 3);
-}
-
-// q|k|v of row r = split sums; rotate q and k by position pos0 + r; q to
-// qout [R][NH][128] fp32, k and v to cache slot pos0 + r in fp16.
-__global__ __launch_bounds__(256) void qkv_rope_kernel(const float* __restrict__ part, int S, int NH, int NKV,
-                                                       long long pos0, RopeTab rt, float* __restrict__ qout,
-                                                       uint16_t* __restrict__ kc, uint16_t* __restrict__ vc,
-                                                       int C) {
-    const int r = blockIdx.x, tid = threadIdx.x;
-    const long long P = pos0 + r;
-    const int NQKV = (NH + 2 * NKV) * kHD;
-    const size_t stride = (size_t)16 * NQKV;
-    const float* row = part + (size_t)r * NQKV;
-    auto colsum = [&](int c) {
-        float a = row[c];
-        for (int s = 1; s < S; ++s) a += row[s * stride + c];
-        return a;
-    };
-    __shared__ float cs[kHalf], sn[kHalf];
-    if (tid < kHalf) {  // the row's rotation, once per frequency
-        const double ang = (double)P * rt.invf[tid];
-        cs[tid] = (float)cos(ang);
-        sn[tid] = (float)sin(ang);
-    }
-    __syncthreads();
-    for (int p = tid; p < (NH + NKV) * kHalf; p += 256) {
-        const int hd = p / kHalf, i = p % kHalf;
-        const float a = colsum(hd * kHD + i), b = colsum(hd * kHD + i + kHalf);
-        const float c = cs[i], s = sn[i];
-        const float a2 = a * c - b * s;
-        const float b2 = b * c + a * s;
-        if (hd < NH) {
-            float* q = qout + ((size_t)r * NH + hd) * kHD;
-            q[i] = a2;
-            q[i + kHalf] = b2;
-        } else {
-            uint16_t* k = kc + ((size_t)(hd - NH) * C + P) * kHD;
-            k[i] = f32_to_f16_bits(a2);
-            k[i + kHalf] = f32_to_f16_bits(b2);
-        }
-    }
-    const size_t vblk = ((size_t)(P / kKStep)) * kHD * kKStep;
-    const int vpos = vslot_pos((int)(P % kKStep));
-    for (int p = tid; p < NKV * kHD; p += 256) {
-        const int g = p / kHD, d = p % kHD;
-        vc[(size_t)g * C * kHD + vblk + (size_t)d * kKStep + vpos] = f32_to_f16_bits(colsum((NH + NKV) * kHD + p));
-    }
-}
+// its 8 slots, so the values' A operand is one 16-byte load.  The q|k|v
+// projection writes new slots in this order (its rotation epilogue).
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 struct AttnArgs {
     const float* q;      // [R][NH][128]
     const uint16_t* kc;  // this layer's keys [NKV][C][128] fp16
-    const uint16_t* vc;  // this layer's values, blocked (vslot_pos)
+    const uint16_t* vc;  // this layer's values, blocked (vslot_pos32)
     float* part;         // [16][NH][nchunk_max][130]
     int R, NH, NKV, C, chunk, nchunk_max;
-    long long pos0;
-    float scale;         // 1/sqrt(128)
+    const long long* positions;  // the step's first position at [kPos0Slot]
+    float scale;                 // 1/sqrt(128)
 };
 
 __device__ __forceinline__ f16x8 load_f16x8(const uint16_t* p) {
@@ -235,9 +190,11 @@ __global__ __launch_bounds__(64) void attn_partial_kernel(AttnArgs a) {
     const bool qok = qi < nq;
     const int r = qok ? qi / gq : 0;
     const int h = g * gq + (qok ? qi % gq : 0);
-    const long long P = a.pos0 + r;
-    const long long pmax = a.pos0 + a.R - 1;
+    const long long pos0 = a.positions[kPos0Slot];
+    const long long P = pos0 + r;
+    const long long pmax = pos0 + a.R - 1;
     const long long cstart = (long long)chunk * a.chunk;
+    if (cstart > pmax) return;  // the grid covers the whole cache; this chunk holds no slot yet
     const long long cend = min(cstart + a.chunk - 1, pmax);
 
     // Q^T fragments: query ln, d = 32 ds + 8 grp + i
@@ -389,7 +346,9 @@ __global__ __launch_bounds__(64) void attn_partial_kernel(AttnArgs a) {
 // o[r][h][d] = bf16(sum_c acc_c[d] e^(m_c - M) / sum_c l_c e^(m_c - M)) over
 // the chunks c = 0 .. (pos0 + r) / chunk, ascending; M = max_c m_c.
 __global__ __launch_bounds__(kHD) void attn_merge_kernel(const float* __restrict__ part, int NH, int chunk,
-                                                         int nchunk_max, long long pos0, uint16_t* __restrict__ o) {
+                                                         int nchunk_max, const long long* __restrict__ positions,
+                                                         uint16_t* __restrict__ o) {
+    const long long pos0 = positions[kPos0Slot];
     __shared__ float sm[kMaxChunks], se[kMaxChunks], sl[kMaxChunks];
     __shared__ float red[2];
     const int r = blockIdx.x, h = blockIdx.y, d = threadIdx.x;
@@ -424,12 +383,24 @@ struct StepLayout {
     int chunk, nchunk_max;
     bool gu_pair;
     size_t off_x, off_n, off_o, off_q, off_part, off_pg, off_pu, off_h, off_att, off_logits, off_pos, off_acc,
-        off_sws, total;
+        off_sws, off_tok, total;
 };
 
 }  // namespace ev
 
 using namespace ev;
+
+// A captured step (everything after embed_norm) for one set of baked
+// arguments; replayed on the caller's stream.
+struct StepGraph {
+    int R;
+    const void* ws;
+    int32_t* sampled;
+    int32_t* n_commit;
+    ev_sampling sampling;
+    hipGraphExec_t exec;
+};
+constexpr size_t kMaxStepGraphs = 16;
 
 struct ev_decoder {
     ev_decoder_config cfg;
@@ -440,25 +411,36 @@ struct ev_decoder {
     uint16_t* kc;
     uint16_t* vc;
     int C;
-    RopeTab rope;
+    float2* rot = nullptr;  // [C][64] (cos, sin) of slot p's rotation, fp32 of the fp64 values
     int NQKV, DQ;
     StepLayout L;
+    bool use_graphs = true;
+    std::mutex graph_mu;            // the cache below
+    hipStream_t capture = nullptr;  // capture stream, default priority
+    std::vector<StepGraph> graphs;
+    ~ev_decoder() {
+        if (!graphs.empty()) (void)hipDeviceSynchronize();
+        for (StepGraph& g : graphs) (void)hipGraphExecDestroy(g.exec);
+        if (capture) (void)hipStreamDestroy(capture);
+        if (rot) (void)hipFree(rot);
+    }
 };
 
 static StepLayout step_layout(const ev_decoder_config& c, int NQKV, int DQ, int C) {
     StepLayout L;
     const int H = c.hidden, I = c.intermediate, V = c.vocab;
-    L.p_qkv = plan_w4(NQKV, H, 1);
+    L.p_qkv = plan_w4_pair(NQKV, H);  // halved launch with the rotation epilogue
     L.p_o = plan_w4(H, DQ, 1);
-    L.gu_pair = use_pair(I);
+    // paired gate/up: at the decoder's sizes every kernel boundary costs more
+    // than the split launch's extra waves win back
+    L.gu_pair = true;
     L.p_gu = L.gu_pair ? plan_w4_pair(I, H) : plan_w4(I, H, 2);
     L.p_down = plan_w4(H, I, 1);
     L.p_lm = plan_w4(V, H, 1);
     // chunk: a multiple of 64 slots with at most kMaxChunks chunks in the cache
     L.chunk = 64 * ((C + 64 * kMaxChunks - 1) / (64 * kMaxChunks));
     L.nchunk_max = (C + L.chunk - 1) / L.chunk;
-    size_t part = (size_t)L.p_qkv.S * NQKV;
-    part = std::max(part, (size_t)L.p_o.S * H);
+    size_t part = (size_t)L.p_o.S * H;
     part = std::max(part, (size_t)L.p_down.S * H);
     part = std::max(part, (size_t)L.p_lm.S * V);
     size_t off = 0;
@@ -477,9 +459,10 @@ static StepLayout step_layout(const ev_decoder_config& c, int NQKV, int DQ, int 
     L.off_h = take(sizeof(uint16_t) * 16 * I);
     L.off_att = take(sizeof(float) * 16 * (size_t)c.heads * L.nchunk_max * kPartStride);
     L.off_logits = take(sizeof(float) * 16 * (size_t)V);
-    L.off_pos = take(sizeof(long long) * 16);
+    L.off_pos = take(sizeof(long long) * (kPos0Slot + 1));
     L.off_acc = take(sizeof(int32_t) * 4);
     L.off_sws = take(keyed_sample_workspace(V));
+    L.off_tok = take(sizeof(int32_t) * 16);
     L.total = off;
     return L;
 }
@@ -525,7 +508,26 @@ extern "C" int32_t toy_decoder_create(const ev_decoder_config* cfg, const ev_dec
             !aligned(y.w_gate, 16) || !aligned(y.w_up, 16) || !aligned(y.w_down, 16))
             return fail(EV_EINVAL, "%s: layer %d: misaligned pointer", who, l);
     }
+    // (cos, sin) of every slot's rotation: angle p * base^(-2i/128) in fp64,
+    // rounded to fp32
+    std::vector<float2> rot((size_t)max_ctx * kHalf);
+    double invf[kHalf];
+    for (int i = 0; i < kHalf; ++i) invf[i] = pow(c.rope_base, -2.0 * i / kHD);
+    for (int p = 0; p < max_ctx; ++p)
+        for (int i = 0; i < kHalf; ++i) {
+            const double ang = (double)p * invf[i];
+            rot[(size_t)p * kHalf + i] = make_float2((float)cos(ang), (float)sin(ang));
+        }
+    float2* rot_dev = nullptr;
+    if (hipMalloc(&rot_dev, rot.size() * sizeof(float2)) != hipSuccess)
+        return fail(EV_EHIP, "%s: hipMalloc of the rotation table failed", who);
+    if ((rc = check_hip(hipMemcpy(rot_dev, rot.data(), rot.size() * sizeof(float2), hipMemcpyHostToDevice),
+                        "rotation table copy"))) {
+        (void)hipFree(rot_dev);
+        return rc;
+    }
     ev_decoder* m = new ev_decoder;
+    m->rot = rot_dev;
     m->cfg = c;
     m->layers.assign(w->layers, w->layers + c.layers);
     m->embed = w->embed;
@@ -534,7 +536,6 @@ extern "C" int32_t toy_decoder_create(const ev_decoder_config* cfg, const ev_dec
     m->kc = k_cache;
     m->vc = v_cache;
     m->C = max_ctx;
-    for (int i = 0; i < kHalf; ++i) m->rope.invf[i] = pow(c.rope_base, -2.0 * i / kHD);
     m->NQKV = NQKV;
     m->DQ = DQ;
     m->L = step_layout(c, NQKV, DQ, max_ctx);
@@ -546,29 +547,24 @@ extern "C" void toy_decoder_destroy(ev_decoder* m) { delete m; }
 
 extern "C" size_t verify_step_workspace(const ev_decoder* m) { return m ? m->L.total : 0; }
 
-extern "C" int32_t verify_step(ev_decoder* m, const int32_t* tokens, int32_t R, int64_t pos0, ev_sampling sampling,
-                               int32_t* sampled, int32_t* n_commit, float* logits, void* ws, size_t ws_bytes,
-                               void* stream) {
+extern "C" int32_t toy_decoder_set_graphs(ev_decoder* m, int32_t enable) {
     clear_error();
-    const char* who = "verify_step";
-    int32_t rc;
-    if (!m) return fail(EV_EINVAL, "%s: NULL decoder", who);
-    if ((rc = check_lanes(who, R))) return rc;
-    if (!tokens || !sampled || !n_commit) return fail(EV_EINVAL, "%s: NULL pointer", who);
-    if (!aligned(tokens, 4) || !aligned(sampled, 4) || !aligned(n_commit, 4) || (logits && !aligned(logits, 16)))
-        return fail(EV_EINVAL, "%s: misaligned pointer", who);
-    if (pos0 < 0 || pos0 + R > m->C)
-        return fail(EV_EINVAL, "%s: slots %lld..%lld outside the cache of %d", who, (long long)pos0,
-                    (long long)pos0 + R - 1, m->C);
-    if ((rc = check_sampling(who, sampling))) return rc;
-    const StepLayout& L = m->L;
-    if ((rc = check_ws(who, ws, ws_bytes, L.total))) return rc;
+    if (!m) return fail(EV_EINVAL, "toy_decoder_set_graphs: NULL decoder");
+    m->use_graphs = enable != 0;
+    return EV_OK;
+}
 
+// Everything of a verify step after embed_norm, on stream st.  The step's
+// position comes from the device (positions[kPos0Slot]) and the drafts from
+// embed_norm's copy, so the same launches can be captured once and replayed
+// at any position with any tokens.
+static int32_t step_body(ev_decoder* m, int R, const ev_sampling& sampling, int32_t* sampled, int32_t* n_commit,
+                         float* logits, unsigned char* b, hipStream_t st) {
+    int32_t rc;
+    const StepLayout& L = m->L;
     const ev_decoder_config& c = m->cfg;
     const int H = c.hidden, I = c.intermediate, V = c.vocab, G = c.group, NH = c.heads, NKV = c.kv_heads;
     const float eps = (float)c.rms_eps;
-    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-    unsigned char* b = reinterpret_cast<unsigned char*>(ws);
     float* x = reinterpret_cast<float*>(b + L.off_x);
     uint16_t* n = reinterpret_cast<uint16_t*>(b + L.off_n);
     uint16_t* o = reinterpret_cast<uint16_t*>(b + L.off_o);
@@ -579,8 +575,9 @@ extern "C" int32_t verify_step(ev_decoder* m, const int32_t* tokens, int32_t R, 
     uint16_t* h = reinterpret_cast<uint16_t*>(b + L.off_h);
     float* att = reinterpret_cast<float*>(b + L.off_att);
     float* lg = logits ? logits : reinterpret_cast<float*>(b + L.off_logits);
-    int64_t* pos = reinterpret_cast<int64_t*>(b + L.off_pos);
+    const long long* pos = reinterpret_cast<const long long*>(b + L.off_pos);
     int32_t* n_accept = reinterpret_cast<int32_t*>(b + L.off_acc);
+    const int32_t* toks = reinterpret_cast<const int32_t*>(b + L.off_tok);
     void* sws = b + L.off_sws;
 
     auto linear = [&](const void* wmat, const uint16_t* xin, int K, int N, const W4Plan& p) {
@@ -594,25 +591,31 @@ extern "C" int32_t verify_step(ev_decoder* m, const int32_t* tokens, int32_t R, 
         return launch_w4(a, 1, p, K, G, st);
     };
 
-    hipLaunchKernelGGL(embed_norm_kernel, dim3(R), dim3(kRowThreads), 0, st, tokens, m->embed, H, V, m->layers[0].attn_norm,
-                       eps, x, n, reinterpret_cast<long long*>(pos), (long long)pos0);
-    if ((rc = check_hip(hipGetLastError(), "embed_norm launch"))) return rc;
-
-    const int nchunks = (int)((pos0 + R - 1) / L.chunk) + 1;
     const int nqt = (R * (NH / NKV) + 15) / 16;
     for (int l = 0; l < c.layers; ++l) {
         const ev_decoder_layer& y = m->layers[l];
         uint16_t* kcl = m->kc + (size_t)l * NKV * m->C * kHD;
         uint16_t* vcl = m->vc + (size_t)l * NKV * m->C * kHD;
-        if ((rc = linear(y.w_qkv, n, H, m->NQKV, L.p_qkv))) return rc;
-        hipLaunchKernelGGL(qkv_rope_kernel, dim3(R), dim3(256), 0, st, part, L.p_qkv.S, NH, NKV, (long long)pos0,
-                           m->rope, q, kcl, vcl, m->C);
-        if ((rc = check_hip(hipGetLastError(), "qkv_rope launch"))) return rc;
-        AttnArgs aa{q, kcl, vcl, att, R, NH, NKV, m->C, L.chunk, L.nchunk_max, (long long)pos0, 0.08838834764831845f};
-        hipLaunchKernelGGL(attn_partial_kernel, dim3(nchunks, NKV, nqt), dim3(64), 0, st, aa);
+        {  // q|k|v, rotated, straight to the query rows and the caches
+            W4Args a{};
+            a.w[0] = a.w[1] = reinterpret_cast<const uint8_t*>(y.w_qkv);
+            a.x = n;
+            a.R = R;
+            a.N = m->NQKV;
+            a.rope.rot = m->rot;
+            a.rope.positions = pos;
+            a.rope.q = q;
+            a.rope.kc = kcl;
+            a.rope.vc = vcl;
+            a.rope.C = m->C;
+            a.rope.NH = NH;
+            a.rope.NKV = NKV;
+            if ((rc = launch_w4_rope(a, L.p_qkv, H, G, st))) return rc;
+        }
+        AttnArgs aa{q, kcl, vcl, att, R, NH, NKV, m->C, L.chunk, L.nchunk_max, pos, 0.08838834764831845f};
+        hipLaunchKernelGGL(attn_partial_kernel, dim3(L.nchunk_max, NKV, nqt), dim3(64), 0, st, aa);
         if ((rc = check_hip(hipGetLastError(), "attn_partial launch"))) return rc;
-        hipLaunchKernelGGL(attn_merge_kernel, dim3(R, NH), dim3(kHD), 0, st, att, NH, L.chunk, L.nchunk_max,
-                           (long long)pos0, o);
+        hipLaunchKernelGGL(attn_merge_kernel, dim3(R, NH), dim3(kHD), 0, st, att, NH, L.chunk, L.nchunk_max, pos, o);
         if ((rc = check_hip(hipGetLastError(), "attn_merge launch"))) return rc;
         if ((rc = linear(y.w_o, o, m->DQ, H, L.p_o))) return rc;
         hipLaunchKernelGGL(res_norm_kernel, dim3(R), dim3(kRowThreads), 0, st, part, L.p_o.S, H, x, y.mlp_norm, eps, n);
@@ -643,7 +646,86 @@ extern "C" int32_t verify_step(ev_decoder* m, const int32_t* tokens, int32_t R, 
     }
     if ((rc = linear(m->w_lm, n, H, V, L.p_lm))) return rc;
     if ((rc = launch_splitk_reduce(part, L.p_lm.S, V, R, lg, st))) return rc;
-    if ((rc = keyed_sample(lg, R, V, pos, sampling, sampled, nullptr, sws, keyed_sample_workspace(V), stream)))
+    void* sv = reinterpret_cast<void*>(st);
+    if ((rc = keyed_sample(lg, R, V, reinterpret_cast<const int64_t*>(pos), sampling, sampled, nullptr, sws,
+                           keyed_sample_workspace(V), sv)))
         return rc;
-    return accept_prefix(sampled, R, R > 1 ? tokens + 1 : nullptr, R - 1, n_accept, n_commit, stream);
+    return accept_prefix(sampled, R, R > 1 ? toks + 1 : nullptr, R - 1, n_accept, n_commit, sv);
+}
+
+static bool same_sampling(const ev_sampling& a, const ev_sampling& b) {
+    return a.temperature == b.temperature && a.top_k == b.top_k && a.top_p == b.top_p && a.seed == b.seed;
+}
+
+// The captured step for these arguments: found in the cache, or captured on
+// the decoder's own stream (nothing runs during capture) and kept.
+static int32_t step_graph(ev_decoder* m, int R, const ev_sampling& sampling, int32_t* sampled, int32_t* n_commit,
+                          void* ws, hipGraphExec_t* out) {
+    for (const StepGraph& g : m->graphs)
+        if (g.R == R && g.ws == ws && g.sampled == sampled && g.n_commit == n_commit && same_sampling(g.sampling, sampling)) {
+            *out = g.exec;
+            return EV_OK;
+        }
+    int32_t rc;
+    if (!m->capture && (rc = check_hip(hipStreamCreateWithFlags(&m->capture, hipStreamNonBlocking), "capture stream")))
+        return rc;
+    if ((rc = check_hip(hipStreamBeginCapture(m->capture, hipStreamCaptureModeThreadLocal), "begin capture")))
+        return rc;
+    rc = step_body(m, R, sampling, sampled, n_commit, nullptr, reinterpret_cast<unsigned char*>(ws), m->capture);
+    hipGraph_t graph = nullptr;
+    const hipError_t end = hipStreamEndCapture(m->capture, &graph);
+    if (!rc) rc = check_hip(end, "end capture");
+    hipGraphExec_t exec = nullptr;
+    if (!rc) rc = check_hip(hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0), "graph instantiate");
+    if (graph) (void)hipGraphDestroy(graph);
+    if (rc) return rc;
+    if (m->graphs.size() >= kMaxStepGraphs) {  // the oldest goes; it may still be queued on some stream
+        if ((rc = check_hip(hipDeviceSynchronize(), "graph eviction"))) {
+            (void)hipGraphExecDestroy(exec);
+            return rc;
+        }
+        (void)hipGraphExecDestroy(m->graphs.front().exec);
+        m->graphs.erase(m->graphs.begin());
+    }
+    m->graphs.push_back(StepGraph{R, ws, sampled, n_commit, sampling, exec});
+    *out = exec;
+    return EV_OK;
+}
+
+extern "C" int32_t verify_step(ev_decoder* m, const int32_t* tokens, int32_t R, int64_t pos0, ev_sampling sampling,
+                               int32_t* sampled, int32_t* n_commit, float* logits, void* ws, size_t ws_bytes,
+                               void* stream) {
+    clear_error();
+    const char* who = "verify_step";
+    int32_t rc;
+    if (!m) return fail(EV_EINVAL, "%s: NULL decoder", who);
+    if ((rc = check_lanes(who, R))) return rc;
+    if (!tokens || !sampled || !n_commit) return fail(EV_EINVAL, "%s: NULL pointer", who);
+    if (!aligned(tokens, 4) || !aligned(sampled, 4) || !aligned(n_commit, 4) || (logits && !aligned(logits, 16)))
+        return fail(EV_EINVAL, "%s: misaligned pointer", who);
+    if (pos0 < 0 || pos0 + R > m->C)
+        return fail(EV_EINVAL, "%s: slots %lld..%lld outside the cache of %d", who, (long long)pos0,
+                    (long long)pos0 + R - 1, m->C);
+    if ((rc = check_sampling(who, sampling))) return rc;
+    const StepLayout& L = m->L;
+    if ((rc = check_ws(who, ws, ws_bytes, L.total))) return rc;
+
+    const ev_decoder_config& c = m->cfg;
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    unsigned char* b = reinterpret_cast<unsigned char*>(ws);
+    // the step's per-call inputs: rows' tokens and positions, on the device
+    hipLaunchKernelGGL(embed_norm_kernel, dim3(R), dim3(kRowThreads), 0, st, tokens, m->embed, c.hidden, c.vocab,
+                       m->layers[0].attn_norm, (float)c.rms_eps, reinterpret_cast<float*>(b + L.off_x),
+                       reinterpret_cast<uint16_t*>(b + L.off_n), reinterpret_cast<long long*>(b + L.off_pos),
+                       (long long)pos0, reinterpret_cast<int*>(b + L.off_tok));
+    if ((rc = check_hip(hipGetLastError(), "embed_norm launch"))) return rc;
+    // the rest: one graph launch when the step can be replayed as captured
+    // (no logits asked for, no per-launch measurement), else launch by launch
+    if (m->use_graphs && !logits && !w4_timing_active()) {
+        std::lock_guard<std::mutex> lk(m->graph_mu);
+        hipGraphExec_t exec;
+        if ((rc = step_graph(m, R, sampling, sampled, n_commit, ws, &exec))) return rc;
+        return check_hip(hipGraphLaunch(exec, st), "step graph launch");
+    }
+    return step_body(m, R, sampling, sampled, n_commit, logits, b, st);
 }

@@ -37,6 +37,11 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
     return (uint16_t)(u >> 16);
 }
 
+// fp32 -> fp16 bits, round to nearest even (the hardware conversion).
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float v) {
+    return __builtin_bit_cast(uint16_t, (_Float16)v);
+}
+
 // fp16 bits -> fp32 (exact) via the hardware conversion.
 __device__ __forceinline__ float f16_to_f32(uint16_t h) {
     _Float16 v = __builtin_bit_cast(_Float16, h);

@@ -93,7 +93,27 @@ struct W4Args {
     uint16_t* h;
     uint16_t* h_copy;
     long hgstride;
+    // q|k|v launch with rotation only (N = (NH + 2 NKV) * 128 columns, heads
+    // q..., k..., v...): row r sits at position positions[kPos0Slot] + r.
+    struct {
+        const float2* rot;             // [C][64] (cos, sin) per slot
+        const long long* positions;    // the step's first position at [kPos0Slot]
+        float* q;                      // [R][NH][128] fp32
+        uint16_t* kc;                  // [NKV][C][128] fp16
+        uint16_t* vc;                  // [NKV][C/32][128][32] fp16, slot order vslot_pos32
+        int C, NH, NKV;
+    } rope;
 };
+
+// Slot of the step's first position in the decoder's positions array (after
+// the 16 rows' sampling positions).
+constexpr int kPos0Slot = 16;
+
+// Value cache: blocks of 32 slots, d-major inside a block, slot s at position
+// vslot_pos32(s): positions 8j..8j+7 hold slots 4j..4j+3 and 16+4j..16+4j+3.
+__host__ __device__ inline int vslot_pos32(int s) {
+    return s < 16 ? 8 * (s >> 2) + (s & 3) : 8 * ((s - 16) >> 2) + 4 + (s & 3);
+}
 
 // Launch the W4 kernel over `ngroups` groups (1 for a plain launch) of
 // `nmat` matrices each.  Fills the plan-derived fields of `args`.
@@ -117,6 +137,10 @@ inline W4Plan plan_w4_pair(int N, int K) {
 // h = bf16(silu(x W_gate^T) * (x W_up^T)) for the launch's rows, per group.
 int32_t launch_w4_pair(W4Args args, const W4Plan& p, int K, int G, hipStream_t st, int ngroups = 1);
 
+// q|k|v projection with rotation (args.w[0] = the q|k|v matrix, args.rope
+// set; plan from plan_w4_pair(N, K)): one workgroup per head.
+int32_t launch_w4_rope(W4Args args, const W4Plan& p, int K, int G, hipStream_t st);
+
 // A dense gate/up pair (I x H each) runs paired when its tiles alone give the
 // target wave count; otherwise as a split launch of both matrices followed by
 // silu_reduce, whose extra split waves outweigh the partial rows.
@@ -136,6 +160,9 @@ int32_t launch_silu_reduce(const float* pg, const float* pu, int S, int I, int R
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 int32_t check_lanes(const char* who, int R);
+
+// True while the per-workgroup timing hook records W4 launches.
+bool w4_timing_active();
 int32_t check_ws(const char* who, void* ws, size_t ws_bytes, size_t need);
 
 }  // namespace ev

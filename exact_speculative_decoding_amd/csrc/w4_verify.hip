@@ -94,23 +94,33 @@ __device__ __forceinline__ uint16_t silu_mul_bf16(float g, float u) {
     return f32_to_bf16_rne(sg * u);
 }
 
+enum W4Mode { kPlain = 0, kPairMode = 1, kRopeMode = 2 };
+
 // One workgroup of a W4 pass.
-//  * Plain (PAIR false, kWaves waves): workgroup blk computes its waves' kNT
-//    tiles of one matrix over one K-split and writes them to the split's
-//    partial (or output) rows.
-//  * Paired gate/up (PAIR true, 2 kWaves waves): wave w's two tiles are the
-//    gate and the up tile of the same 16 columns; the first kWaves waves take
-//    the first half of K (a.cps chunks), the others the rest, each half with
-//    its own activation slabs.  The halves meet in LDS, g = first + second
-//    half (that order), likewise u, and the workgroup writes
-//    h = bf16(silu(g) * u): no partial rows and no second kernel.
-template <int G, bool PAIR>
+//  * kPlain (kWaves waves): workgroup blk computes its waves' kNT tiles of
+//    one matrix over one K-split and writes them to the split's partial (or
+//    output) rows.
+//  * The halved modes (2 kWaves waves): the first kWaves waves take the first
+//    half of K (a.cps chunks), the others the rest, each half with its own
+//    activation slabs; the halves meet in LDS (first half + second half) and
+//    the workgroup writes finished values, with no partial rows and no second
+//    kernel.
+//    - kPairMode: wave w's two tiles are the gate and the up tile of the
+//      same 16 columns; h = bf16(silu(g) * u).
+//    - kRopeMode (the q|k|v projection): workgroup b is head b (8 tiles);
+//      wave w's two tiles are tiles w and w + 4 of the head, so a lane holds
+//      both members (d, d + 64) of its rotation pairs.  Query and key heads
+//      are turned by the row's position (the (cos, sin) table of the slot),
+//      queries go to the fp32 query rows and keys to their cache slot in
+//      fp16; value heads go to the blocked value cache in fp16.
+template <int G, int MODE>
 __device__ __forceinline__ void w4_block(const W4Args& a, long blk, uint8_t (*xlds)[kSlab]) {
+    constexpr bool PAIR = MODE != kPlain;  // the two K-halves in one workgroup
     constexpr int GPC = kKC / G;                // groups per chunk
     constexpr int SBW = GPC;                    // (scale, bias) dwords per lane per chunk
     constexpr uint32_t CB = 1024 + 64 * GPC;    // packed bytes per tile-chunk
     static_assert(kSC % kPD == 0, "ring depth must divide the superchunk");
-    static_assert(!PAIR || kNT == 2, "a paired wave holds one gate and one up tile");
+    static_assert(!PAIR || kNT == 2, "a halved-mode wave holds two tiles");
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -142,7 +152,7 @@ __device__ __forceinline__ void w4_block(const W4Args& a, long blk, uint8_t (*xl
     // rows of this workgroup's pass, their activation rows, weights and outputs
     int rows = a.R;
     const uint8_t* wmat = a.w[mi];
-    const uint8_t* wmat1 = a.w[1];  // the up matrix of a paired launch
+    const uint8_t* wmat1 = MODE == kPairMode ? a.w[1] : a.w[0];  // the second tile's matrix
     float* out = a.out[mi] + (size_t)split * a.split_stride;
     uint16_t* hout = a.h;
     uint16_t* hcopy = a.h_copy;
@@ -171,13 +181,13 @@ __device__ __forceinline__ void w4_block(const W4Args& a, long blk, uint8_t (*xl
     // the buffer descriptors in scalar registers whatever the compiler proved
     const uint32_t wbytes = __builtin_amdgcn_readfirstlane(a.wbytes);
     const rsrc_t rw = make_rsrc(uniform_ptr(wmat), wbytes);
-    const rsrc_t rw1 = PAIR ? make_rsrc(uniform_ptr(wmat1), wbytes) : rw;
+    const rsrc_t rw1 = MODE == kPairMode ? make_rsrc(uniform_ptr(wmat1), wbytes) : rw;
     const rsrc_t rx = make_rsrc(uniform_ptr(a.x), __builtin_amdgcn_readfirstlane(a.xbytes));
     uint32_t tbase[kNT];
     bool tok[kNT];
 #pragma unroll
     for (int t = 0; t < kNT; ++t) {
-        const int tile = PAIR ? cg : cg * kNT + t;
+        const int tile = MODE == kPairMode ? cg : (MODE == kRopeMode ? 8 * cgb + wv + 4 * t : cg * kNT + t);
         tok[t] = tile < a.tiles;
         tbase[t] = tok[t] ? (EV_W4_CHUNK_MAJOR ? (uint32_t)tile * CB : (uint32_t)tile * (uint32_t)a.nchunks * CB)
                           : 0u;
@@ -232,7 +242,7 @@ __device__ __forceinline__ void w4_block(const W4Args& a, long blk, uint8_t (*xl
         for (int t = 0; t < kNT; ++t) {
             const bool ok = live && tok[t];
             const uint32_t so = tbase[t] + (uint32_t)c * cstride;
-            const rsrc_t r = (PAIR && t == 1) ? rw1 : rw;
+            const rsrc_t r = (MODE == kPairMode && t == 1) ? rw1 : rw;
             qr[slot][t] = bload128(r, ok ? vq : kOOB, so);
             if (GPC == 2) {
                 const u32x2 v = bload64(r, ok ? vsb : kOOB, so);
@@ -336,7 +346,40 @@ __device__ __forceinline__ void w4_block(const W4Args& a, long blk, uint8_t (*xl
             for (int t = 0; t < kNT; ++t) ex[(wv * kNT + t) * 64 + lane] = y[t];
         }
         __syncthreads();
-        if (half == 0) {
+        if (half == 0 && MODE == kRopeMode) {
+#pragma unroll
+            for (int t = 0; t < kNT; ++t) y[t] += ex[(wv * kNT + t) * 64 + lane];
+            const int hd = cgb, d = 16 * wv + ln;  // head, and d < 64 of the pair (d, d + 64)
+            const long long pos0 = a.rope.positions[kPos0Slot];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 4 * j + i;
+                if (r >= rows) continue;
+                const long long P = pos0 + r;
+                const float va = y[0][i], vb = y[1][i];
+                if (hd < a.rope.NH + a.rope.NKV) {
+                    const float2 cs = a.rope.rot[(size_t)P * 64 + d];
+                    const float a2 = va * cs.x - vb * cs.y;
+                    const float b2 = vb * cs.x + va * cs.y;
+                    if (hd < a.rope.NH) {
+                        float* q = a.rope.q + ((size_t)r * a.rope.NH + hd) * 128;
+                        q[d] = a2;
+                        q[d + 64] = b2;
+                    } else {
+                        uint16_t* k = a.rope.kc + ((size_t)(hd - a.rope.NH) * a.rope.C + P) * 128;
+                        k[d] = f32_to_f16_bits(a2);
+                        k[d + 64] = f32_to_f16_bits(b2);
+                    }
+                } else {
+                    const int g = hd - a.rope.NH - a.rope.NKV;
+                    uint16_t* v = a.rope.vc + (size_t)g * a.rope.C * 128 + (size_t)(P / 32) * 128 * 32 +
+                                  vslot_pos32((int)(P % 32));
+                    v[(size_t)d * 32] = f32_to_f16_bits(va);
+                    v[(size_t)(d + 64) * 32] = f32_to_f16_bits(vb);
+                }
+            }
+        }
+        if (half == 0 && MODE == kPairMode) {
 #pragma unroll
             for (int t = 0; t < kNT; ++t) y[t] += ex[(wv * kNT + t) * 64 + lane];
             const int n = cg * 16 + ln;
@@ -373,19 +416,20 @@ template <int G>
 __global__ __launch_bounds__(kThreads) void w4_verify_kernel(W4Args a) {
     __shared__ __align__(16) uint8_t xlds[2][kSlab];
     if (a.tstamp && threadIdx.x == 0) a.tstamp[2 * blockIdx.x] = wall_clock64();
-    w4_block<G, false>(a, blockIdx.x, xlds);
+    w4_block<G, kPlain>(a, blockIdx.x, xlds);
     if (a.tstamp) {  // uniform; grouped launches (which may return early) are never timed
         __syncthreads();
         if (threadIdx.x == 0) a.tstamp[2 * blockIdx.x + 1] = wall_clock64();
     }
 }
 
-// Paired gate/up launch: workgroups of two halves (see w4_block).
-template <int G>
+// Halved-mode launches (paired gate/up, q|k|v with rotation): workgroups of
+// two halves (see w4_block).
+template <int G, int MODE>
 __global__ __launch_bounds__(2 * kThreads) void w4_pair_kernel(W4Args a) {
     __shared__ __align__(16) uint8_t xlds[4][kSlab];
     if (a.tstamp && threadIdx.x == 0) a.tstamp[2 * blockIdx.x] = wall_clock64();
-    w4_block<G, true>(a, blockIdx.x, xlds);
+    w4_block<G, MODE>(a, blockIdx.x, xlds);
     if (a.tstamp) {
         __syncthreads();
         if (threadIdx.x == 0) a.tstamp[2 * blockIdx.x + 1] = wall_clock64();
@@ -550,15 +594,18 @@ int32_t launch_w4(W4Args args, int nmat, const W4Plan& p, int K, int G, hipStrea
     return check_hip(hipGetLastError(), "w4_verify_kernel launch");
 }
 
-int32_t launch_w4_pair(W4Args args, const W4Plan& p, int K, int G, hipStream_t st, int ngroups) {
+// A halved-mode launch: paired gate/up (ncgb = column blocks of kWaves
+// tiles) or q|k|v with rotation (ncgb = heads).
+static int32_t launch_w4_halved(W4Args args, const W4Plan& p, int K, int G, hipStream_t st, int ngroups,
+                                bool rope) {
     args.K = K;
-    args.nmat = 2;
+    args.nmat = rope ? 1 : 2;
     args.nchunks = p.nchunks;
     args.tiles = w4_tiles(args.N);
     args.cps = p.cps;
     args.S = 2;
     args.ncg = p.ncg;
-    args.ncgb = (p.ncg + kWaves - 1) / kWaves;
+    args.ncgb = rope ? args.N / 128 : (p.ncg + kWaves - 1) / kWaves;
     args.blocks = (long)ngroups * args.ncgb;
     args.wbytes = (uint32_t)w4_blob_bytes(args.N, K, G);
     if (!args.gexp) args.xbytes = (uint32_t)((size_t)args.R * K * 2);  // grouped: set by the caller
@@ -566,15 +613,32 @@ int32_t launch_w4_pair(W4Args args, const W4Plan& p, int K, int G, hipStream_t s
     args.doff = kDecodeOr;
     args.tstamp = nullptr;
     if (!args.gexp) {
-        int32_t rc = timing_slots(args.blocks, w4_algo_bytes(2, args.R, K, args.N, G), &args.tstamp);
+        int32_t rc = timing_slots(args.blocks, w4_algo_bytes(args.nmat, args.R, K, args.N, G), &args.tstamp);
         if (rc) return rc;
     }
     const unsigned blocks = (unsigned)args.blocks;
-    if (G == 64)
-        hipLaunchKernelGGL(w4_pair_kernel<64>, dim3(blocks), dim3(2 * kThreads), 0, st, args);
-    else
-        hipLaunchKernelGGL(w4_pair_kernel<32>, dim3(blocks), dim3(2 * kThreads), 0, st, args);
-    return check_hip(hipGetLastError(), "w4_pair_kernel launch");
+    if (rope) {
+        if (G == 64)
+            hipLaunchKernelGGL((w4_pair_kernel<64, kRopeMode>), dim3(blocks), dim3(2 * kThreads), 0, st, args);
+        else
+            hipLaunchKernelGGL((w4_pair_kernel<32, kRopeMode>), dim3(blocks), dim3(2 * kThreads), 0, st, args);
+    } else {
+        if (G == 64)
+            hipLaunchKernelGGL((w4_pair_kernel<64, kPairMode>), dim3(blocks), dim3(2 * kThreads), 0, st, args);
+        else
+            hipLaunchKernelGGL((w4_pair_kernel<32, kPairMode>), dim3(blocks), dim3(2 * kThreads), 0, st, args);
+    }
+    return check_hip(hipGetLastError(), "w4 halved-mode launch");
+}
+
+int32_t launch_w4_pair(W4Args args, const W4Plan& p, int K, int G, hipStream_t st, int ngroups) {
+    return launch_w4_halved(args, p, K, G, st, ngroups, false);
+}
+
+int32_t launch_w4_rope(W4Args args, const W4Plan& p, int K, int G, hipStream_t st) {
+    if (args.N % 128 != 0 || args.N / 128 != args.rope.NH + 2 * args.rope.NKV)
+        return fail(EV_EINVAL, "w4 rope launch: N=%d is not (NH + 2 NKV) heads of 128", args.N);
+    return launch_w4_halved(args, p, K, G, st, 1, true);
 }
 
 // Workspace of verify_linear_w4: split partials [S][16][N] (none if S == 1).
@@ -621,6 +685,11 @@ int32_t check_ws(const char* who, void* ws, size_t ws_bytes, size_t need) {
                     ws ? ws_bytes : (size_t)0);
     if (!aligned(ws, 256)) return fail(EV_EINVAL, "%s: workspace must be 256-byte aligned", who);
     return EV_OK;
+}
+
+bool w4_timing_active() {
+    std::lock_guard<std::mutex> lk(g_timing.mu);
+    return g_timing.on;
 }
 
 }  // namespace ev

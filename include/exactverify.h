@@ -263,17 +263,19 @@ typedef struct {
 
 typedef struct ev_decoder ev_decoder;
 
-/* Creates a host-side handle (no device memory) over the caller's weights    */
-/* and caches, 16-byte aligned, max_ctx a multiple of 32:                     */
+/* Creates a handle over the caller's weights and caches, 16-byte aligned,    */
+/* max_ctx a multiple of 32; the handle owns one device table, the (cos, sin) */
+/* of every slot's rotation (max_ctx * 512 bytes):                            */
 /*   k_cache (device) [layers][kv_heads][max_ctx][128] fp16;                  */
 /*   v_cache (device) [layers][kv_heads][max_ctx/32][128][32] fp16: blocks of */
 /*           32 slots, d-major, slot s of a block at position                 */
 /*           8*floor((s%16)/4) + 4*floor(s/16) + s%4.                         */
 /* The handle keeps non-owning pointers: the weights and caches must outlive  */
-/* it.  Errors: EV_EINVAL, EV_EUNSUPPORTED.                                   */
+/* it.  Errors: EV_EINVAL, EV_EUNSUPPORTED, EV_EHIP.                          */
 int32_t toy_decoder_create(const ev_decoder_config* cfg, const ev_decoder_weights* w,
                            uint16_t* k_cache, uint16_t* v_cache, int32_t max_ctx,
                            ev_decoder** out);
+/* Synchronises the device if the handle holds captured steps, then frees.   */
 void toy_decoder_destroy(ev_decoder* m);
 
 /* Workspace of verify_step: a function of the configuration and max_ctx.     */
@@ -295,9 +297,20 @@ size_t verify_step_workspace(const ev_decoder* m);
 /* starts at pos0 + n_commit with sampled[n_commit-1].  R = 1 is serial       */
 /* decoding.  Limits: 1 <= R <= 16.  Errors: EV_EINVAL, EV_EUNSUPPORTED,      */
 /* EV_EWORKSPACE, EV_EHIP; nothing is launched on a validation error.         */
+/* Launches: a first kernel takes tokens and pos0 (copied into ws); the rest  */
+/* of the step reads them from ws.  With graphs on (the default), logits NULL */
+/* and the timing hook off, that rest is captured as a HIP graph on the first */
+/* call with a given (R, ws, sampled, n_commit, sampling) and replayed by     */
+/* later calls with the same five (the handle keeps the 16 latest; dropping   */
+/* one synchronises the device), so a round costs two submissions.  Results   */
+/* are identical either way.  Calls on one handle must not overlap.           */
 int32_t verify_step(ev_decoder* m, const int32_t* tokens, int32_t R, int64_t pos0,
                     ev_sampling sampling, int32_t* sampled, int32_t* n_commit, float* logits,
                     void* ws, size_t ws_bytes, void* stream);
+
+/* Graph replay of verify_step on (enable != 0, the default) or off (every    */
+/* step launched kernel by kernel).  Errors: EV_EINVAL (NULL handle).         */
+int32_t toy_decoder_set_graphs(ev_decoder* m, int32_t enable);
 
 /* ------------------------------------------------------------------------- */
 /* Measurement hook for the W4 verify kernel (every entry point that streams  */

@@ -132,6 +132,37 @@ def test_tiny_drafted_equals_serial_and_matches_oracle(tiny, sampling):
         assert np.array_equal(host(m2.v_cache_standard())[:, :, :L], vc_s[:, :, :L])
 
 
+def test_tiny_graph_replay_equals_eager(tiny):
+    """Every round of a drafted decode (R = 1, 4, 16 and the shorter last
+    rounds) replayed from captured steps, with the eager first kernel, host
+    read-backs and drafting between replays, gives the same sampled tokens,
+    commit counts and caches as the same rounds launched kernel by kernel."""
+    d, cfg = tiny, tiny["cfg"]
+    pos0, n, V = cfg["prefill"], 30, cfg["vocab"]
+    ref = decode(_gpu_round(_fresh(d), SAMPLED), d["first_token"], pos0, n, 1, lambda p, c: [])[0]
+    for R, drafter in ((1, lambda p, c: []), (4, syn.transcript_drafter(ref, pos0 + 1, 0.65, 5, V)),
+                       (16, syn.random_drafter(9, V))):
+        runs = []
+        for graphs in (False, True):
+            m = _fresh(d)
+            m.set_graphs(graphs)
+            log = []
+
+            def fn(tokens, p0):
+                s, c = m.verify_step(torch.tensor(tokens, dtype=torch.int32, device="cuda"), p0, *SAMPLED)
+                out = (host(s).tolist(), int(host(c)[0]))
+                log.append((p0, tuple(tokens), tuple(out[0]), out[1]))
+                return out
+
+            got, _ = decode(fn, d["first_token"], pos0, n, R, drafter)
+            runs.append((got, log, host(m.k_cache), host(m.v_cache)))
+            del m
+        (g0, l0, k0, v0), (g1, l1, k1, v1) = runs
+        assert l1 == l0, R  # every round: position, tokens, sampled, commit count
+        assert g1 == g0 == ref
+        assert np.array_equal(k1, k0) and np.array_equal(v1, v0)
+
+
 def test_tiny_decodes_to_the_last_slot(tiny):
     d, cfg = tiny, tiny["cfg"]
     pos0 = cfg["prefill"]
