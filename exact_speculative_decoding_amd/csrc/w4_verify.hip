@@ -449,9 +449,19 @@ __global__ __launch_bounds__(64) void splitk_reduce_kernel(const float* __restri
     const bool vec = (N & 3) == 0 && (reinterpret_cast<uintptr_t>(y) & 15) == 0 &&
                      (reinterpret_cast<uintptr_t>(part) & 15) == 0;
     if (vec) {
+        // every split's load of a batch is issued before the batch's additions
+        // (one memory round trip per 32 splits), which still run in ascending s
+        constexpr int kB = 32;
         f32x4 acc = *reinterpret_cast<const f32x4*>(part + o);
-#pragma unroll 8
-        for (int s = 1; s < S; ++s) acc += *reinterpret_cast<const f32x4*>(part + s * stride + o);
+        for (int s0 = 1; s0 < S; s0 += kB) {
+            f32x4 v[kB];
+#pragma unroll
+            for (int u = 0; u < kB; ++u)
+                if (s0 + u < S) v[u] = *reinterpret_cast<const f32x4*>(part + (size_t)(s0 + u) * stride + o);
+#pragma unroll
+            for (int u = 0; u < kB; ++u)
+                if (s0 + u < S) acc += v[u];
+        }
         *reinterpret_cast<f32x4*>(y + o) = acc;
     } else {
         for (int i = 0; i < 4 && n4 + i < N; ++i) {
@@ -485,15 +495,35 @@ __global__ __launch_bounds__(64) void silu_reduce_kernel(const float* __restrict
     }
     const size_t stride = (size_t)16 * I;
     const size_t o = (size_t)r * I + 8 * m;
-    f32x4 g0 = *reinterpret_cast<const f32x4*>(pg + o), g1 = *reinterpret_cast<const f32x4*>(pg + o + 4);
-    f32x4 u0 = *reinterpret_cast<const f32x4*>(pu + o), u1 = *reinterpret_cast<const f32x4*>(pu + o + 4);
-#pragma unroll 4
-    for (int sp = 1; sp < S; ++sp) {
-        const size_t so = sp * stride + o;
-        g0 += *reinterpret_cast<const f32x4*>(pg + so);
-        g1 += *reinterpret_cast<const f32x4*>(pg + so + 4);
-        u0 += *reinterpret_cast<const f32x4*>(pu + so);
-        u1 += *reinterpret_cast<const f32x4*>(pu + so + 4);
+    // all loads of a batch of 8 splits are issued before its additions, which
+    // run in ascending split order
+    f32x4 g0 = {0.f, 0.f, 0.f, 0.f}, g1 = g0, u0 = g0, u1 = g0;
+    for (int s0 = 0; s0 < S; s0 += 8) {
+        f32x4 v[8][4];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            if (s0 + u < S) {
+                const size_t so = (size_t)(s0 + u) * stride + o;
+                v[u][0] = *reinterpret_cast<const f32x4*>(pg + so);
+                v[u][1] = *reinterpret_cast<const f32x4*>(pg + so + 4);
+                v[u][2] = *reinterpret_cast<const f32x4*>(pu + so);
+                v[u][3] = *reinterpret_cast<const f32x4*>(pu + so + 4);
+            }
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            if (s0 + u < S) {
+                if (s0 + u == 0) {
+                    g0 = v[u][0];
+                    g1 = v[u][1];
+                    u0 = v[u][2];
+                    u1 = v[u][3];
+                } else {
+                    g0 += v[u][0];
+                    g1 += v[u][1];
+                    u0 += v[u][2];
+                    u1 += v[u][3];
+                }
+            }
     }
     uint16_t hv[8];
 #pragma unroll
