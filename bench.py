@@ -82,17 +82,69 @@ def load_traffic():
     return t.get("bytes_per_launch")
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(d, R):
     """The oracle as it stands on this host: one whole R-row pass of the MLP
-    slice (rows one at a time, OpenMP over output columns), in the same unit."""
+    slice (rows one at a time, OpenMP over output columns), in the same unit;
+    then the same pass on one thread."""
     import oracle
+    nb = mlp_bytes(R, d["H"], d["I"], d["G"])
+    threads = int(oracle.num_threads())
     t0 = time.perf_counter()
     oracle.mlp(d["x"][:R], d["gate"], d["up"], d["down"], d["G"])
     dt = time.perf_counter() - t0
-    gbs = mlp_bytes(R, d["H"], d["I"], d["G"]) / dt / 1e9
-    return {"value": round(gbs, 4), "unit": "GB/s", "cores": int(oracle.num_threads()),
+    oracle.set_num_threads(1)
+    try:
+        t1 = time.perf_counter()
+        oracle.mlp(d["x"][:R], d["gate"], d["up"], d["down"], d["G"])
+        dt1 = time.perf_counter() - t1
+    finally:
+        oracle.set_num_threads(threads)
+    return {"value": round(nb / dt / 1e9, 4), "unit": "GB/s", "cores": threads,
             "kind": "oracle", "seconds": round(dt, 2),
-            "sample": f"one {R}-row pass of the MLP slice (all three W4 linears and the glue)"}
+            "sample": f"one {R}-row pass of the MLP slice (all three W4 linears and the glue)",
+            "one_thread": {"value": round(nb / dt1 / 1e9, 4), "seconds": round(dt1, 2),
+                           "ms_per_row": round(1e3 * dt1 / R, 1)},
+            "cpu_model": cpu_model()}
+
+
+def stream_ceiling(ev, dev, stream, reps=20):
+    """The practical ceiling next to the nominal peak: a plain streaming read
+    (the library's read probe) of the two W4 launch sizes of the MLP slice,
+    timed like the W4 launches.  Launches rotate over disjoint regions of a
+    1 GiB buffer, so the 256 MB MALL holds none of them."""
+    import torch
+    buf = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    gbs = {}
+    for nb in (50405376, 100810752):  # down; gate + up
+        nreg = buf.numel() // nb
+        region = lambda i: buf[(i % nreg) * nb:(i % nreg + 1) * nb]
+        for i in range(3):
+            ev.read_probe(region(i), sink, stream)
+        torch.cuda.synchronize()
+        ev.w4_timing_read()
+        ev.w4_timing(True)
+        for i in range(reps):
+            ev.read_probe(region(i), sink, stream)
+        torch.cuda.synchronize()
+        ev.w4_timing(False)
+        n, ms, by = ev.w4_timing_read()
+        gbs[f"{nb / 1e6:.1f} MB"] = round(by / (ms * 1e-3) / 1e9, 1)
+    del buf
+    torch.cuda.empty_cache()
+    return {"kernel": "plain grid-stride read (1024 x 256 threads, 16-byte loads)", "unit": "GB/s",
+            "GB_s": gbs, "frac_of_peak": {k: round(v / HBM_PEAK_GBS, 3) for k, v in gbs.items()}}
 
 
 def _event_time(stream, fn, steps, warmup):
@@ -306,11 +358,25 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / steps
 
+    def step_percentiles(R, steps):
+        """p10 / p50 / p90 of single steps, each between two events (which add
+        their own overhead; the headline uses one bracket around all steps)."""
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        evs[0].record(stream)
+        for i in range(steps):
+            step(i, R)
+            evs[i + 1].record(stream)
+        torch.cuda.synchronize()
+        t = sorted(1e3 * evs[i].elapsed_time(evs[i + 1]) for i in range(steps))
+        pick = lambda f: round(t[min(steps - 1, int(f * (steps - 1) + 0.5))], 2)
+        return {"p10": pick(0.1), "p50": pick(0.5), "p90": pick(0.9)}
+
     R = args.R
     torch.cuda.set_stream(stream)
     ms = timed(R, args.steps, args.warmup)
     gbs = mlp_bytes(R, H, I, G) / (ms * 1e-3) / 1e9
     print(f"# R={R}: {ms * 1e3:.1f} us/step, {gbs:.0f} GB/s", file=sys.stderr, flush=True)
+    pct = step_percentiles(R, args.steps)
 
     per_r = {}
     if not args.no_sweep:
@@ -351,9 +417,13 @@ def main():
                    "weight_bytes_per_copy": int(mlp_bytes(0, H, I, G))},
         "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "lanes_per_s": round(R / (ms * 1e-3), 1),
+        "step_us_percentiles": pct,
         "per_R": per_r,
         "roofline": roofline,
     }
+    if not args.no_legs:
+        out["stream_ceiling"] = stream_ceiling(ev, dev, stream)
+        print("# stream ceiling done", file=sys.stderr, flush=True)
     if not args.no_legs:
         legs = {}
         legs["lm_head_sampler"] = leg_lm_head(ev, syn, to_dev, stream, args.steps)

@@ -77,6 +77,7 @@ _SIGS = {
     "toy_decoder_destroy": (None, [_vp]),
     "verify_step_workspace": (_sz, [_vp]),
     "verify_step": (_i32, [_vp, _vp, _i32, _i64, Sampling, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "ev_read_probe": (_i32, [_vp, _sz, _vp, _vp]),
     "toy_decoder_set_graphs": (_i32, [_vp, _i32]),
     "ev_w4_timing": (_i32, [_i32]),
     "ev_w4_timing_read": (_i32, [C.POINTER(_i64), C.POINTER(C.c_double), C.POINTER(C.c_double)]),
@@ -405,6 +406,13 @@ def load_decoder(cfg, w, kc, vc, device="cuda"):
 def w4_timing(enable):
     """Turn the per-launch event timing of the W4 kernel on or off."""
     _check(lib().ev_w4_timing(1 if enable else 0))
+
+
+def read_probe(buf, sink, stream=None):
+    """One plain streaming read of the uint8 device tensor buf (the practical
+    read ceiling; timed by the W4 timing hook when it is on)."""
+    _check(lib().ev_read_probe(_dev(buf, "buf", _U8), buf.numel(), _dev(sink, "sink", (torch.int32,)),
+                               _stream(stream)))
 
 
 def w4_timing_read():

@@ -328,6 +328,16 @@ int32_t toy_decoder_set_graphs(ev_decoder* m, int32_t enable);
 int32_t ev_w4_timing(int32_t enable);
 int32_t ev_w4_timing_read(int64_t* launches, double* total_ms, double* total_bytes);
 
+/* Measurement aid: the practical ceiling of a streaming read on this part,  */
+/* next to the nominal HBM peak.  Reads `bytes` at buf (device, 16-byte       */
+/* aligned, a multiple of 16) once with a plain grid-stride kernel (1024      */
+/* workgroups of 256 threads, 16-byte loads, the whole grid sweeping the      */
+/* buffer in 1 KB wave blocks) and writes nothing (sink, device, 4 bytes, is  */
+/* written only if the xor of the data equals a constant).  While the timing  */
+/* hook is on, the launch is recorded like a W4 launch with `bytes` as its    */
+/* bytes.  Errors: EV_EINVAL, EV_EHIP.                                        */
+int32_t ev_read_probe(const void* buf, size_t bytes, uint32_t* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -57,6 +57,8 @@ def _declare(L):
     L.ov_gumbel.argtypes = [C.c_uint64]
     L.ov_gumbel.restype = f64
     L.ov_num_threads.restype = C.c_int
+    L.ov_set_num_threads.argtypes = [C.c_int]
+    L.ov_set_num_threads.restype = None
     L.ov_silu.argtypes = [f64]
     L.ov_silu.restype = f64
     L.ov_w4_linear.argtypes = [_p(u16), i32, i32, _p(u8), _p(u16), _p(u16), i32, i32, _p(f64)]
@@ -149,6 +151,11 @@ def gumbel(h):
 
 def num_threads():
     return int(lib().ov_num_threads())
+
+
+def set_num_threads(n):
+    """OpenMP threads of the column loops (timing only: values do not change)."""
+    lib().ov_set_num_threads(int(n))
 
 
 def silu(v):

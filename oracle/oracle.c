@@ -462,10 +462,13 @@ void ov_sample_many(const float* l, int V, int n, const int64_t* pos,
     }
 }
 
-/* Threads OpenMP would use for the column loops (reported with timings). */
+/* Threads OpenMP would use for the column loops (reported with timings), and
+ * a way to set them (timings with one thread); neither changes any value. */
 #ifdef _OPENMP
 #include <omp.h>
 int ov_num_threads(void) { return omp_get_max_threads(); }
+void ov_set_num_threads(int n) { omp_set_num_threads(n > 0 ? n : 1); }
 #else
 int ov_num_threads(void) { return 1; }
+void ov_set_num_threads(int n) { (void)n; }
 #endif
