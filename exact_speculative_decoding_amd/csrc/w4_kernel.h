@@ -62,6 +62,55 @@ inline W4Plan plan_w4(int N, int K, int nmat) {
     return p;
 }
 
+// Balanced (stream-K) plan of a plain launch.  The work of the launch is a
+// list of units, one superchunk (kSC chunks of 128 k) of one column block
+// (kBlockCols columns: the kWaves * kNT tiles of a workgroup) of one matrix,
+// ordered by matrix, block, superchunk; workgroup w of nwg takes units
+// [w U / nwg, (w + 1) U / nwg).  nwg is three workgroups of four waves per
+// CU (768 on 256 CUs), or U when there are fewer units: about twelve
+// streaming waves per CU give this part its best streaming rate (measured:
+// five per CU, the register-limited maximum, is 20 % slower, two 7 %).
+// Workgroup w writes one partial segment [16][kBlockCols] per block its run
+// touches, at slot w * segmax + (block - first block of the run).  All of it
+// follows from (N, K, nmat), never from R.
+constexpr int kBlockCols = kWaves * kNT * 16;
+#ifndef EV_W4_SK_CUS
+#define EV_W4_SK_CUS 256
+#endif
+#ifndef EV_W4_SK_PER_CU
+#define EV_W4_SK_PER_CU 3
+#endif
+constexpr int kSkWGs = EV_W4_SK_CUS * EV_W4_SK_PER_CU;
+#ifndef EV_W4_SK
+#define EV_W4_SK 1
+#endif
+struct SkPlan {
+    int nsc;     // superchunks per column block
+    int ncgb;    // column blocks per matrix
+    int nwg;     // workgroups
+    int segmax;  // partial segments per workgroup, at most
+    int units;   // nmat * ncgb * nsc
+    bool ok;     // the unit arithmetic fits 32 bits (units * nwg < 2^31)
+};
+inline SkPlan plan_w4_sk(int N, int K, int nmat) {
+    SkPlan p;
+    p.nsc = (w4_chunks(K) + kSC - 1) / kSC;
+    p.ncgb = (w4_tiles(N) + kWaves * kNT - 1) / (kWaves * kNT);
+    const long U = (long)nmat * p.ncgb * p.nsc;
+    const long nwg = U < kSkWGs ? U : kSkWGs;
+    p.ok = U * nwg < (1l << 31);
+    p.units = (int)U;
+    p.nwg = (int)nwg;
+    const long L = (U + nwg - 1) / nwg;  // longest run
+    p.segmax = (int)((L + p.nsc - 2) / p.nsc + 1);
+    return p;
+}
+// A plain launch runs balanced when its split plan would need partial rows
+// anyway (S > 1); a launch whose columns alone fill the chip (S == 1, as the
+// LM head) writes its outputs directly and needs no second kernel.
+inline bool use_sk(const SkPlan& q, const W4Plan& p) { return EV_W4_SK && q.ok && p.S > 1; }
+inline size_t sk_part_bytes(const SkPlan& p) { return (size_t)p.nwg * p.segmax * 16 * kBlockCols * sizeof(float); }
+
 struct W4Args {
     const uint8_t* w[2];  // packed weights; the workgroup's matrix index picks one
     float* out[2];        // split s writes rows at out + s * split_stride
@@ -93,6 +142,9 @@ struct W4Args {
     uint16_t* h;
     uint16_t* h_copy;
     long hgstride;
+    // Balanced launch only: partial segments [nwg][segmax][16][kBlockCols].
+    float* sk_part;
+    int sk_units, sk_nwg, sk_nsc, sk_segmax;
     // q|k|v launch with rotation only (N = (NH + 2 NKV) * 128 columns, heads
     // q..., k..., v...): row r sits at position positions[kPos0Slot] + r.
     struct {
@@ -156,6 +208,17 @@ int32_t launch_splitk_reduce(const float* part, int S, int N, int R, float* y, h
 int32_t launch_silu_reduce(const float* pg, const float* pu, int S, int I, int R, uint16_t* h,
                            uint16_t* h_copy, int ngroups, const int* gcount, const int* gcnt,
                            long gstride_p, long gstride_h, hipStream_t st);
+
+// Balanced launch of nmat (1 or 2) matrices (args.sk_part set, plan from
+// plan_w4_sk(N, K, nmat)); then launch_sk_reduce.
+int32_t launch_w4_sk(W4Args args, int nmat, const SkPlan& q, int K, int G, hipStream_t st);
+
+// After a balanced launch: nmat == 1: y[r][n] = the sum of the segments of
+// column n's block, in ascending workgroup order, for r < R (y [R][N] fp32);
+// nmat == 2 (gate, up): h[r][k] = bf16_rne(silu(g) * u) of the two sums (h and
+// h_copy [R][N] bf16, h_copy may be NULL).
+int32_t launch_sk_reduce(const float* part, const SkPlan& q, int nmat, int N, int R, float* y, uint16_t* h,
+                         uint16_t* h_copy, hipStream_t st);
 
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 

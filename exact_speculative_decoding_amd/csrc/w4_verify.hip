@@ -423,8 +423,232 @@ __global__ __launch_bounds__(kThreads) void w4_verify_kernel(W4Args a) {
     }
 }
 
-// Halved-mode launches (paired gate/up, q|k|v with rotation): workgroups of
-// two halves (see w4_block).
+// Balanced (stream-K) W4 pass.  Workgroup w runs the units [w U / nwg,
+// (w + 1) U / nwg) of the launch's unit list (matrix, column block,
+// superchunk), so every workgroup streams the same weight bytes to within one
+// superchunk and, with nwg equal to the resident capacity of the chip, every
+// CU holds the same number of workgroups: no CU is left with an extra
+// workgroup to finish after the others.  The walk keeps the pipeline of the
+// split pass across unit and block boundaries (the ring of weight chunks and
+// the next superchunk's activations stay in flight); when the next unit starts
+// another block, the workgroup writes its accumulators as one partial segment
+// and starts again from zero.  The segments of a block are added in ascending
+// workgroup order by sk_reduce_kernel.
+template <int G>
+__device__ __forceinline__ void w4_sk_block(const W4Args& a, int w, uint8_t (*xlds)[kSlab]) {
+    constexpr int GPC = kKC / G;
+    constexpr int SBW = GPC;
+    constexpr uint32_t CB = 1024 + 64 * GPC;
+    static_assert(kSC % kPD == 0, "ring depth must divide the superchunk");
+    static_assert(EV_W4_CHUNK_MAJOR, "the balanced walk steps chunk-major tiles");
+
+    const int U = a.sk_units, nwg = a.sk_nwg, nsc = a.sk_nsc;
+    const int u0 = (int)((unsigned)w * (unsigned)U / (unsigned)nwg);
+    const int u1 = (int)((unsigned)(w + 1) * (unsigned)U / (unsigned)nwg);
+    if (u0 >= u1) return;  // whole workgroup (nwg <= U keeps every run non-empty)
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int ln = lane & 15, j = lane >> 4;
+    const int rows = a.R;
+
+    constexpr int kXL = 16 * kSC;
+    constexpr int kXR = kThreads / kXL;
+    constexpr int kXP = 16 / kXR;
+    static_assert(kXR * kXP == 16, "the workgroup's passes must cover the 16 rows");
+    const int xr0 = tid / kXL, col = tid % kXL;
+    const uint32_t wbytes = __builtin_amdgcn_readfirstlane(a.wbytes);
+    const rsrc_t rw0 = make_rsrc(uniform_ptr(a.w[0]), wbytes);
+    const rsrc_t rw1 = make_rsrc(uniform_ptr(a.w[1]), wbytes);
+    const rsrc_t rx = make_rsrc(uniform_ptr(a.x), __builtin_amdgcn_readfirstlane(a.xbytes));
+    const uint32_t cstride = (uint32_t)a.tiles * CB;
+    const uint32_t vq = 16u * lane;
+    const uint32_t vsb = 1024u + 4u * GPC * ln;
+    const uint32_t dm = a.dmask;
+    uint32_t doff;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(doff) : "s"(a.doff));
+
+    // A unit's place: superchunk sc of column block cb of matrix m.
+    struct Unit {
+        int sc, cb, m;
+    };
+    auto next = [&](Unit v) {
+        if (++v.sc == nsc) {
+            v.sc = 0;
+            if (++v.cb == a.ncgb) {
+                v.cb = 0;
+                ++v.m;
+            }
+        }
+        return v;
+    };
+    Unit cur;
+    {
+        const int blk = u0 / nsc;
+        cur.sc = u0 - blk * nsc;
+        cur.m = blk / a.ncgb;
+        cur.cb = blk - cur.m * a.ncgb;
+    }
+
+    // activations of superchunk sc (zeros when !live, for rows >= R, k >= K)
+    const int xc = col >> 4, xst = (col >> 2) & 3, xj = col & 3;
+    u32x4 xin[kXP];
+    auto xload = [&](bool live, int sc) {
+        const int k = sc * (kSC * kKC) + 8 * col;
+#pragma unroll
+        for (int m = 0; m < kXP; ++m) {
+            const int r = xr0 + kXR * m;
+            const bool ok = live && r < rows && k < a.K;
+            xin[m] = bload128(rx, ok ? (uint32_t)(r * a.K + k) * 2u : kOOB, 0u);
+        }
+    };
+    auto xstore = [&](int buf) {
+#pragma unroll
+        for (int m = 0; m < kXP; ++m) {
+            const int r = xr0 + kXR * m;
+            const u32x4 v = xin[m];
+            u32x4 o;
+            o[0] = __builtin_amdgcn_perm(v[2], v[0], 0x05040100u);
+            o[1] = __builtin_amdgcn_perm(v[2], v[0], 0x07060302u);
+            o[2] = __builtin_amdgcn_perm(v[3], v[1], 0x05040100u);
+            o[3] = __builtin_amdgcn_perm(v[3], v[1], 0x07060302u);
+            *reinterpret_cast<u32x4*>(&xlds[buf][(size_t)((xc * 4 + xst) * 64 + r + 16 * xj) * 16]) = o;
+        }
+    };
+
+    // chunk p of unit v for the wave's kNT tiles of the unit's block, into
+    // ring slot `slot` (zeros when !live, past the last chunk or tile)
+    u32x4 qr[kPD][kNT];
+    uint32_t sbr[kPD][kNT][SBW];
+    auto fetch = [&](bool live, Unit v, int p, int slot) {
+        const int c = v.sc * kSC + p;
+        const rsrc_t r = v.m ? rw1 : rw0;
+#pragma unroll
+        for (int t = 0; t < kNT; ++t) {
+            const int tile = (v.cb * kWaves + wave) * kNT + t;
+            const bool ok = live && c < a.nchunks && tile < a.tiles;
+            const uint32_t so = ok ? (uint32_t)tile * CB + (uint32_t)c * cstride : 0u;
+            qr[slot][t] = bload128(r, ok ? vq : kOOB, so);
+            if (GPC == 2) {
+                const u32x2 x2 = bload64(r, ok ? vsb : kOOB, so);
+                sbr[slot][t][0] = x2[0];
+                sbr[slot][t][GPC - 1] = x2[1];
+            } else {
+                const u32x4 x4 = bload128(r, ok ? vsb : kOOB, so);
+#pragma unroll
+                for (int g = 0; g < SBW; ++g) sbr[slot][t][g] = x4[g & 3];
+            }
+        }
+    };
+
+    const u32x4 ones = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
+    f32x4 y[kNT];
+#pragma unroll
+    for (int t = 0; t < kNT; ++t) y[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // one chunk, exactly as in the split pass
+    auto compute = [&](int slot, const uint8_t* xchunk) {
+        f32x4 acc[kNT], xs = {0.f, 0.f, 0.f, 0.f};
+        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+            const u32x4 xa = *reinterpret_cast<const u32x4*>(xchunk + (size_t)(st * 64 + lane) * 16);
+            const bf16x8 A = __builtin_bit_cast(bf16x8, xa);
+            const bool first = (G == 32) || ((st & 1) == 0);
+            xs = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, __builtin_bit_cast(bf16x8, ones),
+                                                        first ? zero : xs, 0, 0, 0);
+#pragma unroll
+            for (int t = 0; t < kNT; ++t) {
+                const bf16x8 B = __builtin_bit_cast(bf16x8, decode_nibbles(qr[slot][t][st], dm, doff));
+                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, first ? zero : acc[t], 0, 0, 0);
+            }
+            const bool last = (G == 32) || ((st & 1) == 1);
+            if (last) {
+                const int gc = (32 * st) / G;
+#pragma unroll
+                for (int t = 0; t < kNT; ++t) {
+                    const uint32_t sb = sbr[slot][t][gc];
+                    const float sv = half_lo(sb), bv = half_hi(sb);
+                    const float bp = fmaf(-kDecodeOffset, sv, bv);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        y[t][i] = fmaf(sv, acc[t][i], y[t][i]);
+                        y[t][i] = fmaf(bp, xs[i], y[t][i]);
+                    }
+                }
+            }
+        }
+    };
+    // segment s of the run: rows r = 4j + i of the block's columns
+    // (wave, tile) * 16 + ln; the accumulators start again from zero
+    auto flush = [&](int s) {
+        float* o = a.sk_part + ((size_t)w * a.sk_segmax + s) * 16 * kBlockCols;
+#pragma unroll
+        for (int t = 0; t < kNT; ++t) {
+            const int cl = (wave * kNT + t) * 16 + ln;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 4 * j + i;
+                if (r < rows) o[(size_t)r * kBlockCols + cl] = y[t][i];
+            }
+            y[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+    };
+
+    // Prologue: unit u0's activations into slab 0, its first kPD chunks of
+    // weights in flight, unit u0 + 1's activations in registers.
+    Unit nxt = next(cur);
+    xload(true, cur.sc);
+    xstore(0);
+#pragma unroll
+    for (int p = 0; p < kPD; ++p) {
+        __builtin_amdgcn_sched_barrier(0);
+        fetch(true, cur, p, p);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    xload(u0 + 1 < u1, nxt.sc);
+    __syncthreads();
+
+    // One unit per trip: kSC chunks of compute on slab `buf`, each refilling
+    // its ring slot with the chunk kPD ahead (in this unit or the next); a
+    // segment ends where the next unit starts a block (or the run ends); then
+    // the next unit's activations go to the other slab, the one after is
+    // loaded, and the workgroup syncs.
+    int buf = 0, seg = 0;
+    for (int u = u0; u < u1; ++u) {
+        const bool live1 = u + 1 < u1;
+#pragma unroll
+        for (int p = 0; p < kSC; ++p) {
+            __builtin_amdgcn_sched_barrier(0);
+            compute(p % kPD, &xlds[buf][(size_t)p * kXChunkBytes]);
+            __builtin_amdgcn_sched_barrier(0);
+            if (p + kPD < kSC)
+                fetch(true, cur, p + kPD, p % kPD);
+            else
+                fetch(live1, nxt, p + kPD - kSC, p % kPD);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (!live1 || nxt.sc == 0) flush(seg++);
+        const Unit nn = next(nxt);
+        xstore(buf ^ 1);
+        xload(u + 2 < u1, nn.sc);
+        __syncthreads();
+        buf ^= 1;
+        cur = nxt;
+        nxt = nn;
+    }
+}
+
+template <int G>
+__global__ __launch_bounds__(kThreads) void w4_sk_kernel(W4Args a) {
+    __shared__ __align__(16) uint8_t xlds[2][kSlab];
+    if (a.tstamp && threadIdx.x == 0) a.tstamp[2 * blockIdx.x] = wall_clock64();
+    w4_sk_block<G>(a, blockIdx.x, xlds);
+    if (a.tstamp) {
+        __syncthreads();
+        if (threadIdx.x == 0) a.tstamp[2 * blockIdx.x + 1] = wall_clock64();
+    }
+}
+
 template <int G, int MODE>
 __global__ __launch_bounds__(2 * kThreads) void w4_pair_kernel(W4Args a) {
     __shared__ __align__(16) uint8_t xlds[4][kSlab];
@@ -539,6 +763,117 @@ __global__ __launch_bounds__(64) void silu_reduce_kernel(const float* __restrict
     if (h_copy) *reinterpret_cast<u32x4*>(h_copy + o) = w;
 }
 
+// Geometry of a balanced launch, as the reduce kernels need it.
+struct SkGeom {
+    int U, nwg, nsc, segmax;
+};
+// The workgroup whose run holds unit u: the largest w with w U / nwg <= u,
+// i.e. ceil((u + 1) nwg / U) - 1 (U * nwg < 2^31).
+__device__ __forceinline__ int sk_owner(int u, const SkGeom& g) {
+    return (int)(((unsigned)(u + 1) * (unsigned)g.nwg + (unsigned)g.U - 1u) / (unsigned)g.U) - 1;
+}
+// The workgroups whose runs touch block b are first(b) .. last(b) (the owners
+// of the block's first and last unit).  Every one after first(b) starts its
+// run inside the block, so the block is its segment 0; in first(b) it is
+// segment b - start(first(b)) / nsc.
+struct SkSpan {
+    int w0, w1;
+    const float* p0;  // first(b)'s segment, row r, column cl
+};
+__device__ __forceinline__ SkSpan sk_span(const float* part, const SkGeom& g, int b, int r, int cl) {
+    SkSpan sp;
+    sp.w0 = sk_owner(b * g.nsc, g);
+    sp.w1 = sk_owner((b + 1) * g.nsc - 1, g);
+    const int s0 = b - (int)((unsigned)sp.w0 * (unsigned)g.U / (unsigned)g.nwg) / g.nsc;
+    sp.p0 = part + (((size_t)sp.w0 * g.segmax + s0) * 16 + r) * kBlockCols + cl;
+    return sp;
+}
+// segment 0 of workgroup w, row r, column cl
+__device__ __forceinline__ const float* sk_seg0(const float* part, const SkGeom& g, int w, int r, int cl) {
+    return part + ((size_t)w * g.segmax * 16 + r) * kBlockCols + cl;
+}
+
+// y[r][n] = the sum of column n's block segments over first(b) .. last(b),
+// ascending, rows r < R (grid y).  One thread per 4 consecutive n; the loads
+// of a batch of 32 workgroups are issued before its additions.
+__global__ __launch_bounds__(64) void sk_reduce_kernel(const float* __restrict__ part, SkGeom g, int N,
+                                                       float* __restrict__ y) {
+    const int n4 = (blockIdx.x * 64 + threadIdx.x) * 4;
+    const int r = blockIdx.y;
+    if (n4 >= N) return;
+    const int b = n4 / kBlockCols, cl = n4 % kBlockCols;
+    const SkSpan sp = sk_span(part, g, b, r, cl);
+    f32x4 acc = *reinterpret_cast<const f32x4*>(sp.p0);
+    constexpr int kB = 32;
+    for (int wb = sp.w0 + 1; wb <= sp.w1; wb += kB) {
+        f32x4 v[kB];
+#pragma unroll
+        for (int i = 0; i < kB; ++i)
+            if (wb + i <= sp.w1) v[i] = *reinterpret_cast<const f32x4*>(sk_seg0(part, g, wb + i, r, cl));
+#pragma unroll
+        for (int i = 0; i < kB; ++i)
+            if (wb + i <= sp.w1) acc += v[i];
+    }
+    float* o = y + (size_t)r * N + n4;
+    if ((N & 3) == 0 && (reinterpret_cast<uintptr_t>(y) & 15) == 0) {
+        *reinterpret_cast<f32x4*>(o) = acc;
+    } else {
+        for (int i = 0; i < 4 && n4 + i < N; ++i) o[i] = acc[i];
+    }
+}
+
+// h[r][k] = bf16_rne(silu(g) * u), g and u the segment sums (ascending
+// workgroups) of column k's block in the gate (blocks 0..ncgb-1) and the up
+// matrix (blocks ncgb..); one thread per 4 consecutive k.  The loads of a
+// batch of 8 workgroups of each matrix are issued together.
+__global__ __launch_bounds__(64) void sk_silu_reduce_kernel(const float* __restrict__ part, SkGeom g, int ncgb,
+                                                            int I, uint16_t* __restrict__ h,
+                                                            uint16_t* __restrict__ h_copy) {
+    const int k4 = (blockIdx.x * 64 + threadIdx.x) * 4;
+    const int r = blockIdx.y;
+    if (k4 >= I) return;
+    const int b = k4 / kBlockCols, cl = k4 % kBlockCols;
+    const SkSpan sg = sk_span(part, g, b, r, cl), su = sk_span(part, g, ncgb + b, r, cl);
+    f32x4 gs = *reinterpret_cast<const f32x4*>(sg.p0), us = *reinterpret_cast<const f32x4*>(su.p0);
+    constexpr int kB = 8;
+    for (int i0 = 1; sg.w0 + i0 <= sg.w1 || su.w0 + i0 <= su.w1; i0 += kB) {
+        f32x4 vg[kB], vu[kB];
+#pragma unroll
+        for (int i = 0; i < kB; ++i) {
+            if (sg.w0 + i0 + i <= sg.w1) vg[i] = *reinterpret_cast<const f32x4*>(sk_seg0(part, g, sg.w0 + i0 + i, r, cl));
+            if (su.w0 + i0 + i <= su.w1) vu[i] = *reinterpret_cast<const f32x4*>(sk_seg0(part, g, su.w0 + i0 + i, r, cl));
+        }
+#pragma unroll
+        for (int i = 0; i < kB; ++i) {
+            if (sg.w0 + i0 + i <= sg.w1) gs += vg[i];
+            if (su.w0 + i0 + i <= su.w1) us += vu[i];
+        }
+    }
+    uint32_t w2[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+        w2[i] = (uint32_t)silu_mul_bf16(gs[2 * i], us[2 * i]) |
+                ((uint32_t)silu_mul_bf16(gs[2 * i + 1], us[2 * i + 1]) << 16);
+    const size_t o = (size_t)r * I + k4;
+    const u32x2 wv = {w2[0], w2[1]};
+    *reinterpret_cast<u32x2*>(h + o) = wv;
+    if (h_copy) *reinterpret_cast<u32x2*>(h_copy + o) = wv;
+}
+
+int32_t launch_sk_reduce(const float* part, const SkPlan& q, int nmat, int N, int R, float* y, uint16_t* h,
+                         uint16_t* h_copy, hipStream_t st) {
+    const SkGeom g{q.units, q.nwg, q.nsc, q.segmax};
+    if (nmat == 1) {
+        dim3 grid((unsigned)((N + 255) / 256), (unsigned)R);
+        hipLaunchKernelGGL(sk_reduce_kernel, grid, dim3(64), 0, st, part, g, N, y);
+    } else {
+        if (N % 32 != 0) return fail(EV_EINVAL, "sk reduce: I=%d is not a multiple of 32", N);
+        dim3 grid((unsigned)((N / 4 + 63) / 64), (unsigned)R);
+        hipLaunchKernelGGL(sk_silu_reduce_kernel, grid, dim3(64), 0, st, part, g, q.ncgb, N, h, h_copy);
+    }
+    return check_hip(hipGetLastError(), "sk reduce launch");
+}
+
 int32_t launch_splitk_reduce(const float* part, int S, int N, int R, float* y, hipStream_t st) {
     dim3 grid((unsigned)((N + 255) / 256), (unsigned)R);
     hipLaunchKernelGGL(splitk_reduce_kernel, grid, dim3(64), 0, st, part, S, N, y);
@@ -624,6 +959,33 @@ int32_t launch_w4(W4Args args, int nmat, const W4Plan& p, int K, int G, hipStrea
     return check_hip(hipGetLastError(), "w4_verify_kernel launch");
 }
 
+int32_t launch_w4_sk(W4Args args, int nmat, const SkPlan& q, int K, int G, hipStream_t st) {
+    if (!q.ok || !args.sk_part || nmat < 1 || nmat > 2 || args.gexp)
+        return fail(EV_EINVAL, "w4 balanced launch: unsupported (N=%d K=%d nmat=%d)", args.N, K, nmat);
+    args.K = K;
+    args.nmat = nmat;
+    args.nchunks = w4_chunks(K);
+    args.tiles = w4_tiles(args.N);
+    args.ncgb = q.ncgb;
+    args.blocks = q.nwg;
+    args.wbytes = (uint32_t)w4_blob_bytes(args.N, K, G);
+    args.xbytes = (uint32_t)((size_t)args.R * K * 2);
+    args.dmask = kDecodeMask;
+    args.doff = kDecodeOr;
+    args.sk_units = q.units;
+    args.sk_nwg = q.nwg;
+    args.sk_nsc = q.nsc;
+    args.sk_segmax = q.segmax;
+    args.tstamp = nullptr;
+    int32_t rc = timing_slots(q.nwg, w4_algo_bytes(nmat, args.R, K, args.N, G), &args.tstamp);
+    if (rc) return rc;
+    if (G == 64)
+        hipLaunchKernelGGL(w4_sk_kernel<64>, dim3(q.nwg), dim3(kThreads), 0, st, args);
+    else
+        hipLaunchKernelGGL(w4_sk_kernel<32>, dim3(q.nwg), dim3(kThreads), 0, st, args);
+    return check_hip(hipGetLastError(), "w4_sk_kernel launch");
+}
+
 // A halved-mode launch: paired gate/up (ncgb = column blocks of kWaves
 // tiles) or q|k|v with rotation (ncgb = heads).
 static int32_t launch_w4_halved(W4Args args, const W4Plan& p, int K, int G, hipStream_t st, int ngroups,
@@ -671,35 +1033,47 @@ int32_t launch_w4_rope(W4Args args, const W4Plan& p, int K, int G, hipStream_t s
     return launch_w4_halved(args, p, K, G, st, 1, true);
 }
 
-// Workspace of verify_linear_w4: split partials [S][16][N] (none if S == 1).
+// Workspace of verify_linear_w4: balanced partial segments, or split partials
+// [S][16][N] (none if S == 1).
 struct LinLayout {
+    bool sk;
+    SkPlan q;
     W4Plan p;
     size_t total;
 };
 static LinLayout lin_layout(int K, int N) {
     LinLayout L;
+    L.q = plan_w4_sk(N, K, 1);
     L.p = plan_w4(N, K, 1);
-    L.total = L.p.S > 1 ? (size_t)L.p.S * 16 * N * sizeof(float) : 0;
+    L.sk = use_sk(L.q, L.p);
+    L.total = L.sk ? sk_part_bytes(L.q) : (L.p.S > 1 ? (size_t)L.p.S * 16 * N * sizeof(float) : 0);
     return L;
 }
 
-// Workspace of the MLP slice: h [16][I] bf16, gate and up partials
-// [S1][16][I] (split launch only), down partials [S2][16][H] (if S2 > 1).
+// Workspace of the MLP slice: h [16][I] bf16, then the gate/up partials
+// (balanced segments of both matrices at off_pg, or split partials [S1][16][I]
+// at off_pg and off_pu; none when paired), then the down partials at off_pd
+// (balanced segments, or [S2][16][H] if S2 > 1).
 struct MlpLayout {
-    bool pair;
+    bool pair, sk1, sk2;
+    SkPlan q1, q2;
     W4Plan p1, p2;
     size_t off_pg, off_pu, off_pd, total;
 };
 static MlpLayout mlp_layout(int H, int I) {
     MlpLayout L;
     L.pair = use_pair(I);
+    L.q1 = plan_w4_sk(I, H, 2);
+    L.q2 = plan_w4_sk(H, I, 1);
     L.p1 = L.pair ? plan_w4_pair(I, H) : plan_w4(I, H, 2);
     L.p2 = plan_w4(H, I, 1);
-    const size_t part1 = L.pair ? 0 : align256((size_t)L.p1.S * 16 * I * sizeof(float));
+    L.sk1 = !L.pair && use_sk(L.q1, L.p1);
+    L.sk2 = use_sk(L.q2, L.p2);
+    const size_t part1 = L.pair || L.sk1 ? 0 : align256((size_t)L.p1.S * 16 * I * sizeof(float));
     L.off_pg = align256((size_t)16 * I * sizeof(uint16_t));
     L.off_pu = L.off_pg + part1;
-    L.off_pd = L.off_pu + part1;
-    L.total = L.off_pd + (L.p2.S > 1 ? (size_t)L.p2.S * 16 * H * sizeof(float) : 0);
+    L.off_pd = L.off_pu + (L.sk1 ? align256(sk_part_bytes(L.q1)) : part1);
+    L.total = L.off_pd + (L.sk2 ? sk_part_bytes(L.q2) : (L.p2.S > 1 ? (size_t)L.p2.S * 16 * H * sizeof(float) : 0));
     return L;
 }
 
@@ -844,6 +1218,11 @@ extern "C" int32_t verify_linear_w4(const uint16_t* x, int32_t R, int32_t K, con
     a.x = x;
     a.R = R;
     a.N = N;
+    if (L.sk) {
+        a.sk_part = part;
+        if ((rc = launch_w4_sk(a, 1, L.q, K, G, st))) return rc;
+        return launch_sk_reduce(part, L.q, 1, N, R, y, nullptr, nullptr, st);
+    }
     a.split_stride = L.p.S > 1 ? (long)16 * N : 0;
     if ((rc = launch_w4(a, 1, L.p, K, G, st))) return rc;
     if (L.p.S > 1 && (rc = launch_splitk_reduce(part, L.p.S, N, R, y, st))) return rc;
@@ -888,6 +1267,10 @@ extern "C" int32_t verify_mlp_w4(const uint16_t* x, int32_t R, int32_t H, int32_
         a.h = h;
         a.h_copy = h_out;
         if ((rc = launch_w4_pair(a, L.p1, H, G, st))) return rc;
+    } else if (L.sk1) {
+        a.sk_part = pg;
+        if ((rc = launch_w4_sk(a, 2, L.q1, H, G, st))) return rc;
+        if ((rc = launch_sk_reduce(pg, L.q1, 2, I, R, nullptr, h, h_out, st))) return rc;
     } else {
         a.out[0] = pg;
         a.out[1] = pu;
@@ -901,6 +1284,11 @@ extern "C" int32_t verify_mlp_w4(const uint16_t* x, int32_t R, int32_t H, int32_
     d.x = h;
     d.R = R;
     d.N = H;
+    if (L.sk2) {
+        d.sk_part = pd;
+        if ((rc = launch_w4_sk(d, 1, L.q2, I, G, st))) return rc;
+        return launch_sk_reduce(pd, L.q2, 1, H, R, y, nullptr, nullptr, st);
+    }
     d.split_stride = L.p2.S > 1 ? (long)16 * H : 0;
     if ((rc = launch_w4(d, 1, L.p2, I, G, st))) return rc;
     if (L.p2.S > 1 && (rc = launch_splitk_reduce(pd, L.p2.S, H, R, y, st))) return rc;

@@ -2,7 +2,7 @@
 
 * exact-integer and one-hot cases: bit-identical to the oracle;
 * random cases at several shapes (ragged N, K with a partial chunk, one and many
-  K-splits, G = 32 and 64): per-row relative error <= 2e-3 (observed ~1e-7);
+  K-splits, balanced runs that cross column blocks, G = 32 and 64): per-row relative error <= 2e-3 (observed ~1e-7);
 * every row of an R-lane call is bit-identical to the same row called alone,
   for every R in 1..16, and two runs give the same bits;
 * the full-size shapes (MLP gate/up 5120->17408, down 17408->5120, LM head
@@ -63,7 +63,9 @@ SHAPES = [  # (K, N, G)
     (192, 130, 64),    # K % 128 == 64
     (2048, 300, 32),   # several chunks
     (5120, 1000, 64),  # several K-splits
-    (4096 + 64, 17, 64),
+    (4096 + 64, 17, 64),  # one column block summed from 17 workgroups
+    (5120, 5000, 64),    # balanced runs of 1-2 superchunks crossing block boundaries
+    (4096, 6200, 32),    # the same with group 32, ragged N
 ]
 
 
@@ -81,7 +83,8 @@ def test_random_parity_with_oracle(K, N, G):
         assert np.all(err <= 1e-5), err
 
 
-@pytest.mark.parametrize("K,N,G", [(256, 512, 64), (320, 40, 32), (5120, 1000, 64), (2048, 300, 32)])
+@pytest.mark.parametrize("K,N,G", [(256, 512, 64), (320, 40, 32), (5120, 1000, 64), (2048, 300, 32),
+                                   (5120, 5000, 64)])
 def test_rows_bit_identical_to_single_row_calls(K, N, G):
     g = np.random.default_rng(5 + K + N)
     w = syn.w4_matrix(g, N, K, G)
