@@ -113,11 +113,14 @@ __global__ __launch_bounds__(kRowThreads) void embed_norm_kernel(const int* __re
     if (tid == 0 && r == 0) positions[kPos0Slot] = pos0;
 }
 
-// x[r] += sum over s ascending of part[s][r] (a linear's split partials);
-// n[r] = bf16(RMSNorm(x[r]) * gain).
-__global__ __launch_bounds__(kRowThreads) void res_norm_kernel(const float* __restrict__ part, int S, int H,
-                                                               float* __restrict__ x, const float* __restrict__ gain,
-                                                               float eps, uint16_t* __restrict__ n) {
+// x[r] += the linear's output row r, summed from its partials: split
+// partials part[s][r] in ascending s (g.nwg == 0), or balanced segments of
+// the column's block in ascending workgroup order; n[r] = bf16(RMSNorm(x[r])
+// * gain).
+__global__ __launch_bounds__(kRowThreads) void res_norm_kernel(const float* __restrict__ part, int S, SkGeom g,
+                                                               int H, float* __restrict__ x,
+                                                               const float* __restrict__ gain, float eps,
+                                                               uint16_t* __restrict__ n) {
     __shared__ float red[kRowThreads / 64];
     const int r = blockIdx.x, tid = threadIdx.x;
     const size_t stride = (size_t)16 * H;
@@ -129,15 +132,31 @@ __global__ __launch_bounds__(kRowThreads) void res_norm_kernel(const float* __re
         xv[j] = f32x4{0.f, 0.f, 0.f, 0.f};
         if (c >= H) continue;
         const size_t o = (size_t)r * H + c;
-        f32x4 lin = *reinterpret_cast<const f32x4*>(part + o);
-        for (int s0 = 1; s0 < S; s0 += 8) {  // 8 splits' loads in flight at a time, added in order
-            f32x4 p[8];
+        f32x4 lin;
+        if (g.nwg > 0) {  // 16 segments' loads in flight at a time, added in order
+            const int b = c / kBlockCols, cl = c % kBlockCols;
+            const SkSpan sp = sk_span(part, g, b, r, cl);
+            lin = *reinterpret_cast<const f32x4*>(sp.p0);
+            for (int wb = sp.w0 + 1; wb <= sp.w1; wb += 16) {
+                f32x4 p[16];
 #pragma unroll
-            for (int u = 0; u < 8; ++u)
-                if (s0 + u < S) p[u] = *reinterpret_cast<const f32x4*>(part + (s0 + u) * stride + o);
+                for (int u = 0; u < 16; ++u)
+                    if (wb + u <= sp.w1) p[u] = *reinterpret_cast<const f32x4*>(sk_seg0(part, g, wb + u, r, cl));
 #pragma unroll
-            for (int u = 0; u < 8; ++u)
-                if (s0 + u < S) lin += p[u];
+                for (int u = 0; u < 16; ++u)
+                    if (wb + u <= sp.w1) lin += p[u];
+            }
+        } else {
+            lin = *reinterpret_cast<const f32x4*>(part + o);
+            for (int s0 = 1; s0 < S; s0 += 8) {  // 8 splits' loads in flight at a time, added in order
+                f32x4 p[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u)
+                    if (s0 + u < S) p[u] = *reinterpret_cast<const f32x4*>(part + (s0 + u) * stride + o);
+#pragma unroll
+                for (int u = 0; u < 8; ++u)
+                    if (s0 + u < S) lin += p[u];
+            }
         }
         const f32x4 v = *reinterpret_cast<const f32x4*>(x + o) + lin;
         *reinterpret_cast<f32x4*>(x + o) = v;
@@ -380,6 +399,8 @@ __global__ __launch_bounds__(kHD) void attn_merge_kernel(const float* __restrict
 // Workspace of a verify step, from the configuration and max_ctx only.
 struct StepLayout {
     W4Plan p_qkv, p_o, p_gu, p_down, p_lm;
+    SkPlan q_o, q_down, q_lm;  // balanced plans, used where use_sk holds
+    bool sk_o, sk_down, sk_lm;
     int chunk, nchunk_max;
     bool gu_pair;
     size_t off_x, off_n, off_o, off_q, off_part, off_pg, off_pu, off_h, off_att, off_logits, off_pos, off_acc,
@@ -437,12 +458,22 @@ static StepLayout step_layout(const ev_decoder_config& c, int NQKV, int DQ, int 
     L.p_gu = L.gu_pair ? plan_w4_pair(I, H) : plan_w4(I, H, 2);
     L.p_down = plan_w4(H, I, 1);
     L.p_lm = plan_w4(V, H, 1);
+    L.q_o = plan_w4_sk(H, DQ, 1);
+    L.q_down = plan_w4_sk(H, I, 1);
+    L.q_lm = plan_w4_sk(V, H, 1);
+    L.sk_o = use_sk(L.q_o, L.p_o);
+    L.sk_down = use_sk(L.q_down, L.p_down);
+    L.sk_lm = use_sk(L.q_lm, L.p_lm);
     // chunk: a multiple of 64 slots with at most kMaxChunks chunks in the cache
     L.chunk = 64 * ((C + 64 * kMaxChunks - 1) / (64 * kMaxChunks));
     L.nchunk_max = (C + L.chunk - 1) / L.chunk;
-    size_t part = (size_t)L.p_o.S * H;
-    part = std::max(part, (size_t)L.p_down.S * H);
-    part = std::max(part, (size_t)L.p_lm.S * V);
+    // floats of the largest linear's partials (split rows or balanced segments)
+    auto part_floats = [](bool sk, const SkPlan& q, const W4Plan& p, int N) {
+        return sk ? sk_part_bytes(q) / sizeof(float) : (size_t)16 * p.S * N;
+    };
+    size_t part = part_floats(L.sk_o, L.q_o, L.p_o, H);
+    part = std::max(part, part_floats(L.sk_down, L.q_down, L.p_down, H));
+    part = std::max(part, part_floats(L.sk_lm, L.q_lm, L.p_lm, V));
     size_t off = 0;
     auto take = [&](size_t bytes) {
         const size_t o = off;
@@ -453,7 +484,7 @@ static StepLayout step_layout(const ev_decoder_config& c, int NQKV, int DQ, int 
     L.off_n = take(sizeof(uint16_t) * 16 * H);
     L.off_o = take(sizeof(uint16_t) * 16 * DQ);
     L.off_q = take(sizeof(float) * 16 * DQ);
-    L.off_part = take(sizeof(float) * 16 * part);
+    L.off_part = take(sizeof(float) * part);
     L.off_pg = take(L.gu_pair ? 0 : sizeof(float) * 16 * (size_t)L.p_gu.S * I);
     L.off_pu = take(L.gu_pair ? 0 : sizeof(float) * 16 * (size_t)L.p_gu.S * I);
     L.off_h = take(sizeof(uint16_t) * 16 * I);
@@ -580,16 +611,23 @@ static int32_t step_body(ev_decoder* m, int R, const ev_sampling& sampling, int3
     const int32_t* toks = reinterpret_cast<const int32_t*>(b + L.off_tok);
     void* sws = b + L.off_sws;
 
-    auto linear = [&](const void* wmat, const uint16_t* xin, int K, int N, const W4Plan& p) {
+    // a linear into the partials at `part`: balanced when sk, else split
+    auto linear = [&](const void* wmat, const uint16_t* xin, int K, int N, const W4Plan& p, const SkPlan& q,
+                      bool sk) {
         W4Args a{};
         a.w[0] = a.w[1] = reinterpret_cast<const uint8_t*>(wmat);
-        a.out[0] = a.out[1] = part;
         a.x = xin;
         a.R = R;
         a.N = N;
+        if (sk) {
+            a.sk_part = part;
+            return launch_w4_sk(a, 1, q, K, G, st);
+        }
+        a.out[0] = a.out[1] = part;
         a.split_stride = (long)16 * N;
         return launch_w4(a, 1, p, K, G, st);
     };
+    const SkGeom no_sk{0, 0, 0, 0};
 
     const int nqt = (R * (NH / NKV) + 15) / 16;
     for (int l = 0; l < c.layers; ++l) {
@@ -617,8 +655,9 @@ static int32_t step_body(ev_decoder* m, int R, const ev_sampling& sampling, int3
         if ((rc = check_hip(hipGetLastError(), "attn_partial launch"))) return rc;
         hipLaunchKernelGGL(attn_merge_kernel, dim3(R, NH), dim3(kHD), 0, st, att, NH, L.chunk, L.nchunk_max, pos, o);
         if ((rc = check_hip(hipGetLastError(), "attn_merge launch"))) return rc;
-        if ((rc = linear(y.w_o, o, m->DQ, H, L.p_o))) return rc;
-        hipLaunchKernelGGL(res_norm_kernel, dim3(R), dim3(kRowThreads), 0, st, part, L.p_o.S, H, x, y.mlp_norm, eps, n);
+        if ((rc = linear(y.w_o, o, m->DQ, H, L.p_o, L.q_o, L.sk_o))) return rc;
+        hipLaunchKernelGGL(res_norm_kernel, dim3(R), dim3(kRowThreads), 0, st, part, L.p_o.S,
+                           L.sk_o ? sk_geom(L.q_o) : no_sk, H, x, y.mlp_norm, eps, n);
         if ((rc = check_hip(hipGetLastError(), "res_norm launch"))) return rc;
         {  // h = SiLU(gate) * up: one paired launch, or gate|up + split sum with SiLU * up
             W4Args a{};
@@ -639,13 +678,18 @@ static int32_t step_body(ev_decoder* m, int R, const ev_sampling& sampling, int3
                     return rc;
             }
         }
-        if ((rc = linear(y.w_down, h, I, H, L.p_down))) return rc;
+        if ((rc = linear(y.w_down, h, I, H, L.p_down, L.q_down, L.sk_down))) return rc;
         const float* next = l + 1 < c.layers ? m->layers[l + 1].attn_norm : m->final_norm;
-        hipLaunchKernelGGL(res_norm_kernel, dim3(R), dim3(kRowThreads), 0, st, part, L.p_down.S, H, x, next, eps, n);
+        hipLaunchKernelGGL(res_norm_kernel, dim3(R), dim3(kRowThreads), 0, st, part, L.p_down.S,
+                           L.sk_down ? sk_geom(L.q_down) : no_sk, H, x, next, eps, n);
         if ((rc = check_hip(hipGetLastError(), "res_norm launch"))) return rc;
     }
-    if ((rc = linear(m->w_lm, n, H, V, L.p_lm))) return rc;
-    if ((rc = launch_splitk_reduce(part, L.p_lm.S, V, R, lg, st))) return rc;
+    if ((rc = linear(m->w_lm, n, H, V, L.p_lm, L.q_lm, L.sk_lm))) return rc;
+    if (L.sk_lm) {
+        if ((rc = launch_sk_reduce(part, L.q_lm, 1, V, R, lg, nullptr, nullptr, st))) return rc;
+    } else if ((rc = launch_splitk_reduce(part, L.p_lm.S, V, R, lg, st))) {
+        return rc;
+    }
     void* sv = reinterpret_cast<void*>(st);
     if ((rc = keyed_sample(lg, R, V, reinterpret_cast<const int64_t*>(pos), sampling, sampled, nullptr, sws,
                            keyed_sample_workspace(V), sv)))

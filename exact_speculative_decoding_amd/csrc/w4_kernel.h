@@ -111,6 +111,37 @@ inline SkPlan plan_w4_sk(int N, int K, int nmat) {
 inline bool use_sk(const SkPlan& q, const W4Plan& p) { return EV_W4_SK && q.ok && p.S > 1; }
 inline size_t sk_part_bytes(const SkPlan& p) { return (size_t)p.nwg * p.segmax * 16 * kBlockCols * sizeof(float); }
 
+// Geometry of a balanced launch, as the kernels that add its segments need it.
+struct SkGeom {
+    int U, nwg, nsc, segmax;
+};
+// The workgroup whose run holds unit u: the largest w with w U / nwg <= u,
+// i.e. ceil((u + 1) nwg / U) - 1 (U * nwg < 2^31).
+__device__ __forceinline__ int sk_owner(int u, const SkGeom& g) {
+    return (int)(((unsigned)(u + 1) * (unsigned)g.nwg + (unsigned)g.U - 1u) / (unsigned)g.U) - 1;
+}
+// The workgroups whose runs touch block b are first(b) .. last(b) (the owners
+// of the block's first and last unit).  Every one after first(b) starts its
+// run inside the block, so the block is its segment 0; in first(b) it is
+// segment b - start(first(b)) / nsc.
+struct SkSpan {
+    int w0, w1;
+    const float* p0;  // first(b)'s segment, row r, column cl
+};
+__device__ __forceinline__ SkSpan sk_span(const float* part, const SkGeom& g, int b, int r, int cl) {
+    SkSpan sp;
+    sp.w0 = sk_owner(b * g.nsc, g);
+    sp.w1 = sk_owner((b + 1) * g.nsc - 1, g);
+    const int s0 = b - (int)((unsigned)sp.w0 * (unsigned)g.U / (unsigned)g.nwg) / g.nsc;
+    sp.p0 = part + (((size_t)sp.w0 * g.segmax + s0) * 16 + r) * kBlockCols + cl;
+    return sp;
+}
+// segment 0 of workgroup w, row r, column cl
+__device__ __forceinline__ const float* sk_seg0(const float* part, const SkGeom& g, int w, int r, int cl) {
+    return part + ((size_t)w * g.segmax * 16 + r) * kBlockCols + cl;
+}
+inline SkGeom sk_geom(const SkPlan& q) { return SkGeom{q.units, q.nwg, q.nsc, q.segmax}; }
+
 struct W4Args {
     const uint8_t* w[2];  // packed weights; the workgroup's matrix index picks one
     float* out[2];        // split s writes rows at out + s * split_stride

@@ -763,36 +763,6 @@ __global__ __launch_bounds__(64) void silu_reduce_kernel(const float* __restrict
     if (h_copy) *reinterpret_cast<u32x4*>(h_copy + o) = w;
 }
 
-// Geometry of a balanced launch, as the reduce kernels need it.
-struct SkGeom {
-    int U, nwg, nsc, segmax;
-};
-// The workgroup whose run holds unit u: the largest w with w U / nwg <= u,
-// i.e. ceil((u + 1) nwg / U) - 1 (U * nwg < 2^31).
-__device__ __forceinline__ int sk_owner(int u, const SkGeom& g) {
-    return (int)(((unsigned)(u + 1) * (unsigned)g.nwg + (unsigned)g.U - 1u) / (unsigned)g.U) - 1;
-}
-// The workgroups whose runs touch block b are first(b) .. last(b) (the owners
-// of the block's first and last unit).  Every one after first(b) starts its
-// run inside the block, so the block is its segment 0; in first(b) it is
-// segment b - start(first(b)) / nsc.
-struct SkSpan {
-    int w0, w1;
-    const float* p0;  // first(b)'s segment, row r, column cl
-};
-__device__ __forceinline__ SkSpan sk_span(const float* part, const SkGeom& g, int b, int r, int cl) {
-    SkSpan sp;
-    sp.w0 = sk_owner(b * g.nsc, g);
-    sp.w1 = sk_owner((b + 1) * g.nsc - 1, g);
-    const int s0 = b - (int)((unsigned)sp.w0 * (unsigned)g.U / (unsigned)g.nwg) / g.nsc;
-    sp.p0 = part + (((size_t)sp.w0 * g.segmax + s0) * 16 + r) * kBlockCols + cl;
-    return sp;
-}
-// segment 0 of workgroup w, row r, column cl
-__device__ __forceinline__ const float* sk_seg0(const float* part, const SkGeom& g, int w, int r, int cl) {
-    return part + ((size_t)w * g.segmax * 16 + r) * kBlockCols + cl;
-}
-
 // y[r][n] = the sum of column n's block segments over first(b) .. last(b),
 // ascending, rows r < R (grid y).  One thread per 4 consecutive n; the loads
 // of a batch of 32 workgroups are issued before its additions.
@@ -862,7 +832,7 @@ __global__ __launch_bounds__(64) void sk_silu_reduce_kernel(const float* __restr
 
 int32_t launch_sk_reduce(const float* part, const SkPlan& q, int nmat, int N, int R, float* y, uint16_t* h,
                          uint16_t* h_copy, hipStream_t st) {
-    const SkGeom g{q.units, q.nwg, q.nsc, q.segmax};
+    const SkGeom g = sk_geom(q);
     if (nmat == 1) {
         dim3 grid((unsigned)((N + 255) / 256), (unsigned)R);
         hipLaunchKernelGGL(sk_reduce_kernel, grid, dim3(64), 0, st, part, g, N, y);
