@@ -16,9 +16,10 @@
 //   * the split plans of gate/up and down follow from (H, I) only.
 //
 // Launches (all on the caller's stream, none depending on R except grids):
-//   moe_route_kernel    1 x 256: routing of all lanes, then per expert its
-//                       lanes in ascending order, the list of touched experts
-//                       in ascending id, and each (lane, rank)'s place;
+//   moe_route_kernel    1 x 1024: routing of all lanes (a wave each), then per
+//                       expert its lanes in ascending order, the list of
+//                       touched experts in ascending id, and each (lane,
+//                       rank)'s place;
 //   w4_pair_kernel      grouped: h = bf16(silu(gate) * up) per expert row, gate
 //                       and up of every touched expert in one paired pass;
 //   w4_verify_kernel    grouped: down of every touched expert;
@@ -42,15 +43,25 @@ struct MoeTables {
     float* w_out;
 };
 
-__global__ __launch_bounds__(256) void moe_route_kernel(const float* __restrict__ rho, int R, int E, int top,
-                                                        MoeTables t) {
+// One workgroup of 16 waves.  Wave r routes lane r; experts are then grouped
+// through a 16-bit mask per expert of the lanes that chose it (a lane picks an
+// expert at most once): its popcount is the group's lane count, the lanes
+// below r give lane r's row in the group, and a ballot scan over the experts
+// numbers the touched ones in ascending id.
+constexpr int kRouteThreads = 1024;
+__global__ __launch_bounds__(kRouteThreads) void moe_route_kernel(const float* __restrict__ rho, int R, int E,
+                                                                  int top, MoeTables t) {
     __shared__ int sids[16][kMoeMaxTop];
-    __shared__ int scnt[kMoeMaxE];
+    __shared__ unsigned smask[kMoeMaxE];
     __shared__ int sgid[kMoeMaxE];
+    __shared__ int swave[kMoeMaxE / 64];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    if (tid < E) smask[tid] = 0u;
+    __syncthreads();
 
-    // one wave per lane r: keys of its E logits, `top` rounds of a wave max
-    for (int r = wave; r < R; r += 4) {
+    // wave r: keys of lane r's E logits, `top` rounds of a wave max
+    if (wave < R) {
+        const int r = wave;
         unsigned long long key[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -88,6 +99,7 @@ __global__ __launch_bounds__(256) void moe_route_kernel(const float* __restrict_
                 if (j < top) {
                     const float wj = ev[j] / sum;
                     sids[r][j] = isel[j];
+                    atomicOr(&smask[isel[j]], 1u << r);
                     t.ids[r * kMoeMaxTop + j] = isel[j];
                     t.w[r * kMoeMaxTop + j] = wj;
                     if (t.ids_out) t.ids_out[r * top + j] = isel[j];
@@ -98,33 +110,34 @@ __global__ __launch_bounds__(256) void moe_route_kernel(const float* __restrict_
     }
     __syncthreads();
 
-    // thread e: how many lanes chose expert e (at most one rank per lane)
-    int cnt = 0;
+    // thread e: touched or not; the touched experts' group ids in ascending e
+    const unsigned msk = tid < E ? smask[tid] : 0u;
+    const bool touched = msk != 0u;
+    const unsigned long long bal = __ballot(touched);
+    if (tid < E && lane == 0) swave[wave] = __popcll(bal);
+    __syncthreads();
     if (tid < E) {
-        for (int r = 0; r < R; ++r)
-            for (int j = 0; j < top; ++j) cnt += sids[r][j] == tid;
-        scnt[tid] = cnt;
+        int g = __popcll(bal & ((1ull << lane) - 1ull));
+        for (int v = 0; v < wave; ++v) g += swave[v];
+        sgid[tid] = touched ? g : -1;
+        if (tid == E - 1) t.gcount[0] = g + (touched ? 1 : 0);
+        if (touched) {
+            t.gexp[g] = tid;
+            t.gcnt[g] = __popc(msk);
+            unsigned rest = msk;
+#pragma unroll
+            for (int m = 0; m < 16; ++m) {
+                t.grows[16 * g + m] = rest ? __ffs(rest) - 1 : 0;  // lanes in ascending order, then 0
+                rest &= rest - 1u;
+            }
+        }
     }
     __syncthreads();
-    if (tid == 0) {
-        int g = 0;
-        for (int e = 0; e < E; ++e) sgid[e] = scnt[e] > 0 ? g++ : -1;
-        t.gcount[0] = g;
-    }
-    __syncthreads();
-    if (tid < E && cnt > 0) {
-        const int g = sgid[tid];
-        t.gexp[g] = tid;
-        t.gcnt[g] = cnt;
-        int m = 0;
-        for (int r = 0; r < R; ++r)
-            for (int j = 0; j < top; ++j)
-                if (sids[r][j] == tid) {
-                    t.grows[16 * g + m] = r;
-                    t.pos[r * kMoeMaxTop + j] = 16 * g + m;
-                    ++m;
-                }
-        for (; m < 16; ++m) t.grows[16 * g + m] = 0;
+
+    // (lane r, rank j): row 16 g + (lanes below r in the group)
+    if (wave < R && lane < top) {
+        const int r = wave, e = sids[r][lane];
+        t.pos[r * kMoeMaxTop + lane] = 16 * sgid[e] + __popc(smask[e] & ((1u << r) - 1u));
     }
 }
 
@@ -231,7 +244,7 @@ extern "C" int32_t verify_moe_w4(const uint16_t* x, const float* router, int32_t
     // groups launched: at most the distinct experts R lanes can touch
     const int ng = E < top * R ? E : top * R;
 
-    hipLaunchKernelGGL(moe_route_kernel, dim3(1), dim3(256), 0, st, router, R, E, top, t);
+    hipLaunchKernelGGL(moe_route_kernel, dim3(1), dim3(kRouteThreads), 0, st, router, R, E, top, t);
     if ((rc = check_hip(hipGetLastError(), "moe_route launch"))) return rc;
 
     W4Args a{};
