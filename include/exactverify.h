@@ -108,8 +108,10 @@ int32_t verify_linear_w4(const uint16_t* x_bf16, int32_t R, int32_t K, const voi
 /*   h = bf16_rne(silu(g) * u),  silu(v) = v / (1 + e^-v)  (fp32)             */
 /*   y = W_down h                      (W4 linear I -> H, fp32 out)           */
 /* Each W4 linear is the one defined above; the three matrices are passed     */
-/* packed (gate and up I x H, down H x I).  g and u are each summed as two    */
-/* halves of K (first half + second half), fixed by (H, G) -- never by R.     */
+/* packed (gate and up I x H, down H x I).  The order in which g and u are    */
+/* summed over K is fixed by (H, I, G) -- never by R: two halves of K when    */
+/* the pair's columns alone fill the GPU, else fixed K-segments added in      */
+/* ascending order.                                                           */
 /*   h_bf16  (device, optional, 16-byte aligned) [R][I] bf16: if non-NULL, h  */
 /*           is also written there.                                           */
 /* Limits as verify_linear_w4 for both shapes.                                */

@@ -8,6 +8,8 @@ the W4 LM head (5120 -> 151936, G 64), then
   (top-two gap below 1e-12, or a top-p cut within 1e-9 Z), which are counted;
   greedy (T = 0) equals the oracle's argmax on every row;
 * the logits match the oracle on sampled columns (per-row relative error);
+* the pages' sampling point (T 1, top-k 20, top-p 0.95, seeds 1234-1238)
+  draws the oracle's token at all 64 positions;
 * drafted rounds of R = 1, 2, 4, 8, 16 lanes slide over the 64 positions:
   lane r of a round at position p samples position p + r from hidden row
   p + r, the drafts for positions p .. p + R - 2 are the serial tokens with
@@ -79,6 +81,26 @@ def test_thousand_seeds_by_sixty_four_positions(lm):
     for i in range(16, N_POS, 16):
         g = np.concatenate([g, host(_gpu_tokens(Ld[i:i + 16], pos[i:i + 16], 0, 0.0))])
     assert np.array_equal(g, np.argmax(logits, axis=1).astype(np.int32))
+
+
+def test_pages_sampling_point(lm):
+    """The pages' own sampling setting (TensorFold README, the DGX Spark
+    measurement after the CUDA engine paragraph: T 1, top-k 20, top-p 0.95,
+    seeds 1234-1238, 64-token replies) on the same 64 hidden rows: every draw
+    equals the oracle's, near-ties counted."""
+    _, _, logits = lm
+    Ld = dev(logits)
+    pos = torch.arange(N_POS, dtype=torch.int64, device="cuda")
+    near = 0
+    for seed in range(1234, 1239):
+        gpu = np.concatenate([host(_gpu_tokens(Ld[i:i + 16], pos[i:i + 16], seed, 1.0)) for i in range(0, N_POS, 16)])
+        for p in range(N_POS):
+            cand = oracle.topk(logits[p], K_TOP)
+            o = oracle.sample_from_candidates(logits[p], cand, p, 1.0, P_TOP, seed)
+            if o.token != gpu[p]:
+                assert o.gap < 1e-12 or o.topp_edge, (seed, p, o.token, gpu[p], o.gap)
+                near += 1
+    print(f"seeds 1234-1238 x {N_POS} positions at T = 1: {near} decisions in the last bits of fp64")
 
 
 @pytest.mark.parametrize("seed", [0, 17, 999])
