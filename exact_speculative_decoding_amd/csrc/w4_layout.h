@@ -5,8 +5,9 @@
 // chunk 0, then those of chunk 1, ...; see w4_tc_offset):
 //   blob[chunk][tile] = 1024 B of nibbles + 64*(128/G) B of (scale, bias)
 //   * nibbles: lane L = ln + 16 j of a wave reads 16 B at 16 L; dword t holds
-//     the 8 codes of row 16*tile + ln for k = 128 c + 32 t + 8 j .. +7, in k
-//     order, low nibble first (the standard byte order of those 8 codes);
+//     the 8 codes q0..q7 of row 16*tile + ln for k = 128 c + 32 t + 8 j .. +7,
+//     nibbles low to high q0 q2 q4 q6 q1 q3 q5 q7 (even k in the low half, odd
+//     k in the high half, so that one shift and mask decodes a k-ordered pair);
 //   * (scale, bias): for row ln and group g of the chunk, the fp16 pair
 //     (scale | bias << 16) at 1024 + 4 (ln * GPC + g).
 // Rows >= N and k >= K are padding: codes, scales and biases 0, which adds
@@ -15,8 +16,7 @@
 //
 // Inside the kernel, the activations of a chunk are staged in LDS as MFMA A
 // fragments: [step][lane L][16 B] = the 8 bf16 x[ln][128 c + 32 st + 8 j + i]
-// in the order i = 0,4,1,5,2,6,3,7 (matching the nibble decode); rows >= R
-// and k >= K are 0.
+// for i = 0..7, a plain copy of 16 B of the row; rows >= R and k >= K are 0.
 #pragma once
 
 #include <hip/hip_runtime.h>

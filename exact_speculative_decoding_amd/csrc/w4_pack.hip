@@ -6,6 +6,19 @@
 
 namespace ev {
 
+// The 8 codes q0..q7 of a standard dword (q_i in bits 4i..4i+3) with the
+// even-k codes moved to the low half and the odd-k codes to the high half:
+// nibbles, low to high, q0 q2 q4 q6 q1 q3 q5 q7.  q_{2m} and q_{2m+1} then sit
+// exactly 16 bits apart, so one shift and mask places both in a bf16 pair.
+__device__ __forceinline__ uint32_t nibble_split(uint32_t w) {
+    uint32_t e = w & 0x0F0F0F0Fu, o = (w >> 4) & 0x0F0F0F0Fu;
+    e = (e | (e >> 4)) & 0x00FF00FFu;
+    o = (o | (o >> 4)) & 0x00FF00FFu;
+    e = (e | (e >> 8)) & 0x0000FFFFu;
+    o = (o | (o >> 8)) & 0x0000FFFFu;
+    return e | (o << 16);
+}
+
 // One thread per (tile, chunk, lane): 16 B of codes, plus (for the lanes of
 // row group j == 0) the row's (scale, bias) pairs of the chunk.
 __global__ void w4_pack_kernel(const uint8_t* __restrict__ q, const uint16_t* __restrict__ s,
@@ -28,7 +41,7 @@ __global__ void w4_pack_kernel(const uint8_t* __restrict__ q, const uint16_t* __
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
         const int k = kKC * c + 32 * t + 8 * j;
-        if (n < N && k < K) w[t] = *reinterpret_cast<const uint32_t*>(q + (size_t)n * Kh + k / 2);
+        if (n < N && k < K) w[t] = nibble_split(*reinterpret_cast<const uint32_t*>(q + (size_t)n * Kh + k / 2));
     }
     *reinterpret_cast<u32x4*>(dst + 16 * L) = w;
     if (j == 0) {

@@ -67,9 +67,10 @@ __device__ __forceinline__ u32x2 bload64(rsrc_t r, uint32_t voff, uint32_t soff)
     return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
 }
 
-// Eight nibbles q0..q7 (q_i in bits 4i..4i+3) -> four bf16 pairs holding
-// 16 + q in the order (q0,q4) (q1,q5) (q2,q6) (q3,q7): bf16 0x4180 is 16, and
-// q goes to mantissa bits 3..6.  Exact.  The offset 16 (rather than 128 with q
+// A packed dword (nibbles, low to high, q0 q2 q4 q6 q1 q3 q5 q7: q_{2m} and
+// q_{2m+1} 16 bits apart) -> four bf16 pairs holding 16 + q in k order (q0,q1)
+// (q2,q3) (q4,q5) (q6,q7): bf16 0x4180 is 16, and q goes to mantissa bits
+// 3..6.  Exact.  The offset 16 (rather than 128 with q
 // in the low mantissa bits, which would save one shift in four) keeps
 // b - 16 s exact in fp32 for every fp16 pair (s, b), so a one-hot row reads
 // back s * q + b with a single rounding.
@@ -214,18 +215,13 @@ __device__ __forceinline__ void w4_block(const W4Args& a, long blk, uint8_t (*xl
             xin[m] = bload128(rx, ok ? (uint32_t)(xrow[m] * a.K + k) * 2u : kOOB, 0u);
         }
     };
-    // reorder (x0,x4) (x1,x5) (x2,x6) (x3,x7) and store as the A fragment of
-    // lane r + 16 xj of step xst of chunk xc
+    // store as the A fragment of lane r + 16 xj of step xst of chunk xc (the
+    // 8 k in their natural order, as the nibble decode pairs them)
     auto xstore = [&](int buf) {
 #pragma unroll
         for (int m = 0; m < kXP; ++m) {
             const int r = xr0 + kXR * m;
-            const u32x4 v = xin[m];
-            u32x4 o;
-            o[0] = __builtin_amdgcn_perm(v[2], v[0], 0x05040100u);
-            o[1] = __builtin_amdgcn_perm(v[2], v[0], 0x07060302u);
-            o[2] = __builtin_amdgcn_perm(v[3], v[1], 0x05040100u);
-            o[3] = __builtin_amdgcn_perm(v[3], v[1], 0x07060302u);
+            const u32x4 o = xin[m];
             *reinterpret_cast<u32x4*>(&xlds[2 * half + buf][(size_t)((xc * 4 + xst) * 64 + r + 16 * xj) * 16]) = o;
         }
     };
@@ -506,12 +502,7 @@ __device__ __forceinline__ void w4_sk_block(const W4Args& a, int w, uint8_t (*xl
 #pragma unroll
         for (int m = 0; m < kXP; ++m) {
             const int r = xr0 + kXR * m;
-            const u32x4 v = xin[m];
-            u32x4 o;
-            o[0] = __builtin_amdgcn_perm(v[2], v[0], 0x05040100u);
-            o[1] = __builtin_amdgcn_perm(v[2], v[0], 0x07060302u);
-            o[2] = __builtin_amdgcn_perm(v[3], v[1], 0x05040100u);
-            o[3] = __builtin_amdgcn_perm(v[3], v[1], 0x07060302u);
+            const u32x4 o = xin[m];
             *reinterpret_cast<u32x4*>(&xlds[buf][(size_t)((xc * 4 + xst) * 64 + r + 16 * xj) * 16]) = o;
         }
     };

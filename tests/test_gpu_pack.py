@@ -1,7 +1,8 @@
 """The packed W4 layout is an exact copy: w4_pack's bytes equal an independent
 numpy construction of the layout (16-row tiles by 128-k chunks, chunk-major:
 all tiles of chunk 0, then of chunk 1, ...; each tile-chunk holds its codes in
-lane order, then its (scale, bias) pairs; zero padding past N and K)."""
+lane order, each dword's 8 codes as even-k then odd-k nibbles, then its
+(scale, bias) pairs; zero padding past N and K)."""
 import numpy as np
 import pytest
 
@@ -29,6 +30,8 @@ def _layout(q, s, b, N, K, G):
                 for t in range(4):
                     k = 128 * c + 32 * t + 8 * j
                     blk[L, t] = qv[16 * tile + ln, k:k + 8]
+            # within a dword, nibbles low to high: q0 q2 q4 q6 q1 q3 q5 q7
+            blk = blk[..., [0, 2, 4, 6, 1, 3, 5, 7]]
             codes = (blk[..., 0::2] | (blk[..., 1::2] << 4)).reshape(-1)
             out[c, tile, :1024] = codes
             pairs = sp[16 * tile:16 * tile + 16, c * GPC:(c + 1) * GPC]  # [ln][g]
