@@ -293,17 +293,18 @@ __device__ __forceinline__ void w4_block(const W4Args& a, long blk, uint8_t (*xl
         }
     };
 
-    // Prologue: superchunk 0 of the split into LDS slab 0, the first kPD
-    // chunks of weights in flight, superchunk 1 in registers.
+    // Prologue: superchunk 0 of the split loaded, the first kPD chunks of
+    // weights in flight behind it, the superchunk into LDS slab 0, superchunk 1
+    // in registers.
     const int sc0 = c0 / kSC;
     xload(sc0);
-    xstore(0);
 #pragma unroll
     for (int p = 0; p < kPD; ++p) {
         __builtin_amdgcn_sched_barrier(0);
         fetch(c0 + p, p);
     }
     __builtin_amdgcn_sched_barrier(0);
+    xstore(0);  // waits for the activations only: they were loaded before the ring
     xload(sc0 + 1);
     __syncthreads();
 
@@ -454,8 +455,6 @@ __device__ __forceinline__ void w4_sk_block(const W4Args& a, int w, uint8_t (*xl
     static_assert(kXR * kXP == 16, "the workgroup's passes must cover the 16 rows");
     const int xr0 = tid / kXL, col = tid % kXL;
     const uint32_t wbytes = __builtin_amdgcn_readfirstlane(a.wbytes);
-    const rsrc_t rw0 = make_rsrc(uniform_ptr(a.w[0]), wbytes);
-    const rsrc_t rw1 = make_rsrc(uniform_ptr(a.w[1]), wbytes);
     const rsrc_t rx = make_rsrc(uniform_ptr(a.x), __builtin_amdgcn_readfirstlane(a.xbytes));
     const uint32_t cstride = (uint32_t)a.tiles * CB;
     const uint32_t vq = 16u * lane;
@@ -513,7 +512,9 @@ __device__ __forceinline__ void w4_sk_block(const W4Args& a, int w, uint8_t (*xl
     uint32_t sbr[kPD][kNT][SBW];
     auto fetch = [&](bool live, Unit v, int p, int slot) {
         const int c = v.sc * kSC + p;
-        const rsrc_t r = v.m ? rw1 : rw0;
+        // the descriptor from a pointer moved to scalar registers, so the
+        // matrix select can never turn it into a per-lane value
+        const rsrc_t r = make_rsrc(uniform_ptr(v.m ? a.w[1] : a.w[0]), wbytes);
 #pragma unroll
         for (int t = 0; t < kNT; ++t) {
             const int tile = (v.cb * kWaves + wave) * kNT + t;
@@ -585,17 +586,18 @@ __device__ __forceinline__ void w4_sk_block(const W4Args& a, int w, uint8_t (*xl
         }
     };
 
-    // Prologue: unit u0's activations into slab 0, its first kPD chunks of
-    // weights in flight, unit u0 + 1's activations in registers.
+    // Prologue: unit u0's activations loaded, its first kPD chunks of weights
+    // in flight behind them, the activations into slab 0, unit u0 + 1's
+    // activations in registers.
     Unit nxt = next(cur);
     xload(true, cur.sc);
-    xstore(0);
 #pragma unroll
     for (int p = 0; p < kPD; ++p) {
         __builtin_amdgcn_sched_barrier(0);
         fetch(true, cur, p, p);
     }
     __builtin_amdgcn_sched_barrier(0);
+    xstore(0);  // waits for the activations only: they were loaded before the ring
     xload(u0 + 1 < u1, nxt.sc);
     __syncthreads();
 
