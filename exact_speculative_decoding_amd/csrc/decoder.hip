@@ -203,8 +203,8 @@ __device__ __forceinline__ f16x8 load_f16x8(const uint16_t* p) {
 //   query ln (replicated over grp) and O^T rows d = 16 dt + 4 grp + v.
 __global__ __launch_bounds__(64) void attn_partial_kernel(AttnArgs a) {
     const int lane = threadIdx.x, ln = lane & 15, grp = lane >> 4;
-    const int chunk = blockIdx.x, g = blockIdx.y, qt = blockIdx.z;
     const int gq = a.NH / a.NKV, nq = a.R * gq;
+    const int chunk = blockIdx.x, g = blockIdx.y, qt = blockIdx.z;
     const int qi = qt * 16 + ln;
     const bool qok = qi < nq;
     const int r = qok ? qi / gq : 0;
@@ -263,9 +263,10 @@ __global__ __launch_bounds__(64) void attn_partial_kernel(AttnArgs a) {
     const uint16_t* vb = a.vc + (size_t)g * a.C * kHD;
     const f16x8 z8 = {};
 
-    for (long long s0 = cstart; s0 <= cend; s0 += kKStep) {
-        // keys: rows slot = s0 + 16 t + ln, d = 32 ds + 8 grp .. + 7
-        f16x8 kf[2][4];
+    // K and V of the step at s0 into (kf, vf): keys rows slot = s0 + 16 t + ln,
+    // d = 32 ds + 8 grp .. + 7; values V^T rows d = 16 dt + ln, positions
+    // 8 grp .. + 7 of block s0 / 32
+    auto load_kv = [&](long long s0, f16x8 (&kf)[2][4], f16x8 (&vf)[8]) {
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
             const long long slot = s0 + 16 * t + ln;
@@ -273,11 +274,12 @@ __global__ __launch_bounds__(64) void attn_partial_kernel(AttnArgs a) {
 #pragma unroll
             for (int ds = 0; ds < 4; ++ds) kf[t][ds] = slot <= pmax ? load_f16x8(kp + 32 * ds) : z8;
         }
-        // values: V^T rows d = 16 dt + ln, positions 8 grp .. + 7 of block s0 / 32
-        f16x8 vf[8];
         const uint16_t* vp = vb + (size_t)(s0 / kKStep) * kHD * kKStep + (size_t)ln * kKStep + 8 * grp;
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) vf[dt] = load_f16x8(vp + (size_t)16 * dt * kKStep);
+    };
+    // one online-softmax step over the slots s0 .. s0 + 31 from (kf, vf)
+    auto step = [&](long long s0, f16x8 (&kf)[2][4], f16x8 (&vf)[8]) {
         if (s0 + kKStep - 1 > pmax) {  // zero the slots past the pass (stale or never written)
 #pragma unroll
             for (int kk = 0; kk < 8; ++kk) {
@@ -347,6 +349,24 @@ __global__ __launch_bounds__(64) void attn_partial_kernel(AttnArgs a) {
 #pragma unroll
             for (int dt = 0; dt < 8; ++dt) acc[dt] = keep[dt];
         }
+    };
+    // The loads of step s + 1 are issued before step s is computed (two
+    // register sets, swapped by unrolling), so each step's memory latency
+    // hides behind the previous step's arithmetic.
+    f16x8 kA[2][4], vA[8], kB[2][4], vB[8];
+    long long s0 = cstart;
+    load_kv(s0, kA, vA);
+    for (;;) {
+        const bool more = s0 + kKStep <= cend;
+        if (more) load_kv(s0 + kKStep, kB, vB);
+        step(s0, kA, vA);
+        if (!more) break;
+        s0 += kKStep;
+        const bool more2 = s0 + kKStep <= cend;
+        if (more2) load_kv(s0 + kKStep, kA, vA);
+        step(s0, kB, vB);
+        if (!more2) break;
+        s0 += kKStep;
     }
 
     if (qok && P >= cstart) {
@@ -363,37 +383,67 @@ __global__ __launch_bounds__(64) void attn_partial_kernel(AttnArgs a) {
 }
 
 // o[r][h][d] = bf16(sum_c acc_c[d] e^(m_c - M) / sum_c l_c e^(m_c - M)) over
-// the chunks c = 0 .. (pos0 + r) / chunk, ascending; M = max_c m_c.
-__global__ __launch_bounds__(kHD) void attn_merge_kernel(const float* __restrict__ part, int NH, int chunk,
-                                                         int nchunk_max, const long long* __restrict__ positions,
-                                                         uint16_t* __restrict__ o) {
+// the chunks c = 0 .. nch-1, nch = (pos0 + r) / chunk + 1; M = max_c m_c.
+// Four groups of kHD threads each sum a fixed quarter of the chunks (chunk
+// order inside a quarter; loads 8 at a time), and the quarters are added in
+// order 0, 1, 2, 3: a fixed order set by the row's own position.
+constexpr int kMergeGroups = 4;
+__global__ __launch_bounds__(kHD * kMergeGroups) void attn_merge_kernel(const float* __restrict__ part, int NH,
+                                                                        int chunk, int nchunk_max,
+                                                                        const long long* __restrict__ positions,
+                                                                        uint16_t* __restrict__ o) {
     const long long pos0 = positions[kPos0Slot];
     __shared__ float sm[kMaxChunks], se[kMaxChunks], sl[kMaxChunks];
-    __shared__ float red[2];
-    const int r = blockIdx.x, h = blockIdx.y, d = threadIdx.x;
+    __shared__ float red[kMergeGroups * kHD / 64];
+    __shared__ float pacc[kMergeGroups][kHD];
+    __shared__ float pl[kMergeGroups];
+    const int r = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+    const int d = tid % kHD, q = tid / kHD;
     const int nch = (int)((pos0 + r) / chunk) + 1;
     const float* b = part + ((size_t)r * NH + h) * nchunk_max * kPartStride;
     float mv = -INFINITY;
-    if (d < nch) {
-        mv = b[(size_t)d * kPartStride];
-        sm[d] = mv;
-        sl[d] = b[(size_t)d * kPartStride + 1];
+    if (tid < nch) {
+        mv = b[(size_t)tid * kPartStride];
+        sm[tid] = mv;
+        sl[tid] = b[(size_t)tid * kPartStride + 1];
     }
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) mv = fmaxf(mv, __shfl_xor(mv, off, 64));
-    if ((d & 63) == 0) red[d >> 6] = mv;
+    if ((tid & 63) == 0) red[tid >> 6] = mv;
     __syncthreads();
-    const float M = fmaxf(red[0], red[1]);
-    if (d < nch) se[d] = expf(sm[d] - M);
+    float M = red[0];
+#pragma unroll
+    for (int i = 1; i < kMergeGroups * kHD / 64; ++i) M = fmaxf(M, red[i]);
+    if (tid < nch) se[tid] = expf(sm[tid] - M);
     __syncthreads();
+    const int per = (nch + kMergeGroups - 1) / kMergeGroups;
+    const int lo = q * per, hi = min(nch, lo + per);
     float L = 0.f, acc = 0.f;
-#pragma unroll 8
-    for (int c = 0; c < nch; ++c) {
-        const float e = se[c];
-        L = fmaf(sl[c], e, L);
-        acc = fmaf(b[(size_t)c * kPartStride + 2 + d], e, acc);
+    for (int c0 = lo; c0 < hi; c0 += 8) {
+        float v[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            if (c0 + i < hi) v[i] = b[(size_t)(c0 + i) * kPartStride + 2 + d];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            if (c0 + i < hi) {
+                const float e = se[c0 + i];
+                L = fmaf(sl[c0 + i], e, L);
+                acc = fmaf(v[i], e, acc);
+            }
     }
-    o[((size_t)r * NH + h) * kHD + d] = f32_to_bf16_rne(acc / L);
+    pacc[q][d] = acc;
+    if (d == 0) pl[q] = L;
+    __syncthreads();
+    if (q == 0) {
+        float Lt = pl[0], at = pacc[0][d];
+#pragma unroll
+        for (int g = 1; g < kMergeGroups; ++g) {
+            Lt += pl[g];
+            at += pacc[g][d];
+        }
+        o[((size_t)r * NH + h) * kHD + d] = f32_to_bf16_rne(at / Lt);
+    }
 }
 
 // Workspace of a verify step, from the configuration and max_ctx only.
@@ -653,7 +703,8 @@ static int32_t step_body(ev_decoder* m, int R, const ev_sampling& sampling, int3
         AttnArgs aa{q, kcl, vcl, att, R, NH, NKV, m->C, L.chunk, L.nchunk_max, pos, 0.08838834764831845f};
         hipLaunchKernelGGL(attn_partial_kernel, dim3(L.nchunk_max, NKV, nqt), dim3(64), 0, st, aa);
         if ((rc = check_hip(hipGetLastError(), "attn_partial launch"))) return rc;
-        hipLaunchKernelGGL(attn_merge_kernel, dim3(R, NH), dim3(kHD), 0, st, att, NH, L.chunk, L.nchunk_max, pos, o);
+        hipLaunchKernelGGL(attn_merge_kernel, dim3(R, NH), dim3(kHD * kMergeGroups), 0, st, att, NH, L.chunk,
+                           L.nchunk_max, pos, o);
         if ((rc = check_hip(hipGetLastError(), "attn_merge launch"))) return rc;
         if ((rc = linear(y.w_o, o, m->DQ, H, L.p_o, L.q_o, L.sk_o))) return rc;
         hipLaunchKernelGGL(res_norm_kernel, dim3(R), dim3(kRowThreads), 0, st, part, L.p_o.S,
