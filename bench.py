@@ -61,9 +61,14 @@ def mlp_bytes(R, H, I, G):
     return 2 * lin(H, I) + lin(I, H)
 
 
+# The sources that define the W4 kernels whose HBM traffic the committed
+# counters measure (kernel code, launch plans, layouts, shared helpers).
+W4_SOURCES = ("w4_verify.hip", "w4_kernel.h", "w4_layout.h", "ev_internal.h")
+
+
 def source_hash():
     h = hashlib.sha256()
-    for f in sorted(os.listdir(os.path.join(ROOT, "exact_speculative_decoding_amd", "csrc"))):
+    for f in W4_SOURCES:
         with open(os.path.join(ROOT, "exact_speculative_decoding_amd", "csrc", f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
@@ -71,7 +76,8 @@ def source_hash():
 
 def load_traffic():
     """HBM traffic per W4 launch from committed rocprofv3 counter runs, valid
-    only while the kernel sources are unchanged since the counters were taken."""
+    only while the W4 kernel sources are unchanged since the counters were
+    taken."""
     p = os.path.join(ROOT, "profiles", "w4_verify_mlp_traffic.json")
     if not os.path.exists(p):
         return None
