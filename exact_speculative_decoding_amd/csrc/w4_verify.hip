@@ -27,12 +27,18 @@
 //   * a ring of kPD chunks of loads is kept in flight per wave; loads past the
 //     split's last chunk use an out-of-range per-lane offset, which the buffer
 //     range check turns into zeros without touching memory;
-//   * K-split partial sums go to a workspace [S][16][N] and are added in
-//     ascending split order by a second kernel (fused with SiLU * up for the
-//     MLP gate/up pair); a gate/up pair with enough tiles to fill the chip on
-//     its own, and every grouped MoE pass, runs instead as one paired launch
-//     that splits K in two halves inside the workgroup and writes
-//     h = bf16(silu(g) * u) itself, with no partial rows.
+//   * dense launches that need a K-split run balanced (w4_sk_kernel): 768
+//     workgroups each take an equal contiguous run of (matrix, column block,
+//     superchunk) units and write one partial segment per block their run
+//     touches; a second kernel adds a block's segments in ascending workgroup
+//     order (fused with SiLU * up for the MLP gate/up pair).  Launches whose
+//     columns alone fill the chip (the LM head) and the grouped MoE down
+//     passes run split (w4_verify_kernel: a plan of S splits, partials
+//     [S][16][N] added in ascending split order, or direct outputs at S = 1);
+//     a gate/up pair with enough tiles to fill the chip on its own, every
+//     grouped MoE gate/up pass and the decoder's gate/up and q|k|v run as one
+//     launch that splits K in two halves inside the workgroup and writes its
+//     finished outputs itself, with no partial rows.
 #include <algorithm>
 #include <mutex>
 #include <vector>
