@@ -240,8 +240,7 @@ def leg_decoder(ev, syn, C, n_tokens=512, R=8, p_draft=0.65):
 
     def run(m, Rr, drafter):
         def fn(tokens, pos):
-            s, nc = m.verify_step(torch.tensor(tokens, dtype=torch.int32, device="cuda"), pos, *samp)
-            return s.cpu().tolist(), int(nc.cpu()[0])
+            return m.verify_step_host(tokens, pos, *samp)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         toks, rounds = decode(fn, d["first_token"], pos0, n_tokens, Rr, drafter)

@@ -317,6 +317,7 @@ class ToyDecoder:
                                         _dev(v_cache, "v_cache", _F16), self.max_ctx, C.byref(h)))
         self._h = h
         self._outs = {}  # R -> (sampled, n_commit) kept for graph replay
+        self._host_io = {}  # R -> buffers of verify_step_host
         self.ws = torch.empty(int(lib().verify_step_workspace(h)), dtype=torch.uint8,
                               device=k_cache.device)
 
@@ -357,6 +358,30 @@ class ToyDecoder:
             None if logits is None else _dev(logits, "logits", (torch.float32,)),
             C.c_void_p(self.ws.data_ptr()), self.ws.numel(), _stream(stream)))
         return sampled, n_commit
+
+
+    def verify_step_host(self, tokens, pos0, temperature, top_k, top_p, seed):
+        """verify_step for a host round loop: `tokens` is a list of R ints;
+        returns (sampled tokens as a list, n_commit).  The tokens go up from
+        pinned host memory, the R sampled tokens and the commit count come
+        back together (one device buffer, one copy into pinned memory), and
+        the call waits for the current stream once."""
+        R = len(tokens)
+        io = self._host_io.get(R)
+        if io is None:
+            dev = self.ws.device
+            io = (torch.empty(R, dtype=torch.int32, pin_memory=True), torch.empty(R, dtype=torch.int32, device=dev),
+                  torch.empty(R + 1, dtype=torch.int32, device=dev),
+                  torch.empty(R + 1, dtype=torch.int32, pin_memory=True))
+            self._host_io[R] = io
+        tok_h, tok_d, out_d, out_h = io
+        tok_h.numpy()[:] = tokens
+        tok_d.copy_(tok_h, non_blocking=True)
+        self.verify_step(tok_d, pos0, temperature, top_k, top_p, seed, sampled=out_d[:R], n_commit=out_d[R:])
+        out_h.copy_(out_d, non_blocking=True)
+        torch.cuda.current_stream(self.ws.device).synchronize()
+        o = out_h.numpy()
+        return o[:R].tolist(), int(o[R])
 
 
 # Value-cache slot order inside a block of 32 slots (see verify_step in

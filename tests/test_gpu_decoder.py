@@ -163,6 +163,35 @@ def test_tiny_graph_replay_equals_eager(tiny):
         assert np.array_equal(k1, k0) and np.array_equal(v1, v0)
 
 
+def test_tiny_host_round_helper_matches_verify_step(tiny):
+    """verify_step_host (pinned upload, one read-back of the sampled tokens
+    and the commit count) drives the same rounds as verify_step."""
+    d, cfg = tiny, tiny["cfg"]
+    pos0, n, V = cfg["prefill"], 24, cfg["vocab"]
+    ref = decode(_gpu_round(_fresh(d), SAMPLED), d["first_token"], pos0, n, 1, lambda p, c: [])[0]
+    for R in (1, 4, 16):
+        drafter = syn.transcript_drafter(ref, pos0 + 1, 0.65, 5, V)
+        logs = []
+        for use_host in (False, True):
+            m = _fresh(d)
+            log = []
+
+            def fn(tokens, p0):
+                if use_host:
+                    out = m.verify_step_host(tokens, p0, *SAMPLED)
+                else:
+                    s, c = m.verify_step(torch.tensor(tokens, dtype=torch.int32, device="cuda"), p0, *SAMPLED)
+                    out = (host(s).tolist(), int(host(c)[0]))
+                log.append((p0, tuple(tokens), tuple(out[0]), out[1]))
+                return out
+
+            got, _ = decode(fn, d["first_token"], pos0, n, R, drafter)
+            assert got == ref, R
+            logs.append(log)
+            del m
+        assert logs[0] == logs[1], R
+
+
 def test_tiny_decodes_to_the_last_slot(tiny):
     d, cfg = tiny, tiny["cfg"]
     pos0 = cfg["prefill"]
