@@ -121,3 +121,31 @@ def test_full_size_sampled_columns(name, K, N):
         assert np.array_equal(y1[0].view(np.uint32), y16[r].view(np.uint32))
     del wp
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("K,N", [(16384, 229376), (229376, 16384)])
+def test_largest_packed_matrix_sampled_columns(K, N):
+    """Packed matrices just under the 2^31-byte limit (G 64): wide (the direct
+    launch) and deep (the balanced launch, 896 superchunks a block), so the
+    kernels' 32-bit offsets reach the top of their range.  Sampled columns,
+    the last ones included, match the oracle; rows equal single-row calls."""
+    G = 64
+    nbytes = ev.w4_packed_bytes(N, K, G)
+    assert 0.98 * 2**31 < nbytes < 2**31
+    g = np.random.default_rng(1009 + K)
+    q, s, b = syn.w4_matrix(g, N, K, G)
+    x = syn.activations(g, 16, K)
+    wp = packed((q, s, b), G)
+    xd = dev(x)
+    y16 = host(ev.verify_linear_w4(xd, wp))
+    cols = np.unique(np.concatenate([np.arange(0, N, N // 61), [N - 1, N - 2, N - 16, N - 17, 127, 128]]))
+    ref = oracle.w4_linear(x, q[cols], s[cols], b[cols], G)
+    del q, s, b
+    err = row_rel_err(y16[:, cols], ref)
+    assert np.all(err <= ROW_REL_TOL), err
+    for r in (0, 15):
+        y1 = host(ev.verify_linear_w4(xd[r:r + 1].contiguous(), wp))
+        assert np.array_equal(y1[0].view(np.uint32), y16[r].view(np.uint32))
+    del wp
+    torch.cuda.empty_cache()
+
