@@ -48,6 +48,7 @@
 namespace ev {
 
 constexpr uint32_t kOOB = 0x80000000u;  // per-lane offset beyond every buffer: reads 0
+constexpr int kLoadNT = 2;  // cache-policy operand of a buffer load: the non-temporal (nt) bit
 constexpr int kSlab = kSC * kXChunkBytes;  // LDS bytes of one superchunk of activations
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
@@ -71,6 +72,16 @@ __device__ __forceinline__ u32x4 bload128(rsrc_t r, uint32_t voff, uint32_t soff
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ u32x2 bload64(rsrc_t r, uint32_t voff, uint32_t soff) {
     return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
+}
+// Weight loads: with NT the non-temporal hint (the lines are streamed once;
+// the caches keep the activations and partial rows instead).
+template <bool NT>
+__device__ __forceinline__ u32x4 wload128(rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, NT ? kLoadNT : 0));
+}
+template <bool NT>
+__device__ __forceinline__ u32x2 wload64(rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, NT ? kLoadNT : 0));
 }
 
 // A packed dword (nibbles, low to high, q0 q2 q4 q6 q1 q3 q5 q7: q_{2m} and
@@ -120,7 +131,7 @@ enum W4Mode { kPlain = 0, kPairMode = 1, kRopeMode = 2 };
 //      are turned by the row's position (the (cos, sin) table of the slot),
 //      queries go to the fp32 query rows and keys to their cache slot in
 //      fp16; value heads go to the blocked value cache in fp16.
-template <int G, int MODE>
+template <int G, int MODE, bool NT>
 __device__ __forceinline__ void w4_block(const W4Args& a, long blk, uint8_t (*xlds)[kSlab]) {
     constexpr bool PAIR = MODE != kPlain;  // the two K-halves in one workgroup
     constexpr int GPC = kKC / G;                // groups per chunk
@@ -245,13 +256,13 @@ __device__ __forceinline__ void w4_block(const W4Args& a, long blk, uint8_t (*xl
             const bool ok = live && tok[t];
             const uint32_t so = tbase[t] + (uint32_t)c * cstride;
             const rsrc_t r = (MODE == kPairMode && t == 1) ? rw1 : rw;
-            qr[slot][t] = bload128(r, ok ? vq : kOOB, so);
+            qr[slot][t] = wload128<NT>(r, ok ? vq : kOOB, so);
             if (GPC == 2) {
-                const u32x2 v = bload64(r, ok ? vsb : kOOB, so);
+                const u32x2 v = wload64<NT>(r, ok ? vsb : kOOB, so);
                 sbr[slot][t][0] = v[0];
                 sbr[slot][t][GPC - 1] = v[1];
             } else {
-                const u32x4 v = bload128(r, ok ? vsb : kOOB, so);
+                const u32x4 v = wload128<NT>(r, ok ? vsb : kOOB, so);
 #pragma unroll
                 for (int g = 0; g < SBW; ++g) sbr[slot][t][g] = v[g & 3];
             }
@@ -415,11 +426,11 @@ __device__ __forceinline__ void w4_block(const W4Args& a, long blk, uint8_t (*xl
     }
 }
 
-template <int G>
+template <int G, bool NT>
 __global__ __launch_bounds__(kThreads) void w4_verify_kernel(W4Args a) {
     __shared__ __align__(16) uint8_t xlds[2][kSlab];
     if (a.tstamp && threadIdx.x == 0) a.tstamp[2 * blockIdx.x] = wall_clock64();
-    w4_block<G, kPlain>(a, blockIdx.x, xlds);
+    w4_block<G, kPlain, NT>(a, blockIdx.x, xlds);
     if (a.tstamp) {  // uniform; grouped launches (which may return early) are never timed
         __syncthreads();
         if (threadIdx.x == 0) a.tstamp[2 * blockIdx.x + 1] = wall_clock64();
@@ -437,7 +448,7 @@ __global__ __launch_bounds__(kThreads) void w4_verify_kernel(W4Args a) {
 // another block, the workgroup writes its accumulators as one partial segment
 // and starts again from zero.  The segments of a block are added in ascending
 // workgroup order by sk_reduce_kernel.
-template <int G>
+template <int G, bool NT>
 __device__ __forceinline__ void w4_sk_block(const W4Args& a, int w, uint8_t (*xlds)[kSlab]) {
     constexpr int GPC = kKC / G;
     constexpr int SBW = GPC;
@@ -526,13 +537,13 @@ __device__ __forceinline__ void w4_sk_block(const W4Args& a, int w, uint8_t (*xl
             const int tile = (v.cb * kWaves + wave) * kNT + t;
             const bool ok = live && c < a.nchunks && tile < a.tiles;
             const uint32_t so = ok ? (uint32_t)tile * CB + (uint32_t)c * cstride : 0u;
-            qr[slot][t] = bload128(r, ok ? vq : kOOB, so);
+            qr[slot][t] = wload128<NT>(r, ok ? vq : kOOB, so);
             if (GPC == 2) {
-                const u32x2 x2 = bload64(r, ok ? vsb : kOOB, so);
+                const u32x2 x2 = wload64<NT>(r, ok ? vsb : kOOB, so);
                 sbr[slot][t][0] = x2[0];
                 sbr[slot][t][GPC - 1] = x2[1];
             } else {
-                const u32x4 x4 = bload128(r, ok ? vsb : kOOB, so);
+                const u32x4 x4 = wload128<NT>(r, ok ? vsb : kOOB, so);
 #pragma unroll
                 for (int g = 0; g < SBW; ++g) sbr[slot][t][g] = x4[g & 3];
             }
@@ -637,22 +648,22 @@ __device__ __forceinline__ void w4_sk_block(const W4Args& a, int w, uint8_t (*xl
     }
 }
 
-template <int G>
+template <int G, bool NT>
 __global__ __launch_bounds__(kThreads) void w4_sk_kernel(W4Args a) {
     __shared__ __align__(16) uint8_t xlds[2][kSlab];
     if (a.tstamp && threadIdx.x == 0) a.tstamp[2 * blockIdx.x] = wall_clock64();
-    w4_sk_block<G>(a, blockIdx.x, xlds);
+    w4_sk_block<G, NT>(a, blockIdx.x, xlds);
     if (a.tstamp) {
         __syncthreads();
         if (threadIdx.x == 0) a.tstamp[2 * blockIdx.x + 1] = wall_clock64();
     }
 }
 
-template <int G, int MODE>
+template <int G, int MODE, bool NT>
 __global__ __launch_bounds__(2 * kThreads) void w4_pair_kernel(W4Args a) {
     __shared__ __align__(16) uint8_t xlds[4][kSlab];
     if (a.tstamp && threadIdx.x == 0) a.tstamp[2 * blockIdx.x] = wall_clock64();
-    w4_block<G, MODE>(a, blockIdx.x, xlds);
+    w4_block<G, MODE, NT>(a, blockIdx.x, xlds);
     if (a.tstamp) {
         __syncthreads();
         if (threadIdx.x == 0) a.tstamp[2 * blockIdx.x + 1] = wall_clock64();
@@ -898,6 +909,14 @@ static void prep_w4(W4Args& args, int nmat, const W4Plan& p, int K, int G, int n
     args.tstamp = nullptr;
 }
 
+// Launches that stream at least kNtBytes of weights load them with the
+// non-temporal hint; smaller ones (the decoder's per-layer matrices, read
+// again every round) load them plainly.
+#ifndef EV_W4_NT_BYTES
+#define EV_W4_NT_BYTES (32.0 * (1 << 20))
+#endif
+static bool stream_hint(double weight_bytes) { return weight_bytes >= EV_W4_NT_BYTES; }
+
 // Timing slots for a launch of `blocks` workgroups moving `bytes` algorithmic
 // bytes, or NULL when the hook is off.
 static int32_t timing_slots(long blocks, double bytes, unsigned long long** out) {
@@ -921,10 +940,15 @@ int32_t launch_w4(W4Args args, int nmat, const W4Plan& p, int K, int G, hipStrea
         if (rc) return rc;
     }
     const unsigned blocks = (unsigned)args.blocks;
-    if (G == 64)
-        hipLaunchKernelGGL(w4_verify_kernel<64>, dim3(blocks), dim3(kThreads), 0, st, args);
+    const bool nt = stream_hint((double)args.wbytes * nmat * ngroups);
+    if (G == 64 && nt)
+        hipLaunchKernelGGL((w4_verify_kernel<64, true>), dim3(blocks), dim3(kThreads), 0, st, args);
+    else if (G == 64)
+        hipLaunchKernelGGL((w4_verify_kernel<64, false>), dim3(blocks), dim3(kThreads), 0, st, args);
+    else if (nt)
+        hipLaunchKernelGGL((w4_verify_kernel<32, true>), dim3(blocks), dim3(kThreads), 0, st, args);
     else
-        hipLaunchKernelGGL(w4_verify_kernel<32>, dim3(blocks), dim3(kThreads), 0, st, args);
+        hipLaunchKernelGGL((w4_verify_kernel<32, false>), dim3(blocks), dim3(kThreads), 0, st, args);
     return check_hip(hipGetLastError(), "w4_verify_kernel launch");
 }
 
@@ -948,10 +972,15 @@ int32_t launch_w4_sk(W4Args args, int nmat, const SkPlan& q, int K, int G, hipSt
     args.tstamp = nullptr;
     int32_t rc = timing_slots(q.nwg, w4_algo_bytes(nmat, args.R, K, args.N, G), &args.tstamp);
     if (rc) return rc;
-    if (G == 64)
-        hipLaunchKernelGGL(w4_sk_kernel<64>, dim3(q.nwg), dim3(kThreads), 0, st, args);
+    const bool nt = stream_hint((double)args.wbytes * nmat);
+    if (G == 64 && nt)
+        hipLaunchKernelGGL((w4_sk_kernel<64, true>), dim3(q.nwg), dim3(kThreads), 0, st, args);
+    else if (G == 64)
+        hipLaunchKernelGGL((w4_sk_kernel<64, false>), dim3(q.nwg), dim3(kThreads), 0, st, args);
+    else if (nt)
+        hipLaunchKernelGGL((w4_sk_kernel<32, true>), dim3(q.nwg), dim3(kThreads), 0, st, args);
     else
-        hipLaunchKernelGGL(w4_sk_kernel<32>, dim3(q.nwg), dim3(kThreads), 0, st, args);
+        hipLaunchKernelGGL((w4_sk_kernel<32, false>), dim3(q.nwg), dim3(kThreads), 0, st, args);
     return check_hip(hipGetLastError(), "w4_sk_kernel launch");
 }
 
@@ -978,16 +1007,25 @@ static int32_t launch_w4_halved(W4Args args, const W4Plan& p, int K, int G, hipS
         if (rc) return rc;
     }
     const unsigned blocks = (unsigned)args.blocks;
+    const bool nt = stream_hint((double)args.wbytes * args.nmat * ngroups);
     if (rope) {
-        if (G == 64)
-            hipLaunchKernelGGL((w4_pair_kernel<64, kRopeMode>), dim3(blocks), dim3(2 * kThreads), 0, st, args);
+        if (G == 64 && nt)
+            hipLaunchKernelGGL((w4_pair_kernel<64, kRopeMode, true>), dim3(blocks), dim3(2 * kThreads), 0, st, args);
+        else if (G == 64)
+            hipLaunchKernelGGL((w4_pair_kernel<64, kRopeMode, false>), dim3(blocks), dim3(2 * kThreads), 0, st, args);
+        else if (nt)
+            hipLaunchKernelGGL((w4_pair_kernel<32, kRopeMode, true>), dim3(blocks), dim3(2 * kThreads), 0, st, args);
         else
-            hipLaunchKernelGGL((w4_pair_kernel<32, kRopeMode>), dim3(blocks), dim3(2 * kThreads), 0, st, args);
+            hipLaunchKernelGGL((w4_pair_kernel<32, kRopeMode, false>), dim3(blocks), dim3(2 * kThreads), 0, st, args);
     } else {
-        if (G == 64)
-            hipLaunchKernelGGL((w4_pair_kernel<64, kPairMode>), dim3(blocks), dim3(2 * kThreads), 0, st, args);
+        if (G == 64 && nt)
+            hipLaunchKernelGGL((w4_pair_kernel<64, kPairMode, true>), dim3(blocks), dim3(2 * kThreads), 0, st, args);
+        else if (G == 64)
+            hipLaunchKernelGGL((w4_pair_kernel<64, kPairMode, false>), dim3(blocks), dim3(2 * kThreads), 0, st, args);
+        else if (nt)
+            hipLaunchKernelGGL((w4_pair_kernel<32, kPairMode, true>), dim3(blocks), dim3(2 * kThreads), 0, st, args);
         else
-            hipLaunchKernelGGL((w4_pair_kernel<32, kPairMode>), dim3(blocks), dim3(2 * kThreads), 0, st, args);
+            hipLaunchKernelGGL((w4_pair_kernel<32, kPairMode, false>), dim3(blocks), dim3(2 * kThreads), 0, st, args);
     }
     return check_hip(hipGetLastError(), "w4 halved-mode launch");
 }
