@@ -189,6 +189,16 @@ struct AttnArgs {
 __device__ __forceinline__ f16x8 load_f16x8(const uint16_t* p) {
     return __builtin_bit_cast(f16x8, *reinterpret_cast<const u32x4*>(p));
 }
+// Cache reads: with NT the non-temporal hint, for passes that read each
+// slot once (one tile of queries per kv head); with more tiles the other
+// tiles' reads of the same slots find them cached.
+template <bool NT>
+__device__ __forceinline__ f16x8 load_kv_f16x8(const uint16_t* p) {
+    if constexpr (NT)
+        return __builtin_bit_cast(f16x8, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p)));
+    else
+        return load_f16x8(p);
+}
 
 // Attention partial of one chunk of slots (blockIdx.x), one kv head
 // (blockIdx.y) and one tile of 16 queries (blockIdx.z; query qi = row qi/gq,
@@ -201,6 +211,7 @@ __device__ __forceinline__ f16x8 load_f16x8(const uint16_t* p) {
 //   cache's slot order), so no data moves between the two.
 //   Online softmax over steps of 32 slots; lane (grp, ln) keeps the state of
 //   query ln (replicated over grp) and O^T rows d = 16 dt + 4 grp + v.
+template <bool NT>
 __global__ __launch_bounds__(64) void attn_partial_kernel(AttnArgs a) {
     const int lane = threadIdx.x, ln = lane & 15, grp = lane >> 4;
     const int gq = a.NH / a.NKV, nq = a.R * gq;
@@ -272,11 +283,11 @@ __global__ __launch_bounds__(64) void attn_partial_kernel(AttnArgs a) {
             const long long slot = s0 + 16 * t + ln;
             const uint16_t* kp = kb + (size_t)slot * kHD + 8 * grp;
 #pragma unroll
-            for (int ds = 0; ds < 4; ++ds) kf[t][ds] = slot <= pmax ? load_f16x8(kp + 32 * ds) : z8;
+            for (int ds = 0; ds < 4; ++ds) kf[t][ds] = slot <= pmax ? load_kv_f16x8<NT>(kp + 32 * ds) : z8;
         }
         const uint16_t* vp = vb + (size_t)(s0 / kKStep) * kHD * kKStep + (size_t)ln * kKStep + 8 * grp;
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt) vf[dt] = load_f16x8(vp + (size_t)16 * dt * kKStep);
+        for (int dt = 0; dt < 8; ++dt) vf[dt] = load_kv_f16x8<NT>(vp + (size_t)16 * dt * kKStep);
     };
     // one online-softmax step over the slots s0 .. s0 + 31 from (kf, vf)
     auto step = [&](long long s0, f16x8 (&kf)[2][4], f16x8 (&vf)[8]) {
@@ -701,7 +712,10 @@ static int32_t step_body(ev_decoder* m, int R, const ev_sampling& sampling, int3
             if ((rc = launch_w4_rope(a, L.p_qkv, H, G, st))) return rc;
         }
         AttnArgs aa{q, kcl, vcl, att, R, NH, NKV, m->C, L.chunk, L.nchunk_max, pos, 0.08838834764831845f};
-        hipLaunchKernelGGL(attn_partial_kernel, dim3(L.nchunk_max, NKV, nqt), dim3(64), 0, st, aa);
+        if (nqt == 1)
+            hipLaunchKernelGGL(attn_partial_kernel<true>, dim3(L.nchunk_max, NKV, nqt), dim3(64), 0, st, aa);
+        else
+            hipLaunchKernelGGL(attn_partial_kernel<false>, dim3(L.nchunk_max, NKV, nqt), dim3(64), 0, st, aa);
         if ((rc = check_hip(hipGetLastError(), "attn_partial launch"))) return rc;
         hipLaunchKernelGGL(attn_merge_kernel, dim3(R, NH), dim3(kHD * kMergeGroups), 0, st, att, NH, L.chunk,
                            L.nchunk_max, pos, o);
