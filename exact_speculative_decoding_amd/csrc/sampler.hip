@@ -9,10 +9,11 @@
 //
 // Two launches per call, neither depending on R except through the grid's row
 // dimension (each row is processed by its own workgroups, identically):
-//   topk_chunk_kernel   grid (ceil(V/8192), R) x 256: each workgroup selects
-//                       the top-kk of its 8192 logits under (logit desc, id asc)
-//                       by kk rounds of a block-wide max of 64-bit order keys
-//                       (DPP/swizzle wave max + a 4-way LDS merge);
+//   topk_chunk_kernel   grid (ceil(V/4096), R) x 256: each workgroup selects
+//                       the top-kk of its 4096 logits under (logit desc, id asc)
+//                       as 64-bit order keys: each wave takes its own top-kk
+//                       by kk rounds of a DPP wave maximum, and the four lists
+//                       are merged by counting larger keys;
 //   merge_sample_kernel grid R x 64: one wave merges the chunk lists into the
 //                       row's top-kk, then top-p and the keyed argmax in fp64.
 // The selection involves no arithmetic, so it is exact; the fp64 stage follows
@@ -64,42 +65,99 @@ __device__ __forceinline__ void sort16_desc(unsigned long long (&k)[kPer]) {
             }
 }
 
-// The chunk's top-kk keys in order (kk rounds): every thread sorts its 16
-// keys once; a round takes the block maximum of the threads' heads, and the
-// thread that held it shifts its list (no scan in a round).
+// Maximum of a 32-bit value over the wave (DPP steps as in wave_max_u64),
+// returned to every lane.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    uint32_t o;
+    o = __builtin_amdgcn_update_dpp(v, v, 0x111, 0xf, 0xf, false);  // row_shr:1
+    v = o > v ? o : v;
+    o = __builtin_amdgcn_update_dpp(v, v, 0x112, 0xf, 0xf, false);  // row_shr:2
+    v = o > v ? o : v;
+    o = __builtin_amdgcn_update_dpp(v, v, 0x114, 0xf, 0xf, false);  // row_shr:4
+    v = o > v ? o : v;
+    o = __builtin_amdgcn_update_dpp(v, v, 0x118, 0xf, 0xf, false);  // row_shr:8
+    v = o > v ? o : v;
+    o = __builtin_amdgcn_update_dpp(v, v, 0x142, 0xa, 0xf, false);  // row_bcast:15
+    v = o > v ? o : v;
+    o = __builtin_amdgcn_update_dpp(v, v, 0x143, 0xc, 0xf, false);  // row_bcast:31
+    v = o > v ? o : v;
+    return __builtin_amdgcn_readlane(v, 63);
+}
+// The wave's largest 64-bit key: the largest high word, then the largest low
+// word among the lanes that hold it (the lexicographic order of the pair).
+__device__ __forceinline__ unsigned long long wave_max_key(unsigned long long k) {
+    const uint32_t hi = (uint32_t)(k >> 32);
+    const uint32_t mh = wave_max_u32(hi);
+    const uint32_t ml = wave_max_u32(hi == mh ? (uint32_t)k : 0u);
+    return ((unsigned long long)mh << 32) | ml;
+}
+// Entries of the descending list l[0..n) greater than e.
+__device__ __forceinline__ int count_greater(const unsigned long long* l, int n, unsigned long long e) {
+    int lo = 0, hi = n;
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (l[mid] > e)
+            lo = mid + 1;
+        else
+            hi = mid;
+    }
+    return lo;
+}
+
+// The chunk's top-kk keys in order.  Every thread sorts its 16 keys once and
+// keeps keys 1..15 in LDS.  Each wave then takes its own top-kk in kk rounds
+// of a wave maximum over the threads' heads (no barrier; the lane that held
+// the winner reads its next key).  The chunk's top-kk lies in the union of
+// the four wave lists, and a candidate's place is the number of larger keys
+// in the four lists (binary search in the other three): keys are unique, so
+// the places of the chunk's top-kk are 0..kk-1 and every other candidate's
+// place is kk or more.
 __global__ __launch_bounds__(kSThreads) void topk_chunk_kernel(const float* __restrict__ logits,
                                                                int V, int kk, int nchunk,
                                                                unsigned long long* __restrict__ out) {
-    __shared__ unsigned long long wbest[kSThreads / 64];
-    __shared__ unsigned long long sel[EV_MAX_TOPK];  // the chunk's winners, in order
-    const int r = blockIdx.y, chunk = blockIdx.x;
+    constexpr int kW = kSThreads / 64;
+    __shared__ unsigned long long rest[kPer - 1][kSThreads];  // thread t's keys 1..15 in column t
+    __shared__ unsigned long long wl[kW][EV_MAX_TOPK];       // each wave's top-kk, in order
+    __shared__ unsigned long long sel[EV_MAX_TOPK];          // the chunk's top-kk, in order
+    const int r = blockIdx.y, chunk = blockIdx.x, tid = threadIdx.x;
     const int base = chunk * kChunk;
     const float* row = logits + (size_t)r * V;
     unsigned long long keys[kPer];
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
-        const int idx = base + i * kSThreads + threadIdx.x;
+        const int idx = base + i * kSThreads + tid;
         keys[i] = idx < V ? order_key(row[idx], idx) : 0ull;
     }
     sort16_desc(keys);
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+#pragma unroll
+    for (int i = 1; i < kPer; ++i) rest[i - 1][tid] = keys[i];
+    if (tid < kk) sel[tid] = 0ull;  // places past the chunk's real keys stay 0
+    const int wave = tid >> 6, lane = tid & 63;
+    unsigned long long head = keys[0];
+    int at = 0;
     for (int round = 0; round < kk; ++round) {
-        const unsigned long long w = wave_max_u64(keys[0]);
-        if (lane == 0) wbest[wave] = w;
-        __syncthreads();
-        unsigned long long win = wbest[0];
+        const unsigned long long w = wave_max_key(head);
+        if (lane == 0) wl[wave][round] = w;
+        if (w != 0ull && head == w) {  // keys are unique: one lane
+            ++at;
+            head = at < kPer ? rest[at - 1][tid] : 0ull;
+        }
+    }
+    __syncthreads();
+    if (tid < kW * kk) {
+        const int v = tid / kk, i = tid - v * kk;
+        const unsigned long long e = wl[v][i];
+        if (e != 0ull) {
+            int place = i;
 #pragma unroll
-        for (int i = 1; i < kSThreads / 64; ++i) win = wbest[i] > win ? wbest[i] : win;
-        __syncthreads();
-        if (threadIdx.x == 0) sel[round] = win;
-        const bool pop = win != 0ull && keys[0] == win;  // keys are unique: one thread
-#pragma unroll
-        for (int i = 0; i < kPer - 1; ++i) keys[i] = pop ? keys[i + 1] : keys[i];
-        keys[kPer - 1] = pop ? 0ull : keys[kPer - 1];
+            for (int u = 0; u < kW; ++u)
+                if (u != v) place += count_greater(wl[u], kk, e);
+            if (place < kk) sel[place] = e;
+        }
     }
     __syncthreads();
     unsigned long long* dst = out + ((size_t)r * nchunk + chunk) * kk;
-    if (threadIdx.x < kk) dst[threadIdx.x] = sel[threadIdx.x];
+    if (tid < kk) dst[tid] = sel[tid];
 }
 
 struct SampleArgs {
