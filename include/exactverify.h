@@ -19,7 +19,8 @@
  * Conventions for every entry point
  *   - Pointers marked (device) are device memory on the current HIP device;
  *     (host) pointers are read before the call returns.  The caller allocates and
- *     owns every buffer; the library never allocates in these calls.
+ *     owns every buffer; the library allocates device memory in two calls only:
+ *     toy_decoder_create (the handle's rotation table) and ev_w4_timing(1).
  *   - bf16 and fp16 values travel as their raw uint16_t bit patterns.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Calls enqueue work
  *     and return without synchronising; outputs are valid once the stream has
