@@ -71,7 +71,9 @@ def _check(layer, x, rho, gate, up, down, top, G, exact_rows=True):
 
 
 @pytest.mark.parametrize("H,I,E,top,G", [(256, 128, 16, 4, 32), (256, 192, 8, 8, 64),
-                                         (512, 256, 32, 1, 32), (384, 96, 24, 3, 32)])
+                                         (512, 256, 32, 1, 32), (384, 96, 24, 3, 32),
+                                         (256, 128, 256, 8, 32),  # the most experts and the largest top
+                                         (256, 96, 100, 6, 32)])  # experts filling part of the last wave
 @pytest.mark.parametrize("R", [1, 5, 16])
 def test_small_moe_parity_and_row_exactness(H, I, E, top, G, R):
     g = np.random.default_rng(H * 7 + I + E + top + G)
