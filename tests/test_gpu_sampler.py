@@ -22,6 +22,8 @@ CASES = [  # V, T, top_k, top_p
     (512, 0.0, 20, 0.95), (8192, 0.7, 64, 1.0), (8193, 1.0, 1, 0.5), (32768, 0.7, 20, 0.95),
     (32768, 0.0, 1, 1.0), (151936, 0.7, 20, 0.95), (151936, 1.0, 20, 0.95),
     (151936, 0.0, 20, 0.95), (262144, 2.0, 64, 0.3), (1000, 0.05, 10, 0.99),
+    (4096, 100.0, 64, 1.0),    # nearly flat: the keyed noise decides
+    (151936, 0.7, 64, 1e-9),   # top-p keeps the best candidate only
 ]
 
 
