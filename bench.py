@@ -38,8 +38,8 @@ HBM_PEAK_GBS = 8000.0
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--R", type=int, default=16)
     ap.add_argument("--copies", type=int, default=4, help="weight copies rotated per step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -122,6 +122,20 @@ def cpu_baseline(d, R):
             "one_thread": {"value": round(nb / dt1 / 1e9, 4), "seconds": round(dt1, 2),
                            "ms_per_row": round(1e3 * dt1 / R, 1)},
             "cpu_model": cpu_model()}
+
+
+def cpu_sampler(syn, R=16, V=151936):
+    """The oracle's keyed sample (top-20, top-p 0.95, T 0.7) of R rows of
+    the LM head's vocabulary, per row."""
+    import numpy as np
+    import oracle
+    g = np.random.default_rng(1003)
+    logits = syn.logits(g, R, V, scale=3.0)
+    pos = np.arange(R, dtype=np.int64)
+    t0 = time.perf_counter()
+    oracle.sample_rows(logits, pos, 0.7, 20, 0.95, 42)
+    dt = time.perf_counter() - t0
+    return {"kind": "oracle", "ms_per_row": round(1e3 * dt / R, 2), "rows": R, "V": V}
 
 
 def stream_ceiling(ev, dev, stream, reps=20):
@@ -225,7 +239,7 @@ def leg_moe(ev, syn, to_dev, stream, steps):
     return {"workload": "MoE layer H2048 E128 top8 I768 W4 G32", "per_R": out}
 
 
-def leg_decoder(ev, syn, C, n_tokens=512, R=8, p_draft=0.65):
+def leg_decoder(ev, syn, C, n_tokens=512, R=8, p_draft=0.65, cpu_steps=0):
     """The 8-layer decoder: serial decoding (R = 1) of n_tokens, then drafted
     decoding with R - 1 drafts a round that match the serial transcript with
     probability p_draft; exact accepted tok/s = committed tokens / wall time
@@ -261,13 +275,26 @@ def leg_decoder(ev, syn, C, n_tokens=512, R=8, p_draft=0.65):
     per_round = n_tokens / rounds
     roof = per_round * HBM_PEAK_GBS * 1e9 / (w_bytes + kv_round)
     tps = n_tokens / t_drafted
+    cpu = None
+    if cpu_steps:  # the oracle's serial steps from the same start, on the host cores
+        import oracle
+        om = oracle.Decoder(cfg, d["w"], d["kc"], d["vc"])
+        tok = d["first_token"]
+        t0 = time.perf_counter()
+        for i in range(cpu_steps):
+            _, tok, _ = om.step(tok, pos0 + i, *samp)
+        dt = time.perf_counter() - t0
+        cpu = {"kind": "oracle", "tokens": cpu_steps, "ms_per_token": round(1e3 * dt / cpu_steps, 1),
+               "tok_s": round(cpu_steps / dt, 3), "cores": int(oracle.num_threads()),
+               "sample": f"{cpu_steps} serial steps of the 8-layer decoder, cache {C}"}
     return {"workload": f"8-layer decoder H2048 16/4 heads MLP6144 V32768 W4 G64, cache {C}",
             "tokens": n_tokens, "R": R, "draft_match": p_draft, "rounds": rounds,
             "tokens_per_round": round(per_round, 3), "identical_to_serial": drafted == serial,
             "accepted_tok_s": round(tps, 1), "serial_tok_s": round(n_tokens / t_serial, 1),
             "ms_per_round": round(1e3 * t_drafted / rounds, 3),
             "bytes_per_round": int(w_bytes + kv_round),
-            "roofline_tok_s": round(roof, 1), "pct_roofline": round(100 * tps / roof, 2)}
+            "roofline_tok_s": round(roof, 1), "pct_roofline": round(100 * tps / roof, 2),
+            **({"cpu_baseline": cpu} if cpu else {})}
 
 
 def main():
@@ -436,7 +463,7 @@ def main():
         print("# lm head leg done", file=sys.stderr, flush=True)
         legs["moe_layer"] = leg_moe(ev, syn, to_dev, stream, args.steps)
         print("# moe leg done", file=sys.stderr, flush=True)
-        legs["decoder_4096"] = leg_decoder(ev, syn, 4096)
+        legs["decoder_4096"] = leg_decoder(ev, syn, 4096, cpu_steps=0 if args.no_cpu_baseline else 3)
         print("# decoder leg (cache 4096) done", file=sys.stderr, flush=True)
         legs["decoder_32768"] = leg_decoder(ev, syn, 32768)
         print("# decoder leg (cache 32768) done", file=sys.stderr, flush=True)
@@ -444,6 +471,9 @@ def main():
         out["exact_accepted_tok_s"] = legs["decoder_4096"]["accepted_tok_s"]
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(d, R)
+        out["cpu_baseline"]["sampler"] = cpu_sampler(syn)
+        if "decoder_4096" in out.get("legs", {}):
+            out["cpu_baseline"]["decoder_4096"] = out["legs"]["decoder_4096"].pop("cpu_baseline")
     print(json.dumps(out), flush=True)
 
 
