@@ -39,7 +39,7 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--R", type=int, default=16)
     ap.add_argument("--copies", type=int, default=4, help="weight copies rotated per step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
