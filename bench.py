@@ -200,7 +200,7 @@ def leg_lm_head(ev, syn, to_dev, stream, steps):
         def step(i):
             ev.verify_linear_w4(h[:R], copies[i % 2], y=y[:R], ws=ws, stream=stream)
             ev.keyed_sample(y[:R], pos, 0.7, 20, 0.95, 42, tokens=tok[:R], ws=sws, stream=stream)
-        ms = _event_time(stream, step, steps, 3)
+        ms = _event_time(stream, step, steps, 100)  # ~10 ms: the part's steady rate
         by = V * K * 0.5 + 4.0 * V * (K // G) + 2.0 * R * K + 4.0 * R * V * 2  # logits written + read
         out[str(R)] = {"us_per_pass": round(ms * 1e3, 2), "GB_s": round(by / (ms * 1e-3) / 1e9, 1),
                        "pct_hbm_peak": round(100 * by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 1),
@@ -229,7 +229,7 @@ def leg_moe(ev, syn, to_dev, stream, steps):
         def step(i):
             g, u, dn = stacks[i % 2]
             ev.verify_moe_w4(x[:R], rho[:R], g, u, dn, top, y=y[:R], expert_ids=ids[:R], ws=ws, stream=stream)
-        ms = _event_time(stream, step, steps, 3)
+        ms = _event_time(stream, step, steps, 200)  # ~10 ms: the part's steady rate
         touched = len(np.unique(ids[:R].cpu().numpy()))
         by = touched * per_expert + 2.0 * R * H + 4.0 * R * H
         out[str(R)] = {"us_per_pass": round(ms * 1e3, 2), "experts": touched,
@@ -413,7 +413,7 @@ def main():
     per_r = {}
     if not args.no_sweep:
         for r in (1, 2, 4, 8, 16):
-            m = timed(r, args.steps, 3)
+            m = timed(r, args.steps, 20)
             g = mlp_bytes(r, H, I, G) / (m * 1e-3) / 1e9
             per_r[str(r)] = {"us_per_pass": round(m * 1e3, 2), "GB_s": round(g, 1),
                              "pct_hbm_peak": round(100 * g / HBM_PEAK_GBS, 1),
