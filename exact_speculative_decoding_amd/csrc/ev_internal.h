@@ -42,6 +42,15 @@ __device__ __forceinline__ uint16_t f32_to_f16_bits(float v) {
     return __builtin_bit_cast(uint16_t, (_Float16)v);
 }
 
+// fp32 -> fp16 bits for a cache entry: clamped to the finite range (+-65504)
+// first, then rounded to nearest even, so that no entry is ever infinite (an
+// infinite value in a slot that a row masks out with weight 0 would turn the
+// row's sum into NaN).
+__device__ __forceinline__ uint16_t f32_to_f16_sat(float v) {
+    const float c = fabsf(v) > 65504.f ? copysignf(65504.f, v) : v;
+    return f32_to_f16_bits(c);
+}
+
 // fp16 bits -> fp32 (exact) via the hardware conversion.
 __device__ __forceinline__ float f16_to_f32(uint16_t h) {
     _Float16 v = __builtin_bit_cast(_Float16, h);

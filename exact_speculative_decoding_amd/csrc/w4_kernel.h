@@ -6,34 +6,19 @@
 #include "ev_internal.h"
 #include "w4_layout.h"
 
-#ifndef EV_W4_NT
-#define EV_W4_NT 2  // 16-row tiles per wave
-#endif
-#ifndef EV_W4_PD
-#define EV_W4_PD 2  // chunks of loads in flight per wave
-#endif
-#ifndef EV_W4_TARGET_WAVES
-#define EV_W4_TARGET_WAVES 4096
-#endif
-#ifndef EV_W4_MIN_CPS
-#define EV_W4_MIN_CPS 4  // at least this many chunks (one superchunk) per K-split when K allows
-#endif
-
 namespace ev {
 
 int32_t check_w4_dims(const char* who, int K, int N, int G);
 
-#ifndef EV_W4_WAVES
-#define EV_W4_WAVES 4
-#endif
-constexpr int kWaves = EV_W4_WAVES;  // waves per workgroup, sharing one activation slab
+// Tuning constants of the W4 launches (each measured against its neighbours
+// on the MLP slice, the LM head and the decoder's matrices).
+constexpr int kWaves = 4;            // waves per workgroup, sharing one activation slab
 constexpr int kThreads = 64 * kWaves;
-constexpr int kNT = EV_W4_NT;
-constexpr int kPD = EV_W4_PD;
-#ifndef EV_W4_SC
-#define EV_W4_SC 2
-#endif
-constexpr int kSC = EV_W4_SC;  // chunks per activation superchunk (staged in LDS together)
+constexpr int kNT = 2;               // 16-row tiles per wave
+constexpr int kPD = 2;               // chunks of weight loads in flight per wave
+constexpr int kSC = 2;               // chunks per activation superchunk (staged in LDS together)
+constexpr long kTargetWaves = 4096;  // waves a split plan aims at (four per SIMD)
+constexpr int kMinCps = 4;           // at least this many chunks per K-split when K allows
 
 struct W4Plan {
     int S;        // K-splits
@@ -50,8 +35,8 @@ inline W4Plan plan_w4(int N, int K, int nmat) {
     p.nchunks = w4_chunks(K);
     p.ncg = (w4_tiles(N) + kNT - 1) / kNT;
     const long base = (long)p.ncg * nmat;
-    long S = (EV_W4_TARGET_WAVES + base - 1) / base;
-    long smax = p.nchunks / EV_W4_MIN_CPS;
+    long S = (kTargetWaves + base - 1) / base;
+    long smax = p.nchunks / kMinCps;
     if (smax < 1) smax = 1;
     if (S > smax) S = smax;
     if (S < 1) S = 1;
@@ -74,16 +59,7 @@ inline W4Plan plan_w4(int N, int K, int nmat) {
 // touches, at slot w * segmax + (block - first block of the run).  All of it
 // follows from (N, K, nmat), never from R.
 constexpr int kBlockCols = kWaves * kNT * 16;
-#ifndef EV_W4_SK_CUS
-#define EV_W4_SK_CUS 256
-#endif
-#ifndef EV_W4_SK_PER_CU
-#define EV_W4_SK_PER_CU 3
-#endif
-constexpr int kSkWGs = EV_W4_SK_CUS * EV_W4_SK_PER_CU;
-#ifndef EV_W4_SK
-#define EV_W4_SK 1
-#endif
+constexpr int kSkWGs = 256 * 3;  // three workgroups on each of the 256 CUs
 struct SkPlan {
     int nsc;     // superchunks per column block
     int ncgb;    // column blocks per matrix
@@ -108,7 +84,7 @@ inline SkPlan plan_w4_sk(int N, int K, int nmat) {
 // A plain launch runs balanced when its split plan would need partial rows
 // anyway (S > 1); a launch whose columns alone fill the chip (S == 1, as the
 // LM head) writes its outputs directly and needs no second kernel.
-inline bool use_sk(const SkPlan& q, const W4Plan& p) { return EV_W4_SK && q.ok && p.S > 1; }
+inline bool use_sk(const SkPlan& q, const W4Plan& p) { return q.ok && p.S > 1; }
 inline size_t sk_part_bytes(const SkPlan& p) { return (size_t)p.nwg * p.segmax * 16 * kBlockCols * sizeof(float); }
 
 // Geometry of a balanced launch, as the kernels that add its segments need it.
@@ -227,7 +203,7 @@ int32_t launch_w4_rope(W4Args args, const W4Plan& p, int K, int G, hipStream_t s
 // A dense gate/up pair (I x H each) runs paired when its tiles alone give the
 // target wave count; otherwise as a split launch of both matrices followed by
 // silu_reduce, whose extra split waves outweigh the partial rows.
-inline bool use_pair(int I) { return 2l * w4_tiles(I) >= EV_W4_TARGET_WAVES; }
+inline bool use_pair(int I) { return 2l * w4_tiles(I) >= kTargetWaves; }
 
 // y[r][n] = sum over s ascending of part[s][r][n] (split stride 16 * N), r < R.
 int32_t launch_splitk_reduce(const float* part, int S, int N, int R, float* y, hipStream_t st);

@@ -35,14 +35,10 @@ __host__ __device__ inline size_t w4_blob_bytes(int N, int K, int G) {
     return (size_t)w4_tiles(N) * (size_t)w4_chunks(K) * (size_t)w4_chunk_bytes(G);
 }
 
-#ifndef EV_W4_CHUNK_MAJOR
-#define EV_W4_CHUNK_MAJOR 1
-#endif
-// Byte offset of tile-chunk (tile, c) in the blob: tile-major (a tile's chunks
-// are adjacent) or chunk-major (a chunk's tiles are adjacent).
-__host__ __device__ inline size_t w4_tc_offset(long tile, int c, int tiles, int nchunks, int G) {
-    return (EV_W4_CHUNK_MAJOR ? ((size_t)c * tiles + tile) : ((size_t)tile * nchunks + c)) *
-           (size_t)w4_chunk_bytes(G);
+// Byte offset of tile-chunk (tile, c) in the blob: chunk-major (a chunk's
+// tiles are adjacent).
+__host__ __device__ inline size_t w4_tc_offset(long tile, int c, int tiles, int G) {
+    return ((size_t)c * tiles + tile) * (size_t)w4_chunk_bytes(G);
 }
 
 }  // namespace ev

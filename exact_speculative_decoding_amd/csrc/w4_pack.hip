@@ -35,7 +35,7 @@ __global__ void w4_pack_kernel(const uint8_t* __restrict__ q, const uint16_t* __
     const int ln = L & 15, j = L >> 4;
     const long n = tile * 16 + ln;
     const int GPC = kKC / G;
-    uint8_t* dst = out + w4_tc_offset(tile, c, w4_tiles(N), NC, G);
+    uint8_t* dst = out + w4_tc_offset(tile, c, w4_tiles(N), G);
     const size_t Kh = (size_t)K / 2;
     u32x4 w = {0u, 0u, 0u, 0u};
 #pragma unroll

@@ -207,10 +207,9 @@ __device__ __forceinline__ void w4_block(const W4Args& a, long blk, uint8_t (*xl
     for (int t = 0; t < kNT; ++t) {
         const int tile = MODE == kPairMode ? cg : (MODE == kRopeMode ? 8 * cgb + wv + 4 * t : cg * kNT + t);
         tok[t] = tile < a.tiles;
-        tbase[t] = tok[t] ? (EV_W4_CHUNK_MAJOR ? (uint32_t)tile * CB : (uint32_t)tile * (uint32_t)a.nchunks * CB)
-                          : 0u;
+        tbase[t] = tok[t] ? (uint32_t)tile * CB : 0u;
     }
-    const uint32_t cstride = EV_W4_CHUNK_MAJOR ? (uint32_t)a.tiles * CB : CB;  // bytes per chunk step
+    const uint32_t cstride = (uint32_t)a.tiles * CB;  // bytes per chunk step (chunk-major tiles)
     const uint32_t vq = 16u * lane;
     const uint32_t vsb = 1024u + 4u * GPC * ln;
     // the mask stays scalar, the or-constant goes to a vector register: gfx9
@@ -381,15 +380,15 @@ __device__ __forceinline__ void w4_block(const W4Args& a, long blk, uint8_t (*xl
                         q[d + 64] = b2;
                     } else {
                         uint16_t* k = a.rope.kc + ((size_t)(hd - a.rope.NH) * a.rope.C + P) * 128;
-                        k[d] = f32_to_f16_bits(a2);
-                        k[d + 64] = f32_to_f16_bits(b2);
+                        k[d] = f32_to_f16_sat(a2);
+                        k[d + 64] = f32_to_f16_sat(b2);
                     }
                 } else {
                     const int g = hd - a.rope.NH - a.rope.NKV;
                     uint16_t* v = a.rope.vc + (size_t)g * a.rope.C * 128 + (size_t)(P / 32) * 128 * 32 +
                                   vslot_pos32((int)(P % 32));
-                    v[(size_t)d * 32] = f32_to_f16_bits(va);
-                    v[(size_t)(d + 64) * 32] = f32_to_f16_bits(vb);
+                    v[(size_t)d * 32] = f32_to_f16_sat(va);
+                    v[(size_t)(d + 64) * 32] = f32_to_f16_sat(vb);
                 }
             }
         }
@@ -454,7 +453,6 @@ __device__ __forceinline__ void w4_sk_block(const W4Args& a, int w, uint8_t (*xl
     constexpr int SBW = GPC;
     constexpr uint32_t CB = 1024 + 64 * GPC;
     static_assert(kSC % kPD == 0, "ring depth must divide the superchunk");
-    static_assert(EV_W4_CHUNK_MAJOR, "the balanced walk steps chunk-major tiles");
 
     const int U = a.sk_units, nwg = a.sk_nwg, nsc = a.sk_nsc;
     const int u0 = (int)((unsigned)w * (unsigned)U / (unsigned)nwg);
@@ -912,10 +910,8 @@ static void prep_w4(W4Args& args, int nmat, const W4Plan& p, int K, int G, int n
 // Launches that stream at least kNtBytes of weights load them with the
 // non-temporal hint; smaller ones (the decoder's per-layer matrices, read
 // again every round) load them plainly.
-#ifndef EV_W4_NT_BYTES
-#define EV_W4_NT_BYTES (32.0 * (1 << 20))
-#endif
-static bool stream_hint(double weight_bytes) { return weight_bytes >= EV_W4_NT_BYTES; }
+constexpr double kNtBytes = 32.0 * (1 << 20);
+static bool stream_hint(double weight_bytes) { return weight_bytes >= kNtBytes; }
 
 // Timing slots for a launch of `blocks` workgroups moving `bytes` algorithmic
 // bytes, or NULL when the hook is off.

@@ -63,6 +63,7 @@ def _declare(L):
     L.ov_silu.restype = f64
     L.ov_w4_linear.argtypes = [_p(u16), i32, i32, _p(u8), _p(u16), _p(u16), i32, i32, _p(f64)]
     L.ov_w4_linear_f32.argtypes = [_p(u16), i32, i32, _p(u8), _p(u16), _p(u16), i32, i32, _p(f32)]
+    L.ov_w4_linear_fp32.argtypes = [_p(u16), i32, i32, _p(u8), _p(u16), _p(u16), i32, i32, _p(f32)]
     L.ov_silu_mul_bf16.argtypes = [_p(f32), _p(f32), C.c_size_t, _p(u16)]
     L.ov_mlp.argtypes = [_p(u16), i32, i32, i32, i32,
                          _p(u8), _p(u16), _p(u16), _p(u8), _p(u16), _p(u16),
@@ -179,6 +180,19 @@ def w4_linear(x, q, s, b, G, out_f32=False):
         y = np.empty((R, N), np.float64)
         L.ov_w4_linear(ptr(x, np.uint16), R, K, ptr(q, np.uint8), ptr(s, np.uint16),
                        ptr(b, np.uint16), N, G, ptr(y, np.float64))
+    return y
+
+
+def w4_linear_fp32(x, q, s, b, G):
+    """The linear evaluated in fp32 arithmetic, two-level order (per group in
+    ascending k, then the groups in ascending order) -> y [R][N] fp32."""
+    x, q, s, b = _c(x, np.uint16), _c(q, np.uint8), _c(s, np.uint16), _c(b, np.uint16)
+    R, K = x.shape
+    N = q.shape[0]
+    assert q.shape == (N, K // 2) and s.shape == (N, K // G) and b.shape == s.shape
+    y = np.empty((R, N), np.float32)
+    lib().ov_w4_linear_fp32(ptr(x, np.uint16), R, K, ptr(q, np.uint8), ptr(s, np.uint16),
+                            ptr(b, np.uint16), N, G, ptr(y, np.float32))
     return y
 
 
@@ -301,4 +315,4 @@ def moe(x, rho, top, G, gate, up, down):
 
 # --- decoder (oracle/decoder.c) ---------------------------------------------
 
-from .decoder import Decoder, attend, rmsnorm_bf16, rope  # noqa: E402,F401
+from .decoder import Decoder, attend, drafted_decode, rmsnorm_bf16, rope, serial_decode  # noqa: E402,F401

@@ -19,8 +19,9 @@
  *     turned by the angle p * base^(-2i/d); cos and sin in double, rounded to
  *     fp32, the rotated values rounded to fp32;
  *   * query head h reads key/value head h / (heads / kv_heads);
- *   * keys and values are stored in fp16 (RNE) at slot p of the cache, and the
- *     token at slot p attends to slots 0..p;
+ *   * keys and values are stored in fp16 (RNE, saturating: a value beyond the
+ *     largest finite fp16, 65504, is stored as +-65504, never as infinity) at
+ *     slot p of the cache, and the token at slot p attends to slots 0..p;
  *   * scores q.k / sqrt(d), softmax, output sum_j pi_j v_j, all in double; the
  *     output is rounded to bf16 as the o projection's input;
  *   * the residual stream is fp32: each linear output is rounded to fp32, then
@@ -54,6 +55,15 @@ typedef struct {
 } ov_sample_out;
 void ov_sample_row(const float* l, int V, int64_t pos, double T, int top_k,
                    double top_p, uint64_t seed, ov_sample_out* out);
+
+/* A cache entry: fp16 by round-to-nearest-even, clamped to the finite range
+ * first, so that a large key or value stays finite. */
+static uint16_t f16_saturating(double v)
+{
+    if (v > 65504.0) v = 65504.0;
+    if (v < -65504.0) v = -65504.0;
+    return ov_f64_to_f16(v);
+}
 
 /* RMSNorm of an fp32 vector with fp32 gains, rounded to bf16. */
 void ov_rmsnorm_bf16(const float* x, int H, const float* gain, double eps, uint16_t* out)
@@ -156,8 +166,8 @@ void ov_decoder_step(const int32_t* ci, const double* cd, const void* const* w,
             ov_rope(k, D, p, base);
             size_t slot = (((size_t)l * NKV + g) * C + (size_t)p) * D;
             for (int i = 0; i < D; i++) {
-                kc[slot + i] = ov_f64_to_f16(k[i]);
-                vc[slot + i] = ov_f64_to_f16(v[i]);
+                kc[slot + i] = f16_saturating(k[i]);
+                vc[slot + i] = f16_saturating(v[i]);
             }
         }
         for (int h = 0; h < NH; h++) {

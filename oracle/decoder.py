@@ -90,3 +90,48 @@ class Decoder:
                                int(seed) & ((1 << 64) - 1), _ptr(logits, np.float32),
                                _ptr(tok, np.int32), _ptr(gap, np.float64))
         return logits, int(tok[0]), float(gap[0])
+
+
+def serial_decode(m, first_token, slot0, n, sampling):
+    """Serial decoding on the oracle decoder `m`: `first_token` sits at slot
+    `slot0`; each step feeds the last token at the next slot and keeps the
+    token it samples.  Returns the n sampled tokens."""
+    out, tok = [], int(first_token)
+    for i in range(n):
+        _, tok, _ = m.step(tok, slot0 + i, *sampling)
+        out.append(tok)
+    return out
+
+
+def drafted_decode(m, first_token, slot0, n, R, drafter, sampling):
+    """Drafted decoding on the oracle decoder, one row at a time (the accept
+    rule of the TensorFold README's exactness paragraph: a draft is kept
+    exactly when it equals the token sampled at its position).
+
+    The stream s holds the committed tokens after `first_token`; with L tokens
+    committed before a round (the last input at slot slot0 + L), the round's
+    rows are the inputs [last, d_0, .., d_{W-2}] at slots slot0 + L + r, W =
+    min(R, n - L) and drafter(position, count) giving the drafts for the
+    positions after the last input.  Each row is one serial oracle step.  With
+    a the number of leading drafts equal to the samples before them, the round
+    keeps samples 0..min(a + 1, W) - 1, and the cache slots the rejected rows
+    wrote are put back as they were before the round.  Returns (tokens,
+    rounds)."""
+    from . import accept
+    s, rounds = [], 0
+    last = int(first_token)
+    while len(s) < n:
+        L = len(s)
+        W = min(R, n - L)
+        base = slot0 + L
+        drafts = [int(t) for t in drafter(base + 1, W - 1)]
+        inputs = [last] + drafts
+        kc0, vc0 = m.kc[:, :, base:base + W].copy(), m.vc[:, :, base:base + W].copy()
+        samples = [m.step(t, base + r, *sampling)[1] for r, t in enumerate(inputs)]
+        _, keep = accept(np.array(samples, np.int32), np.array(drafts, np.int32))
+        m.kc[:, :, base + keep:base + W] = kc0[:, :, keep:]
+        m.vc[:, :, base + keep:base + W] = vc0[:, :, keep:]
+        s.extend(samples[:keep])
+        last = samples[keep - 1]
+        rounds += 1
+    return s, rounds

@@ -195,6 +195,41 @@ void ov_w4_linear_f32(const uint16_t* x, int R, int K, const uint8_t* q,
     free(t);
 }
 
+/* The same linear evaluated in fp32, in the two-level order of its groups:  */
+/* w = fl(fl(s * q) + b); per group g, p_g = the fp32 sum of fl(w * x) over   */
+/* the group's k in ascending order, from 0; y = the fp32 sum of the p_g in   */
+/* ascending g.  Every operation is one binary32 operation (no contraction). */
+/* This is the fp32 form of the definition; ov_w4_linear (fp64, one rounding */
+/* at the output) decides when it and another fp32 evaluation disagree.      */
+void ov_w4_linear_fp32(const uint16_t* x, int R, int K, const uint8_t* q,
+                       const uint16_t* s, const uint16_t* b, int N, int G, float* y)
+{
+    int ng = K / G;
+    float* xf = (float*)malloc(sizeof(float) * (size_t)K);
+    for (int r = 0; r < R; r++) {
+        for (int k = 0; k < K; k++)
+            xf[k] = (float)ov_bf16_to_f64(x[(size_t)r * K + k]);
+#pragma omp parallel for schedule(static)
+        for (int n = 0; n < N; n++) {
+            float total = 0.0f;
+            for (int g = 0; g < ng; g++) {
+                float sc = (float)ov_f16_to_f64(s[(size_t)n * ng + g]);
+                float bi = (float)ov_f16_to_f64(b[(size_t)n * ng + g]);
+                float part = 0.0f;
+                for (int k = g * G; k < (g + 1) * G; k++) {
+                    float sq = sc * (float)q_at(q, K, n, k);
+                    float w = sq + bi;
+                    float wx = w * xf[k];
+                    part = part + wx;
+                }
+                total = total + part;
+            }
+            y[(size_t)r * N + n] = total;
+        }
+    }
+    free(xf);
+}
+
 /* ------------------------------------------------------------------------- */
 /* SiLU-gated MLP glue: h = bf16(silu(g) * u), silu(v) = v / (1 + e^-v).      */
 /* ------------------------------------------------------------------------- */

@@ -27,7 +27,6 @@ from scipy.special import expit
 
 import oracle
 import synthetic as syn
-from exact_speculative_decoding_amd.loop import decode
 
 
 def _f16(bits):
@@ -199,27 +198,66 @@ def test_cache_slot_holds_rotated_key():
 
 # --- drafted == serial ---------------------------------------------------------------
 
-def _oracle_round(m):
-    def fn(tokens, pos0):
-        sampled = [m.step(t, pos0 + r, *SAMPLING)[1] for r, t in enumerate(tokens)]
-        a, n_commit = oracle.accept(np.array(sampled), np.array(tokens[1:], np.int32))
-        return sampled, n_commit
-    return fn
-
-
 def test_drafted_decoding_equals_serial():
+    # the oracle's own round loop (one row at a time, accept rule, rejected
+    # rows' cache slots put back) against its serial loop
     d = syn.tiny_decoder()
     cfg = d["cfg"]
     pos0, n = cfg["prefill"], 40
     serial = oracle.Decoder(cfg, d["w"], d["kc"], d["vc"])
-    ref, rounds = decode(_oracle_round(serial), d["first_token"], pos0, n, 1, lambda p, c: [])
-    assert rounds == n
+    ref = oracle.serial_decode(serial, d["first_token"], pos0, n, SAMPLING)
+    one = oracle.Decoder(cfg, d["w"], d["kc"], d["vc"])
+    got1, rounds1 = oracle.drafted_decode(one, d["first_token"], pos0, n, 1, lambda p, c: [], SAMPLING)
+    assert got1 == ref and rounds1 == n
     V = cfg["vocab"]
-    for R, drafter in ((4, syn.transcript_drafter(ref, pos0 + 1, 0.65, 5, V)),
-                       (3, syn.random_drafter(6, V)), (8, syn.transcript_drafter(ref, pos0 + 1, 0.9, 7, V))):
+    for R, drafter, helps in ((4, syn.transcript_drafter(ref, pos0 + 1, 0.65, 5, V), True),
+                              (3, syn.random_drafter(6, V), False),
+                              (8, syn.transcript_drafter(ref, pos0 + 1, 0.9, 7, V), True)):
         m = oracle.Decoder(cfg, d["w"], d["kc"], d["vc"])
-        got, rounds = decode(_oracle_round(m), d["first_token"], pos0, n, R, drafter)
+        got, rounds = oracle.drafted_decode(m, d["first_token"], pos0, n, R, drafter, SAMPLING)
         assert got == ref
-        L = pos0 + n  # slots 0 .. L - 1 hold committed tokens' keys and values
-        assert np.array_equal(m.kc[:, :, :L], serial.kc[:, :, :L])
-        assert np.array_equal(m.vc[:, :, :L], serial.vc[:, :, :L])
+        assert rounds < n if helps else rounds <= n
+        # committed slots hold the serial bytes; stale slots were put back
+        assert np.array_equal(m.kc, serial.kc)
+        assert np.array_equal(m.vc, serial.vc)
+
+
+def test_drafted_round_count_with_perfect_and_wrong_drafts():
+    # a drafter that always proposes the serial tokens commits R tokens a
+    # round; one that is always wrong commits one token a round
+    d = syn.tiny_decoder()
+    cfg = d["cfg"]
+    pos0, n, V = cfg["prefill"], 24, cfg["vocab"]
+    ref = oracle.serial_decode(oracle.Decoder(cfg, d["w"], d["kc"], d["vc"]), d["first_token"], pos0, n, SAMPLING)
+    good = lambda p, c: [ref[p - pos0 - 1 + i] for i in range(c)]
+    bad = lambda p, c: [(ref[p - pos0 - 1 + i] + 1) % V for i in range(c)]
+    for R in (2, 4, 6):
+        got, rounds = oracle.drafted_decode(oracle.Decoder(cfg, d["w"], d["kc"], d["vc"]), d["first_token"],
+                                            pos0, n, R, good, SAMPLING)
+        assert got == ref and rounds == -(-n // R)
+        got, rounds = oracle.drafted_decode(oracle.Decoder(cfg, d["w"], d["kc"], d["vc"]), d["first_token"],
+                                            pos0, n, R, bad, SAMPLING)
+        assert got == ref and rounds == n
+
+
+def test_cache_entries_saturate_at_the_fp16_limit():
+    # values beyond the largest finite fp16 are stored as +-65504, never inf
+    d = syn.tiny_decoder(layers=1)
+    cfg, w = d["cfg"], dict(d["w"])
+    NH, NKV, D = cfg["heads"], cfg["kv_heads"], cfg["head_dim"]
+    b = np.array(w["qkv_b"], copy=True)
+    rows = slice((NH + NKV) * D, (NH + 2 * NKV) * D)  # the value rows
+    b[0, rows] = syn.fp16_bits(np.full(b[0, rows].shape, 30000.0))
+    w["qkv_b"] = b
+    m = oracle.Decoder(cfg, w, d["kc"], d["vc"])
+    t, pos = 3, 5
+    m.step(t, pos, *SAMPLING)
+    n = oracle.rmsnorm_bf16(syn.bf16_values(w["embed"][t]), w["attn_norm"][0], cfg["eps"])
+    qkv = oracle.w4_linear(n[None], w["qkv_q"][0], w["qkv_s"][0], b[0], cfg["G"], out_f32=True)[0]
+    v = qkv[(NH + NKV) * D:].reshape(NKV, D)
+    assert np.max(np.abs(v)) > 65520  # these would round to infinity
+    stored = _f16(m.vc[0, :, pos])
+    assert np.all(np.isfinite(stored))
+    big = np.abs(v) > 65504
+    assert np.array_equal(stored[big], np.sign(v[big]) * 65504.0)
+    assert np.array_equal(m.vc[0, :, pos][~big], syn.fp16_bits(v[~big]))

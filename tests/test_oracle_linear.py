@@ -118,3 +118,63 @@ def test_mlp_matches_numpy():
     assert np.max(np.abs(hv - h_exact)) <= 2.0 ** -8 * np.max(np.abs(h_exact))
     y_ref = hv @ Wd.T
     assert np.max(np.abs(y - y_ref)) <= 1e-6 * np.max(np.abs(y_ref))
+
+
+# --- the fp32 two-level evaluation (oracle.w4_linear_fp32) ---------------------
+
+@pytest.mark.parametrize("G", [32, 64])
+def test_fp32_mode_exact_integer_case_bitwise(G):
+    # every fp32 product, dequantised weight and partial sum is exact here
+    g = np.random.default_rng(11)
+    R, K, N = 4, 256, 33
+    qv = g.integers(0, 16, (N, K))
+    xi = g.integers(-3, 4, (R, K))
+    bi = g.integers(-8, 9, (N, K // G))
+    x = syn.bf16_bits(xi.astype(np.float32))
+    s = syn.fp16_bits(np.full((N, K // G), 2.0 ** -5))
+    b = syn.fp16_bits(bi * 2.0 ** -10)
+    y = oracle.w4_linear_fp32(x, _pack(qv), s, b, G)
+    w_int = 32 * qv + np.repeat(bi, G, axis=1)
+    ref = (xi.astype(np.int64) @ w_int.T.astype(np.int64)).astype(np.float64) / 1024.0
+    assert np.array_equal(y, ref.astype(np.float32))
+
+
+@pytest.mark.parametrize("G", [32, 64])
+def test_fp32_mode_one_hot_reads_back_fp32_dequant(G):
+    # y = fl32(fl32(s * q) + b): one product and one sum in binary32
+    g = np.random.default_rng(12)
+    K, N = 128, 24
+    qv = g.integers(0, 16, (N, K))
+    s = syn.fp16_bits(g.uniform(0.01, 0.05, (N, K // G)))
+    b = syn.fp16_bits(g.normal(0, 0.1, (N, K // G)))
+    ks = [0, 1, 31, 32, G - 1, G, K - 1]
+    x = np.zeros((len(ks), K), np.float32)
+    for r, k in enumerate(ks):
+        x[r, k] = 1.0
+    y = oracle.w4_linear_fp32(syn.bf16_bits(x), _pack(qv), s, b, G)
+    sv = s.view(np.float16).astype(np.float32)
+    bv = b.view(np.float16).astype(np.float32)
+    for r, k in enumerate(ks):
+        w = (sv[:, k // G] * qv[:, k].astype(np.float32)).astype(np.float32) + bv[:, k // G]
+        assert np.array_equal(y[r], w.astype(np.float32))
+
+
+@pytest.mark.parametrize("R,K,N,G", [(2, 256, 64, 64), (3, 5120, 40, 64), (2, 2048, 32, 32)])
+def test_fp32_mode_within_its_rounding_bound_of_fp64(R, K, N, G):
+    # Every fp32 step rounds once (relative 2^-24): the dequantised weight
+    # twice, each product once, a group's recursive sum at most G - 1 times and
+    # the sum over groups K/G - 1 times, so |y32 - y| <= (G + K/G + 2) 2^-24
+    # sum_k |w x| to first order (the factor 1.01 covers the higher orders).
+    g = np.random.default_rng(K + N)
+    qv = g.integers(0, 16, (N, K))
+    s = syn.fp16_bits(g.uniform(0.01, 0.05, (N, K // G)))
+    b = syn.fp16_bits(g.normal(0, 0.1, (N, K // G)))
+    x = syn.activations(g, R, K)
+    y32 = oracle.w4_linear_fp32(x, _pack(qv), s, b, G).astype(np.float64)
+    y64 = oracle.w4_linear(x, _pack(qv), s, b, G)
+    absum = np.abs(syn.bf16_values(x).astype(np.float64)) @ np.abs(_dequant(qv, s, b, G)).T
+    bound = 1.01 * (G + K // G + 2) * 2.0 ** -24 * absum
+    assert np.all(np.abs(y32 - y64) <= bound)
+    # and far inside the 2e-3 row tolerance the GPU is held to
+    rel = np.max(np.abs(y32 - y64), axis=1) / np.max(np.abs(y64), axis=1)
+    assert np.all(rel < 1e-4)

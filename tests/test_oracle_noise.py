@@ -63,3 +63,27 @@ def test_noise_is_uniform_and_gumbel_distributed():
     # neighbouring positions and tokens are uncorrelated
     assert abs(np.corrcoef(u_pos[:-1], u_pos[1:])[0, 1]) < 0.03
     assert abs(np.corrcoef(u_tok[:-1], u_tok[1:])[0, 1]) < 0.03
+
+
+def _spec_vectors():
+    out = []
+    with open(os.path.join(HERE, "golden", "keyed_noise_spec.txt")) as f:
+        for line in f:
+            if line.strip() and not line.startswith("#"):
+                s, p, t, k, h, u, g = line.split()
+                out.append((int(s), int(p), int(t), int(k, 16), int(h, 16), float(u), float(g)))
+    return out
+
+
+def test_keyed_noise_spec_vectors():
+    # the fixture's seeds 42 and 1234 go through the inner mix64(seed), which
+    # the seed-0 pins above cannot see (mix64(0) == 0)
+    vecs = _spec_vectors()
+    assert len(vecs) == 6 and any(s not in (0,) for s, *_ in vecs)
+    for seed, p, t, k, h, u, g in vecs:
+        assert oracle.mix64((oracle.mix64(seed) + (p + 1) * GAMMA) & M64) == k
+        assert oracle.noise_hash(seed, p, t) == h, (seed, p, t)
+        assert oracle.uniform(h) == u
+        assert oracle.gumbel(h) == pytest.approx(g, rel=4e-16, abs=4e-16)
+    # the seed-0 row's key is the published stream's first output
+    assert [k for s, p, t, k, *_ in vecs if (s, p) == (0, 0)] == [_golden_stream()[0][1]]
