@@ -79,6 +79,9 @@ _SIGS = {
     "verify_step": (_i32, [_vp, _vp, _i32, _i64, Sampling, _vp, _vp, _vp, _vp, _sz, _vp]),
     "ev_read_probe": (_i32, [_vp, _sz, _vp, _vp]),
     "toy_decoder_set_graphs": (_i32, [_vp, _i32]),
+    "toy_decoder_graph_stats": (_i32, [_vp, C.POINTER(_i64), C.POINTER(_i32)]),
+    "verify_probe_workspace": (_sz, [_vp]),
+    "verify_probe": (_i32, [_vp, _vp, _i32, _i64, Sampling, _vp, _vp, _sz, _vp]),
     "ev_w4_timing": (_i32, [_i32]),
     "ev_w4_timing_read": (_i32, [C.POINTER(_i64), C.POINTER(C.c_double), C.POINTER(C.c_double)]),
 }
@@ -334,6 +337,26 @@ class ToyDecoder:
     def set_graphs(self, enable):
         """Graph replay of verify_step on or off (on by default)."""
         _check(lib().toy_decoder_set_graphs(self._h, 1 if enable else 0))
+
+    def verify_probe(self, tokens, pos0, temperature, top_k, top_p, seed, stream=None):
+        """Words that differ between an R-row verify step over tokens [R] int32
+        (device) at slots pos0.. and the same rows stepped one at a time
+        (logits, sampled tokens, cache entries); 0 when R-row passes are exact.
+        Writes the cache slots pos0..pos0+R-1."""
+        R = tokens.shape[0]
+        ws = torch.empty(int(lib().verify_probe_workspace(self._h)), dtype=torch.uint8, device=tokens.device)
+        out = torch.empty(1, dtype=torch.int32, device=tokens.device)
+        sp = Sampling(float(temperature), int(top_k), float(top_p), int(seed) & ((1 << 64) - 1))
+        _check(lib().verify_probe(self._h, _dev(tokens, "tokens", (torch.int32,)), R, int(pos0), sp,
+                                  _dev(out, "mismatch", (torch.int32,)), C.c_void_p(ws.data_ptr()),
+                                  ws.numel(), _stream(stream)))
+        return int(out.cpu()[0])
+
+    def graph_stats(self):
+        """(steps captured since creation, captured steps held now)."""
+        n, k = C.c_int64(), C.c_int32()
+        _check(lib().toy_decoder_graph_stats(self._h, C.byref(n), C.byref(k)))
+        return n.value, k.value
 
     def verify_step(self, tokens, pos0, temperature, top_k, top_p, seed, sampled=None,
                     n_commit=None, logits=None, stream=None):

@@ -81,13 +81,16 @@ __device__ __forceinline__ void norm_store(const f32x4 (&xv)[NV], float ss, cons
 constexpr int kMaxRowVec = 4;  // H <= 4 * 4 * kRowThreads = 8192
 
 // x[r] = embedding row of tokens[r] (bf16 -> fp32); n[r] = bf16(RMSNorm(x) *
-// gain); positions[r] = pos0 + 1 + r (the positions the rows sample).
+// gain); positions[r] = pos0 + 1 + r (the positions the rows sample); the
+// call's tokens and sampling parameters copied where the rest of the step
+// reads them.
 __global__ __launch_bounds__(kRowThreads) void embed_norm_kernel(const int* __restrict__ tokens,
                                                                  const uint16_t* __restrict__ embed, int H, int V,
                                                                  const float* __restrict__ gain, float eps,
                                                                  float* __restrict__ x, uint16_t* __restrict__ n,
                                                                  long long* __restrict__ positions, long long pos0,
-                                                                 int* __restrict__ tok_copy) {
+                                                                 int* __restrict__ tok_copy, ev_sampling samp,
+                                                                 ev_sampling* __restrict__ samp_copy) {
     __shared__ float red[kRowThreads / 64];
     const int r = blockIdx.x, tid = threadIdx.x;
     int tok = tokens[r];
@@ -110,7 +113,10 @@ __global__ __launch_bounds__(kRowThreads) void embed_norm_kernel(const int* __re
     }
     norm_store(xv, ss, gain, eps, H, n + (size_t)r * H, red);
     if (tid == 0) positions[r] = pos0 + 1 + r;
-    if (tid == 0 && r == 0) positions[kPos0Slot] = pos0;
+    if (tid == 0 && r == 0) {
+        positions[kPos0Slot] = pos0;
+        *samp_copy = samp;  // the sampler of the step reads its parameters here
+    }
 }
 
 // x[r] += the linear's output row r, summed from its partials: split
@@ -465,7 +471,7 @@ struct StepLayout {
     int chunk, nchunk_max;
     bool gu_pair;
     size_t off_x, off_n, off_o, off_q, off_part, off_pg, off_pu, off_h, off_att, off_logits, off_pos, off_acc,
-        off_sws, off_tok, total;
+        off_sws, off_tok, off_samp, total;
 };
 
 }  // namespace ev
@@ -479,7 +485,6 @@ struct StepGraph {
     const void* ws;
     int32_t* sampled;
     int32_t* n_commit;
-    ev_sampling sampling;
     hipGraphExec_t exec;
 };
 constexpr size_t kMaxStepGraphs = 16;
@@ -500,6 +505,7 @@ struct ev_decoder {
     std::mutex graph_mu;            // the cache below
     hipStream_t capture = nullptr;  // capture stream, default priority
     std::vector<StepGraph> graphs;
+    long long captures = 0;         // steps captured over the handle's life
     ~ev_decoder() {
         if (!graphs.empty()) (void)hipDeviceSynchronize();
         for (StepGraph& g : graphs) (void)hipGraphExecDestroy(g.exec);
@@ -555,6 +561,7 @@ static StepLayout step_layout(const ev_decoder_config& c, int NQKV, int DQ, int 
     L.off_acc = take(sizeof(int32_t) * 4);
     L.off_sws = take(keyed_sample_workspace(V));
     L.off_tok = take(sizeof(int32_t) * 16);
+    L.off_samp = take(sizeof(ev_sampling));
     L.total = off;
     return L;
 }
@@ -650,8 +657,8 @@ extern "C" int32_t toy_decoder_set_graphs(ev_decoder* m, int32_t enable) {
 // position comes from the device (positions[kPos0Slot]) and the drafts from
 // embed_norm's copy, so the same launches can be captured once and replayed
 // at any position with any tokens.
-static int32_t step_body(ev_decoder* m, int R, const ev_sampling& sampling, int32_t* sampled, int32_t* n_commit,
-                         float* logits, unsigned char* b, hipStream_t st) {
+static int32_t step_body(ev_decoder* m, int R, int32_t* sampled, int32_t* n_commit, float* logits,
+                         unsigned char* b, hipStream_t st) {
     int32_t rc;
     const StepLayout& L = m->L;
     const ev_decoder_config& c = m->cfg;
@@ -756,22 +763,21 @@ static int32_t step_body(ev_decoder* m, int R, const ev_sampling& sampling, int3
         return rc;
     }
     void* sv = reinterpret_cast<void*>(st);
-    if ((rc = keyed_sample(lg, R, V, reinterpret_cast<const int64_t*>(pos), sampling, sampled, nullptr, sws,
-                           keyed_sample_workspace(V), sv)))
+    // the sampling parameters come from the workspace (written by embed_norm);
+    // the host value only bounds the launch and is never read by the kernels
+    const ev_sampling any{1.0, EV_MAX_TOPK, 1.0, 0};
+    if ((rc = launch_keyed_sample(lg, R, V, pos, any, reinterpret_cast<const ev_sampling*>(b + L.off_samp), sampled,
+                                  nullptr, sws, st)))
         return rc;
     return accept_prefix(sampled, R, R > 1 ? toks + 1 : nullptr, R - 1, n_accept, n_commit, sv);
 }
 
-static bool same_sampling(const ev_sampling& a, const ev_sampling& b) {
-    return a.temperature == b.temperature && a.top_k == b.top_k && a.top_p == b.top_p && a.seed == b.seed;
-}
-
 // The captured step for these arguments: found in the cache, or captured on
 // the decoder's own stream (nothing runs during capture) and kept.
-static int32_t step_graph(ev_decoder* m, int R, const ev_sampling& sampling, int32_t* sampled, int32_t* n_commit,
-                          void* ws, hipGraphExec_t* out) {
+static int32_t step_graph(ev_decoder* m, int R, int32_t* sampled, int32_t* n_commit, void* ws,
+                          hipGraphExec_t* out) {
     for (const StepGraph& g : m->graphs)
-        if (g.R == R && g.ws == ws && g.sampled == sampled && g.n_commit == n_commit && same_sampling(g.sampling, sampling)) {
+        if (g.R == R && g.ws == ws && g.sampled == sampled && g.n_commit == n_commit) {
             *out = g.exec;
             return EV_OK;
         }
@@ -780,7 +786,7 @@ static int32_t step_graph(ev_decoder* m, int R, const ev_sampling& sampling, int
         return rc;
     if ((rc = check_hip(hipStreamBeginCapture(m->capture, hipStreamCaptureModeThreadLocal), "begin capture")))
         return rc;
-    rc = step_body(m, R, sampling, sampled, n_commit, nullptr, reinterpret_cast<unsigned char*>(ws), m->capture);
+    rc = step_body(m, R, sampled, n_commit, nullptr, reinterpret_cast<unsigned char*>(ws), m->capture);
     hipGraph_t graph = nullptr;
     const hipError_t end = hipStreamEndCapture(m->capture, &graph);
     if (!rc) rc = check_hip(end, "end capture");
@@ -796,7 +802,8 @@ static int32_t step_graph(ev_decoder* m, int R, const ev_sampling& sampling, int
         (void)hipGraphExecDestroy(m->graphs.front().exec);
         m->graphs.erase(m->graphs.begin());
     }
-    m->graphs.push_back(StepGraph{R, ws, sampled, n_commit, sampling, exec});
+    m->graphs.push_back(StepGraph{R, ws, sampled, n_commit, exec});
+    ++m->captures;
     *out = exec;
     return EV_OK;
 }
@@ -826,15 +833,168 @@ extern "C" int32_t verify_step(ev_decoder* m, const int32_t* tokens, int32_t R, 
     hipLaunchKernelGGL(embed_norm_kernel, dim3(R), dim3(kRowThreads), 0, st, tokens, m->embed, c.hidden, c.vocab,
                        m->layers[0].attn_norm, (float)c.rms_eps, reinterpret_cast<float*>(b + L.off_x),
                        reinterpret_cast<uint16_t*>(b + L.off_n), reinterpret_cast<long long*>(b + L.off_pos),
-                       (long long)pos0, reinterpret_cast<int*>(b + L.off_tok));
+                       (long long)pos0, reinterpret_cast<int*>(b + L.off_tok), sampling,
+                       reinterpret_cast<ev_sampling*>(b + L.off_samp));
     if ((rc = check_hip(hipGetLastError(), "embed_norm launch"))) return rc;
     // the rest: one graph launch when the step can be replayed as captured
     // (no logits asked for, no per-launch measurement), else launch by launch
     if (m->use_graphs && !logits && !w4_timing_active()) {
         std::lock_guard<std::mutex> lk(m->graph_mu);
         hipGraphExec_t exec;
-        if ((rc = step_graph(m, R, sampling, sampled, n_commit, ws, &exec))) return rc;
+        if ((rc = step_graph(m, R, sampled, n_commit, ws, &exec))) return rc;
         return check_hip(hipGraphLaunch(exec, st), "step graph launch");
     }
-    return step_body(m, R, sampling, sampled, n_commit, logits, b, st);
+    return step_body(m, R, sampled, n_commit, logits, b, st);
+}
+
+extern "C" int32_t toy_decoder_graph_stats(const ev_decoder* m, int64_t* captures, int32_t* cached) {
+    clear_error();
+    if (!m) return fail(EV_EINVAL, "toy_decoder_graph_stats: NULL decoder");
+    std::lock_guard<std::mutex> lk(const_cast<ev_decoder*>(m)->graph_mu);
+    if (captures) *captures = m->captures;
+    if (cached) *cached = (int32_t)m->graphs.size();
+    return EV_OK;
+}
+
+// ---- exactness probe --------------------------------------------------------
+// The TensorFold README's model notes: a model checks at load that drafted
+// rows reproduce one-row decoding on the machine it runs on, and drafts only
+// when they do.  verify_probe runs that check on the handle's live shapes: one
+// R-row verify step, then the same R rows as R one-row steps, and counts the
+// 32-bit words of logits, sampled tokens and written cache entries that differ.
+
+namespace ev {
+namespace {
+
+// Probe workspace after the step's own: two logits areas [16][V] fp32, two
+// sampled areas [16] int32, a commit slot, two cache copies and the count.
+struct ProbeLayout {
+    size_t off_la, off_lb, off_sa, off_sb, off_nc, off_ka, off_kb, off_cnt, total;
+    size_t kv_words;  // 32-bit words of one cache copy
+};
+
+// Words of one cache copy: per (layer, kv head), 16 key slots of 128 fp16 and
+// the two 32-slot value blocks that can hold 16 consecutive slots.
+inline size_t probe_kv_words(const ev_decoder_config& c) {
+    return (size_t)c.layers * c.kv_heads * (16 * kHD + 2 * 32 * kHD) / 2;
+}
+
+ProbeLayout probe_layout(const ev_decoder_config& c, size_t step_total) {
+    ProbeLayout P;
+    size_t off = step_total;
+    auto take = [&](size_t bytes) {
+        const size_t o = off;
+        off += align256(bytes);
+        return o;
+    };
+    P.kv_words = probe_kv_words(c);
+    P.off_la = take(sizeof(float) * 16 * (size_t)c.vocab);
+    P.off_lb = take(sizeof(float) * 16 * (size_t)c.vocab);
+    P.off_sa = take(sizeof(int32_t) * 16);
+    P.off_sb = take(sizeof(int32_t) * 16);
+    P.off_nc = take(sizeof(int32_t) * 4);
+    P.off_ka = take(sizeof(uint32_t) * P.kv_words);
+    P.off_kb = take(sizeof(uint32_t) * P.kv_words);
+    P.off_cnt = take(sizeof(int32_t) * 4);
+    P.total = off;
+    return P;
+}
+
+}  // namespace
+
+// Copies the cache entries of slots pos0 .. pos0 + R - 1 of every layer and kv
+// head: the R key slots, and the one or two value blocks that hold them (in
+// full; their other slots are written by neither pass).  Grid (layers,
+// kv_heads), 256 threads.  The rest of each head's area (keys past R slots, a
+// second value block that is not needed) is written as zeros, so that two
+// copies compare equal exactly when the entries do.
+__global__ __launch_bounds__(256) void probe_save_kernel(const uint16_t* __restrict__ kc,
+                                                          const uint16_t* __restrict__ vc, int C, long long pos0,
+                                                          int R, uint32_t* __restrict__ out) {
+    const int l = blockIdx.x, g = blockIdx.y, NKV = gridDim.y;
+    const size_t head = ((size_t)l * NKV + g) * (size_t)C * kHD;
+    uint32_t* o = out + ((size_t)l * NKV + g) * (16 * kHD + 2 * 32 * kHD) / 2;
+    const uint32_t* k = reinterpret_cast<const uint32_t*>(kc + head + (size_t)pos0 * kHD);
+    const int kw = R * kHD / 2;
+    for (int i = threadIdx.x; i < 16 * kHD / 2; i += 256) o[i] = i < kw ? k[i] : 0u;
+    const long long b0 = pos0 / 32, b1 = (pos0 + R - 1) / 32;
+    const uint32_t* v = reinterpret_cast<const uint32_t*>(vc + head + (size_t)b0 * 32 * kHD);
+    const int vw = (int)(b1 - b0 + 1) * 32 * kHD / 2;
+    for (int i = threadIdx.x; i < 2 * 32 * kHD / 2; i += 256) o[16 * kHD / 2 + i] = i < vw ? v[i] : 0u;
+}
+
+// cnt[0] += the number of positions i < n where a[i] != b[i] (words).
+__global__ __launch_bounds__(256) void probe_compare_kernel(const uint32_t* __restrict__ a,
+                                                             const uint32_t* __restrict__ b, long n,
+                                                             int* __restrict__ cnt) {
+    int d = 0;
+    for (long i = blockIdx.x * 256l + threadIdx.x; i < n; i += (long)gridDim.x * 256)
+        d += a[i] != b[i];
+    // one atomic per wave (a vector atomic on global memory)
+    for (int off = 32; off >= 1; off >>= 1) d += __shfl_xor(d, off, 64);
+    if ((threadIdx.x & 63) == 0 && d) atomicAdd(cnt, d);
+}
+
+__global__ void probe_clear_kernel(int* __restrict__ cnt) {
+    if (threadIdx.x == 0) cnt[0] = 0;
+}
+
+__global__ void probe_result_kernel(const int* __restrict__ cnt, int32_t* __restrict__ mismatch) {
+    if (threadIdx.x == 0) mismatch[0] = cnt[0];
+}
+
+}  // namespace ev
+
+extern "C" size_t verify_probe_workspace(const ev_decoder* m) {
+    return m ? probe_layout(m->cfg, m->L.total).total : 0;
+}
+
+extern "C" int32_t verify_probe(ev_decoder* m, const int32_t* tokens, int32_t R, int64_t pos0,
+                                ev_sampling sampling, int32_t* mismatch, void* ws, size_t ws_bytes,
+                                void* stream) {
+    clear_error();
+    const char* who = "verify_probe";
+    int32_t rc;
+    if (!m) return fail(EV_EINVAL, "%s: NULL decoder", who);
+    if ((rc = check_lanes(who, R))) return rc;
+    if (!tokens || !mismatch) return fail(EV_EINVAL, "%s: NULL pointer", who);
+    if (!aligned(tokens, 4) || !aligned(mismatch, 4)) return fail(EV_EINVAL, "%s: misaligned pointer", who);
+    if (pos0 < 0 || pos0 + R > m->C)
+        return fail(EV_EINVAL, "%s: slots %lld..%lld outside the cache of %d", who, (long long)pos0,
+                    (long long)pos0 + R - 1, m->C);
+    if ((rc = check_sampling(who, sampling))) return rc;
+    const ProbeLayout P = probe_layout(m->cfg, m->L.total);
+    if ((rc = check_ws(who, ws, ws_bytes, P.total))) return rc;
+    const ev_decoder_config& c = m->cfg;
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    unsigned char* b = reinterpret_cast<unsigned char*>(ws);
+    const size_t V = (size_t)c.vocab;
+    float* la = reinterpret_cast<float*>(b + P.off_la);
+    float* lb = reinterpret_cast<float*>(b + P.off_lb);
+    int32_t* sa = reinterpret_cast<int32_t*>(b + P.off_sa);
+    int32_t* sb = reinterpret_cast<int32_t*>(b + P.off_sb);
+    int32_t* nc = reinterpret_cast<int32_t*>(b + P.off_nc);
+    uint32_t* ka = reinterpret_cast<uint32_t*>(b + P.off_ka);
+    uint32_t* kb = reinterpret_cast<uint32_t*>(b + P.off_kb);
+    int* cnt = reinterpret_cast<int*>(b + P.off_cnt);
+    const dim3 kvgrid((unsigned)c.layers, (unsigned)c.kv_heads);
+    // the R-row pass (eager: logits are asked for), its cache entries saved
+    if ((rc = verify_step(m, tokens, R, pos0, sampling, sa, nc, la, ws, m->L.total, stream))) return rc;
+    hipLaunchKernelGGL(probe_save_kernel, kvgrid, dim3(256), 0, st, m->kc, m->vc, m->C, (long long)pos0, R, ka);
+    if ((rc = check_hip(hipGetLastError(), "probe save launch"))) return rc;
+    // the same rows one at a time, from the same cache
+    for (int r = 0; r < R; ++r)
+        if ((rc = verify_step(m, tokens + r, 1, pos0 + r, sampling, sb + r, nc, lb + (size_t)r * V, ws, m->L.total,
+                              stream)))
+            return rc;
+    hipLaunchKernelGGL(probe_save_kernel, kvgrid, dim3(256), 0, st, m->kc, m->vc, m->C, (long long)pos0, R, kb);
+    hipLaunchKernelGGL(probe_clear_kernel, dim3(1), dim3(64), 0, st, cnt);
+    const long nl = (long)R * (long)V;
+    hipLaunchKernelGGL(probe_compare_kernel, dim3(256), dim3(256), 0, st, reinterpret_cast<const uint32_t*>(la),
+                       reinterpret_cast<const uint32_t*>(lb), nl, cnt);
+    hipLaunchKernelGGL(probe_compare_kernel, dim3(1), dim3(256), 0, st, reinterpret_cast<const uint32_t*>(sa),
+                       reinterpret_cast<const uint32_t*>(sb), (long)R, cnt);
+    hipLaunchKernelGGL(probe_compare_kernel, dim3(64), dim3(256), 0, st, ka, kb, (long)P.kv_words, cnt);
+    hipLaunchKernelGGL(probe_result_kernel, dim3(1), dim3(64), 0, st, cnt, mismatch);
+    return check_hip(hipGetLastError(), "probe compare launch");
 }

@@ -19,6 +19,12 @@ int32_t check_hip(hipError_t e, const char* what);
 // Sampling parameters as keyed_sample accepts them (EV_OK or the error code).
 int32_t check_sampling(const char* who, const ev_sampling& s);
 
+// The launches of keyed_sample on checked arguments; with `sd` (device) the
+// kernels read the sampling parameters there rather than from `s`, which then
+// only has to give a valid top-k for the launch's candidate count bound.
+int32_t launch_keyed_sample(const float* logits, int R, int V, const long long* positions, const ev_sampling& s,
+                            const ev_sampling* sd, int32_t* tokens, double* gap, void* ws, hipStream_t st);
+
 inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 // ---- device helpers -------------------------------------------------------

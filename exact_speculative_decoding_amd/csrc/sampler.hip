@@ -112,9 +112,20 @@ __device__ __forceinline__ int count_greater(const unsigned long long* l, int n,
 // in the four lists (binary search in the other three): keys are unique, so
 // the places of the chunk's top-kk are 0..kk-1 and every other candidate's
 // place is kk or more.
+// Candidates a row keeps: the top_k largest, 2 when greedy (the argmax and
+// the runner-up for the gap), never more than V; always within 1..64, the
+// bound of the kernels' lists (validated parameters are inside it anyway).
+__host__ __device__ inline int sample_kk_of(double T, int top_k, int V) {
+    int k = T == 0.0 ? 2 : top_k;
+    k = k < 1 ? 1 : (k > EV_MAX_TOPK ? EV_MAX_TOPK : k);
+    return k < V ? k : V;
+}
+
 __global__ __launch_bounds__(kSThreads) void topk_chunk_kernel(const float* __restrict__ logits,
                                                                int V, int kk, int nchunk,
+                                                               const ev_sampling* __restrict__ sd,
                                                                unsigned long long* __restrict__ out) {
+    if (sd) kk = sample_kk_of(sd->temperature, sd->top_k, V);  // parameters kept on the device
     constexpr int kW = kSThreads / 64;
     __shared__ unsigned long long rest[kPer - 1][kSThreads];  // thread t's keys 1..15 in column t
     __shared__ unsigned long long wl[kW][EV_MAX_TOPK];       // each wave's top-kk, in order
@@ -166,11 +177,19 @@ struct SampleArgs {
     int nchunk, kk, V;
     double T, top_p;
     unsigned long long seed;
+    const ev_sampling* sd;  // when non-NULL, T, top_k, top_p and seed are read here
     int* tokens;
     double* gap;
 };
 
 __global__ __launch_bounds__(64) void merge_sample_kernel(SampleArgs a) {
+    if (a.sd) {
+        const ev_sampling s = *a.sd;
+        a.T = s.temperature;
+        a.top_p = s.top_p;
+        a.seed = s.seed;
+        a.kk = sample_kk_of(s.temperature, s.top_k, a.V);
+    }
     __shared__ unsigned long long lists[kMaxChunks * EV_MAX_TOPK];  // [chunk][kk], each in order
     const int r = blockIdx.x, lane = threadIdx.x;
     const int n = a.nchunk * a.kk;  // <= 64 * 64
@@ -264,10 +283,6 @@ __global__ __launch_bounds__(64) void accept_kernel(const int* __restrict__ samp
 }
 
 static int sample_nchunk(int V) { return (V + kChunk - 1) / kChunk; }
-static int sample_kk(const ev_sampling& s, int V) {
-    const int k = s.temperature == 0.0 ? 2 : s.top_k;
-    return k < V ? k : V;
-}
 
 }  // namespace ev
 
@@ -291,35 +306,55 @@ extern "C" size_t keyed_sample_workspace(int32_t V) {
     return (size_t)EV_MAX_LANES * sample_nchunk(V) * EV_MAX_TOPK * sizeof(unsigned long long);
 }
 
-extern "C" int32_t keyed_sample(const float* logits, int32_t R, int32_t V, const int64_t* positions,
-                                ev_sampling s, int32_t* tokens, double* gap, void* ws,
-                                size_t ws_bytes, void* stream) {
-    clear_error();
-    const char* who = "keyed_sample";
+// Checks the shapes and pointers of a keyed sample (the sampling parameters
+// are checked by the caller).
+static int32_t check_sample_args(const char* who, const float* logits, int32_t R, int32_t V,
+                                 const int64_t* positions, int32_t* tokens, double* gap, void* ws,
+                                 size_t ws_bytes) {
     if (R < 1 || R > EV_MAX_LANES) return fail(EV_EINVAL, "%s: R=%d outside 1..16", who, R);
     if (V < 1) return fail(EV_EINVAL, "%s: V=%d", who, V);
     if (V > kMaxChunks * kChunk) return fail(EV_EUNSUPPORTED, "%s: V=%d above %d", who, V, kMaxChunks * kChunk);
     if (!logits || !positions || !tokens) return fail(EV_EINVAL, "%s: NULL pointer", who);
     if (!aligned(logits, 4) || !aligned(positions, 8) || !aligned(tokens, 4) || (gap && !aligned(gap, 8)))
         return fail(EV_EINVAL, "%s: misaligned pointer", who);
-    int32_t rc0 = check_sampling(who, s);
-    if (rc0) return rc0;
     const size_t need = keyed_sample_workspace(V);
     if (!ws || ws_bytes < need)
         return fail(EV_EWORKSPACE, "%s: workspace needs %zu bytes, got %zu", who, need, ws ? ws_bytes : (size_t)0);
     if (!aligned(ws, 8)) return fail(EV_EINVAL, "%s: workspace must be 8-byte aligned", who);
-    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    return EV_OK;
+}
+
+namespace ev {
+// The two launches of a keyed sample.  `sd` (device, may be NULL): when
+// given, the kernels read the sampling parameters there instead of from `s`
+// (the verify step keeps them in its workspace, so that one captured step
+// serves every seed and temperature).
+int32_t launch_keyed_sample(const float* logits, int R, int V, const long long* positions, const ev_sampling& s,
+                            const ev_sampling* sd, int32_t* tokens, double* gap, void* ws, hipStream_t st) {
     const int nchunk = sample_nchunk(V);
-    const int kk = sample_kk(s, V);
+    const int kk = sample_kk_of(s.temperature, s.top_k, V);
     unsigned long long* cand = reinterpret_cast<unsigned long long*>(ws);
-    hipLaunchKernelGGL(topk_chunk_kernel, dim3(nchunk, R), dim3(kSThreads), 0, st, logits, V, kk,
-                       nchunk, cand);
+    hipLaunchKernelGGL(topk_chunk_kernel, dim3(nchunk, R), dim3(kSThreads), 0, st, logits, V, kk, nchunk, sd,
+                       cand);
     int32_t rc = check_hip(hipGetLastError(), "topk_chunk launch");
     if (rc) return rc;
-    SampleArgs a{cand, reinterpret_cast<const long long*>(positions), nchunk, kk, V,
-                 s.temperature, s.top_p, (unsigned long long)s.seed, tokens, gap};
+    SampleArgs a{cand, positions, nchunk, kk, V, s.temperature, s.top_p, (unsigned long long)s.seed, sd,
+                 tokens, gap};
     hipLaunchKernelGGL(merge_sample_kernel, dim3(R), dim3(64), 0, st, a);
     return check_hip(hipGetLastError(), "merge_sample launch");
+}
+}  // namespace ev
+
+extern "C" int32_t keyed_sample(const float* logits, int32_t R, int32_t V, const int64_t* positions,
+                                ev_sampling s, int32_t* tokens, double* gap, void* ws,
+                                size_t ws_bytes, void* stream) {
+    clear_error();
+    const char* who = "keyed_sample";
+    int32_t rc;
+    if ((rc = check_sample_args(who, logits, R, V, positions, tokens, gap, ws, ws_bytes))) return rc;
+    if ((rc = check_sampling(who, s))) return rc;
+    return launch_keyed_sample(logits, R, V, reinterpret_cast<const long long*>(positions), s, nullptr, tokens,
+                               gap, ws, reinterpret_cast<hipStream_t>(stream));
 }
 
 extern "C" int32_t accept_prefix(const int32_t* sampled, int32_t R, const int32_t* draft, int32_t D,

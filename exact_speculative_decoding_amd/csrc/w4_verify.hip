@@ -1237,11 +1237,10 @@ extern "C" size_t verify_mlp_w4_workspace(int32_t H, int32_t I, int32_t G) {
     return mlp_layout(H, I).total;
 }
 
-extern "C" int32_t verify_mlp_w4(const uint16_t* x, int32_t R, int32_t H, int32_t I, int32_t G,
-                                 const void* w_gate, const void* w_up, const void* w_down, float* y,
-                                 uint16_t* h_out, void* ws, size_t ws_bytes, void* stream) {
-    clear_error();
-    const char* who = "verify_mlp_w4";
+// Argument checks shared by the MLP entry points (EV_OK or the error code).
+static int32_t check_mlp_args(const char* who, const uint16_t* x, int32_t R, int32_t H, int32_t I, int32_t G,
+                              const void* w_gate, const void* w_up, const void* w_down, const float* y,
+                              const uint16_t* h_out) {
     int32_t rc;
     if ((rc = check_lanes(who, R)) || (rc = check_w4_dims(who, H, I, G)) ||
         (rc = check_w4_dims(who, I, H, G)))
@@ -1250,8 +1249,16 @@ extern "C" int32_t verify_mlp_w4(const uint16_t* x, int32_t R, int32_t H, int32_
     if (!aligned(x, 16) || !aligned(w_gate, 16) || !aligned(w_up, 16) || !aligned(w_down, 16) ||
         !aligned(y, 4) || (h_out && !aligned(h_out, 16)))
         return fail(EV_EINVAL, "%s: misaligned pointer (x, weights, h 16 B; y 4 B)", who);
+    return EV_OK;
+}
+
+// The MLP slice's launches on a checked workspace `ws` of at least
+// mlp_layout(H, I).total bytes.
+static int32_t mlp_launches(const uint16_t* x, int32_t R, int32_t H, int32_t I, int32_t G, const void* w_gate,
+                            const void* w_up, const void* w_down, float* y, uint16_t* h_out, void* ws,
+                            void* stream) {
+    int32_t rc;
     const MlpLayout L = mlp_layout(H, I);
-    if ((rc = check_ws(who, ws, ws_bytes, L.total))) return rc;
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     unsigned char* wsb = reinterpret_cast<unsigned char*>(ws);
     uint16_t* h = reinterpret_cast<uint16_t*>(wsb);
@@ -1297,3 +1304,15 @@ extern "C" int32_t verify_mlp_w4(const uint16_t* x, int32_t R, int32_t H, int32_
     if (L.p2.S > 1 && (rc = launch_splitk_reduce(pd, L.p2.S, H, R, y, st))) return rc;
     return EV_OK;
 }
+
+extern "C" int32_t verify_mlp_w4(const uint16_t* x, int32_t R, int32_t H, int32_t I, int32_t G,
+                                 const void* w_gate, const void* w_up, const void* w_down, float* y,
+                                 uint16_t* h_out, void* ws, size_t ws_bytes, void* stream) {
+    clear_error();
+    const char* who = "verify_mlp_w4";
+    int32_t rc;
+    if ((rc = check_mlp_args(who, x, R, H, I, G, w_gate, w_up, w_down, y, h_out))) return rc;
+    if ((rc = check_ws(who, ws, ws_bytes, mlp_layout(H, I).total))) return rc;
+    return mlp_launches(x, R, H, I, G, w_gate, w_up, w_down, y, h_out, ws, stream);
+}
+

@@ -30,3 +30,24 @@ def decode(round_fn, first_token, pos0, n_tokens, R, drafter, on_round=None):
         if on_round is not None:
             on_round(tokens, sampled, n_commit)
     return out, rounds
+
+
+def rows_after_probe(probe, R):
+    """The rows a round may use: R when probe(R), a count of differing words
+    between an R-row pass and the same rows stepped one at a time, is 0; else
+    1 (serial decoding, the same output, slower).  The TensorFold README's
+    model notes: a model checks at load that drafted rows reproduce one-row
+    decoding on the machine, and drafts only when they do."""
+    if R <= 1:
+        return 1
+    return R if int(probe(R)) == 0 else 1
+
+
+def token_sha(tokens):
+    """sha256 (hex) of a committed token stream, the ids as little-endian
+    int32: a fingerprint of one reply, equal for drafted and serial decoding
+    of the same request (the blog's FAQ: the server reports a token hash per
+    reply)."""
+    import hashlib
+    import struct
+    return hashlib.sha256(struct.pack(f"<{len(tokens)}i", *[int(t) for t in tokens])).hexdigest()

@@ -300,13 +300,15 @@ size_t verify_step_workspace(const ev_decoder* m);
 /* starts at pos0 + n_commit with sampled[n_commit-1].  R = 1 is serial       */
 /* decoding.  Limits: 1 <= R <= 16.  Errors: EV_EINVAL, EV_EUNSUPPORTED,      */
 /* EV_EWORKSPACE, EV_EHIP; nothing is launched on a validation error.         */
-/* Launches: a first kernel takes tokens and pos0 (copied into ws); the rest  */
-/* of the step reads them from ws.  With graphs on (the default), logits NULL */
-/* and the timing hook off, that rest is captured as a HIP graph on the first */
-/* call with a given (R, ws, sampled, n_commit, sampling) and replayed by     */
-/* later calls with the same five (the handle keeps the 16 latest; dropping   */
-/* one synchronises the device), so a round costs two submissions.  Results   */
-/* are identical either way.  Calls on one handle must not overlap.           */
+/* Launches: a first kernel takes tokens, pos0 and the sampling parameters   */
+/* (copied into ws); the rest of the step reads them from ws.  With graphs on */
+/* (the default), logits NULL and the timing hook off, that rest is captured  */
+/* as a HIP graph on the first call with a given (R, ws, sampled, n_commit)   */
+/* and replayed by later calls with the same four, whatever their tokens,     */
+/* position, seed, temperature, top_k or top_p (the handle keeps the 16       */
+/* latest; dropping one synchronises the device), so a round costs two        */
+/* submissions and a new seed never captures.  Results are identical either  */
+/* way.  Calls on one handle must not overlap.                                */
 int32_t verify_step(ev_decoder* m, const int32_t* tokens, int32_t R, int64_t pos0,
                     ev_sampling sampling, int32_t* sampled, int32_t* n_commit, float* logits,
                     void* ws, size_t ws_bytes, void* stream);
@@ -314,6 +316,37 @@ int32_t verify_step(ev_decoder* m, const int32_t* tokens, int32_t R, int64_t pos
 /* Graph replay of verify_step on (enable != 0, the default) or off (every    */
 /* step launched kernel by kernel).  Errors: EV_EINVAL (NULL handle).         */
 int32_t toy_decoder_set_graphs(ev_decoder* m, int32_t enable);
+
+/* How many steps the handle has captured since it was created (captures,    */
+/* host, may be NULL) and how many it holds now (cached, host, may be NULL).  */
+/* Errors: EV_EINVAL (NULL handle).                                           */
+int32_t toy_decoder_graph_stats(const ev_decoder* m, int64_t* captures, int32_t* cached);
+
+/* ------------------------------------------------------------------------- */
+/* Exactness probe.                                                           */
+/*                                                                            */
+/* The TensorFold README's model notes: a model checks at load that drafted   */
+/* rows reproduce one-row decoding on the machine it runs on, and drafts only */
+/* when they do (otherwise it decodes one token a round: same output,         */
+/* slower).  verify_probe is that check on the handle's live shapes: one      */
+/* verify_step of R rows (tokens, pos0, sampling as for verify_step), then    */
+/* the same R rows as R one-row steps at slots pos0 + r from the same cache,  */
+/* and the number of 32-bit words that differ between the two, over the      */
+/* rows' logits, their sampled tokens and the cache entries they wrote, is    */
+/* written to mismatch.  0: R-row passes are exact here; otherwise the caller */
+/* should decode with R = 1.                                                  */
+/*   tokens   (device) [R] int32, values in [0, V).                           */
+/*   mismatch (device) [1] int32, written.                                    */
+/*   ws       (device) verify_probe_workspace(m) bytes, 256-byte aligned.     */
+/* Writes cache slots pos0 .. pos0+R-1 like verify_step (the one-row steps    */
+/* last): run it where those slots are free, such as just before the round    */
+/* that starts at pos0, which rewrites them.  Limits and errors as            */
+/* verify_step.                                                               */
+/* ------------------------------------------------------------------------- */
+size_t verify_probe_workspace(const ev_decoder* m);
+int32_t verify_probe(ev_decoder* m, const int32_t* tokens, int32_t R, int64_t pos0,
+                     ev_sampling sampling, int32_t* mismatch, void* ws, size_t ws_bytes,
+                     void* stream);
 
 /* ------------------------------------------------------------------------- */
 /* Measurement hook for the W4 verify kernel (every entry point that streams  */

@@ -89,16 +89,29 @@ void ov_rope(float* v, int d, int64_t p, double base)
     }
 }
 
+/* Every fp16 pattern's value, filled once from ov_f16_to_f64 (the same exact
+ * conversion, looked up instead of recomputed for each cache entry read). */
+static double f16_value[65536];
+static int f16_value_ready;
+
+static void f16_table_init(void)
+{
+    if (f16_value_ready) return;
+    for (int h = 0; h < 65536; h++) f16_value[h] = ov_f16_to_f64((uint16_t)h);
+    f16_value_ready = 1;
+}
+
 /* Attention of one query q[d] (fp32) over n cached slots K/V [n][d] (fp16):
  * o = sum_j softmax_j(q.k_j / sqrt(d)) v_j, in double. */
 void ov_attend(const float* q, const uint16_t* K, const uint16_t* V, int n, int d, double* o)
 {
+    f16_table_init();
     double* s = (double*)malloc(sizeof(double) * (size_t)n);
     double m = -INFINITY;
     for (int j = 0; j < n; j++) {
         double acc = 0.0;
         for (int i = 0; i < d; i++)
-            acc += (double)q[i] * ov_f16_to_f64(K[(size_t)j * d + i]);
+            acc += (double)q[i] * f16_value[K[(size_t)j * d + i]];
         s[j] = acc / sqrt((double)d);
         if (s[j] > m) m = s[j];
     }
@@ -111,7 +124,7 @@ void ov_attend(const float* q, const uint16_t* K, const uint16_t* V, int n, int 
     for (int j = 0; j < n; j++) {
         double pj = s[j] / Z;
         for (int i = 0; i < d; i++)
-            o[i] += pj * ov_f16_to_f64(V[(size_t)j * d + i]);
+            o[i] += pj * f16_value[V[(size_t)j * d + i]];
     }
     free(s);
 }
@@ -147,7 +160,7 @@ void ov_decoder_step(const int32_t* ci, const double* cd, const void* const* w,
     float* x = (float*)malloc(sizeof(float) * (size_t)H);
     float* t = (float*)malloc(sizeof(float) * (size_t)(H > NQKV ? H : NQKV));
     uint16_t* nb = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)(H > DQ ? H : DQ));
-    double* o = (double*)malloc(sizeof(double) * (size_t)D);
+    double* o = (double*)malloc(sizeof(double) * (size_t)NH * D); /* one output per head */
 
     for (int i = 0; i < H; i++)
         x[i] = (float)ov_bf16_to_f64(embed[(size_t)token * H + i]);
@@ -170,11 +183,14 @@ void ov_decoder_step(const int32_t* ci, const double* cd, const void* const* w,
                 vc[slot + i] = f16_saturating(v[i]);
             }
         }
-        for (int h = 0; h < NH; h++) {
+        f16_table_init(); /* before the heads run in parallel */
+#pragma omp parallel for schedule(static)
+        for (int h = 0; h < NH; h++) { /* heads are independent outputs */
             int g = h / (NH / NKV);
             size_t head = ((size_t)l * NKV + g) * C * D;
-            ov_attend(t + (size_t)h * D, kc + head, vc + head, (int)(p + 1), D, o);
-            for (int i = 0; i < D; i++) nb[(size_t)h * D + i] = ov_f64_to_bf16(o[i]);
+            double* oh = o + (size_t)h * D;
+            ov_attend(t + (size_t)h * D, kc + head, vc + head, (int)(p + 1), D, oh);
+            for (int i = 0; i < D; i++) nb[(size_t)h * D + i] = ov_f64_to_bf16(oh[i]);
         }
         ov_w4_linear_f32(nb, 1, DQ,
                          (const uint8_t*)w[7] + (size_t)l * H * (DQ / 2),

@@ -212,21 +212,25 @@ def _full(C):
     return syn.decoder(C=C)
 
 
-@pytest.mark.parametrize("C,n,positions", [(4096, 96, (0, 1, 2, 47)), (32768, 24, (0, 5))])
-def test_full_decoder_drafted_equals_serial_and_oracle(C, n, positions):
+@pytest.mark.parametrize("C,n,sampling", [(4096, 96, SAMPLED), (32768, 24, SAMPLED), (4096, 48, GREEDY)])
+def test_full_decoder_drafted_equals_serial_and_oracle(C, n, sampling):
+    """The 8-layer decoder: serial decoding of n tokens; drafted decoding (8
+    rows a round, drafts matching the serial transcript at 65 %) commits the
+    same tokens and cache bytes; and the oracle, teacher-forced on the
+    committed stream, checks the GPU's logits (per-row relative error <=
+    2e-3) and token at every one of the n positions."""
+    print(f"full decoder C={C} n={n} T={sampling[0]}", flush=True)
     d = _full(C)
     cfg = d["cfg"]
     pos0, V = cfg["prefill"], cfg["vocab"]
     m = _fresh(d)
     log = []
-    serial, _ = decode(_gpu_round(m, SAMPLED, log), d["first_token"], pos0, n, 1, lambda p, c: [])
+    serial, _ = decode(_gpu_round(m, sampling, log), d["first_token"], pos0, n, 1, lambda p, c: [])
     kc_s, vc_s = m.k_cache.clone(), m.v_cache_standard()
     del m
     m2 = _fresh(d)
-    rounds_log = []
-    got, rounds = decode(_gpu_round(m2, SAMPLED), d["first_token"], pos0, n, 8,
-                         syn.transcript_drafter(serial, pos0 + 1, 0.65, 21, V),
-                         on_round=lambda t, s, c: rounds_log.append(c))
+    got, rounds = decode(_gpu_round(m2, sampling), d["first_token"], pos0, n, 8,
+                         syn.transcript_drafter(serial, pos0 + 1, 0.65, 21, V))
     assert got == serial
     L = pos0 + n
     assert torch.equal(m2.k_cache[:, :, :L], kc_s[:, :, :L])
@@ -235,7 +239,76 @@ def test_full_decoder_drafted_equals_serial_and_oracle(C, n, positions):
     print(f"C={C}: {n} tokens in {rounds} rounds of 8 rows ({n / rounds:.2f} per round), sha256 {sha}")
     del m2
     gpu_logits = [x[2][0] for x in log]
-    res = _teacher_forced(d, serial, pos0, SAMPLED, set(positions), gpu_logits)
+    res = _teacher_forced(d, serial, pos0, sampling, set(range(n)), gpu_logits)
+    assert len(res) == n
     near = _check_stream(res)
-    print(f"C={C}: oracle at positions {positions}: max row err "
-          f"{max(r[0] for r in res):.3e}, {near} near ties")
+    print(f"C={C} T={sampling[0]}: oracle at all {n} positions: max row err "
+          f"{max(r[0] for r in res):.3e}, {near} near ties (gap < 1e-4)")
+
+
+def test_tiny_one_capture_serves_every_seed(tiny):
+    """The captured step keeps no sampling parameter: 50 seeds (and greedy,
+    and other temperatures and top-k / top-p) decoded through one handle
+    capture nothing after the first rounds, and every round equals the same
+    round launched kernel by kernel."""
+    d, cfg = tiny, tiny["cfg"]
+    pos0, n, V = cfg["prefill"], 12, cfg["vocab"]
+    settings = [(0.7, 20, 0.95, s) for s in range(50)] + [GREEDY, (1.0, 5, 0.5, 7), (0.3, 64, 1.0, 8)]
+    mg, me = _fresh(d), _fresh(d)
+    me.set_graphs(False)
+    kc0, vc0 = mg.k_cache.clone(), mg.v_cache.clone()
+    for samp in settings:
+        logs = []
+        for m in (mg, me):
+            m.k_cache.copy_(kc0)
+            m.v_cache.copy_(vc0)
+            log = []
+
+            def fn(tokens, p0):
+                out = m.verify_step_host(tokens, p0, *samp)
+                log.append((p0, tuple(tokens), tuple(out[0]), out[1]))
+                return out
+
+            serial = decode(fn, d["first_token"], pos0, n, 1, lambda p, c: [])[0]
+            decode(fn, d["first_token"], pos0, n, 4, syn.transcript_drafter(serial, pos0 + 1, 0.65, 5, V))
+            logs.append(log)
+        assert logs[0] == logs[1], samp
+    # one capture per row count (R = 1..4, the rounds' widths), none per setting
+    captures, cached = mg.graph_stats()
+    print(f"{len(settings)} sampling settings: {captures} captures")
+    assert 1 <= captures <= 4 and cached == captures
+    assert me.graph_stats() == (0, 0)
+
+
+def test_probe_finds_row_passes_exact(tiny):
+    """verify_probe on the live shapes: an R-row pass and the same rows one
+    at a time agree word for word (logits, samples, cache entries), so the
+    round loop keeps drafting; the slots it wrote are then rewritten by the
+    round that starts there, which still equals serial decoding."""
+    from exact_speculative_decoding_amd.loop import rows_after_probe
+    d, cfg = tiny, tiny["cfg"]
+    pos0, n, V = cfg["prefill"], 20, cfg["vocab"]
+    ref = decode(_gpu_round(_fresh(d), SAMPLED), d["first_token"], pos0, n, 1, lambda p, c: [])[0]
+    m = _fresh(d)
+    for R in (2, 8, 16):
+        toks = torch.tensor([d["first_token"]] + [(7 * i + 3) % V for i in range(R - 1)], dtype=torch.int32,
+                            device="cuda")
+        for samp in (SAMPLED, GREEDY):
+            assert m.verify_probe(toks, pos0, *samp) == 0, (R, samp)
+    R = rows_after_probe(lambda r: m.verify_probe(torch.tensor([d["first_token"]] * r, dtype=torch.int32,
+                                                                device="cuda"), pos0, *SAMPLED), 8)
+    assert R == 8
+    got, _ = decode(_gpu_round(m, SAMPLED), d["first_token"], pos0, n, R,
+                    syn.transcript_drafter(ref, pos0 + 1, 0.65, 5, V))
+    assert got == ref
+
+
+def test_probe_on_the_full_decoder():
+    print("probe: full decoder C=4096 R=8", flush=True)
+    d = _full(4096)
+    cfg = d["cfg"]
+    m = _fresh(d)
+    toks = torch.tensor([d["first_token"]] + [(31 * i + 5) % cfg["vocab"] for i in range(7)], dtype=torch.int32,
+                        device="cuda")
+    assert m.verify_probe(toks, cfg["prefill"], *SAMPLED) == 0
+    assert m.verify_probe(toks[:1].repeat(16).contiguous(), cfg["prefill"] + 9, *GREEDY) == 0
