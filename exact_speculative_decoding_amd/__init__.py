@@ -84,6 +84,7 @@ _SIGS = {
     "verify_probe": (_i32, [_vp, _vp, _i32, _i64, Sampling, _vp, _vp, _sz, _vp]),
     "ev_w4_timing": (_i32, [_i32]),
     "ev_w4_timing_read": (_i32, [C.POINTER(_i64), C.POINTER(C.c_double), C.POINTER(C.c_double)]),
+    "ev_w4_timing_stamps": (_i32, [_vp, _i64, _vp, _i32, C.POINTER(_i32)]),
 }
 
 
@@ -468,3 +469,16 @@ def w4_timing_read():
     n, ms, by = C.c_int64(), C.c_double(), C.c_double()
     _check(lib().ev_w4_timing_read(C.byref(n), C.byref(ms), C.byref(by)))
     return n.value, ms.value, by.value
+
+
+def w4_timing_stamps(max_pairs=1 << 20, max_launches=1 << 14):
+    """(per-launch workgroup counts, [workgroups][2] device wall-clock stamps)
+    of the launches recorded since the last w4_timing_read (not reset)."""
+    import numpy as np
+    st = np.empty((max_pairs, 2), np.uint64)
+    cnt = np.empty(max_launches, np.int32)
+    n = C.c_int32()
+    _check(lib().ev_w4_timing_stamps(st.ctypes.data, max_pairs, cnt.ctypes.data, max_launches, C.byref(n)))
+    c = cnt[:n.value].copy()
+    return c, st[:int(c.sum())].copy()
+

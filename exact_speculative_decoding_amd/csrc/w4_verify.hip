@@ -1154,6 +1154,26 @@ extern "C" int32_t ev_w4_timing_read(int64_t* launches, double* total_ms, double
     return EV_OK;
 }
 
+extern "C" int32_t ev_w4_timing_stamps(uint64_t* stamps, int64_t max_pairs, int32_t* counts, int32_t max_launches,
+                                       int32_t* n_launches) {
+    clear_error();
+    std::lock_guard<std::mutex> lk(g_timing.mu);
+    const long n = (long)g_timing.first.size();
+    if (!stamps || !counts || !n_launches) return fail(EV_EINVAL, "ev_w4_timing_stamps: NULL pointer");
+    if (n > max_launches || g_timing.used > max_pairs)
+        return fail(EV_EINVAL, "ev_w4_timing_stamps: %ld launches / %ld workgroups recorded, room for %d / %lld", n,
+                    g_timing.used, max_launches, (long long)max_pairs);
+    if (g_timing.used > 0) {
+        if (hipDeviceSynchronize() != hipSuccess ||
+            hipMemcpy(stamps, g_timing.slots, sizeof(unsigned long long) * 2 * g_timing.used, hipMemcpyDeviceToHost) !=
+                hipSuccess)
+            return fail(EV_EHIP, "ev_w4_timing_stamps: copy failed");
+    }
+    for (long i = 0; i < n; ++i) counts[i] = (int32_t)g_timing.count[i];
+    *n_launches = (int32_t)n;
+    return EV_OK;
+}
+
 // Practical ceiling of a streaming read: the whole grid sweeps the buffer in
 // 1 KB wave blocks (wave w reads blocks w, w + nwaves, ..., four in flight),
 // as a plain read kernel would; timed by the same per-workgroup stamps.  The

@@ -363,6 +363,14 @@ int32_t verify_probe(ev_decoder* m, const int32_t* tokens, int32_t R, int64_t po
 /* ------------------------------------------------------------------------- */
 int32_t ev_w4_timing(int32_t enable);
 int32_t ev_w4_timing_read(int64_t* launches, double* total_ms, double* total_bytes);
+/* The raw stamps behind the next ev_w4_timing_read (which it does not reset):*/
+/* stamps (host) receives the (start, end) device wall-clock pairs of every   */
+/* recorded workgroup, launch after launch in workgroup order; counts (host)  */
+/* each launch's workgroup count; *n_launches the number of launches.         */
+/* Errors: EV_EINVAL (NULL pointer, or more launches or workgroups than       */
+/* max_launches / max_pairs), EV_EHIP.                                        */
+int32_t ev_w4_timing_stamps(uint64_t* stamps, int64_t max_pairs, int32_t* counts, int32_t max_launches,
+                            int32_t* n_launches);
 
 /* Measurement aid: the practical ceiling of a streaming read on this part,  */
 /* next to the nominal HBM peak.  Reads `bytes` at buf (device, 16-byte       */
