@@ -66,6 +66,7 @@ _SIGS = {
     "verify_mlp_w4_workspace": (_sz, [_i32, _i32, _i32]),
     "verify_mlp_w4": (_i32, [_vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _sz,
                              _vp]),
+    "verify_mlp_w4_noalloc": (_i32, [_vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp]),
     "verify_moe_w4_workspace": (_sz, [_i32, _i32, _i32, _i32, _i32]),
     "verify_moe_w4": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp,
                              _vp, _vp, _sz, _vp]),
@@ -206,6 +207,20 @@ def verify_mlp_w4(x, gate, up, down, y=None, h=None, ws=None, stream=None):
         _dev(down.blob, "down", _U8), _dev(y, "y", (torch.float32,)),
         None if h is None else _dev(h, "h", _B16),
         C.c_void_p(ws.data_ptr()), nb, _stream(stream)))
+    return y
+
+
+def verify_mlp_w4_noalloc(x, gate, up, down, y, h=None, stream=None):
+    """verify_mlp_w4 on the library's own device scratch (no workspace; the
+    caller passes the output y [R][H] fp32, and optionally h [R][I] bf16)."""
+    R, H = x.shape
+    I, G = gate.N, gate.G
+    if not (gate.K == up.K == down.N == H and up.N == down.K == I and up.G == down.G == G):
+        raise ValueError("inconsistent MLP matrix shapes")
+    _check(lib().verify_mlp_w4_noalloc(
+        _dev(x, "x", _B16), R, H, I, G, _dev(gate.blob, "gate", _U8), _dev(up.blob, "up", _U8),
+        _dev(down.blob, "down", _U8), _dev(y, "y", (torch.float32,)),
+        None if h is None else _dev(h, "h", _B16), _stream(stream)))
     return y
 
 

@@ -1336,3 +1336,43 @@ extern "C" int32_t verify_mlp_w4(const uint16_t* x, int32_t R, int32_t H, int32_
     return mlp_launches(x, R, H, I, G, w_gate, w_up, w_down, y, h_out, ws, stream);
 }
 
+// ---- the same slice for callers that cannot allocate ----------------------
+// Its workspace is `scratch`, a device array of the library (one per GPU,
+// held until the process ends).  Host code never passes the array's name to a
+// kernel: that is a host-side stand-in, not a device address.  The device
+// address is looked up once per device with hipGetSymbolAddress and kept.
+static __device__ __align__(256) unsigned char scratch[EV_MLP_SCRATCH_BYTES];
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[64];
+
+static int32_t scratch_on_current_device(void** out) {
+    int dev = -1;
+    int32_t rc;
+    if ((rc = check_hip(hipGetDevice(&dev), "hipGetDevice"))) return rc;
+    if (dev < 0 || dev >= 64) return fail(EV_EUNSUPPORTED, "device %d: only devices 0..63", dev);
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        if ((rc = check_hip(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "scratch address"))) return rc;
+        if (!p) return fail(EV_EHIP, "scratch address: NULL");
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return EV_OK;
+}
+
+extern "C" int32_t verify_mlp_w4_noalloc(const uint16_t* x, int32_t R, int32_t H, int32_t I, int32_t G,
+                                         const void* w_gate, const void* w_up, const void* w_down, float* y,
+                                         uint16_t* h_out, void* stream) {
+    clear_error();
+    const char* who = "verify_mlp_w4_noalloc";
+    int32_t rc;
+    if ((rc = check_mlp_args(who, x, R, H, I, G, w_gate, w_up, w_down, y, h_out))) return rc;
+    const size_t need = mlp_layout(H, I).total;
+    if (need > (size_t)EV_MLP_SCRATCH_BYTES)
+        return fail(EV_EWORKSPACE, "%s: H=%d I=%d needs %zu bytes of scratch, above the %zu of the library", who,
+                    H, I, need, (size_t)EV_MLP_SCRATCH_BYTES);
+    void* ws = nullptr;
+    if ((rc = scratch_on_current_device(&ws))) return rc;
+    return mlp_launches(x, R, H, I, G, w_gate, w_up, w_down, y, h_out, ws, stream);
+}

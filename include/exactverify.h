@@ -123,6 +123,28 @@ int32_t verify_mlp_w4(const uint16_t* x_bf16, int32_t R, int32_t H, int32_t I, i
                       float* y, uint16_t* h_bf16, void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------- */
+/* The MLP slice for callers that cannot allocate device memory: code under   */
+/* HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.   */
+/*                                                                            */
+/* verify_mlp_w4 without the workspace arguments: the same launches, results  */
+/* bit-identical to verify_mlp_w4's.  The workspace is a device array inside  */
+/* the library, EV_MLP_SCRATCH_BYTES long, one per GPU the library runs on,   */
+/* held until the process ends.  The call allocates nothing (no hipMalloc, no */
+/* allocating library routine); the first call on a device looks the array's */
+/* address up once.  Every call on one GPU shares that GPU's array, and the   */
+/* array keeps the last call's contents (nothing in it has to start at zero): */
+/* calls that overlap on one GPU, on any streams, race and must not be made.  */
+/* Limits: those of verify_mlp_w4, and verify_mlp_w4_workspace(H, I, G) <=    */
+/* EV_MLP_SCRATCH_BYTES (EV_EWORKSPACE otherwise; the MLP slice 5120 <->      */
+/* 17408 needs 24.5 MiB).  Errors: EV_EINVAL, EV_EUNSUPPORTED, EV_EWORKSPACE, */
+/* EV_EHIP.                                                                   */
+/* ------------------------------------------------------------------------- */
+#define EV_MLP_SCRATCH_BYTES (32u << 20)
+int32_t verify_mlp_w4_noalloc(const uint16_t* x_bf16, int32_t R, int32_t H, int32_t I, int32_t G,
+                              const void* gate_packed, const void* up_packed, const void* down_packed,
+                              float* y, uint16_t* h_bf16, void* stream);
+
+/* ------------------------------------------------------------------------- */
 /* MoE verify layer (top-`top` routing over E experts, SiLU-gated experts).   */
 /*                                                                            */
 /* The pages' MoE models (TensorFold README model notes; blog "The numbers":  */
