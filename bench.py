@@ -355,6 +355,38 @@ def leg_decoder(ev, syn, C, n_tokens=512, R=8, p_draft=0.65, cpu_steps=0):
             **({"cpu_baseline": cpu} if cpu else {})}
 
 
+def leg_prefill(ev, syn, C=4096, P=3584, grid=2048, reps=3):
+    """Grid-aligned chunked prefill of a P-token prompt into the 8-layer
+    decoder's cache (passes of at most 16 rows, never across a multiple of 16
+    or of the 2,048-token grid).  Bytes per pass: the layers' W4 weights plus
+    the cache entries read (attention over the slots before each pass's rows)."""
+    import numpy as np
+    import torch
+    d = syn.decoder(C=C, prefill=0)
+    cfg = d["cfg"]
+    m = ev.load_decoder(cfg, d["w"], d["kc"], d["vc"])
+    prompt = torch.from_numpy(np.random.default_rng(7).integers(0, cfg["vocab"], P).astype(np.int32)).cuda()
+    m.prefill(prompt[:64], 0, grid)  # warm-up (captures the pass graphs)
+    torch.cuda.synchronize()
+    t = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        m.prefill(prompt, 0, grid)
+        torch.cuda.synchronize()
+        t.append(time.perf_counter() - t0)
+    dt = min(t)
+    w_layers = sum(np.asarray(d["w"][k]).nbytes for k in d["w"]
+                   if k.endswith(("_q", "_s", "_b")) and not k.startswith("lm"))
+    passes = P // 16
+    kv = sum(2 * cfg["layers"] * cfg["kv_heads"] * (16 * i + 16) * cfg["head_dim"] * 2 for i in range(passes))
+    by = passes * w_layers + kv
+    roof = P * HBM_PEAK_GBS * 1e9 / by
+    tps = P / dt
+    return {"workload": f"prefill of a {P}-token prompt, 8-layer decoder H2048, cache {C}, grid {grid}",
+            "ms": round(1e3 * dt, 2), "tok_s": round(tps, 1), "passes": passes,
+            "roofline_tok_s": round(roof, 1), "pct_roofline": round(100 * tps / roof, 2)}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -548,6 +580,8 @@ def main():
         print("# decoder leg (cache 4096) done", file=sys.stderr, flush=True)
         legs["decoder_32768"] = leg_decoder(ev, syn, 32768, cpu_steps=0 if args.no_cpu_baseline else 16)
         print("# decoder leg (cache 32768) done", file=sys.stderr, flush=True)
+        legs["prefill_4096"] = leg_prefill(ev, syn)
+        print("# prefill leg done", file=sys.stderr, flush=True)
         out["legs"] = legs
         out["exact_accepted_tok_s"] = legs["decoder_4096"]["accepted_tok_s"]
     if not args.no_cpu_baseline:

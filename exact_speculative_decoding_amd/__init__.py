@@ -81,6 +81,7 @@ _SIGS = {
     "ev_read_probe": (_i32, [_vp, _sz, _vp, _vp]),
     "toy_decoder_set_graphs": (_i32, [_vp, _i32]),
     "toy_decoder_graph_stats": (_i32, [_vp, C.POINTER(_i64), C.POINTER(_i32)]),
+    "toy_decoder_prefill": (_i32, [_vp, _vp, _i32, _i64, _i32, _vp, _sz, _vp]),
     "verify_probe_workspace": (_sz, [_vp]),
     "verify_probe": (_i32, [_vp, _vp, _i32, _i64, Sampling, _vp, _vp, _sz, _vp]),
     "ev_w4_timing": (_i32, [_i32]),
@@ -353,6 +354,14 @@ class ToyDecoder:
     def set_graphs(self, enable):
         """Graph replay of verify_step on or off (on by default)."""
         _check(lib().toy_decoder_set_graphs(self._h, 1 if enable else 0))
+
+    def prefill(self, tokens, pos0, grid=2048, stream=None):
+        """Write the cache entries of slots pos0.. for tokens [n] int32 (device),
+        in grid-aligned passes of at most 16 rows."""
+        n = tokens.shape[0]
+        _check(lib().toy_decoder_prefill(self._h, _dev(tokens, "tokens", (torch.int32,)) if n else None, n,
+                                         int(pos0), int(grid), C.c_void_p(self.ws.data_ptr()), self.ws.numel(),
+                                         _stream(stream)))
 
     def verify_probe(self, tokens, pos0, temperature, top_k, top_p, seed, stream=None):
         """Words that differ between an R-row verify step over tokens [R] int32

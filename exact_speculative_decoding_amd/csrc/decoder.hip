@@ -481,6 +481,7 @@ using namespace ev;
 // A captured step (everything after embed_norm) for one set of baked
 // arguments; replayed on the caller's stream.
 struct StepGraph {
+    int kind;  // 0: a verify step after embed_norm; 1: a prefill pass's layers
     int R;
     const void* ws;
     int32_t* sampled;
@@ -658,7 +659,7 @@ extern "C" int32_t toy_decoder_set_graphs(ev_decoder* m, int32_t enable) {
 // embed_norm's copy, so the same launches can be captured once and replayed
 // at any position with any tokens.
 static int32_t step_body(ev_decoder* m, int R, int32_t* sampled, int32_t* n_commit, float* logits,
-                         unsigned char* b, hipStream_t st) {
+                         unsigned char* b, hipStream_t st, bool head = true) {
     int32_t rc;
     const StepLayout& L = m->L;
     const ev_decoder_config& c = m->cfg;
@@ -756,6 +757,7 @@ static int32_t step_body(ev_decoder* m, int R, int32_t* sampled, int32_t* n_comm
                            L.sk_down ? sk_geom(L.q_down) : no_sk, H, x, next, eps, n);
         if ((rc = check_hip(hipGetLastError(), "res_norm launch"))) return rc;
     }
+    if (!head) return EV_OK;  // prefill: the layers only (their cache entries)
     if ((rc = linear(m->w_lm, n, H, V, L.p_lm, L.q_lm, L.sk_lm))) return rc;
     if (L.sk_lm) {
         if ((rc = launch_sk_reduce(part, L.q_lm, 1, V, R, lg, nullptr, nullptr, st))) return rc;
@@ -775,9 +777,9 @@ static int32_t step_body(ev_decoder* m, int R, int32_t* sampled, int32_t* n_comm
 // The captured step for these arguments: found in the cache, or captured on
 // the decoder's own stream (nothing runs during capture) and kept.
 static int32_t step_graph(ev_decoder* m, int R, int32_t* sampled, int32_t* n_commit, void* ws,
-                          hipGraphExec_t* out) {
+                          hipGraphExec_t* out, int kind = 0) {
     for (const StepGraph& g : m->graphs)
-        if (g.R == R && g.ws == ws && g.sampled == sampled && g.n_commit == n_commit) {
+        if (g.kind == kind && g.R == R && g.ws == ws && g.sampled == sampled && g.n_commit == n_commit) {
             *out = g.exec;
             return EV_OK;
         }
@@ -786,7 +788,7 @@ static int32_t step_graph(ev_decoder* m, int R, int32_t* sampled, int32_t* n_com
         return rc;
     if ((rc = check_hip(hipStreamBeginCapture(m->capture, hipStreamCaptureModeThreadLocal), "begin capture")))
         return rc;
-    rc = step_body(m, R, sampled, n_commit, nullptr, reinterpret_cast<unsigned char*>(ws), m->capture);
+    rc = step_body(m, R, sampled, n_commit, nullptr, reinterpret_cast<unsigned char*>(ws), m->capture, kind == 0);
     hipGraph_t graph = nullptr;
     const hipError_t end = hipStreamEndCapture(m->capture, &graph);
     if (!rc) rc = check_hip(end, "end capture");
@@ -802,7 +804,7 @@ static int32_t step_graph(ev_decoder* m, int R, int32_t* sampled, int32_t* n_com
         (void)hipGraphExecDestroy(m->graphs.front().exec);
         m->graphs.erase(m->graphs.begin());
     }
-    m->graphs.push_back(StepGraph{R, ws, sampled, n_commit, exec});
+    m->graphs.push_back(StepGraph{kind, R, ws, sampled, n_commit, exec});
     ++m->captures;
     *out = exec;
     return EV_OK;
@@ -845,6 +847,58 @@ extern "C" int32_t verify_step(ev_decoder* m, const int32_t* tokens, int32_t R, 
         return check_hip(hipGraphLaunch(exec, st), "step graph launch");
     }
     return step_body(m, R, sampled, n_commit, logits, b, st);
+}
+
+// Grid-aligned chunked prefill (650 Group, "Faster, provably the same model",
+// "The regression it published against itself": prompts processed in chunks
+// aligned to a fixed grid of 2,048 tokens, caches kept only at grid points, so
+// that a chunk's bits do not depend on where a conversation resumed).  The
+// inputs tokens[0..n) go to slots pos0 .. pos0+n-1 in passes of at most 16
+// rows that never cross a multiple of 16 or of `grid`, so a pass's rows are a
+// function of the absolute slots alone; each pass is the verify step's
+// embedding and layers (no LM head, no sampling), replayed from a captured
+// graph per row count.
+extern "C" int32_t toy_decoder_prefill(ev_decoder* m, const int32_t* tokens, int32_t n, int64_t pos0, int32_t grid,
+                                       void* ws, size_t ws_bytes, void* stream) {
+    clear_error();
+    const char* who = "toy_decoder_prefill";
+    int32_t rc;
+    if (!m) return fail(EV_EINVAL, "%s: NULL decoder", who);
+    if (n < 0 || (n > 0 && !tokens)) return fail(EV_EINVAL, "%s: n=%d or NULL tokens", who, n);
+    if (n > 0 && !aligned(tokens, 4)) return fail(EV_EINVAL, "%s: misaligned tokens", who);
+    if (grid < 16 || grid % 16 != 0) return fail(EV_EINVAL, "%s: grid=%d (a positive multiple of 16)", who, grid);
+    if (pos0 < 0 || pos0 + n > m->C)
+        return fail(EV_EINVAL, "%s: slots %lld..%lld outside the cache of %d", who, (long long)pos0,
+                    (long long)pos0 + n - 1, m->C);
+    const StepLayout& L = m->L;
+    if ((rc = check_ws(who, ws, ws_bytes, L.total))) return rc;
+    const ev_decoder_config& c = m->cfg;
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    unsigned char* b = reinterpret_cast<unsigned char*>(ws);
+    const ev_sampling none{0.0, 1, 1.0, 0};
+    for (long long p = pos0; p < pos0 + n;) {
+        long long e = (p / 16 + 1) * 16;
+        const long long g = (p / grid + 1) * grid;
+        if (g < e) e = g;
+        if (pos0 + n < e) e = pos0 + n;
+        const int R = (int)(e - p);
+        hipLaunchKernelGGL(embed_norm_kernel, dim3(R), dim3(kRowThreads), 0, st, tokens + (p - pos0), m->embed,
+                           c.hidden, c.vocab, m->layers[0].attn_norm, (float)c.rms_eps,
+                           reinterpret_cast<float*>(b + L.off_x), reinterpret_cast<uint16_t*>(b + L.off_n),
+                           reinterpret_cast<long long*>(b + L.off_pos), p, reinterpret_cast<int*>(b + L.off_tok),
+                           none, reinterpret_cast<ev_sampling*>(b + L.off_samp));
+        if ((rc = check_hip(hipGetLastError(), "embed_norm launch"))) return rc;
+        if (m->use_graphs && !w4_timing_active()) {
+            std::lock_guard<std::mutex> lk(m->graph_mu);
+            hipGraphExec_t exec;
+            if ((rc = step_graph(m, R, nullptr, nullptr, ws, &exec, 1))) return rc;
+            if ((rc = check_hip(hipGraphLaunch(exec, st), "prefill graph launch"))) return rc;
+        } else if ((rc = step_body(m, R, nullptr, nullptr, nullptr, b, st, false))) {
+            return rc;
+        }
+        p = e;
+    }
+    return EV_OK;
 }
 
 extern "C" int32_t toy_decoder_graph_stats(const ev_decoder* m, int64_t* captures, int32_t* cached) {

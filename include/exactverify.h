@@ -339,6 +339,24 @@ int32_t verify_step(ev_decoder* m, const int32_t* tokens, int32_t R, int64_t pos
 /* step launched kernel by kernel).  Errors: EV_EINVAL (NULL handle).         */
 int32_t toy_decoder_set_graphs(ev_decoder* m, int32_t enable);
 
+/* Grid-aligned chunked prefill (650 Group, "Faster, provably the same       */
+/* model", section "The regression it published against itself": a prompt is */
+/* processed in chunks aligned to a fixed grid of 2,048 tokens and prompt     */
+/* caches are kept only at grid points, so that a chunk's bits do not depend  */
+/* on where a conversation resumed).  Writes the cache entries of slots       */
+/* pos0 .. pos0+n-1 for the input tokens[0..n) (device, int32, values in      */
+/* [0, V)), in passes of at most 16 rows that never cross a multiple of 16 or */
+/* of grid (a positive multiple of 16); each pass is a verify step's          */
+/* embedding and layers without the LM head or sampling.  Every row is        */
+/* row-exact, so the entries are bit-identical to those serial decoding       */
+/* writes for the same tokens, and a prefill resumed from a cache copied at   */
+/* any slot reproduces a fresh one.  The first decoding step after a prompt   */
+/* t_0 .. t_{P-1} prefilled up to slot P-2 is verify_step(t_{P-1}, pos0 =     */
+/* P-1).  ws: verify_step_workspace(m) bytes.  Errors: EV_EINVAL (slots       */
+/* outside the cache, grid, pointers), EV_EWORKSPACE, EV_EHIP.                */
+int32_t toy_decoder_prefill(ev_decoder* m, const int32_t* tokens, int32_t n, int64_t pos0, int32_t grid,
+                            void* ws, size_t ws_bytes, void* stream);
+
 /* How many steps the handle has captured since it was created (captures,    */
 /* host, may be NULL) and how many it holds now (cached, host, may be NULL).  */
 /* Errors: EV_EINVAL (NULL handle).                                           */
