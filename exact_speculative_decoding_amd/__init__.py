@@ -82,6 +82,8 @@ _SIGS = {
     "toy_decoder_set_graphs": (_i32, [_vp, _i32]),
     "toy_decoder_graph_stats": (_i32, [_vp, C.POINTER(_i64), C.POINTER(_i32)]),
     "toy_decoder_prefill": (_i32, [_vp, _vp, _i32, _i64, _i32, _vp, _sz, _vp]),
+    "toy_decoder_draft_workspace": (_sz, [_vp]),
+    "toy_decoder_draft": (_i32, [_vp, _vp, _vp, _vp, _i32, C.c_double, _vp, _vp, _vp, _vp, _sz, _vp]),
     "verify_probe_workspace": (_sz, [_vp]),
     "verify_probe": (_i32, [_vp, _vp, _i32, _i64, Sampling, _vp, _vp, _sz, _vp]),
     "ev_w4_timing": (_i32, [_i32]),
@@ -354,6 +356,48 @@ class ToyDecoder:
     def set_graphs(self, enable):
         """Graph replay of verify_step on or off (on by default)."""
         _check(lib().toy_decoder_set_graphs(self._h, 1 if enable else 0))
+
+    def draft(self, head, n_commit, sampled, max_drafts, min_conf, drafts, n_drafts, stream=None):
+        """The MTP-style draft chain after a verify step (device tensors: the
+        step's n_commit [1] and sampled [R]; outputs drafts [max_drafts] and
+        n_drafts [1] int32)."""
+        if getattr(self, "_dws", None) is None:
+            self._dws = torch.empty(int(lib().toy_decoder_draft_workspace(self._h)), dtype=torch.uint8,
+                                    device=self.ws.device)
+        _check(lib().toy_decoder_draft(
+            self._h, _dev(head.blob, "w_draft", _U8), _dev(n_commit, "n_commit", (torch.int32,)),
+            _dev(sampled, "sampled", (torch.int32,)), int(max_drafts), float(min_conf),
+            _dev(drafts, "drafts", (torch.int32,)), _dev(n_drafts, "n_drafts", (torch.int32,)),
+            C.c_void_p(self.ws.data_ptr()), C.c_void_p(self._dws.data_ptr()), self._dws.numel(),
+            _stream(stream)))
+
+    def verify_and_draft_host(self, tokens, pos0, temperature, top_k, top_p, seed, head, max_drafts,
+                              min_conf=0.3):
+        """One round for a host loop with an MTP-style head: verify `tokens`
+        (a list), then draft the next round's tokens from the last committed
+        row.  One upload, one read-back; returns (sampled tokens, n_commit,
+        the next round's drafts)."""
+        R = len(tokens)
+        key = ("mtp", R, max_drafts)
+        io = self._host_io.get(key)
+        if io is None:
+            dev = self.ws.device
+            n = R + 2 + max_drafts
+            io = (torch.empty(R, dtype=torch.int32, pin_memory=True), torch.empty(R, dtype=torch.int32, device=dev),
+                  torch.empty(n, dtype=torch.int32, device=dev), torch.empty(n, dtype=torch.int32, pin_memory=True))
+            self._host_io[key] = io
+        tok_h, tok_d, out_d, out_h = io
+        tok_h.numpy()[:] = tokens
+        tok_d.copy_(tok_h, non_blocking=True)
+        sampled, n_commit = out_d[:R], out_d[R:R + 1]
+        drafts, n_drafts = out_d[R + 1:R + 1 + max_drafts], out_d[R + 1 + max_drafts:]
+        self.verify_step(tok_d, pos0, temperature, top_k, top_p, seed, sampled=sampled, n_commit=n_commit)
+        self.draft(head, n_commit, sampled, max_drafts, min_conf, drafts, n_drafts)
+        out_h.copy_(out_d, non_blocking=True)
+        torch.cuda.current_stream(self.ws.device).synchronize()
+        o = out_h.numpy()
+        nd = int(o[R + 1 + max_drafts])
+        return o[:R].tolist(), int(o[R]), o[R + 1:R + 1 + nd].tolist()
 
     def prefill(self, tokens, pos0, grid=2048, stream=None):
         """Write the cache entries of slots pos0.. for tokens [n] int32 (device),

@@ -1052,3 +1052,180 @@ extern "C" int32_t verify_probe(ev_decoder* m, const int32_t* tokens, int32_t R,
     hipLaunchKernelGGL(probe_result_kernel, dim3(1), dim3(64), 0, st, cnt, mismatch);
     return check_hip(hipGetLastError(), "probe compare launch");
 }
+
+// ---- MTP-style draft chain ----------------------------------------------------
+// The TensorFold README's options table: --mtp-drafts N caps the drafts a
+// round (3, or 6 on CUDA), and on CUDA the chain also stops under 30 %
+// confidence.  The head here is the simplest multi-token-prediction head on
+// the decoder's own parts: from the final-normed hidden row h of the last
+// committed token t,
+//   a = bf16(h + embed[t]);  z = W_draft a  (W4, H -> H);
+//   h' = bf16(RMSNorm(z) * final_norm);  logits = W_lm h'  (the shared head);
+//   draft = argmax logits (lower id on ties), confidence = its softmax
+//   probability 1 / sum_j exp(l_j - l_max);
+// then again from (h', draft).  Drafts only change how many rows a round
+// verifies, never what is committed.
+
+namespace ev {
+namespace {
+
+struct DraftLayout {
+    size_t off_a, off_z, off_h, off_logits, off_state, off_lin, total;
+};
+
+DraftLayout draft_layout(const ev_decoder_config& c) {
+    DraftLayout D;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t o = off;
+        off += align256(bytes);
+        return o;
+    };
+    D.off_a = take(sizeof(uint16_t) * (size_t)c.hidden);
+    D.off_z = take(sizeof(float) * (size_t)c.hidden);
+    D.off_h = take(sizeof(uint16_t) * (size_t)c.hidden);
+    D.off_logits = take(sizeof(float) * (size_t)c.vocab);
+    D.off_state = take(sizeof(int32_t) * 4);
+    D.off_lin = take(std::max(verify_linear_w4_workspace(c.hidden, c.hidden, c.group),
+                              verify_linear_w4_workspace(c.hidden, c.vocab, c.group)));
+    D.total = off;
+    return D;
+}
+
+}  // namespace
+
+// state[0] = 1 once the chain has stopped; n_drafts = 0.
+__global__ void draft_init_kernel(int32_t* __restrict__ state, int32_t* __restrict__ n_drafts) {
+    if (threadIdx.x == 0) {
+        state[0] = 0;
+        n_drafts[0] = 0;
+    }
+}
+
+// a = bf16(h + embed[t]), one row: draft 0 starts from the verify step's row
+// n_commit - 1 (its final-normed hidden and its sample), later drafts from the
+// previous draft's h' and token.
+__global__ __launch_bounds__(kRowThreads) void draft_input_kernel(
+    const uint16_t* __restrict__ nrows, const int32_t* __restrict__ n_commit, const int32_t* __restrict__ sampled,
+    const uint16_t* __restrict__ h_prev, const int32_t* __restrict__ drafts, int i, const uint16_t* __restrict__ embed,
+    int H, int V, const int32_t* __restrict__ state, uint16_t* __restrict__ a) {
+    if (state[0]) return;  // the chain has stopped: nothing of this draft is used
+    const int nc = n_commit[0];
+    const uint16_t* h = i == 0 ? nrows + (size_t)(nc - 1) * H : h_prev;
+    int t = i == 0 ? sampled[nc - 1] : drafts[i - 1];
+    t = t < 0 ? 0 : (t >= V ? V - 1 : t);
+    const uint16_t* e = embed + (size_t)t * H;
+    for (int c = threadIdx.x; c < H; c += kRowThreads) a[c] = f32_to_bf16_rne(bf16_to_f32(h[c]) + bf16_to_f32(e[c]));
+}
+
+// h' = bf16(RMSNorm(z) * gain), one row.
+__global__ __launch_bounds__(kRowThreads) void draft_norm_kernel(const float* __restrict__ z, int H,
+                                                                 const float* __restrict__ gain, float eps,
+                                                                 const int32_t* __restrict__ state,
+                                                                 uint16_t* __restrict__ h) {
+    __shared__ float red[kRowThreads / 64];
+    if (state[0]) return;
+    f32x4 xv[kMaxRowVec];
+    float ss = 0.f;
+#pragma unroll
+    for (int j = 0; j < kMaxRowVec; ++j) {
+        const int c = 4 * (threadIdx.x + kRowThreads * j);
+        xv[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (c >= H) continue;
+        xv[j] = *reinterpret_cast<const f32x4*>(z + c);
+        ss += xv[j][0] * xv[j][0] + xv[j][1] * xv[j][1] + xv[j][2] * xv[j][2] + xv[j][3] * xv[j][3];
+    }
+    norm_store(xv, ss, gain, eps, H, h, red);
+}
+
+// drafts[i] = argmax of the logits row (lower id on ties); its confidence p =
+// 1 / sum_j exp(l_j - l_max), summed in a fixed order.  The chain keeps the
+// draft while p >= min_conf and stops at the first draft below it.
+__global__ __launch_bounds__(1024) void draft_pick_kernel(const float* __restrict__ logits, int V, int i,
+                                                          float min_conf, int32_t* __restrict__ state,
+                                                          int32_t* __restrict__ drafts,
+                                                          int32_t* __restrict__ n_drafts) {
+    __shared__ unsigned long long kred[16];
+    __shared__ float fred[16];
+    if (state[0]) return;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    unsigned long long best = 0ull;
+    for (int j = tid; j < V; j += 1024) {
+        const unsigned long long k = order_key(logits[j], j);
+        best = k > best ? k : best;
+    }
+    best = wave_max_u64(best);
+    if (lane == 0) kred[w] = best;
+    __syncthreads();
+    unsigned long long top = kred[0];
+    for (int u = 1; u < 16; ++u) top = kred[u] > top ? kred[u] : top;
+    const float lmax = key_logit(top);
+    float sum = 0.f;  // each thread in ascending j, then the waves' sums in a fixed tree
+    for (int j = tid; j < V; j += 1024) sum += expf(logits[j] - lmax);
+    for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off, 64);
+    if (lane == 0) fred[w] = sum;
+    __syncthreads();
+    if (tid == 0) {
+        float z = 0.f;
+        for (int u = 0; u < 16; ++u) z += fred[u];
+        const float p = 1.0f / z;
+        drafts[i] = key_id(top);
+        if (p >= min_conf)
+            n_drafts[0] = i + 1;
+        else
+            state[0] = 1;
+    }
+}
+
+}  // namespace ev
+
+extern "C" size_t toy_decoder_draft_workspace(const ev_decoder* m) { return m ? draft_layout(m->cfg).total : 0; }
+
+extern "C" int32_t toy_decoder_draft(ev_decoder* m, const void* w_draft, const int32_t* n_commit,
+                                     const int32_t* sampled, int32_t max_drafts, double min_conf, int32_t* drafts,
+                                     int32_t* n_drafts, const void* step_ws, void* ws, size_t ws_bytes,
+                                     void* stream) {
+    clear_error();
+    const char* who = "toy_decoder_draft";
+    int32_t rc;
+    if (!m) return fail(EV_EINVAL, "%s: NULL decoder", who);
+    if (!w_draft || !n_commit || !sampled || !drafts || !n_drafts || !step_ws)
+        return fail(EV_EINVAL, "%s: NULL pointer", who);
+    if (!aligned(w_draft, 16) || !aligned(n_commit, 4) || !aligned(sampled, 4) || !aligned(drafts, 4) ||
+        !aligned(n_drafts, 4) || !aligned(step_ws, 256))
+        return fail(EV_EINVAL, "%s: misaligned pointer", who);
+    if (max_drafts < 1 || max_drafts > EV_MAX_LANES - 1)
+        return fail(EV_EINVAL, "%s: max_drafts=%d outside 1..15", who, max_drafts);
+    if (!(min_conf >= 0.0 && min_conf <= 1.0)) return fail(EV_EINVAL, "%s: min_conf outside [0, 1]", who);
+    const DraftLayout D = draft_layout(m->cfg);
+    if ((rc = check_ws(who, ws, ws_bytes, D.total))) return rc;
+    const ev_decoder_config& c = m->cfg;
+    const int H = c.hidden, V = c.vocab, G = c.group;
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    unsigned char* b = reinterpret_cast<unsigned char*>(ws);
+    uint16_t* a = reinterpret_cast<uint16_t*>(b + D.off_a);
+    float* z = reinterpret_cast<float*>(b + D.off_z);
+    uint16_t* h = reinterpret_cast<uint16_t*>(b + D.off_h);
+    float* lg = reinterpret_cast<float*>(b + D.off_logits);
+    int32_t* state = reinterpret_cast<int32_t*>(b + D.off_state);
+    void* lin = b + D.off_lin;
+    const size_t lin_bytes = D.total - D.off_lin;
+    const uint16_t* nrows = reinterpret_cast<const uint16_t*>(reinterpret_cast<const unsigned char*>(step_ws) +
+                                                              m->L.off_n);
+    hipLaunchKernelGGL(draft_init_kernel, dim3(1), dim3(64), 0, st, state, n_drafts);
+    if ((rc = check_hip(hipGetLastError(), "draft init launch"))) return rc;
+    for (int i = 0; i < max_drafts; ++i) {
+        hipLaunchKernelGGL(draft_input_kernel, dim3(1), dim3(kRowThreads), 0, st, nrows, n_commit, sampled, h,
+                           drafts, i, m->embed, H, V, state, a);
+        if ((rc = check_hip(hipGetLastError(), "draft input launch"))) return rc;
+        if ((rc = verify_linear_w4(a, 1, H, w_draft, H, G, z, lin, lin_bytes, stream))) return rc;
+        hipLaunchKernelGGL(draft_norm_kernel, dim3(1), dim3(kRowThreads), 0, st, z, H, m->final_norm,
+                           (float)c.rms_eps, state, h);
+        if ((rc = check_hip(hipGetLastError(), "draft norm launch"))) return rc;
+        if ((rc = verify_linear_w4(h, 1, H, m->w_lm, V, G, lg, lin, lin_bytes, stream))) return rc;
+        hipLaunchKernelGGL(draft_pick_kernel, dim3(1), dim3(1024), 0, st, lg, V, i, (float)min_conf, state, drafts,
+                           n_drafts);
+        if ((rc = check_hip(hipGetLastError(), "draft pick launch"))) return rc;
+    }
+    return EV_OK;
+}

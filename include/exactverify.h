@@ -357,6 +357,31 @@ int32_t toy_decoder_set_graphs(ev_decoder* m, int32_t enable);
 int32_t toy_decoder_prefill(ev_decoder* m, const int32_t* tokens, int32_t n, int64_t pos0, int32_t grid,
                             void* ws, size_t ws_bytes, void* stream);
 
+/* MTP-style draft chain (TensorFold README options table: --mtp-drafts N    */
+/* caps the drafts of a round; on CUDA the chain also stops under 30 %        */
+/* confidence).  Run after a verify_step on the same stream, with that step's */
+/* workspace (step_ws) and its n_commit and sampled outputs (device): from    */
+/* the final-normed hidden row h of row n_commit-1 and its sample t, for i =  */
+/* 0 .. max_drafts-1:                                                         */
+/*   a = bf16(h + embed[t]);  z = W_draft a  (W4, hidden x hidden);           */
+/*   h = bf16(RMSNorm(z) * final_norm);  logits = W_lm h;                     */
+/*   t = drafts[i] = argmax logits (lower id on ties), with confidence        */
+/*   p = 1 / sum_j exp(l_j - l_max);                                          */
+/* n_drafts (device, [1]) = the number of leading drafts with p >= min_conf   */
+/* (the chain stops at the first one below it).  The next round verifies     */
+/* [sampled[n_commit-1], drafts[0 .. n_drafts-1]].  Drafts change how many    */
+/* rows are verified, never the committed tokens.                             */
+/*   w_draft  (device) packed hidden x hidden W4 matrix (w4_pack), 16-B       */
+/*            aligned, group as the decoder's.                                */
+/*   drafts   (device) [max_drafts] int32, written up to the stop.            */
+/*   ws       (device) toy_decoder_draft_workspace(m) bytes, 256-B aligned.   */
+/* Limits: 1 <= max_drafts <= 15, 0 <= min_conf <= 1.  Errors: EV_EINVAL,     */
+/* EV_EWORKSPACE, EV_EHIP.                                                    */
+size_t toy_decoder_draft_workspace(const ev_decoder* m);
+int32_t toy_decoder_draft(ev_decoder* m, const void* w_draft, const int32_t* n_commit, const int32_t* sampled,
+                          int32_t max_drafts, double min_conf, int32_t* drafts, int32_t* n_drafts,
+                          const void* step_ws, void* ws, size_t ws_bytes, void* stream);
+
 /* How many steps the handle has captured since it was created (captures,    */
 /* host, may be NULL) and how many it holds now (cached, host, may be NULL).  */
 /* Errors: EV_EINVAL (NULL handle).                                           */

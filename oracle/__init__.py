@@ -315,4 +315,4 @@ def moe(x, rho, top, G, gate, up, down):
 
 # --- decoder (oracle/decoder.c) ---------------------------------------------
 
-from .decoder import Decoder, attend, drafted_decode, rmsnorm_bf16, rope, serial_decode  # noqa: E402,F401
+from .decoder import Decoder, attend, draft_chain, drafted_decode, rmsnorm_bf16, rope, serial_decode  # noqa: E402,F401

@@ -143,10 +143,10 @@ void ov_attend(const float* q, const uint16_t* K, const uint16_t* V, int n, int 
  * token sampled there. */
 enum { CI_L, CI_H, CI_NH, CI_NKV, CI_D, CI_I, CI_V, CI_G };
 
-void ov_decoder_step(const int32_t* ci, const double* cd, const void* const* w,
-                     uint16_t* kc, uint16_t* vc, int C, int32_t token, int64_t p,
-                     double T, int top_k, double top_p, uint64_t seed,
-                     float* logits, int32_t* token_out, double* gap_out)
+void ov_decoder_step_h(const int32_t* ci, const double* cd, const void* const* w,
+                       uint16_t* kc, uint16_t* vc, int C, int32_t token, int64_t p,
+                       double T, int top_k, double top_p, uint64_t seed,
+                       float* logits, int32_t* token_out, double* gap_out, uint16_t* hidden_out)
 {
     const int L = ci[CI_L], H = ci[CI_H], NH = ci[CI_NH], NKV = ci[CI_NKV], D = ci[CI_D];
     const int I = ci[CI_I], V = ci[CI_V], G = ci[CI_G];
@@ -211,6 +211,7 @@ void ov_decoder_step(const int32_t* ci, const double* cd, const void* const* w,
     }
 
     ov_rmsnorm_bf16(x, H, fn, eps, nb);
+    if (hidden_out) memcpy(hidden_out, nb, sizeof(uint16_t) * (size_t)H); /* the LM head's input */
     ov_w4_linear_f32(nb, 1, H, (const uint8_t*)w[19], (const uint16_t*)w[20],
                      (const uint16_t*)w[21], V, G, logits);
     ov_sample_out so;
@@ -223,3 +224,13 @@ void ov_decoder_step(const int32_t* ci, const double* cd, const void* const* w,
     free(nb);
     free(o);
 }
+
+/* The step without the hidden row. */
+void ov_decoder_step(const int32_t* ci, const double* cd, const void* const* w,
+                     uint16_t* kc, uint16_t* vc, int C, int32_t token, int64_t p,
+                     double T, int top_k, double top_p, uint64_t seed,
+                     float* logits, int32_t* token_out, double* gap_out)
+{
+    ov_decoder_step_h(ci, cd, w, kc, vc, C, token, p, T, top_k, top_p, seed, logits, token_out, gap_out, NULL);
+}
+

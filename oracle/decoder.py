@@ -14,6 +14,8 @@ def declare(L):
     L.ov_attend.argtypes = [P(f32), P(u16), P(u16), i32, i32, P(f64)]
     L.ov_decoder_step.argtypes = [P(i32), P(f64), P(C.c_void_p), P(u16), P(u16), i32, i32, i64,
                                   f64, i32, f64, C.c_uint64, P(f32), P(i32), P(f64)]
+    L.ov_decoder_step_h.argtypes = [P(i32), P(f64), P(C.c_void_p), P(u16), P(u16), i32, i32, i64,
+                                    f64, i32, f64, C.c_uint64, P(f32), P(i32), P(f64), P(u16)]
 
 
 def _lib():
@@ -77,18 +79,22 @@ class Decoder:
         self.vc = np.array(vc, np.uint16, copy=True)
         self.C = self.kc.shape[2]
 
-    def step(self, token, pos, T, top_k, top_p, seed):
+    def step(self, token, pos, T, top_k, top_p, seed, hidden=False):
         """Token at slot `pos` -> (logits of position pos + 1 [V] fp32, the token
-        sampled there, its gap).  Writes slot `pos` of the caches."""
+        sampled there, its gap), and with hidden=True also the final-normed
+        hidden row (the LM head's bf16 input).  Writes slot `pos` of the caches."""
         V = self.cfg["vocab"]
         logits = np.empty(V, np.float32)
         tok = np.zeros(1, np.int32)
         gap = np.zeros(1, np.float64)
-        _lib().ov_decoder_step(_ptr(self.ci, np.int32), _ptr(self.cd, np.float64), self.tab,
-                               _ptr(self.kc, np.uint16), _ptr(self.vc, np.uint16), self.C,
-                               int(token), int(pos), float(T), int(top_k), float(top_p),
-                               int(seed) & ((1 << 64) - 1), _ptr(logits, np.float32),
-                               _ptr(tok, np.int32), _ptr(gap, np.float64))
+        h = np.empty(self.cfg["hidden"], np.uint16)
+        _lib().ov_decoder_step_h(_ptr(self.ci, np.int32), _ptr(self.cd, np.float64), self.tab,
+                                 _ptr(self.kc, np.uint16), _ptr(self.vc, np.uint16), self.C,
+                                 int(token), int(pos), float(T), int(top_k), float(top_p),
+                                 int(seed) & ((1 << 64) - 1), _ptr(logits, np.float32),
+                                 _ptr(tok, np.int32), _ptr(gap, np.float64), _ptr(h, np.uint16))
+        if hidden:
+            return logits, int(tok[0]), float(gap[0]), h
         return logits, int(tok[0]), float(gap[0])
 
 
@@ -135,3 +141,37 @@ def drafted_decode(m, first_token, slot0, n, R, drafter, sampling):
         last = samples[keep - 1]
         rounds += 1
     return s, rounds
+
+
+def draft_chain(cfg, weights, w_draft, hidden, token, max_drafts, min_conf):
+    """The MTP-style draft chain, one draft at a time, from the final-normed
+    hidden row `hidden` (bf16 bits) of the last committed token `token`:
+    a = bf16(h + embed[t]); z = W_draft a (W4, fp32 out); h = bf16(RMSNorm(z)
+    * final_norm); logits = W_lm h; the draft is the argmax (lower id on
+    ties) and its confidence the softmax probability 1 / sum_j exp(l_j - l_max)
+    (fp64).  The chain stops at the first draft whose confidence is below
+    min_conf.  Returns (drafts kept, every draft's (token, confidence, gap
+    between the two best logits)) for all max_drafts steps."""
+    from . import f64_to_bf16, w4_linear
+    G, eps = cfg["G"], cfg["eps"]
+    embed = np.asarray(weights["embed"], np.uint16)
+    h, t = np.asarray(hidden, np.uint16), int(token)
+    steps, kept, stopped = [], [], False
+    for _ in range(max_drafts):
+        hv = (np.asarray(h, np.uint32) << 16).view(np.float32).astype(np.float64)
+        ev_ = (np.asarray(embed[t], np.uint32) << 16).view(np.float32).astype(np.float64)
+        a = f64_to_bf16(hv + ev_)  # the exact sum, rounded once
+        z = w4_linear(a[None], *w_draft, G, out_f32=True)[0]
+        h = rmsnorm_bf16(z, weights["final_norm"], eps)
+        logits = w4_linear(h[None], weights["lm_q"], weights["lm_s"], weights["lm_b"], G, out_f32=True)[0]
+        l = logits.astype(np.float64)
+        t = int(np.argmax(l))
+        p = 1.0 / np.sum(np.exp(l - l[t]))
+        top2 = np.sort(l)[-2:]
+        steps.append((t, float(p), float(top2[1] - top2[0])))
+        if not stopped and p >= min_conf:
+            kept.append(t)
+        else:
+            stopped = True
+    return kept, steps
+

@@ -179,3 +179,10 @@ def random_drafter(seed, V):
     def draft(position, count):
         return [int(rng((seed, q)).integers(0, V)) for q in range(position, position + count)]
     return draft
+
+
+def draft_head(seed, hidden, G):
+    """W4 weights of a random-init MTP-style draft head (hidden x hidden), in
+    the cfg-2 distributions (standard layout q, s, b)."""
+    return w4_matrix(rng(seed), hidden, hidden, G)
+
