@@ -481,7 +481,8 @@ using namespace ev;
 // A captured step (everything after embed_norm) for one set of baked
 // arguments; replayed on the caller's stream.
 struct StepGraph {
-    int kind;  // 0: a verify step after embed_norm; 1: a prefill pass's layers
+    int kind;  // 0: a verify step after embed_norm (top-k sampler); 1: a prefill pass's layers;
+             // 2: a verify step whose sampler takes top-p over the whole vocabulary
     int R;
     const void* ws;
     int32_t* sampled;
@@ -659,7 +660,7 @@ extern "C" int32_t toy_decoder_set_graphs(ev_decoder* m, int32_t enable) {
 // embed_norm's copy, so the same launches can be captured once and replayed
 // at any position with any tokens.
 static int32_t step_body(ev_decoder* m, int R, int32_t* sampled, int32_t* n_commit, float* logits,
-                         unsigned char* b, hipStream_t st, bool head = true) {
+                         unsigned char* b, hipStream_t st, bool head = true, bool topp_full = false) {
     int32_t rc;
     const StepLayout& L = m->L;
     const ev_decoder_config& c = m->cfg;
@@ -766,8 +767,9 @@ static int32_t step_body(ev_decoder* m, int R, int32_t* sampled, int32_t* n_comm
     }
     void* sv = reinterpret_cast<void*>(st);
     // the sampling parameters come from the workspace (written by embed_norm);
-    // the host value only bounds the launch and is never read by the kernels
-    const ev_sampling any{1.0, EV_MAX_TOPK, 1.0, 0};
+    // the host value only picks the launch sequence (top-k candidates, or top-p
+    // over the whole vocabulary) and is never read by the kernels
+    const ev_sampling any{1.0, topp_full ? 0 : EV_MAX_TOPK, 1.0, 0};
     if ((rc = launch_keyed_sample(lg, R, V, pos, any, reinterpret_cast<const ev_sampling*>(b + L.off_samp), sampled,
                                   nullptr, sws, st)))
         return rc;
@@ -788,7 +790,8 @@ static int32_t step_graph(ev_decoder* m, int R, int32_t* sampled, int32_t* n_com
         return rc;
     if ((rc = check_hip(hipStreamBeginCapture(m->capture, hipStreamCaptureModeThreadLocal), "begin capture")))
         return rc;
-    rc = step_body(m, R, sampled, n_commit, nullptr, reinterpret_cast<unsigned char*>(ws), m->capture, kind == 0);
+    rc = step_body(m, R, sampled, n_commit, nullptr, reinterpret_cast<unsigned char*>(ws), m->capture, kind != 1,
+                   kind == 2);
     hipGraph_t graph = nullptr;
     const hipError_t end = hipStreamEndCapture(m->capture, &graph);
     if (!rc) rc = check_hip(end, "end capture");
@@ -838,15 +841,16 @@ extern "C" int32_t verify_step(ev_decoder* m, const int32_t* tokens, int32_t R, 
                        (long long)pos0, reinterpret_cast<int*>(b + L.off_tok), sampling,
                        reinterpret_cast<ev_sampling*>(b + L.off_samp));
     if ((rc = check_hip(hipGetLastError(), "embed_norm launch"))) return rc;
+    const bool topp_full = sampling.temperature > 0.0 && sampling.top_k == 0;
     // the rest: one graph launch when the step can be replayed as captured
     // (no logits asked for, no per-launch measurement), else launch by launch
     if (m->use_graphs && !logits && !w4_timing_active()) {
         std::lock_guard<std::mutex> lk(m->graph_mu);
         hipGraphExec_t exec;
-        if ((rc = step_graph(m, R, sampled, n_commit, ws, &exec))) return rc;
+        if ((rc = step_graph(m, R, sampled, n_commit, ws, &exec, topp_full ? 2 : 0))) return rc;
         return check_hip(hipGraphLaunch(exec, st), "step graph launch");
     }
-    return step_body(m, R, sampled, n_commit, logits, b, st);
+    return step_body(m, R, sampled, n_commit, logits, b, st, true, topp_full);
 }
 
 // Grid-aligned chunked prefill (650 Group, "Faster, provably the same model",

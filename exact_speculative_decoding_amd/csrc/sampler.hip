@@ -267,6 +267,308 @@ __global__ __launch_bounds__(64) void merge_sample_kernel(SampleArgs a) {
     }
 }
 
+// ---- top-p over the whole vocabulary (top_k == 0) ------------------------------
+// The nucleus is cut on fixed-point masses, which add to the same total in any
+// order: with the tokens ordered (logit desc, id asc) and m the largest logit,
+// token j's mass is e_j = nearest(exp((l_j - m) / T) * 2^40), Z = sum e_j, and
+// thr = max(1, trunc(fl(top_p * fl(Z)))); token j is kept iff the mass of the
+// tokens before it is below thr.  The last kept token is found by a
+// most-significant-digit-first select on the 64-bit order keys: six passes of
+// 11, 11, 11, 11, 11 and 9 bits, each a histogram of integer masses over the
+// keys that share the digits chosen so far (integer additions, so the
+// histogram is the same whatever order the atomics land in); a pass picks the
+// largest digit at which the mass of the keys above, plus that digit's, first
+// reaches thr.  Then the keyed argmax over the tokens whose key is at least
+// that last kept key.
+constexpr int kTpPasses = 6;
+constexpr int kTpBuckets = 2048;
+constexpr double kTpScale = 1099511627776.0;  // 2^40
+__device__ __forceinline__ int tp_shift(int d) { return d < 5 ? 53 - 11 * d : 0; }
+__device__ __forceinline__ int tp_bits(int d) { return d < 5 ? 11 : 9; }
+
+struct TpArgs {
+    const float* logits;
+    int V, nchunk;
+    const long long* positions;
+    double T, top_p;
+    unsigned long long seed;
+    const ev_sampling* sd;          // when non-NULL, T, top_p and seed are read here
+    unsigned long long* cmax;       // [R][kMaxChunks] chunk maxima (order keys)
+    unsigned long long* hist;       // [R][kTpPasses][kTpBuckets] fixed-point masses
+    double* best;                   // [R][kMaxChunks][4]: z1, z2, id1 (as double), unused
+    int* tokens;
+    double* gap;
+};
+
+__device__ __forceinline__ void tp_params(const TpArgs& a, double& T, double& top_p, unsigned long long& seed) {
+    if (a.sd) {
+        const ev_sampling s = *a.sd;
+        T = s.temperature;
+        top_p = s.top_p;
+        seed = s.seed;
+    } else {
+        T = a.T;
+        top_p = a.top_p;
+        seed = a.seed;
+    }
+}
+
+// The row's largest order key (every wave computes it; no barrier needed).
+__device__ __forceinline__ unsigned long long tp_row_max(const TpArgs& a, int r) {
+    const int lane = threadIdx.x & 63;
+    unsigned long long k = lane < a.nchunk ? a.cmax[(size_t)r * kMaxChunks + lane] : 0ull;
+    return wave_max_u64(k);
+}
+
+// Chunk maxima; chunk 0 of each row also clears the row's histograms.
+__global__ __launch_bounds__(kSThreads) void tp_max_kernel(TpArgs a) {
+    __shared__ unsigned long long red[kSThreads / 64];
+    const int r = blockIdx.y, chunk = blockIdx.x, tid = threadIdx.x;
+    const float* row = a.logits + (size_t)r * a.V;
+    unsigned long long k = 0ull;
+    for (int i = 0; i < kPer; ++i) {
+        const int idx = chunk * kChunk + i * kSThreads + tid;
+        if (idx < a.V) {
+            const unsigned long long o = order_key(row[idx], idx);
+            k = o > k ? o : k;
+        }
+    }
+    k = wave_max_u64(k);
+    if ((tid & 63) == 0) red[tid >> 6] = k;
+    __syncthreads();
+    if (tid == 0) {
+        unsigned long long m = red[0];
+        for (int w = 1; w < kSThreads / 64; ++w) m = red[w] > m ? red[w] : m;
+        a.cmax[(size_t)r * kMaxChunks + chunk] = m;
+    }
+    if (chunk == 0) {
+        unsigned long long* h = a.hist + (size_t)r * kTpPasses * kTpBuckets;
+        for (int i = tid; i < kTpPasses * kTpBuckets; i += kSThreads) h[i] = 0ull;
+    }
+}
+
+// Block-wide inclusive prefix sum of one integer per thread, in thread order.
+__device__ __forceinline__ unsigned long long tp_block_scan(unsigned long long v, unsigned long long* sh) {
+    const int tid = threadIdx.x;
+    sh[tid] = v;
+    __syncthreads();
+    for (int off = 1; off < kSThreads; off <<= 1) {
+        const unsigned long long add = tid >= off ? sh[tid - off] : 0ull;
+        __syncthreads();
+        sh[tid] += add;
+        __syncthreads();
+    }
+    const unsigned long long out = sh[tid];
+    __syncthreads();
+    return out;
+}
+
+// One pass's choice: the largest digit b at which A + (mass of digits >= b)
+// reaches thr; *A becomes A + (mass of digits > b).  Digits descend with the
+// thread index (thread t holds digits 2047 - 8t .. 2040 - 8t).
+__device__ int tp_select(const unsigned long long* h, unsigned long long* A, unsigned long long thr,
+                         unsigned long long* sh, int* win) {
+    const int tid = threadIdx.x;
+    constexpr int per = kTpBuckets / kSThreads;
+    unsigned long long v[per], tot = 0ull;
+#pragma unroll
+    for (int i = 0; i < per; ++i) {
+        v[i] = h[kTpBuckets - 1 - (per * tid + i)];
+        tot += v[i];
+    }
+    const unsigned long long incl = tp_block_scan(tot, sh);
+    unsigned long long run = *A + incl - tot;  // mass of the digits above this thread's
+    int mine = -1;
+    unsigned long long above = 0ull;
+#pragma unroll
+    for (int i = 0; i < per; ++i) {
+        if (mine < 0 && run + v[i] >= thr) {
+            mine = kTpBuckets - 1 - (per * tid + i);
+            above = run;
+        }
+        run += v[i];
+    }
+    if (tid == 0) *win = kSThreads;
+    __syncthreads();
+    if (mine >= 0) atomicMin(win, tid);
+    __syncthreads();
+    const int w = *win;
+    __syncthreads();
+    if (tid == w) {
+        sh[0] = above;
+        sh[1] = (unsigned long long)mine;
+    }
+    __syncthreads();
+    const int digit = w < kSThreads ? (int)sh[1] : 0;  // a winner always exists for a consistent histogram
+    if (w < kSThreads) *A = sh[0];
+    __syncthreads();
+    return digit;
+}
+
+// Z, thr and the digits of passes < d: the key prefix and the mass above it.
+__device__ void tp_prefix(const TpArgs& a, int r, int d, double top_p, unsigned long long* prefix,
+                          unsigned long long* thr_out, unsigned long long* sh, int* win) {
+    const unsigned long long* h = a.hist + (size_t)r * kTpPasses * kTpBuckets;
+    const int tid = threadIdx.x;
+    unsigned long long z = 0ull;
+    for (int i = tid; i < kTpBuckets; i += kSThreads) z += h[i];
+    const unsigned long long Z = tp_block_scan(z, sh);  // the last thread holds the total
+    if (tid == kSThreads - 1) sh[kSThreads] = Z;
+    __syncthreads();
+    const unsigned long long Zt = sh[kSThreads];
+    __syncthreads();
+    unsigned long long thr = (unsigned long long)(top_p * (double)Zt);
+    if (thr < 1ull) thr = 1ull;
+    unsigned long long A = 0ull, pre = 0ull;
+    for (int p = 0; p < d; ++p) {
+        const int b = tp_select(h + (size_t)p * kTpBuckets, &A, thr, sh, win);
+        pre |= (unsigned long long)b << tp_shift(p);
+    }
+    *prefix = pre;
+    *thr_out = thr;
+}
+
+// Pass d: the fixed-point masses of the keys that match the prefix, by digit d.
+__global__ __launch_bounds__(kSThreads) void tp_hist_kernel(TpArgs a, int d) {
+    __shared__ unsigned long long sh[kSThreads + 1];
+    __shared__ unsigned long long lh[kTpBuckets];
+    __shared__ int win;
+    const int r = blockIdx.y, chunk = blockIdx.x, tid = threadIdx.x;
+    double T, top_p;
+    unsigned long long seed;
+    tp_params(a, T, top_p, seed);
+    const double m = (double)key_logit(tp_row_max(a, r));
+    unsigned long long pre = 0ull, thr = 0ull;
+    if (d > 0) tp_prefix(a, r, d, top_p, &pre, &thr, sh, &win);
+    for (int i = tid; i < kTpBuckets; i += kSThreads) lh[i] = 0ull;
+    __syncthreads();
+    const int hi = d > 0 ? tp_shift(d - 1) : 64;  // bits at and above hi are fixed
+    const float* row = a.logits + (size_t)r * a.V;
+    for (int i = 0; i < kPer; ++i) {
+        const int idx = chunk * kChunk + i * kSThreads + tid;
+        if (idx >= a.V) continue;
+        const float l = row[idx];
+        const unsigned long long k = order_key(l, idx);
+        if (hi < 64 && (k >> hi) != (pre >> hi)) continue;
+        const int digit = (int)((k >> tp_shift(d)) & ((1ull << tp_bits(d)) - 1ull));
+        const unsigned long long e = (unsigned long long)rint(exp(((double)l - m) / T) * kTpScale);
+        if (e) atomicAdd(&lh[digit], e);
+    }
+    __syncthreads();
+    unsigned long long* h = a.hist + ((size_t)r * kTpPasses + d) * kTpBuckets;
+    for (int i = tid; i < kTpBuckets; i += kSThreads)
+        if (lh[i]) atomicAdd(&h[i], lh[i]);
+}
+
+// The keyed argmax over the kept tokens (keys >= the last kept key), per
+// chunk: the best and second-best perturbed scores (lower id on equal scores).
+__global__ __launch_bounds__(kSThreads) void tp_pick_kernel(TpArgs a) {
+    __shared__ unsigned long long sh[kSThreads + 1];
+    __shared__ double zs[kSThreads / 64];
+    __shared__ int ids[kSThreads / 64];
+    __shared__ int win;
+    const int r = blockIdx.y, chunk = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    double T, top_p;
+    unsigned long long seed;
+    tp_params(a, T, top_p, seed);
+    unsigned long long kstar = 0ull, thr = 0ull;
+    tp_prefix(a, r, kTpPasses, top_p, &kstar, &thr, sh, &win);
+    const long long pos = a.positions[r];
+    const float* row = a.logits + (size_t)r * a.V;
+    double z[kPer];
+    int id[kPer];
+    double bz = -__builtin_huge_val();
+    int bid = 0x7fffffff;
+    for (int i = 0; i < kPer; ++i) {
+        const int idx = chunk * kChunk + i * kSThreads + tid;
+        z[i] = -__builtin_huge_val();
+        id[i] = 0x7fffffff;
+        if (idx >= a.V) continue;
+        const float l = row[idx];
+        if (order_key(l, idx) < kstar) continue;
+        z[i] = (double)l / T + keyed_gumbel(seed, pos, idx);
+        id[i] = idx;
+        if (z[i] > bz || (z[i] == bz && idx < bid)) {
+            bz = z[i];
+            bid = idx;
+        }
+    }
+    // the chunk's best (z desc, id asc)
+    for (int off = 32; off >= 1; off >>= 1) {
+        const double oz = __shfl_xor(bz, off, 64);
+        const int oid = __shfl_xor(bid, off, 64);
+        if (oz > bz || (oz == bz && oid < bid)) {
+            bz = oz;
+            bid = oid;
+        }
+    }
+    if (lane == 0) {
+        zs[w] = bz;
+        ids[w] = bid;
+    }
+    __syncthreads();
+    double cz = zs[0];
+    int cid = ids[0];
+    for (int u = 1; u < kSThreads / 64; ++u)
+        if (zs[u] > cz || (zs[u] == cz && ids[u] < cid)) {
+            cz = zs[u];
+            cid = ids[u];
+        }
+    __syncthreads();
+    // the best score among the chunk's other kept tokens
+    double sz = -__builtin_huge_val();
+    for (int i = 0; i < kPer; ++i)
+        if (id[i] != 0x7fffffff && id[i] != cid) sz = z[i] > sz ? z[i] : sz;
+    for (int off = 32; off >= 1; off >>= 1) {
+        const double oz = __shfl_xor(sz, off, 64);
+        sz = oz > sz ? oz : sz;
+    }
+    if (lane == 0) zs[w] = sz;
+    __syncthreads();
+    if (tid == 0) {
+        double s2 = zs[0];
+        for (int u = 1; u < kSThreads / 64; ++u) s2 = zs[u] > s2 ? zs[u] : s2;
+        double* o = a.best + ((size_t)r * kMaxChunks + chunk) * 4;
+        o[0] = cz;
+        o[1] = s2;
+        o[2] = (double)cid;
+    }
+}
+
+// The row's token: the best of the chunks' bests (lower id on equal scores);
+// gap = best - the best score among all other kept tokens.
+__global__ __launch_bounds__(64) void tp_merge_kernel(TpArgs a) {
+    const int r = blockIdx.x, lane = threadIdx.x;
+    double z1 = -__builtin_huge_val(), z2 = -__builtin_huge_val();
+    int id1 = 0x7fffffff;
+    if (lane < a.nchunk) {
+        const double* o = a.best + ((size_t)r * kMaxChunks + lane) * 4;
+        z1 = o[0];
+        z2 = o[1];
+        id1 = (int)o[2];
+    }
+    double bz = z1;
+    int bid = id1;
+    for (int off = 32; off >= 1; off >>= 1) {
+        const double oz = __shfl_xor(bz, off, 64);
+        const int oid = __shfl_xor(bid, off, 64);
+        if (oz > bz || (oz == bz && oid < bid)) {
+            bz = oz;
+            bid = oid;
+        }
+    }
+    // second: the other chunks' bests and every chunk's second best
+    double sz = id1 == bid ? z2 : (z1 > z2 ? z1 : z2);
+    for (int off = 32; off >= 1; off >>= 1) {
+        const double oz = __shfl_xor(sz, off, 64);
+        sz = oz > sz ? oz : sz;
+    }
+    if (lane == 0) {
+        a.tokens[r] = bid;
+        if (a.gap) a.gap[r] = sz == -__builtin_huge_val() ? __builtin_huge_val() : bz - sz;
+    }
+}
+
 // n_accept = leading i < D with draft[i] == sampled[i]; n_commit = min(a+1, R).
 __global__ __launch_bounds__(64) void accept_kernel(const int* __restrict__ sampled, int R,
                                                     const int* __restrict__ draft, int D,
@@ -293,7 +595,7 @@ int32_t check_sampling(const char* who, const ev_sampling& s) {
     if (!(s.temperature >= 0.0) || !(s.temperature < __builtin_huge_val()))
         return fail(EV_EINVAL, "%s: temperature must be finite and >= 0", who);
     if (s.temperature > 0.0) {
-        if (s.top_k < 1) return fail(EV_EINVAL, "%s: top_k=%d", who, s.top_k);
+        if (s.top_k < 0) return fail(EV_EINVAL, "%s: top_k=%d", who, s.top_k);
         if (s.top_k > EV_MAX_TOPK) return fail(EV_EUNSUPPORTED, "%s: top_k=%d above 64", who, s.top_k);
         if (!(s.top_p > 0.0 && s.top_p <= 1.0)) return fail(EV_EINVAL, "%s: top_p outside (0,1]", who);
     }
@@ -301,22 +603,33 @@ int32_t check_sampling(const char* who, const ev_sampling& s) {
 }
 }  // namespace ev
 
+// Workspace: the top-k candidate lists [16][nchunk][64], then for top-p over
+// the whole vocabulary the chunk maxima [16][64], the select histograms
+// [16][6][2048] and the chunks' best scores [16][64][4].
+static size_t al256(size_t v) { return (v + 255) & ~(size_t)255; }
+static size_t tp_off_cmax(int V) { return al256((size_t)EV_MAX_LANES * sample_nchunk(V) * EV_MAX_TOPK * 8); }
+static size_t tp_off_hist() { return al256((size_t)EV_MAX_LANES * kMaxChunks * 8); }
+static size_t tp_off_best() { return al256((size_t)EV_MAX_LANES * kTpPasses * kTpBuckets * 8); }
+
 extern "C" size_t keyed_sample_workspace(int32_t V) {
     if (V <= 0) return 0;
-    return (size_t)EV_MAX_LANES * sample_nchunk(V) * EV_MAX_TOPK * sizeof(unsigned long long);
+    return tp_off_cmax(V) + tp_off_hist() + tp_off_best() + (size_t)EV_MAX_LANES * kMaxChunks * 4 * sizeof(double);
 }
 
 // Checks the shapes and pointers of a keyed sample (the sampling parameters
 // are checked by the caller).
 static int32_t check_sample_args(const char* who, const float* logits, int32_t R, int32_t V,
-                                 const int64_t* positions, int32_t* tokens, double* gap, void* ws,
-                                 size_t ws_bytes) {
+                                 const int64_t* positions, int32_t* tokens, double* gap) {
     if (R < 1 || R > EV_MAX_LANES) return fail(EV_EINVAL, "%s: R=%d outside 1..16", who, R);
     if (V < 1) return fail(EV_EINVAL, "%s: V=%d", who, V);
     if (V > kMaxChunks * kChunk) return fail(EV_EUNSUPPORTED, "%s: V=%d above %d", who, V, kMaxChunks * kChunk);
     if (!logits || !positions || !tokens) return fail(EV_EINVAL, "%s: NULL pointer", who);
     if (!aligned(logits, 4) || !aligned(positions, 8) || !aligned(tokens, 4) || (gap && !aligned(gap, 8)))
         return fail(EV_EINVAL, "%s: misaligned pointer", who);
+    return EV_OK;
+}
+
+static int32_t check_sample_ws(const char* who, int32_t V, void* ws, size_t ws_bytes) {
     const size_t need = keyed_sample_workspace(V);
     if (!ws || ws_bytes < need)
         return fail(EV_EWORKSPACE, "%s: workspace needs %zu bytes, got %zu", who, need, ws ? ws_bytes : (size_t)0);
@@ -332,6 +645,19 @@ namespace ev {
 int32_t launch_keyed_sample(const float* logits, int R, int V, const long long* positions, const ev_sampling& s,
                             const ev_sampling* sd, int32_t* tokens, double* gap, void* ws, hipStream_t st) {
     const int nchunk = sample_nchunk(V);
+    if (s.temperature > 0.0 && s.top_k == 0) {  // top-p over the whole vocabulary
+        unsigned char* b = reinterpret_cast<unsigned char*>(ws);
+        const size_t oc = tp_off_cmax(V), oh = oc + tp_off_hist(), ob = oh + tp_off_best();
+        TpArgs a{logits, V, nchunk, positions, s.temperature, s.top_p, (unsigned long long)s.seed, sd,
+                 reinterpret_cast<unsigned long long*>(b + oc), reinterpret_cast<unsigned long long*>(b + oh),
+                 reinterpret_cast<double*>(b + ob), tokens, gap};
+        const dim3 grid(nchunk, R);
+        hipLaunchKernelGGL(tp_max_kernel, grid, dim3(kSThreads), 0, st, a);
+        for (int d = 0; d < kTpPasses; ++d) hipLaunchKernelGGL(tp_hist_kernel, grid, dim3(kSThreads), 0, st, a, d);
+        hipLaunchKernelGGL(tp_pick_kernel, grid, dim3(kSThreads), 0, st, a);
+        hipLaunchKernelGGL(tp_merge_kernel, dim3(R), dim3(64), 0, st, a);
+        return check_hip(hipGetLastError(), "top-p launches");
+    }
     const int kk = sample_kk_of(s.temperature, s.top_k, V);
     unsigned long long* cand = reinterpret_cast<unsigned long long*>(ws);
     hipLaunchKernelGGL(topk_chunk_kernel, dim3(nchunk, R), dim3(kSThreads), 0, st, logits, V, kk, nchunk, sd,
@@ -351,8 +677,9 @@ extern "C" int32_t keyed_sample(const float* logits, int32_t R, int32_t V, const
     clear_error();
     const char* who = "keyed_sample";
     int32_t rc;
-    if ((rc = check_sample_args(who, logits, R, V, positions, tokens, gap, ws, ws_bytes))) return rc;
+    if ((rc = check_sample_args(who, logits, R, V, positions, tokens, gap))) return rc;
     if ((rc = check_sampling(who, s))) return rc;
+    if ((rc = check_sample_ws(who, V, ws, ws_bytes))) return rc;
     return launch_keyed_sample(logits, R, V, reinterpret_cast<const long long*>(positions), s, nullptr, tokens,
                                gap, ws, reinterpret_cast<hipStream_t>(stream));
 }

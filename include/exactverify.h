@@ -191,6 +191,11 @@ int32_t verify_moe_w4(const uint16_t* x_bf16, const float* router, int32_t R, in
 /*      g = -log(-log(u)), all fp64;                                          */
 /*   4. z = (double)l / (double)T + g; token = argmax z, lower id on ties;    */
 /*      gap = best z - second z (+inf with one kept candidate).               */
+/* top_k == 0 (with temperature > 0): no top-k; top-p over the whole         */
+/* vocabulary, on fixed-point masses that add to the same total in any order: */
+/* with the tokens ordered (l desc, id asc), e_j = nearest(exp((l_j - l_0)/T) */
+/* * 2^40) (integers), Z = sum e_j, thr = max(1, trunc(top_p * Z)) (fp64      */
+/* product); token j is kept while the mass before it is below thr.           */
 /* temperature == 0: greedy, token = argmax l (lower id on ties), gap = l(1) - */
 /* l(2) on the raw logits (+inf if V == 1); top_k / top_p are ignored.        */
 /*                                                                            */
@@ -199,13 +204,13 @@ int32_t verify_moe_w4(const uint16_t* x_bf16, const float* router, int32_t R, in
 /*   tokens     (device) [R] int32, written.                                  */
 /*   gap        (device, optional) [R] fp64, written when non-NULL.           */
 /*   ws         (device) at least keyed_sample_workspace(V) bytes.            */
-/* Limits: 1 <= R <= 16; V >= 1; temperature >= 0 and finite; when            */
-/* temperature > 0: 1 <= top_k <= 64 and 0 < top_p <= 1.                      */
+/* Limits: 1 <= R <= 16; 1 <= V <= 262144; temperature >= 0 and finite; when */
+/* temperature > 0: 0 <= top_k <= 64 and 0 < top_p <= 1.                      */
 /* Errors: EV_EINVAL, EV_EUNSUPPORTED (top_k > 64), EV_EWORKSPACE, EV_EHIP.   */
 /* ------------------------------------------------------------------------- */
 typedef struct {
     double temperature; /* T; 0 selects greedy */
-    int32_t top_k;      /* 1..64 when T > 0   */
+    int32_t top_k;      /* 1..64 when T > 0; 0: no top-k (whole-vocabulary top-p) */
     double top_p;       /* (0, 1] when T > 0  */
     uint64_t seed;      /* key of the noise    */
 } ev_sampling;

@@ -358,7 +358,81 @@ void ov_sample_from_candidates(const float* l, const int32_t* cand, int n,
     free(e);
 }
 
-/* One row: greedy when T == 0, else top-k, top-p and the keyed argmax. */
+/* Top-p over the whole vocabulary (top_k == 0).  The nucleus cut reads the  */
+/* masses in fixed point so that they can be added in any order to the same  */
+/* total: with the tokens ordered (logit desc, id asc) and m the largest      */
+/* logit, token j's mass is the integer e_j = nearest(exp((l_j - m) / T) *    */
+/* 2^40) (the largest token's is 2^40), Z = sum of all e_j (< 2^58), and the  */
+/* threshold thr = max(1, trunc(fl(top_p * fl(Z)))) in fp64.  Token j is     */
+/* kept iff the mass of the tokens before it is below thr (token 0 always).   */
+/* Then the keyed argmax over the kept tokens, as for the candidates above.   */
+/* topp_edge flags a cut within Z / 2^30 of thr.                              */
+#define OV_FX_SCALE 1099511627776.0 /* 2^40 */
+
+static const float* g_sort_l; /* qsort's view of the row */
+static int cmp_rank(const void* a, const void* b)
+{
+    int i = *(const int32_t*)a, j = *(const int32_t*)b;
+    if (ranks_before(g_sort_l, i, j)) return -1;
+    if (ranks_before(g_sort_l, j, i)) return 1;
+    return 0;
+}
+
+void ov_sample_topp_full(const float* l, int V, int64_t pos, double T, double top_p,
+                         uint64_t seed, ov_sample_out* out)
+{
+    int32_t* ord = (int32_t*)malloc(sizeof(int32_t) * (size_t)V);
+    uint64_t* e = (uint64_t*)malloc(sizeof(uint64_t) * (size_t)V);
+    for (int i = 0; i < V; i++) ord[i] = i;
+    g_sort_l = l;
+    qsort(ord, (size_t)V, sizeof(int32_t), cmp_rank);
+    double m = (double)l[ord[0]];
+    uint64_t Z = 0;
+    for (int j = 0; j < V; j++) {
+        e[j] = (uint64_t)nearbyint(exp(((double)l[ord[j]] - m) / T) * OV_FX_SCALE);
+        Z += e[j];
+    }
+    uint64_t thr = (uint64_t)(top_p * (double)Z);
+    if (thr < 1) thr = 1;
+    int kept = 0, edge = 0;
+    uint64_t before = 0;
+    for (int j = 0; j < V; j++) {
+        if (j > 0 && !(before < thr)) break;
+        kept = j + 1;
+        before += e[j];
+    }
+    {
+        uint64_t acc = 0;
+        double tol = (double)Z / 1073741824.0; /* Z / 2^30 */
+        for (int j = 0; j < V; j++) {
+            if (j > 0 && fabs((double)acc - (double)thr) < tol) edge = 1;
+            acc += e[j];
+        }
+    }
+    int best = -1;
+    double zb = -INFINITY, z2 = -INFINITY;
+    for (int j = 0; j < kept; j++) {
+        int t = ord[j];
+        double z = (double)l[t] / T + ov_gumbel(ov_noise_hash(seed, pos, t));
+        if (best < 0 || z > zb || (z == zb && t < best)) {
+            z2 = zb;
+            zb = z;
+            best = t;
+        } else if (z > z2) {
+            z2 = z;
+        }
+    }
+    out->token = best;
+    out->gap = (kept > 1) ? zb - z2 : INFINITY;
+    out->n_cand = V;
+    out->n_kept = kept;
+    out->topp_edge = edge;
+    free(ord);
+    free(e);
+}
+
+/* One row: greedy when T == 0, else top-k (none when top_k == 0), top-p and  */
+/* the keyed argmax. */
 void ov_sample_row(const float* l, int V, int64_t pos, double T, int top_k,
                    double top_p, uint64_t seed, ov_sample_out* out)
 {
@@ -376,6 +450,10 @@ void ov_sample_row(const float* l, int V, int64_t pos, double T, int top_k,
         out->n_cand = V;
         out->n_kept = 1;
         out->topp_edge = 0;
+        return;
+    }
+    if (top_k == 0) { /* no top-k: top-p over the whole vocabulary */
+        ov_sample_topp_full(l, V, pos, T, top_p, seed, out);
         return;
     }
     int k = top_k < V ? top_k : V;

@@ -28,6 +28,7 @@ pytestmark = pytest.mark.gpu
 
 SAMPLED = (0.7, 20, 0.95, 42)
 GREEDY = (0.0, 1, 1.0, 0)
+TOPP_ONLY = (0.8, 0, 0.9, 42)  # no top-k: top-p over the whole vocabulary
 
 
 def _gpu_round(m, sampling, logits_log=None):
@@ -109,7 +110,7 @@ def test_tiny_rows_bit_identical_to_single_row_steps(tiny):
         assert torch.equal(m.k_cache, kcR) and torch.equal(m.v_cache, vcR)
 
 
-@pytest.mark.parametrize("sampling", [SAMPLED, GREEDY])
+@pytest.mark.parametrize("sampling", [SAMPLED, GREEDY, TOPP_ONLY])
 def test_tiny_drafted_equals_serial_and_matches_oracle(tiny, sampling):
     d, cfg = tiny, tiny["cfg"]
     pos0, n, V = cfg["prefill"], 40, cfg["vocab"]
@@ -254,6 +255,7 @@ def test_tiny_one_capture_serves_every_seed(tiny):
     d, cfg = tiny, tiny["cfg"]
     pos0, n, V = cfg["prefill"], 12, cfg["vocab"]
     settings = [(0.7, 20, 0.95, s) for s in range(50)] + [GREEDY, (1.0, 5, 0.5, 7), (0.3, 64, 1.0, 8)]
+    settings += [(0.8, 0, 0.9, s) for s in range(5)]  # top-p over the whole vocabulary: a second capture per R
     mg, me = _fresh(d), _fresh(d)
     me.set_graphs(False)
     kc0, vc0 = mg.k_cache.clone(), mg.v_cache.clone()
@@ -273,10 +275,11 @@ def test_tiny_one_capture_serves_every_seed(tiny):
             decode(fn, d["first_token"], pos0, n, 4, syn.transcript_drafter(serial, pos0 + 1, 0.65, 5, V))
             logs.append(log)
         assert logs[0] == logs[1], samp
-    # one capture per row count (R = 1..4, the rounds' widths), none per setting
+    # one capture per row count (R = 1..4, the rounds' widths) and sampler
+    # kind (top-k candidates or whole-vocabulary top-p), none per setting
     captures, cached = mg.graph_stats()
     print(f"{len(settings)} sampling settings: {captures} captures")
-    assert 1 <= captures <= 4 and cached == captures
+    assert 1 <= captures <= 8 and cached == captures
     assert me.graph_stats() == (0, 0)
 
 

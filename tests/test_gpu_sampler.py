@@ -3,7 +3,8 @@
 The same seeded fp32 logits go to both sides, so the sampled tokens must be
 identical; the only allowed differences are rows whose decision sits at the
 last bits of fp64 (a top-two gap below 1e-12, or a top-p cut within 1e-9 Z of
-the threshold), which are counted.  Gaps must agree to fp64 rounding.
+the threshold; with top_k 0, top-p over the whole vocabulary on fixed-point
+masses, a cut within Z / 2^30), which are counted.  Gaps must agree to fp64 rounding.
 Rows of an R-row call are bit-identical to single-row calls.
 """
 import numpy as np
@@ -24,6 +25,10 @@ CASES = [  # V, T, top_k, top_p
     (151936, 0.0, 20, 0.95), (262144, 2.0, 64, 0.3), (1000, 0.05, 10, 0.99),
     (4096, 100.0, 64, 1.0),    # nearly flat: the keyed noise decides
     (151936, 0.7, 64, 1e-9),   # top-p keeps the best candidate only
+    # top_k 0: top-p over the whole vocabulary
+    (1, 0.7, 0, 0.95), (2, 1.0, 0, 0.5), (16, 1.0, 0, 1.0), (4097, 0.8, 0, 0.9), (32768, 0.7, 0, 0.95),
+    (151936, 0.7, 0, 0.95), (151936, 1.0, 0, 0.5), (262144, 1.5, 0, 0.99), (151936, 0.7, 0, 1e-9),
+    (4096, 100.0, 0, 0.95),    # nearly flat: the nucleus holds most of the vocabulary
 ]
 
 
@@ -64,7 +69,7 @@ def test_sampler_ties_and_many_seeds():
     logits = g.integers(-3, 4, (16, V)).astype(np.float32)
     pos = np.arange(16, dtype=np.int64)
     for seed in range(40):
-        for T, k, p in ((0.0, 20, 1.0), (1.0, 20, 0.95), (0.5, 64, 0.7)):
+        for T, k, p in ((0.0, 20, 1.0), (1.0, 20, 0.95), (0.5, 64, 0.7), (0.9, 0, 0.8)):
             _compare(logits, pos, T, k, p, seed)
 
 

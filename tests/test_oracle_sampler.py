@@ -178,3 +178,80 @@ def test_single_candidate_and_topk_one():
     assert o.token == 1 and math.isinf(o.gap) and o.n_kept == 1
     o = oracle.sample_row(l, 0, 1.0, 4, 1e-6, 9)  # tiny top_p keeps one
     assert o.token == 1 and o.n_kept == 1
+
+
+# --- top-p over the whole vocabulary (top_k == 0) ---------------------------------
+
+@pytest.mark.parametrize("T", [0.5, 1.0])
+def test_no_topk_full_nucleus_frequencies_match_softmax(T):
+    # top_k 0 and top_p 1: every token stays, the draw is softmax over all V
+    g = np.random.default_rng(200 + int(T * 10))
+    l = (g.standard_normal(16) * 1.5).astype(np.float32)
+    p = softmax(l.astype(np.float64) / T)
+    n = 100_000
+    tok = oracle.sample_many(l, np.full(n, 5, np.int64), np.arange(n, dtype=np.uint64), T, 0, 1.0)
+    assert _chi2(np.bincount(tok, minlength=16), p) < CHI2_15_0001
+
+
+def _fixed_point_nucleus(l, T, top_p):
+    """The nucleus by brute force over subsets: the smallest set of tokens
+    whose fixed-point mass (nearest(exp((l - m) / T) * 2^40)) reaches the
+    threshold trunc(top_p * Z), among equal sizes the heaviest (unique for
+    distinct logits); None when a subset's mass sits within Z / 2^30 of it."""
+    V = len(l)
+    m = max(float(x) for x in l)
+    e = [int(np.rint(math.exp((float(l[i]) - m) / T) * 2.0 ** 40)) for i in range(V)]
+    Z = sum(e)
+    thr = max(1, int(top_p * float(Z)))
+    for size in range(1, V + 1):
+        best = None
+        for sub in itertools.combinations(range(V), size):
+            mass = sum(e[i] for i in sub)
+            if abs(mass - thr) < Z / 2 ** 30:
+                return None
+            if mass >= thr and (best is None or mass > best[0]):
+                best = (mass, set(sub))
+        if best is not None:
+            return best[1]
+    return set(range(V))
+
+
+def test_no_topk_nucleus_matches_brute_force():
+    g = np.random.default_rng(21)
+    checked = 0
+    for trial in range(300):
+        V = int(g.integers(2, 10))
+        l = (g.standard_normal(V) * 2).astype(np.float32)
+        if len(set(l.tolist())) < V:
+            continue
+        T = float(g.uniform(0.3, 2.0))
+        top_p = float(g.uniform(0.05, 1.0))
+        nuc = _fixed_point_nucleus(l, T, top_p)
+        if nuc is None:
+            continue
+        seed, pos = int(g.integers(0, 1 << 62)), int(g.integers(0, 1000))
+        o = oracle.sample_row(l, pos, T, 0, top_p, seed)
+        assert o.n_kept == len(nuc) and o.n_cand == V
+        z = {t: float(l[t]) / T + oracle.gumbel(oracle.noise_hash(seed, pos, t)) for t in nuc}
+        assert o.token == max(sorted(nuc), key=lambda t: z[t])
+        checked += 1
+    assert checked > 150
+
+
+def test_no_topk_agrees_with_topk_of_the_whole_vocabulary_off_the_edge():
+    # top_k = V keeps every token too; the two cuts read the masses in fp64 and
+    # in fixed point, so they agree except at a cut within rounding of top_p Z
+    g = np.random.default_rng(22)
+    agree = 0
+    for trial in range(200):
+        V = int(g.integers(2, 65))
+        l = (g.standard_normal(V) * 2).astype(np.float32)
+        T, top_p = float(g.uniform(0.3, 2.0)), float(g.uniform(0.1, 1.0))
+        seed, pos = int(g.integers(0, 1 << 62)), int(g.integers(0, 1000))
+        a = oracle.sample_row(l, pos, T, 0, top_p, seed)
+        b = oracle.sample_row(l, pos, T, V, top_p, seed)
+        if a.topp_edge or b.topp_edge:
+            continue
+        assert (a.token, a.n_kept) == (b.token, b.n_kept)
+        agree += 1
+    assert agree > 180
