@@ -64,6 +64,11 @@ def _declare(L):
     L.ov_w4_linear.argtypes = [_p(u16), i32, i32, _p(u8), _p(u16), _p(u16), i32, i32, _p(f64)]
     L.ov_w4_linear_f32.argtypes = [_p(u16), i32, i32, _p(u8), _p(u16), _p(u16), i32, i32, _p(f32)]
     L.ov_w4_linear_fp32.argtypes = [_p(u16), i32, i32, _p(u8), _p(u16), _p(u16), i32, i32, _p(f32)]
+    L.ov_e2m1_to_f64.argtypes = [i32]
+    L.ov_e2m1_to_f64.restype = f64
+    L.ov_e4m3_to_f64.argtypes = [u8]
+    L.ov_e4m3_to_f64.restype = f64
+    L.ov_nvfp4_linear_f32.argtypes = [_p(u16), i32, i32, _p(u8), _p(u8), f32, i32, _p(f32)]
     L.ov_silu_mul_bf16.argtypes = [_p(f32), _p(f32), C.c_size_t, _p(u16)]
     L.ov_mlp.argtypes = [_p(u16), i32, i32, i32, i32,
                          _p(u8), _p(u16), _p(u16), _p(u8), _p(u16), _p(u16),
@@ -193,6 +198,27 @@ def w4_linear_fp32(x, q, s, b, G):
     y = np.empty((R, N), np.float32)
     lib().ov_w4_linear_fp32(ptr(x, np.uint16), R, K, ptr(q, np.uint8), ptr(s, np.uint16),
                             ptr(b, np.uint16), N, G, ptr(y, np.float32))
+    return y
+
+
+def e2m1_to_f64(code):
+    return float(lib().ov_e2m1_to_f64(int(code)))
+
+
+def e4m3_to_f64(b):
+    return float(lib().ov_e4m3_to_f64(int(b)))
+
+
+def nvfp4_linear(x, q, s, s_t, out_f32=True):
+    """x [R][K] bf16 bits, q [N][K/2] u8 (E2M1 pairs, low nibble = even k),
+    s [N][K/16] u8 (E4M3 block scales), s_t fp32 tensor scale -> y [R][N] fp32."""
+    x, q, s = _c(x, np.uint16), _c(q, np.uint8), _c(s, np.uint8)
+    R, K = x.shape
+    N = q.shape[0]
+    assert q.shape == (N, K // 2) and s.shape == (N, K // 16)
+    y = np.empty((R, N), np.float32)
+    lib().ov_nvfp4_linear_f32(ptr(x, np.uint16), R, K, ptr(q, np.uint8), ptr(s, np.uint8), float(s_t), N,
+                              ptr(y, np.float32))
     return y
 
 

@@ -231,6 +231,60 @@ void ov_w4_linear_fp32(const uint16_t* x, int R, int K, const uint8_t* q,
 }
 
 /* ------------------------------------------------------------------------- */
+/* A second 4-bit format: NVFP4-style block scales [blog "The honest limits": */
+/* NVFP4 checkpoints].  w[n][k] = e2m1(q[n][k]) * e4m3(s[n][k/16]) * s_t:     */
+/*   q  [N][K/2] bytes, two FP4 E2M1 codes per byte, low nibble = even k;     */
+/*   s  [N][K/16] FP8 E4M3 block scales (one per 16 k);                       */
+/*   s_t one fp32 scale for the whole tensor.                                 */
+/* E2M1 (the OCP microscaling formats' FP4): sign, 2 exponent bits (bias 1),  */
+/* 1 mantissa bit: 0, 0.5, 1, 1.5, 2, 3, 4, 6 and their negatives.            */
+/* E4M3 (OCP, "FN": no infinities): sign, 4 exponent bits (bias 7), 3         */
+/* mantissa bits; exponent 0 is subnormal (m/8 * 2^-6); S.1111.111 is NaN.    */
+/* ------------------------------------------------------------------------- */
+
+double ov_e2m1_to_f64(int code)
+{
+    int sign = (code >> 3) & 1, e = (code >> 1) & 3, m = code & 1;
+    double v = (e == 0) ? 0.5 * m : ldexp(1.0 + 0.5 * m, e - 1);
+    return sign ? -v : v;
+}
+
+double ov_e4m3_to_f64(uint8_t b)
+{
+    int sign = (b >> 7) & 1, e = (b >> 3) & 15, m = b & 7;
+    double v;
+    if (e == 15 && m == 7)
+        v = NAN;
+    else if (e == 0)
+        v = ldexp((double)m / 8.0, -6);
+    else
+        v = ldexp(1.0 + (double)m / 8.0, e - 7);
+    return sign ? -v : v;
+}
+
+/* y[r][n] = sum_k x[r][k] * w[n][k] in fp64, rows one at a time, rounded to fp32. */
+void ov_nvfp4_linear_f32(const uint16_t* x, int R, int K, const uint8_t* q, const uint8_t* s,
+                         float s_t, int N, float* y)
+{
+    double* xd = (double*)malloc(sizeof(double) * (size_t)K);
+    for (int r = 0; r < R; r++) {
+        for (int k = 0; k < K; k++)
+            xd[k] = ov_bf16_to_f64(x[(size_t)r * K + k]);
+#pragma omp parallel for schedule(static)
+        for (int n = 0; n < N; n++) {
+            double acc = 0.0;
+            for (int k = 0; k < K; k++) {
+                double w = ov_e2m1_to_f64(q_at(q, K, n, k)) *
+                           ov_e4m3_to_f64(s[(size_t)n * (K / 16) + k / 16]) * (double)s_t;
+                acc += w * xd[k];
+            }
+            y[(size_t)r * N + n] = (float)acc;
+        }
+    }
+    free(xd);
+}
+
+/* ------------------------------------------------------------------------- */
 /* SiLU-gated MLP glue: h = bf16(silu(g) * u), silu(v) = v / (1 + e^-v).      */
 /* ------------------------------------------------------------------------- */
 

@@ -186,3 +186,16 @@ def draft_head(seed, hidden, G):
     the cfg-2 distributions (standard layout q, s, b)."""
     return w4_matrix(rng(seed), hidden, hidden, G)
 
+
+
+def nvfp4_matrix(g, N, K, s_lo=0.002, s_hi=0.02):
+    """An NVFP4-style N x K matrix in standard layout: q [N][K/2] (FP4 E2M1
+    codes uniform over all 16, low nibble = even k), s [N][K/16] FP8 E4M3 block
+    scales ~ U(s_lo, s_hi) rounded to nearest E4M3, and a tensor scale."""
+    import torch
+    codes = g.integers(0, 16, (N, K), dtype=np.uint8)
+    q = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    sv = g.uniform(s_lo, s_hi, (N, K // 16)).astype(np.float32)
+    s = torch.from_numpy(sv).to(torch.float8_e4m3fn).view(torch.uint8).numpy().copy()
+    s_t = float(np.float32(g.uniform(0.5, 2.0)))
+    return q, s, s_t
