@@ -355,6 +355,45 @@ def leg_decoder(ev, syn, C, n_tokens=512, R=8, p_draft=0.65, cpu_steps=0):
             **({"cpu_baseline": cpu} if cpu else {})}
 
 
+def leg_formats(ev, syn, to_dev, stream, steps):
+    """The W4 kernel on the two 4-bit formats, one linear at a time: affine
+    uint4 (fp16 scale and bias per 64) and NVFP4-style (E2M1 codes, E4M3 scale
+    per 16, tensor scale), both 0.5625 bytes a weight, for the slice's two
+    matrix shapes, four rotating copies each; kernel-only GB/s from the
+    per-workgroup stamps (the split sums excluded), per R."""
+    import numpy as np
+    import torch
+    out = {}
+    g = np.random.default_rng(1011)
+    for K, N in ((5120, 17408), (17408, 5120)):
+        aff = [ev.w4_pack(*(to_dev(a) for a in syn.w4_matrix(g, N, K, 64)), 64) for _ in range(4)]
+        q, s, st = syn.nvfp4_matrix(g, N, K)
+        fp4 = [ev.nvfp4_pack(to_dev(q), to_dev(s), st) for _ in range(4)]
+        x = to_dev(syn.activations(g, 16, K))
+        y = torch.empty((16, N), dtype=torch.float32, device="cuda")
+        ws = torch.empty(max(ev.verify_linear_w4_workspace(K, N, 64), 1), dtype=torch.uint8, device="cuda")
+        row = {}
+        for R in (1, 16):
+            for name, mats, fn in (("affine_g64", aff, ev.verify_linear_w4), ("nvfp4", fp4, ev.verify_linear_nvfp4)):
+                for i in range(200):
+                    fn(x[:R], mats[i % 4], y=y[:R], ws=ws, stream=stream)
+                torch.cuda.synchronize()
+                ev.w4_timing_read()
+                ev.w4_timing(True)
+                for i in range(steps):
+                    fn(x[:R], mats[i % 4], y=y[:R], ws=ws, stream=stream)
+                torch.cuda.synchronize()
+                ev.w4_timing(False)
+                n, ms, by = ev.w4_timing_read()
+                row.setdefault(name, {})[str(R)] = {"kernel_us": round(1e3 * ms / n, 2),
+                                                    "GB_s": round(by / (ms * 1e-3) / 1e9, 1),
+                                                    "frac": round(by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        out[f"{K}->{N}"] = row
+        del aff, fp4
+        torch.cuda.empty_cache()
+    return {"workload": "one W4 linear, affine G64 vs NVFP4, kernel only", "shapes": out}
+
+
 def leg_prefill(ev, syn, C=4096, P=3584, grid=2048, reps=3):
     """Grid-aligned chunked prefill of a P-token prompt into the 8-layer
     decoder's cache (passes of at most 16 rows, never across a multiple of 16
@@ -576,6 +615,8 @@ def main():
         print("# lm head leg done", file=sys.stderr, flush=True)
         legs["moe_layer"] = leg_moe(ev, syn, to_dev, stream, args.steps)
         print("# moe leg done", file=sys.stderr, flush=True)
+        legs["formats"] = leg_formats(ev, syn, to_dev, stream, args.steps)
+        print("# formats leg done", file=sys.stderr, flush=True)
         legs["decoder_4096"] = leg_decoder(ev, syn, 4096, cpu_steps=0 if args.no_cpu_baseline else 24)
         print("# decoder leg (cache 4096) done", file=sys.stderr, flush=True)
         legs["decoder_32768"] = leg_decoder(ev, syn, 32768, cpu_steps=0 if args.no_cpu_baseline else 16)

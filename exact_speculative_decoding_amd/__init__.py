@@ -63,6 +63,10 @@ _SIGS = {
     "w4_pack": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _vp, _sz, _vp]),
     "verify_linear_w4_workspace": (_sz, [_i32, _i32, _i32]),
     "verify_linear_w4": (_i32, [_vp, _i32, _i32, _vp, _i32, _i32, _vp, _vp, _sz, _vp]),
+    "nvfp4_packed_bytes": (_sz, [_i32, _i32]),
+    "nvfp4_pack": (_i32, [_vp, _vp, _i32, _i32, _vp, _sz, _vp]),
+    "verify_linear_nvfp4_workspace": (_sz, [_i32, _i32]),
+    "verify_linear_nvfp4": (_i32, [_vp, _i32, _i32, _vp, _i32, C.c_float, _vp, _vp, _sz, _vp]),
     "verify_mlp_w4_workspace": (_sz, [_i32, _i32, _i32]),
     "verify_mlp_w4": (_i32, [_vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _sz,
                              _vp]),
@@ -189,6 +193,40 @@ def verify_linear_w4(x, w, y=None, ws=None, stream=None):
         _dev(x, "x", _B16), R, K, _dev(w.blob, "w", _U8), w.N, w.G,
         _dev(y, "y", (torch.float32,)),
         None if ws is None else C.c_void_p(ws.data_ptr()), nb, _stream(stream)))
+    return y
+
+
+class PackedNvfp4:
+    """An NVFP4-style matrix in the packed layout (device bytes), its shape and
+    tensor scale."""
+
+    def __init__(self, blob, N, K, tensor_scale):
+        self.blob, self.N, self.K, self.tensor_scale = blob, N, K, float(tensor_scale)
+
+
+def nvfp4_pack(q, s, tensor_scale, out=None, stream=None):
+    """Pack q [N][K/2] u8 (E2M1 pairs) and s [N][K/16] u8 (E4M3), device."""
+    N, Kh = q.shape
+    K = 2 * Kh
+    nb = int(lib().nvfp4_packed_bytes(N, K))
+    if out is None:
+        out = torch.empty(nb, dtype=torch.uint8, device=q.device)
+    _check(lib().nvfp4_pack(_dev(q, "q", _U8), _dev(s, "s", _U8), N, K, _dev(out, "packed", _U8), out.numel(),
+                            _stream(stream)))
+    return PackedNvfp4(out, N, K, tensor_scale)
+
+
+def verify_linear_nvfp4(x, w, y=None, ws=None, stream=None):
+    """y[R][N] fp32 = the NVFP4 linear of x[R][K] (bf16) with the packed matrix w."""
+    R, K = x.shape
+    if K != w.K:
+        raise ValueError(f"x has K={K}, the matrix K={w.K}")
+    if y is None:
+        y = torch.empty((R, w.N), dtype=torch.float32, device=x.device)
+    ws, nb = _workspace(int(lib().verify_linear_nvfp4_workspace(K, w.N)), x.device, ws)
+    _check(lib().verify_linear_nvfp4(
+        _dev(x, "x", _B16), R, K, _dev(w.blob, "w", _U8), w.N, C.c_float(w.tensor_scale),
+        _dev(y, "y", (torch.float32,)), None if ws is None else C.c_void_p(ws.data_ptr()), nb, _stream(stream)))
     return y
 
 

@@ -131,6 +131,9 @@ struct W4Args {
     // nibble-decode constants, passed as arguments so that they sit in
     // registers (gfx9 VOP3 encodings cannot carry 32-bit literals)
     uint32_t dmask, doff;
+    // NVFP4 launches: the tensor scale every output is multiplied by
+    float tscale;
+    int fmt;  // W4Format of the launch
     // measurement: when non-NULL, workgroup b stores the device wall clock at
     // its start in tstamp[2b] and at its end in tstamp[2b + 1]
     unsigned long long* tstamp;

@@ -58,6 +58,52 @@ __global__ void w4_pack_kernel(const uint8_t* __restrict__ q, const uint16_t* __
     }
 }
 
+// NVFP4 packing, one thread per (tile, chunk, lane): dword t of lane (ln, j)
+// holds the 8 E2M1 codes of row 16 tile + ln at k = 128 c + 32 t + 4 j + {0..3}
+// (bytes 0, 1) and + 16 + {0..3} (bytes 2, 3), low nibble first -- the B
+// fragments of the step's two 16 x 16 x 16 MFMA; lanes of row group j == 0
+// copy the row's 8 E4M3 block scales of the chunk after the 1 KB of codes.
+__device__ __forceinline__ uint32_t fp4_code(const uint8_t* q, size_t Kh, long n, int k) {
+    const uint8_t b = q[(size_t)n * Kh + k / 2];
+    return (k & 1) ? (uint32_t)(b >> 4) : (uint32_t)(b & 15);
+}
+
+__global__ void nvfp4_pack_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ s, int N, int K,
+                                  uint8_t* __restrict__ out) {
+    const int NC = w4_chunks(K);
+    const long total = (long)w4_tiles(N) * NC * 64;
+    const long gid = (long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (gid >= total) return;
+    const int L = (int)(gid & 63);
+    const long tc = gid >> 6;
+    const int c = (int)(tc % NC);
+    const long tile = tc / NC;
+    const int ln = L & 15, j = L >> 4;
+    const long n = tile * 16 + ln;
+    uint8_t* dst = out + w4_tc_offset(tile, c, w4_tiles(N), 64);
+    const size_t Kh = (size_t)K / 2;
+    u32x4 w = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        uint32_t v = 0u;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int k = kKC * c + 32 * t + 4 * j + (e & 3) + 16 * (e >> 2);
+            if (n < N && k < K) v |= fp4_code(q, Kh, n, k) << (4 * e);
+        }
+        w[t] = v;
+    }
+    *reinterpret_cast<u32x4*>(dst + 16 * L) = w;
+    if (j == 0) {
+        const int KB = K / 16;
+#pragma unroll
+        for (int b = 0; b < 8; ++b) {
+            const int kb = kKC * c + 16 * b;
+            dst[1024 + 8 * ln + b] = (n < N && kb < K) ? s[(size_t)n * KB + kb / 16] : (uint8_t)0;
+        }
+    }
+}
+
 int32_t check_w4_dims(const char* who, int K, int N, int G) {
     if (G != 32 && G != 64) return fail(EV_EUNSUPPORTED, "%s: group size %d (32 or 64)", who, G);
     if (K <= 0 || N <= 0) return fail(EV_EINVAL, "%s: K=%d N=%d must be positive", who, K, N);
@@ -96,3 +142,26 @@ extern "C" int32_t w4_pack(const uint8_t* q, const uint16_t* s, const uint16_t* 
                        reinterpret_cast<uint8_t*>(packed));
     return check_hip(hipGetLastError(), "w4_pack launch");
 }
+
+extern "C" size_t nvfp4_packed_bytes(int32_t N, int32_t K) {
+    if (N <= 0 || K <= 0) return 0;
+    return w4_blob_bytes(N, K, 64);
+}
+
+extern "C" int32_t nvfp4_pack(const uint8_t* q, const uint8_t* s, int32_t N, int32_t K, void* packed,
+                              size_t packed_bytes, void* stream) {
+    clear_error();
+    const char* who = "nvfp4_pack";
+    int32_t rc = check_w4_dims(who, K, N, 32);  // K a multiple of 32
+    if (rc) return rc;
+    if (!q || !s || !packed) return fail(EV_EINVAL, "%s: NULL pointer", who);
+    if (!aligned(packed, 16)) return fail(EV_EINVAL, "%s: misaligned packed buffer (16 B)", who);
+    if (packed_bytes < w4_blob_bytes(N, K, 64))
+        return fail(EV_EINVAL, "%s: packed buffer needs %zu bytes, got %zu", who, w4_blob_bytes(N, K, 64),
+                    packed_bytes);
+    const long total = (long)w4_tiles(N) * w4_chunks(K) * 64;
+    hipLaunchKernelGGL(nvfp4_pack_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
+                       reinterpret_cast<hipStream_t>(stream), q, s, N, K, reinterpret_cast<uint8_t*>(packed));
+    return check_hip(hipGetLastError(), "nvfp4_pack launch");
+}
+

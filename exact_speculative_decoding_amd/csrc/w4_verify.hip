@@ -114,6 +114,80 @@ __device__ __forceinline__ uint16_t silu_mul_bf16(float g, float u) {
 
 enum W4Mode { kPlain = 0, kPairMode = 1, kRopeMode = 2 };
 
+// Weight formats the plain W4 launches stream:
+//  * kAffine: uint4 codes with an fp16 (scale, bias) pair per group of G;
+//  * kNvfp4: FP4 E2M1 codes with an FP8 E4M3 scale per block of 16 and one
+//    fp32 tensor scale (the NVFP4-style checkpoints the blog's "The honest
+//    limits" section names).  Same tile-chunk size as affine G = 64: 1 KB of
+//    codes, then 8 scale bytes per row (block b of the chunk at byte b).
+enum W4Format { kAffine = 0, kNvfp4 = 1 };
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+// Four E2M1 codes (one 16-bit half of a packed dword, low nibble first) ->
+// four bf16, exact (the conversion's scale 1.0 leaves them unscaled).
+__device__ __forceinline__ bf16x4 e2m1x4_to_bf16(uint32_t d, int half) {
+    const bf16x2 lo = half ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, 1.0f, 2)
+                           : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, 1.0f, 0);
+    const bf16x2 hi = half ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, 1.0f, 3)
+                           : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, 1.0f, 1);
+    return bf16x4{lo[0], lo[1], hi[0], hi[1]};
+}
+
+// Byte `b` (0..3) of a dword as an FP8 E4M3 value, exact in fp32.
+__device__ __forceinline__ float e4m3_byte(uint32_t d, int b) {
+    switch (b) {
+        case 0: return __builtin_amdgcn_cvt_f32_fp8((int)d, 0);
+        case 1: return __builtin_amdgcn_cvt_f32_fp8((int)d, 1);
+        case 2: return __builtin_amdgcn_cvt_f32_fp8((int)d, 2);
+        default: return __builtin_amdgcn_cvt_f32_fp8((int)d, 3);
+    }
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// NVFP4 activation staging: the 16 x 16 x 16 MFMA steps of a 32-k step take
+// lane (r, j)'s A fragment as x[r][4j .. 4j+3] of the step's first 16 k (one
+// scale block) and x[r][16+4j .. 16+4j+3] of its second, which sit side by
+// side in the lane's 16 bytes.  o holds x[r][8 xj .. 8 xj + 7] of step xst.
+__device__ __forceinline__ void xstore_nvfp4(uint8_t* slab, int xc, int xst, int xj, int r, const u32x4& o) {
+    const size_t base = (size_t)(xc * 4 + xst) * 64;
+    const int j0 = 2 * (xj & 1), off = 8 * (xj >> 1);
+    *reinterpret_cast<u32x2*>(slab + (base + r + 16 * j0) * 16 + off) = u32x2{o[0], o[1]};
+    *reinterpret_cast<u32x2*>(slab + (base + r + 16 * (j0 + 1)) * 16 + off) = u32x2{o[2], o[3]};
+}
+
+// One NVFP4 chunk of kNT tiles: per 32-k step and tile, two 16 x 16 x 16 MFMA
+// (one per scale block) on exactly decoded E2M1 weights, each folded into y
+// with its block's E4M3 scale.  Chunks loaded as zeros (past the end) add 0.
+template <int NT_>
+__device__ __forceinline__ void nvfp4_chunk(const u32x4 (&q)[NT_], const uint32_t (&sb)[NT_][2],
+                                            const uint8_t* xchunk, int lane, f32x4 (&y)[NT_]) {
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+        const u32x4 xa = *reinterpret_cast<const u32x4*>(xchunk + (size_t)(st * 64 + lane) * 16);
+        const s16x4 A0 = __builtin_bit_cast(s16x4, u32x2{xa[0], xa[1]});
+        const s16x4 A1 = __builtin_bit_cast(s16x4, u32x2{xa[2], xa[3]});
+#pragma unroll
+        for (int t = 0; t < NT_; ++t) {
+            const uint32_t d = q[t][st];
+            const f32x4 a0 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+                A0, __builtin_bit_cast(s16x4, e2m1x4_to_bf16(d, 0)), zero, 0, 0, 0);
+            const f32x4 a1 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+                A1, __builtin_bit_cast(s16x4, e2m1x4_to_bf16(d, 1)), zero, 0, 0, 0);
+            const uint32_t sc = sb[t][st >> 1];
+            const float s0 = e4m3_byte(sc, 2 * (st & 1)), s1 = e4m3_byte(sc, 2 * (st & 1) + 1);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                y[t][i] = fmaf(s0, a0[i], y[t][i]);
+                y[t][i] = fmaf(s1, a1[i], y[t][i]);
+            }
+        }
+    }
+}
+
 // One workgroup of a W4 pass.
 //  * kPlain (kWaves waves): workgroup blk computes its waves' kNT tiles of
 //    one matrix over one K-split and writes them to the split's partial (or
@@ -131,8 +205,9 @@ enum W4Mode { kPlain = 0, kPairMode = 1, kRopeMode = 2 };
 //      are turned by the row's position (the (cos, sin) table of the slot),
 //      queries go to the fp32 query rows and keys to their cache slot in
 //      fp16; value heads go to the blocked value cache in fp16.
-template <int G, int MODE, bool NT>
+template <int G, int MODE, bool NT, int FMT = kAffine>
 __device__ __forceinline__ void w4_block(const W4Args& a, long blk, uint8_t (*xlds)[kSlab]) {
+    static_assert(FMT == kAffine || (MODE == kPlain && G == 64), "NVFP4 streams plain launches of 1152-B tile-chunks");
     constexpr bool PAIR = MODE != kPlain;  // the two K-halves in one workgroup
     constexpr int GPC = kKC / G;                // groups per chunk
     constexpr int SBW = GPC;                    // (scale, bias) dwords per lane per chunk
@@ -238,7 +313,10 @@ __device__ __forceinline__ void w4_block(const W4Args& a, long blk, uint8_t (*xl
         for (int m = 0; m < kXP; ++m) {
             const int r = xr0 + kXR * m;
             const u32x4 o = xin[m];
-            *reinterpret_cast<u32x4*>(&xlds[2 * half + buf][(size_t)((xc * 4 + xst) * 64 + r + 16 * xj) * 16]) = o;
+            if constexpr (FMT == kNvfp4)
+                xstore_nvfp4(&xlds[2 * half + buf][0], xc, xst, xj, r, o);
+            else
+                *reinterpret_cast<u32x4*>(&xlds[2 * half + buf][(size_t)((xc * 4 + xst) * 64 + r + 16 * xj) * 16]) = o;
         }
     };
 
@@ -277,6 +355,10 @@ __device__ __forceinline__ void w4_block(const W4Args& a, long blk, uint8_t (*xl
     // tile; per group, y += s * acc + (b - 16 s) * xs.  A chunk that was
     // loaded as zeros (past c1) adds exactly zero.
     auto compute = [&](int slot, const uint8_t* xchunk) {
+        if constexpr (FMT == kNvfp4) {
+            nvfp4_chunk<kNT>(qr[slot], sbr[slot], xchunk, lane, y);
+            return;
+        }
         f32x4 acc[kNT], xs = {0.f, 0.f, 0.f, 0.f};
         const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -419,17 +501,17 @@ __device__ __forceinline__ void w4_block(const W4Args& a, long blk, uint8_t (*xl
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = 4 * j + i;
-                if (r < rows) out[(size_t)r * a.N + n] = y[t][i];
+                if (r < rows) out[(size_t)r * a.N + n] = FMT == kNvfp4 ? y[t][i] * a.tscale : y[t][i];
             }
         }
     }
 }
 
-template <int G, bool NT>
+template <int G, bool NT, int FMT = kAffine>
 __global__ __launch_bounds__(kThreads) void w4_verify_kernel(W4Args a) {
     __shared__ __align__(16) uint8_t xlds[2][kSlab];
     if (a.tstamp && threadIdx.x == 0) a.tstamp[2 * blockIdx.x] = wall_clock64();
-    w4_block<G, kPlain, NT>(a, blockIdx.x, xlds);
+    w4_block<G, kPlain, NT, FMT>(a, blockIdx.x, xlds);
     if (a.tstamp) {  // uniform; grouped launches (which may return early) are never timed
         __syncthreads();
         if (threadIdx.x == 0) a.tstamp[2 * blockIdx.x + 1] = wall_clock64();
@@ -447,8 +529,9 @@ __global__ __launch_bounds__(kThreads) void w4_verify_kernel(W4Args a) {
 // another block, the workgroup writes its accumulators as one partial segment
 // and starts again from zero.  The segments of a block are added in ascending
 // workgroup order by sk_reduce_kernel.
-template <int G, bool NT>
+template <int G, bool NT, int FMT = kAffine>
 __device__ __forceinline__ void w4_sk_block(const W4Args& a, int w, uint8_t (*xlds)[kSlab]) {
+    static_assert(FMT == kAffine || G == 64, "NVFP4 tile-chunks have the 1152-B size of G = 64");
     constexpr int GPC = kKC / G;
     constexpr int SBW = GPC;
     constexpr uint32_t CB = 1024 + 64 * GPC;
@@ -517,7 +600,10 @@ __device__ __forceinline__ void w4_sk_block(const W4Args& a, int w, uint8_t (*xl
         for (int m = 0; m < kXP; ++m) {
             const int r = xr0 + kXR * m;
             const u32x4 o = xin[m];
-            *reinterpret_cast<u32x4*>(&xlds[buf][(size_t)((xc * 4 + xst) * 64 + r + 16 * xj) * 16]) = o;
+            if constexpr (FMT == kNvfp4)
+                xstore_nvfp4(&xlds[buf][0], xc, xst, xj, r, o);
+            else
+                *reinterpret_cast<u32x4*>(&xlds[buf][(size_t)((xc * 4 + xst) * 64 + r + 16 * xj) * 16]) = o;
         }
     };
 
@@ -554,6 +640,10 @@ __device__ __forceinline__ void w4_sk_block(const W4Args& a, int w, uint8_t (*xl
     for (int t = 0; t < kNT; ++t) y[t] = f32x4{0.f, 0.f, 0.f, 0.f};
     // one chunk, exactly as in the split pass
     auto compute = [&](int slot, const uint8_t* xchunk) {
+        if constexpr (FMT == kNvfp4) {
+            nvfp4_chunk<kNT>(qr[slot], sbr[slot], xchunk, lane, y);
+            return;
+        }
         f32x4 acc[kNT], xs = {0.f, 0.f, 0.f, 0.f};
         const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -595,7 +685,7 @@ __device__ __forceinline__ void w4_sk_block(const W4Args& a, int w, uint8_t (*xl
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = 4 * j + i;
-                if (r < rows) o[(size_t)r * kBlockCols + cl] = y[t][i];
+                if (r < rows) o[(size_t)r * kBlockCols + cl] = FMT == kNvfp4 ? y[t][i] * a.tscale : y[t][i];
             }
             y[t] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
@@ -646,11 +736,11 @@ __device__ __forceinline__ void w4_sk_block(const W4Args& a, int w, uint8_t (*xl
     }
 }
 
-template <int G, bool NT>
+template <int G, bool NT, int FMT = kAffine>
 __global__ __launch_bounds__(kThreads) void w4_sk_kernel(W4Args a) {
     __shared__ __align__(16) uint8_t xlds[2][kSlab];
     if (a.tstamp && threadIdx.x == 0) a.tstamp[2 * blockIdx.x] = wall_clock64();
-    w4_sk_block<G, NT>(a, blockIdx.x, xlds);
+    w4_sk_block<G, NT, FMT>(a, blockIdx.x, xlds);
     if (a.tstamp) {
         __syncthreads();
         if (threadIdx.x == 0) a.tstamp[2 * blockIdx.x + 1] = wall_clock64();
@@ -937,7 +1027,12 @@ int32_t launch_w4(W4Args args, int nmat, const W4Plan& p, int K, int G, hipStrea
     }
     const unsigned blocks = (unsigned)args.blocks;
     const bool nt = stream_hint((double)args.wbytes * nmat * ngroups);
-    if (G == 64 && nt)
+    if (args.fmt == kNvfp4) {
+        if (nt)
+            hipLaunchKernelGGL((w4_verify_kernel<64, true, kNvfp4>), dim3(blocks), dim3(kThreads), 0, st, args);
+        else
+            hipLaunchKernelGGL((w4_verify_kernel<64, false, kNvfp4>), dim3(blocks), dim3(kThreads), 0, st, args);
+    } else if (G == 64 && nt)
         hipLaunchKernelGGL((w4_verify_kernel<64, true>), dim3(blocks), dim3(kThreads), 0, st, args);
     else if (G == 64)
         hipLaunchKernelGGL((w4_verify_kernel<64, false>), dim3(blocks), dim3(kThreads), 0, st, args);
@@ -969,7 +1064,12 @@ int32_t launch_w4_sk(W4Args args, int nmat, const SkPlan& q, int K, int G, hipSt
     int32_t rc = timing_slots(q.nwg, w4_algo_bytes(nmat, args.R, K, args.N, G), &args.tstamp);
     if (rc) return rc;
     const bool nt = stream_hint((double)args.wbytes * nmat);
-    if (G == 64 && nt)
+    if (args.fmt == kNvfp4) {
+        if (nt)
+            hipLaunchKernelGGL((w4_sk_kernel<64, true, kNvfp4>), dim3(q.nwg), dim3(kThreads), 0, st, args);
+        else
+            hipLaunchKernelGGL((w4_sk_kernel<64, false, kNvfp4>), dim3(q.nwg), dim3(kThreads), 0, st, args);
+    } else if (G == 64 && nt)
         hipLaunchKernelGGL((w4_sk_kernel<64, true>), dim3(q.nwg), dim3(kThreads), 0, st, args);
     else if (G == 64)
         hipLaunchKernelGGL((w4_sk_kernel<64, false>), dim3(q.nwg), dim3(kThreads), 0, st, args);
@@ -1248,6 +1348,48 @@ extern "C" int32_t verify_linear_w4(const uint16_t* x, int32_t R, int32_t K, con
     }
     a.split_stride = L.p.S > 1 ? (long)16 * N : 0;
     if ((rc = launch_w4(a, 1, L.p, K, G, st))) return rc;
+    if (L.p.S > 1 && (rc = launch_splitk_reduce(part, L.p.S, N, R, y, st))) return rc;
+    return EV_OK;
+}
+
+// NVFP4: the same launches as verify_linear_w4 at G = 64 (the tile-chunks have
+// that size), with the NVFP4 decode and the tensor scale.
+extern "C" size_t verify_linear_nvfp4_workspace(int32_t K, int32_t N) {
+    if (K <= 0 || N <= 0) return 0;
+    return lin_layout(K, N).total;
+}
+
+extern "C" int32_t verify_linear_nvfp4(const uint16_t* x, int32_t R, int32_t K, const void* w, int32_t N,
+                                       float tensor_scale, float* y, void* ws, size_t ws_bytes, void* stream) {
+    clear_error();
+    const char* who = "verify_linear_nvfp4";
+    int32_t rc;
+    // K a multiple of 32 (whole 16-k scale blocks, whole 32-k MFMA steps)
+    if ((rc = check_lanes(who, R)) || (rc = check_w4_dims(who, K, N, 32))) return rc;
+    if (!(tensor_scale == tensor_scale) || tensor_scale == __builtin_huge_valf() || tensor_scale == -__builtin_huge_valf())
+        return fail(EV_EINVAL, "%s: tensor scale must be finite", who);
+    if (!x || !w || !y) return fail(EV_EINVAL, "%s: NULL pointer", who);
+    if (!aligned(x, 16) || !aligned(w, 16) || !aligned(y, 4))
+        return fail(EV_EINVAL, "%s: misaligned pointer (x, w 16 B; y 4 B)", who);
+    const LinLayout L = lin_layout(K, N);
+    if ((rc = check_ws(who, ws, ws_bytes, L.total))) return rc;
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    float* part = reinterpret_cast<float*>(ws);
+    W4Args a{};
+    a.w[0] = a.w[1] = reinterpret_cast<const uint8_t*>(w);
+    a.out[0] = a.out[1] = L.p.S > 1 ? part : y;
+    a.x = x;
+    a.R = R;
+    a.N = N;
+    a.fmt = kNvfp4;
+    a.tscale = tensor_scale;
+    if (L.sk) {
+        a.sk_part = part;
+        if ((rc = launch_w4_sk(a, 1, L.q, K, 64, st))) return rc;
+        return launch_sk_reduce(part, L.q, 1, N, R, y, nullptr, nullptr, st);
+    }
+    a.split_stride = L.p.S > 1 ? (long)16 * N : 0;
+    if ((rc = launch_w4(a, 1, L.p, K, 64, st))) return rc;
     if (L.p.S > 1 && (rc = launch_splitk_reduce(part, L.p.S, N, R, y, st))) return rc;
     return EV_OK;
 }

@@ -103,6 +103,33 @@ int32_t verify_linear_w4(const uint16_t* x_bf16, int32_t R, int32_t K, const voi
                          void* stream);
 
 /* ------------------------------------------------------------------------- */
+/* A second 4-bit format: NVFP4-style block scales (the blog's "The honest    */
+/* limits" section: NVFP4 checkpoints).                                       */
+/*                                                                            */
+/* w[n][k] = e2m1(q[n][k]) * e4m3(s[n][k/16]) * tensor_scale, with           */
+/*   q [N][K/2] bytes: two FP4 E2M1 codes per byte (sign, 2 exponent bits of  */
+/*     bias 1, 1 mantissa bit: 0 .. 6), low nibble = even k;                 */
+/*   s [N][K/16] bytes: one FP8 E4M3 scale (OCP, no infinities) per 16 k.     */
+/* nvfp4_pack copies a matrix once into the packed layout the kernel streams  */
+/* (tiles of 16 rows by chunks of 128 k: 1 KB of codes in the kernel's lane   */
+/* order, then the rows' 8 block scales; nvfp4_packed_bytes(N, K) bytes, the  */
+/* standard N*K/2 + N*K/16 when N % 16 == 0 and K % 128 == 0).               */
+/* verify_linear_nvfp4: y[r][n] = sum_k x[r][k] * w[n][k] for the R <= 16     */
+/* rows, arguments as verify_linear_w4 (workspace from                        */
+/* verify_linear_nvfp4_workspace), with the same row exactness: the order of  */
+/* every reduction is fixed by (N, K).  Limits: K > 0, K % 32 == 0, N > 0,    */
+/* tensor_scale finite.  Errors: EV_EINVAL, EV_EUNSUPPORTED, EV_EWORKSPACE,   */
+/* EV_EHIP.                                                                   */
+/* ------------------------------------------------------------------------- */
+size_t nvfp4_packed_bytes(int32_t N, int32_t K);
+int32_t nvfp4_pack(const uint8_t* q, const uint8_t* scale_e4m3, int32_t N, int32_t K, void* packed,
+                   size_t packed_bytes, void* stream);
+size_t verify_linear_nvfp4_workspace(int32_t K, int32_t N);
+int32_t verify_linear_nvfp4(const uint16_t* x_bf16, int32_t R, int32_t K, const void* w_packed,
+                            int32_t N, float tensor_scale, float* y, void* ws, size_t ws_bytes,
+                            void* stream);
+
+/* ------------------------------------------------------------------------- */
 /* SiLU-gated MLP verify slice (dense).                                       */
 /*                                                                            */
 /*   g = W_gate x, u = W_up x          (W4 linears H -> I, fp32 out)          */
