@@ -46,6 +46,8 @@ def parse():
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-legs", action="store_true",
                     help="skip the LM-head, MoE and decoder legs")
+    ap.add_argument("--legs", default="lm_head,moe,formats,decoder_4096,decoder_32768,prefill",
+                    help="comma list of the legs to run after the MLP slice")
     ap.add_argument("--graph", action="store_true",
                     help="replay each step from a captured HIP graph (checked against eager)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -610,21 +612,22 @@ def main():
         out["stream_ceiling"] = stream_ceiling(ev, dev, stream)
         print("# stream ceiling done", file=sys.stderr, flush=True)
     if not args.no_legs:
-        legs = {}
-        legs["lm_head_sampler"] = leg_lm_head(ev, syn, to_dev, stream, args.steps)
-        print("# lm head leg done", file=sys.stderr, flush=True)
-        legs["moe_layer"] = leg_moe(ev, syn, to_dev, stream, args.steps)
-        print("# moe leg done", file=sys.stderr, flush=True)
-        legs["formats"] = leg_formats(ev, syn, to_dev, stream, args.steps)
-        print("# formats leg done", file=sys.stderr, flush=True)
-        legs["decoder_4096"] = leg_decoder(ev, syn, 4096, cpu_steps=0 if args.no_cpu_baseline else 24)
-        print("# decoder leg (cache 4096) done", file=sys.stderr, flush=True)
-        legs["decoder_32768"] = leg_decoder(ev, syn, 32768, cpu_steps=0 if args.no_cpu_baseline else 16)
-        print("# decoder leg (cache 32768) done", file=sys.stderr, flush=True)
-        legs["prefill_4096"] = leg_prefill(ev, syn)
-        print("# prefill leg done", file=sys.stderr, flush=True)
+        legs, want = {}, set(args.legs.split(","))
+        runs = [("lm_head", "lm_head_sampler", lambda: leg_lm_head(ev, syn, to_dev, stream, args.steps)),
+                ("moe", "moe_layer", lambda: leg_moe(ev, syn, to_dev, stream, args.steps)),
+                ("formats", "formats", lambda: leg_formats(ev, syn, to_dev, stream, args.steps)),
+                ("decoder_4096", "decoder_4096",
+                 lambda: leg_decoder(ev, syn, 4096, cpu_steps=0 if args.no_cpu_baseline else 24)),
+                ("decoder_32768", "decoder_32768",
+                 lambda: leg_decoder(ev, syn, 32768, cpu_steps=0 if args.no_cpu_baseline else 16)),
+                ("prefill", "prefill_4096", lambda: leg_prefill(ev, syn))]
+        for name, key, fn in runs:
+            if name in want:
+                legs[key] = fn()
+                print(f"# {key} leg done", file=sys.stderr, flush=True)
         out["legs"] = legs
-        out["exact_accepted_tok_s"] = legs["decoder_4096"]["accepted_tok_s"]
+        if "decoder_4096" in legs:
+            out["exact_accepted_tok_s"] = legs["decoder_4096"]["accepted_tok_s"]
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(d, R)
         out["cpu_baseline"]["sampler"] = cpu_sampler(syn)
