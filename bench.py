@@ -48,6 +48,9 @@ def parse():
                     help="skip the LM-head, MoE and decoder legs")
     ap.add_argument("--legs", default="lm_head,moe,formats,decoder_4096,decoder_32768,prefill",
                     help="comma list of the legs to run after the MLP slice")
+    ap.add_argument("--legs-only", action="store_true",
+                    help="run only the legs named by --legs (no MLP slice, no headline line): "
+                         "for profiling one leg at a time")
     ap.add_argument("--graph", action="store_true",
                     help="replay each step from a captured HIP graph (checked against eager)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -428,6 +431,24 @@ def leg_prefill(ev, syn, C=4096, P=3584, grid=2048, reps=3):
             "roofline_tok_s": round(roof, 1), "pct_roofline": round(100 * tps / roof, 2)}
 
 
+def run_legs(args, ev, syn, to_dev, stream):
+    """The legs named by --legs, in a fixed order, each timed on its own."""
+    legs, want = {}, set(args.legs.split(","))
+    runs = [("lm_head", "lm_head_sampler", lambda: leg_lm_head(ev, syn, to_dev, stream, args.steps)),
+            ("moe", "moe_layer", lambda: leg_moe(ev, syn, to_dev, stream, args.steps)),
+            ("formats", "formats", lambda: leg_formats(ev, syn, to_dev, stream, args.steps)),
+            ("decoder_4096", "decoder_4096",
+             lambda: leg_decoder(ev, syn, 4096, cpu_steps=0 if args.no_cpu_baseline else 24)),
+            ("decoder_32768", "decoder_32768",
+             lambda: leg_decoder(ev, syn, 32768, cpu_steps=0 if args.no_cpu_baseline else 16)),
+            ("prefill", "prefill_4096", lambda: leg_prefill(ev, syn))]
+    for name, key, fn in runs:
+        if name in want:
+            legs[key] = fn()
+            print(f"# {key} leg done", file=sys.stderr, flush=True)
+    return legs
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -459,14 +480,18 @@ def main():
                           "launches": 5}), flush=True)
         return
 
-    d = syn.mlp()
-    H, I, G = d["H"], d["I"], d["G"]
-
     def to_dev(a):
         a = np.ascontiguousarray(a)
         if a.dtype == np.uint16:
             a = a.view(np.int16)
         return torch.from_numpy(a).to(dev)
+
+    if args.legs_only:
+        print(json.dumps({"legs": run_legs(args, ev, syn, to_dev, torch.cuda.current_stream())}), flush=True)
+        return
+
+    d = syn.mlp()
+    H, I, G = d["H"], d["I"], d["G"]
 
     copies = []
     for c in range(args.copies):
@@ -612,19 +637,7 @@ def main():
         out["stream_ceiling"] = stream_ceiling(ev, dev, stream)
         print("# stream ceiling done", file=sys.stderr, flush=True)
     if not args.no_legs:
-        legs, want = {}, set(args.legs.split(","))
-        runs = [("lm_head", "lm_head_sampler", lambda: leg_lm_head(ev, syn, to_dev, stream, args.steps)),
-                ("moe", "moe_layer", lambda: leg_moe(ev, syn, to_dev, stream, args.steps)),
-                ("formats", "formats", lambda: leg_formats(ev, syn, to_dev, stream, args.steps)),
-                ("decoder_4096", "decoder_4096",
-                 lambda: leg_decoder(ev, syn, 4096, cpu_steps=0 if args.no_cpu_baseline else 24)),
-                ("decoder_32768", "decoder_32768",
-                 lambda: leg_decoder(ev, syn, 32768, cpu_steps=0 if args.no_cpu_baseline else 16)),
-                ("prefill", "prefill_4096", lambda: leg_prefill(ev, syn))]
-        for name, key, fn in runs:
-            if name in want:
-                legs[key] = fn()
-                print(f"# {key} leg done", file=sys.stderr, flush=True)
+        legs = run_legs(args, ev, syn, to_dev, stream)
         out["legs"] = legs
         if "decoder_4096" in legs:
             out["exact_accepted_tok_s"] = legs["decoder_4096"]["accepted_tok_s"]
