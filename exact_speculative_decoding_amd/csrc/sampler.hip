@@ -11,11 +11,11 @@
 // dimension (each row is processed by its own workgroups, identically):
 //   topk_chunk_kernel   grid (ceil(V/4096), R) x 256: each workgroup selects
 //                       the top-kk of its 4096 logits under (logit desc, id asc)
-//                       as 64-bit order keys: each wave takes its own top-kk
-//                       by kk rounds of a DPP wave maximum, and the four lists
-//                       are merged by counting larger keys;
-//   merge_sample_kernel grid R x 64: one wave merges the chunk lists into the
-//                       row's top-kk, then top-p and the keyed argmax in fp64.
+//                       as 64-bit order keys: the keys at or above a lower
+//                       bound of the kk-th are placed by counting larger keys;
+//   merge_sample_kernel grid R x 256: the workgroup merges the chunk lists
+//                       into the row's top-kk the same way, then one wave
+//                       takes top-p and the keyed argmax in fp64.
 // The selection involves no arithmetic, so it is exact; the fp64 stage follows
 // the same fixed order for every row.
 #include "ev_internal.h"
@@ -65,32 +65,6 @@ __device__ __forceinline__ void sort16_desc(unsigned long long (&k)[kPer]) {
             }
 }
 
-// Maximum of a 32-bit value over the wave (DPP steps as in wave_max_u64),
-// returned to every lane.
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-    uint32_t o;
-    o = __builtin_amdgcn_update_dpp(v, v, 0x111, 0xf, 0xf, false);  // row_shr:1
-    v = o > v ? o : v;
-    o = __builtin_amdgcn_update_dpp(v, v, 0x112, 0xf, 0xf, false);  // row_shr:2
-    v = o > v ? o : v;
-    o = __builtin_amdgcn_update_dpp(v, v, 0x114, 0xf, 0xf, false);  // row_shr:4
-    v = o > v ? o : v;
-    o = __builtin_amdgcn_update_dpp(v, v, 0x118, 0xf, 0xf, false);  // row_shr:8
-    v = o > v ? o : v;
-    o = __builtin_amdgcn_update_dpp(v, v, 0x142, 0xa, 0xf, false);  // row_bcast:15
-    v = o > v ? o : v;
-    o = __builtin_amdgcn_update_dpp(v, v, 0x143, 0xc, 0xf, false);  // row_bcast:31
-    v = o > v ? o : v;
-    return __builtin_amdgcn_readlane(v, 63);
-}
-// The wave's largest 64-bit key: the largest high word, then the largest low
-// word among the lanes that hold it (the lexicographic order of the pair).
-__device__ __forceinline__ unsigned long long wave_max_key(unsigned long long k) {
-    const uint32_t hi = (uint32_t)(k >> 32);
-    const uint32_t mh = wave_max_u32(hi);
-    const uint32_t ml = wave_max_u32(hi == mh ? (uint32_t)k : 0u);
-    return ((unsigned long long)mh << 32) | ml;
-}
 // Entries of the descending list l[0..n) greater than e.
 __device__ __forceinline__ int count_greater(const unsigned long long* l, int n, unsigned long long e) {
     int lo = 0, hi = n;
@@ -104,14 +78,86 @@ __device__ __forceinline__ int count_greater(const unsigned long long* l, int n,
     return lo;
 }
 
-// The chunk's top-kk keys in order.  Every thread sorts its 16 keys once and
-// keeps keys 1..15 in LDS.  Each wave then takes its own top-kk in kk rounds
-// of a wave maximum over the threads' heads (no barrier; the lane that held
-// the winner reads its next key).  The chunk's top-kk lies in the union of
-// the four wave lists, and a candidate's place is the number of larger keys
-// in the four lists (binary search in the other three): keys are unique, so
-// the places of the chunk's top-kk are 0..kk-1 and every other candidate's
-// place is kk or more.
+// Lane src's value, the same in every lane (v_readlane: no LDS round trip;
+// src must be the same in every lane).
+__device__ __forceinline__ int lane_i32(int v, int src) { return __builtin_amdgcn_readlane(v, src); }
+__device__ __forceinline__ float lane_f32(float v, int src) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), src));
+}
+__device__ __forceinline__ double lane_f64(double v, int src) {
+    const unsigned long long b = __builtin_bit_cast(unsigned long long, v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, src);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), src);
+    return __builtin_bit_cast(double, ((unsigned long long)hi << 32) | lo);
+}
+__device__ __forceinline__ unsigned long long lane_u64(unsigned long long v, int src) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, src);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), src);
+    return ((unsigned long long)hi << 32) | lo;
+}
+// Order key of a double (larger key, larger value; -0 folded onto +0, so equal
+// values have equal keys); 0 is below every key of a non-NaN value.
+__device__ __forceinline__ unsigned long long f64_order_key(double v) {
+    const unsigned long long b = v == 0.0 ? 0ull : __builtin_bit_cast(unsigned long long, v);
+    return (b >> 63) ? ~b : (b | 0x8000000000000000ull);
+}
+
+// Inclusive prefix sum of v over the wave's lanes.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int o = __shfl_up(v, off, 64);
+        if (lane >= off) v += o;
+    }
+    return v;
+}
+
+// Selection by rank: cand[0..n) holds distinct keys; the key with exactly
+// `rank` larger keys among them goes to out[rank] when rank < kk.  nthreads
+// threads share the candidates (every thread reads every candidate: LDS
+// broadcasts).  The caller syncs before (cand complete) and after (out).
+__device__ __forceinline__ int rank_of(const unsigned long long* cand, int n, unsigned long long e) {
+    int rank = 0;
+    int i = 0;
+    for (; i + 8 <= n; i += 8) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) rank += cand[i + u] > e ? 1 : 0;
+    }
+    for (; i < n; ++i) rank += cand[i] > e ? 1 : 0;
+    return rank;
+}
+__device__ __forceinline__ void place_by_rank(const unsigned long long* cand, int n, int kk,
+                                              unsigned long long* out, int nthreads) {
+    for (int j = threadIdx.x; j < n; j += nthreads) {
+        const unsigned long long e = cand[j];
+        const int rank = rank_of(cand, n, e);
+        if (rank < kk) out[rank] = e;
+    }
+}
+// The kk-th largest nonzero key of sample[0..S) (keys distinct except 0), or
+// 0 when the sample holds fewer than kk nonzero keys: written to *t by the
+// thread that holds it.  The caller zeroes *t and syncs before and after.
+__device__ __forceinline__ void kth_of_sample(const unsigned long long* sample, int S, int kk,
+                                              unsigned long long* t, int nthreads) {
+    for (int j = threadIdx.x; j < S; j += nthreads) {
+        const unsigned long long e = sample[j];
+        if (e != 0ull && rank_of(sample, S, e) == kk - 1) *t = e;
+    }
+}
+constexpr int kRankCap = 256;  // candidates ranked directly; more fall back to selection rounds
+constexpr int kRoundsMax = 2;  // kk up to this (greedy) always selects in rounds: two are cheaper
+
+// The chunk's top-kk keys in order.  Every thread sorts its 16 keys once.
+// The kk-th largest of the maxima of groups of adjacent threads is a lower
+// bound t of the chunk's kk-th largest key (kk distinct keys are at or above
+// it; t = 0 when fewer than kk groups hold a key).  The keys >= t (the chunk's top-kk
+// among them, usually a few more) are gathered in LDS and each is placed by
+// the number of larger ones.  When more than kRankCap keys reach t (ties,
+// short chunks), the selection runs in kk rounds instead: each wave takes its
+// own top-kk by a wave maximum over the threads' heads, and a candidate's
+// place is the number of larger keys in the four wave lists (binary search):
+// keys are unique, so the places of the chunk's top-kk are 0..kk-1.
 // Candidates a row keeps: the top_k largest, 2 when greedy (the argmax and
 // the runner-up for the gap), never more than V; always within 1..64, the
 // bound of the kernels' lists (validated parameters are inside it anyway).
@@ -130,6 +176,10 @@ __global__ __launch_bounds__(kSThreads) void topk_chunk_kernel(const float* __re
     __shared__ unsigned long long rest[kPer - 1][kSThreads];  // thread t's keys 1..15 in column t
     __shared__ unsigned long long wl[kW][EV_MAX_TOPK];       // each wave's top-kk, in order
     __shared__ unsigned long long sel[EV_MAX_TOPK];          // the chunk's top-kk, in order
+    __shared__ unsigned long long cand[kRankCap];            // the keys >= t
+    __shared__ unsigned long long smax[kSThreads];           // the threads' maxima
+    __shared__ unsigned long long s_t;
+    __shared__ int wsum[kW];
     const int r = blockIdx.y, chunk = blockIdx.x, tid = threadIdx.x;
     const int base = chunk * kChunk;
     const float* row = logits + (size_t)r * V;
@@ -140,18 +190,65 @@ __global__ __launch_bounds__(kSThreads) void topk_chunk_kernel(const float* __re
         keys[i] = idx < V ? order_key(row[idx], idx) : 0ull;
     }
     sort16_desc(keys);
-#pragma unroll
-    for (int i = 1; i < kPer; ++i) rest[i - 1][tid] = keys[i];
     if (tid < kk) sel[tid] = 0ull;  // places past the chunk's real keys stay 0
     const int wave = tid >> 6, lane = tid & 63;
-    unsigned long long head = keys[0];
-    int at = 0;
+
+    if (kk > kRoundsMax) {
+        // the lower bound t: the kk-th largest maximum of groups of gs adjacent
+        // threads
+        const int gs = kk <= 32 ? 4 : 2;  // at least 2 kk groups
+        unsigned long long gm = keys[0];
+        for (int off = 1; off < gs; off <<= 1) {
+            const unsigned long long o = __shfl_xor(gm, off, 64);
+            gm = o > gm ? o : gm;
+        }
+        if ((lane & (gs - 1)) == 0) smax[tid / gs] = gm;
+        if (tid == 0) s_t = 0ull;
+        __syncthreads();
+        kth_of_sample(smax, kSThreads / gs, kk, &s_t, kSThreads);
+        __syncthreads();
+        const unsigned long long t = s_t;
+        // the thread's keys >= t (a prefix of its sorted 16; key 0 pads past V)
+        int c = 0;
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) c += (keys[i] >= t && keys[i] != 0ull) ? 1 : 0;
+        const int incl = wave_incl_scan(c);
+        if (lane == 63) wsum[wave] = incl;
+        __syncthreads();
+        int off0 = 0, n = 0;
+#pragma unroll
+        for (int v = 0; v < kW; ++v) {
+            off0 += v < wave ? wsum[v] : 0;
+            n += wsum[v];
+        }
+        if (n <= kRankCap) {
+            const int o = off0 + incl - c;
+#pragma unroll
+            for (int i = 0; i < kPer; ++i)
+                if (i < c) cand[o + i] = keys[i];
+            __syncthreads();
+            place_by_rank(cand, n, kk, sel, kSThreads);
+            __syncthreads();
+            unsigned long long* dst = out + ((size_t)r * nchunk + chunk) * kk;
+            if (tid < kk) dst[tid] = sel[tid];
+            return;
+        }
+    }
+
+    // selection rounds: the thread's keys 1..15 in LDS (its own column); its
+    // current key and the one after it (read ahead, so that a win does not
+    // wait for LDS); nxt is key at of the sorted 16
+#pragma unroll
+    for (int i = 1; i < kPer; ++i) rest[i - 1][tid] = keys[i];
+    unsigned long long head = keys[0], nxt = keys[1];
+    int at = 1;
     for (int round = 0; round < kk; ++round) {
-        const unsigned long long w = wave_max_key(head);
+        const unsigned long long w = wave_max_u64(head);
         if (lane == 0) wl[wave][round] = w;
         if (w != 0ull && head == w) {  // keys are unique: one lane
+            head = nxt;
             ++at;
-            head = at < kPer ? rest[at - 1][tid] : 0ull;
+            nxt = at < kPer ? rest[at - 1][tid] : 0ull;
         }
     }
     __syncthreads();
@@ -182,7 +279,29 @@ struct SampleArgs {
     double* gap;
 };
 
-__global__ __launch_bounds__(64) void merge_sample_kernel(SampleArgs a) {
+// k-way merge of sorted lists in kk rounds by one wave (lane c follows list
+// c, `has` for c < nchunk): a round takes the maximum of the heads, the lane
+// that held it advances (keys are unique), and lane j keeps round j's key.
+// Each lane also holds the entry after its head, read ahead.
+__device__ __forceinline__ void merge_rounds(const unsigned long long* mylist, bool has, int kk,
+                                             unsigned long long& mine) {
+    const int lane = threadIdx.x & 63;
+    int at = 0;
+    unsigned long long head = has ? mylist[0] : 0ull;
+    unsigned long long nxt = has && kk > 1 ? mylist[1] : 0ull;
+    for (int round = 0; round < kk; ++round) {
+        const unsigned long long win = wave_max_u64(head);
+        if (lane == round) mine = win;
+        if (win != 0ull && head == win) {
+            ++at;
+            head = nxt;
+            nxt = at + 1 < kk ? mylist[at + 1] : 0ull;
+        }
+    }
+}
+
+constexpr int kMThreads = 256;  // merge workgroup: four waves select, wave 0 samples
+__global__ __launch_bounds__(kMThreads) void merge_sample_kernel(SampleArgs a) {
     if (a.sd) {
         const ev_sampling s = *a.sd;
         a.T = s.temperature;
@@ -191,22 +310,84 @@ __global__ __launch_bounds__(64) void merge_sample_kernel(SampleArgs a) {
         a.kk = sample_kk_of(s.temperature, s.top_k, a.V);
     }
     __shared__ unsigned long long lists[kMaxChunks * EV_MAX_TOPK];  // [chunk][kk], each in order
-    const int r = blockIdx.x, lane = threadIdx.x;
+    __shared__ unsigned long long cand[kRankCap];                   // the sample, then the keys >= t
+    __shared__ unsigned long long top[EV_MAX_TOPK];
+    __shared__ unsigned long long s_t;
+    __shared__ int s_nc;
+    const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
     const int n = a.nchunk * a.kk;  // <= 64 * 64
     const unsigned long long* src = a.cand + (size_t)r * n;
-    for (int i = lane; i < n; i += 64) lists[i] = src[i];
-    __syncthreads();
-    // k-way merge: lane c follows list c; a round takes the maximum of the
-    // heads, and the lane that held it advances (keys are unique)
-    int at = 0;
-    unsigned long long head = lane < a.nchunk ? lists[lane * a.kk] : 0ull;
-    unsigned long long mine = 0ull;  // candidate j ends up in lane j
-    for (int round = 0; round < a.kk; ++round) {
-        const unsigned long long win = wave_max_u64(head);
-        if (lane == round) mine = win;
-        if (win != 0ull && head == win) {
-            ++at;
-            head = at < a.kk ? lists[lane * a.kk + at] : 0ull;
+    // the lists into LDS, up to sixteen loads in flight per thread
+    {
+        unsigned long long v[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            const int i = kMThreads * u + tid;
+            v[u] = i < n ? src[i] : 0ull;
+        }
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            const int i = kMThreads * u + tid;
+            if (i < n) lists[i] = v[u];
+        }
+    }
+    // The row's top-kk from the chunk lists.  The kk-th largest of a sample
+    // -- the first ms = ceil(kk / nchunk) keys of every list -- is a lower
+    // bound t of the row's kk-th key (t = 0 when the sample holds fewer than
+    // kk keys): the keys >= t are gathered and each is placed by the number
+    // of larger ones.  With more than kRankCap of them, wave 0 merges the
+    // lists in kk rounds instead: a round takes the maximum of the lists'
+    // heads and the lane that held it advances (keys are unique).
+    const bool has = tid < a.nchunk;
+    const unsigned long long* mylist = lists + (has ? tid : 0) * a.kk;
+    unsigned long long mine = 0ull;  // candidate j ends up in lane j of wave 0
+    if (a.kk <= kRoundsMax) {
+        __syncthreads();
+        if (tid >= 64) return;
+        merge_rounds(mylist, has, a.kk, mine);
+    } else {
+        const int ms = (a.kk + a.nchunk - 1) / a.nchunk;
+        const int S = a.nchunk * ms;  // < kk + nchunk <= 128
+        if (tid < a.kk) top[tid] = 0ull;
+        if (tid == 0) s_t = 0ull;
+        __syncthreads();
+        if (tid < S) cand[tid] = lists[(tid / ms) * a.kk + tid % ms];
+        __syncthreads();
+        kth_of_sample(cand, S, a.kk, &s_t, kMThreads);
+        __syncthreads();
+        const unsigned long long t = s_t;
+        // wave 0: lane c counts list c's keys >= t (a prefix: binary search; key
+        // 0 pads) and copies them after the lists before it
+        int c = 0, incl = 0;
+        if (tid < 64) {
+            if (has) {
+                int lo = 0, hi = a.kk;
+                while (lo < hi) {
+                    const int mid = (lo + hi) >> 1;
+                    const unsigned long long e = mylist[mid];
+                    if (e >= t && e != 0ull)
+                        lo = mid + 1;
+                    else
+                        hi = mid;
+                }
+                c = lo;
+            }
+            incl = wave_incl_scan(c);
+            if (tid == 63) s_nc = incl;
+        }
+        __syncthreads();
+        const int nc = s_nc;
+        if (nc <= kRankCap) {
+            if (tid < 64 && incl <= kRankCap)
+                for (int i = 0; i < c; ++i) cand[incl - c + i] = mylist[i];
+            __syncthreads();
+            place_by_rank(cand, nc, a.kk, top, kMThreads);
+            __syncthreads();
+            if (tid >= 64) return;
+            if (lane < a.kk) mine = top[lane];
+        } else {
+            if (tid >= 64) return;
+            merge_rounds(mylist, has, a.kk, mine);
         }
     }
     const int ncand = a.kk < a.V ? a.kk : a.V;
@@ -214,8 +395,8 @@ __global__ __launch_bounds__(64) void merge_sample_kernel(SampleArgs a) {
     const int id = key_id(mine);
 
     if (a.T == 0.0) {  // greedy: candidates 0 and 1 of the exact order
-        const double l0 = (double)__shfl(l, 0, 64), l1 = (double)__shfl(l, 1, 64);
-        const int id0 = __shfl(id, 0, 64);
+        const double l0 = (double)lane_f32(l, 0), l1 = (double)lane_f32(l, 1);
+        const int id0 = lane_i32(id, 0);
         if (lane == 0) {
             a.tokens[r] = id0;
             if (a.gap) a.gap[r] = ncand > 1 ? l0 - l1 : __builtin_huge_val();
@@ -223,44 +404,42 @@ __global__ __launch_bounds__(64) void merge_sample_kernel(SampleArgs a) {
         return;
     }
 
-    // top-p: e_j = exp((l_j - l_0) / T), Z summed in candidate order; keep j
-    // while the mass before it is below top_p * Z.  Every lane runs the same
-    // sequential loop on the shuffled values, so all lanes agree.
-    const double m = (double)__shfl(l, 0, 64);
+    // top-p: e_j = exp((l_j - l_0) / T), Z summed in candidate order (every
+    // lane runs the same sequential sum on values read from lane j); lane j
+    // keeps the mass before it, P_j.  Candidate j is kept while P_j < top_p Z
+    // (j = 0 always): the masses are >= 0, so P_j grows with j and the kept
+    // candidates are 0 and the lanes j >= 1 with P_j < top_p Z.
+    const double m = (double)lane_f32(l, 0);
     const double e = lane < ncand ? exp(((double)l - m) / a.T) : 0.0;
-    double Z = 0.0;
-    for (int jj = 0; jj < ncand; ++jj) Z += __shfl(e, jj, 64);
-    const double thr = a.top_p * Z;
-    int kept = 0;
-    double before = 0.0;
+    double Z = 0.0, P = 0.0;
     for (int jj = 0; jj < ncand; ++jj) {
-        if (jj > 0 && !(before < thr)) break;
-        kept = jj + 1;
-        before += __shfl(e, jj, 64);
+        if (lane == jj) P = Z;
+        Z += lane_f64(e, jj);
     }
+    const double thr = a.top_p * Z;
+    const int kept = 1 + __popcll(__ballot(lane >= 1 && lane < ncand && P < thr));
 
-    // perturbed scores and the argmax (lower id on equal scores)
+    // perturbed scores (one per lane) and the argmax under (score desc, id
+    // asc): a wave maximum of the scores' order keys (-0 folded onto +0, so
+    // equal scores have equal keys), the lowest id among the lanes that hold
+    // it; then the best score among the other kept candidates (from the
+    // lowest lane that holds it)
     const long long pos = a.positions[r];
     double z = -__builtin_huge_val();
     if (lane < kept) z = (double)l / a.T + keyed_gumbel(a.seed, pos, id);
-    double bz = z;
-    int bid = lane < kept ? id : 0x7fffffff;
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        const double oz = __shfl_xor(bz, off, 64);
-        const int oid = __shfl_xor(bid, off, 64);
-        if (oz > bz || (oz == bz && oid < bid)) {
-            bz = oz;
-            bid = oid;
-        }
+    const unsigned long long kz = lane < kept ? f64_order_key(z) : 0ull;
+    const unsigned long long kb = wave_max_u64(kz);
+    const unsigned long long tie = __ballot(kz == kb);
+    int bl = __builtin_ctzll(tie);
+    if (__popcll(tie) > 1) {  // equal best scores: the lowest id
+        const unsigned long long mi = wave_max_u64(kz == kb ? (unsigned long long)(0xffffffffu - (uint32_t)id) : 0ull);
+        bl = __builtin_ctzll(__ballot(kz == kb && (unsigned long long)(0xffffffffu - (uint32_t)id) == mi));
     }
-    // second best: the best score among the other kept candidates
-    double sz = (lane < kept && id != bid) ? z : -__builtin_huge_val();
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        const double oz = __shfl_xor(sz, off, 64);
-        sz = oz > sz ? oz : sz;
-    }
+    const int bid = lane_i32(id, bl);
+    const double bz = lane_f64(z, bl);
+    const unsigned long long k2 = id != bid ? kz : 0ull;
+    const unsigned long long ks = wave_max_u64(k2);
+    const double sz = ks ? lane_f64(z, __builtin_ctzll(__ballot(k2 == ks))) : -__builtin_huge_val();
     if (lane == 0) {
         a.tokens[r] = bid;
         if (a.gap) a.gap[r] = kept > 1 ? bz - sz : __builtin_huge_val();
@@ -666,7 +845,7 @@ int32_t launch_keyed_sample(const float* logits, int R, int V, const long long* 
     if (rc) return rc;
     SampleArgs a{cand, positions, nchunk, kk, V, s.temperature, s.top_p, (unsigned long long)s.seed, sd,
                  tokens, gap};
-    hipLaunchKernelGGL(merge_sample_kernel, dim3(R), dim3(64), 0, st, a);
+    hipLaunchKernelGGL(merge_sample_kernel, dim3(R), dim3(kMThreads), 0, st, a);
     return check_hip(hipGetLastError(), "merge_sample launch");
 }
 }  // namespace ev

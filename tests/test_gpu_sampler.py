@@ -93,3 +93,24 @@ def test_accept_matches_oracle():
         a, n = ev.accept_prefix(dev(sampled), dev(draft) if D else None)
         ra, rn = oracle.accept(sampled, draft)
         assert (int(host(a)[0]), int(host(n)[0])) == (ra, rn)
+
+
+@pytest.mark.parametrize("V,k", [(4096, 20), (8192, 64), (32768, 20), (262144, 64)])
+def test_sampler_selection_fallbacks(V, k):
+    """Inputs that defeat the selection's lower bound, so that both kernels
+    also take their round-by-round paths: logits fall by one every four
+    adjacent positions mod 256 (the thread groups of a chunk), so the keys at
+    or above the kk-th group maximum number kk * 64 in a chunk; V = 262144
+    (64 chunks, one sampled key per list at k = 64) gives the merge a loose
+    bound as well.  Tokens and gaps against the oracle, rows bit-exact."""
+    g = np.random.default_rng(V + k)
+    R = 4
+    idx = np.arange(V)
+    base = (100.0 - (idx % 256) // 4).astype(np.float32)
+    logits = np.stack([base + g.integers(0, 3, V).astype(np.float32) * 0.25 for _ in range(R)])
+    pos = g.integers(0, 1 << 30, R).astype(np.int64)
+    for seed in range(5):
+        tok, gap, _ = _compare(logits, pos, 0.8, k, 0.95, seed)
+        t1 = torch.empty(1, dtype=torch.float64, device="cuda")
+        o = host(ev.keyed_sample(dev(logits[2:3]), dev(pos[2:3]), 0.8, k, 0.95, seed, gap=t1))
+        assert o[0] == tok[2] and host(t1)[0].tobytes() == gap[2].tobytes()
