@@ -61,17 +61,29 @@ __device__ __forceinline__ float row_sum(float v, float* red) {
     return t;
 }
 
-// n = bf16(RMSNorm(x) * gain) of one row held as float4s by the block
-// (thread tid owns columns 4 (tid + kRowThreads j)); ss = its sum of squares.
+// The gains of the columns the thread owns (4 (tid + kRowThreads j)), loaded
+// before the row's own inputs so that the norm does not wait for them.
 template <int NV>
-__device__ __forceinline__ void norm_store(const f32x4 (&xv)[NV], float ss, const float* __restrict__ gain,
-                                           float eps, int H, uint16_t* __restrict__ nrow, float* red) {
+__device__ __forceinline__ void gain_load(const float* __restrict__ gain, int H, f32x4 (&gv)[NV]) {
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+        const int c = 4 * (threadIdx.x + kRowThreads * j);
+        gv[j] = c < H ? *reinterpret_cast<const f32x4*>(gain + c) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+}
+
+// n = bf16(RMSNorm(x) * gain) of one row held as float4s by the block
+// (thread tid owns columns 4 (tid + kRowThreads j), gains gv); ss = its sum
+// of squares.
+template <int NV>
+__device__ __forceinline__ void norm_store(const f32x4 (&xv)[NV], const f32x4 (&gv)[NV], float ss, float eps,
+                                           int H, uint16_t* __restrict__ nrow, float* red) {
     const float rs = 1.0f / sqrtf(row_sum(ss, red) / (float)H + eps);
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
         const int c = 4 * (threadIdx.x + kRowThreads * j);
         if (c >= H) continue;
-        const f32x4 g = *reinterpret_cast<const f32x4*>(gain + c);
+        const f32x4 g = gv[j];
         uint32_t w0 = (uint32_t)f32_to_bf16_rne(xv[j][0] * rs * g[0]) | ((uint32_t)f32_to_bf16_rne(xv[j][1] * rs * g[1]) << 16);
         uint32_t w1 = (uint32_t)f32_to_bf16_rne(xv[j][2] * rs * g[2]) | ((uint32_t)f32_to_bf16_rne(xv[j][3] * rs * g[3]) << 16);
         *reinterpret_cast<uint2*>(nrow + c) = make_uint2(w0, w1);
@@ -97,7 +109,8 @@ __global__ __launch_bounds__(kRowThreads) void embed_norm_kernel(const int* __re
     if (tid == 0) tok_copy[r] = tok;  // the drafts, where the rest of the step reads them
     tok = tok < 0 ? 0 : (tok >= V ? V - 1 : tok);  // keeps the read inside the table
     const uint16_t* e = embed + (size_t)tok * H;
-    f32x4 xv[kMaxRowVec];
+    f32x4 gv[kMaxRowVec], xv[kMaxRowVec];
+    gain_load(gain, H, gv);
     float ss = 0.f;
 #pragma unroll
     for (int j = 0; j < kMaxRowVec; ++j) {
@@ -111,7 +124,7 @@ __global__ __launch_bounds__(kRowThreads) void embed_norm_kernel(const int* __re
         *reinterpret_cast<f32x4*>(x + (size_t)r * H + c) = v;
         ss += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
     }
-    norm_store(xv, ss, gain, eps, H, n + (size_t)r * H, red);
+    norm_store(xv, gv, ss, eps, H, n + (size_t)r * H, red);
     if (tid == 0) positions[r] = pos0 + 1 + r;
     if (tid == 0 && r == 0) {
         positions[kPos0Slot] = pos0;
@@ -130,7 +143,8 @@ __global__ __launch_bounds__(kRowThreads) void res_norm_kernel(const float* __re
     __shared__ float red[kRowThreads / 64];
     const int r = blockIdx.x, tid = threadIdx.x;
     const size_t stride = (size_t)16 * H;
-    f32x4 xv[kMaxRowVec];
+    f32x4 gv[kMaxRowVec], xv[kMaxRowVec];
+    gain_load(gain, H, gv);
     float ss = 0.f;
 #pragma unroll
     for (int j = 0; j < kMaxRowVec; ++j) {
@@ -169,7 +183,7 @@ __global__ __launch_bounds__(kRowThreads) void res_norm_kernel(const float* __re
         xv[j] = v;
         ss += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
     }
-    norm_store(xv, ss, gain, eps, H, n + (size_t)r * H, red);
+    norm_store(xv, gv, ss, eps, H, n + (size_t)r * H, red);
 }
 
 // Value cache layout: blocks of 32 slots, d-major inside a block
@@ -226,14 +240,8 @@ __global__ __launch_bounds__(64) void attn_partial_kernel(AttnArgs a) {
     const bool qok = qi < nq;
     const int r = qok ? qi / gq : 0;
     const int h = g * gq + (qok ? qi % gq : 0);
-    const long long pos0 = a.positions[kPos0Slot];
-    const long long P = pos0 + r;
-    const long long pmax = pos0 + a.R - 1;
-    const long long cstart = (long long)chunk * a.chunk;
-    if (cstart > pmax) return;  // the grid covers the whole cache; this chunk holds no slot yet
-    const long long cend = min(cstart + a.chunk - 1, pmax);
-
-    // Q^T fragments: query ln, d = 32 ds + 8 grp + i
+    // Q^T fragments: query ln, d = 32 ds + 8 grp + i (loaded before the
+    // step's position, which they do not need)
     float qv[4][8];
     const float* qp = a.q + ((size_t)r * a.NH + h) * kHD + 8 * grp;
 #pragma unroll
@@ -249,29 +257,15 @@ __global__ __launch_bounds__(64) void attn_partial_kernel(AttnArgs a) {
             qv[ds][4 + i] = v1[i];
         }
     }
-    float amax = 0.f;
-#pragma unroll
-    for (int ds = 0; ds < 4; ++ds)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(qv[ds][i]));
-    amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
-    amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
-    int ex = 0;
-    frexpf(amax, &ex);  // amax in [2^(ex-1), 2^ex)
-    const int e = amax > 0.f ? max(-100, min(100, 15 - ex)) : 0;
-    const float up = ldexpf(1.0f, e);
-    const float sback = ldexpf(1.0f, -e) * a.scale;  // exact: a power of two times the scale
-    f16x8 qh[4], ql[4];
-#pragma unroll
-    for (int ds = 0; ds < 4; ++ds)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const float v = qv[ds][i] * up;
-            const _Float16 hv = (_Float16)v;
-            qh[ds][i] = hv;
-            ql[ds][i] = (_Float16)(v - (float)hv);
-        }
+    const long long pos0 = a.positions[kPos0Slot];
+    const long long P = pos0 + r;
+    const long long pmax = pos0 + a.R - 1;
+    const long long cstart = (long long)chunk * a.chunk;
+    if (cstart > pmax) return;  // the grid covers the whole cache; this chunk holds no slot yet
+    const long long cend = min(cstart + a.chunk - 1, pmax);
 
+    f16x8 qh[4], ql[4];  // the scaled query, split (set after the first keys are requested)
+    float sback = 0.f;
     float m = -INFINITY, l = 0.f;
     f32x4 acc[8];
 #pragma unroll
@@ -373,6 +367,29 @@ __global__ __launch_bounds__(64) void attn_partial_kernel(AttnArgs a) {
     f16x8 kA[2][4], vA[8], kB[2][4], vB[8];
     long long s0 = cstart;
     load_kv(s0, kA, vA);
+    // the query's scale and fp16 halves while the first keys and values load
+    float amax = 0.f;
+#pragma unroll
+    for (int ds = 0; ds < 4; ++ds)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(qv[ds][i]));
+    amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
+    amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+    int ex = 0;
+    frexpf(amax, &ex);  // amax in [2^(ex-1), 2^ex)
+    const int e = amax > 0.f ? max(-100, min(100, 15 - ex)) : 0;
+    const float up = ldexpf(1.0f, e);
+    sback = ldexpf(1.0f, -e) * a.scale;  // exact: a power of two times the scale
+#pragma unroll
+    for (int ds = 0; ds < 4; ++ds)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float v = qv[ds][i] * up;
+            const _Float16 hv = (_Float16)v;
+            qh[ds][i] = hv;
+            ql[ds][i] = (_Float16)(v - (float)hv);
+        }
+
     for (;;) {
         const bool more = s0 + kKStep <= cend;
         if (more) load_kv(s0 + kKStep, kB, vB);
@@ -402,8 +419,9 @@ __global__ __launch_bounds__(64) void attn_partial_kernel(AttnArgs a) {
 // o[r][h][d] = bf16(sum_c acc_c[d] e^(m_c - M) / sum_c l_c e^(m_c - M)) over
 // the chunks c = 0 .. nch-1, nch = (pos0 + r) / chunk + 1; M = max_c m_c.
 // Four groups of kHD threads each sum a fixed quarter of the chunks (chunk
-// order inside a quarter; loads 8 at a time), and the quarters are added in
-// order 0, 1, 2, 3: a fixed order set by the row's own position.
+// order inside a quarter; the quarter's entries loaded up front), and the
+// quarters are added in order 0, 1, 2, 3: a fixed order set by the row's own
+// position.
 constexpr int kMergeGroups = 4;
 __global__ __launch_bounds__(kHD * kMergeGroups) void attn_merge_kernel(const float* __restrict__ part, int NH,
                                                                         int chunk, int nchunk_max,
@@ -418,6 +436,14 @@ __global__ __launch_bounds__(kHD * kMergeGroups) void attn_merge_kernel(const fl
     const int d = tid % kHD, q = tid / kHD;
     const int nch = (int)((pos0 + r) / chunk) + 1;
     const float* b = part + ((size_t)r * NH + h) * nchunk_max * kPartStride;
+    // this thread's accumulator entries (column d of its quarter's chunks),
+    // loaded together with the maxima and sums below: one memory round trip
+    constexpr int kPerMax = kMaxChunks / kMergeGroups;
+    const int per = (nch + kMergeGroups - 1) / kMergeGroups;
+    const int lo = q * per, hi = min(nch, lo + per);
+    float v[kPerMax];
+#pragma unroll
+    for (int i = 0; i < kPerMax; ++i) v[i] = lo + i < hi ? b[(size_t)(lo + i) * kPartStride + 2 + d] : 0.f;
     float mv = -INFINITY;
     if (tid < nch) {
         mv = b[(size_t)tid * kPartStride];
@@ -433,22 +459,14 @@ __global__ __launch_bounds__(kHD * kMergeGroups) void attn_merge_kernel(const fl
     for (int i = 1; i < kMergeGroups * kHD / 64; ++i) M = fmaxf(M, red[i]);
     if (tid < nch) se[tid] = expf(sm[tid] - M);
     __syncthreads();
-    const int per = (nch + kMergeGroups - 1) / kMergeGroups;
-    const int lo = q * per, hi = min(nch, lo + per);
     float L = 0.f, acc = 0.f;
-    for (int c0 = lo; c0 < hi; c0 += 8) {
-        float v[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-            if (c0 + i < hi) v[i] = b[(size_t)(c0 + i) * kPartStride + 2 + d];
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-            if (c0 + i < hi) {
-                const float e = se[c0 + i];
-                L = fmaf(sl[c0 + i], e, L);
-                acc = fmaf(v[i], e, acc);
-            }
-    }
+    for (int i = 0; i < kPerMax; ++i)
+        if (lo + i < hi) {
+            const float e = se[lo + i];
+            L = fmaf(sl[lo + i], e, L);
+            acc = fmaf(v[i], e, acc);
+        }
     pacc[q][d] = acc;
     if (d == 0) pl[q] = L;
     __syncthreads();
@@ -1129,7 +1147,8 @@ __global__ __launch_bounds__(kRowThreads) void draft_norm_kernel(const float* __
                                                                  uint16_t* __restrict__ h) {
     __shared__ float red[kRowThreads / 64];
     if (state[0]) return;
-    f32x4 xv[kMaxRowVec];
+    f32x4 gv[kMaxRowVec], xv[kMaxRowVec];
+    gain_load(gain, H, gv);
     float ss = 0.f;
 #pragma unroll
     for (int j = 0; j < kMaxRowVec; ++j) {
@@ -1139,7 +1158,7 @@ __global__ __launch_bounds__(kRowThreads) void draft_norm_kernel(const float* __
         xv[j] = *reinterpret_cast<const f32x4*>(z + c);
         ss += xv[j][0] * xv[j][0] + xv[j][1] * xv[j][1] + xv[j][2] * xv[j][2] + xv[j][3] * xv[j][3];
     }
-    norm_store(xv, ss, gain, eps, H, h, red);
+    norm_store(xv, gv, ss, eps, H, h, red);
 }
 
 // drafts[i] = argmax of the logits row (lower id on ties); its confidence p =
