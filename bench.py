@@ -334,20 +334,8 @@ def leg_decoder(ev, syn, C, n_tokens=512, R=8, p_draft=0.65, cpu_steps=0):
     roof = per_round * HBM_PEAK_GBS * 1e9 / (w_bytes + kv_round)
     tps = n_tokens / t_drafted
     cpu = None
-    if cpu_steps:  # the oracle's serial steps from the same start, on the host cores
-        import oracle
-        om = oracle.Decoder(cfg, d["w"], d["kc"], d["vc"])
-        tok = d["first_token"]
-        oracle_tokens = []
-        t0 = time.perf_counter()
-        for i in range(cpu_steps):
-            _, tok, _ = om.step(tok, pos0 + i, *samp)
-            oracle_tokens.append(tok)
-        dt = time.perf_counter() - t0
-        cpu = {"kind": "oracle", "tokens": cpu_steps, "ms_per_token": round(1e3 * dt / cpu_steps, 1),
-               "matches_gpu_serial": [int(t) for t in oracle_tokens] == serial[:cpu_steps],
-               "tok_s": round(cpu_steps / dt, 3), "cores": int(oracle.num_threads()),
-               "sample": f"{cpu_steps} serial steps of the 8-layer decoder, cache {C}"}
+    if cpu_steps:  # run after every GPU leg (see run_legs), so its threads disturb none
+        cpu = lambda: cpu_decoder(d, C, cpu_steps, serial, samp)
     return {"workload": f"8-layer decoder H2048 16/4 heads MLP6144 V32768 W4 G64, cache {C}",
             "tokens": n_tokens, "R": R_used, "probe_mismatch_words": probe_words[0],
             "draft_match": p_draft, "rounds": rounds,
@@ -358,6 +346,26 @@ def leg_decoder(ev, syn, C, n_tokens=512, R=8, p_draft=0.65, cpu_steps=0):
             "bytes_per_round": int(w_bytes + kv_round),
             "roofline_tok_s": round(roof, 1), "pct_roofline": round(100 * tps / roof, 2),
             **({"cpu_baseline": cpu} if cpu else {})}
+
+
+def cpu_decoder(d, C, cpu_steps, serial, samp):
+    """The oracle's serial steps of the decoder from the GPU run's start, on
+    the host cores, and whether they sample the GPU's serial tokens."""
+    import oracle
+    cfg = d["cfg"]
+    pos0 = cfg["prefill"]
+    om = oracle.Decoder(cfg, d["w"], d["kc"], d["vc"])
+    tok = d["first_token"]
+    oracle_tokens = []
+    t0 = time.perf_counter()
+    for i in range(cpu_steps):
+        _, tok, _ = om.step(tok, pos0 + i, *samp)
+        oracle_tokens.append(tok)
+    dt = time.perf_counter() - t0
+    return {"kind": "oracle", "tokens": cpu_steps, "ms_per_token": round(1e3 * dt / cpu_steps, 1),
+            "matches_gpu_serial": [int(t) for t in oracle_tokens] == serial[:cpu_steps],
+            "tok_s": round(cpu_steps / dt, 3), "cores": int(oracle.num_threads()),
+            "sample": f"{cpu_steps} serial steps of the 8-layer decoder, cache {C}"}
 
 
 def leg_formats(ev, syn, to_dev, stream, steps):
@@ -446,6 +454,10 @@ def run_legs(args, ev, syn, to_dev, stream):
         if name in want:
             legs[key] = fn()
             print(f"# {key} leg done", file=sys.stderr, flush=True)
+    # the oracle timings of the decoder legs, after all GPU timing
+    for key, leg in legs.items():
+        if callable(leg.get("cpu_baseline")):
+            leg["cpu_baseline"] = leg["cpu_baseline"]()
     return legs
 
 

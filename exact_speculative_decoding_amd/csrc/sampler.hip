@@ -90,11 +90,6 @@ __device__ __forceinline__ double lane_f64(double v, int src) {
     const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), src);
     return __builtin_bit_cast(double, ((unsigned long long)hi << 32) | lo);
 }
-__device__ __forceinline__ unsigned long long lane_u64(unsigned long long v, int src) {
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, src);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), src);
-    return ((unsigned long long)hi << 32) | lo;
-}
 // Order key of a double (larger key, larger value; -0 folded onto +0, so equal
 // values have equal keys); 0 is below every key of a non-NaN value.
 __device__ __forceinline__ unsigned long long f64_order_key(double v) {
