@@ -114,3 +114,23 @@ def test_sampler_selection_fallbacks(V, k):
         t1 = torch.empty(1, dtype=torch.float64, device="cuda")
         o = host(ev.keyed_sample(dev(logits[2:3]), dev(pos[2:3]), 0.8, k, 0.95, seed, gap=t1))
         assert o[0] == tok[2] and host(t1)[0].tobytes() == gap[2].tobytes()
+
+
+def test_sampler_random_configurations():
+    """Forty seeded random configurations (V from 1 to 262144, k from 1 to 64
+    and 0, T 0 or up to 2, top-p, R from 1 to 16) against the oracle: every
+    selection path of both kernels (bound and rank, rounds, greedy)."""
+    g = np.random.default_rng(2024)
+    for trial in range(40):
+        V = int(np.exp(g.uniform(0, np.log(262144)))) if trial % 4 else int(g.choice([1, 2, 4095, 4096, 4097, 262144]))
+        V = max(1, min(V, 262144))
+        k = int(g.integers(0, 65)) if trial % 5 else int(g.choice([1, 2, 3, 20, 64]))
+        T = 0.0 if trial % 7 == 3 else float(g.uniform(0.05, 2.0))
+        p = float(g.choice([1.0, 0.95, 0.5, 1e-6])) if trial % 3 else float(g.uniform(0.01, 1.0))
+        if k == 0 and T == 0.0:
+            k = 1
+        R = int(g.integers(1, 17))
+        logits = syn.logits(g, R, V, scale=float(g.choice([0.5, 3.0, 20.0])))
+        pos = g.integers(0, 1 << 40, R).astype(np.int64)
+        seed = int(g.integers(0, 1 << 63))
+        _compare(logits, pos, T, k, p, seed)
