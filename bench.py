@@ -464,7 +464,7 @@ def run_legs(args, ev, syn, to_dev, stream):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+        print(f"bench.py: runs on one GPU only (asked for --gpus {args.gpus}); "
               "the path's multi-GPU sharding is a design, not a measured configuration.",
               file=sys.stderr)
         sys.exit(2)

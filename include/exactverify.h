@@ -44,7 +44,7 @@ extern "C" {
 
 #define EV_OK 0
 #define EV_EINVAL (-1)      /* bad pointer, size, alignment or parameter value */
-#define EV_EUNSUPPORTED (-2)/* a valid value this build does not handle     */
+#define EV_EUNSUPPORTED (-2)/* a valid value the library does not handle     */
 #define EV_EHIP (-3)        /* the HIP runtime reported an error             */
 #define EV_EWORKSPACE (-4)  /* workspace pointer NULL or smaller than needed */
 
