@@ -391,6 +391,11 @@ __device__ __forceinline__ void w4_block(const W4Args& a, long blk, uint8_t (*xl
         }
     };
 
+    // kRopeMode: the step's position, read first; each row's (cos, sin) is
+    // requested after the prologue, so that neither waits at the epilogue
+    long long rp0 = 0;
+    if constexpr (MODE == kRopeMode) rp0 = a.rope.positions[kPos0Slot];
+
     // Prologue: superchunk 0 of the split loaded, the first kPD chunks of
     // weights in flight behind it, the superchunk into LDS slab 0, superchunk 1
     // in registers.
@@ -405,6 +410,16 @@ __device__ __forceinline__ void w4_block(const W4Args& a, long blk, uint8_t (*xl
     xstore(0);  // waits for the activations only: they were loaded before the ring
     xload(sc0 + 1);
     __syncthreads();
+    float2 rcs[4];  // kRopeMode, the first half: (cos, sin) of rows 4j + i at pair index d
+    if constexpr (MODE == kRopeMode) {
+        const int hd = cgb, d = 16 * wv + ln;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 4 * j + i;
+            rcs[i] = half == 0 && r < rows && hd < a.rope.NH + a.rope.NKV ? a.rope.rot[(size_t)(rp0 + r) * 64 + d]
+                                                                            : float2{0.f, 0.f};
+        }
+    }
 
     // Main loop over superchunks: kSC chunks of compute on slab `buf`, each
     // refilling its ring slot; then the next superchunk's activations go to
@@ -445,17 +460,18 @@ __device__ __forceinline__ void w4_block(const W4Args& a, long blk, uint8_t (*xl
 #pragma unroll
             for (int t = 0; t < kNT; ++t) y[t] += ex[(wv * kNT + t) * 64 + lane];
             const int hd = cgb, d = 16 * wv + ln;  // head, and d < 64 of the pair (d, d + 64)
-            const long long pos0 = a.rope.positions[kPos0Slot];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = 4 * j + i;
                 if (r >= rows) continue;
-                const long long P = pos0 + r;
+                const long long P = rp0 + r;
                 const float va = y[0][i], vb = y[1][i];
                 if (hd < a.rope.NH + a.rope.NKV) {
-                    const float2 cs = a.rope.rot[(size_t)P * 64 + d];
-                    const float a2 = va * cs.x - vb * cs.y;
-                    const float b2 = vb * cs.x + va * cs.y;
+                    // one fused step each, written out so that the compiler
+                    // has no contraction to choose
+                    const float2 cs = rcs[i];
+                    const float a2 = fmaf(va, cs.x, -(vb * cs.y));
+                    const float b2 = fmaf(vb, cs.x, va * cs.y);
                     if (hd < a.rope.NH) {
                         float* q = a.rope.q + ((size_t)r * a.rope.NH + hd) * 128;
                         q[d] = a2;
