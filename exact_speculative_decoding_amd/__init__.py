@@ -63,6 +63,8 @@ _SIGS = {
     "w4_pack": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _vp, _sz, _vp]),
     "verify_linear_w4_workspace": (_sz, [_i32, _i32, _i32]),
     "verify_linear_w4": (_i32, [_vp, _i32, _i32, _vp, _i32, _i32, _vp, _vp, _sz, _vp]),
+    "verify_linear_w4_standard_workspace": (_sz, [_i32, _i32, _i32]),
+    "verify_linear_w4_standard": (_i32, [_vp, _i32, _i32, _vp, _vp, _vp, _i32, _i32, _vp, _vp, _sz, _vp]),
     "nvfp4_packed_bytes": (_sz, [_i32, _i32]),
     "nvfp4_pack": (_i32, [_vp, _vp, _i32, _i32, _vp, _sz, _vp]),
     "verify_linear_nvfp4_workspace": (_sz, [_i32, _i32]),
@@ -193,6 +195,26 @@ def verify_linear_w4(x, w, y=None, ws=None, stream=None):
         _dev(x, "x", _B16), R, K, _dev(w.blob, "w", _U8), w.N, w.G,
         _dev(y, "y", (torch.float32,)),
         None if ws is None else C.c_void_p(ws.data_ptr()), nb, _stream(stream)))
+    return y
+
+
+def verify_linear_w4_standard_workspace(K, N, G):
+    return int(lib().verify_linear_w4_standard_workspace(K, N, G))
+
+
+def verify_linear_w4_standard(x, q, s, b, G, y=None, ws=None, stream=None):
+    """y[R][N] fp32 = W4 linear of x[R][K] (bf16) with the standard-layout
+    matrix q [N][K/2] u8, s/b [N][K/G] fp16 (packed inside the call)."""
+    R, K = x.shape
+    N, Kh = q.shape
+    if 2 * Kh != K:
+        raise ValueError(f"x has K={K}, the matrix K={2 * Kh}")
+    if y is None:
+        y = torch.empty((R, N), dtype=torch.float32, device=x.device)
+    ws, nb = _workspace(verify_linear_w4_standard_workspace(K, N, G), x.device, ws)
+    _check(lib().verify_linear_w4_standard(
+        _dev(x, "x", _B16), R, K, _dev(q, "q", _U8), _dev(s, "s", _F16), _dev(b, "b", _F16), N, G,
+        _dev(y, "y", (torch.float32,)), None if ws is None else C.c_void_p(ws.data_ptr()), nb, _stream(stream)))
     return y
 
 

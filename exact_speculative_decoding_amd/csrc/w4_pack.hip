@@ -1,8 +1,7 @@
 // Exact repacking of W4 weights (once, at load) into the layout of
 // w4_layout.h.  Pure data movement: every output value is a copy of an input
 // value or a padding zero.
-#include "ev_internal.h"
-#include "w4_layout.h"
+#include "w4_kernel.h"  // the layout, and the argument checks of the entry points
 
 namespace ev {
 
@@ -165,3 +164,32 @@ extern "C" int32_t nvfp4_pack(const uint8_t* q, const uint8_t* s, int32_t N, int
     return check_hip(hipGetLastError(), "nvfp4_pack launch");
 }
 
+// ---- the linear on standard-layout weights ---------------------------------
+// The matrix is packed into the front of the workspace (w4_pack, an exact
+// byte permutation), then the packed launches run on the rest: the same
+// arithmetic as verify_linear_w4 on a matrix packed once at load, at the
+// cost of streaming the weights twice per call.
+static size_t std_pack_bytes(int32_t K, int32_t N, int32_t G) { return (w4_blob_bytes(N, K, G) + 255) & ~(size_t)255; }
+
+extern "C" size_t verify_linear_w4_standard_workspace(int32_t K, int32_t N, int32_t G) {
+    if (K <= 0 || N <= 0 || (G != 32 && G != 64) || K % G != 0 || K % 32 != 0) return 0;
+    return std_pack_bytes(K, N, G) + verify_linear_w4_workspace(K, N, G);
+}
+
+extern "C" int32_t verify_linear_w4_standard(const uint16_t* x, int32_t R, int32_t K, const uint8_t* q,
+                                             const uint16_t* scale_f16, const uint16_t* bias_f16, int32_t N,
+                                             int32_t G, float* y, void* ws, size_t ws_bytes, void* stream) {
+    clear_error();
+    const char* who = "verify_linear_w4_standard";
+    int32_t rc;
+    // every check of both steps before either launches
+    if ((rc = check_lanes(who, R)) || (rc = check_w4_dims(who, K, N, G))) return rc;
+    if (!x || !q || !scale_f16 || !bias_f16 || !y) return fail(EV_EINVAL, "%s: NULL pointer", who);
+    if (!aligned(x, 16) || !aligned(q, 4) || !aligned(scale_f16, 2) || !aligned(bias_f16, 2) || !aligned(y, 4))
+        return fail(EV_EINVAL, "%s: misaligned pointer (x 16 B, q 4 B, scale/bias 2 B, y 4 B)", who);
+    const size_t pack = std_pack_bytes(K, N, G);
+    if ((rc = check_ws(who, ws, ws_bytes, pack + verify_linear_w4_workspace(K, N, G)))) return rc;
+    unsigned char* wsb = reinterpret_cast<unsigned char*>(ws);
+    if ((rc = w4_pack(q, scale_f16, bias_f16, N, K, G, wsb, pack, stream))) return rc;
+    return verify_linear_w4(x, R, K, wsb, N, G, y, wsb + pack, ws_bytes - pack, stream);
+}

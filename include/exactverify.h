@@ -102,6 +102,19 @@ int32_t verify_linear_w4(const uint16_t* x_bf16, int32_t R, int32_t K, const voi
                          int32_t N, int32_t G, float* y, void* ws, size_t ws_bytes,
                          void* stream);
 
+/* The same linear on standard-layout weights (q [N][K/2], scale and bias     */
+/* [N][K/G] fp16, as w4_pack takes them), for callers that do not keep a      */
+/* packed copy: the call packs the matrix into the front of its workspace     */
+/* (w4_pack) and runs verify_linear_w4 on it, so y is bit-identical to        */
+/* verify_linear_w4 on the packed matrix; the weights are streamed twice.     */
+/*   ws (device) at least verify_linear_w4_standard_workspace(K, N, G) bytes, */
+/*   256-byte aligned; contents are scratch.  Pointers and limits: those of   */
+/*   w4_pack and verify_linear_w4, all checked before anything is launched.   */
+size_t verify_linear_w4_standard_workspace(int32_t K, int32_t N, int32_t G);
+int32_t verify_linear_w4_standard(const uint16_t* x_bf16, int32_t R, int32_t K, const uint8_t* q,
+                                  const uint16_t* scale_f16, const uint16_t* bias_f16, int32_t N,
+                                  int32_t G, float* y, void* ws, size_t ws_bytes, void* stream);
+
 /* ------------------------------------------------------------------------- */
 /* A second 4-bit format: NVFP4-style block scales (the blog's "The honest    */
 /* limits" section: NVFP4 checkpoints).                                       */

@@ -68,6 +68,29 @@ def test_linear_rejects_bad_arguments(kw, code):
     assert ev.lib().ev_last_error()
 
 
+def _lin_std(**kw):
+    a = dict(x=P, R=4, K=256, q=P, s=P, b=P, N=512, G=64, y=P, ws=P, nb=1 << 30)
+    a.update(kw)
+    return ev.lib().verify_linear_w4_standard(a["x"], a["R"], a["K"], a["q"], a["s"], a["b"], a["N"], a["G"],
+                                              a["y"], a["ws"], a["nb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(R=0), ev.EV_EINVAL), (dict(R=17), ev.EV_EINVAL), (dict(K=100), ev.EV_EINVAL),
+    (dict(G=16), ev.EV_EUNSUPPORTED), (dict(q=None), ev.EV_EINVAL), (dict(s=None), ev.EV_EINVAL),
+    (dict(b=None), ev.EV_EINVAL), (dict(y=None), ev.EV_EINVAL), (dict(x=C.c_void_p(0x10002)), ev.EV_EINVAL),
+    (dict(q=C.c_void_p(0x10002)), ev.EV_EINVAL), (dict(s=C.c_void_p(0x10001)), ev.EV_EINVAL),
+    (dict(ws=None), ev.EV_EWORKSPACE), (dict(nb=1024), ev.EV_EWORKSPACE),
+    (dict(ws=C.c_void_p(0x10010)), ev.EV_EINVAL),
+])
+def test_standard_layout_linear_rejects_bad_arguments(kw, code):
+    """Every check of the pack and of the linear comes before either launches
+    (the workspace always holds the packed matrix, so it is never empty)."""
+    assert ev.verify_linear_w4_standard_workspace(256, 512, 64) >= ev.w4_packed_bytes(512, 256, 64)
+    assert _lin_std(**kw) == code
+    assert ev.lib().ev_last_error()
+
+
 @pytest.mark.parametrize("args,code", [
     ((P, P, P, 0, 256, 64), ev.EV_EINVAL), ((P, P, P, 512, 100, 64), ev.EV_EINVAL),
     ((P, P, P, 512, 256, 48), ev.EV_EUNSUPPORTED), ((None, P, P, 512, 256, 64), ev.EV_EINVAL),

@@ -7,7 +7,9 @@
   for every R in 1..16, and two runs give the same bits;
 * the full-size shapes (MLP gate/up 5120->17408, down 17408->5120, LM head
   5120->151936) in the launch configuration the benchmark uses, on sampled
-  output columns the oracle computes one by one.
+  output columns the oracle computes one by one;
+* the standard-layout entry point (packing inside the call) gives the packed
+  entry point's bits.
 """
 import numpy as np
 import pytest
@@ -149,3 +151,15 @@ def test_largest_packed_matrix_sampled_columns(K, N):
     del wp
     torch.cuda.empty_cache()
 
+
+
+@pytest.mark.parametrize("K,N,G", [(256, 512, 64), (384, 200, 32), (5120, 1000, 64), (17408, 64, 64)])
+def test_standard_layout_entry_equals_packed(K, N, G):
+    g = np.random.default_rng(K + N + G)
+    q, sc, bi = syn.w4_matrix(g, N, K, G)
+    x = syn.bf16_bits(g.standard_normal((16, K)).astype(np.float32))
+    wp = packed((q, sc, bi), G)
+    for R in (1, 7, 16):
+        ref = host(ev.verify_linear_w4(dev(x[:R]), wp))
+        got = host(ev.verify_linear_w4_standard(dev(x[:R]), dev(q), dev(sc), dev(bi), G))
+        assert np.array_equal(ref.view(np.int32), got.view(np.int32)), R
