@@ -50,6 +50,8 @@ namespace ev {
 constexpr uint32_t kOOB = 0x80000000u;  // per-lane offset beyond every buffer: reads 0
 constexpr int kLoadNT = 2;  // cache-policy operand of a buffer load: the non-temporal (nt) bit
 constexpr int kSlab = kSC * kXChunkBytes;  // LDS bytes of one superchunk of activations
+constexpr int kParts = 8;       // K-parts launches: waves per workgroup, each a run of K
+constexpr int kPartChunks = 2;  // at most this many chunks per run
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
@@ -774,6 +776,220 @@ __global__ __launch_bounds__(2 * kThreads) void w4_pair_kernel(W4Args a) {
     }
 }
 
+// K-parts launch of the two halved modes for dense matrices with at most
+// kParts * kPartChunks chunks of K: a workgroup of kParts waves owns one
+// column unit (kPairMode: the gate and the up tile of 16 columns; kRopeMode:
+// tiles u and u + 4 of head hd, the rotation pairs (d, d + 64) with
+// d = 16 u + ln) and wave p takes the p-th run of a.cps <= kPartChunks
+// chunks of K.  A wave requests its whole run at once, the activation
+// fragments straight from memory (lane r + 16 xj of step st of chunk c holds
+// x[r][128 c + 32 st + 8 xj .. + 7], the layout the LDS slabs of w4_block
+// hold) and both tiles' weights.  The parts meet in LDS and wave 0 adds them
+// in ascending p, then writes the finished values as w4_block's epilogues
+// do.  Four workgroups per head and one per gate/up tile spread a
+// decoder-sized matrix over four times the CUs of the halved launch; at these
+// sizes a CU's share of the bytes, not the chip's bandwidth, sets the time.
+template <int G, int MODE, bool NT>
+__device__ __forceinline__ void w4_parts_block(const W4Args& a, f32x4 (*ex)[2][64]) {
+    static_assert(MODE == kPairMode || MODE == kRopeMode, "K-parts launches are the halved modes");
+    constexpr int GPC = kKC / G;
+    constexpr int SBW = GPC;
+    constexpr uint32_t CB = 1024 + 64 * GPC;
+    constexpr int PD = kPartChunks;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int part = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int ln = lane & 15, j = lane >> 4;
+    const int rows = a.R;
+    const int unit = blockIdx.x;
+    const int hd = MODE == kRopeMode ? unit >> 2 : 0, u = MODE == kRopeMode ? unit & 3 : 0;
+    const int tile0 = MODE == kRopeMode ? 8 * hd + u : unit;
+    const int tile1 = MODE == kRopeMode ? tile0 + 4 : unit;
+    const int c0 = part * a.cps;
+    const int c1 = min(a.nchunks, c0 + a.cps);
+
+    const uint32_t wbytes = __builtin_amdgcn_readfirstlane(a.wbytes);
+    const rsrc_t rw0 = make_rsrc(uniform_ptr(a.w[0]), wbytes);
+    const rsrc_t rw1 = MODE == kPairMode ? make_rsrc(uniform_ptr(a.w[1]), wbytes) : rw0;
+    const rsrc_t rx = make_rsrc(uniform_ptr(a.x), __builtin_amdgcn_readfirstlane(a.xbytes));
+    const bool tok[2] = {tile0 < a.tiles, tile1 < a.tiles};
+    const uint32_t tbase[2] = {tok[0] ? (uint32_t)tile0 * CB : 0u, tok[1] ? (uint32_t)tile1 * CB : 0u};
+    const uint32_t cstride = (uint32_t)a.tiles * CB;
+    const uint32_t vq = 16u * lane;
+    const uint32_t vsb = 1024u + 4u * GPC * ln;
+    const uint32_t dm = a.dmask;
+    uint32_t doff;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(doff) : "s"(a.doff));
+    const bool xrow_ok = ln < rows;
+    const uint32_t xoff = (uint32_t)(ln * a.K + 8 * j) * 2u;
+
+    // the run: activation fragments and both tiles' weights of PD chunks;
+    // chunks at or past c1 read zeros and add exactly zero
+    u32x4 xa[PD][4];
+    u32x4 qr[PD][2];
+    uint32_t sbr[PD][2][SBW];
+    auto fetch = [&](int c, int slot) {
+        const bool live = c < c1;
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+            const int k = 128 * c + 32 * st;
+            const bool ok = live && xrow_ok && k + 8 * j < a.K;
+            xa[slot][st] = bload128(rx, ok ? xoff + (uint32_t)k * 2u : kOOB, 0u);
+        }
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const bool ok = live && tok[t];
+            const uint32_t so = tbase[t] + (uint32_t)c * cstride;
+            const rsrc_t r = t == 1 ? rw1 : rw0;
+            qr[slot][t] = wload128<NT>(r, ok ? vq : kOOB, so);
+            if (GPC == 2) {
+                const u32x2 v = wload64<NT>(r, ok ? vsb : kOOB, so);
+                sbr[slot][t][0] = v[0];
+                sbr[slot][t][GPC - 1] = v[1];
+            } else {
+                const u32x4 v = wload128<NT>(r, ok ? vsb : kOOB, so);
+#pragma unroll
+                for (int g = 0; g < SBW; ++g) sbr[slot][t][g] = v[g & 3];
+            }
+        }
+    };
+
+    const u32x4 ones = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
+    f32x4 y[2];
+    y[0] = y[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // one chunk, the arithmetic of w4_block's affine chunk: per 32-k step one
+    // MFMA for the group sums of x and one per tile; per group
+    // y += s * acc + (b - 16 s) * xs
+    auto compute = [&](int slot) {
+        f32x4 acc[2], xs = {0.f, 0.f, 0.f, 0.f};
+        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+            const bf16x8 A = __builtin_bit_cast(bf16x8, xa[slot][st]);
+            const bool first = (G == 32) || ((st & 1) == 0);
+            xs = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, __builtin_bit_cast(bf16x8, ones), first ? zero : xs, 0,
+                                                        0, 0);
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const bf16x8 B = __builtin_bit_cast(bf16x8, decode_nibbles(qr[slot][t][st], dm, doff));
+                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, first ? zero : acc[t], 0, 0, 0);
+            }
+            const bool last = (G == 32) || ((st & 1) == 1);
+            if (last) {
+                const int gc = (32 * st) / G;
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    const uint32_t sb = sbr[slot][t][gc];
+                    const float sv = half_lo(sb), bv = half_hi(sb);
+                    const float bp = fmaf(-kDecodeOffset, sv, bv);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        y[t][i] = fmaf(sv, acc[t][i], y[t][i]);
+                        y[t][i] = fmaf(bp, xs[i], y[t][i]);
+                    }
+                }
+            }
+        }
+    };
+
+    // kRopeMode: the step's position first, then the run, then the rows'
+    // (cos, sin), so that the epilogue waits for none of them
+    long long rp0 = 0;
+    if constexpr (MODE == kRopeMode) rp0 = a.rope.positions[kPos0Slot];
+#pragma unroll
+    for (int p = 0; p < PD; ++p) {
+        __builtin_amdgcn_sched_barrier(0);
+        fetch(c0 + p, p);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    float2 rcs[4];
+    if constexpr (MODE == kRopeMode) {
+        const int d = 16 * u + ln;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 4 * j + i;
+            rcs[i] = part == 0 && r < rows && hd < a.rope.NH + a.rope.NKV ? a.rope.rot[(size_t)(rp0 + r) * 64 + d]
+                                                                           : float2{0.f, 0.f};
+        }
+    }
+#pragma unroll
+    for (int p = 0; p < PD; ++p) {
+        __builtin_amdgcn_sched_barrier(0);
+        compute(p);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // parts 1.. through LDS; wave 0 adds them in ascending part order
+    if (part > 0) {
+        ex[part - 1][0][lane] = y[0];
+        ex[part - 1][1][lane] = y[1];
+    }
+    __syncthreads();
+    if (part != 0) return;
+#pragma unroll
+    for (int p = 1; p < kParts; ++p) {
+        y[0] += ex[p - 1][0][lane];
+        y[1] += ex[p - 1][1][lane];
+    }
+    if constexpr (MODE == kRopeMode) {
+        const int d = 16 * u + ln;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 4 * j + i;
+            if (r >= rows) continue;
+            const long long P = rp0 + r;
+            const float va = y[0][i], vb = y[1][i];
+            if (hd < a.rope.NH + a.rope.NKV) {
+                // one fused step each, written out so that the compiler has
+                // no contraction to choose
+                const float2 cs = rcs[i];
+                const float a2 = fmaf(va, cs.x, -(vb * cs.y));
+                const float b2 = fmaf(vb, cs.x, va * cs.y);
+                if (hd < a.rope.NH) {
+                    float* q = a.rope.q + ((size_t)r * a.rope.NH + hd) * 128;
+                    q[d] = a2;
+                    q[d + 64] = b2;
+                } else {
+                    uint16_t* k = a.rope.kc + ((size_t)(hd - a.rope.NH) * a.rope.C + P) * 128;
+                    k[d] = f32_to_f16_sat(a2);
+                    k[d + 64] = f32_to_f16_sat(b2);
+                }
+            } else {
+                const int g = hd - a.rope.NH - a.rope.NKV;
+                uint16_t* v = a.rope.vc + (size_t)g * a.rope.C * 128 + (size_t)(P / 32) * 128 * 32 +
+                              vslot_pos32((int)(P % 32));
+                v[(size_t)d * 32] = f32_to_f16_sat(va);
+                v[(size_t)(d + 64) * 32] = f32_to_f16_sat(vb);
+            }
+        }
+    } else {
+        const int n = unit * 16 + ln;
+        if (tok[0] && n < a.N) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 4 * j + i;
+                if (r < rows) {
+                    const uint16_t hv = silu_mul_bf16(y[0][i], y[1][i]);
+                    a.h[(size_t)r * a.N + n] = hv;
+                    if (a.h_copy) a.h_copy[(size_t)r * a.N + n] = hv;
+                }
+            }
+        }
+    }
+}
+
+template <int G, int MODE, bool NT>
+__global__ __launch_bounds__(64 * kParts) void w4_parts_kernel(W4Args a) {
+    __shared__ f32x4 ex[kParts - 1][2][64];
+    if (a.tstamp && threadIdx.x == 0) a.tstamp[2 * blockIdx.x] = wall_clock64();
+    w4_parts_block<G, MODE, NT>(a, ex);
+    if (a.tstamp) {
+        __syncthreads();
+        if (threadIdx.x == 0) a.tstamp[2 * blockIdx.x + 1] = wall_clock64();
+    }
+}
+
 // y[r][n] = sum over s = 0..S-1, ascending, of part[s][r][n].  One thread per
 // 4 consecutive n of one row; the loads of all splits are issued ahead of the
 // additions, which run in ascending s.
@@ -1142,13 +1358,59 @@ static int32_t launch_w4_halved(W4Args args, const W4Plan& p, int K, int G, hipS
     return check_hip(hipGetLastError(), "w4 halved-mode launch");
 }
 
+// A K-parts launch (dense only): one workgroup of kParts waves per gate/up
+// tile, or four per q|k|v head.
+static int32_t launch_w4_parts(W4Args args, int K, int G, hipStream_t st, bool rope) {
+    args.K = K;
+    args.nmat = rope ? 1 : 2;
+    args.nchunks = w4_chunks(K);
+    args.tiles = w4_tiles(args.N);
+    args.cps = (args.nchunks + kParts - 1) / kParts;
+    args.blocks = rope ? 4l * (args.N / 128) : args.tiles;
+    args.wbytes = (uint32_t)w4_blob_bytes(args.N, K, G);
+    args.xbytes = (uint32_t)((size_t)args.R * K * 2);
+    args.dmask = kDecodeMask;
+    args.doff = kDecodeOr;
+    args.tstamp = nullptr;
+    int32_t rc = timing_slots(args.blocks, w4_algo_bytes(args.nmat, args.R, K, args.N, G), &args.tstamp);
+    if (rc) return rc;
+    const unsigned blocks = (unsigned)args.blocks;
+    const bool nt = stream_hint((double)args.wbytes * args.nmat);
+    const dim3 th(64 * kParts);
+    if (rope) {
+        if (G == 64 && nt)
+            hipLaunchKernelGGL((w4_parts_kernel<64, kRopeMode, true>), dim3(blocks), th, 0, st, args);
+        else if (G == 64)
+            hipLaunchKernelGGL((w4_parts_kernel<64, kRopeMode, false>), dim3(blocks), th, 0, st, args);
+        else if (nt)
+            hipLaunchKernelGGL((w4_parts_kernel<32, kRopeMode, true>), dim3(blocks), th, 0, st, args);
+        else
+            hipLaunchKernelGGL((w4_parts_kernel<32, kRopeMode, false>), dim3(blocks), th, 0, st, args);
+    } else {
+        if (G == 64 && nt)
+            hipLaunchKernelGGL((w4_parts_kernel<64, kPairMode, true>), dim3(blocks), th, 0, st, args);
+        else if (G == 64)
+            hipLaunchKernelGGL((w4_parts_kernel<64, kPairMode, false>), dim3(blocks), th, 0, st, args);
+        else if (nt)
+            hipLaunchKernelGGL((w4_parts_kernel<32, kPairMode, true>), dim3(blocks), th, 0, st, args);
+        else
+            hipLaunchKernelGGL((w4_parts_kernel<32, kPairMode, false>), dim3(blocks), th, 0, st, args);
+    }
+    return check_hip(hipGetLastError(), "w4 K-parts launch");
+}
+
+// Dense launches whose K fits the K-parts runs take them.
+static bool use_parts(int K) { return w4_chunks(K) <= kParts * kPartChunks; }
+
 int32_t launch_w4_pair(W4Args args, const W4Plan& p, int K, int G, hipStream_t st, int ngroups) {
+    if (ngroups == 1 && !args.gexp && use_parts(K)) return launch_w4_parts(args, K, G, st, false);
     return launch_w4_halved(args, p, K, G, st, ngroups, false);
 }
 
 int32_t launch_w4_rope(W4Args args, const W4Plan& p, int K, int G, hipStream_t st) {
     if (args.N % 128 != 0 || args.N / 128 != args.rope.NH + 2 * args.rope.NKV)
         return fail(EV_EINVAL, "w4 rope launch: N=%d is not (NH + 2 NKV) heads of 128", args.N);
+    if (use_parts(K)) return launch_w4_parts(args, K, G, st, true);
     return launch_w4_halved(args, p, K, G, st, 1, true);
 }
 
