@@ -486,6 +486,7 @@ struct StepLayout {
     W4Plan p_qkv, p_o, p_gu, p_down, p_lm;
     SkPlan q_o, q_down, q_lm;  // balanced plans, used where use_sk holds
     bool sk_o, sk_down, sk_lm;
+    bool parts_o, parts_down;  // K-parts launches writing finished rows
     int chunk, nchunk_max;
     bool gu_pair;
     size_t off_x, off_n, off_o, off_q, off_part, off_pg, off_pu, off_h, off_att, off_logits, off_pos, off_acc,
@@ -550,6 +551,11 @@ static StepLayout step_layout(const ev_decoder_config& c, int NQKV, int DQ, int 
     L.q_lm = plan_w4_sk(V, H, 1);
     L.sk_o = use_sk(L.q_o, L.p_o);
     L.sk_down = use_sk(L.q_down, L.p_down);
+    // o and down as K-parts launches (one workgroup per tile, finished rows):
+    // the row kernel after them then reads one row instead of the balanced
+    // launch's segments
+    L.parts_o = parts_fits(DQ);
+    L.parts_down = parts_fits(I);
     L.sk_lm = use_sk(L.q_lm, L.p_lm);
     // chunk: a multiple of 64 slots with at most kMaxChunks chunks in the cache
     L.chunk = 64 * ((C + 64 * kMaxChunks - 1) / (64 * kMaxChunks));
@@ -701,12 +707,16 @@ static int32_t step_body(ev_decoder* m, int R, int32_t* sampled, int32_t* n_comm
 
     // a linear into the partials at `part`: balanced when sk, else split
     auto linear = [&](const void* wmat, const uint16_t* xin, int K, int N, const W4Plan& p, const SkPlan& q,
-                      bool sk) {
+                      bool sk, bool parts) {
         W4Args a{};
         a.w[0] = a.w[1] = reinterpret_cast<const uint8_t*>(wmat);
         a.x = xin;
         a.R = R;
         a.N = N;
+        if (parts) {
+            a.out[0] = a.out[1] = part;
+            return launch_w4_plain_parts(a, K, G, st);
+        }
         if (sk) {
             a.sk_part = part;
             return launch_w4_sk(a, 1, q, K, G, st);
@@ -747,9 +757,9 @@ static int32_t step_body(ev_decoder* m, int R, int32_t* sampled, int32_t* n_comm
         hipLaunchKernelGGL(attn_merge_kernel, dim3(R, NH), dim3(kHD * kMergeGroups), 0, st, att, NH, L.chunk,
                            L.nchunk_max, pos, o);
         if ((rc = check_hip(hipGetLastError(), "attn_merge launch"))) return rc;
-        if ((rc = linear(y.w_o, o, m->DQ, H, L.p_o, L.q_o, L.sk_o))) return rc;
-        hipLaunchKernelGGL(res_norm_kernel, dim3(R), dim3(kRowThreads), 0, st, part, L.p_o.S,
-                           L.sk_o ? sk_geom(L.q_o) : no_sk, H, x, y.mlp_norm, eps, n);
+        if ((rc = linear(y.w_o, o, m->DQ, H, L.p_o, L.q_o, L.sk_o, L.parts_o))) return rc;
+        hipLaunchKernelGGL(res_norm_kernel, dim3(R), dim3(kRowThreads), 0, st, part, L.parts_o ? 1 : L.p_o.S,
+                           L.sk_o && !L.parts_o ? sk_geom(L.q_o) : no_sk, H, x, y.mlp_norm, eps, n);
         if ((rc = check_hip(hipGetLastError(), "res_norm launch"))) return rc;
         {  // h = SiLU(gate) * up: one paired launch, or gate|up + split sum with SiLU * up
             W4Args a{};
@@ -770,14 +780,15 @@ static int32_t step_body(ev_decoder* m, int R, int32_t* sampled, int32_t* n_comm
                     return rc;
             }
         }
-        if ((rc = linear(y.w_down, h, I, H, L.p_down, L.q_down, L.sk_down))) return rc;
+        if ((rc = linear(y.w_down, h, I, H, L.p_down, L.q_down, L.sk_down, L.parts_down))) return rc;
         const float* next = l + 1 < c.layers ? m->layers[l + 1].attn_norm : m->final_norm;
-        hipLaunchKernelGGL(res_norm_kernel, dim3(R), dim3(kRowThreads), 0, st, part, L.p_down.S,
-                           L.sk_down ? sk_geom(L.q_down) : no_sk, H, x, next, eps, n);
+        hipLaunchKernelGGL(res_norm_kernel, dim3(R), dim3(kRowThreads), 0, st, part,
+                           L.parts_down ? 1 : L.p_down.S, L.sk_down && !L.parts_down ? sk_geom(L.q_down) : no_sk, H,
+                           x, next, eps, n);
         if ((rc = check_hip(hipGetLastError(), "res_norm launch"))) return rc;
     }
     if (!head) return EV_OK;  // prefill: the layers only (their cache entries)
-    if ((rc = linear(m->w_lm, n, H, V, L.p_lm, L.q_lm, L.sk_lm))) return rc;
+    if ((rc = linear(m->w_lm, n, H, V, L.p_lm, L.q_lm, L.sk_lm, false))) return rc;
     if (L.sk_lm) {
         if ((rc = launch_sk_reduce(part, L.q_lm, 1, V, R, lg, nullptr, nullptr, st))) return rc;
     } else if ((rc = launch_splitk_reduce(part, L.p_lm.S, V, R, lg, st))) {

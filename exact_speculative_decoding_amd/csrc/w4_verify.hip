@@ -50,8 +50,6 @@ namespace ev {
 constexpr uint32_t kOOB = 0x80000000u;  // per-lane offset beyond every buffer: reads 0
 constexpr int kLoadNT = 2;  // cache-policy operand of a buffer load: the non-temporal (nt) bit
 constexpr int kSlab = kSC * kXChunkBytes;  // LDS bytes of one superchunk of activations
-constexpr int kParts = 8;       // K-parts launches: waves per workgroup, each a run of K
-constexpr int kPartChunks = 2;  // at most this many chunks per run
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
@@ -776,26 +774,28 @@ __global__ __launch_bounds__(2 * kThreads) void w4_pair_kernel(W4Args a) {
     }
 }
 
-// K-parts launch of the two halved modes for dense matrices with at most
-// kParts * kPartChunks chunks of K: a workgroup of kParts waves owns one
-// column unit (kPairMode: the gate and the up tile of 16 columns; kRopeMode:
-// tiles u and u + 4 of head hd, the rotation pairs (d, d + 64) with
-// d = 16 u + ln) and wave p takes the p-th run of a.cps <= kPartChunks
-// chunks of K.  A wave requests its whole run at once, the activation
-// fragments straight from memory (lane r + 16 xj of step st of chunk c holds
-// x[r][128 c + 32 st + 8 xj .. + 7], the layout the LDS slabs of w4_block
-// hold) and both tiles' weights.  The parts meet in LDS and wave 0 adds them
-// in ascending p, then writes the finished values as w4_block's epilogues
-// do.  Four workgroups per head and one per gate/up tile spread a
-// decoder-sized matrix over four times the CUs of the halved launch; at these
-// sizes a CU's share of the bytes, not the chip's bandwidth, sets the time.
-template <int G, int MODE, bool NT>
-__device__ __forceinline__ void w4_parts_block(const W4Args& a, f32x4 (*ex)[2][64]) {
-    static_assert(MODE == kPairMode || MODE == kRopeMode, "K-parts launches are the halved modes");
+// K-parts launch for dense matrices with at most PARTS * PC chunks of K: a
+// workgroup of PARTS waves owns one column unit and wave p takes the p-th run
+// of a.cps <= PC chunks of K.  The unit is
+//   * kPlain: one tile of 16 columns; the workgroup writes the finished fp32
+//     rows (a split partial of S = 1);
+//   * kPairMode: the gate and the up tile of 16 columns; h = bf16(silu(g)*u);
+//   * kRopeMode: tiles u and u + 4 of head hd, the rotation pairs (d, d + 64)
+//     with d = 16 u + ln, rotated and written as w4_block's epilogue does.
+// A wave requests its whole run at once, the activation fragments straight
+// from memory (lane r + 16 xj of step st of chunk c holds x[r][128 c + 32 st
+// + 8 xj .. + 7], the layout the LDS slabs of w4_block hold) and its tiles'
+// weights.  The parts meet in LDS and wave 0 adds them in ascending p, an
+// order fixed by K alone.  One workgroup per tile (four per head) spreads a
+// decoder-sized matrix over many CUs: at these sizes a CU's share of the
+// bytes, not the chip's bandwidth, sets the time.
+template <int G, int MODE, bool NT, int PARTS, int PC>
+__device__ __forceinline__ void w4_parts_block(const W4Args& a, f32x4 (*ex)[MODE == kPlain ? 1 : 2][64]) {
+    constexpr int NTW = MODE == kPlain ? 1 : 2;  // tiles per wave
     constexpr int GPC = kKC / G;
     constexpr int SBW = GPC;
     constexpr uint32_t CB = 1024 + 64 * GPC;
-    constexpr int PD = kPartChunks;
+    constexpr int PD = PC;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -805,7 +805,7 @@ __device__ __forceinline__ void w4_parts_block(const W4Args& a, f32x4 (*ex)[2][6
     const int unit = blockIdx.x;
     const int hd = MODE == kRopeMode ? unit >> 2 : 0, u = MODE == kRopeMode ? unit & 3 : 0;
     const int tile0 = MODE == kRopeMode ? 8 * hd + u : unit;
-    const int tile1 = MODE == kRopeMode ? tile0 + 4 : unit;
+    const int tile1 = MODE == kRopeMode ? tile0 + 4 : unit;  // unused in kPlain
     const int c0 = part * a.cps;
     const int c1 = min(a.nchunks, c0 + a.cps);
 
@@ -827,8 +827,8 @@ __device__ __forceinline__ void w4_parts_block(const W4Args& a, f32x4 (*ex)[2][6
     // the run: activation fragments and both tiles' weights of PD chunks;
     // chunks at or past c1 read zeros and add exactly zero
     u32x4 xa[PD][4];
-    u32x4 qr[PD][2];
-    uint32_t sbr[PD][2][SBW];
+    u32x4 qr[PD][NTW];
+    uint32_t sbr[PD][NTW][SBW];
     auto fetch = [&](int c, int slot) {
         const bool live = c < c1;
 #pragma unroll
@@ -838,7 +838,7 @@ __device__ __forceinline__ void w4_parts_block(const W4Args& a, f32x4 (*ex)[2][6
             xa[slot][st] = bload128(rx, ok ? xoff + (uint32_t)k * 2u : kOOB, 0u);
         }
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
+        for (int t = 0; t < NTW; ++t) {
             const bool ok = live && tok[t];
             const uint32_t so = tbase[t] + (uint32_t)c * cstride;
             const rsrc_t r = t == 1 ? rw1 : rw0;
@@ -856,13 +856,14 @@ __device__ __forceinline__ void w4_parts_block(const W4Args& a, f32x4 (*ex)[2][6
     };
 
     const u32x4 ones = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
-    f32x4 y[2];
-    y[0] = y[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    f32x4 y[NTW];
+#pragma unroll
+    for (int t = 0; t < NTW; ++t) y[t] = f32x4{0.f, 0.f, 0.f, 0.f};
     // one chunk, the arithmetic of w4_block's affine chunk: per 32-k step one
     // MFMA for the group sums of x and one per tile; per group
     // y += s * acc + (b - 16 s) * xs
     auto compute = [&](int slot) {
-        f32x4 acc[2], xs = {0.f, 0.f, 0.f, 0.f};
+        f32x4 acc[NTW], xs = {0.f, 0.f, 0.f, 0.f};
         const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int st = 0; st < 4; ++st) {
@@ -871,7 +872,7 @@ __device__ __forceinline__ void w4_parts_block(const W4Args& a, f32x4 (*ex)[2][6
             xs = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, __builtin_bit_cast(bf16x8, ones), first ? zero : xs, 0,
                                                         0, 0);
 #pragma unroll
-            for (int t = 0; t < 2; ++t) {
+            for (int t = 0; t < NTW; ++t) {
                 const bf16x8 B = __builtin_bit_cast(bf16x8, decode_nibbles(qr[slot][t][st], dm, doff));
                 acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, first ? zero : acc[t], 0, 0, 0);
             }
@@ -879,7 +880,7 @@ __device__ __forceinline__ void w4_parts_block(const W4Args& a, f32x4 (*ex)[2][6
             if (last) {
                 const int gc = (32 * st) / G;
 #pragma unroll
-                for (int t = 0; t < 2; ++t) {
+                for (int t = 0; t < NTW; ++t) {
                     const uint32_t sb = sbr[slot][t][gc];
                     const float sv = half_lo(sb), bv = half_hi(sb);
                     const float bp = fmaf(-kDecodeOffset, sv, bv);
@@ -922,17 +923,26 @@ __device__ __forceinline__ void w4_parts_block(const W4Args& a, f32x4 (*ex)[2][6
 
     // parts 1.. through LDS; wave 0 adds them in ascending part order
     if (part > 0) {
-        ex[part - 1][0][lane] = y[0];
-        ex[part - 1][1][lane] = y[1];
+#pragma unroll
+        for (int t = 0; t < NTW; ++t) ex[part - 1][t][lane] = y[t];
     }
     __syncthreads();
     if (part != 0) return;
 #pragma unroll
-    for (int p = 1; p < kParts; ++p) {
-        y[0] += ex[p - 1][0][lane];
-        y[1] += ex[p - 1][1][lane];
+    for (int p = 1; p < PARTS; ++p) {
+#pragma unroll
+        for (int t = 0; t < NTW; ++t) y[t] += ex[p - 1][t][lane];
     }
-    if constexpr (MODE == kRopeMode) {
+    if constexpr (MODE == kPlain) {
+        const int n = unit * 16 + ln;
+        if (tok[0] && n < a.N) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 4 * j + i;
+                if (r < rows) a.out[0][(size_t)r * a.N + n] = y[0][i];
+            }
+        }
+    } else if constexpr (MODE == kRopeMode) {
         const int d = 16 * u + ln;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -970,7 +980,7 @@ __device__ __forceinline__ void w4_parts_block(const W4Args& a, f32x4 (*ex)[2][6
             for (int i = 0; i < 4; ++i) {
                 const int r = 4 * j + i;
                 if (r < rows) {
-                    const uint16_t hv = silu_mul_bf16(y[0][i], y[1][i]);
+                    const uint16_t hv = silu_mul_bf16(y[0][i], y[NTW - 1][i]);
                     a.h[(size_t)r * a.N + n] = hv;
                     if (a.h_copy) a.h_copy[(size_t)r * a.N + n] = hv;
                 }
@@ -979,11 +989,11 @@ __device__ __forceinline__ void w4_parts_block(const W4Args& a, f32x4 (*ex)[2][6
     }
 }
 
-template <int G, int MODE, bool NT>
-__global__ __launch_bounds__(64 * kParts) void w4_parts_kernel(W4Args a) {
-    __shared__ f32x4 ex[kParts - 1][2][64];
+template <int G, int MODE, bool NT, int PARTS, int PC>
+__global__ __launch_bounds__(64 * PARTS) void w4_parts_kernel(W4Args a) {
+    __shared__ f32x4 ex[PARTS - 1][MODE == kPlain ? 1 : 2][64];
     if (a.tstamp && threadIdx.x == 0) a.tstamp[2 * blockIdx.x] = wall_clock64();
-    w4_parts_block<G, MODE, NT>(a, ex);
+    w4_parts_block<G, MODE, NT, PARTS, PC>(a, ex);
     if (a.tstamp) {
         __syncthreads();
         if (threadIdx.x == 0) a.tstamp[2 * blockIdx.x + 1] = wall_clock64();
@@ -1358,15 +1368,31 @@ static int32_t launch_w4_halved(W4Args args, const W4Plan& p, int K, int G, hipS
     return check_hip(hipGetLastError(), "w4 halved-mode launch");
 }
 
-// A K-parts launch (dense only): one workgroup of kParts waves per gate/up
-// tile, or four per q|k|v head.
-static int32_t launch_w4_parts(W4Args args, int K, int G, hipStream_t st, bool rope) {
+// K-parts shapes: 8 waves of up to 2 chunks (K <= 2048), or 16 waves of up
+// to 3 (K <= 6144, plain launches).
+template <int MODE, int PARTS, int PC>
+static void launch_parts_g(const W4Args& args, int G, bool nt, unsigned blocks, hipStream_t st) {
+    const dim3 th(64 * PARTS);
+    if (G == 64 && nt)
+        hipLaunchKernelGGL((w4_parts_kernel<64, MODE, true, PARTS, PC>), dim3(blocks), th, 0, st, args);
+    else if (G == 64)
+        hipLaunchKernelGGL((w4_parts_kernel<64, MODE, false, PARTS, PC>), dim3(blocks), th, 0, st, args);
+    else if (nt)
+        hipLaunchKernelGGL((w4_parts_kernel<32, MODE, true, PARTS, PC>), dim3(blocks), th, 0, st, args);
+    else
+        hipLaunchKernelGGL((w4_parts_kernel<32, MODE, false, PARTS, PC>), dim3(blocks), th, 0, st, args);
+}
+
+// A K-parts launch (dense only): one workgroup per tile, per gate/up tile,
+// or four per q|k|v head.
+static int32_t launch_w4_parts(W4Args args, int K, int G, hipStream_t st, int mode) {
     args.K = K;
-    args.nmat = rope ? 1 : 2;
+    args.nmat = mode == kPairMode ? 2 : 1;
     args.nchunks = w4_chunks(K);
     args.tiles = w4_tiles(args.N);
-    args.cps = (args.nchunks + kParts - 1) / kParts;
-    args.blocks = rope ? 4l * (args.N / 128) : args.tiles;
+    const bool wide = args.nchunks > 16;
+    args.cps = wide ? (args.nchunks + 15) / 16 : (args.nchunks + 7) / 8;
+    args.blocks = mode == kRopeMode ? 4l * (args.N / 128) : args.tiles;
     args.wbytes = (uint32_t)w4_blob_bytes(args.N, K, G);
     args.xbytes = (uint32_t)((size_t)args.R * K * 2);
     args.dmask = kDecodeMask;
@@ -1376,41 +1402,36 @@ static int32_t launch_w4_parts(W4Args args, int K, int G, hipStream_t st, bool r
     if (rc) return rc;
     const unsigned blocks = (unsigned)args.blocks;
     const bool nt = stream_hint((double)args.wbytes * args.nmat);
-    const dim3 th(64 * kParts);
-    if (rope) {
-        if (G == 64 && nt)
-            hipLaunchKernelGGL((w4_parts_kernel<64, kRopeMode, true>), dim3(blocks), th, 0, st, args);
-        else if (G == 64)
-            hipLaunchKernelGGL((w4_parts_kernel<64, kRopeMode, false>), dim3(blocks), th, 0, st, args);
-        else if (nt)
-            hipLaunchKernelGGL((w4_parts_kernel<32, kRopeMode, true>), dim3(blocks), th, 0, st, args);
-        else
-            hipLaunchKernelGGL((w4_parts_kernel<32, kRopeMode, false>), dim3(blocks), th, 0, st, args);
-    } else {
-        if (G == 64 && nt)
-            hipLaunchKernelGGL((w4_parts_kernel<64, kPairMode, true>), dim3(blocks), th, 0, st, args);
-        else if (G == 64)
-            hipLaunchKernelGGL((w4_parts_kernel<64, kPairMode, false>), dim3(blocks), th, 0, st, args);
-        else if (nt)
-            hipLaunchKernelGGL((w4_parts_kernel<32, kPairMode, true>), dim3(blocks), th, 0, st, args);
-        else
-            hipLaunchKernelGGL((w4_parts_kernel<32, kPairMode, false>), dim3(blocks), th, 0, st, args);
-    }
+    if (mode == kRopeMode)
+        launch_parts_g<kRopeMode, 8, 2>(args, G, nt, blocks, st);
+    else if (mode == kPairMode)
+        launch_parts_g<kPairMode, 8, 2>(args, G, nt, blocks, st);
+    else if (wide)
+        launch_parts_g<kPlain, 16, 3>(args, G, nt, blocks, st);
+    else
+        launch_parts_g<kPlain, 8, 2>(args, G, nt, blocks, st);
     return check_hip(hipGetLastError(), "w4 K-parts launch");
 }
 
-// Dense launches whose K fits the K-parts runs take them.
-static bool use_parts(int K) { return w4_chunks(K) <= kParts * kPartChunks; }
+// Dense halved-mode launches whose K fits 8 runs of 2 chunks take K-parts.
+static bool use_parts(int K) { return w4_chunks(K) <= 16; }
+
+bool parts_fits(int K) { return w4_chunks(K) <= 48; }
+
+int32_t launch_w4_plain_parts(W4Args args, int K, int G, hipStream_t st) {
+    if (!parts_fits(K)) return fail(EV_EINVAL, "w4 K-parts launch: K=%d has more than 48 chunks", K);
+    return launch_w4_parts(args, K, G, st, kPlain);
+}
 
 int32_t launch_w4_pair(W4Args args, const W4Plan& p, int K, int G, hipStream_t st, int ngroups) {
-    if (ngroups == 1 && !args.gexp && use_parts(K)) return launch_w4_parts(args, K, G, st, false);
+    if (ngroups == 1 && !args.gexp && use_parts(K)) return launch_w4_parts(args, K, G, st, kPairMode);
     return launch_w4_halved(args, p, K, G, st, ngroups, false);
 }
 
 int32_t launch_w4_rope(W4Args args, const W4Plan& p, int K, int G, hipStream_t st) {
     if (args.N % 128 != 0 || args.N / 128 != args.rope.NH + 2 * args.rope.NKV)
         return fail(EV_EINVAL, "w4 rope launch: N=%d is not (NH + 2 NKV) heads of 128", args.N);
-    if (use_parts(K)) return launch_w4_parts(args, K, G, st, true);
+    if (use_parts(K)) return launch_w4_parts(args, K, G, st, kRopeMode);
     return launch_w4_halved(args, p, K, G, st, 1, true);
 }
 
