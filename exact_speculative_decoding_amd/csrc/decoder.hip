@@ -486,7 +486,7 @@ struct StepLayout {
     W4Plan p_qkv, p_o, p_gu, p_down, p_lm;
     SkPlan q_o, q_down, q_lm;  // balanced plans, used where use_sk holds
     bool sk_o, sk_down, sk_lm;
-    bool parts_o, parts_down;  // K-parts launches writing finished rows
+    bool parts_o, parts_down;  // K-parts launches writing kSplitsO / kSplitsDown split rows
     int chunk, nchunk_max;
     bool gu_pair;
     size_t off_x, off_n, off_o, off_q, off_part, off_pg, off_pu, off_h, off_att, off_logits, off_pos, off_acc,
@@ -535,6 +535,11 @@ struct ev_decoder {
     }
 };
 
+// o and down as K-parts launches in these many K-splits (more workgroups,
+// each reading less of the activations, for more partial rows per column in
+// the row kernel after them).
+constexpr int kSplitsO = 1, kSplitsDown = 2;
+
 static StepLayout step_layout(const ev_decoder_config& c, int NQKV, int DQ, int C) {
     StepLayout L;
     const int H = c.hidden, I = c.intermediate, V = c.vocab;
@@ -554,8 +559,8 @@ static StepLayout step_layout(const ev_decoder_config& c, int NQKV, int DQ, int 
     // o and down as K-parts launches (one workgroup per tile, finished rows):
     // the row kernel after them then reads one row instead of the balanced
     // launch's segments
-    L.parts_o = parts_fits(DQ);
-    L.parts_down = parts_fits(I);
+    L.parts_o = parts_fits(DQ, kSplitsO);
+    L.parts_down = parts_fits(I, kSplitsDown);
     L.sk_lm = use_sk(L.q_lm, L.p_lm);
     // chunk: a multiple of 64 slots with at most kMaxChunks chunks in the cache
     L.chunk = 64 * ((C + 64 * kMaxChunks - 1) / (64 * kMaxChunks));
@@ -564,7 +569,8 @@ static StepLayout step_layout(const ev_decoder_config& c, int NQKV, int DQ, int 
     auto part_floats = [](bool sk, const SkPlan& q, const W4Plan& p, int N) {
         return sk ? sk_part_bytes(q) / sizeof(float) : (size_t)16 * p.S * N;
     };
-    size_t part = part_floats(L.sk_o, L.q_o, L.p_o, H);
+    size_t part = (size_t)16 * std::max(kSplitsO, kSplitsDown) * H;  // K-parts o and down
+    part = std::max(part, part_floats(L.sk_o, L.q_o, L.p_o, H));
     part = std::max(part, part_floats(L.sk_down, L.q_down, L.p_down, H));
     part = std::max(part, part_floats(L.sk_lm, L.q_lm, L.p_lm, V));
     size_t off = 0;
@@ -707,7 +713,7 @@ static int32_t step_body(ev_decoder* m, int R, int32_t* sampled, int32_t* n_comm
 
     // a linear into the partials at `part`: balanced when sk, else split
     auto linear = [&](const void* wmat, const uint16_t* xin, int K, int N, const W4Plan& p, const SkPlan& q,
-                      bool sk, bool parts) {
+                      bool sk, bool parts, int splits = 1) {
         W4Args a{};
         a.w[0] = a.w[1] = reinterpret_cast<const uint8_t*>(wmat);
         a.x = xin;
@@ -715,7 +721,7 @@ static int32_t step_body(ev_decoder* m, int R, int32_t* sampled, int32_t* n_comm
         a.N = N;
         if (parts) {
             a.out[0] = a.out[1] = part;
-            return launch_w4_plain_parts(a, K, G, st);
+            return launch_w4_plain_parts(a, K, G, st, splits);
         }
         if (sk) {
             a.sk_part = part;
@@ -757,8 +763,8 @@ static int32_t step_body(ev_decoder* m, int R, int32_t* sampled, int32_t* n_comm
         hipLaunchKernelGGL(attn_merge_kernel, dim3(R, NH), dim3(kHD * kMergeGroups), 0, st, att, NH, L.chunk,
                            L.nchunk_max, pos, o);
         if ((rc = check_hip(hipGetLastError(), "attn_merge launch"))) return rc;
-        if ((rc = linear(y.w_o, o, m->DQ, H, L.p_o, L.q_o, L.sk_o, L.parts_o))) return rc;
-        hipLaunchKernelGGL(res_norm_kernel, dim3(R), dim3(kRowThreads), 0, st, part, L.parts_o ? 1 : L.p_o.S,
+        if ((rc = linear(y.w_o, o, m->DQ, H, L.p_o, L.q_o, L.sk_o, L.parts_o, kSplitsO))) return rc;
+        hipLaunchKernelGGL(res_norm_kernel, dim3(R), dim3(kRowThreads), 0, st, part, L.parts_o ? kSplitsO : L.p_o.S,
                            L.sk_o && !L.parts_o ? sk_geom(L.q_o) : no_sk, H, x, y.mlp_norm, eps, n);
         if ((rc = check_hip(hipGetLastError(), "res_norm launch"))) return rc;
         {  // h = SiLU(gate) * up: one paired launch, or gate|up + split sum with SiLU * up
@@ -780,10 +786,10 @@ static int32_t step_body(ev_decoder* m, int R, int32_t* sampled, int32_t* n_comm
                     return rc;
             }
         }
-        if ((rc = linear(y.w_down, h, I, H, L.p_down, L.q_down, L.sk_down, L.parts_down))) return rc;
+        if ((rc = linear(y.w_down, h, I, H, L.p_down, L.q_down, L.sk_down, L.parts_down, kSplitsDown))) return rc;
         const float* next = l + 1 < c.layers ? m->layers[l + 1].attn_norm : m->final_norm;
         hipLaunchKernelGGL(res_norm_kernel, dim3(R), dim3(kRowThreads), 0, st, part,
-                           L.parts_down ? 1 : L.p_down.S, L.sk_down && !L.parts_down ? sk_geom(L.q_down) : no_sk, H,
+                           L.parts_down ? kSplitsDown : L.p_down.S, L.sk_down && !L.parts_down ? sk_geom(L.q_down) : no_sk, H,
                            x, next, eps, n);
         if ((rc = check_hip(hipGetLastError(), "res_norm launch"))) return rc;
     }

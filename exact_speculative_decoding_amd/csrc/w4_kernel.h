@@ -203,11 +203,13 @@ int32_t launch_w4_pair(W4Args args, const W4Plan& p, int K, int G, hipStream_t s
 // set; plan from plan_w4_pair(N, K)): one workgroup per head.
 int32_t launch_w4_rope(W4Args args, const W4Plan& p, int K, int G, hipStream_t st);
 
-// K-parts plain launch (dense, one matrix): y = x W^T as finished fp32 rows
-// [R][N] at args.out[0], one workgroup per 16-column tile whose waves each
-// take a run of K (K of at most 48 chunks: parts_fits).
-bool parts_fits(int K);
-int32_t launch_w4_plain_parts(W4Args args, int K, int G, hipStream_t st);
+// K-parts plain launch (dense, one matrix): y = x W^T in S K-splits (1..4)
+// as fp32 rows [S][16][N] at args.out[0] (split stride 16 N), added in
+// ascending split order by the consumer; one workgroup per 16-column tile
+// and split, whose waves each take a run of K (at most 48 chunks per split:
+// parts_fits).
+bool parts_fits(int K, int S);
+int32_t launch_w4_plain_parts(W4Args args, int K, int G, hipStream_t st, int S);
 
 // A dense gate/up pair (I x H each) runs paired when its tiles alone give the
 // target wave count; otherwise as a split launch of both matrices followed by

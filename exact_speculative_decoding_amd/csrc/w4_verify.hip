@@ -777,8 +777,9 @@ __global__ __launch_bounds__(2 * kThreads) void w4_pair_kernel(W4Args a) {
 // K-parts launch for dense matrices with at most PARTS * PC chunks of K: a
 // workgroup of PARTS waves owns one column unit and wave p takes the p-th run
 // of a.cps <= PC chunks of K.  The unit is
-//   * kPlain: one tile of 16 columns; the workgroup writes the finished fp32
-//     rows (a split partial of S = 1);
+//   * kPlain: one tile of 16 columns of one of a.S K-splits (workgroup
+//     split * tiles + tile); the workgroup writes the split's fp32 rows at
+//     out + split * split_stride, to be added in ascending split order;
 //   * kPairMode: the gate and the up tile of 16 columns; h = bf16(silu(g)*u);
 //   * kRopeMode: tiles u and u + 4 of head hd, the rotation pairs (d, d + 64)
 //     with d = 16 u + ln, rotated and written as w4_block's epilogue does.
@@ -802,11 +803,12 @@ __device__ __forceinline__ void w4_parts_block(const W4Args& a, f32x4 (*ex)[MODE
     const int part = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int ln = lane & 15, j = lane >> 4;
     const int rows = a.R;
-    const int unit = blockIdx.x;
+    const int split = MODE == kPlain ? blockIdx.x / a.tiles : 0;
+    const int unit = blockIdx.x - split * (MODE == kPlain ? a.tiles : 0);
     const int hd = MODE == kRopeMode ? unit >> 2 : 0, u = MODE == kRopeMode ? unit & 3 : 0;
     const int tile0 = MODE == kRopeMode ? 8 * hd + u : unit;
     const int tile1 = MODE == kRopeMode ? tile0 + 4 : unit;  // unused in kPlain
-    const int c0 = part * a.cps;
+    const int c0 = (split * PARTS + part) * a.cps;
     const int c1 = min(a.nchunks, c0 + a.cps);
 
     const uint32_t wbytes = __builtin_amdgcn_readfirstlane(a.wbytes);
@@ -939,7 +941,7 @@ __device__ __forceinline__ void w4_parts_block(const W4Args& a, f32x4 (*ex)[MODE
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = 4 * j + i;
-                if (r < rows) a.out[0][(size_t)r * a.N + n] = y[0][i];
+                if (r < rows) a.out[0][(size_t)split * a.split_stride + (size_t)r * a.N + n] = y[0][i];
             }
         }
     } else if constexpr (MODE == kRopeMode) {
@@ -1383,16 +1385,21 @@ static void launch_parts_g(const W4Args& args, int G, bool nt, unsigned blocks, 
         hipLaunchKernelGGL((w4_parts_kernel<32, MODE, false, PARTS, PC>), dim3(blocks), th, 0, st, args);
 }
 
-// A K-parts launch (dense only): one workgroup per tile, per gate/up tile,
-// or four per q|k|v head.
-static int32_t launch_w4_parts(W4Args args, int K, int G, hipStream_t st, int mode) {
+// A K-parts launch (dense only): one workgroup per tile and K-split (plain),
+// per gate/up tile, or four per q|k|v head.  Chunks per workgroup up to 16:
+// 8 waves of 2; up to 24: 8 of 3; up to 48: 16 of 3.
+static int32_t launch_w4_parts(W4Args args, int K, int G, hipStream_t st, int mode, int S = 1) {
     args.K = K;
     args.nmat = mode == kPairMode ? 2 : 1;
     args.nchunks = w4_chunks(K);
     args.tiles = w4_tiles(args.N);
-    const bool wide = args.nchunks > 16;
-    args.cps = wide ? (args.nchunks + 15) / 16 : (args.nchunks + 7) / 8;
-    args.blocks = mode == kRopeMode ? 4l * (args.N / 128) : args.tiles;
+    args.S = S;
+    args.split_stride = (long)16 * args.N;
+    const int cpw = (args.nchunks + S - 1) / S;  // chunks per workgroup
+    const int shape = cpw <= 16 ? 0 : cpw <= 24 ? 1 : 2;
+    const int waves = shape == 2 ? 16 : 8;
+    args.cps = (args.nchunks + S * waves - 1) / (S * waves);
+    args.blocks = mode == kRopeMode ? 4l * (args.N / 128) : (long)S * args.tiles;
     args.wbytes = (uint32_t)w4_blob_bytes(args.N, K, G);
     args.xbytes = (uint32_t)((size_t)args.R * K * 2);
     args.dmask = kDecodeMask;
@@ -1406,8 +1413,10 @@ static int32_t launch_w4_parts(W4Args args, int K, int G, hipStream_t st, int mo
         launch_parts_g<kRopeMode, 8, 2>(args, G, nt, blocks, st);
     else if (mode == kPairMode)
         launch_parts_g<kPairMode, 8, 2>(args, G, nt, blocks, st);
-    else if (wide)
+    else if (shape == 2)
         launch_parts_g<kPlain, 16, 3>(args, G, nt, blocks, st);
+    else if (shape == 1)
+        launch_parts_g<kPlain, 8, 3>(args, G, nt, blocks, st);
     else
         launch_parts_g<kPlain, 8, 2>(args, G, nt, blocks, st);
     return check_hip(hipGetLastError(), "w4 K-parts launch");
@@ -1416,11 +1425,11 @@ static int32_t launch_w4_parts(W4Args args, int K, int G, hipStream_t st, int mo
 // Dense halved-mode launches whose K fits 8 runs of 2 chunks take K-parts.
 static bool use_parts(int K) { return w4_chunks(K) <= 16; }
 
-bool parts_fits(int K) { return w4_chunks(K) <= 48; }
+bool parts_fits(int K, int S) { return S >= 1 && S <= 4 && (w4_chunks(K) + S - 1) / S <= 48; }
 
-int32_t launch_w4_plain_parts(W4Args args, int K, int G, hipStream_t st) {
-    if (!parts_fits(K)) return fail(EV_EINVAL, "w4 K-parts launch: K=%d has more than 48 chunks", K);
-    return launch_w4_parts(args, K, G, st, kPlain);
+int32_t launch_w4_plain_parts(W4Args args, int K, int G, hipStream_t st, int S) {
+    if (!parts_fits(K, S)) return fail(EV_EINVAL, "w4 K-parts launch: K=%d in %d splits (at most 48 chunks each)", K, S);
+    return launch_w4_parts(args, K, G, st, kPlain, S);
 }
 
 int32_t launch_w4_pair(W4Args args, const W4Plan& p, int K, int G, hipStream_t st, int ngroups) {
