@@ -178,11 +178,15 @@ __global__ __launch_bounds__(kSThreads) void topk_chunk_kernel(const float* __re
     const int r = blockIdx.y, chunk = blockIdx.x, tid = threadIdx.x;
     const int base = chunk * kChunk;
     const float* row = logits + (size_t)r * V;
+    // all sixteen loads issued before the first use: the index is clamped
+    // and the key masked, rather than the load made conditional (a
+    // conditional load waits for each one in turn)
     unsigned long long keys[kPer];
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
         const int idx = base + i * kSThreads + tid;
-        keys[i] = idx < V ? order_key(row[idx], idx) : 0ull;
+        const float v = row[idx < V ? idx : V - 1];
+        keys[i] = order_key(v, idx) & (0ull - (unsigned long long)(idx < V));
     }
     sort16_desc(keys);
     if (tid < kk) sel[tid] = 0ull;  // places past the chunk's real keys stay 0
@@ -500,12 +504,12 @@ __global__ __launch_bounds__(kSThreads) void tp_max_kernel(TpArgs a) {
     const int r = blockIdx.y, chunk = blockIdx.x, tid = threadIdx.x;
     const float* row = a.logits + (size_t)r * a.V;
     unsigned long long k = 0ull;
-    for (int i = 0; i < kPer; ++i) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {  // clamped index: the loads are all in flight at once
         const int idx = chunk * kChunk + i * kSThreads + tid;
-        if (idx < a.V) {
-            const unsigned long long o = order_key(row[idx], idx);
-            k = o > k ? o : k;
-        }
+        const float v = row[idx < a.V ? idx : a.V - 1];
+        const unsigned long long o = order_key(v, idx) & (0ull - (unsigned long long)(idx < a.V));
+        k = o > k ? o : k;
     }
     k = wave_max_u64(k);
     if ((tid & 63) == 0) red[tid >> 6] = k;
