@@ -45,7 +45,8 @@ __device__ __forceinline__ double keyed_gumbel(unsigned long long seed, long lon
     return -log(-log(u));
 }
 
-// Sorts 16 keys descending in registers (a fixed bitonic network).
+// Sorts 16 keys descending in registers (a fixed bitonic network); the
+// selection rounds need each thread's keys in order.
 __device__ __forceinline__ void sort16_desc(unsigned long long (&k)[kPer]) {
     static_assert(kPer == 16, "network for 16 keys");
 #pragma unroll
@@ -188,15 +189,17 @@ __global__ __launch_bounds__(kSThreads) void topk_chunk_kernel(const float* __re
         const float v = row[idx < V ? idx : V - 1];
         keys[i] = order_key(v, idx) & (0ull - (unsigned long long)(idx < V));
     }
-    sort16_desc(keys);
     if (tid < kk) sel[tid] = 0ull;  // places past the chunk's real keys stay 0
     const int wave = tid >> 6, lane = tid & 63;
 
     if (kk > kRoundsMax) {
         // the lower bound t: the kk-th largest maximum of groups of gs adjacent
-        // threads
+        // threads (no sort here: only the thread's maximum and its keys >= t,
+        // in any order, are needed)
         const int gs = kk <= 32 ? 4 : 2;  // at least 2 kk groups
         unsigned long long gm = keys[0];
+#pragma unroll
+        for (int i = 1; i < kPer; ++i) gm = keys[i] > gm ? keys[i] : gm;
         for (int off = 1; off < gs; off <<= 1) {
             const unsigned long long o = __shfl_xor(gm, off, 64);
             gm = o > gm ? o : gm;
@@ -207,7 +210,7 @@ __global__ __launch_bounds__(kSThreads) void topk_chunk_kernel(const float* __re
         kth_of_sample(smax, kSThreads / gs, kk, &s_t, kSThreads);
         __syncthreads();
         const unsigned long long t = s_t;
-        // the thread's keys >= t (a prefix of its sorted 16; key 0 pads past V)
+        // the thread's keys >= t (key 0 pads past V)
         int c = 0;
 #pragma unroll
         for (int i = 0; i < kPer; ++i) c += (keys[i] >= t && keys[i] != 0ull) ? 1 : 0;
@@ -221,10 +224,10 @@ __global__ __launch_bounds__(kSThreads) void topk_chunk_kernel(const float* __re
             n += wsum[v];
         }
         if (n <= kRankCap) {
-            const int o = off0 + incl - c;
+            int o = off0 + incl - c;
 #pragma unroll
             for (int i = 0; i < kPer; ++i)
-                if (i < c) cand[o + i] = keys[i];
+                if (keys[i] >= t && keys[i] != 0ull) cand[o++] = keys[i];
             __syncthreads();
             place_by_rank(cand, n, kk, sel, kSThreads);
             __syncthreads();
@@ -234,9 +237,10 @@ __global__ __launch_bounds__(kSThreads) void topk_chunk_kernel(const float* __re
         }
     }
 
-    // selection rounds: the thread's keys 1..15 in LDS (its own column); its
-    // current key and the one after it (read ahead, so that a win does not
-    // wait for LDS); nxt is key at of the sorted 16
+    // selection rounds: the thread's keys sorted, 1..15 in LDS (its own
+    // column); its current key and the one after it (read ahead, so that a
+    // win does not wait for LDS); nxt is key at of the sorted 16
+    sort16_desc(keys);
 #pragma unroll
     for (int i = 1; i < kPer; ++i) rest[i - 1][tid] = keys[i];
     unsigned long long head = keys[0], nxt = keys[1];

@@ -5,8 +5,9 @@
   maximum over the lanes' heads, then each candidate's place is its index in
   its own list plus the number of larger keys in the other three lists.
 * Bound and rank (the top-k kernel for kk > 2): t = the kk-th largest maximum
-  of groups of 4 adjacent threads (2 when kk > 32); the keys >= t are placed
-  by the number of larger ones, unless more than 256 reach t.
+  of groups of 4 adjacent threads (2 when kk > 32); the keys >= t, in any
+  order, are placed by the number of larger ones, unless more than 256 reach
+  t.
 * The merge kernel's bound: the kk-th largest of the first ceil(kk / nchunk)
   keys of every chunk list; the keys >= t are placed by rank.
 For unique keys each gives exactly the top-kk in order, also with many equal
@@ -69,11 +70,11 @@ def _rank_place(cand, kk):
 
 
 def _chunk_bound_rank(thread_keys, kk):
-    """None when the kernel falls back to rounds (more than 256 candidates)."""
-    keys = -np.sort(-thread_keys, axis=1)
+    """None when the kernel falls back to rounds (more than 256 candidates).
+    As the kernel: each thread's maximum, its keys >= t in load order (no sort)."""
     gs = 4 if kk <= 32 else 2
-    t = _kth_nonzero(keys[:, 0].reshape(-1, gs).max(axis=1), kk)
-    cand = keys[(keys >= t) & (keys != 0)]
+    t = _kth_nonzero(thread_keys.max(axis=1).reshape(-1, gs).max(axis=1), kk)
+    cand = thread_keys[(thread_keys >= t) & (thread_keys != 0)]
     return None if len(cand) > 256 else _rank_place(cand, kk)
 
 
