@@ -206,18 +206,22 @@ struct AttnArgs {
     float scale;                 // 1/sqrt(128)
 };
 
-__device__ __forceinline__ f16x8 load_f16x8(const uint16_t* p) {
-    return __builtin_bit_cast(f16x8, *reinterpret_cast<const u32x4*>(p));
+// Buffer loads: a per-lane offset past the buffer reads zeros without touching
+// memory, so a load that some lanes must skip stays one unconditional
+// instruction (a load under a branch makes the compiler wait for it, and for
+// everything issued before it, at the branch's end).
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr uint32_t kNoLoad = 0x80000000u;  // offset beyond every buffer here
+__device__ __forceinline__ rsrc_t buf_rsrc(const void* p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
 }
-// Cache reads: with NT the non-temporal hint, for passes that read each
-// slot once (one tile of queries per kv head); with more tiles the other
-// tiles' reads of the same slots find them cached.
+// With NT the non-temporal hint (the nt bit of the cache-policy operand): the
+// cache reads of passes that read each slot once (one tile of queries per kv
+// head); with more tiles the other tiles' reads of the same slots find them
+// cached.
 template <bool NT>
-__device__ __forceinline__ f16x8 load_kv_f16x8(const uint16_t* p) {
-    if constexpr (NT)
-        return __builtin_bit_cast(f16x8, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p)));
-    else
-        return load_f16x8(p);
+__device__ __forceinline__ u32x4 buf_load128(rsrc_t r, uint32_t voff) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0u, NT ? 2 : 0));
 }
 
 // Attention partial of one chunk of slots (blockIdx.x), one kv head
@@ -243,14 +247,12 @@ __global__ __launch_bounds__(64) void attn_partial_kernel(AttnArgs a) {
     // Q^T fragments: query ln, d = 32 ds + 8 grp + i (loaded before the
     // step's position, which they do not need)
     float qv[4][8];
-    const float* qp = a.q + ((size_t)r * a.NH + h) * kHD + 8 * grp;
+    const rsrc_t rq = buf_rsrc(a.q, (uint32_t)(a.R * a.NH * kHD) * 4u);
+    const uint32_t qo = qok ? (uint32_t)(((r * a.NH + h) * kHD + 8 * grp) * 4) : kNoLoad;
 #pragma unroll
     for (int ds = 0; ds < 4; ++ds) {
-        f32x4 v0 = {0.f, 0.f, 0.f, 0.f}, v1 = v0;
-        if (qok) {
-            v0 = *reinterpret_cast<const f32x4*>(qp + 32 * ds);
-            v1 = *reinterpret_cast<const f32x4*>(qp + 32 * ds + 4);
-        }
+        const f32x4 v0 = __builtin_bit_cast(f32x4, buf_load128<false>(rq, qo + 128u * ds));
+        const f32x4 v1 = __builtin_bit_cast(f32x4, buf_load128<false>(rq, qo + 128u * ds + 16u));
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             qv[ds][i] = v0[i];
@@ -272,22 +274,27 @@ __global__ __launch_bounds__(64) void attn_partial_kernel(AttnArgs a) {
     for (int dt = 0; dt < 8; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     const uint16_t* kb = a.kc + (size_t)g * a.C * kHD;
     const uint16_t* vb = a.vc + (size_t)g * a.C * kHD;
-    const f16x8 z8 = {};
 
     // K and V of the step at s0 into (kf, vf): keys rows slot = s0 + 16 t + ln,
     // d = 32 ds + 8 grp .. + 7; values V^T rows d = 16 dt + ln, positions
     // 8 grp .. + 7 of block s0 / 32
-    auto load_kv = [&](long long s0, f16x8 (&kf)[2][4], f16x8 (&vf)[8]) {
+    // (buffer loads: a step past the chunk (live false) reads zeros, so the
+    // loop can request the next step unconditionally)
+    const rsrc_t rk = buf_rsrc(kb, (uint32_t)a.C * kHD * 2u);
+    const rsrc_t rv = buf_rsrc(vb, (uint32_t)a.C * kHD * 2u);
+    auto load_kv = [&](long long s0, f16x8 (&kf)[2][4], f16x8 (&vf)[8], bool live) {
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
             const long long slot = s0 + 16 * t + ln;
-            const uint16_t* kp = kb + (size_t)slot * kHD + 8 * grp;
+            const uint32_t ko = live && slot <= pmax ? (uint32_t)(slot * kHD + 8 * grp) * 2u : kNoLoad;  // 0 past the pass
 #pragma unroll
-            for (int ds = 0; ds < 4; ++ds) kf[t][ds] = slot <= pmax ? load_kv_f16x8<NT>(kp + 32 * ds) : z8;
+            for (int ds = 0; ds < 4; ++ds) kf[t][ds] = __builtin_bit_cast(f16x8, buf_load128<NT>(rk, ko + 64u * ds));
         }
-        const uint16_t* vp = vb + (size_t)(s0 / kKStep) * kHD * kKStep + (size_t)ln * kKStep + 8 * grp;
+        const uint32_t vo =
+            live ? (uint32_t)((s0 / kKStep) * kHD * kKStep + ln * kKStep + 8 * grp) * 2u : kNoLoad;
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt) vf[dt] = load_kv_f16x8<NT>(vp + (size_t)16 * dt * kKStep);
+        for (int dt = 0; dt < 8; ++dt)
+            vf[dt] = __builtin_bit_cast(f16x8, buf_load128<NT>(rv, vo + (uint32_t)(16 * dt * kKStep) * 2u));
     };
     // one online-softmax step over the slots s0 .. s0 + 31 from (kf, vf)
     auto step = [&](long long s0, f16x8 (&kf)[2][4], f16x8 (&vf)[8]) {
@@ -366,7 +373,7 @@ __global__ __launch_bounds__(64) void attn_partial_kernel(AttnArgs a) {
     // hides behind the previous step's arithmetic.
     f16x8 kA[2][4], vA[8], kB[2][4], vB[8];
     long long s0 = cstart;
-    load_kv(s0, kA, vA);
+    load_kv(s0, kA, vA, true);
     // the query's scale and fp16 halves while the first keys and values load
     float amax = 0.f;
 #pragma unroll
@@ -392,12 +399,12 @@ __global__ __launch_bounds__(64) void attn_partial_kernel(AttnArgs a) {
 
     for (;;) {
         const bool more = s0 + kKStep <= cend;
-        if (more) load_kv(s0 + kKStep, kB, vB);
+        load_kv(s0 + kKStep, kB, vB, more);
         step(s0, kA, vA);
         if (!more) break;
         s0 += kKStep;
         const bool more2 = s0 + kKStep <= cend;
-        if (more2) load_kv(s0 + kKStep, kA, vA);
+        load_kv(s0 + kKStep, kA, vA, more2);
         step(s0, kB, vB);
         if (!more2) break;
         s0 += kKStep;
