@@ -64,9 +64,10 @@ __global__ __launch_bounds__(kRouteThreads) void moe_route_kernel(const float* _
         const int r = wave;
         unsigned long long key[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < 4; ++i) {  // clamped index, masked key: the four loads in flight together
             const int e = lane + 64 * i;
-            key[i] = e < E ? order_key(rho[(size_t)r * E + e], e) : 0ull;
+            const float v = rho[(size_t)r * E + (e < E ? e : E - 1)];
+            key[i] = order_key(v, e) & (0ull - (unsigned long long)(e < E));
         }
         float lsel[kMoeMaxTop];
         int isel[kMoeMaxTop];

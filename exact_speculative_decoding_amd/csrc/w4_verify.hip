@@ -249,14 +249,6 @@ __device__ __forceinline__ void w4_block(const W4Args& a, long blk, uint8_t (*xl
     float* out = a.out[mi] + (size_t)split * a.split_stride;
     uint16_t* hout = a.h;
     uint16_t* hcopy = a.h_copy;
-    if (a.gexp) {
-        if (grp >= a.gcount[0]) return;  // whole workgroup: no barrier reached
-        rows = a.gcnt[grp];
-        wmat += (size_t)a.gexp[grp] * a.wstride;
-        wmat1 += (size_t)a.gexp[grp] * a.wstride;
-        out += (size_t)grp * a.ogstride;
-        hout += (size_t)grp * a.hgstride;
-    }
     // activation staging: a superchunk is 16 rows of kSC * 128 k; thread tid
     // loads 16 B (8 k) of row tid / kXL + kXR * m at k = 8 (tid % kXL), m < kXP
     constexpr int kXL = 16 * kSC;          // lanes per row
@@ -266,9 +258,29 @@ __device__ __forceinline__ void w4_block(const W4Args& a, long blk, uint8_t (*xl
     const int xr0 = xt / kXL, col = xt % kXL;
     int xrow[kXP];
 #pragma unroll
-    for (int m = 0; m < kXP; ++m) {
-        const int r = xr0 + kXR * m;
-        xrow[m] = a.grows ? a.grows[16 * grp + r] : (a.gexp ? 16 * grp + r : r);
+    for (int m = 0; m < kXP; ++m) xrow[m] = xr0 + kXR * m;
+    if (a.gexp) {
+        // every table entry of a launched group is in bounds: all of them are
+        // requested before the count is tested (the empty asm takes them as
+        // inputs, so none is sunk past the test into a wait of its own)
+        const int gc = a.gcount[0], cnt = a.gcnt[grp], ge = a.gexp[grp];
+        // the row gather as a buffer load (an empty descriptor without a
+        // table reads zeros), so that no branch sits between the loads
+        const rsrc_t rg = make_rsrc(uniform_ptr(a.grows), a.grows ? (uint32_t)(16 * (grp + 1)) * 4u : 0u);
+        int gr[kXP];
+#pragma unroll
+        for (int m = 0; m < kXP; ++m)
+            gr[m] = (int)__builtin_amdgcn_raw_buffer_load_b32(rg, (uint32_t)(16 * grp + xrow[m]) * 4u, 0u, 0);
+        static_assert(kXP == 2, "the asm below takes both gathered rows");
+        asm volatile("" ::"v"(gc), "v"(cnt), "v"(ge), "v"(gr[0]), "v"(gr[1]));
+#pragma unroll
+        for (int m = 0; m < kXP; ++m) xrow[m] = a.grows ? gr[m] : 16 * grp + xrow[m];
+        if (grp >= gc) return;  // whole workgroup: no barrier reached
+        rows = cnt;
+        wmat += (size_t)ge * a.wstride;
+        wmat1 += (size_t)ge * a.wstride;
+        out += (size_t)grp * a.ogstride;
+        hout += (size_t)grp * a.hgstride;
     }
 
     // the buffer descriptors in scalar registers whatever the compiler proved
