@@ -84,6 +84,7 @@ _SIGS = {
     "toy_decoder_destroy": (None, [_vp]),
     "verify_step_workspace": (_sz, [_vp]),
     "verify_step": (_i32, [_vp, _vp, _i32, _i64, Sampling, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "verify_step_host": (_i32, [_vp, _vp, _i32, _i64, Sampling, _vp, _vp, _vp, _sz, _vp]),
     "ev_read_probe": (_i32, [_vp, _sz, _vp, _vp]),
     "toy_decoder_set_graphs": (_i32, [_vp, _i32]),
     "toy_decoder_graph_stats": (_i32, [_vp, C.POINTER(_i64), C.POINTER(_i32)]),
@@ -512,28 +513,22 @@ class ToyDecoder:
         return sampled, n_commit
 
 
-    def verify_step_host(self, tokens, pos0, temperature, top_k, top_p, seed):
+    def verify_step_host(self, tokens, pos0, temperature, top_k, top_p, seed, stream=None):
         """verify_step for a host round loop: `tokens` is a list of R ints;
-        returns (sampled tokens as a list, n_commit).  The tokens go up from
-        pinned host memory, the R sampled tokens and the commit count come
-        back together (one device buffer, one copy into pinned memory), and
-        the call waits for the current stream once."""
+        returns (sampled tokens as a list, n_commit).  One native call: the
+        tokens go to the step's first kernel as an argument, the results come
+        back in one copy, and the call waits for the stream."""
         R = len(tokens)
-        io = self._host_io.get(R)
+        io = self._host_io.get(("native", R))
         if io is None:
-            dev = self.ws.device
-            io = (torch.empty(R, dtype=torch.int32, pin_memory=True), torch.empty(R, dtype=torch.int32, device=dev),
-                  torch.empty(R + 1, dtype=torch.int32, device=dev),
-                  torch.empty(R + 1, dtype=torch.int32, pin_memory=True))
-            self._host_io[R] = io
-        tok_h, tok_d, out_d, out_h = io
-        tok_h.numpy()[:] = tokens
-        tok_d.copy_(tok_h, non_blocking=True)
-        self.verify_step(tok_d, pos0, temperature, top_k, top_p, seed, sampled=out_d[:R], n_commit=out_d[R:])
-        out_h.copy_(out_d, non_blocking=True)
-        torch.cuda.current_stream(self.ws.device).synchronize()
-        o = out_h.numpy()
-        return o[:R].tolist(), int(o[R])
+            io = ((C.c_int32 * R)(), (C.c_int32 * R)(), C.c_int32())
+            self._host_io[("native", R)] = io
+        tok, smp, nc = io
+        tok[:] = [int(t) for t in tokens]
+        sp = Sampling(float(temperature), int(top_k), float(top_p), int(seed) & ((1 << 64) - 1))
+        _check(lib().verify_step_host(self._h, tok, R, int(pos0), sp, smp, C.byref(nc),
+                                      C.c_void_p(self.ws.data_ptr()), self.ws.numel(), _stream(stream)))
+        return list(smp), int(nc.value)
 
 
 # Value-cache slot order inside a block of 32 slots (see verify_step in

@@ -27,6 +27,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <cstring>
 #include <mutex>
 #include <vector>
 
@@ -96,7 +97,12 @@ constexpr int kMaxRowVec = 4;  // H <= 4 * 4 * kRowThreads = 8192
 // gain); positions[r] = pos0 + 1 + r (the positions the rows sample); the
 // call's tokens and sampling parameters copied where the rest of the step
 // reads them.
-__global__ __launch_bounds__(kRowThreads) void embed_norm_kernel(const int* __restrict__ tokens,
+// A host round's tokens, passed by value to the first kernel of the step.
+struct RowTokens {
+    int32_t t[EV_MAX_LANES];
+};
+
+__global__ __launch_bounds__(kRowThreads) void embed_norm_kernel(const int* __restrict__ tokens, RowTokens ht,
                                                                  const uint16_t* __restrict__ embed, int H, int V,
                                                                  const float* __restrict__ gain, float eps,
                                                                  float* __restrict__ x, uint16_t* __restrict__ n,
@@ -105,7 +111,7 @@ __global__ __launch_bounds__(kRowThreads) void embed_norm_kernel(const int* __re
                                                                  ev_sampling* __restrict__ samp_copy) {
     __shared__ float red[kRowThreads / 64];
     const int r = blockIdx.x, tid = threadIdx.x;
-    int tok = tokens[r];
+    int tok = tokens ? tokens[r] : ht.t[r];  // device tokens, or the host round's by value
     if (tid == 0) tok_copy[r] = tok;  // the drafts, where the rest of the step reads them
     tok = tok < 0 ? 0 : (tok >= V ? V - 1 : tok);  // keeps the read inside the table
     const uint16_t* e = embed + (size_t)tok * H;
@@ -496,7 +502,7 @@ struct StepLayout {
     bool parts_o, parts_down;  // K-parts launches writing kSplitsO / kSplitsDown split rows
     int chunk, nchunk_max;
     bool gu_pair;
-    size_t off_x, off_n, off_o, off_q, off_part, off_pg, off_pu, off_h, off_att, off_logits, off_pos, off_acc,
+    size_t off_x, off_n, off_o, off_q, off_part, off_hres, off_pg, off_pu, off_h, off_att, off_logits, off_pos, off_acc,
         off_sws, off_tok, off_samp, total;
 };
 
@@ -527,6 +533,7 @@ struct ev_decoder {
     uint16_t* vc;
     int C;
     float2* rot = nullptr;  // [C][64] (cos, sin) of slot p's rotation, fp32 of the fp64 values
+    int32_t* hres = nullptr;  // pinned host copy of a host round's results (sampled[16], n_commit)
     int NQKV, DQ;
     StepLayout L;
     bool use_graphs = true;
@@ -539,6 +546,7 @@ struct ev_decoder {
         for (StepGraph& g : graphs) (void)hipGraphExecDestroy(g.exec);
         if (capture) (void)hipStreamDestroy(capture);
         if (rot) (void)hipFree(rot);
+        if (hres) (void)hipHostFree(hres);
     }
 };
 
@@ -601,6 +609,7 @@ static StepLayout step_layout(const ev_decoder_config& c, int NQKV, int DQ, int 
     L.off_sws = take(keyed_sample_workspace(V));
     L.off_tok = take(sizeof(int32_t) * 16);
     L.off_samp = take(sizeof(ev_sampling));
+    L.off_hres = take(sizeof(int32_t) * (EV_MAX_LANES + 1));  // a host round's sampled[16], n_commit
     L.total = off;
     return L;
 }
@@ -664,8 +673,15 @@ extern "C" int32_t toy_decoder_create(const ev_decoder_config* cfg, const ev_dec
         (void)hipFree(rot_dev);
         return rc;
     }
+    int32_t* hres = nullptr;
+    if (hipHostMalloc(reinterpret_cast<void**>(&hres), sizeof(int32_t) * (EV_MAX_LANES + 1), hipHostMallocDefault) !=
+        hipSuccess) {
+        (void)hipFree(rot_dev);
+        return fail(EV_EHIP, "%s: pinned allocation of the round results failed", who);
+    }
     ev_decoder* m = new ev_decoder;
     m->rot = rot_dev;
+    m->hres = hres;
     m->cfg = c;
     m->layers.assign(w->layers, w->layers + c.layers);
     m->embed = w->embed;
@@ -855,30 +871,18 @@ static int32_t step_graph(ev_decoder* m, int R, int32_t* sampled, int32_t* n_com
     return EV_OK;
 }
 
-extern "C" int32_t verify_step(ev_decoder* m, const int32_t* tokens, int32_t R, int64_t pos0, ev_sampling sampling,
-                               int32_t* sampled, int32_t* n_commit, float* logits, void* ws, size_t ws_bytes,
-                               void* stream) {
-    clear_error();
-    const char* who = "verify_step";
+// The step's launches after validation: tokens from device memory, or (tokens
+// NULL) the host round's by value.
+static int32_t step_launch(ev_decoder* m, const int32_t* tokens, const RowTokens& ht, int32_t R, int64_t pos0,
+                           ev_sampling sampling, int32_t* sampled, int32_t* n_commit, float* logits, void* ws,
+                           hipStream_t st) {
     int32_t rc;
-    if (!m) return fail(EV_EINVAL, "%s: NULL decoder", who);
-    if ((rc = check_lanes(who, R))) return rc;
-    if (!tokens || !sampled || !n_commit) return fail(EV_EINVAL, "%s: NULL pointer", who);
-    if (!aligned(tokens, 4) || !aligned(sampled, 4) || !aligned(n_commit, 4) || (logits && !aligned(logits, 16)))
-        return fail(EV_EINVAL, "%s: misaligned pointer", who);
-    if (pos0 < 0 || pos0 + R > m->C)
-        return fail(EV_EINVAL, "%s: slots %lld..%lld outside the cache of %d", who, (long long)pos0,
-                    (long long)pos0 + R - 1, m->C);
-    if ((rc = check_sampling(who, sampling))) return rc;
     const StepLayout& L = m->L;
-    if ((rc = check_ws(who, ws, ws_bytes, L.total))) return rc;
-
     const ev_decoder_config& c = m->cfg;
-    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     unsigned char* b = reinterpret_cast<unsigned char*>(ws);
     // the step's per-call inputs: rows' tokens and positions, on the device
-    hipLaunchKernelGGL(embed_norm_kernel, dim3(R), dim3(kRowThreads), 0, st, tokens, m->embed, c.hidden, c.vocab,
-                       m->layers[0].attn_norm, (float)c.rms_eps, reinterpret_cast<float*>(b + L.off_x),
+    hipLaunchKernelGGL(embed_norm_kernel, dim3(R), dim3(kRowThreads), 0, st, tokens, ht, m->embed, c.hidden,
+                       c.vocab, m->layers[0].attn_norm, (float)c.rms_eps, reinterpret_cast<float*>(b + L.off_x),
                        reinterpret_cast<uint16_t*>(b + L.off_n), reinterpret_cast<long long*>(b + L.off_pos),
                        (long long)pos0, reinterpret_cast<int*>(b + L.off_tok), sampling,
                        reinterpret_cast<ev_sampling*>(b + L.off_samp));
@@ -893,6 +897,59 @@ extern "C" int32_t verify_step(ev_decoder* m, const int32_t* tokens, int32_t R, 
         return check_hip(hipGraphLaunch(exec, st), "step graph launch");
     }
     return step_body(m, R, sampled, n_commit, logits, b, st, true, topp_full);
+}
+
+// Checks shared by verify_step and verify_step_host.
+static int32_t check_step(const char* who, ev_decoder* m, int32_t R, int64_t pos0, ev_sampling sampling, void* ws,
+                          size_t ws_bytes) {
+    int32_t rc;
+    if ((rc = check_lanes(who, R))) return rc;
+    if (pos0 < 0 || pos0 + R > m->C)
+        return fail(EV_EINVAL, "%s: slots %lld..%lld outside the cache of %d", who, (long long)pos0,
+                    (long long)pos0 + R - 1, m->C);
+    if ((rc = check_sampling(who, sampling))) return rc;
+    return check_ws(who, ws, ws_bytes, m->L.total);
+}
+
+extern "C" int32_t verify_step(ev_decoder* m, const int32_t* tokens, int32_t R, int64_t pos0, ev_sampling sampling,
+                               int32_t* sampled, int32_t* n_commit, float* logits, void* ws, size_t ws_bytes,
+                               void* stream) {
+    clear_error();
+    const char* who = "verify_step";
+    int32_t rc;
+    if (!m) return fail(EV_EINVAL, "%s: NULL decoder", who);
+    if (!tokens || !sampled || !n_commit) return fail(EV_EINVAL, "%s: NULL pointer", who);
+    if (!aligned(tokens, 4) || !aligned(sampled, 4) || !aligned(n_commit, 4) || (logits && !aligned(logits, 16)))
+        return fail(EV_EINVAL, "%s: misaligned pointer", who);
+    if ((rc = check_step(who, m, R, pos0, sampling, ws, ws_bytes))) return rc;
+    return step_launch(m, tokens, RowTokens{}, R, pos0, sampling, sampled, n_commit, logits, ws,
+                       reinterpret_cast<hipStream_t>(stream));
+}
+
+extern "C" int32_t verify_step_host(ev_decoder* m, const int32_t* tokens, int32_t R, int64_t pos0,
+                                    ev_sampling sampling, int32_t* sampled, int32_t* n_commit, void* ws,
+                                    size_t ws_bytes, void* stream) {
+    clear_error();
+    const char* who = "verify_step_host";
+    int32_t rc;
+    if (!m) return fail(EV_EINVAL, "%s: NULL decoder", who);
+    if (!tokens || !sampled || !n_commit) return fail(EV_EINVAL, "%s: NULL pointer", who);
+    if ((rc = check_step(who, m, R, pos0, sampling, ws, ws_bytes))) return rc;
+    RowTokens ht{};
+    std::memcpy(ht.t, tokens, sizeof(int32_t) * (size_t)R);
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    // the results at a fixed place in ws (so that the captured step is the
+    // same for every host round with this R and ws), one copy back
+    int32_t* dres = reinterpret_cast<int32_t*>(reinterpret_cast<unsigned char*>(ws) + m->L.off_hres);
+    if ((rc = step_launch(m, nullptr, ht, R, pos0, sampling, dres, dres + EV_MAX_LANES, nullptr, ws, st))) return rc;
+    if ((rc = check_hip(hipMemcpyAsync(m->hres, dres, sizeof(int32_t) * (EV_MAX_LANES + 1), hipMemcpyDeviceToHost,
+                                       st),
+                        "round results copy")))
+        return rc;
+    if ((rc = check_hip(hipStreamSynchronize(st), "round synchronise"))) return rc;
+    std::memcpy(sampled, m->hres, sizeof(int32_t) * (size_t)R);
+    *n_commit = m->hres[EV_MAX_LANES];
+    return EV_OK;
 }
 
 // Grid-aligned chunked prefill (650 Group, "Faster, provably the same model",
@@ -928,7 +985,8 @@ extern "C" int32_t toy_decoder_prefill(ev_decoder* m, const int32_t* tokens, int
         if (g < e) e = g;
         if (pos0 + n < e) e = pos0 + n;
         const int R = (int)(e - p);
-        hipLaunchKernelGGL(embed_norm_kernel, dim3(R), dim3(kRowThreads), 0, st, tokens + (p - pos0), m->embed,
+        hipLaunchKernelGGL(embed_norm_kernel, dim3(R), dim3(kRowThreads), 0, st, tokens + (p - pos0), RowTokens{},
+                           m->embed,
                            c.hidden, c.vocab, m->layers[0].attn_norm, (float)c.rms_eps,
                            reinterpret_cast<float*>(b + L.off_x), reinterpret_cast<uint16_t*>(b + L.off_n),
                            reinterpret_cast<long long*>(b + L.off_pos), p, reinterpret_cast<int*>(b + L.off_tok),

@@ -380,6 +380,22 @@ int32_t verify_step(ev_decoder* m, const int32_t* tokens, int32_t R, int64_t pos
                     ev_sampling sampling, int32_t* sampled, int32_t* n_commit, float* logits,
                     void* ws, size_t ws_bytes, void* stream);
 
+/* verify_step for a host round loop (TensorFold README, exactness paragraph: */
+/* the round's rows are the last committed token and the drafts, and the     */
+/* reply commits the accepted prefix plus the verifier's token).             */
+/*   tokens   (host) [R] int32, read before the call returns: passed to the   */
+/*            step's first kernel as an argument (no copy to the device).     */
+/*   sampled  (host) [R] int32, written; n_commit (host) [1] int32, written:  */
+/*            as for verify_step.                                             */
+/* The step runs on `stream` as verify_step does (graph replay included; its  */
+/* results sit in ws); one copy brings sampled and n_commit back into pinned  */
+/* memory the handle holds, and the call waits for the stream.  Same limits   */
+/* and errors as verify_step (no logits); nothing is launched on a           */
+/* validation error.  Calls on one handle must not overlap.                  */
+int32_t verify_step_host(ev_decoder* m, const int32_t* tokens, int32_t R, int64_t pos0,
+                         ev_sampling sampling, int32_t* sampled, int32_t* n_commit, void* ws,
+                         size_t ws_bytes, void* stream);
+
 /* Graph replay of verify_step on (enable != 0, the default) or off (every    */
 /* step launched kernel by kernel).  Errors: EV_EINVAL (NULL handle).         */
 int32_t toy_decoder_set_graphs(ev_decoder* m, int32_t enable);

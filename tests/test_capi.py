@@ -168,3 +168,10 @@ def test_moe_workspace_depends_on_shapes_only():
     assert a > 0 and a == ev.verify_moe_w4_workspace(2048, 768, 128, 8, 32)
     assert ev.verify_moe_w4_workspace(2048, 768, 128, 9, 32) == 0
     assert ev.verify_moe_w4_workspace(256, 128, 16, 4, 32) < a
+
+
+def test_decoder_steps_reject_a_null_handle():
+    sp = ev.Sampling(0.7, 20, 0.95, 1)
+    toks, smp, nc = (C.c_int32 * 2)(1, 2), (C.c_int32 * 2)(), C.c_int32()
+    assert ev.lib().verify_step_host(None, toks, 2, 0, sp, smp, C.byref(nc), P, 1, None) == ev.EV_EINVAL
+    assert ev.lib().verify_step(None, P, 2, 0, sp, P, P, None, P, 1, None) == ev.EV_EINVAL

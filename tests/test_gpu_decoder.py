@@ -165,8 +165,9 @@ def test_tiny_graph_replay_equals_eager(tiny):
 
 
 def test_tiny_host_round_helper_matches_verify_step(tiny):
-    """verify_step_host (pinned upload, one read-back of the sampled tokens
-    and the commit count) drives the same rounds as verify_step."""
+    """verify_step_host (the native host round: tokens passed to the first
+    kernel by value, one read-back of the sampled tokens and the commit
+    count) drives the same rounds as verify_step."""
     d, cfg = tiny, tiny["cfg"]
     pos0, n, V = cfg["prefill"], 24, cfg["vocab"]
     ref = decode(_gpu_round(_fresh(d), SAMPLED), d["first_token"], pos0, n, 1, lambda p, c: [])[0]
