@@ -208,6 +208,31 @@ def test_tiny_decodes_to_the_last_slot(tiny):
         m2.verify_step(torch.zeros(2, dtype=torch.int32, device="cuda"), cfg["C"] - 1, *SAMPLED)
 
 
+@pytest.mark.parametrize("kw", [dict(heads=32, kv_heads=8), dict(hidden=2176, inter=256)])
+def test_tiny_decoder_launch_shapes(kw):
+    """Shapes whose W4 launches take the other forms: 32 query heads give an o
+    projection of K = 4096 (32 chunks: the 16-wave K-parts workgroups);
+    hidden 2176 (17 chunks) puts q|k|v and gate/up on the halved launches and
+    the LM head on its own plan.  Drafted equals serial, and the oracle checks
+    every position's logits and token."""
+    d = syn.tiny_decoder(seed=1007, **kw)
+    cfg = d["cfg"]
+    pos0, n, V = cfg["prefill"], 16, cfg["vocab"]
+    m = _fresh(d)
+    log = []
+    serial, _ = decode(_gpu_round(m, SAMPLED, log), d["first_token"], pos0, n, 1, lambda p, c: [])
+    m2 = _fresh(d)
+    got, _ = decode(_gpu_round(m2, SAMPLED), d["first_token"], pos0, n, 5,
+                    syn.transcript_drafter(serial, pos0 + 1, 0.65, 4, V))
+    assert got == serial
+    L = pos0 + n
+    assert torch.equal(m2.k_cache[:, :, :L], m.k_cache[:, :, :L])
+    assert torch.equal(m2.v_cache_standard()[:, :, :L], m.v_cache_standard()[:, :, :L])
+    res = _teacher_forced(d, serial, pos0, SAMPLED, set(range(n)), [x[2][0] for x in log])
+    near = _check_stream(res)
+    print(f"{kw}: max row err {max(r[0] for r in res):.3e}, {near} near ties")
+
+
 # --- 8-layer decoder ------------------------------------------------------------------
 
 def _full(C):
