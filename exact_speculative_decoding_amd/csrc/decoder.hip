@@ -192,6 +192,44 @@ __global__ __launch_bounds__(kRowThreads) void res_norm_kernel(const float* __re
     norm_store(xv, gv, ss, eps, H, n + (size_t)r * H, red);
 }
 
+// res_norm_kernel for S (1 or 2) split rows and NV float4s per thread
+// (H <= NV * 4 * kRowThreads): the same sums in the same order, with every
+// load (gain, residual, split rows) issued before the first is used.
+template <int NV, int S>
+__global__ __launch_bounds__(kRowThreads) void res_norm_rows_kernel(const float* __restrict__ part, int H,
+                                                                    float* __restrict__ x,
+                                                                    const float* __restrict__ gain, float eps,
+                                                                    uint16_t* __restrict__ n) {
+    __shared__ float red[kRowThreads / 64];
+    const int r = blockIdx.x, tid = threadIdx.x;
+    const size_t stride = (size_t)16 * H;
+    f32x4 gv[NV], xv[NV], pv[NV][S];
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {  // clamped to the row: a column past H reads column H - 4 and is dropped
+        const int c = 4 * (tid + kRowThreads * j);
+        const size_t o = (size_t)r * H + (c < H ? c : H - 4);
+        gv[j] = *reinterpret_cast<const f32x4*>(gain + (c < H ? c : H - 4));
+        xv[j] = *reinterpret_cast<const f32x4*>(x + o);
+#pragma unroll
+        for (int sp = 0; sp < S; ++sp) pv[j][sp] = *reinterpret_cast<const f32x4*>(part + sp * stride + o);
+    }
+    float ss = 0.f;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+        const int c = 4 * (tid + kRowThreads * j);
+        f32x4 lin = pv[j][0];
+#pragma unroll
+        for (int sp = 1; sp < S; ++sp) lin += pv[j][sp];
+        const f32x4 v = xv[j] + lin;
+        if (c < H) {
+            *reinterpret_cast<f32x4*>(x + (size_t)r * H + c) = v;
+            ss += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
+        }
+        xv[j] = c < H ? v : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    norm_store(xv, gv, ss, eps, H, n + (size_t)r * H, red);
+}
+
 // Value cache layout: blocks of 32 slots, d-major inside a block
 // ([kv_heads][C/32][128][32]), and within a block slot s at position
 // vslot_pos32(s): positions 8j..8j+7 hold slots 4j..4j+3 and 16+4j..16+4j+3.
@@ -755,6 +793,28 @@ static int32_t step_body(ev_decoder* m, int R, int32_t* sampled, int32_t* n_comm
         return launch_w4(a, 1, p, K, G, st);
     };
     const SkGeom no_sk{0, 0, 0, 0};
+    // x += the linear's rows (split rows of a K-parts launch: the specialised
+    // kernel; segments or wider splits: the general one), then n = the norm
+    auto res_norm = [&](bool parts, int S, const SkGeom& g, const float* gain) {
+        const int nv = (H + 4 * kRowThreads - 1) / (4 * kRowThreads);
+        if (parts && (S == 1 || S == 2) && nv <= kMaxRowVec) {
+            if (S == 1 && nv == 1)
+                hipLaunchKernelGGL((res_norm_rows_kernel<1, 1>), dim3(R), dim3(kRowThreads), 0, st, part, H, x,
+                                   gain, eps, n);
+            else if (nv == 1)
+                hipLaunchKernelGGL((res_norm_rows_kernel<1, 2>), dim3(R), dim3(kRowThreads), 0, st, part, H, x,
+                                   gain, eps, n);
+            else if (S == 1)
+                hipLaunchKernelGGL((res_norm_rows_kernel<kMaxRowVec, 1>), dim3(R), dim3(kRowThreads), 0, st, part,
+                                   H, x, gain, eps, n);
+            else
+                hipLaunchKernelGGL((res_norm_rows_kernel<kMaxRowVec, 2>), dim3(R), dim3(kRowThreads), 0, st, part,
+                                   H, x, gain, eps, n);
+        } else {
+            hipLaunchKernelGGL(res_norm_kernel, dim3(R), dim3(kRowThreads), 0, st, part, S, g, H, x, gain, eps, n);
+        }
+        return check_hip(hipGetLastError(), "res_norm launch");
+    };
 
     const int nqt = (R * (NH / NKV) + 15) / 16;
     for (int l = 0; l < c.layers; ++l) {
@@ -787,9 +847,9 @@ static int32_t step_body(ev_decoder* m, int R, int32_t* sampled, int32_t* n_comm
                            L.nchunk_max, pos, o);
         if ((rc = check_hip(hipGetLastError(), "attn_merge launch"))) return rc;
         if ((rc = linear(y.w_o, o, m->DQ, H, L.p_o, L.q_o, L.sk_o, L.parts_o, kSplitsO))) return rc;
-        hipLaunchKernelGGL(res_norm_kernel, dim3(R), dim3(kRowThreads), 0, st, part, L.parts_o ? kSplitsO : L.p_o.S,
-                           L.sk_o && !L.parts_o ? sk_geom(L.q_o) : no_sk, H, x, y.mlp_norm, eps, n);
-        if ((rc = check_hip(hipGetLastError(), "res_norm launch"))) return rc;
+        if ((rc = res_norm(L.parts_o, L.parts_o ? kSplitsO : L.p_o.S, L.sk_o && !L.parts_o ? sk_geom(L.q_o) : no_sk,
+                           y.mlp_norm)))
+            return rc;
         {  // h = SiLU(gate) * up: one paired launch, or gate|up + split sum with SiLU * up
             W4Args a{};
             a.w[0] = reinterpret_cast<const uint8_t*>(y.w_gate);
@@ -811,10 +871,9 @@ static int32_t step_body(ev_decoder* m, int R, int32_t* sampled, int32_t* n_comm
         }
         if ((rc = linear(y.w_down, h, I, H, L.p_down, L.q_down, L.sk_down, L.parts_down, kSplitsDown))) return rc;
         const float* next = l + 1 < c.layers ? m->layers[l + 1].attn_norm : m->final_norm;
-        hipLaunchKernelGGL(res_norm_kernel, dim3(R), dim3(kRowThreads), 0, st, part,
-                           L.parts_down ? kSplitsDown : L.p_down.S, L.sk_down && !L.parts_down ? sk_geom(L.q_down) : no_sk, H,
-                           x, next, eps, n);
-        if ((rc = check_hip(hipGetLastError(), "res_norm launch"))) return rc;
+        if ((rc = res_norm(L.parts_down, L.parts_down ? kSplitsDown : L.p_down.S,
+                           L.sk_down && !L.parts_down ? sk_geom(L.q_down) : no_sk, next)))
+            return rc;
     }
     if (!head) return EV_OK;  // prefill: the layers only (their cache entries)
     if ((rc = linear(m->w_lm, n, H, V, L.p_lm, L.q_lm, L.sk_lm, false))) return rc;
