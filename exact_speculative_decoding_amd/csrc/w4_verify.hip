@@ -102,6 +102,25 @@ __device__ __forceinline__ u32x4 decode_nibbles(uint32_t d, uint32_t m, uint32_t
     return r;
 }
 
+// Issue priority from a wave's progress through its own run of chunks: 3 in
+// the first quarter, 2, 1, then 0 in the last.  Waves that share a CU are
+// otherwise served oldest first, so the workgroups dispatched first finish
+// early and the last ones run the end of the launch on a part-empty CU; with
+// the priority falling as a wave gets ahead, the ones behind are served first
+// and the runs of a CU end together.  Only the order in which ready waves
+// issue changes, never what they compute.
+__device__ __forceinline__ void progress_priority(int done, int total) {
+    const int lv = (4 * done >= total) + (4 * done >= 2 * total) + (4 * done >= 3 * total);
+    if (lv == 0)
+        __builtin_amdgcn_s_setprio(3);
+    else if (lv == 1)
+        __builtin_amdgcn_s_setprio(2);
+    else if (lv == 2)
+        __builtin_amdgcn_s_setprio(1);
+    else
+        __builtin_amdgcn_s_setprio(0);
+}
+
 __device__ __forceinline__ float half_lo(uint32_t w) { return f16_to_f32((uint16_t)(w & 0xffffu)); }
 __device__ __forceinline__ float half_hi(uint32_t w) { return f16_to_f32((uint16_t)(w >> 16)); }
 
@@ -411,6 +430,8 @@ __device__ __forceinline__ void w4_block(const W4Args& a, long blk, uint8_t (*xl
     // Prologue: superchunk 0 of the split loaded, the first kPD chunks of
     // weights in flight behind it, the superchunk into LDS slab 0, superchunk 1
     // in registers.
+    const bool prio = MODE == kPlain && !a.gexp;  // uniform: dense plain launches
+    if (prio) progress_priority(0, 1);
     const int sc0 = c0 / kSC;
     xload(sc0);
 #pragma unroll
@@ -445,6 +466,7 @@ __device__ __forceinline__ void w4_block(const W4Args& a, long blk, uint8_t (*xl
     for (int it = 0, cb = c0; it < ntrip; ++it, cb += kSC) {
 #pragma unroll
         for (int p = 0; p < kSC; ++p) {
+            if (prio) progress_priority(kSC * it + p, kSC * ntrip);
             __builtin_amdgcn_sched_barrier(0);
             compute(p % kPD, &xlds[2 * half + buf][(size_t)p * kXChunkBytes]);
             __builtin_amdgcn_sched_barrier(0);
@@ -722,6 +744,7 @@ __device__ __forceinline__ void w4_sk_block(const W4Args& a, int w, uint8_t (*xl
     // Prologue: unit u0's activations loaded, its first kPD chunks of weights
     // in flight behind them, the activations into slab 0, unit u0 + 1's
     // activations in registers.
+    progress_priority(0, 1);
     Unit nxt = next(cur);
     xload(true, cur.sc);
 #pragma unroll
@@ -744,6 +767,7 @@ __device__ __forceinline__ void w4_sk_block(const W4Args& a, int w, uint8_t (*xl
         const bool live1 = u + 1 < u1;
 #pragma unroll
         for (int p = 0; p < kSC; ++p) {
+            progress_priority(kSC * (u - u0) + p, kSC * (u1 - u0));
             __builtin_amdgcn_sched_barrier(0);
             compute(p % kPD, &xlds[buf][(size_t)p * kXChunkBytes]);
             __builtin_amdgcn_sched_barrier(0);
