@@ -66,7 +66,7 @@ struct SkPlan {
     int nwg;     // workgroups
     int segmax;  // partial segments per workgroup, at most
     int units;   // nmat * ncgb * nsc
-    bool ok;     // the unit arithmetic fits 32 bits (units * nwg < 2^31)
+    bool ok;     // the unit arithmetic fits 32 bits (units * nwg < 2^31), the segments 4 GiB
 };
 inline SkPlan plan_w4_sk(int N, int K, int nmat) {
     SkPlan p;
@@ -79,6 +79,8 @@ inline SkPlan plan_w4_sk(int N, int K, int nmat) {
     p.nwg = (int)nwg;
     const long L = (U + nwg - 1) / nwg;  // longest run
     p.segmax = (int)((L + p.nsc - 2) / p.nsc + 1);
+    // the segments are stored through a buffer descriptor: 32-bit byte range
+    p.ok = p.ok && (double)nwg * p.segmax * 16 * kBlockCols * 4 < 4294967296.0;
     return p;
 }
 // A plain launch runs balanced when its split plan would need partial rows

@@ -725,19 +725,30 @@ __device__ __forceinline__ void w4_sk_block(const W4Args& a, int w, uint8_t (*xl
             }
         }
     };
-    // segment s of the run: rows r = 4j + i of the block's columns
-    // (wave, tile) * 16 + ln; the accumulators start again from zero
+    // segment s of the run: the wave's 16 rows x (kNT * 16) columns
+    // (block columns (wave, tile) * 16 + ln hold rows 4j + i) are turned
+    // through a wave-private LDS tile, so that a lane stores 4 consecutive
+    // columns of one row and every store writes whole 128-B lines (rows
+    // >= R are not written); the accumulators start again from zero
+    static_assert(kNT * 16 == 32, "a lane stores a quarter of a wave's 128-B row");
+    __shared__ __align__(16) float segx[kWaves][16 * 32];
+    float* const sx = segx[wave];
+    const rsrc_t rp = make_rsrc(uniform_ptr(a.sk_part),
+                                (uint32_t)((size_t)a.sk_nwg * a.sk_segmax * 16 * kBlockCols * sizeof(float)));
     auto flush = [&](int s) {
-        float* o = a.sk_part + ((size_t)w * a.sk_segmax + s) * 16 * kBlockCols;
 #pragma unroll
         for (int t = 0; t < kNT; ++t) {
-            const int cl = (wave * kNT + t) * 16 + ln;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = 4 * j + i;
-                if (r < rows) o[(size_t)r * kBlockCols + cl] = FMT == kNvfp4 ? y[t][i] * a.tscale : y[t][i];
-            }
+            for (int i = 0; i < 4; ++i) sx[(4 * j + i) * 32 + t * 16 + ln] = FMT == kNvfp4 ? y[t][i] * a.tscale : y[t][i];
             y[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        const uint32_t seg = (uint32_t)(((size_t)w * a.sk_segmax + s) * 16 * kBlockCols * sizeof(float));
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int r = (lane >> 3) + 8 * h, c4 = 4 * (lane & 7);
+            const u32x4 v = *reinterpret_cast<const u32x4*>(&sx[r * 32 + c4]);
+            const uint32_t off = seg + (uint32_t)(r * kBlockCols + wave * 32 + c4) * 4u;
+            __builtin_amdgcn_raw_buffer_store_b128(v, rp, r < rows ? off : kOOB, 0u, 0);
         }
     };
 
