@@ -590,9 +590,10 @@ def main():
     pct = step_percentiles(R, args.steps)
 
     per_r = {}
+    sweep_steps = max(args.steps, 100)  # ~4 ms a point: a short window is at the mercy of clock noise
     if not args.no_sweep:
         for r in (1, 2, 4, 8, 16):
-            m = timed(r, args.steps, 20)
+            m = timed(r, sweep_steps, 50)
             g = mlp_bytes(r, H, I, G) / (m * 1e-3) / 1e9
             per_r[str(r)] = {"us_per_pass": round(m * 1e3, 2), "GB_s": round(g, 1),
                              "pct_hbm_peak": round(100 * g / HBM_PEAK_GBS, 1),
@@ -602,11 +603,11 @@ def main():
     # dominant kernel: the W4 kernel (both W4 launches of the slice), each
     # launch timed by the device wall-clock stamps of its workgroups, over as
     # many steps again; at the config's R, then at every R of the sweep
-    def kernel_roofline(r):
+    def kernel_roofline(r, steps):
         torch.cuda.synchronize()
         ev.w4_timing_read()
         ev.w4_timing(True)
-        for i in range(args.steps):
+        for i in range(steps):
             eager(i, r)
         torch.cuda.synchronize()
         ev.w4_timing(False)
@@ -614,7 +615,7 @@ def main():
         k_gbs = k_bytes / (k_ms * 1e-3) / 1e9
         return n_launch, k_ms, k_bytes, k_gbs
 
-    n_launch, k_ms, k_bytes, k_gbs = kernel_roofline(R)
+    n_launch, k_ms, k_bytes, k_gbs = kernel_roofline(R, args.steps)
     traffic = load_traffic()
     roofline = {"kernel": "w4_sk_kernel", "bound": "hbm", "achieved": round(k_gbs, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(k_gbs / HBM_PEAK_GBS, 4),
@@ -624,7 +625,7 @@ def main():
     if not args.no_sweep:
         roofline["per_R"] = {}
         for r in (1, 2, 4, 8, 16):
-            nl, kms, kby, kg = kernel_roofline(r)
+            nl, kms, kby, kg = kernel_roofline(r, sweep_steps)
             roofline["per_R"][str(r)] = {"achieved": round(kg, 1), "frac": round(kg / HBM_PEAK_GBS, 4),
                                          "avg_launch_us": round(1e3 * kms / max(nl, 1), 2),
                                          "algorithmic_bytes_per_launch": round(kby / max(nl, 1))}
