@@ -27,11 +27,15 @@
 //   * a ring of kPD chunks of loads is kept in flight per wave; loads past the
 //     split's last chunk use an out-of-range per-lane offset, which the buffer
 //     range check turns into zeros without touching memory;
+//   * in the balanced launch and the dense plain split launches a wave's issue
+//     priority falls as it gets through its run (progress_priority), so the
+//     workgroups that share a CU end together;
 //   * dense launches that need a K-split run balanced (w4_sk_kernel): 768
 //     workgroups each take an equal contiguous run of (matrix, column block,
 //     superchunk) units and write one partial segment per block their run
-//     touches; a second kernel adds a block's segments in ascending workgroup
-//     order (fused with SiLU * up for the MLP gate/up pair).  Launches whose
+//     touches (whole 128-B lines, turned through LDS); a second kernel adds
+//     a block's segments in ascending workgroup order (fused with SiLU * up
+//     for the MLP gate/up pair).  Launches whose
 //     columns alone fill the chip (the LM head) and the grouped MoE down
 //     passes run split (w4_verify_kernel: a plan of S splits, partials
 //     [S][16][N] added in ascending split order, or direct outputs at S = 1);
