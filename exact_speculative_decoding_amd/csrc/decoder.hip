@@ -316,6 +316,7 @@ __global__ __launch_bounds__(64) void attn_partial_kernel(AttnArgs a) {
     f32x4 acc[8];
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    __shared__ f32x4 keep[8][64];  // the workgroup is one wave
     const uint16_t* kb = a.kc + (size_t)g * a.C * kHD;
     const uint16_t* vb = a.vc + (size_t)g * a.C * kHD;
 
@@ -397,19 +398,24 @@ __global__ __launch_bounds__(64) void attn_partial_kernel(AttnArgs a) {
             ph[i] = hv;
             pl[i] = (_Float16)(p[i] - (float)hv);
         }
-        // O^T = O^T * scale + V^T P^T; a query without a slot here keeps its state bit for bit
+        // O^T = O^T * scale + V^T P^T; a query without a slot here keeps its
+        // state bit for bit.  Its copy waits in LDS, and only in the steps
+        // where some query of the wave has no slot: as 32 more registers it
+        // would hold the kernel to one wave per SIMD.
         const bool keep_any = __any(qok && !live);
-        f32x4 keep[8];
+        if (keep_any) {
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt) keep[dt][lane] = acc[dt];
+        }
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) {
-            keep[dt] = acc[dt];
             acc[dt] *= scl;
             acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf[dt], ph, acc[dt], 0, 0, 0);
             acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf[dt], pl, acc[dt], 0, 0, 0);
         }
         if (keep_any && !live) {
 #pragma unroll
-            for (int dt = 0; dt < 8; ++dt) acc[dt] = keep[dt];
+            for (int dt = 0; dt < 8; ++dt) acc[dt] = keep[dt][lane];
         }
     };
     // The loads of step s + 1 are issued before step s is computed (two
