@@ -68,6 +68,7 @@ SHAPES = [  # (K, N, G)
     (4096 + 64, 17, 64),  # one column block summed from 17 workgroups
     (5120, 5000, 64),    # balanced runs of 1-2 superchunks crossing block boundaries
     (4096, 6200, 32),    # the same with group 32, ragged N
+    (5248, 2000, 64),    # balanced, an odd number of full chunks (the last superchunk half past K)
 ]
 
 
@@ -86,7 +87,7 @@ def test_random_parity_with_oracle(K, N, G):
 
 
 @pytest.mark.parametrize("K,N,G", [(256, 512, 64), (320, 40, 32), (5120, 1000, 64), (2048, 300, 32),
-                                   (5120, 5000, 64)])
+                                   (5120, 5000, 64), (4096 + 64, 17, 64), (4096, 6200, 32), (5248, 2000, 64)])
 def test_rows_bit_identical_to_single_row_calls(K, N, G):
     g = np.random.default_rng(5 + K + N)
     w = syn.w4_matrix(g, N, K, G)
