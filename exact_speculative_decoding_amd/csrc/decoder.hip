@@ -649,7 +649,7 @@ static StepLayout step_layout(const ev_decoder_config& c, int NQKV, int DQ, int 
     L.off_att = take(sizeof(float) * 16 * (size_t)c.heads * L.nchunk_max * kPartStride);
     L.off_logits = take(sizeof(float) * 16 * (size_t)V);
     L.off_pos = take(sizeof(long long) * (kPos0Slot + 1));
-    L.off_acc = take(sizeof(int32_t) * 4);
+    L.off_acc = take(sizeof(int32_t) * 4);  // n_accept, the sampler's accept count
     L.off_sws = take(keyed_sample_workspace(V));
     L.off_tok = take(sizeof(int32_t) * 16);
     L.off_samp = take(sizeof(ev_sampling));
@@ -888,15 +888,15 @@ static int32_t step_body(ev_decoder* m, int R, int32_t* sampled, int32_t* n_comm
     } else if ((rc = launch_splitk_reduce(part, L.p_lm.S, V, R, lg, st))) {
         return rc;
     }
-    void* sv = reinterpret_cast<void*>(st);
     // the sampling parameters come from the workspace (written by embed_norm);
     // the host value only picks the launch sequence (top-k candidates, or top-p
     // over the whole vocabulary) and is never read by the kernels
     const ev_sampling any{1.0, topp_full ? 0 : EV_MAX_TOPK, 1.0, 0};
-    if ((rc = launch_keyed_sample(lg, R, V, pos, any, reinterpret_cast<const ev_sampling*>(b + L.off_samp), sampled,
-                                  nullptr, sws, st)))
-        return rc;
-    return accept_prefix(sampled, R, R > 1 ? toks + 1 : nullptr, R - 1, n_accept, n_commit, sv);
+    // the accept prefix against the drafts (the step's tokens 1..R-1) by the
+    // sampler's last workgroup; its count sits in the word after n_accept
+    const FusedAccept acc{n_accept + 1, R > 1 ? toks + 1 : nullptr, R - 1, n_accept, n_commit};
+    return launch_keyed_sample(lg, R, V, pos, any, reinterpret_cast<const ev_sampling*>(b + L.off_samp), sampled,
+                               nullptr, sws, st, &acc);
 }
 
 // The captured step for these arguments: found in the cache, or captured on

@@ -22,8 +22,20 @@ int32_t check_sampling(const char* who, const ev_sampling& s);
 // The launches of keyed_sample on checked arguments; with `sd` (device) the
 // kernels read the sampling parameters there rather than from `s`, which then
 // only has to give a valid top-k for the launch's candidate count bound.
+// The accept prefix folded into the top-k sampler's last workgroup (the verify
+// step): n_accept = leading i < D with draft[i] == tokens[i], n_commit =
+// min(n_accept + 1, R); `count` is a device int the sampler's first kernel
+// clears and its last workgroup to finish restores to zero.
+struct FusedAccept {
+    int* count;
+    const int32_t* draft;
+    int D;
+    int32_t* n_accept;
+    int32_t* n_commit;
+};
 int32_t launch_keyed_sample(const float* logits, int R, int V, const long long* positions, const ev_sampling& s,
-                            const ev_sampling* sd, int32_t* tokens, double* gap, void* ws, hipStream_t st);
+                            const ev_sampling* sd, int32_t* tokens, double* gap, void* ws, hipStream_t st,
+                            const FusedAccept* acc = nullptr);
 
 inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 

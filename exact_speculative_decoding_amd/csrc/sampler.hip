@@ -166,7 +166,9 @@ __host__ __device__ inline int sample_kk_of(double T, int top_k, int V) {
 __global__ __launch_bounds__(kSThreads) void topk_chunk_kernel(const float* __restrict__ logits,
                                                                int V, int kk, int nchunk,
                                                                const ev_sampling* __restrict__ sd,
-                                                               unsigned long long* __restrict__ out) {
+                                                               unsigned long long* __restrict__ out,
+                                                               int* __restrict__ acc_count) {
+    if (acc_count && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *acc_count = 0;
     if (sd) kk = sample_kk_of(sd->temperature, sd->top_k, V);  // parameters kept on the device
     constexpr int kW = kSThreads / 64;
     __shared__ unsigned long long rest[kPer - 1][kSThreads];  // thread t's keys 1..15 in column t
@@ -280,7 +282,35 @@ struct SampleArgs {
     const ev_sampling* sd;  // when non-NULL, T, top_k, top_p and seed are read here
     int* tokens;
     double* gap;
+    FusedAccept acc;  // acc.count == NULL: no accept here
+    int R;
 };
+
+// The accept prefix by the last of the R merge workgroups to store its token
+// (wave 0, after its lane 0 stored the row's token): each workgroup makes its
+// token visible device-wide before it counts itself; the one that completes
+// the count sees every row's token, compares the drafts as accept_kernel
+// does, and clears the count for the next step.
+__device__ __forceinline__ void fused_accept(const SampleArgs& a) {
+    if (!a.acc.count) return;
+    const int lane = threadIdx.x & 63;
+    int last = 0;
+    if (lane == 0) {
+        __threadfence();
+        last = atomicAdd(a.acc.count, 1) == a.R - 1;
+    }
+    if (!__shfl(last, 0, 64)) return;
+    __threadfence();
+    const int i = lane;
+    const bool mism = i < a.acc.D && a.acc.draft[i] != a.tokens[i];
+    const unsigned long long mask = __ballot(mism);
+    const int n = mask ? (__ffsll((long long)mask) - 1) : a.acc.D;
+    if (lane == 0) {
+        *a.acc.n_accept = n;
+        *a.acc.n_commit = n + 1 < a.R ? n + 1 : a.R;
+        *a.acc.count = 0;
+    }
+}
 
 // k-way merge of sorted lists in kk rounds by one wave (lane c follows list
 // c, `has` for c < nchunk): a round takes the maximum of the heads, the lane
@@ -404,6 +434,7 @@ __global__ __launch_bounds__(kMThreads) void merge_sample_kernel(SampleArgs a) {
             a.tokens[r] = id0;
             if (a.gap) a.gap[r] = ncand > 1 ? l0 - l1 : __builtin_huge_val();
         }
+        fused_accept(a);
         return;
     }
 
@@ -447,6 +478,7 @@ __global__ __launch_bounds__(kMThreads) void merge_sample_kernel(SampleArgs a) {
         a.tokens[r] = bid;
         if (a.gap) a.gap[r] = kept > 1 ? bz - sz : __builtin_huge_val();
     }
+    fused_accept(a);
 }
 
 // ---- top-p over the whole vocabulary (top_k == 0) ------------------------------
@@ -825,7 +857,8 @@ namespace ev {
 // (the verify step keeps them in its workspace, so that one captured step
 // serves every seed and temperature).
 int32_t launch_keyed_sample(const float* logits, int R, int V, const long long* positions, const ev_sampling& s,
-                            const ev_sampling* sd, int32_t* tokens, double* gap, void* ws, hipStream_t st) {
+                            const ev_sampling* sd, int32_t* tokens, double* gap, void* ws, hipStream_t st,
+                            const FusedAccept* acc) {
     const int nchunk = sample_nchunk(V);
     if (s.temperature > 0.0 && s.top_k == 0) {  // top-p over the whole vocabulary
         unsigned char* b = reinterpret_cast<unsigned char*>(ws);
@@ -838,16 +871,19 @@ int32_t launch_keyed_sample(const float* logits, int R, int V, const long long* 
         for (int d = 0; d < kTpPasses; ++d) hipLaunchKernelGGL(tp_hist_kernel, grid, dim3(kSThreads), 0, st, a, d);
         hipLaunchKernelGGL(tp_pick_kernel, grid, dim3(kSThreads), 0, st, a);
         hipLaunchKernelGGL(tp_merge_kernel, dim3(R), dim3(64), 0, st, a);
+        if (acc)  // here the accept prefix stays a launch of its own
+            hipLaunchKernelGGL(accept_kernel, dim3(1), dim3(64), 0, st, tokens, R, acc->draft, acc->D,
+                               acc->n_accept, acc->n_commit);
         return check_hip(hipGetLastError(), "top-p launches");
     }
     const int kk = sample_kk_of(s.temperature, s.top_k, V);
     unsigned long long* cand = reinterpret_cast<unsigned long long*>(ws);
     hipLaunchKernelGGL(topk_chunk_kernel, dim3(nchunk, R), dim3(kSThreads), 0, st, logits, V, kk, nchunk, sd,
-                       cand);
+                       cand, acc ? acc->count : nullptr);
     int32_t rc = check_hip(hipGetLastError(), "topk_chunk launch");
     if (rc) return rc;
     SampleArgs a{cand, positions, nchunk, kk, V, s.temperature, s.top_p, (unsigned long long)s.seed, sd,
-                 tokens, gap};
+                 tokens, gap, acc ? *acc : FusedAccept{}, R};
     hipLaunchKernelGGL(merge_sample_kernel, dim3(R), dim3(kMThreads), 0, st, a);
     return check_hip(hipGetLastError(), "merge_sample launch");
 }
